@@ -1,0 +1,251 @@
+"""Plain CPU oracle for DeepSeek-V3 Multi-head Latent Attention (MLA).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or links
+this module: only the tests, ``__graft_entry__.smoke()`` and the cpu_baseline
+leg of ``bench.py`` use it.  It shares no code with the HIP library; the only
+module both sides consume is ``mla_inputs`` (seeded draws, no arithmetic of the
+method).
+
+Everything is float64 numpy and follows the non-absorbed MLA equations in the
+order the pages write them:
+  "DeepSeek V3 technical paper, close reading" notes (hk.pswp.cn), section 2.1
+  "Multi-Head Latent Attention", items "Key and Value compression", "Query
+  compression" and "attention computation";
+  the V3 technical-report summary (cooktownmusic.com), "hyperparameters"
+  paragraph, for the dimensions;
+  the same section 2.1, "advantages of MLA", for what the cache holds.
+
+Readings of passages the pages leave open (their sub- and superscripts were
+lost in extraction):
+  * the RoPE key k_R is one vector per token shared by all heads (the cache
+    holds only c_KV and k_R); the RoPE query q_R is split per head;
+  * RoPE rotates interleaved pairs (2k, 2k+1) by p * base^(-2k/d_R), with p the
+    0-based position in the sequence;
+  * attention is causal: query at position t sees keys 0..t;
+  * the softmax scale is 1/sqrt(d_h + d_R) (d_h the per-head content width);
+  * head i owns the i-th contiguous slice of each up-projection output and of
+    W_O's input;
+  * weights are stored [out][in] because the pages write W*h;
+  * decode appends the new tokens first: the n_q queries of a sequence with L
+    tokens sit at positions L-n_q..L-1.
+
+Pins (tests/test_oracle.py): absorbed == non-absorbed form; softmax rows sum
+to 1; causal invariance; the closed-form cache size; single-key and
+zero-query closed forms; the plain-MHA special case against PyTorch's
+scaled_dot_product_attention; RoPE rotation properties; prefill + decode ==
+longer prefill; a scalar brute force on a micro case.  The RoPE pairing
+convention (interleaved versus half-split) is a reading the mathematics does
+not fix: any pairing passes the rotation pins, so that one choice is parity
+unpinned beyond agreement of the two sides on the same reading.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "rope", "compress_kv", "project_queries", "head_keys_values", "attend_head",
+    "output_projection", "prefill", "decode", "decode_absorbed",
+    "cache_elements_per_token", "mha_elements_per_token", "softmax_scale",
+]
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# RoPE (section 2.1: "ROPE(W_KR h)" and "ROPE(W_QR c_Q)")
+# ---------------------------------------------------------------------------
+
+def rope(x, pos, base):
+    """Rotate interleaved pairs (x[2k], x[2k+1]) by angle pos * base^(-2k/d_R).
+
+    x: [..., d_R]; pos: integer array broadcastable to x.shape[:-1]."""
+    x = _f64(x)
+    d_r = x.shape[-1]
+    k = np.arange(d_r // 2, dtype=np.float64)
+    theta = np.power(float(base), -2.0 * k / d_r)
+    ang = _f64(pos)[..., None] * theta
+    c, s = np.cos(ang), np.sin(ang)
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = xe * c - xo * s
+    out[..., 1::2] = xe * s + xo * c
+    return out
+
+
+def softmax_scale(dims):
+    """1/sqrt(d_h + d_R): section 2.1, attention computation."""
+    return 1.0 / np.sqrt(dims.d_nope + dims.d_rope)
+
+
+# ---------------------------------------------------------------------------
+# Key/value compression (section 2.1, "Key and Value compression")
+# ---------------------------------------------------------------------------
+
+def compress_kv(W, h, pos, dims):
+    """c_KV = W_DKV h and k_R = RoPE(W_KR h) for tokens h [T][d_model] at
+    positions pos [T].  These two are the whole cached row."""
+    h = _f64(h)
+    c_kv = h @ _f64(W["w_dkv"]).T
+    k_r = rope(h @ _f64(W["w_kr"]).T, pos, dims.rope_base)
+    return c_kv, k_r
+
+
+def head_keys_values(W, c_kv, i, dims):
+    """Head i's content keys k_C = W_UK c_KV and values v_C = W_UV c_KV
+    (rows i*d_h..(i+1)*d_h of the up-projections)."""
+    w_uk_i = _f64(W["w_uk"])[i * dims.d_nope:(i + 1) * dims.d_nope]
+    w_uv_i = _f64(W["w_uv"])[i * dims.d_v:(i + 1) * dims.d_v]
+    c_kv = _f64(c_kv)
+    return c_kv @ w_uk_i.T, c_kv @ w_uv_i.T
+
+
+# ---------------------------------------------------------------------------
+# Query compression (section 2.1, "Query compression")
+# ---------------------------------------------------------------------------
+
+def project_queries(W, h, pos, dims):
+    """c_Q = W_DQ h; q_C = W_UQ c_Q split into heads; q_R = RoPE(W_QR c_Q)
+    split into heads.  Returns q_C [T][n_h][d_h], q_R [T][n_h][d_R]."""
+    h = _f64(h)
+    T = h.shape[0]
+    c_q = h @ _f64(W["w_dq"]).T
+    q_c = (c_q @ _f64(W["w_uq"]).T).reshape(T, dims.n_heads, dims.d_nope)
+    q_r_raw = (c_q @ _f64(W["w_qr"]).T).reshape(T, dims.n_heads, dims.d_rope)
+    q_r = rope(q_r_raw, _f64(pos)[:, None], dims.rope_base)
+    return q_c, q_r
+
+
+# ---------------------------------------------------------------------------
+# Attention (section 2.1, "attention computation")
+# ---------------------------------------------------------------------------
+
+def attend_head(q_c_i, q_r_i, qpos, k_c_i, k_r, v_i, scale, return_probs=False):
+    """o_{t,i} = sum_{j<=t} softmax_j((q_{t,i} . k_{j,i}) * scale) v_{j,i}
+    with q = [q_C; q_R] and k = [k_C; k_R].
+
+    q_c_i [T][d_h], q_r_i [T][d_R], qpos [T]; k_c_i [L][d_h], k_r [L][d_R],
+    v_i [L][d_v].  The full score row is formed, masked, and normalised in one
+    piece (no online softmax)."""
+    s = (_f64(q_c_i) @ _f64(k_c_i).T + _f64(q_r_i) @ _f64(k_r).T) * scale
+    L = s.shape[1]
+    visible = np.arange(L)[None, :] <= np.asarray(qpos)[:, None]
+    s = np.where(visible, s, -np.inf)
+    m = np.max(s, axis=1, keepdims=True)
+    e = np.exp(s - m)
+    p = e / np.sum(e, axis=1, keepdims=True)
+    o = p @ _f64(v_i)
+    return (o, p) if return_probs else o
+
+
+def output_projection(W, o):
+    """u_t = W_O [o_{t,1}; ...; o_{t,n_h}]; o is [T][n_h][d_v]."""
+    o = _f64(o)
+    return o.reshape(o.shape[0], -1) @ _f64(W["w_o"]).T
+
+
+# ---------------------------------------------------------------------------
+# One sequence end to end
+# ---------------------------------------------------------------------------
+
+def _heads(dims, heads):
+    return range(dims.n_heads) if heads is None else heads
+
+
+def prefill(dims, W, h, rows=None, heads=None, return_probs=False):
+    """Causal MLA over one whole sequence h [L][d_model] (positions 0..L-1).
+
+    rows: query positions to evaluate (default all); heads: heads to evaluate
+    (default all; u is only formed when all heads are).  Returns a dict with
+    u [R][d_model] (or None), o [R][n_h][d_v] (zeros for skipped heads),
+    and the cache rows c_kv [L][d_c], k_r [L][d_R]."""
+    h = _f64(h)
+    L = h.shape[0]
+    pos = np.arange(L)
+    c_kv, k_r = compress_kv(W, h, pos, dims)
+    qpos = pos if rows is None else np.asarray(rows)
+    q_c, q_r = project_queries(W, h[qpos], qpos, dims)
+    scale = softmax_scale(dims)
+    o = np.zeros((len(qpos), dims.n_heads, dims.d_v))
+    probs = {}
+    for i in _heads(dims, heads):
+        k_c_i, v_i = head_keys_values(W, c_kv, i, dims)
+        res = attend_head(q_c[:, i], q_r[:, i], qpos, k_c_i, k_r, v_i, scale, return_probs)
+        if return_probs:
+            o[:, i], probs[i] = res
+        else:
+            o[:, i] = res
+    u = output_projection(W, o) if heads is None else None
+    out = dict(u=u, o=o, c_kv=c_kv, k_r=k_r)
+    if return_probs:
+        out["probs"] = probs
+    return out
+
+
+def decode(dims, W, h, cache_rows, heads=None):
+    """n_q new tokens h [n_q][d_model] appended to one sequence whose first
+    cached rows ``cache_rows`` [L-n_q][d_c+d_R] (each [c_KV || k_R]) are given.
+    The new tokens take positions L-n_q..L-1 and query i sees keys
+    0..L-n_q+i.  Returns u [n_q][d_model] (None when heads is a subset),
+    o [n_q][n_h][d_v] and the new cache rows [n_q][d_c+d_R]."""
+    h = _f64(h)
+    cache_rows = _f64(cache_rows)
+    n_q = h.shape[0]
+    L = cache_rows.shape[0] + n_q
+    qpos = np.arange(L - n_q, L)
+    c_new, kr_new = compress_kv(W, h, qpos, dims)
+    c_kv = np.concatenate([cache_rows[:, :dims.d_c], c_new], axis=0)
+    k_r = np.concatenate([cache_rows[:, dims.d_c:], kr_new], axis=0)
+    q_c, q_r = project_queries(W, h, qpos, dims)
+    scale = softmax_scale(dims)
+    o = np.zeros((n_q, dims.n_heads, dims.d_v))
+    for i in _heads(dims, heads):
+        k_c_i, v_i = head_keys_values(W, c_kv, i, dims)
+        o[:, i] = attend_head(q_c[:, i], q_r[:, i], qpos, k_c_i, k_r, v_i, scale)
+    u = output_projection(W, o) if heads is None else None
+    return dict(u=u, o=o, row_new=np.concatenate([c_new, kr_new], axis=1))
+
+
+def decode_absorbed(dims, W, h, cache_rows):
+    """The same decode computed in latent space, used only to pin the
+    non-absorbed form above: by associativity q_C,i . (W_UK,i c_KV) equals
+    (W_UK,i^T q_C,i) . c_KV, and sum_j p_j W_UV,i c_KV,j equals
+    W_UV,i sum_j p_j c_KV,j."""
+    h = _f64(h)
+    cache_rows = _f64(cache_rows)
+    n_q = h.shape[0]
+    L = cache_rows.shape[0] + n_q
+    qpos = np.arange(L - n_q, L)
+    c_new, kr_new = compress_kv(W, h, qpos, dims)
+    rows = np.concatenate([cache_rows, np.concatenate([c_new, kr_new], axis=1)], axis=0)
+    q_c, q_r = project_queries(W, h, qpos, dims)
+    w_uk = _f64(W["w_uk"]).reshape(dims.n_heads, dims.d_nope, dims.d_c)
+    w_uv = _f64(W["w_uv"]).reshape(dims.n_heads, dims.d_v, dims.d_c)
+    scale = softmax_scale(dims)
+    o = np.zeros((n_q, dims.n_heads, dims.d_v))
+    for t in range(n_q):
+        for i in range(dims.n_heads):
+            q_lat = w_uk[i].T @ q_c[t, i]                  # [d_c]
+            q_full = np.concatenate([q_lat, q_r[t, i]])    # [d_c + d_R]
+            n_vis = qpos[t] + 1
+            s = rows[:n_vis] @ q_full * scale
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            o_lat = p @ rows[:n_vis, :dims.d_c]
+            o[t, i] = w_uv[i] @ o_lat
+    return dict(u=output_projection(W, o), o=o)
+
+
+# ---------------------------------------------------------------------------
+# Cache size (section 2.1, "advantages of MLA": only c_KV and k_R are cached)
+# ---------------------------------------------------------------------------
+
+def cache_elements_per_token(dims):
+    """Elements cached per token and layer by MLA: c_KV plus the shared k_R."""
+    return dims.d_c + dims.d_rope
+
+
+def mha_elements_per_token(dims):
+    """Elements a standard multi-head attention caches: a key and a value per head."""
+    return 2 * dims.n_heads * dims.d_nope

@@ -1,0 +1,324 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each pin ties the oracle to something other than itself: a closed form, an
+identity, a library routine (PyTorch's scaled_dot_product_attention), the
+rotation properties of RoPE, the dimensions the pages print, or a scalar brute
+force.  ``test_oracle_mutations.py`` plants plausible mistakes in the oracle and
+checks that these pins catch each one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from mla_inputs import TINY, DSV3, Dims, draw_weights, make_workload
+from oracle import mla_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+SMALL = Dims(d_model=48, n_heads=3, d_nope=8, d_rope=6, d_v=5, d_c=12, d_cq=10)
+
+
+def _weights(dims, seed=0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    f32, _ = draw_weights(rng, dims, bf16=False)
+    return {k: v.astype(np.float64) for k, v in f32.items()}
+
+
+def _h(T, dims, seed=1):
+    return np.random.Generator(np.random.PCG64(seed)).standard_normal((T, dims.d_model))
+
+
+# ---------------------------------------------------------------------------
+# Pin functions (plain, so the mutation test can re-run them)
+# ---------------------------------------------------------------------------
+
+def pin_absorbed_equals_plain(dims=TINY, L=20, n_q=3, seed=3):
+    """P1: weight absorption (decode in latent space) equals the literal form."""
+    W = _weights(dims, seed)
+    rng = np.random.Generator(np.random.PCG64(seed + 1))
+    cache = rng.standard_normal((L - n_q, dims.d_row))
+    h = rng.standard_normal((n_q, dims.d_model))
+    a = O.decode(dims, W, h, cache)
+    b = O.decode_absorbed(dims, W, h, cache)
+    err = np.max(np.abs(a["u"] - b["u"])) / np.max(np.abs(b["u"]))
+    assert err <= 1e-12, err
+    erro = np.max(np.abs(a["o"] - b["o"])) / np.max(np.abs(b["o"]))
+    assert erro <= 1e-12, erro
+
+
+def pin_softmax_rows(dims=TINY, L=17):
+    """P2: every probability row sums to one and masked entries are zero."""
+    W = _weights(dims, 5)
+    r = O.prefill(dims, W, _h(L, dims, 6), return_probs=True)
+    for i, p in r["probs"].items():
+        assert np.allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+        assert np.all(p[np.triu_indices(L, k=1)] == 0.0)
+        assert np.all(p >= 0)
+
+
+def pin_causal(dims=TINY, L=16, t=9):
+    """P3: changing tokens after t leaves outputs up to t bitwise unchanged."""
+    W = _weights(dims, 7)
+    h = _h(L, dims, 8)
+    h2 = h.copy()
+    h2[t + 1:] += np.random.Generator(np.random.PCG64(9)).standard_normal(h2[t + 1:].shape)
+    a = O.prefill(dims, W, h)["u"]
+    b = O.prefill(dims, W, h2)["u"]
+    assert np.array_equal(a[:t + 1], b[:t + 1])
+    assert not np.allclose(a[t + 1:], b[t + 1:])
+
+
+def pin_single_key(dims=TINY):
+    """P5: at position 0 the only visible key has probability one, so
+    u_0 = W_O [W_UV,i c_KV,0]_i."""
+    W = _weights(dims, 11)
+    h = _h(5, dims, 12)
+    r = O.prefill(dims, W, h)
+    c0 = W["w_dkv"] @ h[0]
+    expect = W["w_o"] @ (W["w_uv"] @ c0)
+    assert np.allclose(r["u"][0], expect, rtol=1e-12, atol=1e-12)
+
+
+def pin_zero_query(dims=TINY, L=11):
+    """P6: with W_UQ = W_QR = 0 every score is zero, so each output is the mean
+    of the values visible to it."""
+    W = _weights(dims, 13)
+    W["w_uq"][:] = 0
+    W["w_qr"][:] = 0
+    h = _h(L, dims, 14)
+    r = O.prefill(dims, W, h)
+    c = h @ W["w_dkv"].T
+    v = (c @ W["w_uv"].T).reshape(L, dims.n_heads, dims.d_v)
+    mean = np.cumsum(v, axis=0) / np.arange(1, L + 1)[:, None, None]
+    assert np.allclose(r["o"], mean, rtol=1e-12, atol=1e-12)
+
+
+def pin_head_isolation(dims=TINY, L=9):
+    """Head slicing: with W_UQ = 0 and W_QR zero outside head k's rows, every
+    head but k attends uniformly, and head k does not."""
+    for k in range(dims.n_heads):
+        W = _weights(dims, 15 + k)
+        W["w_uq"][:] = 0
+        keep = W["w_qr"][k * dims.d_rope:(k + 1) * dims.d_rope].copy() * 8.0
+        W["w_qr"][:] = 0
+        W["w_qr"][k * dims.d_rope:(k + 1) * dims.d_rope] = keep
+        r = O.prefill(dims, W, _h(L, dims, 30 + k), return_probs=True)
+        for i, p in r["probs"].items():
+            uniform = np.tril(np.ones((L, L))) / np.arange(1, L + 1)[:, None]
+            if i == k:
+                assert not np.allclose(p, uniform, atol=1e-6)
+            else:
+                assert np.allclose(p, uniform, rtol=0, atol=1e-14)
+    # the same for the content query through W_UQ
+    for k in range(dims.n_heads):
+        W = _weights(dims, 40 + k)
+        W["w_qr"][:] = 0
+        keep = W["w_uq"][k * dims.d_nope:(k + 1) * dims.d_nope].copy() * 8.0
+        W["w_uq"][:] = 0
+        W["w_uq"][k * dims.d_nope:(k + 1) * dims.d_nope] = keep
+        r = O.prefill(dims, W, _h(L, dims, 50 + k), return_probs=True)
+        for i, p in r["probs"].items():
+            uniform = np.tril(np.ones((L, L))) / np.arange(1, L + 1)[:, None]
+            assert (not np.allclose(p, uniform, atol=1e-6)) if i == k else np.allclose(p, uniform, atol=1e-14)
+
+
+def pin_mha_special_case(dims=None, L=13):
+    """P7: with d_c = d_model, W_DKV = I and W_KR = W_QR = 0, MLA is causal
+    multi-head attention with Q = W_UQ W_DQ h, K = W_UK h, V = W_UV h; compare
+    with PyTorch's scaled_dot_product_attention in float64, then W_O."""
+    d = dims or Dims(d_model=24, n_heads=3, d_nope=8, d_rope=4, d_v=6, d_c=24, d_cq=16)
+    W = _weights(d, 21)
+    W["w_dkv"] = np.eye(d.d_c)
+    W["w_kr"][:] = 0
+    W["w_qr"][:] = 0
+    h = _h(L, d, 22)
+    got = O.prefill(d, W, h)["u"]
+    th = torch.from_numpy(h)
+    Q = th @ torch.from_numpy(W["w_dq"]).T @ torch.from_numpy(W["w_uq"]).T
+    K = th @ torch.from_numpy(W["w_uk"]).T
+    V = th @ torch.from_numpy(W["w_uv"]).T
+    q = Q.reshape(L, d.n_heads, d.d_nope).transpose(0, 1).unsqueeze(0)
+    k = K.reshape(L, d.n_heads, d.d_nope).transpose(0, 1).unsqueeze(0)
+    v = V.reshape(L, d.n_heads, d.d_v).transpose(0, 1).unsqueeze(0)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, is_causal=True, scale=1.0 / math.sqrt(d.d_nope + d.d_rope))
+    ref = o.squeeze(0).transpose(0, 1).reshape(L, -1) @ torch.from_numpy(W["w_o"]).T
+    assert np.allclose(got, ref.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def pin_rope_rotation():
+    """P8: explicit rotation at d_R = 2 (angle = position), the frequency at
+    d_R = 4, identity at position 0, norm preservation, and the relative
+    property RoPE(x,m).RoPE(y,n) = f(m-n)."""
+    for p in (0, 1, 3, 17):
+        assert np.allclose(O.rope(np.array([1.0, 0.0]), p, 10000.0), [math.cos(p), math.sin(p)], atol=1e-15)
+        assert np.allclose(O.rope(np.array([0.0, 1.0]), p, 10000.0), [-math.sin(p), math.cos(p)], atol=1e-15)
+    th1 = 10000.0 ** (-0.5)
+    got = O.rope(np.array([0.0, 0.0, 1.0, 0.0]), 5, 10000.0)
+    assert np.allclose(got, [0.0, 0.0, math.cos(5 * th1), math.sin(5 * th1)], atol=1e-15)
+    rng = np.random.Generator(np.random.PCG64(4))
+    x = rng.standard_normal(16)
+    y = rng.standard_normal(16)
+    assert np.array_equal(O.rope(x, 0, 10000.0), x)
+    assert np.isclose(np.linalg.norm(O.rope(x, 123, 10000.0)), np.linalg.norm(x), rtol=1e-14)
+    d1 = O.rope(x, 40, 10000.0) @ O.rope(y, 30, 10000.0)
+    d2 = O.rope(x, 1010, 10000.0) @ O.rope(y, 1000, 10000.0)
+    assert np.isclose(d1, d2, rtol=1e-10)
+    assert not np.isclose(d1, O.rope(x, 41, 10000.0) @ O.rope(y, 30, 10000.0), rtol=1e-6)
+
+
+def pin_rope_in_scores():
+    """RoPE acts on both the query (at its position t) and the key (at its
+    position j): with no content score (W_UQ = 0), d_R = 2 and the same token
+    at positions 0 and 1, the scores at t = 1 are a.R(-1)b and a.b with
+    a = W_QR,i c_Q, b = W_KR h and R the textbook 2x2 rotation, so the
+    probability of key 0 has a closed form."""
+    d = Dims(d_model=12, n_heads=2, d_nope=4, d_rope=2, d_v=3, d_c=5, d_cq=6)
+    W = _weights(d, 27)
+    W["w_uq"][:] = 0
+    x = _h(1, d, 28)[0]
+    r = O.prefill(d, W, np.stack([x, x]), return_probs=True)
+    scale = 1.0 / math.sqrt(d.d_nope + d.d_rope)
+    b = W["w_kr"] @ x
+    rot = lambda ang: np.array([[math.cos(ang), -math.sin(ang)], [math.sin(ang), math.cos(ang)]])
+    for i in range(d.n_heads):
+        a = W["w_qr"][2 * i:2 * i + 2] @ (W["w_dq"] @ x)
+        s0 = a @ rot(-1.0) @ b * scale
+        s1 = a @ b * scale
+        p0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        assert abs(r["probs"][i][1, 0] - p0) <= 1e-14, (r["probs"][i][1, 0], p0)
+
+
+def pin_prefill_decode_agree(dims=TINY, L=24, steps=5):
+    """P9: a prefill of L followed by decode steps equals one longer prefill."""
+    W = _weights(dims, 23)
+    h = _h(L + steps, dims, 24)
+    full = O.prefill(dims, W, h)
+    r = O.prefill(dims, W, h[:L])
+    rows = np.concatenate([r["c_kv"], r["k_r"]], axis=1)
+    for s in range(steps):
+        d = O.decode(dims, W, h[L + s:L + s + 1], rows)
+        assert np.allclose(d["u"][0], full["u"][L + s], rtol=1e-12, atol=1e-12)
+        rows = np.concatenate([rows, d["row_new"]], axis=0)
+    # two query tokens at once (causal between themselves)
+    d2 = O.decode(dims, W, h[L:L + 2], np.concatenate([r["c_kv"], r["k_r"]], axis=1))
+    assert np.allclose(d2["u"], full["u"][L:L + 2], rtol=1e-12, atol=1e-12)
+
+
+def pin_brute_force(dims=SMALL, L=4):
+    """Scalar-loop MLA on a micro case, written independently of numpy's
+    vectorised reshapes."""
+    W = _weights(dims, 25)
+    h = _h(L, dims, 26)
+    got = O.prefill(dims, W, h)["u"]
+
+    def mv(M, x):
+        return [sum(M[r][c] * x[c] for c in range(len(x))) for r in range(len(M))]
+
+    def rot(x, p):
+        out = list(x)
+        for k in range(len(x) // 2):
+            a = p * dims.rope_base ** (-2.0 * k / len(x))
+            out[2 * k] = x[2 * k] * math.cos(a) - x[2 * k + 1] * math.sin(a)
+            out[2 * k + 1] = x[2 * k] * math.sin(a) + x[2 * k + 1] * math.cos(a)
+        return out
+
+    Wl = {k: v.tolist() for k, v in W.items()}
+    hs = h.tolist()
+    ckv = [mv(Wl["w_dkv"], hs[t]) for t in range(L)]
+    kr = [rot(mv(Wl["w_kr"], hs[t]), t) for t in range(L)]
+    for t in range(L):
+        cq = mv(Wl["w_dq"], hs[t])
+        qc_all = mv(Wl["w_uq"], cq)
+        qr_all = mv(Wl["w_qr"], cq)
+        ocat = []
+        for i in range(dims.n_heads):
+            qc = qc_all[i * dims.d_nope:(i + 1) * dims.d_nope]
+            qr = rot(qr_all[i * dims.d_rope:(i + 1) * dims.d_rope], t)
+            scores, vals = [], []
+            for j in range(t + 1):
+                kc = mv(Wl["w_uk"][i * dims.d_nope:(i + 1) * dims.d_nope], ckv[j])
+                v = mv(Wl["w_uv"][i * dims.d_v:(i + 1) * dims.d_v], ckv[j])
+                s = sum(a * b for a, b in zip(qc + qr, kc + kr[j])) / math.sqrt(dims.d_nope + dims.d_rope)
+                scores.append(s)
+                vals.append(v)
+            mx = max(scores)
+            ex = [math.exp(s - mx) for s in scores]
+            z = sum(ex)
+            ocat += [sum(ex[j] / z * vals[j][c] for j in range(t + 1)) for c in range(dims.d_v)]
+        u = mv(Wl["w_o"], ocat)
+        assert np.allclose(got[t], u, rtol=1e-11, atol=1e-12)
+
+
+ALL_PINS = [pin_absorbed_equals_plain, pin_softmax_rows, pin_causal, pin_single_key,
+            pin_zero_query, pin_head_isolation, pin_mha_special_case, pin_rope_rotation, pin_rope_in_scores,
+            pin_prefill_decode_agree, pin_brute_force]
+
+
+# ---------------------------------------------------------------------------
+# Tests
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_absorbed_random_shapes(seed):
+    rng = np.random.Generator(np.random.PCG64(100 + seed))
+    dr = 2 * int(rng.integers(1, 5))
+    d = Dims(d_model=int(rng.integers(8, 40)), n_heads=int(rng.integers(1, 5)),
+             d_nope=int(rng.integers(2, 12)), d_rope=dr, d_v=int(rng.integers(2, 12)),
+             d_c=int(rng.integers(4, 24)), d_cq=int(rng.integers(4, 24)))
+    pin_absorbed_equals_plain(d, L=int(rng.integers(3, 30)), n_q=int(rng.integers(1, 3)), seed=seed)
+
+
+def test_cache_size_closed_form():
+    """P4: the cache holds only c_KV and k_R: (d_c + d_R) elements per token,
+    against a key and a value per head for MHA.  Dimensions from the pages."""
+    g = json.load(open(os.path.join(GOLDEN, "dsv3_mla_dims.json")))
+    d = Dims(d_model=g["d_model"], n_heads=g["n_heads"], d_nope=g["d_head"], d_rope=g["d_rope"],
+             d_v=g["d_head"], d_c=g["d_c"], d_cq=g["d_cq"])
+    assert d == DSV3
+    e = g["expected"]
+    assert O.cache_elements_per_token(d) == e["mla_cache_elements_per_token"]
+    assert O.mha_elements_per_token(d) == e["mha_cache_elements_per_token"]
+    assert 2 * O.cache_elements_per_token(d) == e["mla_cache_bytes_per_token_bf16"]
+    assert 2 * O.cache_elements_per_token(d) * g["n_layers"] == e["mla_cache_bytes_per_token_61_layers_bf16"]
+    assert O.cache_elements_per_token(TINY) == 80 and O.mha_elements_per_token(TINY) == 256
+    # and the oracle's decode really only needs those rows: the new row it
+    # returns has exactly that width
+    W = _weights(TINY, 1)
+    r = O.decode(TINY, W, _h(1, TINY), np.zeros((3, TINY.d_row)))
+    assert r["row_new"].shape == (1, O.cache_elements_per_token(TINY))
+
+
+def test_tiny_workload_end_to_end():
+    """The tiny workload's prefill + 8 decode steps agree with one 72-token
+    prefill on the workload's own seeded inputs."""
+    wl = make_workload(1)
+    d = wl.dims
+    W = {k: v.astype(np.float64) for k, v in wl.weights_f32.items()}
+    h = wl.h_f32[0].astype(np.float64)
+    full = O.prefill(d, W, h)
+    r = O.prefill(d, W, h[:wl.seq_len])
+    rows = np.concatenate([r["c_kv"], r["k_r"]], axis=1)
+    assert np.allclose(r["u"], full["u"][:wl.seq_len], rtol=1e-12, atol=1e-12)
+    for s in range(wl.n_steps):
+        t = wl.seq_len + s
+        dd = O.decode(d, W, h[t:t + 1], rows)
+        rows = np.concatenate([rows, dd["row_new"]], axis=0)
+        assert np.allclose(dd["u"][0], full["u"][t], rtol=1e-12, atol=1e-12)
+
+
+def test_head_subset_matches_full():
+    W = _weights(TINY, 2)
+    h = _h(12, TINY, 3)
+    full = O.prefill(TINY, W, h)
+    part = O.prefill(TINY, W, h, rows=[0, 5, 11], heads=[1, 3])
+    assert part["u"] is None
+    assert np.allclose(part["o"][:, [1, 3]], full["o"][[0, 5, 11]][:, [1, 3]], rtol=1e-13, atol=1e-14)

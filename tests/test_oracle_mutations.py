@@ -1,0 +1,136 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+in test_oracle.py catch every one of them."""
+import numpy as np
+import pytest
+
+from oracle import mla_oracle as O
+from tests import test_oracle as P
+
+_rope = O.rope
+_attend = O.attend_head
+_hkv = O.head_keys_values
+_pq = O.project_queries
+_out = O.output_projection
+_ckv = O.compress_kv
+
+
+def _rope_sign(x, pos, base):
+    return _rope(x, -np.asarray(pos), base)
+
+
+def _rope_freq(x, pos, base):
+    # frequency base^(-k/d_R) instead of base^(-2k/d_R)
+    d = np.asarray(x).shape[-1]
+    return _rope(x, pos, base ** 0.5) if d > 2 else _rope(x, pos, base)
+
+
+def _rope_halfsplit_pairs_wrong(x, pos, base):
+    # rotate (x[k], x[k+1]) over overlapping pairs: a wrong index
+    x = np.asarray(x, dtype=np.float64)
+    y = np.roll(x, 1, axis=-1)
+    return np.roll(_rope(y, pos, base), -1, axis=-1)
+
+
+def _attend_drop_rope(q_c_i, q_r_i, qpos, k_c_i, k_r, v_i, scale, return_probs=False):
+    return _attend(q_c_i, np.zeros_like(q_r_i), qpos, k_c_i, k_r, v_i, scale, return_probs)
+
+
+def _attend_strict_mask(q_c_i, q_r_i, qpos, k_c_i, k_r, v_i, scale, return_probs=False):
+    return _attend(q_c_i, q_r_i, np.asarray(qpos) - 1, k_c_i, k_r, v_i, scale, return_probs)
+
+
+def _attend_no_mask(q_c_i, q_r_i, qpos, k_c_i, k_r, v_i, scale, return_probs=False):
+    L = np.asarray(k_r).shape[0]
+    return _attend(q_c_i, q_r_i, np.full_like(np.asarray(qpos), L - 1), k_c_i, k_r, v_i, scale, return_probs)
+
+
+def _attend_wrong_axis(q_c_i, q_r_i, qpos, k_c_i, k_r, v_i, scale, return_probs=False):
+    s = (q_c_i @ k_c_i.T + q_r_i @ k_r.T) * scale
+    L = s.shape[1]
+    vis = np.arange(L)[None, :] <= np.asarray(qpos)[:, None]
+    e = np.where(vis, np.exp(s - s.max()), 0.0)
+    p = e / e.sum(axis=0, keepdims=True).clip(1e-300)
+    o = p @ v_i
+    return (o, p) if return_probs else o
+
+
+def _attend_transposed_key(q_c_i, q_r_i, qpos, k_c_i, k_r, v_i, scale, return_probs=False):
+    # scores against k_R without the content key (k_C dropped)
+    return _attend(np.zeros_like(q_c_i), q_r_i, qpos, k_c_i, k_r, v_i, scale, return_probs)
+
+
+def _hkv_values_from_uk(W, c_kv, i, dims):
+    k, v = _hkv(W, c_kv, i, dims)
+    if dims.d_v == dims.d_nope:
+        return k, k
+    w = np.asarray(W["w_uk"], dtype=np.float64)[i * dims.d_nope:(i + 1) * dims.d_nope]
+    kk = np.asarray(c_kv) @ w.T
+    return k, np.resize(kk, v.shape)
+
+
+def _hkv_strided_heads(W, c_kv, i, dims):
+    w_uk = np.asarray(W["w_uk"], dtype=np.float64)[i::dims.n_heads][:dims.d_nope]
+    w_uv = np.asarray(W["w_uv"], dtype=np.float64)[i::dims.n_heads][:dims.d_v]
+    c = np.asarray(c_kv, dtype=np.float64)
+    return c @ w_uk.T, c @ w_uv.T
+
+
+def _pq_qr_head_split(W, h, pos, dims):
+    q_c, q_r = _pq(W, h, pos, dims)
+    T = q_r.shape[0]
+    c_q = np.asarray(h, dtype=np.float64) @ np.asarray(W["w_dq"], dtype=np.float64).T
+    raw = (c_q @ np.asarray(W["w_qr"], dtype=np.float64).T).reshape(T, dims.d_rope, dims.n_heads).transpose(0, 2, 1)
+    return q_c, O.rope(raw, np.asarray(pos)[:, None], dims.rope_base)
+
+
+def _pq_no_rope(W, h, pos, dims):
+    q_c, _ = _pq(W, h, pos, dims)
+    T = q_c.shape[0]
+    c_q = np.asarray(h, dtype=np.float64) @ np.asarray(W["w_dq"], dtype=np.float64).T
+    return q_c, (c_q @ np.asarray(W["w_qr"], dtype=np.float64).T).reshape(T, dims.n_heads, dims.d_rope)
+
+
+def _out_head_order(W, o):
+    o = np.asarray(o, dtype=np.float64)
+    return o.transpose(0, 2, 1).reshape(o.shape[0], -1) @ np.asarray(W["w_o"], dtype=np.float64).T
+
+
+def _ckv_kr_unroped(W, h, pos, dims):
+    c, _ = _ckv(W, h, pos, dims)
+    return c, np.asarray(h, dtype=np.float64) @ np.asarray(W["w_kr"], dtype=np.float64).T
+
+
+MUTATIONS = {
+    "rope_sign": ("rope", _rope_sign),
+    "rope_frequency": ("rope", _rope_freq),
+    "rope_pairs": ("rope", _rope_halfsplit_pairs_wrong),
+    "scale_dh_only": ("softmax_scale", lambda d: 1.0 / np.sqrt(d.d_nope)),
+    "scale_missing": ("softmax_scale", lambda d: 1.0),
+    "drop_rope_score": ("attend_head", _attend_drop_rope),
+    "drop_content_score": ("attend_head", _attend_transposed_key),
+    "mask_strict": ("attend_head", _attend_strict_mask),
+    "mask_missing": ("attend_head", _attend_no_mask),
+    "softmax_axis": ("attend_head", _attend_wrong_axis),
+    "values_from_uk": ("head_keys_values", _hkv_values_from_uk),
+    "heads_strided": ("head_keys_values", _hkv_strided_heads),
+    "qr_head_split": ("project_queries", _pq_qr_head_split),
+    "q_no_rope": ("project_queries", _pq_no_rope),
+    "output_head_order": ("output_projection", _out_head_order),
+    "k_no_rope": ("compress_kv", _ckv_kr_unroped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for pin in P.ALL_PINS:
+        if pin is P.pin_brute_force:
+            continue  # the scalar brute force is a restatement; real pins must catch it
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except Exception as e:  # AssertionError, or a shape error the mistake causes
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"mutation {name} passed every pin"
