@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""libmla benchmark: one MI355X, synthetic DeepSeek-V3-shaped MLA layer.
+
+A step is one mla_decode call on the DeepSeek-V3 decode workload (batch 32,
+one new token per sequence, cache length 4096 after the append, bf16): query
+and KV down-projections with RoPE and the cache append, the query
+up-projection, W_UK absorption, split-KV latent attention, the split combine,
+W_UV and W_O.  ``value`` is decode tokens/s (batch / step time) with every
+input resident in HBM.  Input sets (weights, cache, h) are rotated over
+several copies so consecutive steps do not find their operands in the 256 MB
+Infinity Cache.
+
+Also reported: per-kernel times from HIP events recorded by the library on
+the launch stream, the roofline of the dominant kernel, a causal prefill of
+4096 tokens (TFLOPS against the bf16 MFMA peak), a sampled parity check, and
+the CPU oracle's throughput on a bounded sample (cpu_baseline).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_kernel_bytes(d, B, n_q, sum_len, e=2):
+    """Algorithmic HBM bytes per launch of each decode kernel (weights and
+    cache read once, activations read/written once)."""
+    T = B * n_q
+    nh = d.n_heads
+    D = d.d_c + d.d_rope
+    return {
+        "q_kv_down": e * ((d.d_cq + D) * d.d_model + T * d.d_model + T * d.d_cq + T * D),
+        "q_up": e * (nh * (d.d_nope + d.d_rope) * d.d_cq + T * d.d_cq + T * nh * (d.d_nope + d.d_rope)),
+        "absorb": e * (nh * d.d_nope * d.d_c + T * nh * d.d_nope + T * nh * d.d_c),
+        "decode_attn": e * (sum_len * D + T * nh * D),
+        "decode_combine": e * T * nh * d.d_c,
+        "unabsorb": e * (nh * d.d_v * d.d_c + T * nh * d.d_c + T * nh * d.d_v),
+        "o_proj": e * (d.d_model * nh * d.d_v + T * nh * d.d_v + T * d.d_model),
+    }
+
+
+def decode_step_bytes(d, B, n_q, sum_len, e=2):
+    """Whole decode step: every weight once, every cached row once, h in, u out."""
+    nparams = (d.d_cq * d.d_model + d.n_heads * (d.d_nope + d.d_rope) * d.d_cq + (d.d_c + d.d_rope) * d.d_model
+               + d.n_heads * (d.d_nope + d.d_v) * d.d_c + d.d_model * d.n_heads * d.d_v)
+    return e * (nparams + sum_len * (d.d_c + d.d_rope) + 2 * B * n_q * d.d_model)
+
+
+def prefill_flops(d, B, L):
+    T = B * L
+    pairs = B * L * (L + 1) // 2
+    return (2 * T * d.d_model * (d.d_cq + d.d_c + d.d_rope)
+            + 2 * T * d.d_cq * d.n_heads * (d.d_nope + d.d_rope)
+            + 2 * T * d.d_c * d.n_heads * (d.d_nope + d.d_v)
+            + pairs * d.n_heads * 2 * (d.d_nope + d.d_rope + d.d_v)
+            + 2 * T * d.n_heads * d.d_v * d.d_model)
+
+
+def kernel_times(run, steps):
+    """Run `steps` calls with library kernel timing on; average ms per launch."""
+    import torch
+    from head_latent_attention_18_amd import libmla as L
+    torch.cuda.synchronize()
+    L.mla_timing_enable(True)
+    for i in range(steps):
+        run(i)
+    torch.cuda.synchronize()
+    t = L.mla_timing_read()
+    L.mla_timing_enable(False)
+    return {k: {"avg_ms": ms / max(n, 1), "launches_per_step": n / steps} for k, (ms, n) in t.items()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=3, help="rotated input copies (defeat the Infinity Cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the oracle's timed sample")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from head_latent_attention_18_amd import libmla as L
+    from head_latent_attention_18_amd.layer import MlaLayer, cache_from_rows, upload
+    from mla_inputs import make_workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ------------------------------------------------------------ decode
+    t0 = time.perf_counter()
+    wl = make_workload(2)
+    d = wl.dims
+    B, nq = wl.batch, wl.n_q
+    Lmax = int(wl.lens.max())
+    log(f"workload {wl.name}: inputs drawn in {time.perf_counter() - t0:.1f}s")
+    layer0 = MlaLayer.from_host(d, "bf16", wl.weights_f32, wl.weights_bits)
+    cache0 = cache_from_rows(wl.cache_bits, wl.lens, d.d_row, True)
+    h0 = upload(wl.h_f32, wl.h_bits, True)
+    lens = torch.from_numpy(wl.lens.astype(np.int32)).to(dev)
+    sets = [(layer0, cache0, h0)]
+    for _ in range(args.sets - 1):
+        lw = MlaLayer(d, "bf16", {k: v.clone() for k, v in layer0.weights.items()})
+        c = type(cache0)(cache0.pool.clone(), None, max_len=cache0.max_len)
+        c.desc = L.make_cache(c.pool, max_len=cache0.max_len)
+        sets.append((lw, c, h0.clone()))
+    outs = [torch.empty(B, nq, d.d_model, dtype=torch.bfloat16, device=dev) for _ in sets]
+
+    def step(i):
+        lw, c, h = sets[i % len(sets)]
+        lw.decode(h, lens, Lmax, c, u=outs[i % len(sets)])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    log(f"decode: {dt * 1e6:.1f} us/step")
+    ktimes = kernel_times(step, args.steps)
+    sum_len = int(wl.lens.sum())
+    kbytes = decode_kernel_bytes(d, B, nq, sum_len)
+    kernels = {}
+    for name, v in ktimes.items():
+        ent = {"avg_us": round(v["avg_ms"] * 1e3, 2), "launches_per_step": v["launches_per_step"]}
+        if name in kbytes:
+            gbs = kbytes[name] / (v["avg_ms"] * 1e-3) / 1e9
+            ent["alg_bytes"] = kbytes[name]
+            ent["alg_GBps"] = round(gbs, 1)
+            ent["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
+        kernels[name] = ent
+    dom = max((k for k in kernels if k in kbytes), key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches_per_step"])
+    dom_gbs = kernels[dom]["alg_GBps"]
+    step_bytes = decode_step_bytes(d, B, nq, sum_len)
+
+    # sampled parity of the timed output against the oracle (sequences 0 and B-1)
+    from oracle import mla_oracle as O
+    W = {k: v.astype(np.float64) for k, v in wl.weights_f32.items()}
+    u_gpu = outs[(args.steps - 1) % len(sets)].float().cpu().numpy()
+    parity = {}
+    cpu = None
+    t_or = 0.0
+    n_or = 0
+    for b in ([0, B - 1] + list(range(1, max(0, args.cpu_seqs - 2) + 1))):
+        t1 = time.perf_counter()
+        ref = O.decode(d, W, wl.h_f32[b].astype(np.float64), wl.cache_f32[b].astype(np.float64))["u"]
+        t_or += time.perf_counter() - t1
+        n_or += nq
+        diff = u_gpu[b] - ref
+        parity[f"seq{b}"] = {"max_abs": float(np.max(np.abs(diff))),
+                             "rel_frob": float(np.linalg.norm(diff) / np.linalg.norm(ref))}
+        if args.no_cpu_baseline and len(parity) >= 2:
+            break
+    if not args.no_cpu_baseline:
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            blas_threads = None
+        cores = len(os.sched_getaffinity(0))
+        cpu = {"value": round(n_or / t_or, 3), "unit": "tokens/s", "cores": int(blas_threads or cores),
+               "kind": "oracle",
+               "sample": f"fp64 numpy oracle decode of {n_or} of the {B} sequences (one token each, cache "
+                         f"length {Lmax}), {t_or:.1f}s; host has {cores} cores"}
+
+    del sets, outs
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ prefill
+    prefill = None
+    if not args.no_prefill:
+        wp = make_workload(3)
+        lp = MlaLayer.from_host(wp.dims, "bf16", wp.weights_f32, wp.weights_bits)
+        hp = upload(wp.h_f32, wp.h_bits, True)
+        cp = lp.new_cache(wp.batch, wp.seq_len)
+        for _ in range(3):
+            lp.prefill(hp, cp)
+        torch.cuda.synchronize()
+        pk = max(3, args.steps // 5)
+        t0 = time.perf_counter()
+        for _ in range(pk):
+            lp.prefill(hp, cp)
+        torch.cuda.synchronize()
+        pdt = (time.perf_counter() - t0) / pk
+        pk_times = kernel_times(lambda i: lp.prefill(hp, cp), pk)
+        fl = prefill_flops(wp.dims, wp.batch, wp.seq_len)
+        prefill = {"workload": wp.name, "ms": round(pdt * 1e3, 4), "TFLOPS": round(fl / pdt / 1e12, 1),
+                   "mfma_frac": round(fl / pdt / 1e12 / BF16_PEAK_TFLOPS, 4), "alg_flops": fl,
+                   "kernels": {k: {"avg_us": round(v["avg_ms"] * 1e3, 2), "launches_per_step": v["launches_per_step"]}
+                               for k, v in pk_times.items()}}
+        log(f"prefill: {pdt * 1e3:.3f} ms, {fl / pdt / 1e12:.1f} TFLOPS")
+
+    out = {
+        "metric": "MLA decode tokens/s (DeepSeek-V3 layer, batch 32, cache 4096)",
+        "value": round(B * nq / dt, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "n_q": nq, "cache_len": Lmax, "d_model": d.d_model,
+                   "n_heads": d.n_heads, "d_c": d.d_c, "d_rope": d.d_rope, "paged": False},
+        "step_hbm": {"alg_bytes": step_bytes, "GBps": round(step_bytes / dt / 1e9, 1),
+                     "frac": round(step_bytes / dt / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "kernels": kernels,
+        "parity": parity,
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

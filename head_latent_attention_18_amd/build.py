@@ -1,0 +1,73 @@
+"""Build libmla.so (gfx950) in place with hipcc.
+
+    python -m head_latent_attention_18_amd.build [--verbose]
+
+Every .hip file under csrc/ is compiled to an object in parallel and the
+objects are linked into head_latent_attention_18_amd/libmla.so.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import glob
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+ROOT = os.path.dirname(PKG)
+LIB = os.path.join(PKG, "lib", "libmla.so")
+ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
+
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # packed fp32 VALU forms stay off (hipcc's host pass warns it does not know the feature)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libmla)")
+
+
+def _compile(src: str, obj: str, extra) -> str:
+    cmd = [hipcc(), *FLAGS, *extra, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {os.path.basename(src)}:\n{r.stderr}")
+    return "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    tmp = tempfile.mkdtemp(prefix="libmla_")
+    try:
+        objs = [os.path.join(tmp, os.path.basename(s) + ".o") for s in srcs]
+        with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+            logs = list(ex.map(lambda so: _compile(so[0], so[1], list(extra)), zip(srcs, objs)))
+        if verbose:
+            for s, l in zip(srcs, logs):
+                if l.strip():
+                    print(f"== {os.path.basename(s)}\n{l}")
+        os.makedirs(os.path.dirname(LIB), exist_ok=True)
+        out = LIB + ".tmp"
+        r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stderr}")
+        os.replace(out, LIB)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    v = "--verbose" in sys.argv
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if "--resources" in sys.argv else []
+    print(build(verbose=v or bool(extra), extra=extra))

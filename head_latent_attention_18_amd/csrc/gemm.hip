@@ -1,0 +1,265 @@
+// Projection GEMMs of the MLA layer: Y[M][N] = X[M][K] * W^T, with W stored
+// [N][K] (the pages' W*h orientation, every projection of section 2.1 of the
+// DeepSeek-V3 paper-reading notes) or, for the absorbed query, [K][N].
+//
+// One templated kernel serves the large-token tiles (prefill) and the
+// skinny tiles (decode, weight streaming with split-K).  X and W tiles are
+// staged through LDS in two buffers; the MFMA operands are read as 16-byte
+// runs (see mla_internal.h).  With SWAP the weight tile is the MFMA A operand,
+// so each lane ends with four consecutive output features of one token: the
+// epilogue can apply RoPE to (2k, 2k+1) pairs and write cache rows without
+// any cross-lane exchange.  Without SWAP the lane holds four consecutive
+// tokens of one feature, which is what a transposed store (V^T) needs.
+#include "mla_internal.h"
+
+namespace mla {
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool SWAP, bool WKN>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int KPL = Mma<T>::KPL;
+  constexpr int VE = Vec<T>::N;
+  constexpr int LDK = BK + VE;          // LDS row stride: 16 bytes of padding
+  constexpr int RUN = BK / 4;
+  constexpr int STEPS = RUN / KPL;
+  static_assert(RUN % KPL == 0, "k run must hold whole MFMA operands");
+  static_assert(RUN % VE == 0 || !WKN, "transposed W tile needs whole chunks");
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 16x16 block");
+  constexpr int XCH = BM * BK / VE;
+  constexpr int WCH = BN * BK / VE;
+  constexpr int XPT = (XCH + NT - 1) / NT;
+  constexpr int WPT = (WCH + NT - 1) / NT;
+  typedef typename Mma<T>::frag frag;
+
+  __shared__ __attribute__((aligned(16))) T xs[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) T ws[2][BN * LDK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+  const int lrow = lane & 15, lgrp = lane >> 4;
+
+  // XCD-aware order: the dispatcher deals blocks round-robin over the 8 XCDs,
+  // so remap to give each XCD a contiguous range of tiles (shared W rows).
+  int bid = blockIdx.x;
+  const int nb = gridDim.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int tm = bid % a.tiles_m, tn = bid / a.tiles_m;
+  const int bz = blockIdx.y / a.splits, sp = blockIdx.y % a.splits;
+  const int M = a.M, N = a.N;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = sp * a.k_chunk;
+  const int nk = a.k_chunk / BK;
+
+  const T *X = (const T *)a.x + (long)bz * a.x_bs;
+
+  // per-thread source pointers (rows fixed across the k loop)
+  const T *xsrc[XPT];
+  int xdst[XPT];
+  bool xok[XPT];
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int c = tid + i * NT;
+    xok[i] = c < XCH;
+    const int r = c / (BK / VE), kc = c % (BK / VE);
+    const int gm = min(m0 + r, M - 1);
+    xsrc[i] = X + (long)gm * a.ldx + kbeg + kc * VE;
+    xdst[i] = r * LDK + kc * VE;
+  }
+  const T *wsrc[WPT];
+  int wdst[WPT];
+  bool wok[WPT];
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int c = tid + i * NT;
+    wok[i] = c < WCH;
+    if (!WKN) {
+      const int r = c / (BK / VE), kc = c % (BK / VE);
+      const int n = min(n0 + r, N - 1);
+      int s = 0, beg = 0;
+      while (s < a.nw - 1 && n >= a.w_end[s]) { beg = a.w_end[s]; ++s; }
+      wsrc[i] = (const T *)a.w[s] + (long)bz * a.w_bs + (long)(n - beg) * a.ldw + kbeg + kc * VE;
+      wdst[i] = r * LDK + kc * VE;
+    } else {
+      const int kr = c / (BN / VE), nc = c % (BN / VE);
+      const int n = min(n0 + nc * VE, N - VE);
+      wsrc[i] = (const T *)a.w[0] + (long)bz * a.w_bs + (long)(kbeg + kr) * a.ldw + n;
+      wdst[i] = (nc * VE) * LDK + kr;
+    }
+  }
+
+  u32x4 xr[XPT], wr[WPT];
+  auto gload = [&](int kt) {
+    const long koff = (long)kt * BK;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i)
+      if (xok[i]) xr[i] = *(const u32x4 *)(xsrc[i] + koff);
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      if (wok[i]) {
+        if (!WKN) wr[i] = *(const u32x4 *)(wsrc[i] + koff);
+        else wr[i] = *(const u32x4 *)(wsrc[i] + koff * a.ldw);
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i)
+      if (xok[i]) *(u32x4 *)&xs[buf][xdst[i]] = xr[i];
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      if (wok[i]) {
+        if (!WKN) {
+          *(u32x4 *)&ws[buf][wdst[i]] = wr[i];
+        } else {
+          const T *e = (const T *)&wr[i];
+#pragma unroll
+          for (int j = 0; j < VE; ++j) ws[buf][wdst[i] + j * LDK] = e[j];
+        }
+      }
+    }
+  };
+
+  f32x4 acc[SWAP ? FN : FM][SWAP ? FM : FN];
+#pragma unroll
+  for (int i = 0; i < (SWAP ? FN : FM); ++i)
+#pragma unroll
+    for (int j = 0; j < (SWAP ? FM : FN); ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      frag xa[FM], wb[FN];
+#pragma unroll
+      for (int f = 0; f < FM; ++f)
+        xa[f] = *(const frag *)&xs[buf][(wm * TM + f * 16 + lrow) * LDK + lgrp * RUN + s * KPL];
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+        wb[f] = *(const frag *)&ws[buf][(wn * TN + f * 16 + lrow) * LDK + lgrp * RUN + s * KPL];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if (SWAP) acc[j][i] = Mma<T>::mma(wb[j], xa[i], acc[j][i]);
+          else acc[i][j] = Mma<T>::mma(xa[i], wb[j], acc[i][j]);
+        }
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (SWAP) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * TM + i * 16 + lrow;
+        const int n = n0 + wn * TN + j * 16 + 4 * lgrp;
+        if (m < M && n < N) {
+          float v[4] = {acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]};
+          if (a.splits > 1) {
+            float *p = a.partial + (((long)bz * a.splits + sp) * M + m) * N + n;
+            *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
+          } else {
+            epi_store4<T>(a.epi, bz, m, n, v);
+          }
+        }
+      }
+  } else {
+    const Seg &g = a.epi.seg[0];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = n0 + wn * TN + j * 16 + lrow;
+        const int mb = m0 + wm * TM + i * 16 + 4 * lgrp;
+        if (n < N) {
+          T *dst = (T *)g.dst + (long)bz * g.batch_stride + (long)n * g.ld;
+          if (mb + 3 < M && (g.ld & 3) == 0) {
+            float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+            store4<T>(dst, mb, v, 0);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (mb + r < M) dst[mb + r] = from_f32<T>(acc[i][j][r]);
+          }
+        }
+      }
+  }
+}
+
+// Sum the split-K partials in split order (deterministic) and apply the epilogue.
+template <typename T>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a) {
+  const int n4 = a.N >> 2;
+  const long total = (long)a.batch * a.M * n4;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int bz = (int)(idx / ((long)a.M * n4));
+  const long rem = idx - (long)bz * a.M * n4;
+  const int m = (int)(rem / n4), n = (int)(rem % n4) * 4;
+  f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < a.splits; ++p)
+    s += *(const f32x4 *)(a.partial + (((long)bz * a.splits + p) * a.M + m) * a.N + n);
+  float v[4] = {s[0], s[1], s[2], s[3]};
+  epi_store4<T>(a.epi, bz, m, n, v);
+}
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool SWAP, bool WKN>
+static hipError_t launch_t(GemmArgs &a, hipStream_t st, const char *name) {
+  a.tiles_m = (a.M + BM - 1) / BM;
+  a.tiles_n = (a.N + BN - 1) / BN;
+  dim3 grid(a.tiles_m * a.tiles_n, a.batch * a.splits);
+  if (a.name) name = a.name;
+  timing_before(name, st);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, SWAP, WKN>), grid, dim3(64 * WM * WN), 0, st, a);
+  timing_after(name, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.splits > 1) {
+    const long total = (long)a.batch * a.M * (a.N / 4);
+    const char *rname = a.reduce_name ? a.reduce_name : "splitk_reduce";
+    timing_before(rname, st);
+    hipLaunchKernelGGL(splitk_reduce_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a);
+    timing_after(rname, st);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+// K granularity each tile needs (host checks K % gemm_bk == 0 per split).
+int gemm_bk(int dtype, int tile) {
+  if (dtype == 0) return 32;
+  return 64;
+}
+int gemm_bm(int dtype, int tile) {
+  if (dtype == 0) return 32;
+  return tile == TILE_BIG ? 128 : 32;
+}
+
+hipError_t launch_gemm(int dtype, int tile, int swap, int wkn, GemmArgs &a, hipStream_t st) {
+  if (dtype == 1) {
+    if (tile == TILE_BIG) {
+      if (swap && !wkn) return launch_t<bf16, 128, 128, 64, 2, 2, true, false>(a, st, "gemm_bf16_128x128");
+      if (!swap && !wkn) return launch_t<bf16, 128, 128, 64, 2, 2, false, false>(a, st, "gemm_bf16_128x128_t");
+      if (swap && wkn) return launch_t<bf16, 128, 128, 64, 2, 2, true, true>(a, st, "gemm_bf16_128x128_kn");
+    } else {
+      if (swap && !wkn) return launch_t<bf16, 32, 64, 64, 1, 4, true, false>(a, st, "gemm_bf16_32x64");
+      if (!swap && !wkn) return launch_t<bf16, 32, 64, 64, 1, 4, false, false>(a, st, "gemm_bf16_32x64_t");
+      if (swap && wkn) return launch_t<bf16, 32, 64, 64, 1, 4, true, true>(a, st, "gemm_bf16_32x64_kn");
+    }
+  } else {
+    if (swap && !wkn) return launch_t<float, 32, 32, 32, 2, 2, true, false>(a, st, "gemm_f32_32x32");
+    if (!swap && !wkn) return launch_t<float, 32, 32, 32, 2, 2, false, false>(a, st, "gemm_f32_32x32_t");
+    if (swap && wkn) return launch_t<float, 32, 32, 32, 2, 2, true, true>(a, st, "gemm_f32_32x32_kn");
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mla

@@ -1,0 +1,245 @@
+// Internal definitions shared by the libmla HIP sources (not part of the ABI).
+//
+// Matrix-core conventions used by every kernel (CDNA3/CDNA4 16x16 MFMA):
+//   A operand (16 x K): lane l holds row (l & 15), k-slots [(l>>4)*KPL, +KPL)
+//   B operand (K x 16): lane l holds col (l & 15), k-slots [(l>>4)*KPL, +KPL)
+//   C/D (16 x 16 fp32): lane l holds col (l & 15), rows 4*(l>>4) + [0, 4)
+// KPL = 8 for v_mfma_f32_16x16x32_bf16 and 1 for v_mfma_f32_16x16x4_f32.
+//
+// A contraction of length D is always fed as four contiguous runs: lane group
+// g = l>>4 owns k in [g*D/4, (g+1)*D/4) and instruction s uses the slots
+// [g*D/4 + s*KPL, +KPL).  A and B use the same assignment, so the sum is the
+// full dot product (in a different order), and each lane reads one contiguous
+// run per operand row: 16-byte LDS and global reads.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T> struct Mma;
+template <> struct Mma<bf16> {
+  static constexpr int KPL = 8;
+  typedef bf16x8 frag;
+  __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mma<float> {
+  static constexpr int KPL = 1;
+  typedef float frag;
+  __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// elements per 16-byte chunk
+template <typename T> struct Vec { static constexpr int N = 16 / sizeof(T); };
+
+__device__ inline float to_f32(float x) { return x; }
+__device__ inline float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ inline T from_f32(float x);
+template <> __device__ inline float from_f32<float>(float x) { return x; }
+template <> __device__ inline bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// ---------------------------------------------------------------------------
+// Row -> (sequence, position) maps used by the GEMM epilogues
+// ---------------------------------------------------------------------------
+enum RowMode { ROWS_DENSE = 0, ROWS_DECODE = 1, ROWS_EXPLICIT = 2 };
+struct RowMap {
+  int mode;
+  int per_seq;          // DENSE: tokens per sequence; DECODE: n_q
+  const int *lens;      // DECODE: [batch] lengths after append
+  const int *seq_idx;   // EXPLICIT
+  const int *pos;       // EXPLICIT
+};
+
+__device__ inline void row_seq_pos(const RowMap &r, int m, int &seq, int &pos) {
+  if (r.mode == ROWS_DENSE) {
+    seq = m / r.per_seq;
+    pos = m - seq * r.per_seq;
+  } else if (r.mode == ROWS_DECODE) {
+    seq = m / r.per_seq;
+    pos = r.lens[seq] - r.per_seq + (m - seq * r.per_seq);
+  } else {
+    seq = r.seq_idx[m];
+    pos = r.pos[m];
+  }
+}
+
+struct CacheRef {
+  void *pool;
+  const int *table;   // NULL = contiguous
+  int block_size;
+  int max_blocks;
+  int max_len;
+  int d_row;          // elements per cached row
+  int batch;          // sequences the descriptor covers
+  long cap;           // positions per sequence: max_len, or max_blocks * block_size
+};
+
+__device__ inline long cache_row(const CacheRef &c, int seq, int pos) {
+  if (c.table) {
+    int blk = c.table[(long)seq * c.max_blocks + pos / c.block_size];
+    return (long)blk * c.block_size + (pos % c.block_size);
+  }
+  return (long)seq * c.max_len + pos;
+}
+
+// ---------------------------------------------------------------------------
+// GEMM epilogue: the output columns [0, N) are cut into up to four segments,
+// each with its own destination.  A lane always holds four consecutive
+// columns of one row; segment and RoPE-group widths are multiples of 4.
+// ---------------------------------------------------------------------------
+enum SegKind { SEG_PLAIN = 0, SEG_HEADS = 1, SEG_CACHE = 2 };
+struct Seg {
+  int n_end;      // exclusive end column
+  int kind;
+  int rope;       // rotate pairs (2k, 2k+1) inside each group of head_w columns
+  int head_w;     // HEADS: columns per head; rope: group width
+  float scale;    // applied after RoPE
+  int out_f32;    // 1: store fp32 instead of the element type
+  void *dst;      // PLAIN: dst[m*ld + col_off + c]; HEADS: dst[m*ld + h*head_ld + col_off + d]
+  long ld;
+  long head_ld;
+  int col_off;    // also CACHE: column offset inside the cached row
+  void *dst2;     // optional PLAIN mirror: dst2[m*ld2 + c] (element type)
+  long ld2;
+  long batch_stride;  // added to dst per batch index (batched GEMMs)
+};
+#define MLA_MAX_ROPE_PAIRS 64
+struct Epi {
+  Seg seg[4];
+  int nseg;
+  RowMap rows;
+  CacheRef cache;
+  double inv_freq[MLA_MAX_ROPE_PAIRS];  // base^(-2k/d_R), computed on the host in fp64
+};
+
+// angle = pos * inv_freq[k]: formed and reduced modulo 2*pi in fp64 so that
+// positions up to 2^20 keep full fp32 accuracy, then sin/cos in fp32.
+__device__ inline void rope_sincos(int pos, double inv_freq, float &s, float &c) {
+  double a = (double)pos * inv_freq;
+  double r = a - 6.283185307179586476925 * rint(a * 0.15915494309189533576888);
+  sincosf((float)r, &s, &c);
+}
+
+template <typename T>
+__device__ inline void store4(void *base, long off, const float v[4], int as_f32) {
+  if (as_f32) {
+    float *p = (float *)base + off;
+    *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
+  } else if (sizeof(T) == 2) {
+    bf16x4 w = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+    *(bf16x4 *)((bf16 *)base + off) = w;
+  } else {
+    float *p = (float *)base + off;
+    *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
+  }
+}
+
+// Apply the epilogue to columns n..n+3 of row m (batch index z).
+template <typename T>
+__device__ inline void epi_store4(const Epi &e, int z, int m, int n, float v[4]) {
+  int s = 0, nb = 0;
+  while (s < e.nseg - 1 && n >= e.seg[s].n_end) { nb = e.seg[s].n_end; ++s; }
+  const Seg &g = e.seg[s];
+  const int c = n - nb;
+  int seq = 0, pos = 0;
+  if (g.rope || g.kind == SEG_CACHE) row_seq_pos(e.rows, m, seq, pos);
+  if (g.rope) {
+    const int k0 = (c % g.head_w) >> 1;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      float sn, cs;
+      rope_sincos(pos, e.inv_freq[k0 + p], sn, cs);
+      float x0 = v[2 * p], x1 = v[2 * p + 1];
+      v[2 * p] = x0 * cs - x1 * sn;
+      v[2 * p + 1] = x0 * sn + x1 * cs;
+    }
+  }
+  if (g.scale != 1.0f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] *= g.scale;
+  }
+  long off;
+  void *base = g.dst;
+  if (g.kind == SEG_PLAIN) {
+    off = (long)z * g.batch_stride + (long)m * g.ld + g.col_off + c;
+  } else if (g.kind == SEG_HEADS) {
+    const int hh = c / g.head_w, d = c - hh * g.head_w;
+    off = (long)z * g.batch_stride + (long)m * g.ld + (long)hh * g.head_ld + g.col_off + d;
+  } else {
+    // rows outside the described cache are never written
+    if (seq < 0 || seq >= e.cache.batch || pos < 0 || pos >= e.cache.cap) return;
+    base = e.cache.pool;
+    off = cache_row(e.cache, seq, pos) * e.cache.d_row + g.col_off + c;
+  }
+  store4<T>(base, off, v, g.out_f32);
+  if (g.dst2) store4<T>(g.dst2, (long)m * g.ld2 + c, v, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch descriptions
+// ---------------------------------------------------------------------------
+enum GemmTile { TILE_BIG = 0, TILE_SKINNY = 1 };
+
+struct GemmArgs {
+  const void *x; long ldx; long x_bs;           // X [M][K], row stride ldx, batch stride x_bs
+  const void *w[4]; int w_end[4]; int nw;       // row segments of W ([N][K]) or one [K][N] matrix
+  long ldw; long w_bs;
+  int M, N, K;
+  int splits, k_chunk;                          // split-K: K = splits * k_chunk
+  int batch;
+  float *partial;                               // splits > 1: [batch][splits][M][N]
+  int tiles_m, tiles_n;
+  const char *name;          // timing labels (static strings)
+  const char *reduce_name;
+  Epi epi;
+};
+
+// dtype: 0 fp32, 1 bf16.  swap: 1 -> output rows are tokens (segment
+// epilogue); 0 -> transposed plain store dst[n*ld + m].  wkn: W stored [K][N].
+hipError_t launch_gemm(int dtype, int tile, int swap, int wkn, GemmArgs &a, hipStream_t st);
+
+struct FlashArgs {
+  const void *q;    // [B*L][n_h][d_nope + d_rope] (q_C, then roped q_R)
+  const void *k;    // [B*L][n_h][d_nope]
+  const void *kr;   // [B*L][d_rope]
+  const void *vt;   // [n_h*d_v][B*L]
+  void *o;          // [B*L][n_h][d_v]
+  int B, L, n_h, d_nope, d_rope, d_v;
+  float scale_log2;  // softmax scale * log2(e)
+};
+hipError_t launch_flash_prefill(int dtype, const FlashArgs &a, hipStream_t st);
+
+struct DecodeArgs {
+  const void *q;      // q_abs [B*n_q][n_h][d_c + d_rope], softmax scale folded in
+  CacheRef cache;
+  const int *lens;    // [B]
+  int B, n_q, n_h, d_c, d_rope;
+  float scale_log2;   // softmax scale * log2(e)
+  int chunk;          // kv rows per split (multiple of the kv tile)
+  int n_splits;       // splits per sequence in the grid
+  int row_groups;     // groups of query rows (n_q*n_h rows per sequence)
+  float *o_part;      // [B][n_splits][n_q*n_h][d_c]
+  float *lse_part;    // [B][n_splits][n_q*n_h]  (log2 units)
+  void *o_lat;        // combine output [B*n_q][n_h][d_c]
+};
+int decode_rows_per_group(int dtype);
+int decode_kv_tile(int dtype);
+hipError_t launch_decode_attn(int dtype, const DecodeArgs &a, hipStream_t st);
+hipError_t launch_decode_combine(int dtype, const DecodeArgs &a, hipStream_t st);
+
+// kernel timing hooks (implemented with the C ABI)
+void timing_before(const char *name, hipStream_t st);
+void timing_after(const char *name, hipStream_t st);
+
+}  // namespace mla

@@ -1,0 +1,125 @@
+"""GPU parity: libmla (through the C ABI) against the CPU oracle on the same
+seeded inputs, element by element.  fp32: max-abs <= 1e-4; bf16: relative
+Frobenius <= 2e-2 and max-abs <= 5e-2."""
+import numpy as np
+import pytest
+import torch
+
+from mla_inputs import DSV3, make_workload
+from oracle import mla_oracle as O
+
+from tests.gpu_harness import (CacheBuf, Timer, assert_close, decode_cache, layer_for, oracle_decode_seq,
+                               run_decode, say, upload, weights64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill_check(wl, layer, paged=False, rows=None, want_o=False):
+    """Run mla_prefill on wl (kind prefill) and compare u, o and the cache rows."""
+    d, bf16 = wl.dims, wl.bf16
+    B, L = wl.batch, wl.seq_len
+    h = upload(wl.h_f32, wl.h_bits, bf16)
+    if paged:
+        bs = 64
+        nb = (L + bs - 1) // bs
+        perm = np.random.Generator(np.random.PCG64(5)).permutation(B * nb).astype(np.int32)
+        table = perm.reshape(B, nb)
+        pool = torch.zeros(B * nb * bs, d.d_row, dtype=layer.tdtype, device="cuda")
+        cache = CacheBuf.paged(pool, bs, table)
+    else:
+        cache = layer.new_cache(B, L)
+    say(f"prefill {wl.name} B={B} L={L} paged={paged}")
+    u, o = layer.prefill(h, cache, want_o=True)
+    torch.cuda.synchronize()
+    W = weights64(wl)
+    for b in range(B):
+        with Timer(f"oracle prefill b={b}"):
+            ref = O.prefill(d, W, wl.h_f32[b].astype(np.float64), rows=rows)
+        sel = np.arange(L) if rows is None else np.asarray(rows)
+        if ref["u"] is not None:
+            assert_close(u[b, torch.from_numpy(sel).cuda()], ref["u"], bf16, f"u b={b}")
+        assert_close(o.view(B, L, d.n_heads, d.d_v)[b, torch.from_numpy(sel).cuda()], ref["o"], bf16, f"o b={b}")
+        got_rows = cache.read_rows(b, np.arange(L))
+        ref_rows = np.concatenate([ref["c_kv"], ref["k_r"]], axis=1)
+        assert_close(got_rows, ref_rows, bf16, f"cache rows b={b}")
+    return u, o, cache
+
+
+def test_tiny_fp32_prefill_then_decode():
+    """Workload 1: 64-token prefill, then 8 single-token decode steps, fp32."""
+    wl = make_workload(1)
+    d = wl.dims
+    layer = layer_for(wl)
+    W = weights64(wl)
+    h_all = wl.h_f32[0].astype(np.float64)
+    full = O.prefill(d, W, h_all)
+    for paged in (False, True):
+        L, steps = wl.seq_len, wl.n_steps
+        total = L + steps
+        if paged:
+            bs = 16
+            nb = (total + bs - 1) // bs
+            table = np.random.Generator(np.random.PCG64(3)).permutation(nb).astype(np.int32).reshape(1, nb)
+            pool = torch.zeros(nb * bs, d.d_row, dtype=torch.float32, device="cuda")
+            cache = CacheBuf.paged(pool, bs, table)
+        else:
+            cache = layer.new_cache(1, total)
+        say(f"tiny prefill paged={paged}")
+        h = torch.from_numpy(wl.h_f32[:, :L]).cuda()
+        u = layer.prefill(h, cache)
+        torch.cuda.synchronize()
+        assert_close(u[0], full["u"][:L], False, "tiny prefill u")
+        ref_rows = np.concatenate([full["c_kv"], full["k_r"]], axis=1)
+        assert_close(cache.read_rows(0, np.arange(L)), ref_rows[:L], False, "tiny prefill cache rows")
+        for s in range(steps):
+            t = L + s
+            say(f"tiny decode step {s} paged={paged}")
+            hs = torch.from_numpy(wl.h_f32[:, t:t + 1]).cuda()
+            lens = torch.tensor([t + 1], dtype=torch.int32, device="cuda")
+            u1 = layer.decode(hs, lens, total, cache)
+            torch.cuda.synchronize()
+            assert_close(u1[0, 0], full["u"][t], False, f"tiny decode u step {s}")
+        assert_close(cache.read_rows(0, np.arange(total)), ref_rows, False, "tiny cache after decode")
+
+
+@pytest.mark.parametrize("B,L", [(1, 64), (2, 200), (1, 1), (3, 37)])
+def test_dsv3_prefill_small(B, L):
+    """DeepSeek-V3 shapes, bf16, small sequences with ragged tiles."""
+    wl = make_workload(3, batch=B, seq_len=L)
+    layer = layer_for(wl)
+    _prefill_check(wl, layer)
+
+
+def test_dsv3_prefill_paged():
+    wl = make_workload(3, batch=2, seq_len=130)
+    layer = layer_for(wl)
+    _prefill_check(wl, layer, paged=True)
+
+
+@pytest.mark.parametrize("B,L,nq", [(4, 300, 1), (2, 33, 1), (3, 1, 1), (2, 500, 2), (2, 2, 2), (1, 97, 3)])
+def test_dsv3_decode_small(B, L, nq):
+    """DeepSeek-V3 shapes, bf16 decode against a contiguous latent cache."""
+    wl = make_workload(2, batch=B, uniform_len=L, n_q=nq)
+    layer = layer_for(wl)
+    cache = decode_cache(wl, layer)
+    say(f"decode B={B} L={L} n_q={nq}")
+    u, o = run_decode(wl, layer, cache)
+    d = wl.dims
+    for b in range(B):
+        ref = oracle_decode_seq(wl, b)
+        assert_close(u[b], ref["u"], True, f"u b={b}")
+        assert_close(o.view(B, nq, d.n_heads, d.d_v)[b], ref["o"], True, f"o b={b}")
+        got_new = cache.read_rows(b, np.arange(L - nq, L))
+        assert_close(got_new, ref["row_new"], True, f"new cache rows b={b}")
+
+
+def test_dsv3_decode_ragged_paged_small():
+    """Ragged lengths, paged 64-row blocks in a permuted order."""
+    wl = make_workload(4, batch=6, ragged_max=700)
+    layer = layer_for(wl)
+    cache = decode_cache(wl, layer)
+    say(f"ragged paged decode lens={wl.lens.tolist()}")
+    u, o = run_decode(wl, layer, cache)
+    for b in range(wl.batch):
+        ref = oracle_decode_seq(wl, b)
+        assert_close(u[b], ref["u"], True, f"u b={b} len={wl.lens[b]}")
