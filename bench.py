@@ -82,6 +82,33 @@ def kernel_times(run, steps):
     return {k: {"avg_ms": ms / max(n, 1), "launches_per_step": n / steps} for k, (ms, n) in t.items()}
 
 
+def run_prefill(args, dev):
+    """Causal prefill of the DeepSeek-V3 layer, batch 1 x 4096 tokens, bf16."""
+    import torch
+    from head_latent_attention_18_amd.layer import MlaLayer, upload
+    from mla_inputs import make_workload
+    wp = make_workload(3)
+    lp = MlaLayer.from_host(wp.dims, "bf16", wp.weights_f32, wp.weights_bits)
+    hp = upload(wp.h_f32, wp.h_bits, True)
+    cp = lp.new_cache(wp.batch, wp.seq_len)
+    for _ in range(3):
+        lp.prefill(hp, cp)
+    torch.cuda.synchronize()
+    pk = max(3, args.steps // 5)
+    t0 = time.perf_counter()
+    for _ in range(pk):
+        lp.prefill(hp, cp)
+    torch.cuda.synchronize()
+    pdt = (time.perf_counter() - t0) / pk
+    pk_times = kernel_times(lambda i: lp.prefill(hp, cp), pk)
+    fl = prefill_flops(wp.dims, wp.batch, wp.seq_len)
+    log(f"prefill: {pdt * 1e3:.3f} ms, {fl / pdt / 1e12:.1f} TFLOPS")
+    return {"workload": wp.name, "ms": round(pdt * 1e3, 4), "TFLOPS": round(fl / pdt / 1e12, 1),
+            "mfma_frac": round(fl / pdt / 1e12 / BF16_PEAK_TFLOPS, 4), "alg_flops": fl,
+            "kernels": {k: {"avg_us": round(v["avg_ms"] * 1e3, 2), "launches_per_step": v["launches_per_step"]}
+                        for k, v in pk_times.items()}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,7 +117,11 @@ def main():
     ap.add_argument("--sets", type=int, default=3, help="rotated input copies (defeat the Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the oracle's timed sample")
+    ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the oracle's timed sample")
+    ap.add_argument("--only", choices=["all", "decode", "prefill"], default="all",
+                    help="profiling runs: time one path only (the JSON line is printed for 'all' and 'decode')")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="only copy a buffer of this many MB three times (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -104,6 +135,21 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: 3 copies of {args.copy_probe_mb} MiB")
+        return
+    if args.only == "prefill":
+        args.no_cpu_baseline = True
+
+    if args.only == "prefill":
+        run_prefill(args, dev)
+        return
 
     # ------------------------------------------------------------ decode
     t0 = time.perf_counter()
@@ -186,29 +232,7 @@ def main():
     del sets, outs
     torch.cuda.empty_cache()
 
-    # ------------------------------------------------------------ prefill
-    prefill = None
-    if not args.no_prefill:
-        wp = make_workload(3)
-        lp = MlaLayer.from_host(wp.dims, "bf16", wp.weights_f32, wp.weights_bits)
-        hp = upload(wp.h_f32, wp.h_bits, True)
-        cp = lp.new_cache(wp.batch, wp.seq_len)
-        for _ in range(3):
-            lp.prefill(hp, cp)
-        torch.cuda.synchronize()
-        pk = max(3, args.steps // 5)
-        t0 = time.perf_counter()
-        for _ in range(pk):
-            lp.prefill(hp, cp)
-        torch.cuda.synchronize()
-        pdt = (time.perf_counter() - t0) / pk
-        pk_times = kernel_times(lambda i: lp.prefill(hp, cp), pk)
-        fl = prefill_flops(wp.dims, wp.batch, wp.seq_len)
-        prefill = {"workload": wp.name, "ms": round(pdt * 1e3, 4), "TFLOPS": round(fl / pdt / 1e12, 1),
-                   "mfma_frac": round(fl / pdt / 1e12 / BF16_PEAK_TFLOPS, 4), "alg_flops": fl,
-                   "kernels": {k: {"avg_us": round(v["avg_ms"] * 1e3, 2), "launches_per_step": v["launches_per_step"]}
-                               for k, v in pk_times.items()}}
-        log(f"prefill: {pdt * 1e3:.3f} ms, {fl / pdt / 1e12:.1f} TFLOPS")
+    prefill = None if (args.no_prefill or args.only == "decode") else run_prefill(args, dev)
 
     out = {
         "metric": "MLA decode tokens/s (DeepSeek-V3 layer, batch 32, cache 4096)",

@@ -195,6 +195,9 @@ CacheRef cache_ref(const mla_config *c, const mla_cache *k, int32_t batch) {
   r.max_blocks = k->max_blocks_per_seq;
   r.max_len = k->max_len;
   r.d_row = c->d_c + c->d_rope;
+  r.bs_shift = -1;
+  for (int sh = 0; sh < 31; ++sh)
+    if ((1 << sh) == r.block_size) r.bs_shift = sh;
   return r;
 }
 

@@ -83,12 +83,18 @@ struct CacheRef {
   int d_row;          // elements per cached row
   int batch;          // sequences the descriptor covers
   long cap;           // positions per sequence: max_len, or max_blocks * block_size
+  int bs_shift;       // log2(block_size) when it is a power of two, else -1
 };
+
+__device__ inline int block_of(const CacheRef &c, int pos) {
+  return c.bs_shift >= 0 ? (pos >> c.bs_shift) : pos / c.block_size;
+}
 
 __device__ inline long cache_row(const CacheRef &c, int seq, int pos) {
   if (c.table) {
-    int blk = c.table[(long)seq * c.max_blocks + pos / c.block_size];
-    return (long)blk * c.block_size + (pos % c.block_size);
+    const int q = block_of(c, pos);
+    const int blk = c.table[(long)seq * c.max_blocks + q];
+    return (long)blk * c.block_size + (pos - q * c.block_size);
   }
   return (long)seq * c.max_len + pos;
 }

@@ -113,9 +113,11 @@ def test_dsv3_decode_small(B, L, nq):
         assert_close(got_new, ref["row_new"], True, f"new cache rows b={b}")
 
 
-def test_dsv3_decode_ragged_paged_small():
-    """Ragged lengths, paged 64-row blocks in a permuted order."""
-    wl = make_workload(4, batch=6, ragged_max=700)
+@pytest.mark.parametrize("block_size", [64, 32, 16, 96])
+def test_dsv3_decode_ragged_paged_small(block_size):
+    """Ragged lengths, paged blocks in a permuted order (block sizes that are
+    and are not multiples of the 32-row cache tile)."""
+    wl = make_workload(4, batch=6, ragged_max=700, block_size=block_size)
     layer = layer_for(wl)
     cache = decode_cache(wl, layer)
     say(f"ragged paged decode lens={wl.lens.tolist()}")
