@@ -379,9 +379,12 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_dma_kernel(DecodeArgs 
   const int ntiles = (kv_end - kv_beg + KVT - 1) / KVT;
   issue(0, std::integral_constant<int, 0>());
   if (ntiles > 1) issue(1, std::integral_constant<int, 1>());
-  const int kvl0 = 8 * (lrow >> 2) + (lrow & 3);   // permuted cache row of this A slot
-  const int a_off = kvl0 * LDC + lgrp * RUN;
-  const int t_off = (8 * lgrp + (lrow >> 2)) * LDC + 4 * (lrow & 3);
+  // Scores use the tile rows in natural order (A slot = row, conflict-free
+  // 16-byte reads): lane group g then holds rows 4g..4g+3 and 16+4g..16+4g+3.
+  // The transposed reads of P.V fetch exactly those rows (any four rows can
+  // form the 4x16 block), so the probabilities stay in registers.
+  const int a_off = lrow * LDC + lgrp * RUN;
+  const int t_off = (4 * lgrp + (lrow >> 2)) * LDC + 4 * (lrow & 3);
 
   // one tile; CUR is the stage holding it (compile-time, see above)
   auto step = [&](int t, auto cur_c) {
@@ -410,12 +413,12 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_dma_kernel(DecodeArgs 
       for (int hb = 0; hb < HB; ++hb) sacc[kb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
     bf16x8 ca[2][2];
     ca[0][0] = *(const lds_bf16x8 *)(ca_p);
-    ca[0][1] = *(const lds_bf16x8 *)(ca_p + 4 * LDC);
+    ca[0][1] = *(const lds_bf16x8 *)(ca_p + 16 * LDC);
 #pragma unroll
     for (int q = 0; q < QS; ++q) {
       if (q + 1 < QS) {
         ca[(q + 1) & 1][0] = *(const lds_bf16x8 *)(ca_p + (q + 1) * 8);
-        ca[(q + 1) & 1][1] = *(const lds_bf16x8 *)(ca_p + 4 * LDC + (q + 1) * 8);
+        ca[(q + 1) & 1][1] = *(const lds_bf16x8 *)(ca_p + 16 * LDC + (q + 1) * 8);
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -433,7 +436,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_dma_kernel(DecodeArgs 
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int kv = kvb + 8 * lgrp + 4 * kb + i;
+          const int kv = kvb + 16 * kb + 4 * lgrp + i;
           const float x = sacc[kb][hb][i] * sl2;
           sv[kb][i] = (kv <= limit[hb]) ? x : -INFINITY;
           mt = fmaxf(mt, sv[kb][i]);
@@ -460,7 +463,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_dma_kernel(DecodeArgs 
 
     // O^T[d][row] += C_lat^T[d][kv] . P^T[kv][row]; C_lat^T is read transposed
     // out of the row tile, one 16-dim block ahead of its MFMAs
-    constexpr int TRH = LDC;   // four rows further, in 4-element units
+    constexpr int TRH = 4 * LDC;   // sixteen rows further, in 4-element units
     v4i16 vt[2][2];
     vt[0][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(tr_p);
     vt[0][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(tr_p + TRH);

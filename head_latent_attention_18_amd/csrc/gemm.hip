@@ -10,6 +10,8 @@
 // epilogue can apply RoPE to (2k, 2k+1) pairs and write cache rows without
 // any cross-lane exchange.  Without SWAP the lane holds four consecutive
 // tokens of one feature, which is what a transposed store (V^T) needs.
+#include <type_traits>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -194,6 +196,126 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Weight-streaming GEMM for few tokens (decode): bf16, W stored [N][K].
+// Each wave owns 16 output features and streams its weight rows straight from
+// HBM into MFMA A-operand registers (a ring of three 256-wide k stages, so two
+// stages are in flight while one is multiplied); the tokens' activations are
+// staged in LDS once per workgroup and read as the B operand.  Within a stage,
+// MFMA step s of lane group g uses the 16-byte chunk 4*s+g of its row, so one
+// load instruction covers 64 contiguous bytes of each of 16 rows.
+// ---------------------------------------------------------------------------
+// The stage count NST is a template parameter and the pipeline is fully
+// unrolled: with a loop, the compiler's wait-count tracking loses which load
+// fills which ring slot at the back edge and waits for every load in flight.
+#ifndef SKINNY_AHEAD
+#define SKINNY_AHEAD 2
+#endif
+template <int MB, int BK, int NST>
+__global__ __launch_bounds__(256, 2) void gemm_skinny_kernel(GemmArgs a) {
+  constexpr int NW = 4, BN = 16 * NW, VE = 8;
+  constexpr int STEPS = BK / 32;              // MFMA k-steps per stage
+  constexpr int CHS = BK / VE;                // 16-byte chunks per row per stage
+  constexpr int XLD = BK + VE;                // LDS row pitch of the activation stage
+  constexpr int XCH = 16 * MB * CHS;          // activation chunks per stage
+  constexpr int XPT = (XCH + 255) / 256;
+  constexpr int AHEAD = SKINNY_AHEAD;         // weight stages in flight beyond the current one
+  static_assert(STEPS * 4 == CHS, "");
+  __shared__ __attribute__((aligned(16))) bf16 xs[2][16 * MB * XLD];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  int bid = blockIdx.x;
+  const int nb = gridDim.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int tn = bid;                                   // one N tile per block column (tiles_m == 1)
+  const int bz = blockIdx.y / a.splits, sp = blockIdx.y % a.splits;
+  const int M = a.M, N = a.N;
+  const int n0 = tn * BN;
+  const int kbeg = sp * a.k_chunk;
+
+  // weight row of this lane (segments of W rows are separate matrices)
+  const int n = min(n0 + wave * 16 + lrow, N - 1);
+  int seg = 0, beg = 0;
+  while (seg < a.nw - 1 && n >= a.w_end[seg]) { beg = a.w_end[seg]; ++seg; }
+  const bf16 *wrow = (const bf16 *)a.w[seg] + (long)bz * a.w_bs + (long)(n - beg) * a.ldw + kbeg + lgrp * VE;
+  const bf16 *X = (const bf16 *)a.x + (long)bz * a.x_bs;
+
+  bf16x8 wr[NST][STEPS];
+  auto wload = [&](int st) {
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) wr[st][s] = *(const bf16x8 *)(wrow + (long)st * BK + s * 4 * VE);
+  };
+  u32x4 xr[NST][XPT];   // activations travel AHEAD stages early, with their weights
+  auto xload = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int c = tid + i * 256;
+      if (c < XCH) {
+        const int r = c / CHS, kc = c % CHS;
+        xr[st][i] = *(const u32x4 *)(X + (long)min(r, M - 1) * a.ldx + kbeg + (long)st * BK + kc * VE);
+      }
+    }
+  };
+  auto xstore = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int c = tid + i * 256;
+      if (c < XCH) {
+        const int r = c / CHS, kc = c % CHS;
+        *(u32x4 *)&xs[st & 1][r * XLD + kc * VE] = xr[st][i];
+      }
+    }
+  };
+
+  f32x4 acc[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int i = 0; i <= AHEAD && i < NST; ++i) {
+    xload(i);
+    wload(i);
+  }
+  xstore(0);
+  __syncthreads();
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    const int buf = st & 1;
+    if (st + AHEAD + 1 < NST) {                  // stage st+AHEAD+1 enters the pipe
+      xload(st + AHEAD + 1);
+      wload(st + AHEAD + 1);
+    }
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 xb = *(const bf16x8 *)&xs[buf][(mb * 16 + lrow) * XLD + (4 * s + lgrp) * VE];
+        acc[mb] = Mma<bf16>::mma(wr[st][s], xb, acc[mb]);
+      }
+    }
+    if (st + 1 < NST) {
+      xstore(st + 1);
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = mb * 16 + lrow;
+    const int nn = n0 + wave * 16 + 4 * lgrp;
+    if (m < M && nn < N) {
+      float v[4] = {acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]};
+      if (a.splits > 1) {
+        float *p = a.partial + (((long)bz * a.splits + sp) * M + m) * N + nn;
+        *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
+      } else {
+        epi_store4<bf16>(a.epi, bz, m, nn, v);
+      }
+    }
+  }
+}
+
 // Sum the split-K partials in split order (deterministic) and apply the epilogue.
 template <typename T>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a) {
@@ -204,9 +326,19 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a) {
   const int bz = (int)(idx / ((long)a.M * n4));
   const long rem = idx - (long)bz * a.M * n4;
   const int m = (int)(rem / n4), n = (int)(rem % n4) * 4;
+  // issue the loads of eight splits before summing them (in split order)
   f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int p = 0; p < a.splits; ++p)
-    s += *(const f32x4 *)(a.partial + (((long)bz * a.splits + p) * a.M + m) * a.N + n);
+  const float *src = a.partial + ((long)bz * a.splits * a.M + m) * a.N + n;
+  const long step = (long)a.M * a.N;
+  int p = 0;
+  for (; p + 8 <= a.splits; p += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = *(const f32x4 *)(src + (p + j) * step);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += v[j];
+  }
+  for (; p < a.splits; ++p) s += *(const f32x4 *)(src + p * step);
   float v[4] = {s[0], s[1], s[2], s[3]};
   epi_store4<T>(a.epi, bz, m, n, v);
 }
@@ -233,6 +365,44 @@ static hipError_t launch_t(GemmArgs &a, hipStream_t st, const char *name) {
   return e;
 }
 
+template <int MB, int BK, int NST>
+static void launch_skinny_nst(GemmArgs &a, hipStream_t st, dim3 grid) {
+  hipLaunchKernelGGL((gemm_skinny_kernel<MB, BK, NST>), grid, dim3(256), 0, st, a);
+}
+// stage counts with an instantiation (the host planner picks k_chunk among these)
+int skinny_nst_supported(int nst) { return nst == 1 || nst == 2 || nst == 3 || nst == 4 || nst == 6 || nst == 8 || nst == 16; }
+template <int MB, int BK>
+static hipError_t launch_skinny(GemmArgs &a, hipStream_t st, const char *name) {
+  a.tiles_m = 1;
+  a.tiles_n = (a.N + 63) / 64;
+  dim3 grid(a.tiles_n, a.batch * a.splits);
+  if (a.name) name = a.name;
+  const int nst = a.k_chunk / BK;
+  timing_before(name, st);
+  switch (nst) {
+    case 1: launch_skinny_nst<MB, BK, 1>(a, st, grid); break;
+    case 2: launch_skinny_nst<MB, BK, 2>(a, st, grid); break;
+    case 3: launch_skinny_nst<MB, BK, 3>(a, st, grid); break;
+    case 4: launch_skinny_nst<MB, BK, 4>(a, st, grid); break;
+    case 6: launch_skinny_nst<MB, BK, 6>(a, st, grid); break;
+    case 8: launch_skinny_nst<MB, BK, 8>(a, st, grid); break;
+    case 16: launch_skinny_nst<MB, BK, 16>(a, st, grid); break;
+    default: return hipErrorInvalidValue;
+  }
+  timing_after(name, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.splits > 1) {
+    const long total = (long)a.batch * a.M * (a.N / 4);
+    const char *rname = a.reduce_name ? a.reduce_name : "splitk_reduce";
+    timing_before(rname, st);
+    hipLaunchKernelGGL(splitk_reduce_kernel<bf16>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a);
+    timing_after(rname, st);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
 // K granularity each tile needs (host checks K % gemm_bk == 0 per split).
 int gemm_bk(int dtype, int tile) {
   if (dtype == 0) return 32;
@@ -250,7 +420,15 @@ hipError_t launch_gemm(int dtype, int tile, int swap, int wkn, GemmArgs &a, hipS
       if (!swap && !wkn) return launch_t<bf16, 128, 128, 64, 2, 2, false, false>(a, st, "gemm_bf16_128x128_t");
       if (swap && wkn) return launch_t<bf16, 128, 128, 64, 2, 2, true, true>(a, st, "gemm_bf16_128x128_kn");
     } else {
-      if (swap && !wkn) return launch_t<bf16, 32, 64, 64, 1, 4, true, false>(a, st, "gemm_bf16_32x64");
+      if (swap && !wkn) {
+        if (a.M <= 32 && a.k_chunk % 256 == 0 && skinny_nst_supported(a.k_chunk / 256))
+          return launch_skinny<2, 256>(a, st, "gemm_bf16_stream_m32");
+        if (a.M <= 64 && a.k_chunk % 256 == 0 && skinny_nst_supported(a.k_chunk / 256))
+          return launch_skinny<4, 256>(a, st, "gemm_bf16_stream_m64");
+        if (a.M <= 128 && a.k_chunk % 128 == 0 && skinny_nst_supported(a.k_chunk / 128))
+          return launch_skinny<8, 128>(a, st, "gemm_bf16_stream_m128");
+        return launch_t<bf16, 32, 64, 64, 1, 4, true, false>(a, st, "gemm_bf16_32x64");
+      }
       if (!swap && !wkn) return launch_t<bf16, 32, 64, 64, 1, 4, false, false>(a, st, "gemm_bf16_32x64_t");
       if (swap && wkn) return launch_t<bf16, 32, 64, 64, 1, 4, true, true>(a, st, "gemm_bf16_32x64_kn");
     }

@@ -25,6 +25,7 @@
 namespace mla {
 int gemm_bk(int dtype, int tile);
 int gemm_bm(int dtype, int tile);
+int skinny_nst_supported(int nst);
 }
 
 using namespace mla;
@@ -112,22 +113,32 @@ struct SplitK { int splits, k_chunk; };
 
 int gemm_tile_for(int dtype, int64_t M) { return (dtype == MLA_BF16 && M >= 256) ? TILE_BIG : TILE_SKINNY; }
 
-// Choose a split of K so that tiles * splits reaches about 2 workgroups per CU.
+// Split K only as far as needed for about two workgroups per CU: the
+// weight-streaming kernel (bf16, up to 128 tokens) works on 64-feature tiles
+// and 256-wide k stages (128 above 64 tokens); other shapes use 32x64 tiles.
 SplitK choose_splitk(int dtype, int64_t M, int64_t N, int64_t K, int batch) {
+  SplitK r;
+  r.splits = 1;
+  r.k_chunk = (int)K;
   const int tile = gemm_tile_for(dtype, M);
-  const int bk = gemm_bk(dtype, tile), bm = gemm_bm(dtype, tile);
-  const int bn = dtype == MLA_BF16 ? (tile == TILE_BIG ? 128 : 64) : 32;
+  if (tile != TILE_SKINNY) return r;
+  int bk, bn;
+  if (dtype == MLA_BF16 && M <= 128) {
+    bk = M <= 64 ? 256 : 128;
+    bn = 64;
+    if (K % bk) { bk = gemm_bk(dtype, tile); bn = 64; }
+  } else {
+    bk = gemm_bk(dtype, tile);
+    bn = dtype == MLA_BF16 ? 64 : 32;
+  }
+  const int bm = dtype == MLA_BF16 && M <= 128 ? (int)M : gemm_bm(dtype, tile);
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn) * batch;
   const int64_t nkt = K / bk;
-  int best = 1;
-  if (tile == TILE_SKINNY) {
-    const int64_t want = (2 * kCUs + tiles - 1) / tiles;
-    for (int64_t s = 1; s <= nkt && s <= 32; ++s)
-      if (nkt % s == 0 && s <= want) best = (int)s;
-  }
-  SplitK r;
-  r.splits = best;
-  r.k_chunk = (int)(K / best);
+  const int64_t want = std::max<int64_t>(1, (2 * kCUs) / tiles);
+  const bool stream = dtype == MLA_BF16 && M <= 128 && K % bk == 0;
+  for (int64_t s = 1; s <= nkt && s <= 32; ++s)
+    if (nkt % s == 0 && s <= want && (!stream || skinny_nst_supported((int)(nkt / s)))) r.splits = (int)s;
+  r.k_chunk = (int)(K / r.splits);
   return r;
 }
 
@@ -352,11 +363,11 @@ void timing_before(const char *name, hipStream_t st) {
     g_events.push_back(t);
   }
   g_events[g_used].name = name;
-  hipEventRecord(g_events[g_used].start, st);
+  (void)hipEventRecord(g_events[g_used].start, st);
 }
 void timing_after(const char *name, hipStream_t st) {
   if (!g_timing || g_used >= g_events.size() || g_events[g_used].name != name) return;
-  hipEventRecord(g_events[g_used].stop, st);
+  (void)hipEventRecord(g_events[g_used].stop, st);
   ++g_used;
 }
 }  // namespace mla

@@ -12,7 +12,8 @@ import os
 from ctypes import POINTER, c_char_p, c_double, c_int32, c_int64, c_size_t, c_void_p
 from typing import Dict, Optional
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmla.so")
+LIB_PATH = os.environ.get("MLA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib",
+                                                         "libmla.so")
 
 MLA_FP32, MLA_BF16 = 0, 1
 MLA_OP_PREFILL, MLA_OP_DECODE = 0, 1
