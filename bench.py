@@ -148,7 +148,7 @@ def main():
         args.no_cpu_baseline = True
 
     if args.only == "prefill":
-        run_prefill(args, dev)
+        print(json.dumps(run_prefill(args, dev)), flush=True)
         return
 
     # ------------------------------------------------------------ decode

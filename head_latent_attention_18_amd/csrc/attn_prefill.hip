@@ -15,8 +15,14 @@
 
 namespace mla {
 
-template <typename T, int QB, int DN, int DR, int DV>
-__global__ __launch_bounds__(256, 1) void flash_prefill_kernel(FlashArgs a) {
+#ifndef FLASH_QB
+#define FLASH_QB 2   // 16-query blocks per wave
+#define FLASH_NW 8   // waves per workgroup
+#endif
+
+template <typename T, int QB, int NW, int DN, int DR, int DV>
+__global__ __launch_bounds__(64 * NW, 1) void flash_prefill_kernel(FlashArgs a) {
+  constexpr int NT = 64 * NW;
   constexpr int KVB = 4, KVT = 64;
   constexpr int DQK = DN + DR;
   constexpr int KPL = Mma<T>::KPL;
@@ -28,17 +34,19 @@ __global__ __launch_bounds__(256, 1) void flash_prefill_kernel(FlashArgs a) {
   constexpr int DVB = DV / 16;
   constexpr int LDK = DQK + VE;
   constexpr int LDV = KVT + VE;
-  constexpr int BQ = 64 * QB;
+  constexpr int BQ = 16 * QB * NW;
   static_assert(RUNQ % KPL == 0 && PRUN % KPL == 0, "");
   static_assert(DN % VE == 0 && DR % VE == 0 && KVT % VE == 0, "");
   constexpr int KCH = KVT * (DQK / VE);
   constexpr int VCH = DV * (KVT / VE);
-  constexpr int KPT = (KCH + 255) / 256;
-  constexpr int VPT = (VCH + 255) / 256;
+  constexpr int KPT = (KCH + NT - 1) / NT;
+  constexpr int VPT = (VCH + NT - 1) / NT;
   typedef typename Mma<T>::frag frag;
+  typedef __attribute__((address_space(3))) T lds_T;
+  typedef __attribute__((address_space(3))) frag lds_frag;
 
-  __shared__ __attribute__((aligned(16))) T ks[KVT * LDK];
-  __shared__ __attribute__((aligned(16))) T vs[DV * LDV];
+  __shared__ __attribute__((aligned(16))) T ks[2][KVT * LDK];
+  __shared__ __attribute__((aligned(16))) T vs[2][DV * LDV];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 15, lgrp = lane >> 4;
@@ -84,9 +92,9 @@ __global__ __launch_bounds__(256, 1) void flash_prefill_kernel(FlashArgs a) {
   for (int i = 0; i < DVB; ++i)
 #pragma unroll
     for (int j = 0; j < QB; ++j) oacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrun[QB], lrun[QB];
+  float mref[QB], lrun[QB];
 #pragma unroll
-  for (int j = 0; j < QB; ++j) { mrun[j] = -1e30f; lrun[j] = 0.f; }
+  for (int j = 0; j < QB; ++j) { mref[j] = -1e30f; lrun[j] = 0.f; }
 
   const T *Kn = (const T *)a.k;
   const T *Kr = (const T *)a.kr;
@@ -95,7 +103,7 @@ __global__ __launch_bounds__(256, 1) void flash_prefill_kernel(FlashArgs a) {
   auto gload = [&](int kvb) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * 256;
+      const int c = tid + i * NT;
       if (c < KCH) {
         const int r = c / (DQK / VE), cc = (c % (DQK / VE)) * VE;
         const long tok = tok0 + min(kvb + r, L - 1);
@@ -105,7 +113,7 @@ __global__ __launch_bounds__(256, 1) void flash_prefill_kernel(FlashArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int c = tid + i * 256;
+      const int c = tid + i * NT;
       if (c < VCH) {
         const int d = c / (KVT / VE), kc = (c % (KVT / VE)) * VE;
         const int kv = kvb + kc;
@@ -121,111 +129,134 @@ __global__ __launch_bounds__(256, 1) void flash_prefill_kernel(FlashArgs a) {
       }
     }
   };
-  auto lstore = [&]() {
+  auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * 256;
+      const int c = tid + i * NT;
       if (c < KCH) {
         const int r = c / (DQK / VE), cc = (c % (DQK / VE)) * VE;
-        *(u32x4 *)&ks[r * LDK + cc] = kr_[i];
+        *(u32x4 *)&ks[buf][r * LDK + cc] = kr_[i];
       }
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int c = tid + i * 256;
+      const int c = tid + i * NT;
       if (c < VCH) {
         const int d = c / (KVT / VE), kc = (c % (KVT / VE)) * VE;
-        *(u32x4 *)&vs[d * LDV + kc] = vr_[i];
+        *(u32x4 *)&vs[buf][d * LDV + kc] = vr_[i];
       }
     }
   };
 
   const int ntiles = blk_qmax / KVT + 1;
-  const int kvl0 = 4 * KVB * (lrow >> 2) + (lrow & 3);   // permuted key row of this A slot
+  // Scores use the key rows in natural order (A slot = row); lane group g
+  // then holds keys 4g+i of each 16-key block, and V^T is read with the same
+  // key order for P.V.
+  const int a_off = lrow * LDK + lgrp * RUNQ;
   gload(0);
+  lstore(0);
+  __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int kvb = t * KVT;
-    __syncthreads();
-    lstore();
-    __syncthreads();
+    const int buf = t & 1;
     if (t + 1 < ntiles) gload(kvb + KVT);
-    if (kvb > wave_qmax) continue;   // every key of this tile is after every query of this wave
-
-    f32x4 sacc[KVB][QB];
+    if (kvb <= wave_qmax) {   // otherwise every key of this tile is after every query of this wave
+      const lds_T *kb_p = (const lds_T *)ks[buf] + a_off;
+      const lds_T *vb_p = (const lds_T *)vs[buf];
+      f32x4 sacc[KVB][QB];
 #pragma unroll
-    for (int kb = 0; kb < KVB; ++kb)
+      for (int kb = 0; kb < KVB; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < QS; ++s) {
+      for (int s = 0; s < QS; ++s) {
 #pragma unroll
-      for (int kb = 0; kb < KVB; ++kb) {
-        const frag ka = *(const frag *)&ks[(kvl0 + 4 * kb) * LDK + lgrp * RUNQ + s * KPL];
+        for (int kb = 0; kb < KVB; ++kb) {
+          const frag ka = *(const lds_frag *)(kb_p + kb * 16 * LDK + s * KPL);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = Mma<T>::mma(ka, qf[qb][s], sacc[kb][qb]);
+          for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = Mma<T>::mma(ka, qf[qb][s], sacc[kb][qb]);
+        }
       }
-    }
 
-    const bool diag = kvb + KVT - 1 > q0;
-    frag pf[QB][PS];
+      const bool diag = kvb + KVT - 1 > q0;
+      frag pf[QB][PS];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int qpos = q0 + qb * 16 + lrow;
-      float sv[KVB][4];
-      float mt = -INFINITY;
+      for (int qb = 0; qb < QB; ++qb) {
+        const int qpos = q0 + qb * 16 + lrow;
+        float sv[KVB][4];
+        float mt = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < KVB; ++kb)
+        for (int kb = 0; kb < KVB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kv = kvb + 4 * KVB * lgrp + 4 * kb + i;
-          float x = sacc[kb][qb][i] * sl2;
-          if (diag && kv > qpos) x = -INFINITY;
-          sv[kb][i] = x;
-          mt = fmaxf(mt, x);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mnew = fmaxf(mrun[qb], mt);
-      const float alpha = exp2f(mrun[qb] - mnew);
-      mrun[qb] = mnew;
-      float psum = 0.f;
-      float p[KVB][4];
-#pragma unroll
-      for (int kb = 0; kb < KVB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[kb][i] = exp2f(sv[kb][i] - mnew);
-          psum += p[kb][i];
-        }
-      lrun[qb] = lrun[qb] * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < DVB; ++db) oacc[db][qb] *= alpha;
-      // lane-group run of 16 keys: slot j <-> key block j/4, row j%4
-      if constexpr (KPL == 8) {
-#pragma unroll
-        for (int ps = 0; ps < PS; ++ps) {
-          bf16x8 f;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int jj = ps * 8 + j;
-            f[j] = (bf16)p[jj >> 2][jj & 3];
+          for (int i = 0; i < 4; ++i) {
+            const int kv = kvb + 16 * kb + 4 * lgrp + i;
+            float x = sacc[kb][qb][i] * sl2;
+            if (diag && kv > qpos) x = -INFINITY;
+            sv[kb][i] = x;
+            mt = fmaxf(mt, x);
           }
-          pf[qb][ps] = f;
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        // the running reference max only moves when a tile exceeds it by 2^8
+        if (__any(mt > mref[qb] + 8.0f)) {
+          const float mnew = fmaxf(mref[qb], mt);
+          const float alpha = exp2f(mref[qb] - mnew);
+          mref[qb] = mnew;
+          lrun[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DVB; ++db) oacc[db][qb] *= alpha;
         }
-      } else {
+        float psum = 0.f;
+        float p[KVB][4];
 #pragma unroll
-        for (int ps = 0; ps < PS; ++ps) pf[qb][ps] = p[ps >> 2][ps & 3];
+        for (int kb = 0; kb < KVB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[kb][i] = exp2f(sv[kb][i] - mref[qb]);
+            psum += p[kb][i];
+          }
+        lrun[qb] += psum;
+        // P.V step ps covers key blocks 2ps/KPL... : slot j of lane group g is
+        // key 16*(j/4) + 4g + (j%4) of the tile
+        if constexpr (KPL == 8) {
+#pragma unroll
+          for (int ps = 0; ps < PS; ++ps) {
+            bf16x8 f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int jj = ps * 8 + j;
+              f[j] = (bf16)p[jj >> 2][jj & 3];
+            }
+            pf[qb][ps] = f;
+          }
+        } else {
+#pragma unroll
+          for (int ps = 0; ps < PS; ++ps) pf[qb][ps] = p[ps >> 2][ps & 3];
+        }
       }
-    }
 
+      // V^T rows d, key slots in the same order as the probabilities: slot j
+      // of lane group g is key 16*(j/4) + 4g + (j%4), i.e. two 4-key runs
 #pragma unroll
-    for (int ps = 0; ps < PS; ++ps)
+      for (int ps = 0; ps < PS; ++ps)
 #pragma unroll
-      for (int db = 0; db < DVB; ++db) {
-        const frag va = *(const frag *)&vs[(db * 16 + lrow) * LDV + lgrp * PRUN + ps * KPL];
+        for (int db = 0; db < DVB; ++db) {
+          frag va;
+          if constexpr (KPL == 8) {
+            typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+            const lds_T *row = vb_p + (db * 16 + lrow) * LDV + 4 * lgrp;
+            const bf16x4 lo = *(const lds_bf16x4 *)(row + 32 * ps);
+            const bf16x4 hi = *(const lds_bf16x4 *)(row + 32 * ps + 16);
+            va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          } else {
+            va = *(const lds_frag *)(vb_p + (db * 16 + lrow) * LDV + 16 * (ps >> 2) + 4 * lgrp + (ps & 3));
+          }
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = Mma<T>::mma(va, pf[qb][ps], oacc[db][qb]);
-      }
+          for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = Mma<T>::mma(va, pf[qb][ps], oacc[db][qb]);
+        }
+    }
+    if (t + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
   }
 
 #pragma unroll
@@ -246,19 +277,19 @@ __global__ __launch_bounds__(256, 1) void flash_prefill_kernel(FlashArgs a) {
   }
 }
 
-template <typename T, int QB, int DN, int DR, int DV>
+template <typename T, int QB, int NW, int DN, int DR, int DV>
 static hipError_t launch_fp(const FlashArgs &a, hipStream_t st) {
-  const int qtiles = (a.L + 64 * QB - 1) / (64 * QB);
+  const int qtiles = (a.L + 16 * QB * NW - 1) / (16 * QB * NW);
   const long grid = (long)qtiles * a.B * a.n_h;
   timing_before("flash_prefill", st);
-  hipLaunchKernelGGL((flash_prefill_kernel<T, QB, DN, DR, DV>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((flash_prefill_kernel<T, QB, NW, DN, DR, DV>), dim3((unsigned)grid), dim3(64 * NW), 0, st, a);
   timing_after("flash_prefill", st);
   return hipGetLastError();
 }
 
 hipError_t launch_flash_prefill(int dtype, const FlashArgs &a, hipStream_t st) {
-  if (dtype == 1 && a.d_nope == 128 && a.d_rope == 64 && a.d_v == 128) return launch_fp<bf16, 4, 128, 64, 128>(a, st);
-  if (dtype == 0 && a.d_nope == 32 && a.d_rope == 16 && a.d_v == 32) return launch_fp<float, 1, 32, 16, 32>(a, st);
+  if (dtype == 1 && a.d_nope == 128 && a.d_rope == 64 && a.d_v == 128) return launch_fp<bf16, FLASH_QB, FLASH_NW, 128, 64, 128>(a, st);
+  if (dtype == 0 && a.d_nope == 32 && a.d_rope == 16 && a.d_v == 32) return launch_fp<float, 1, 4, 32, 16, 32>(a, st);
   return hipErrorInvalidValue;
 }
 

@@ -413,11 +413,20 @@ int gemm_bm(int dtype, int tile) {
   return tile == TILE_BIG ? 128 : 32;
 }
 
+#ifndef BIG_BM
+#define BIG_BM 128
+#define BIG_BN 128
+#endif
+#ifndef BIG_BK
+#define BIG_BK 64
+#define BIG_WM 2   // 8 waves: 64x32 per wave
+#define BIG_WN 4
+#endif
 hipError_t launch_gemm(int dtype, int tile, int swap, int wkn, GemmArgs &a, hipStream_t st) {
   if (dtype == 1) {
     if (tile == TILE_BIG) {
-      if (swap && !wkn) return launch_t<bf16, 128, 128, 64, 2, 2, true, false>(a, st, "gemm_bf16_128x128");
-      if (!swap && !wkn) return launch_t<bf16, 128, 128, 64, 2, 2, false, false>(a, st, "gemm_bf16_128x128_t");
+      if (swap && !wkn) return launch_t<bf16, BIG_BM, BIG_BN, BIG_BK, BIG_WM, BIG_WN, true, false>(a, st, "gemm_bf16_big");
+      if (!swap && !wkn) return launch_t<bf16, BIG_BM, BIG_BN, BIG_BK, BIG_WM, BIG_WN, false, false>(a, st, "gemm_bf16_big_t");
       if (swap && wkn) return launch_t<bf16, 128, 128, 64, 2, 2, true, true>(a, st, "gemm_bf16_128x128_kn");
     } else {
       if (swap && !wkn) {
