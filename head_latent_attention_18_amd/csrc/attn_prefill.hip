@@ -54,7 +54,9 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_kernel(FlashArgs a) 
   const int qtiles = (L + BQ - 1) / BQ;
 
   // block -> (query tile, longest first; sequence; head).  Heads that share
-  // bid % 8 land on one XCD, so a head's K/V tiles stay in one L2.
+  // bid % 8 land on one XCD, so the query tiles of a head running together
+  // share its K/V tiles in that XCD's L2; longest-first keeps the causal tail
+  // short.
   int bid = blockIdx.x, h, b, qt_rev;
   if ((NH & 7) == 0) {
     const int hx = bid & 7;

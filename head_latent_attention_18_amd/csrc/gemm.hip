@@ -42,12 +42,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
   const int wm = wave % WM, wn = wave / WM;
   const int lrow = lane & 15, lgrp = lane >> 4;
 
-  // XCD-aware order: the dispatcher deals blocks round-robin over the 8 XCDs,
-  // so remap to give each XCD a contiguous range of tiles (shared W rows).
-  int bid = blockIdx.x;
-  const int nb = gridDim.x;
-  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
-  const int tm = bid % a.tiles_m, tn = bid / a.tiles_m;
+  // Tile order.  The dispatcher deals blocks round-robin over the 8 XCDs
+  // (block b runs on XCD b % 8).  The tiles are cut into 8x8 groups; each XCD
+  // takes whole groups, so the blocks running together on one XCD share eight
+  // X row-tiles and eight W row-tiles: every k-slab they load is reused eight
+  // times from that XCD's L2.  The grid covers the tile counts rounded up to
+  // whole groups; blocks past the edge exit.
+  int tm, tn;
+  if (!a.grouped) {
+    tm = blockIdx.x % a.tiles_m;
+    tn = blockIdx.x / a.tiles_m;
+  } else {
+    const int bid = blockIdx.x, xcd = bid & 7, local = bid >> 3;
+    const int gm_n = (a.tiles_m + 7) >> 3;                // groups along M
+    const int g = (local >> 6) * 8 + xcd, w = local & 63;
+    tm = (g % gm_n) * 8 + (w & 7);
+    tn = (g / gm_n) * 8 + (w >> 3);
+    if (tm >= a.tiles_m || tn >= a.tiles_n) return;
+  }
   const int bz = blockIdx.y / a.splits, sp = blockIdx.y % a.splits;
   const int M = a.M, N = a.N;
   const int m0 = tm * BM, n0 = tn * BN;
@@ -347,7 +359,9 @@ template <typename T, int BM, int BN, int BK, int WM, int WN, bool SWAP, bool WK
 static hipError_t launch_t(GemmArgs &a, hipStream_t st, const char *name) {
   a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + BN - 1) / BN;
-  dim3 grid(a.tiles_m * a.tiles_n, a.batch * a.splits);
+  a.grouped = a.tiles_m >= 8 && a.tiles_n >= 8;
+  dim3 grid(a.grouped ? ((a.tiles_m + 7) / 8) * ((a.tiles_n + 7) / 8) * 64 : a.tiles_m * a.tiles_n,
+            a.batch * a.splits);
   if (a.name) name = a.name;
   timing_before(name, st);
   hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, SWAP, WKN>), grid, dim3(64 * WM * WN), 0, st, a);

@@ -206,6 +206,7 @@ struct GemmArgs {
   int batch;
   float *partial;                               // splits > 1: [batch][splits][M][N]
   int tiles_m, tiles_n;
+  int grouped;               // 8x8 tile groups per XCD (set by the launcher)
   const char *name;          // timing labels (static strings)
   const char *reduce_name;
   Epi epi;
