@@ -243,53 +243,108 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_kernel(DecodeArgs a) {
     if (r < R) {
       const float inv = l > 0.f ? 1.f / l : 0.f;
       const long pbase = ((long)b * a.n_splits + s) * R + r;
-      float *op = a.o_part + pbase * DC;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) *(f32x4 *)(op + db * 16 + 4 * lgrp) = oacc[db][hb] * inv;
+      for (int db = 0; db < DB; ++db) {
+        const f32x4 o4 = oacc[db][hb] * inv;
+        const float v[4] = {o4[0], o4[1], o4[2], o4[3]};
+        store4<T>(a.o_part, pbase * DC + db * 16 + 4 * lgrp, v, 0);
+      }
       if (lgrp == 0) a.lse_part[pbase] = l > 0.f ? mrun[hb] + log2f(l) : -INFINITY;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel for gfx950.  The cache tile goes HBM -> LDS with
-// global_load_lds_dwordx4 (lane i's 16 bytes land at base + 16*i; no staging
-// registers) into a ring of stages, one barrier per tile.  Both contractions
-// read the one row-major copy: the scores with 16-byte row reads, P.V with
-// ds_read_b64_tr_b16, which hands lane i column i of the 4x16 block of 16-bit
-// elements that its 16-lane group addresses (row j>>2, columns 4*(j&3)..+3
-// from lane j).  The running max is only moved when a tile's max exceeds it
-// by more than 8 (log2 units), so the O rescale is rare; the result is the
-// same softmax since numerator and denominator share the reference.
+// bf16 kernel for gfx950 (d_c = 512, d_R = 64).  The cache tile goes HBM ->
+// LDS with global_load_lds_dwordx4 (lane i's 16 bytes land at base + 16*i;
+// no staging registers) into a ring of three stages.  Per tile, two phases
+// separated by a barrier:
+//   A (scores): wave w owns query rows 32w..32w+31 and computes their scores
+//     against the 32 cached rows, S^T = C . Q^T, from 16-byte row reads of the
+//     stage; the softmax is lane-local (each lane holds eight scores of one
+//     query row) plus two shuffles.  The bf16 probabilities go to LDS.
+//   B (P.V): wave w owns latent columns 128w..128w+127 for all 128 query rows:
+//     O^T[d][row] += C_lat^T[d][kv] . P^T[kv][row], with C_lat^T read by
+//     ds_read_b64_tr_b16 (lane i of a 16-lane group receives column i of the
+//     4x16 block of 16-bit elements the group addresses) and P^T from LDS.
+// So each wave reads the tile once as rows and only its own quarter of the
+// latent part transposed.  One wave per SIMD: 512 registers hold the queries
+// of 32 rows and the 128x128 O^T block (in AGPRs).  The softmax reference of a
+// row is the max of its first tile and never moves (no O rescale: numerator
+// and denominator share the reference, so the result is the same softmax);
+// a row whose scores later rise more than 2^32 above it is flagged and
+// recomputed exactly by the combine.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
-constexpr int DECODE_TBL = 256;   // block-table entries a split may span (staged in LDS)
-#ifndef DECODE_NW
-#define DECODE_NW 8               // waves per workgroup; each owns 128/NW query rows
+#ifndef DECODE_PF
+#define DECODE_PF 2               // score steps of cache fragments read ahead
 #endif
+constexpr int DECODE_TBL = 256;   // block-table entries a split may span (staged in LDS)
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) bf16 lds_bf16;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 template <int N>
 __device__ inline void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "");
   __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
 }
+__device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4)); }
 
-template <int DC, int DR, bool PAGED, int NW, int HB>
-__global__ __launch_bounds__(64 * NW, 1) void decode_attn_dma_kernel(DecodeArgs a) {
-  constexpr int D = DC + DR, NT = 64 * NW;
+// HBM -> LDS copy of 16 bytes per lane: lane i's bytes from gbase + off land
+// at LDS address lds + 16*i (lds wave-uniform).  Issued as an asm statement,
+// so the compiler does not see an LDS write that it would order every later
+// LDS read after (with a wait for all loads in flight): the kernels using it
+// wait for their copies themselves (vmcnt, then a barrier) before reading.
+__device__ inline void dma16(const void *gbase, unsigned off, unsigned lds) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(gbase)
+      : "memory", "m0");
+}
+
+// Max over the four 16-lane groups (lanes l, l^16, l^32, l^48) with the
+// gfx950 cross-row swaps (VALU, no LDS round trip).
+__device__ inline float row_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads (those
+// would also wait for the cache copies still in flight).  The empty asm
+// statements keep the compiler from moving LDS accesses across it.
+__device__ inline void bar() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int DC, int DR, bool PAGED>
+__global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
+  constexpr int NW = 4, NT = 64 * NW;
+  constexpr int D = DC + DR;
   constexpr int CH = D / 8;                          // 16-byte chunks per cached row
-  constexpr int PITCH = CH + 1;                      // LDS row pitch in chunks (one pad chunk)
+  constexpr int PITCH = CH + 2;                      // LDS row pitch in chunks (two pad chunks)
   constexpr int LDC = PITCH * 8;                     // ... in elements
   constexpr int LOADS = (KVT * PITCH + NT - 1) / NT; // DMA instructions per wave per tile
   constexpr int STAGE = LOADS * NT * 8;              // elements per stage, including the tail slots
-  constexpr int RUN = D / 4, QS = RUN / 8, DB = DC / 16;
-  constexpr int ROWS = 16 * NW * HB;
-  constexpr float TAU = 8.0f;
-  static_assert(D % 32 == 0 && DC % 16 == 0, "");
+  constexpr int QS = D / 32;                         // 32-wide k steps of the scores
+  constexpr int ROWS = 128;                          // query rows per workgroup
+  constexpr int HA = ROWS / (16 * NW);               // 16-row blocks per wave in the scores
+  constexpr int DW = DC / NW, DBW = DW / 16;         // latent columns per wave in P.V
+  constexpr int HBS = ROWS / 16;                     // 16-row blocks in P.V
+  constexpr int PF = DECODE_PF;                      // score steps read ahead
+  // P = exp2(score - reference) stays below 2^TAU, so P (bf16), l and O (fp32)
+  // keep their range without ever rescaling O
+  constexpr float TAU = 32.0f, MREF0 = -1e30f;
+  static_assert(D % 32 == 0 && DC % (16 * NW) == 0 && QS > PF, "");
 
   // Three stages in three separate LDS objects: reads of one stage are then
   // provably disjoint from the copies in flight into the others, so the
@@ -297,6 +352,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_dma_kernel(DecodeArgs 
   __shared__ __attribute__((aligned(16))) bf16 stage0[STAGE];
   __shared__ __attribute__((aligned(16))) bf16 stage1[STAGE];
   __shared__ __attribute__((aligned(16))) bf16 stage2[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16x8 pbuf[4 * ROWS];   // P[g][row]: keys 4g..+3, 16+4g..+3
+  __shared__ __attribute__((aligned(16))) float fac[ROWS];         // per row: 1/l
   __shared__ int tbl[PAGED ? DECODE_TBL : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -312,7 +369,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_dma_kernel(DecodeArgs 
   if (kv_beg >= len) return;
   const int kv_end = min(len, kv_beg + a.chunk);
   const int R = a.n_q * a.n_h;
-  const int row0 = rg * ROWS + wave * 16 * HB;
+  const int rbase = rg * ROWS;
   const float sl2 = a.scale_log2;
   const bf16 *pool = (const bf16 *)a.cache.pool;
 
@@ -332,7 +389,17 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_dma_kernel(DecodeArgs 
   // DMA of tile t into stage st: every wave issues exactly LOADS instructions;
   // the tail and pad slots fetch a valid chunk into slots nobody reads.  A
   // tile lies inside one cache block (block_size is a multiple of the tile),
-  // so its rows are contiguous: a uniform base plus 32-bit lane offsets.
+  // so its rows are contiguous: a uniform base plus 32-bit lane offsets,
+  // fixed for full tiles; a partial last tile repeats its last row.
+  auto dma_off = [&](int i, int last) {
+    const int sl = i * NT + tid;
+    const int r = sl / PITCH;
+    const int row = min(r, last), ch = min(sl - r * PITCH, CH - 1);
+    return (unsigned)(row * D + ch * 8) * 2u;
+  };
+  unsigned doff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) doff[i] = dma_off(i, KVT - 1);
   auto issue = [&](int t, auto st) {
     const int kvb = kv_beg + t * KVT;
     const int last = min(KVT, kv_end - kvb) - 1;
@@ -347,89 +414,93 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_dma_kernel(DecodeArgs 
     }
     const char *tbase = (const char *)(pool + trow * D);
     bf16 *sbase = (st.value == 0 ? stage0 : st.value == 1 ? stage1 : stage2) + wave * 64 * 8;
+    const unsigned lbase = (unsigned)(size_t)(lds_void *)sbase;
+    if (last == KVT - 1) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int sl = i * NT + tid;
-      const int r = sl / PITCH;
-      const int row = min(r, last), ch = min(sl - r * PITCH, CH - 1);
-      const unsigned off = (unsigned)(row * D + ch * 8) * 2u;
-      __builtin_amdgcn_global_load_lds((const void *)(tbase + off), (lds_void *)(sbase + i * NT * 8), 16, 0, 0);
+      for (int i = 0; i < LOADS; ++i) dma16(tbase, doff[i], lbase + i * NT * 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) dma16(tbase, dma_off(i, last), lbase + i * NT * 16);
     }
   };
 
-  bf16x8 qf[HB][QS];
-  int limit[HB];
+  // score state: this wave's HA blocks of 16 query rows
+  bf16x8 qf[HA][QS];
+  int limit[HA];
+  float mref[HA], lrun[HA];
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const int r = min(row0 + hb * 16 + lrow, R - 1);
-    const bf16 *qrow = (const bf16 *)a.q + ((long)b * R + r) * D + lgrp * RUN;
+  for (int ha = 0; ha < HA; ++ha) {
+    const int r = min(rbase + (wave * HA + ha) * 16 + lrow, R - 1);
+    const bf16 *qrow = (const bf16 *)a.q + ((long)b * R + r) * D + lgrp * 8;
 #pragma unroll
-    for (int q = 0; q < QS; ++q) qf[hb][q] = *(const bf16x8 *)(qrow + q * 8);
-    limit[hb] = min(len - a.n_q + r / a.n_h, kv_end - 1);
+    for (int q = 0; q < QS; ++q) qf[ha][q] = *(const bf16x8 *)(qrow + q * 32);
+    limit[ha] = min(len - a.n_q + r / a.n_h, kv_end - 1);
+    mref[ha] = MREF0;
+    lrun[ha] = 0.f;
   }
-  f32x4 oacc[DB][HB];
+  bool ovf = false;
+
+  // P.V state: O^T for latent columns wave*DW.. and all ROWS rows
+  f32x4 oacc[DBW][HBS];
 #pragma unroll
-  for (int i = 0; i < DB; ++i)
+  for (int i = 0; i < DBW; ++i)
 #pragma unroll
-    for (int j = 0; j < HB; ++j) oacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mref[HB], lrun[HB];
-#pragma unroll
-  for (int j = 0; j < HB; ++j) { mref[j] = -1e30f; lrun[j] = 0.f; }
+    for (int j = 0; j < HBS; ++j) oacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int ntiles = (kv_end - kv_beg + KVT - 1) / KVT;
+  // the queries are in registers before the first copy is issued, so no wait
+  // for them is left inside the loop (where it would also wait for copies)
+  wait_vmcnt<0>();
   issue(0, std::integral_constant<int, 0>());
   if (ntiles > 1) issue(1, std::integral_constant<int, 1>());
-  // Scores use the tile rows in natural order (A slot = row, conflict-free
-  // 16-byte reads): lane group g then holds rows 4g..4g+3 and 16+4g..16+4g+3.
-  // The transposed reads of P.V fetch exactly those rows (any four rows can
-  // form the 4x16 block), so the probabilities stay in registers.
-  const int a_off = lrow * LDC + lgrp * RUN;
-  const int t_off = (4 * lgrp + (lrow >> 2)) * LDC + 4 * (lrow & 3);
+  // Scores use the tile rows in natural order (A slot = row) and natural k
+  // order (lane group g reads dims 32q+8g..+7 of step q): with the 74-chunk
+  // row pitch these 16-byte reads are free of bank conflicts.  Lane group g
+  // then holds the scores of rows 4g..4g+3 and 16+4g..16+4g+3, and the
+  // transposed reads of P.V fetch exactly those rows (any four rows can form
+  // the 4x16 block), so P keeps that key order in LDS.
+  const int a_off = lrow * LDC + lgrp * 8;
+  const int t_off = (4 * lgrp + (lrow >> 2)) * LDC + 4 * (lrow & 3) + wave * DW;
+  lds_bf16x8 *pl = (lds_bf16x8 *)pbuf;
+  float *facl = fac;
 
   // one tile; CUR is the stage holding it (compile-time, see above)
   auto step = [&](int t, auto cur_c) {
     constexpr int CUR = decltype(cur_c)::value;
     if (t + 1 < ntiles) wait_vmcnt<LOADS>();   // tile t+1 may stay in flight
     else wait_vmcnt<0>();
-    // Workgroup barrier without the release/acquire fences of __syncthreads:
-    // this wave's copies of tile t are complete (wait above), and its reads of
-    // the stage about to be refilled were consumed by MFMAs before this point.
-    // The empty asm statements keep the compiler from moving LDS accesses
-    // across the barrier.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    bar();   // tile t landed for every wave; P and stage t-1 are free
     if (t + 2 < ntiles) issue(t + 2, std::integral_constant<int, (CUR + 2) % 3>());
     const lds_bf16 *cur = (const lds_bf16 *)(CUR == 0 ? stage0 : CUR == 1 ? stage1 : stage2);
     const lds_bf16 *ca_p = cur + a_off;
-    lds_v4i16 *tr_p = (lds_v4i16 *)(cur + t_off);
     const int kvb = kv_beg + t * KVT;
 
-    // S^T = C . Q^T; the A fragments of step q+1 are read while step q multiplies
-    f32x4 sacc[2][HB];
+    // ---- scores: S^T = C . Q^T, PF steps of A fragments in flight
+    f32x4 sacc[2][HA];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) sacc[kb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 ca[2][2];
-    ca[0][0] = *(const lds_bf16x8 *)(ca_p);
-    ca[0][1] = *(const lds_bf16x8 *)(ca_p + 16 * LDC);
+      for (int ha = 0; ha < HA; ++ha) sacc[kb][ha] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 ca[PF + 1][2];
+#pragma unroll
+    for (int q = 0; q < PF; ++q) {
+      ca[q][0] = *(const lds_bf16x8 *)(ca_p + q * 32);
+      ca[q][1] = *(const lds_bf16x8 *)(ca_p + 16 * LDC + q * 32);
+    }
 #pragma unroll
     for (int q = 0; q < QS; ++q) {
-      if (q + 1 < QS) {
-        ca[(q + 1) & 1][0] = *(const lds_bf16x8 *)(ca_p + (q + 1) * 8);
-        ca[(q + 1) & 1][1] = *(const lds_bf16x8 *)(ca_p + 16 * LDC + (q + 1) * 8);
+      if (q + PF < QS) {
+        ca[(q + PF) % (PF + 1)][0] = *(const lds_bf16x8 *)(ca_p + (q + PF) * 32);
+        ca[(q + PF) % (PF + 1)][1] = *(const lds_bf16x8 *)(ca_p + 16 * LDC + (q + PF) * 32);
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) sacc[kb][hb] = Mma<bf16>::mma(ca[q & 1][kb], qf[hb][q], sacc[kb][hb]);
+        for (int ha = 0; ha < HA; ++ha) sacc[kb][ha] = Mma<bf16>::mma(ca[q % (PF + 1)][kb], qf[ha][q], sacc[kb][ha]);
       __builtin_amdgcn_sched_barrier(0);
     }
-
-    bf16x8 pf[HB];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
+    for (int ha = 0; ha < HA; ++ha) {
       float sv[2][4];
       float mt = -INFINITY;
 #pragma unroll
@@ -437,47 +508,44 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_dma_kernel(DecodeArgs 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int kv = kvb + 16 * kb + 4 * lgrp + i;
-          const float x = sacc[kb][hb][i] * sl2;
-          sv[kb][i] = (kv <= limit[hb]) ? x : -INFINITY;
+          const float x = sacc[kb][ha][i] * sl2;
+          sv[kb][i] = (kv <= limit[ha]) ? x : -INFINITY;
           mt = fmaxf(mt, sv[kb][i]);
         }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      if (__any(mt > mref[hb] + TAU)) {
-        const float mnew = fmaxf(mref[hb], mt);
-        const float alpha = exp2f(mref[hb] - mnew);
-        mref[hb] = mnew;
-        lrun[hb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db][hb] *= alpha;
-      }
+      // The first tile fixes the reference of each row (max over the four
+      // lane groups that share it).  Later tiles only check, per lane, that
+      // their scores stay within TAU of it; the flags are merged at the end.
+      if (t == 0) mref[ha] = fmaxf(row_max(mt), MREF0);
+      else ovf |= mt > mref[ha] + TAU;
+      bf16x8 pf;
       float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float p = exp2f(sv[j >> 2][j & 3] - mref[hb]);
+        const float p = __builtin_amdgcn_exp2f(sv[j >> 2][j & 3] - mref[ha]);
         psum += p;
-        pf[hb][j] = (bf16)p;
+        pf[j] = (bf16)p;
       }
-      lrun[hb] += psum;
+      lrun[ha] += psum;
+      pl[lgrp * ROWS + (wave * HA + ha) * 16 + lrow] = pf;
     }
+    wait_lgkm0();
+    bar();   // P of every row is in LDS
 
-    // O^T[d][row] += C_lat^T[d][kv] . P^T[kv][row]; C_lat^T is read transposed
-    // out of the row tile, one 16-dim block ahead of its MFMAs
+    // ---- P.V: O^T[d][row] += C_lat^T[d][kv] . P^T[kv][row] for this wave's columns
     constexpr int TRH = 4 * LDC;   // sixteen rows further, in 4-element units
-    v4i16 vt[2][2];
-    vt[0][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(tr_p);
-    vt[0][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(tr_p + TRH);
+    const lds_v4i16 *tr_p = (const lds_v4i16 *)(cur + t_off);
+    bf16x8 va[DBW];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      if (db + 1 < DB) {
-        vt[(db + 1) & 1][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(tr_p + (db + 1) * 4);
-        vt[(db + 1) & 1][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(tr_p + TRH + (db + 1) * 4);
-      }
-      const bf16x8 va =
-          __builtin_bit_cast(bf16x8, __builtin_shufflevector(vt[db & 1][0], vt[db & 1][1], 0, 1, 2, 3, 4, 5, 6, 7));
+    for (int db = 0; db < DBW; ++db) {
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(tr_p + db * 4));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(tr_p + TRH + db * 4));
+      va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) oacc[db][hb] = Mma<bf16>::mma(va, pf[hb], oacc[db][hb]);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int hb = 0; hb < HBS; ++hb) {
+      const bf16x8 pb = pl[lgrp * ROWS + hb * 16 + lrow];
+#pragma unroll
+      for (int db = 0; db < DBW; ++db) oacc[db][hb] = Mma<bf16>::mma(va[db], pb, oacc[db][hb]);
     }
   };
 
@@ -487,27 +555,90 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_dma_kernel(DecodeArgs 
     if (t + 2 < ntiles) step(t + 2, std::integral_constant<int, 2>());
   }
 
+  // normalise and store this split's partial result: the score lanes hold l
+  // and the reference of their rows, the P.V lanes the O columns.  A row
+  // marked in overflow gets lse = NaN; the combine recomputes it exactly.
+  bar();
+  ovf = row_max(ovf ? 1.f : 0.f) > 0.f;
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    float l = lrun[hb];
+  for (int ha = 0; ha < HA; ++ha) {
+    float l = lrun[ha];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    const int r = row0 + hb * 16 + lrow;
-    if (r < R) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      const long pbase = ((long)b * a.n_splits + s) * R + r;
-      float *op = a.o_part + pbase * DC;
+    const int rl = (wave * HA + ha) * 16 + lrow;
+    if (lgrp == 0) {
+      facl[rl] = l > 0.f ? 1.f / l : 0.f;
+      if (rbase + rl < R)
+        a.lse_part[((long)b * a.n_splits + s) * R + rbase + rl] =
+            ovf ? __builtin_nanf("") : l > 0.f ? mref[ha] + log2f(l) : -INFINITY;
+    }
+  }
+  wait_lgkm0();
+  bar();
 #pragma unroll
-      for (int db = 0; db < DB; ++db) *(f32x4 *)(op + db * 16 + 4 * lgrp) = oacc[db][hb] * inv;
-      if (lgrp == 0) a.lse_part[pbase] = l > 0.f ? mref[hb] + log2f(l) : -INFINITY;
+  for (int hb = 0; hb < HBS; ++hb) {
+    const int r = rbase + hb * 16 + lrow;
+    if (r < R) {
+      const float inv = facl[hb * 16 + lrow];
+      bf16 *op = (bf16 *)a.o_part + (((long)b * a.n_splits + s) * R + r) * DC + wave * DW + 4 * lgrp;
+#pragma unroll
+      for (int db = 0; db < DBW; ++db) {
+        const f32x4 o4 = oacc[db][hb] * inv;
+        *(bf16x4 *)(op + db * 16) = bf16x4{(bf16)o4[0], (bf16)o4[1], (bf16)o4[2], (bf16)o4[3]};
+      }
     }
   }
 }
 
+// Exact attention of one query row over its whole sequence, straight from the
+// cache, for rows an attention kernel flagged (lse = NaN): two passes, the
+// first for the max, the second for the sum and the weighted latent rows.
+template <typename T, int DC, int DR>
+__device__ void decode_row_exact(const DecodeArgs &a, int b, int r, int len, T *out) {
+  constexpr int D = DC + DR, PER = (DC + 63) / 64, QP = (D + 63) / 64;
+  const int lane = threadIdx.x & 63;
+  const int R = a.n_q * a.n_h;
+  const T *qrow = (const T *)a.q + ((long)b * R + r) * D;
+  float qv[QP];
+#pragma unroll
+  for (int i = 0; i < QP; ++i) qv[i] = (lane + 64 * i < D) ? to_f32(qrow[lane + 64 * i]) : 0.f;
+  const int limit = min(len - a.n_q + r / a.n_h, len - 1);
+  auto score = [&](const T *crow) {
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < QP; ++i)
+      if (lane + 64 * i < D) dot += qv[i] * to_f32(crow[lane + 64 * i]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+    return dot * a.scale_log2;
+  };
+  float m = -INFINITY;
+  for (int kv = 0; kv <= limit; ++kv) m = fmaxf(m, score((const T *)a.cache.pool + cache_row(a.cache, b, kv) * D));
+  float l = 0.f, acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  for (int kv = 0; kv <= limit; ++kv) {
+    const T *crow = (const T *)a.cache.pool + cache_row(a.cache, b, kv) * D;
+    const float p = exp2f(score(crow) - m);
+    l += p;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (lane + 64 * i < DC) acc[i] += p * to_f32(crow[lane + 64 * i]);
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (lane + 64 * i < DC) out[lane + 64 * i] = from_f32<T>(acc[i] * inv);
+}
+
+template <typename T, int N>
+struct alignas(N * sizeof(T)) Pack { T x[N]; };
+
 // One wave per query row: merge the splits of its sequence.
-template <typename T, int DC>
+template <typename T, int DC, int DR>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-  constexpr int PER = (DC + 63) / 64;
+  static_assert(DC % 64 == 0, "");
+  constexpr int PER = DC / 64;
   const int lane = threadIdx.x & 63;
   const int R = a.n_q * a.n_h;
   const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -516,8 +647,20 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int len = (int)min((long)a.lens[b], min((long)a.n_splits * a.chunk, a.cache.cap));
   const int nsp = len > 0 ? min(a.n_splits, (len + a.chunk - 1) / a.chunk) : 0;
   const long base = (long)b * a.n_splits * R + r;
+  T *out = (T *)a.o_lat + row * DC;
   float lmax = -INFINITY;
-  for (int s = 0; s < nsp; ++s) lmax = fmaxf(lmax, a.lse_part[base + (long)s * R]);
+  bool flagged = false;
+  for (int s = 0; s < nsp; ++s) {
+    const float ls = a.lse_part[base + (long)s * R];
+    flagged |= ls != ls;
+    lmax = fmaxf(lmax, ls);
+  }
+  if (flagged) {
+    decode_row_exact<T, DC, DR>(a, b, r, len, out);
+    return;
+  }
+  // lane owns PER consecutive latent columns (one 16-byte load per split for
+  // bf16 and d_c = 512)
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
@@ -526,20 +669,16 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     const float ls = a.lse_part[base + (long)s * R];
     const float w = (ls == -INFINITY) ? 0.f : exp2f(ls - lmax);
     wsum += w;
-    const float *op = a.o_part + (base + (long)s * R) * DC;
+    const T *op = (const T *)a.o_part + (base + (long)s * R) * DC + lane * PER;
+    const Pack<T, PER> v = *(const Pack<T, PER> *)op;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int d = lane + 64 * i;
-      if (d < DC) acc[i] += w * op[d];
-    }
+    for (int i = 0; i < PER; ++i) acc[i] += w * to_f32(v.x[i]);
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  T *out = (T *)a.o_lat + row * DC;
+  Pack<T, PER> o;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int d = lane + 64 * i;
-    if (d < DC) out[d] = from_f32<T>(acc[i] * inv);
-  }
+  for (int i = 0; i < PER; ++i) o.x[i] = from_f32<T>(acc[i] * inv);
+  *(Pack<T, PER> *)(out + lane * PER) = o;
 }
 
 int decode_kv_tile(int) { return KVT; }
@@ -561,11 +700,10 @@ hipError_t launch_decode_attn(int dtype, const DecodeArgs &a, hipStream_t st) {
     const int units = a.B * a.n_splits;
     const int grid = ((units + 7) / 8) * 8 * a.row_groups;
     timing_before("decode_attn", st);
-    constexpr int NW = DECODE_NW, HB = 8 / DECODE_NW;
     if (a.cache.table)
-      hipLaunchKernelGGL((decode_attn_dma_kernel<512, 64, true, NW, HB>), dim3(grid), dim3(64 * NW), 0, st, a);
+      hipLaunchKernelGGL((decode_attn_dma_kernel<512, 64, true>), dim3(grid), dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((decode_attn_dma_kernel<512, 64, false, NW, HB>), dim3(grid), dim3(64 * NW), 0, st, a);
+      hipLaunchKernelGGL((decode_attn_dma_kernel<512, 64, false>), dim3(grid), dim3(256), 0, st, a);
     timing_after("decode_attn", st);
     return hipGetLastError();
   }
@@ -578,8 +716,10 @@ hipError_t launch_decode_combine(int dtype, const DecodeArgs &a, hipStream_t st)
   const long rows = (long)a.B * a.n_q * a.n_h;
   dim3 grid((unsigned)((rows + 3) / 4));
   timing_before("decode_combine", st);
-  if (dtype == 1 && a.d_c == 512) hipLaunchKernelGGL((decode_combine_kernel<bf16, 512>), grid, dim3(256), 0, st, a);
-  else if (dtype == 0 && a.d_c == 64) hipLaunchKernelGGL((decode_combine_kernel<float, 64>), grid, dim3(256), 0, st, a);
+  if (dtype == 1 && a.d_c == 512 && a.d_rope == 64)
+    hipLaunchKernelGGL((decode_combine_kernel<bf16, 512, 64>), grid, dim3(256), 0, st, a);
+  else if (dtype == 0 && a.d_c == 64 && a.d_rope == 16)
+    hipLaunchKernelGGL((decode_combine_kernel<float, 64, 16>), grid, dim3(256), 0, st, a);
   else return hipErrorInvalidValue;
   timing_after("decode_combine", st);
   return hipGetLastError();

@@ -175,7 +175,7 @@ DecodePlan plan_decode(const mla_config *c, int32_t B, int32_t n_q, int32_t max_
   p.c_q = take((size_t)T * c->d_cq * e);
   p.q_nope = take((size_t)T * c->n_heads * c->d_nope * e);
   p.q_abs = take((size_t)T * c->n_heads * D * e);
-  p.o_part = take((size_t)B * p.splits * R * c->d_c * 4);
+  p.o_part = take((size_t)B * p.splits * R * c->d_c * e);
   p.lse = take((size_t)B * p.splits * R * 4);
   p.o_lat = take((size_t)T * c->n_heads * c->d_c * e);
   p.o = take((size_t)T * c->n_heads * c->d_v * e);
@@ -554,7 +554,7 @@ mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h
   d.chunk = p.chunk;
   d.n_splits = p.splits;
   d.row_groups = p.row_groups;
-  d.o_part = (float *)(ws + p.o_part);
+  d.o_part = ws + p.o_part;
   d.lse_part = (float *)(ws + p.lse);
   d.o_lat = ws + p.o_lat;
   e = launch_decode_attn(dt == MLA_BF16, d, st);

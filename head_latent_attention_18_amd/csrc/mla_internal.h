@@ -228,7 +228,7 @@ struct FlashArgs {
 hipError_t launch_flash_prefill(int dtype, const FlashArgs &a, hipStream_t st);
 
 struct DecodeArgs {
-  const void *q;      // q_abs [B*n_q][n_h][d_c + d_rope], softmax scale folded in
+  const void *q;      // absorbed queries [B*n_q][n_h][d_c + d_rope]
   CacheRef cache;
   const int *lens;    // [B]
   int B, n_q, n_h, d_c, d_rope;
@@ -236,8 +236,8 @@ struct DecodeArgs {
   int chunk;          // kv rows per split (multiple of the kv tile)
   int n_splits;       // splits per sequence in the grid
   int row_groups;     // groups of query rows (n_q*n_h rows per sequence)
-  float *o_part;      // [B][n_splits][n_q*n_h][d_c]
-  float *lse_part;    // [B][n_splits][n_q*n_h]  (log2 units)
+  void *o_part;       // [B][n_splits][n_q*n_h][d_c], normalised, in the layer's dtype
+  float *lse_part;    // [B][n_splits][n_q*n_h]  (log2 units; NaN = recompute the row)
   void *o_lat;        // combine output [B*n_q][n_h][d_c]
 };
 int decode_rows_per_group(int dtype);

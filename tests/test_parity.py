@@ -125,3 +125,31 @@ def test_dsv3_decode_ragged_paged_small(block_size):
     for b in range(wl.batch):
         ref = oracle_decode_seq(wl, b)
         assert_close(u[b], ref["u"], True, f"u b={b} len={wl.lens[b]}")
+
+
+def test_dsv3_decode_large_logit_spread():
+    """Cached rows scaled by 64 late in a split: their scores exceed the
+    split's first-tile reference by far more than the kernel's fixed-reference
+    range, so those query rows take the exact recomputation path; all rows
+    still match the oracle."""
+    from mla_inputs import bf16_bits_to_f32, bf16_round
+    wl = make_workload(2, batch=32, uniform_len=300)
+    for b, pos, src in ((0, 40, 3), (5, 100, 7), (9, 250, 2)):
+        big = bf16_round(bf16_bits_to_f32(wl.cache_bits[b][src]) * 64.0)
+        wl.cache_bits[b][pos] = big
+        wl.cache_f32[b][pos] = bf16_bits_to_f32(big)
+    layer = layer_for(wl)
+    cache = decode_cache(wl, layer)
+    say("decode with large logit spread B=32 L=300")
+    u, o = run_decode(wl, layer, cache)
+    d = wl.dims
+    from tests.gpu_harness import BF16_MAX_ABS, BF16_REL_FROB, err
+    for b in (0, 5, 9, 1):
+        ref = oracle_decode_seq(wl, b)
+        for what, got, r in (("u", u[b], ref["u"]), ("o", o.view(wl.batch, 1, d.n_heads, d.d_v)[b], ref["o"])):
+            # the scaled rows raise the outputs' magnitude, so the max-abs
+            # bound is taken relative to max(1, max|oracle|)
+            e = err(got, r)
+            mag = max(1.0, float(np.max(np.abs(r))))
+            say(f"{what} b={b}: max_abs={e.max_abs:.3e} (max|ref|={mag:.1f}) rel_frob={e.rel_frob:.3e}")
+            assert e.rel_frob <= BF16_REL_FROB and e.max_abs <= BF16_MAX_ABS * mag, (what, b, e)
