@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
   constexpr int CH = D / 8;                          // 16-byte chunks per cached row
   constexpr int PITCH = CH + 2;                      // LDS row pitch in chunks (two pad chunks)
   constexpr int LDC = PITCH * 8;                     // ... in elements
-  constexpr int LOADS = (KVT * PITCH + NT - 1) / NT; // DMA instructions per wave per tile
+  constexpr int LOADS = (KVT * PITCH + NT - 1) / NT; // copy instructions per wave per tile
   constexpr int STAGE = LOADS * NT * 8;              // elements per stage, including the tail slots
   constexpr int QS = D / 32;                         // 32-wide k steps of the scores
   constexpr int ROWS = 128;                          // query rows per workgroup
@@ -341,19 +341,15 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
   constexpr int DW = DC / NW, DBW = DW / 16;         // latent columns per wave in P.V
   constexpr int HBS = ROWS / 16;                     // 16-row blocks in P.V
   constexpr int PF = DECODE_PF;                      // score steps read ahead
+  constexpr int PVS = HBS - 2;                       // P.V row blocks interleaved with the scores
   // P = exp2(score - reference) stays below 2^TAU, so P (bf16), l and O (fp32)
   // keep their range without ever rescaling O
   constexpr float TAU = 32.0f, MREF0 = -1e30f;
-  static_assert(D % 32 == 0 && DC % (16 * NW) == 0 && QS > PF, "");
+  static_assert(D % 32 == 0 && DC % (16 * NW) == 0 && QS > PF && QS >= 2 * PVS, "");
 
-  // Three stages in three separate LDS objects: reads of one stage are then
-  // provably disjoint from the copies in flight into the others, so the
-  // compiler adds no wait for those copies before the reads.
-  __shared__ __attribute__((aligned(16))) bf16 stage0[STAGE];
-  __shared__ __attribute__((aligned(16))) bf16 stage1[STAGE];
-  __shared__ __attribute__((aligned(16))) bf16 stage2[STAGE];
-  __shared__ __attribute__((aligned(16))) bf16x8 pbuf[4 * ROWS];   // P[g][row]: keys 4g..+3, 16+4g..+3
-  __shared__ __attribute__((aligned(16))) float fac[ROWS];         // per row: 1/l
+  __shared__ __attribute__((aligned(16))) bf16 stages[3 * STAGE];
+  __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2 * 4 * ROWS];   // P[buf][g][row]
+  __shared__ __attribute__((aligned(16))) float fac[ROWS];             // per row: 1/l
   __shared__ int tbl[PAGED ? DECODE_TBL : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -385,12 +381,13 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
     __syncthreads();
   }
   const long seq_row0 = (long)b * a.cache.max_len;
+  const unsigned lds_stages = (unsigned)(size_t)(lds_void *)stages;
 
-  // DMA of tile t into stage st: every wave issues exactly LOADS instructions;
-  // the tail and pad slots fetch a valid chunk into slots nobody reads.  A
-  // tile lies inside one cache block (block_size is a multiple of the tile),
-  // so its rows are contiguous: a uniform base plus 32-bit lane offsets,
-  // fixed for full tiles; a partial last tile repeats its last row.
+  // Copy of tile t into stage t % 3: every wave issues exactly LOADS
+  // instructions; the tail and pad slots fetch a valid chunk into slots nobody
+  // reads.  A tile lies inside one cache block (block_size is a multiple of
+  // the tile), so its rows are contiguous: a uniform base plus 32-bit lane
+  // offsets, fixed for full tiles; a partial last tile repeats its last row.
   auto dma_off = [&](int i, int last) {
     const int sl = i * NT + tid;
     const int r = sl / PITCH;
@@ -400,7 +397,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
   unsigned doff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) doff[i] = dma_off(i, KVT - 1);
-  auto issue = [&](int t, auto st) {
+  auto issue = [&](int t) {
     const int kvb = kv_beg + t * KVT;
     const int last = min(KVT, kv_end - kvb) - 1;
     long trow;
@@ -413,14 +410,22 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
       trow = seq_row0 + kvb;
     }
     const char *tbase = (const char *)(pool + trow * D);
-    bf16 *sbase = (st.value == 0 ? stage0 : st.value == 1 ? stage1 : stage2) + wave * 64 * 8;
-    const unsigned lbase = (unsigned)(size_t)(lds_void *)sbase;
+    const unsigned lbase = lds_stages + (unsigned)((t % 3) * STAGE * 2) + wave * 64 * 16;
     if (last == KVT - 1) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) dma16(tbase, doff[i], lbase + i * NT * 16);
     } else {
+      // rare partial tile: offsets recomputed here (an opaque copy of the lane
+      // index keeps the compiler from holding them in registers all along)
+      int ot = tid;
+      asm volatile("" : "+v"(ot));
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) dma16(tbase, dma_off(i, last), lbase + i * NT * 16);
+      for (int i = 0; i < LOADS; ++i) {
+        const int sl = i * NT + ot;
+        const int r = sl / PITCH;
+        const int row = min(r, last), ch = min(sl - r * PITCH, CH - 1);
+        dma16(tbase, (unsigned)(row * D + ch * 8) * 2u, lbase + i * NT * 16);
+      }
     }
   };
 
@@ -451,8 +456,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
   // the queries are in registers before the first copy is issued, so no wait
   // for them is left inside the loop (where it would also wait for copies)
   wait_vmcnt<0>();
-  issue(0, std::integral_constant<int, 0>());
-  if (ntiles > 1) issue(1, std::integral_constant<int, 1>());
+  issue(0);
   // Scores use the tile rows in natural order (A slot = row) and natural k
   // order (lane group g reads dims 32q+8g..+7 of step q): with the 74-chunk
   // row pitch these 16-byte reads are free of bank conflicts.  Lane group g
@@ -461,21 +465,35 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
   // the 4x16 block), so P keeps that key order in LDS.
   const int a_off = lrow * LDC + lgrp * 8;
   const int t_off = (4 * lgrp + (lrow >> 2)) * LDC + 4 * (lrow & 3) + wave * DW;
+  constexpr int TRH = 4 * LDC;   // sixteen rows further, in 4-element units
+  const lds_bf16 *st_base = (const lds_bf16 *)stages;
   lds_bf16x8 *pl = (lds_bf16x8 *)pbuf;
-  float *facl = fac;
 
-  // one tile; CUR is the stage holding it (compile-time, see above)
-  auto step = [&](int t, auto cur_c) {
-    constexpr int CUR = decltype(cur_c)::value;
-    if (t + 1 < ntiles) wait_vmcnt<LOADS>();   // tile t+1 may stay in flight
-    else wait_vmcnt<0>();
-    bar();   // tile t landed for every wave; P and stage t-1 are free
-    if (t + 2 < ntiles) issue(t + 2, std::integral_constant<int, (CUR + 2) % 3>());
-    const lds_bf16 *cur = (const lds_bf16 *)(CUR == 0 ? stage0 : CUR == 1 ? stage1 : stage2);
-    const lds_bf16 *ca_p = cur + a_off;
+  // P.V of tile u (stage u % 3, P buffer u & 1) for row blocks [h0, h1); the
+  // V^T fragments of the wave's columns are read once per tile
+  bf16x8 va[DBW];
+  auto load_v = [&](int u) {
+    const lds_v4i16 *tr_p = (const lds_v4i16 *)(st_base + (u % 3) * STAGE + t_off);
+#pragma unroll
+    for (int db = 0; db < DBW; ++db) {
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(tr_p + db * 4));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(tr_p + TRH + db * 4));
+      va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  auto pv_block = [&](int u, int hb) {
+    const bf16x8 pb = pl[((u & 1) * 4 + lgrp) * ROWS + hb * 16 + lrow];
+#pragma unroll
+    for (int db = 0; db < DBW; ++db) oacc[db][hb] = Mma<bf16>::mma(va[db], pb, oacc[db][hb]);
+  };
+
+  // scores and softmax of tile t (stage t % 3) into P buffer t & 1; when
+  // WITH_PV, the P.V of tile t-1 is interleaved: row blocks 0..PVS-1 between
+  // the score steps, the last two with the softmax
+  auto scores = [&](int t, auto with_pv_c) {
+    constexpr bool WITH_PV = decltype(with_pv_c)::value;
+    const lds_bf16 *ca_p = st_base + (t % 3) * STAGE + a_off;
     const int kvb = kv_beg + t * KVT;
-
-    // ---- scores: S^T = C . Q^T, PF steps of A fragments in flight
     f32x4 sacc[2][HA];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -497,6 +515,9 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int ha = 0; ha < HA; ++ha) sacc[kb][ha] = Mma<bf16>::mma(ca[q % (PF + 1)][kb], qf[ha][q], sacc[kb][ha]);
+      if constexpr (WITH_PV) {
+        if (q % 2 == 1 && q / 2 < PVS) pv_block(t - 1, q / 2);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -526,39 +547,36 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
         pf[j] = (bf16)p;
       }
       lrun[ha] += psum;
-      pl[lgrp * ROWS + (wave * HA + ha) * 16 + lrow] = pf;
-    }
-    wait_lgkm0();
-    bar();   // P of every row is in LDS
-
-    // ---- P.V: O^T[d][row] += C_lat^T[d][kv] . P^T[kv][row] for this wave's columns
-    constexpr int TRH = 4 * LDC;   // sixteen rows further, in 4-element units
-    const lds_v4i16 *tr_p = (const lds_v4i16 *)(cur + t_off);
-    bf16x8 va[DBW];
-#pragma unroll
-    for (int db = 0; db < DBW; ++db) {
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(tr_p + db * 4));
-      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(tr_p + TRH + db * 4));
-      va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-#pragma unroll
-    for (int hb = 0; hb < HBS; ++hb) {
-      const bf16x8 pb = pl[lgrp * ROWS + hb * 16 + lrow];
-#pragma unroll
-      for (int db = 0; db < DBW; ++db) oacc[db][hb] = Mma<bf16>::mma(va[db], pb, oacc[db][hb]);
+      pl[((t & 1) * 4 + lgrp) * ROWS + (wave * HA + ha) * 16 + lrow] = pf;
+      if constexpr (WITH_PV) pv_block(t - 1, PVS + ha);
     }
   };
 
-  for (int t = 0; t < ntiles; t += 3) {
-    step(t, std::integral_constant<int, 0>());
-    if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>());
-    if (t + 2 < ntiles) step(t + 2, std::integral_constant<int, 2>());
+  // Iteration i: tile i has landed; the copy of tile i+1 goes out; the scores
+  // of tile i run with the P.V of tile i-1 (whose P every wave wrote in
+  // iteration i-1).  One barrier per iteration: it also retires stage (i-1)%3
+  // reads before the copy into stage (i+1)%3 = (i-2)%3 ... of the next one.
+  auto sync = [&](int i) {
+    wait_vmcnt<0>();   // this wave's copies of tile i
+    wait_lgkm0();      // this wave's P of tile i-1
+    bar();
+    if (i + 1 < ntiles) issue(i + 1);
+  };
+  sync(0);
+  scores(0, std::false_type());
+  for (int i = 1; i < ntiles; ++i) {
+    sync(i);
+    load_v(i - 1);
+    scores(i, std::true_type());
   }
+  sync(ntiles);
+  load_v(ntiles - 1);
+#pragma unroll
+  for (int hb = 0; hb < HBS; ++hb) pv_block(ntiles - 1, hb);
 
   // normalise and store this split's partial result: the score lanes hold l
   // and the reference of their rows, the P.V lanes the O columns.  A row
   // marked in overflow gets lse = NaN; the combine recomputes it exactly.
-  bar();
   ovf = row_max(ovf ? 1.f : 0.f) > 0.f;
 #pragma unroll
   for (int ha = 0; ha < HA; ++ha) {
@@ -567,19 +585,18 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
     l += __shfl_xor(l, 32);
     const int rl = (wave * HA + ha) * 16 + lrow;
     if (lgrp == 0) {
-      facl[rl] = l > 0.f ? 1.f / l : 0.f;
+      fac[rl] = l > 0.f ? 1.f / l : 0.f;
       if (rbase + rl < R)
         a.lse_part[((long)b * a.n_splits + s) * R + rbase + rl] =
             ovf ? __builtin_nanf("") : l > 0.f ? mref[ha] + log2f(l) : -INFINITY;
     }
   }
-  wait_lgkm0();
-  bar();
+  __syncthreads();
 #pragma unroll
   for (int hb = 0; hb < HBS; ++hb) {
     const int r = rbase + hb * 16 + lrow;
     if (r < R) {
-      const float inv = facl[hb * 16 + lrow];
+      const float inv = fac[hb * 16 + lrow];
       bf16 *op = (bf16 *)a.o_part + (((long)b * a.n_splits + s) * R + r) * DC + wave * DW + 4 * lgrp;
 #pragma unroll
       for (int db = 0; db < DBW; ++db) {
