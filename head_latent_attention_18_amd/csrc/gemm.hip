@@ -443,6 +443,7 @@ hipError_t launch_gemm(int dtype, int tile, int swap, int wkn, GemmArgs &a, hipS
       if (!swap && !wkn) return launch_t<bf16, BIG_BM, BIG_BN, BIG_BK, BIG_WM, BIG_WN, false, false>(a, st, "gemm_bf16_big_t");
       if (swap && wkn) return launch_t<bf16, 128, 128, 64, 2, 2, true, true>(a, st, "gemm_bf16_128x128_kn");
     } else {
+      if (swap && gemm_stream_ok(a, wkn)) return launch_gemm_stream(a, wkn, st);
       if (swap && !wkn) {
         if (a.M <= 32 && a.k_chunk % 256 == 0 && skinny_nst_supported(a.k_chunk / 256))
           return launch_skinny<2, 256>(a, st, "gemm_bf16_stream_m32");

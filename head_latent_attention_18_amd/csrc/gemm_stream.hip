@@ -1,0 +1,299 @@
+// Weight-streaming GEMM for few tokens (bf16, up to 64 rows of activations):
+// Y[z][m][n] = sum_k X[z][m][k] W[z][n][k]   (W stored [N][K]: the down/up
+// projections, W_UV and W_O), or W stored [K][N] (W_UK in the absorption).
+//
+// With 32 tokens every weight element feeds two MFMAs, so these products are
+// bound by streaming the weights from HBM.  The kernel is built for that:
+//   * the work is a flat list of units (matrix z, 64-row weight tile t,
+//     128-wide k step j) of 16 KB of weights each; a persistent grid of
+//     workgroups takes equal contiguous ranges of it (no tail wave);
+//   * weights and the matching activation slice go HBM -> LDS with
+//     global_load_lds_dwordx4 into a ring of stages, whole rows per
+//     instruction (coalesced), several units ahead;
+//   * LDS rows are 16 chunks of 16 bytes with the chunk index XORed by the
+//     row (no padding, no bank conflicts for the 16-row MFMA reads);
+//   * a tile finished inside one workgroup goes straight through the
+//     epilogue; a tile shared by several leaves fp32 partials that the reduce
+//     kernel adds up in workgroup order (deterministic).
+#include "mla_internal.h"
+
+namespace mla {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) bf16 lds_bf16;
+
+constexpr int SBN = 64;          // weight rows (output features) per tile
+constexpr int SBK = 128;         // k per unit
+constexpr int SNT = 256;         // threads per workgroup
+constexpr int MAX_PARTS = 16;    // workgroups that may share one tile
+
+// ring stages: as many units in flight as LDS holds (24 KB per unit at 32 rows)
+template <int MB> constexpr int stream_stages() { return MB <= 2 ? 6 : 4; }
+
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+}
+
+// 16 bytes per lane HBM -> LDS (lane i lands at lds + 16*i).  An asm
+// statement: the compiler sees no LDS write to order later reads after; the
+// kernel waits for its copies itself (vmcnt, then a barrier).
+__device__ inline void dma16(const void *gbase, unsigned off, unsigned lds) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(gbase)
+      : "memory", "m0");
+}
+
+__device__ inline void bar() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// first unit of workgroup b out of G over U units (U * G < 2^31, checked on the host)
+__device__ __host__ inline int unit_start(int b, int U, int G) { return b * U / G; }
+// workgroup holding unit u
+__device__ __host__ inline int unit_owner(int u, int U, int G) { return ((u + 1) * G - 1) / U; }
+
+}  // namespace
+
+// MB: 16-row blocks of activations (M <= 16*MB).  WKN: W stored [K][N].
+template <int MB, bool WKN>
+__global__ __launch_bounds__(SNT, 1) void gemm_stream_kernel(GemmArgs a) {
+  constexpr int SNS = stream_stages<MB>();
+  constexpr int WCH = SBN * SBK / 8;                // weight chunks per unit (1024)
+  constexpr int XCH = 16 * MB * SBK / 8;            // activation chunks per unit
+  constexpr int WLD = WCH / SNT, XLD = XCH / SNT;   // copy instructions per unit
+  constexpr int LOADS = WLD + XLD;
+  constexpr int STAGE = (WCH + XCH) * 8;            // elements per stage
+  static_assert(WCH % SNT == 0 && XCH % SNT == 0 && LOADS * (SNS - 2) < 64, "");
+  __shared__ __attribute__((aligned(16))) bf16 ring[SNS * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  const int KS = a.K / SBK;                         // units per tile
+  const int U = a.batch * a.tiles_n * KS;
+  const int G = gridDim.x;
+  const int u0 = unit_start(blockIdx.x, U, G), u1 = unit_start(blockIdx.x + 1, U, G);
+  const int nu = u1 - u0;
+  if (nu <= 0) return;
+  const unsigned lring = (unsigned)(size_t)(lds_void *)ring;
+
+  // copy of unit u into stage st
+  auto issue = [&](int u, int st) {
+    const int tt = u / KS;
+    const int j = u - tt * KS;
+    const int z = tt / a.tiles_n, t = tt - z * a.tiles_n;
+    const int n0 = t * SBN, k0 = j * SBK;
+    const unsigned lst = lring + (unsigned)(st * STAGE * 2) + wave * 1024;
+    // weights
+    if constexpr (!WKN) {
+      int seg = 0, beg = 0;
+      while (seg < a.nw - 1 && n0 >= a.w_end[seg]) { beg = a.w_end[seg]; ++seg; }
+      const char *wb = (const char *)((const bf16 *)a.w[seg] + (long)z * a.w_bs + (long)(n0 - beg) * a.ldw + k0);
+      const int rows = min(SBN, a.w_end[seg] - n0);
+#pragma unroll
+      for (int i = 0; i < WLD; ++i) {
+        const int s = i * SNT + tid, r = s >> 4, pc = s & 15;
+        const unsigned off = (unsigned)(min(r, rows - 1) * a.ldw + ((pc ^ (r & 15)) << 3)) * 2u;
+        dma16(wb, off, lst + i * SNT * 16);
+      }
+    } else {
+      const char *wb = (const char *)((const bf16 *)a.w[0] + (long)z * a.w_bs + (long)k0 * a.ldw + n0);
+#pragma unroll
+      for (int i = 0; i < WLD; ++i) {
+        const int s = i * SNT + tid, kr = s >> 3, pc = s & 7;
+        const unsigned off = (unsigned)(kr * a.ldw + ((pc ^ (kr & 7)) << 3)) * 2u;
+        dma16(wb, off, lst + i * SNT * 16);
+      }
+    }
+    // activations
+    const char *xb = (const char *)((const bf16 *)a.x + (long)z * a.x_bs + k0);
+#pragma unroll
+    for (int i = 0; i < XLD; ++i) {
+      const int s = i * SNT + tid, r = s >> 4, pc = s & 15;
+      const unsigned off = (unsigned)(min(r, a.M - 1) * a.ldx + ((pc ^ (r & 15)) << 3)) * 2u;
+      dma16(xb, off, lst + (WLD + i) * SNT * 16);
+    }
+  };
+
+  f32x4 acc[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const lds_bf16 *rl = (const lds_bf16 *)ring;
+  const int first_tile = u0 / KS;
+
+  // store (or leave as a partial) the tile of unit u, which ends here
+  auto flush = [&](int u) {
+    const int tt = u / KS;
+    const int z = tt / a.tiles_n, t = tt - z * a.tiles_n;
+    const bool whole = tt * KS >= u0 && (tt + 1) * KS <= u1;
+    const int nn = t * SBN + wave * 16 + 4 * lgrp;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = mb * 16 + lrow;
+      if (m < a.M && nn < a.N) {
+        float v[4] = {acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]};
+        if (whole) {
+          epi_store4<bf16>(a.epi, z, m, nn, v);
+        } else {
+          const int slot = tt == first_tile ? 0 : 1;
+          float *p = a.partial + (((long)blockIdx.x * 2 + slot) * 16 * MB + m) * SBN + wave * 16 + 4 * lgrp;
+          *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
+        }
+      }
+      acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  for (int i = 0; i < SNS - 1 && i < nu; ++i) issue(u0 + i, i);
+  for (int k = 0; k < nu; ++k) {
+    if (k + SNS - 2 < nu) wait_vm<LOADS * (SNS - 2)>();
+    else wait_vm<0>();
+    bar();   // unit k landed for every wave; stage (k-1) % SNS is free
+    if (k + SNS - 1 < nu) issue(u0 + k + SNS - 1, (k + SNS - 1) % SNS);
+    const lds_bf16 *ws = rl + (k % SNS) * STAGE;
+    const lds_bf16 *xs = ws + WCH * 8;
+#pragma unroll
+    for (int s = 0; s < SBK / 32; ++s) {
+      const int c = 4 * s + lgrp;                  // logical 16-byte chunk of the k step
+      bf16x8 wf;
+      if constexpr (!WKN) {
+        const int r = wave * 16 + lrow;
+        wf = *(const lds_bf16x8 *)(ws + (r * 16 + (c ^ (r & 15))) * 8);
+      } else {
+        // W^T fragment: k = 32s + 8*lgrp + 0..7 for feature wave*16 + lrow,
+        // two transposed 4x16 reads of the [k][n] tile
+        const int kr = 32 * s + 8 * lgrp + (lrow >> 2);
+        const int col = wave * 16 + 4 * (lrow & 3);        // element column
+        const int ch = col >> 3, half = col & 7;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16 *)(ws + (kr * 8 + (ch ^ (kr & 7))) * 8 + half));
+        const int kr2 = kr + 4;
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16 *)(ws + (kr2 * 8 + (ch ^ (kr2 & 7))) * 8 + half));
+        wf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int r = mb * 16 + lrow;
+        const bf16x8 xf = *(const lds_bf16x8 *)(xs + (r * 16 + (c ^ (r & 15))) * 8);
+        acc[mb] = Mma<bf16>::mma(wf, xf, acc[mb]);
+      }
+    }
+    const int u = u0 + k;
+    if ((u + 1) % KS == 0 || k == nu - 1) flush(u);
+  }
+}
+
+// Sum the partials of tiles shared by several workgroups, in workgroup order,
+// then the epilogue.  One thread per (tile, row, 4 columns); all partial loads
+// are issued before the sum.
+template <int MB>
+__global__ __launch_bounds__(256) void gemm_stream_reduce_kernel(GemmArgs a, int G) {
+  const int KS = a.K / SBK;
+  const int U = a.batch * a.tiles_n * KS;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int per_tile = a.M * (SBN / 4);
+  const int tt = idx / per_tile;
+  if (tt >= a.batch * a.tiles_n) return;
+  const int rem = idx - tt * per_tile;
+  const int m = rem / (SBN / 4), c4 = (rem % (SBN / 4)) * 4;
+  const int bf = unit_owner(tt * KS, U, G), bl = unit_owner((tt + 1) * KS - 1, U, G);
+  if (bf == bl) return;   // stored by its only workgroup
+  const int z = tt / a.tiles_n, t = tt - z * a.tiles_n;
+  const int n = t * SBN + c4;
+  if (n >= a.N) return;
+  // the first contributor holds the tile as its last one (slot 1) unless the
+  // tile is also its first; every later contributor starts with it (slot 0)
+  const int slot0 = unit_start(bf, U, G) / KS == tt ? 0 : 1;
+  f32x4 v[MAX_PARTS];
+#pragma unroll
+  for (int i = 0; i < MAX_PARTS; ++i)
+    if (bf + i <= bl) {
+      const int b = bf + i, slot = i == 0 ? slot0 : 0;
+      v[i] = *(const f32x4 *)(a.partial + ((b * 2 + slot) * 16 * MB + m) * SBN + c4);
+    }
+  f32x4 s = v[0];
+#pragma unroll
+  for (int i = 1; i < MAX_PARTS; ++i)
+    if (bf + i <= bl) s += v[i];
+  float o[4] = {s[0], s[1], s[2], s[3]};
+  epi_store4<bf16>(a.epi, z, m, n, o);
+}
+
+int gemm_stream_grid() { return 256; }
+
+size_t gemm_stream_partial_bytes(int M) {
+  const int mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+  return (size_t)gemm_stream_grid() * 2 * 16 * mb * SBN * sizeof(float);
+}
+
+bool gemm_stream_ok(const GemmArgs &a, int wkn) {
+  // Long products only: the ring's fill and drain cost a few microseconds,
+  // which shorter weight streams (q_up, W_UK, W_UV) do not amortise; those
+  // keep the register-streaming kernels.
+  if (wkn || a.K < 4096) return false;
+  if (a.M > 64 || a.K % SBK != 0 || !a.partial) return false;
+  const long units = (long)a.batch * ((a.N + SBN - 1) / SBN) * (a.K / SBK);
+  if (units * gemm_stream_grid() >= (1L << 31)) return false;
+  // a tile is shared by at most MAX_PARTS workgroups
+  const long per = std::max<long>(1, units / gemm_stream_grid()), ks = a.K / SBK;
+  if (ks / per + 2 > MAX_PARTS) return false;
+  if (wkn) return a.N % SBN == 0 && a.nw == 1;
+  for (int s = 0; s < a.nw - 1; ++s)
+    if (a.w_end[s] % SBN != 0) return false;   // a tile never straddles two weight segments
+  return true;
+}
+
+// Workgroups: whole tiles per workgroup when that keeps at least 3/4 of the
+// CUs busy (no partials, no reduce); otherwise an even split of the units.
+static int stream_grid_for(int U, int KS, int tiles) {
+  const int full = gemm_stream_grid();
+  if (U <= full) return U;
+  for (int g = full; g * 4 >= full * 3; --g)
+    if (tiles % g == 0) return g;
+  return full;
+}
+
+template <int MB, bool WKN>
+static hipError_t launch_stream_t(GemmArgs &a, hipStream_t st) {
+  a.tiles_m = 1;
+  a.tiles_n = (a.N + SBN - 1) / SBN;
+  const int KS = a.K / SBK;
+  const int tiles = a.batch * a.tiles_n;
+  const int U = tiles * KS;
+  const int G = stream_grid_for(U, KS, tiles);
+  timing_before(a.name ? a.name : "gemm_stream", st);
+  hipLaunchKernelGGL((gemm_stream_kernel<MB, WKN>), dim3(G), dim3(SNT), 0, st, a);
+  timing_after(a.name ? a.name : "gemm_stream", st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bool split = false;   // does a workgroup boundary fall inside a tile?
+  for (int b = 1; b < G && !split; ++b) split = unit_start(b, U, G) % KS != 0;
+  if (!split) return hipSuccess;
+  const long total = (long)tiles * a.M * (SBN / 4);
+  const char *rn = a.reduce_name ? a.reduce_name : "gemm_stream.reduce";
+  timing_before(rn, st);
+  hipLaunchKernelGGL((gemm_stream_reduce_kernel<MB>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a, G);
+  timing_after(rn, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_stream(GemmArgs &a, int wkn, hipStream_t st) {
+  if (a.M <= 16) return wkn ? launch_stream_t<1, true>(a, st) : launch_stream_t<1, false>(a, st);
+  if (a.M <= 32) return wkn ? launch_stream_t<2, true>(a, st) : launch_stream_t<2, false>(a, st);
+  return wkn ? launch_stream_t<4, true>(a, st) : launch_stream_t<4, false>(a, st);
+}
+
+}  // namespace mla

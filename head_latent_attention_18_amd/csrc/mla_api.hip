@@ -186,6 +186,7 @@ DecodePlan plan_decode(const mla_config *c, int32_t B, int32_t n_q, int32_t max_
   need(p.sk1, N1);
   need(p.sk2, (int64_t)c->n_heads * (c->d_nope + c->d_rope));
   need(p.sk5, c->d_model);
+  if (dt == MLA_BF16 && T <= 64) part = std::max(part, gemm_stream_partial_bytes((int)T));
   p.partial = take(part);
   p.total = off;
   return p;
@@ -536,6 +537,7 @@ mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h
     sg.batch_stride = D;
     a.epi.seg[0] = sg;
     a.epi.nseg = 1;
+    a.partial = partial;
     a.name = "absorb";
     e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M), 1, 1, a, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
@@ -573,6 +575,7 @@ mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h
     sg.batch_stride = cfg->d_v;
     a.epi.seg[0] = sg;
     a.epi.nseg = 1;
+    a.partial = partial;
     a.name = "unabsorb";
     e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M), 1, 0, a, st);
     if (e != hipSuccess) return MLA_ERR_HIP;

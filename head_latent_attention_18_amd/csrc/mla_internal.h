@@ -216,6 +216,13 @@ struct GemmArgs {
 // epilogue); 0 -> transposed plain store dst[n*ld + m].  wkn: W stored [K][N].
 hipError_t launch_gemm(int dtype, int tile, int swap, int wkn, GemmArgs &a, hipStream_t st);
 
+// weight-streaming GEMM for up to 64 activation rows (bf16): usable when K is
+// a multiple of 128, weight segments start on 64-row boundaries and a
+// partial buffer of gemm_stream_partial_bytes(M) is given
+bool gemm_stream_ok(const GemmArgs &a, int wkn);
+size_t gemm_stream_partial_bytes(int M);
+hipError_t launch_gemm_stream(GemmArgs &a, int wkn, hipStream_t st);
+
 struct FlashArgs {
   const void *q;    // [B*L][n_h][d_nope + d_rope] (q_C, then roped q_R)
   const void *k;    // [B*L][n_h][d_nope]
