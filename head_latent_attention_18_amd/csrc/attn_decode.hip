@@ -331,10 +331,9 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
   constexpr int NW = 4, NT = 64 * NW;
   constexpr int D = DC + DR;
   constexpr int CH = D / 8;                          // 16-byte chunks per cached row
-  constexpr int PITCH = CH + 2;                      // LDS row pitch in chunks (two pad chunks)
-  constexpr int LDC = PITCH * 8;                     // ... in elements
-  constexpr int LOADS = (KVT * PITCH + NT - 1) / NT; // copy instructions per wave per tile
-  constexpr int STAGE = LOADS * NT * 8;              // elements per stage, including the tail slots
+  constexpr int LOADS = KVT * CH / NT;               // copy instructions per wave per tile
+  constexpr int STAGE = KVT * D;                     // elements per stage
+  constexpr int NS = 4;                              // ring stages (two tiles ahead)
   constexpr int QS = D / 32;                         // 32-wide k steps of the scores
   constexpr int ROWS = 128;                          // query rows per workgroup
   constexpr int HA = ROWS / (16 * NW);               // 16-row blocks per wave in the scores
@@ -345,12 +344,14 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
   // P = exp2(score - reference) stays below 2^TAU, so P (bf16), l and O (fp32)
   // keep their range without ever rescaling O
   constexpr float TAU = 32.0f, MREF0 = -1e30f;
-  static_assert(D % 32 == 0 && DC % (16 * NW) == 0 && QS > PF && QS >= 2 * PVS, "");
+  static_assert(KVT * CH % NT == 0 && CH % 8 == 0 && DC % (16 * NW) == 0 && DBW == 8, "");
+  static_assert(QS > PF && QS >= 2 * PVS && QS >= 2 * LOADS, "");
 
-  __shared__ __attribute__((aligned(16))) bf16 stages[3 * STAGE];
+  // 4 x 36 KB stages + 2 x 8 KB of P = 160 KB.  Rows have no padding: the
+  // 16-byte chunk index is XORed with (row & 7), which keeps both the 16-byte
+  // score reads and the transposed reads free of bank conflicts.
+  __shared__ __attribute__((aligned(16))) bf16 stages[NS * STAGE];
   __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2 * 4 * ROWS];   // P[buf][g][row]
-  __shared__ __attribute__((aligned(16))) float fac[ROWS];             // per row: 1/l
-  __shared__ int tbl[PAGED ? DECODE_TBL : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 15, lgrp = lane >> 4;
@@ -368,65 +369,40 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
   const int rbase = rg * ROWS;
   const float sl2 = a.scale_log2;
   const bf16 *pool = (const bf16 *)a.cache.pool;
-
-  // block-table slice of this split (the host keeps it within DECODE_TBL entries)
-  int blk0 = 0;
-  bool tbl_ok = false;
-  if constexpr (PAGED) {
-    blk0 = block_of(a.cache, kv_beg);
-    const int nblk = block_of(a.cache, kv_end - 1) - blk0 + 1;
-    tbl_ok = nblk <= DECODE_TBL;
-    if (tbl_ok)
-      for (int i = tid; i < nblk; i += NT) tbl[i] = a.cache.table[(long)b * a.cache.max_blocks + blk0 + i];
-    __syncthreads();
-  }
   const long seq_row0 = (long)b * a.cache.max_len;
   const unsigned lds_stages = (unsigned)(size_t)(lds_void *)stages;
+  const int ntiles = (kv_end - kv_beg + KVT - 1) / KVT;
 
-  // Copy of tile t into stage t % 3: every wave issues exactly LOADS
-  // instructions; the tail and pad slots fetch a valid chunk into slots nobody
-  // reads.  A tile lies inside one cache block (block_size is a multiple of
-  // the tile), so its rows are contiguous: a uniform base plus 32-bit lane
-  // offsets, fixed for full tiles; a partial last tile repeats its last row.
-  auto dma_off = [&](int i, int last) {
-    const int sl = i * NT + tid;
-    const int r = sl / PITCH;
-    const int row = min(r, last), ch = min(sl - r * PITCH, CH - 1);
-    return (unsigned)(row * D + ch * 8) * 2u;
-  };
-  unsigned doff[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) doff[i] = dma_off(i, KVT - 1);
-  auto issue = [&](int t) {
+  // Copies.  Stage slot (row, c) holds cache chunk (row, c ^ (row & 7)); a
+  // tile lies inside one cache block (block_size is a multiple of the tile),
+  // so its rows are contiguous: a uniform base plus 32-bit lane offsets.  The
+  // lane's slot of instruction i is i*NT + tid; its (row, chunk) advances by
+  // NT = 3*CH + 40 per instruction.  Rows past the end of a partial last tile
+  // repeat its last row (finite values; their probabilities are 0).
+  static_assert(NT / CH == 3 && NT % CH == 40, "");
+  const int r0 = tid / CH, c0 = tid - (tid / CH) * CH;
+  auto tile_src = [&](int t) {
     const int kvb = kv_beg + t * KVT;
-    const int last = min(KVT, kv_end - kvb) - 1;
     long trow;
     if constexpr (PAGED) {
       const int q = block_of(a.cache, kvb);
-      const int blk = __builtin_amdgcn_readfirstlane(tbl_ok ? tbl[q - blk0]
-                                                            : a.cache.table[(long)b * a.cache.max_blocks + q]);
+      const int blk = __builtin_amdgcn_readfirstlane(a.cache.table[(long)b * a.cache.max_blocks + q]);
       trow = (long)blk * a.cache.block_size + (kvb - q * a.cache.block_size);
     } else {
       trow = seq_row0 + kvb;
     }
-    const char *tbase = (const char *)(pool + trow * D);
-    const unsigned lbase = lds_stages + (unsigned)((t % 3) * STAGE * 2) + wave * 64 * 16;
-    if (last == KVT - 1) {
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) dma16(tbase, doff[i], lbase + i * NT * 16);
-    } else {
-      // rare partial tile: offsets recomputed here (an opaque copy of the lane
-      // index keeps the compiler from holding them in registers all along)
-      int ot = tid;
-      asm volatile("" : "+v"(ot));
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int sl = i * NT + ot;
-        const int r = sl / PITCH;
-        const int row = min(r, last), ch = min(sl - r * PITCH, CH - 1);
-        dma16(tbase, (unsigned)(row * D + ch * 8) * 2u, lbase + i * NT * 16);
-      }
-    }
+    return (const char *)(pool + trow * D);
+  };
+  struct Cursor { int r, c; };
+  auto copy_next = [&](const char *src, int t, int i, Cursor &cu) {
+    const int last = min(KVT, kv_end - (kv_beg + t * KVT)) - 1;
+    const int r = min(cu.r, last);
+    const unsigned dst = lds_stages + (unsigned)((t % NS) * STAGE * 2) + i * NT * 16 + wave * 1024;
+    dma16(src, (unsigned)(r * D + ((cu.c ^ (r & 7)) << 3)) * 2u, dst);
+    cu.c += NT % CH;
+    const bool wrap = cu.c >= CH;
+    cu.c -= wrap ? CH : 0;
+    cu.r += NT / CH + (wrap ? 1 : 0);
   };
 
   // score state: this wave's HA blocks of 16 query rows
@@ -452,32 +428,48 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < HBS; ++j) oacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int ntiles = (kv_end - kv_beg + KVT - 1) / KVT;
   // the queries are in registers before the first copy is issued, so no wait
   // for them is left inside the loop (where it would also wait for copies)
   wait_vmcnt<0>();
-  issue(0);
-  // Scores use the tile rows in natural order (A slot = row) and natural k
-  // order (lane group g reads dims 32q+8g..+7 of step q): with the 74-chunk
-  // row pitch these 16-byte reads are free of bank conflicts.  Lane group g
-  // then holds the scores of rows 4g..4g+3 and 16+4g..16+4g+3, and the
-  // transposed reads of P.V fetch exactly those rows (any four rows can form
-  // the 4x16 block), so P keeps that key order in LDS.
-  const int a_off = lrow * LDC + lgrp * 8;
-  const int t_off = (4 * lgrp + (lrow >> 2)) * LDC + 4 * (lrow & 3) + wave * DW;
-  constexpr int TRH = 4 * LDC;   // sixteen rows further, in 4-element units
+  for (int t = 0; t < 2 && t < ntiles; ++t) {
+    const char *src = tile_src(t);
+    Cursor cu = {r0, c0};
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) copy_next(src, t, i, cu);
+  }
+
+  // Score reads: rows lrow and 16+lrow, logical chunk 4q+lgrp (natural k
+  // order), physical chunk (4q+lgrp) ^ (lrow & 7) = 4(q ^ fq) + (lgrp ^ (lrow & 3))
+  // with fq = (lrow >> 2) & 1: even and odd steps use two base offsets.
+  // Lane group g then holds the scores of rows 4g..4g+3 and 16+4g..16+4g+3,
+  // and the transposed reads of P.V fetch exactly those rows (any four rows
+  // can form the 4x16 block), so P keeps that key order in LDS.
+  const int fq = (lrow >> 2) & 1, gq = lgrp ^ (lrow & 3);
+  const int a_even = lrow * D + (4 * fq + gq) * 8, a_odd = lrow * D + (gq - 4 * fq) * 8;
+  // Transposed reads: row r = 4*lgrp + (lrow >> 2) (and r + 16), elements
+  // 4*(lrow & 3).. of the wave's 16-column block db: physical chunk
+  // wave*16 + 2*(db ^ fh) + cl, fh = (r & 7) >> 1, cl = ((lrow & 3) >> 1) ^ (r & 1).
+  int t_base, t_fh;
+  {
+    const int r = 4 * lgrp + (lrow >> 2), fr = r & 7;
+    const int cl = ((lrow & 3) >> 1) ^ (fr & 1), half = (lrow & 1) * 4;
+    t_base = r * D + (wave * 16 + cl) * 8 + half;
+    t_fh = fr >> 1;
+  }
+  constexpr int TRH = 16 * D;   // sixteen rows further
   const lds_bf16 *st_base = (const lds_bf16 *)stages;
   lds_bf16x8 *pl = (lds_bf16x8 *)pbuf;
 
-  // P.V of tile u (stage u % 3, P buffer u & 1) for row blocks [h0, h1); the
-  // V^T fragments of the wave's columns are read once per tile
+  // P.V of tile u (stage u % NS, P buffer u & 1); the V^T fragments of the
+  // wave's columns are read once per tile
   bf16x8 va[DBW];
   auto load_v = [&](int u) {
-    const lds_v4i16 *tr_p = (const lds_v4i16 *)(st_base + (u % 3) * STAGE + t_off);
+    const lds_bf16 *st = st_base + (u % NS) * STAGE;
 #pragma unroll
     for (int db = 0; db < DBW; ++db) {
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(tr_p + db * 4));
-      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(tr_p + TRH + db * 4));
+      const int o = t_base + 16 * ((db & 3) ^ t_fh) + 64 * (db >> 2);
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + o));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + o + TRH));
       va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
@@ -487,29 +479,39 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
     for (int db = 0; db < DBW; ++db) oacc[db][hb] = Mma<bf16>::mma(va[db], pb, oacc[db][hb]);
   };
 
-  // scores and softmax of tile t (stage t % 3) into P buffer t & 1; when
+  // Scores and softmax of tile t (stage t % NS) into P buffer t & 1.  When
   // WITH_PV, the P.V of tile t-1 is interleaved: row blocks 0..PVS-1 between
-  // the score steps, the last two with the softmax
+  // the score steps, the last two with the softmax.  The copy of tile t+2 is
+  // spread over the odd score steps (one instruction each).
   auto scores = [&](int t, auto with_pv_c) {
     constexpr bool WITH_PV = decltype(with_pv_c)::value;
-    const lds_bf16 *ca_p = st_base + (t % 3) * STAGE + a_off;
+    const lds_bf16 *ca_p = st_base + (t % NS) * STAGE;
     const int kvb = kv_beg + t * KVT;
+    if (t + 2 < ntiles) {
+      const char *src = tile_src(t + 2);
+      Cursor cu = {r0, c0};
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) copy_next(src, t + 2, i, cu);
+    }
     f32x4 sacc[2][HA];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ha = 0; ha < HA; ++ha) sacc[kb][ha] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto rd = [&](int q, int kb) {
+      return *(const lds_bf16x8 *)(ca_p + ((q & 1) ? a_odd : a_even) + q * 32 + kb * 16 * D);
+    };
     bf16x8 ca[PF + 1][2];
 #pragma unroll
     for (int q = 0; q < PF; ++q) {
-      ca[q][0] = *(const lds_bf16x8 *)(ca_p + q * 32);
-      ca[q][1] = *(const lds_bf16x8 *)(ca_p + 16 * LDC + q * 32);
+      ca[q][0] = rd(q, 0);
+      ca[q][1] = rd(q, 1);
     }
 #pragma unroll
     for (int q = 0; q < QS; ++q) {
       if (q + PF < QS) {
-        ca[(q + PF) % (PF + 1)][0] = *(const lds_bf16x8 *)(ca_p + (q + PF) * 32);
-        ca[(q + PF) % (PF + 1)][1] = *(const lds_bf16x8 *)(ca_p + 16 * LDC + (q + PF) * 32);
+        ca[(q + PF) % (PF + 1)][0] = rd(q + PF, 0);
+        ca[(q + PF) % (PF + 1)][1] = rd(q + PF, 1);
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -518,6 +520,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
       if constexpr (WITH_PV) {
         if (q % 2 == 1 && q / 2 < PVS) pv_block(t - 1, q / 2);
       }
+
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -552,15 +555,15 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
     }
   };
 
-  // Iteration i: tile i has landed; the copy of tile i+1 goes out; the scores
-  // of tile i run with the P.V of tile i-1 (whose P every wave wrote in
-  // iteration i-1).  One barrier per iteration: it also retires stage (i-1)%3
-  // reads before the copy into stage (i+1)%3 = (i-2)%3 ... of the next one.
+  // Iteration i: tile i has landed (tile i+1 may still be in flight); the
+  // scores of tile i run with the P.V of tile i-1 (whose P every wave wrote in
+  // iteration i-1) and the copy of tile i+2 into stage (i+2) % 4, last read by
+  // the P.V of tile i-2 in the previous iteration.  One barrier per iteration.
   auto sync = [&](int i) {
-    wait_vmcnt<0>();   // this wave's copies of tile i
-    wait_lgkm0();      // this wave's P of tile i-1
+    if (i + 1 < ntiles) wait_vmcnt<LOADS>();   // this wave's copies of tile i
+    else wait_vmcnt<0>();
+    wait_lgkm0();                              // this wave's P of tile i-1
     bar();
-    if (i + 1 < ntiles) issue(i + 1);
   };
   sync(0);
   scores(0, std::false_type());
@@ -578,6 +581,8 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
   // and the reference of their rows, the P.V lanes the O columns.  A row
   // marked in overflow gets lse = NaN; the combine recomputes it exactly.
   ovf = row_max(ovf ? 1.f : 0.f) > 0.f;
+  __syncthreads();   // P no longer read: its space holds 1/l per row
+  float *fac = (float *)pbuf;
 #pragma unroll
   for (int ha = 0; ha < HA; ++ha) {
     float l = lrun[ha];
