@@ -68,6 +68,31 @@ def prefill_flops(d, B, L):
             + 2 * T * d.n_heads * d.d_v * d.d_model)
 
 
+def measured_traffic(kernel_label):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary, scaled by the copy-kernel
+    calibration; None when no summary covers this kernel or its source has
+    changed since the counters were taken."""
+    import hashlib
+    files = {"decode_attn": ("profiles/decode_attn_b32_len4096_traffic.txt",
+                             "head_latent_attention_18_amd/csrc/attn_decode.hip")}
+    if kernel_label not in files:
+        return None
+    summ, src = (os.path.join(ROOT, f) for f in files[kernel_label])
+    try:
+        kv = {}
+        for line in open(summ):
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if kv.get("source_sha256") != sha:
+            return None
+        return int(float(kv["traffic_bytes"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def kernel_times(run, steps):
     """Run `steps` calls with library kernel timing on; average ms per launch."""
     import torch
@@ -252,7 +277,8 @@ def main():
         "step_hbm": {"alg_bytes": step_bytes, "GBps": round(step_bytes / dt / 1e9, 1),
                      "frac": round(step_bytes / dt / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom),
+                     "alg_bytes": kbytes[dom]},
         "kernels": kernels,
         "parity": parity,
         "prefill": prefill,
