@@ -439,6 +439,7 @@ int gemm_bm(int dtype, int tile) {
 hipError_t launch_gemm(int dtype, int tile, int swap, int wkn, GemmArgs &a, hipStream_t st) {
   if (dtype == 1) {
     if (tile == TILE_BIG) {
+      if (!wkn && gemm_big_ok(a)) return launch_gemm_big(a, swap, st);
       if (swap && !wkn) return launch_t<bf16, BIG_BM, BIG_BN, BIG_BK, BIG_WM, BIG_WN, true, false>(a, st, "gemm_bf16_big");
       if (!swap && !wkn) return launch_t<bf16, BIG_BM, BIG_BN, BIG_BK, BIG_WM, BIG_WN, false, false>(a, st, "gemm_bf16_big_t");
       if (swap && wkn) return launch_t<bf16, 128, 128, 64, 2, 2, true, true>(a, st, "gemm_bf16_128x128_kn");

@@ -1,0 +1,261 @@
+// Large-M GEMM (bf16, prefill): Y[m][n] = sum_k X[m][k] W[n][k] with the
+// segment epilogues of the projections (W stored [N][K]).
+//
+//   * tile 256 tokens x 256 features, k slabs of 64; 8 waves (two per SIMD),
+//     each computing a 128-token x 64-feature block of Y^T with 32x32x16
+//     MFMAs; operand fragments are read two k steps ahead of their MFMAs;
+//   * X and W slabs go HBM/L2 -> LDS with global_load_lds_dwordx4 into a
+//     two-stage ring (no staging registers), one slab ahead: 64 KB per slab
+//     for 8.4 MFLOP keeps the L2 -> LDS stream (about 90 GB/s per CU) below
+//     what the matrix cores consume;
+//   * LDS rows are 8 chunks of 16 bytes with the chunk index XORed by
+//     (row >> 1) & 7, so the 16-row fragment reads hit 16 distinct bank groups;
+//   * tiles are handed out in GxG groups per XCD (G = 8, 4, 2 or 1, the
+//     largest that keeps the XCDs evenly loaded), so the X and W slabs of a
+//     group are read from HBM once and reused from that XCD's L2;
+//   * the epilogue goes through LDS (fp32, half a tile at a time) and runs as
+//     a loop over (token, 4 features) items, so the segment/RoPE/cache
+//     epilogue is compiled once instead of once per accumulator.
+#include <type_traits>
+
+#include "mla_internal.h"
+
+namespace mla {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) bf16 lds_bf16;
+typedef __attribute__((address_space(3))) float lds_float;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int GBM = 256, GBN = 256, GBK = 64;
+constexpr int GNT = 512;                        // threads (8 waves)
+constexpr int GNS = 2;                          // ring stages
+constexpr int RCH = GBK / 8;                    // 16-byte chunks per row of a slab (8)
+constexpr int XCHK = GBM * RCH;                 // activation chunks per slab (2048)
+constexpr int WCHK = GBN * RCH;                 // weight chunks per slab (2048)
+constexpr int GLOADS = (XCHK + WCHK) / GNT;     // copy instructions per wave per slab (8)
+constexpr int GSTAGE = (XCHK + WCHK) * 8;       // elements per stage (32768 = 64 KB)
+constexpr int NSTEP = GBK / 16;                 // MFMA k steps per slab (4)
+constexpr int EPI_LD = GBN + 4;                 // fp32 row pitch of the epilogue staging
+// LDS: the ring, reused for half a tile of fp32 results in the epilogue
+constexpr int RING_ELEMS = (GNS * GSTAGE > GBM / 2 * EPI_LD * 2) ? GNS * GSTAGE : GBM / 2 * EPI_LD * 2;
+
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4)); }
+
+// 16 bytes per lane HBM -> LDS (lane i lands at lds + 16*i).  An asm
+// statement: the compiler sees no LDS write to order later reads after; the
+// kernel waits for its copies itself (vmcnt, then a barrier).
+__device__ inline void dma16(const void *gbase, unsigned off, unsigned lds) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(gbase)
+      : "memory", "m0");
+}
+
+__device__ inline void bar() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// rows of 8 chunks: XOR by (row >> 1) & 7 spreads 16 consecutive rows over
+// 16 distinct 16-byte bank groups
+__device__ inline int swz(int row) { return (row >> 1) & 7; }
+
+}  // namespace
+
+template <bool SWAP>
+__global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 ring[RING_ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;      // 128-token x 64-feature block of the wave
+
+  // tile of this workgroup: GxG groups of tiles, one group per XCD at a time
+  const int G = a.grouped;                      // group side (host-chosen)
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int gi = local / (G * G), ti = local % (G * G);
+  const int groups_m = (a.tiles_m + G - 1) / G;
+  const int group = gi * 8 + xcd;
+  const int tm = (group % groups_m) * G + ti % G;
+  const int tn = (group / groups_m) * G + ti / G;
+  if (tm >= a.tiles_m || tn >= a.tiles_n) return;
+  const int m0 = tm * GBM, n0 = tn * GBN;
+
+  int seg = 0, beg = 0;
+  while (seg < a.nw - 1 && n0 >= a.w_end[seg]) { beg = a.w_end[seg]; ++seg; }
+  const bf16 *wsrc = (const bf16 *)a.w[seg] + (long)(n0 - beg) * a.ldw;
+  const int wrows = min(GBN, a.w_end[seg] - n0);
+  const bf16 *xsrc = (const bf16 *)a.x + (long)m0 * a.ldx;
+  const int xrows = min(GBM, a.M - m0);
+  const unsigned lring = (unsigned)(size_t)(lds_void *)ring;
+
+  // per-lane byte offsets of the slab copies (k-independent part); slots
+  // 0..XCHK-1 are activation rows, then weight rows, RCH chunks per row
+  constexpr int XL = XCHK / GNT;                 // the first XL instructions copy activations
+  unsigned coff[GLOADS];
+#pragma unroll
+  for (int i = 0; i < GLOADS; ++i) {
+    const int s = (i < XL ? i : i - XL) * GNT + tid, r = s / RCH, c = (s % RCH) ^ swz(r);
+    coff[i] = i < XL ? (unsigned)(min(r, xrows - 1) * a.ldx + c * 8) * 2u
+                     : (unsigned)(min(r, wrows - 1) * a.ldw + c * 8) * 2u;
+  }
+  auto issue = [&](int kt, int st) {
+    const unsigned dst = lring + (unsigned)(st * GSTAGE * 2) + wave * 1024;
+    const char *xb = (const char *)(xsrc + kt * GBK), *wb = (const char *)(wsrc + kt * GBK);
+#pragma unroll
+    for (int i = 0; i < GLOADS; ++i) dma16(i < XL ? xb : wb, coff[i], dst + i * GNT * 16);
+  };
+
+  f32x16 acc[2][4];   // [feature block][token block]
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const lds_bf16 *rl = (const lds_bf16 *)ring;
+  // fragment rows of this lane: 32x32x16 operands hold row (lane & 31) and
+  // k chunk 2s + (lane >> 5) of the 16-wide step s
+  const int fr = lane & 31, fh = lane >> 5;
+  bf16x8 wf[3][2], xf[3][4];   // three steps of fragments in flight
+  auto rd = [&](int st, int s, int buf) {
+    const lds_bf16 *xs = rl + st * GSTAGE;
+    const lds_bf16 *ws = xs + XCHK * 8;
+    const int c = 2 * s + fh;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int wr = wn * 64 + b * 32 + fr;
+      wf[buf][b] = *(const lds_bf16x8 *)(ws + (wr * RCH + (c ^ swz(wr))) * 8);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int xr = wm * 128 + b * 32 + fr;
+      xf[buf][b] = *(const lds_bf16x8 *)(xs + (xr * RCH + (c ^ swz(xr))) * 8);
+    }
+  };
+  auto mm = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][i], xf[buf][j], acc[i][j], 0, 0, 0);
+  };
+
+  const int nkt = a.K / GBK;
+  issue(0, 0);
+  // slab kt: wait for it, free the other stage for slab kt+1, multiply with
+  // the fragments read two steps ahead (ring of three fragment buffers)
+  for (int kt = 0; kt < nkt; ++kt) {
+    wait_vm<0>();     // this wave's copies of slab kt
+    wait_lgkm0();     // its reads of slab kt-1 are in registers
+    bar();            // slab kt landed for every wave; stage (kt+1) % 2 is free
+    if (kt + 1 < nkt) issue(kt + 1, (kt + 1) % GNS);
+    const int st = kt % GNS;
+    rd(st, 0, 0);
+    rd(st, 1, 1);
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      if (s + 2 < NSTEP) rd(st, s + 2, (s + 2) % 3);
+      mm(s % 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Epilogue through LDS, half a tile (128 tokens) at a time: the waves of
+  // that half store their accumulators as rows [token][feature] (fp32), then
+  // all threads run the epilogue over (token, 4 features) items.
+  lds_float *ep = (lds_float *)((lds_void *)ring);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    wait_lgkm0();
+    __syncthreads();
+    if (wm == half) {
+      // acc[i][j]: features wn*64 + 32i + 8q + 4fh + 0..3, token 32j + fr
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int f = wn * 64 + i * 32 + 8 * q + 4 * fh, t = j * 32 + fr;
+            *(lds_f32x4 *)(ep + t * EPI_LD + f) =
+                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          }
+    }
+    __syncthreads();
+    const int mh = m0 + half * 128;
+    if constexpr (SWAP) {
+      for (int it = tid; it < 128 * (GBN / 4); it += GNT) {
+        const int t = it / (GBN / 4), f = (it % (GBN / 4)) * 4;
+        const int m = mh + t, n = n0 + f;
+        if (m < a.M && n < a.N) {
+          const f32x4 v4 = *(const lds_f32x4 *)(ep + t * EPI_LD + f);
+          float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+          epi_store4<bf16>(a.epi, 0, m, n, v);
+        }
+      }
+    } else {
+      // transposed plain store dst[n * ld + m]: items of 4 consecutive tokens
+      const Seg &g = a.epi.seg[0];
+      for (int it = tid; it < GBN * (128 / 4); it += GNT) {
+        const int f = it / 32, t = (it % 32) * 4;
+        const int n = n0 + f, m = mh + t;
+        if (n < a.N && m < a.M) {
+          bf16 *dst = (bf16 *)g.dst + (long)n * g.ld;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = ep[(t + e) * EPI_LD + f];
+          if (m + 3 < a.M && (g.ld & 3) == 0) {
+            store4<bf16>(dst, m, v, 0);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (m + e < a.M) dst[m + e] = (bf16)v[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+bool gemm_big_ok(const GemmArgs &a) {
+  if (a.batch != 1 || a.M < GBM || a.K % GBK != 0) return false;
+  for (int s = 0; s < a.nw - 1; ++s)
+    if (a.w_end[s] % GBN != 0) return false;   // a tile never straddles two weight segments
+  // 32-bit lane offsets
+  if ((long)GBM * a.ldx * 2 >= (1L << 31) || (long)GBN * a.ldw * 2 >= (1L << 31)) return false;
+  return true;
+}
+
+hipError_t launch_gemm_big(GemmArgs &a, int swap, hipStream_t st) {
+  a.tiles_m = (a.M + GBM - 1) / GBM;
+  a.tiles_n = (a.N + GBN - 1) / GBN;
+  int G = 1, groups = a.tiles_m * a.tiles_n;
+  for (int g : {8, 4, 2}) {
+    const int n = ((a.tiles_m + g - 1) / g) * ((a.tiles_n + g - 1) / g);
+    if (n >= 8 && ((n + 7) / 8) * 8 <= n + n / 20) { G = g; groups = n; break; }
+  }
+  a.grouped = G;
+  const int grid = ((groups + 7) / 8) * 8 * G * G;
+  const char *name = a.name ? a.name : "gemm_big";
+  timing_before(name, st);
+  if (swap) hipLaunchKernelGGL((gemm_big_kernel<true>), dim3(grid), dim3(GNT), 0, st, a);
+  else hipLaunchKernelGGL((gemm_big_kernel<false>), dim3(grid), dim3(GNT), 0, st, a);
+  timing_after(name, st);
+  return hipGetLastError();
+}
+
+}  // namespace mla

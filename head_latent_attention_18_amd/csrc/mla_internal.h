@@ -220,6 +220,9 @@ hipError_t launch_gemm(int dtype, int tile, int swap, int wkn, GemmArgs &a, hipS
 // a multiple of 128, weight segments start on 64-row boundaries and a
 // partial buffer of gemm_stream_partial_bytes(M) is given
 bool gemm_stream_ok(const GemmArgs &a, int wkn);
+// 256x128-tile GEMM for many tokens (bf16, W stored [N][K], batch 1)
+bool gemm_big_ok(const GemmArgs &a);
+hipError_t launch_gemm_big(GemmArgs &a, int swap, hipStream_t st);
 size_t gemm_stream_partial_bytes(int M);
 hipError_t launch_gemm_stream(GemmArgs &a, int wkn, hipStream_t st);
 
