@@ -41,6 +41,7 @@ constexpr int GLOADS = (XCHK + WCHK) / GNT;     // copy instructions per wave pe
 constexpr int GSTAGE = (XCHK + WCHK) * 8;       // elements per stage (32768 = 64 KB)
 constexpr int NSTEP = GBK / 16;                 // MFMA k steps per slab (4)
 constexpr int EPI_LD = GBN + 4;                 // fp32 row pitch of the epilogue staging
+static_assert(GNT % (GBN / 4) == 0, "");
 // LDS: the ring, reused for half a tile of fp32 results in the epilogue
 constexpr int RING_ELEMS = (GNS * GSTAGE > GBM / 2 * EPI_LD * 2) ? GNS * GSTAGE : GBM / 2 * EPI_LD * 2;
 
@@ -198,13 +199,18 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
     __syncthreads();
     const int mh = m0 + half * 128;
     if constexpr (SWAP) {
-      for (int it = tid; it < 128 * (GBN / 4); it += GNT) {
-        const int t = it / (GBN / 4), f = (it % (GBN / 4)) * 4;
-        const int m = mh + t, n = n0 + f;
-        if (m < a.M && n < a.N) {
-          const f32x4 v4 = *(const lds_f32x4 *)(ep + t * EPI_LD + f);
-          float v[4] = {v4[0], v4[1], v4[2], v4[3]};
-          epi_store4<bf16>(a.epi, 0, m, n, v);
+      // a thread always handles the same 4 features (GNT is a multiple of
+      // GBN / 4): their column plan is prepared once, outside the row loop
+      const int f = (tid % (GBN / 4)) * 4, n = n0 + f;
+      if (n < a.N) {
+        const ColPlan cp = col_plan(a.epi, n);
+        for (int t = tid / (GBN / 4); t < 128; t += GNT / (GBN / 4)) {
+          const int m = mh + t;
+          if (m < a.M) {
+            const f32x4 v4 = *(const lds_f32x4 *)(ep + t * EPI_LD + f);
+            float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+            col_store<bf16>(cp, a.epi, 0, m, v);
+          }
         }
       }
     } else {

@@ -132,9 +132,12 @@ struct Epi {
 // angle = pos * inv_freq[k]: formed and reduced modulo 2*pi in fp64 so that
 // positions up to 2^20 keep full fp32 accuracy, then sin/cos in fp32.
 __device__ inline void rope_sincos(int pos, double inv_freq, float &s, float &c) {
-  double a = (double)pos * inv_freq;
-  double r = a - 6.283185307179586476925 * rint(a * 0.15915494309189533576888);
-  sincosf((float)r, &s, &c);
+  // turns = angle / 2pi in fp64, reduced to [-1/2, 1/2]; the hardware sin/cos
+  // take turns (max abs error ~2e-7 over positions < 2^16, as sincosf)
+  const double turns = (double)pos * inv_freq * 0.15915494309189533576888;
+  const float f = (float)(turns - rint(turns));
+  s = __builtin_amdgcn_sinf(f);
+  c = __builtin_amdgcn_cosf(f);
 }
 
 template <typename T>
@@ -190,6 +193,88 @@ __device__ inline void epi_store4(const Epi &e, int z, int m, int n, float v[4])
   }
   store4<T>(base, off, v, g.out_f32);
   if (g.dst2) store4<T>(g.dst2, (long)m * g.ld2 + c, v, 0);
+}
+
+// The same epilogue for a thread whose columns n..n+3 are fixed (a tile that
+// lies inside one segment): everything that depends on the columns, including
+// the kernel-argument reads, is prepared once, so the per-row store issues no
+// memory reads (on gfx9 a read after stores waits for those stores).
+struct ColPlan {
+  int kind, rope, out_f32, c;
+  float scale;
+  void *dst;
+  long ld, col;        // element offset of the columns inside a row (PLAIN/HEADS) or cached row (CACHE)
+  long batch_stride;
+  void *dst2;
+  long ld2;
+  double inv0, inv1;   // RoPE frequencies of the two column pairs
+};
+
+__device__ inline int epi_segment(const Epi &e, int n, int &nb) {
+  int s = 0;
+  nb = 0;
+  while (s < e.nseg - 1 && n >= e.seg[s].n_end) { nb = e.seg[s].n_end; ++s; }
+  return s;
+}
+
+__device__ inline ColPlan col_plan(const Epi &e, int n) {
+  int nb;
+  const Seg &g = e.seg[epi_segment(e, n, nb)];
+  ColPlan p;
+  p.c = n - nb;
+  p.kind = g.kind;
+  p.rope = g.rope;
+  p.out_f32 = g.out_f32;
+  p.scale = g.scale;
+  p.dst = g.dst;
+  p.ld = g.ld;
+  p.batch_stride = g.batch_stride;
+  p.dst2 = g.dst2;
+  p.ld2 = g.ld2;
+  if (g.kind == SEG_HEADS) {
+    const int hh = p.c / g.head_w, d = p.c - hh * g.head_w;
+    p.col = (long)hh * g.head_ld + g.col_off + d;
+  } else {
+    p.col = g.col_off + p.c;
+  }
+  p.inv0 = p.inv1 = 0.0;
+  if (g.rope) {
+    const int k0 = (p.c % g.head_w) >> 1;
+    p.inv0 = e.inv_freq[k0];
+    p.inv1 = e.inv_freq[k0 + 1];
+  }
+  return p;
+}
+
+template <typename T>
+__device__ inline void col_store(const ColPlan &p, const Epi &e, int z, int m, float v[4]) {
+  int seq = 0, pos = 0;
+  if (p.rope || p.kind == SEG_CACHE) row_seq_pos(e.rows, m, seq, pos);
+  if (p.rope) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float sn, cs;
+      rope_sincos(pos, q ? p.inv1 : p.inv0, sn, cs);
+      const float x0 = v[2 * q], x1 = v[2 * q + 1];
+      v[2 * q] = x0 * cs - x1 * sn;
+      v[2 * q + 1] = x0 * sn + x1 * cs;
+    }
+  }
+  if (p.scale != 1.0f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] *= p.scale;
+  }
+  long off;
+  void *base = p.dst;
+  if (p.kind != SEG_CACHE) {
+    off = (long)z * p.batch_stride + (long)m * p.ld + p.col;
+  } else {
+    if (seq < 0 || seq >= e.cache.batch || pos < 0 || pos >= e.cache.cap) return;
+    base = e.cache.pool;
+    off = cache_row(e.cache, seq, pos) * e.cache.d_row + p.col;
+  }
+  store4<T>(base, off, v, p.out_f32);
+  if (p.dst2) store4<T>(p.dst2, (long)m * p.ld2 + p.c, v, 0);
 }
 
 // ---------------------------------------------------------------------------
