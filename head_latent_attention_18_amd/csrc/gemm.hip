@@ -170,21 +170,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
 
   if (SWAP) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * TN + j * 16 + 4 * lgrp;
+      if (n >= N) continue;
+      // the lane's columns are fixed for all its rows: plan them once
+      const ColPlan cp = a.splits > 1 ? ColPlan{} : col_plan(a.epi, n);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int m = m0 + wm * TM + i * 16 + lrow;
-        const int n = n0 + wn * TN + j * 16 + 4 * lgrp;
-        if (m < M && n < N) {
+        if (m < M) {
           float v[4] = {acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]};
           if (a.splits > 1) {
             float *p = a.partial + (((long)bz * a.splits + sp) * M + m) * N + n;
             *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
           } else {
-            epi_store4<T>(a.epi, bz, m, n, v);
+            col_store<T>(cp, a.epi, bz, m, v);
           }
         }
       }
+    }
   } else {
     const Seg &g = a.epi.seg[0];
 #pragma unroll
@@ -312,17 +316,21 @@ __global__ __launch_bounds__(256, 2) void gemm_skinny_kernel(GemmArgs a) {
     }
   }
 
+  const int nn = n0 + wave * 16 + 4 * lgrp;
+  if (nn < N) {
+    // the lane's columns are fixed for all its rows: plan them once
+    const ColPlan cp = a.splits > 1 ? ColPlan{} : col_plan(a.epi, nn);
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int m = mb * 16 + lrow;
-    const int nn = n0 + wave * 16 + 4 * lgrp;
-    if (m < M && nn < N) {
-      float v[4] = {acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]};
-      if (a.splits > 1) {
-        float *p = a.partial + (((long)bz * a.splits + sp) * M + m) * N + nn;
-        *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
-      } else {
-        epi_store4<bf16>(a.epi, bz, m, nn, v);
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = mb * 16 + lrow;
+      if (m < M) {
+        float v[4] = {acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]};
+        if (a.splits > 1) {
+          float *p = a.partial + (((long)bz * a.splits + sp) * M + m) * N + nn;
+          *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
+        } else {
+          col_store<bf16>(cp, a.epi, bz, m, v);
+        }
       }
     }
   }

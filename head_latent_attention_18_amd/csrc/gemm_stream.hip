@@ -139,13 +139,15 @@ __global__ __launch_bounds__(SNT, 1) void gemm_stream_kernel(GemmArgs a) {
     const int z = tt / a.tiles_n, t = tt - z * a.tiles_n;
     const bool whole = tt * KS >= u0 && (tt + 1) * KS <= u1;
     const int nn = t * SBN + wave * 16 + 4 * lgrp;
+    // the lane's columns are fixed for all its rows: plan them once
+    const ColPlan cp = (whole && nn < a.N) ? col_plan(a.epi, nn) : ColPlan{};
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int m = mb * 16 + lrow;
       if (m < a.M && nn < a.N) {
         float v[4] = {acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]};
         if (whole) {
-          epi_store4<bf16>(a.epi, z, m, nn, v);
+          col_store<bf16>(cp, a.epi, z, m, v);
         } else {
           const int slot = tt == first_tile ? 0 : 1;
           float *p = a.partial + (((long)blockIdx.x * 2 + slot) * 16 * MB + m) * SBN + wave * 16 + 4 * lgrp;
