@@ -279,6 +279,257 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_kernel(FlashArgs a) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernel for gfx950 (d_nope 128, d_R 64, d_v 128, L a multiple of 8).
+// Same work split and softmax as above; the K and V^T tiles go HBM -> LDS
+// with global_load_lds_dwordx4 into a three-stage ring (two tiles ahead, one
+// barrier per tile, no staging registers), as three sub-tiles per stage:
+// K_C rows (16 chunks of 16 bytes), k_R rows (8 chunks) and V^T rows (8
+// chunks of 8 keys).  Chunk indices are XORed with the row so that the
+// 16-row fragment reads hit distinct banks; the scores read the head
+// dimension in natural order.  Keys past the end of the sequence repeat valid
+// data (their probabilities are 0).
+// ---------------------------------------------------------------------------
+namespace {
+typedef __attribute__((address_space(3))) void lds_void_t;
+template <int N>
+__device__ inline void fp_wait_vm() {
+  static_assert(N >= 0 && N < 64, "");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+}
+template <int N>
+__device__ inline void fp_wait_vm_lgkm() {
+  static_assert(N >= 0 && N < 64, "");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4));
+}
+__device__ inline void fp_dma16(const void *gbase, unsigned off, unsigned lds) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(gbase)
+      : "memory", "m0");
+}
+__device__ inline void fp_bar() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+}  // namespace
+
+template <int QB, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void flash_prefill_dma_kernel(FlashArgs a) {
+  constexpr int DN = 128, DR = 64, DV = 128, KVT = 64, NT = 64 * NW;
+  constexpr int KVB = KVT / 16, QS = (DN + DR) / 32, PS = KVT / 32, DVB = DV / 16;
+  constexpr int KN_E = KVT * DN, KR_E = KVT * DR, V_E = DV * KVT;
+  constexpr int STAGE = KN_E + KR_E + V_E;       // elements (40 KB)
+  constexpr int NS = 3;
+  constexpr int LKN = KN_E / 8 / NT, LKR = KR_E / 8 / NT, LV = V_E / 8 / NT;
+  constexpr int LOADS = LKN + LKR + LV;          // copy instructions per wave per tile
+  constexpr int BQ = 16 * QB * NW;
+  static_assert(KN_E % (8 * NT) == 0 && KR_E % (8 * NT) == 0 && V_E % (8 * NT) == 0, "");
+  typedef __attribute__((address_space(3))) bf16 lds_T;
+  typedef __attribute__((address_space(3))) bf16x8 lds_frag;
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+  __shared__ __attribute__((aligned(16))) bf16 stages[NS * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  const int L = a.L, NH = a.n_h;
+  const int qtiles = (L + BQ - 1) / BQ;
+
+  // block -> (query tile, longest first; sequence; head), heads interleaved
+  // over the XCDs (see above)
+  int bid = blockIdx.x, h, b, qt_rev;
+  if ((NH & 7) == 0) {
+    const int hx = bid & 7;
+    int rest = bid >> 3;
+    const int hh = rest % (NH >> 3);
+    rest /= (NH >> 3);
+    b = rest % a.B;
+    qt_rev = rest / a.B;
+    h = hh * 8 + hx;
+  } else {
+    h = bid % NH;
+    int rest = bid / NH;
+    b = rest % a.B;
+    qt_rev = rest / a.B;
+  }
+  const int qt = qtiles - 1 - qt_rev;
+  const long tok0 = (long)b * L;
+  const long ntok = (long)a.B * L;
+  const int q0 = qt * BQ + wave * 16 * QB;
+  const int wave_qmax = min(q0 + 16 * QB - 1, L - 1);
+  const int blk_qmax = min(qt * BQ + BQ - 1, L - 1);
+  const float sl2 = a.scale_log2;
+
+  bf16x8 qf[QB][QS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int t = min(q0 + qb * 16 + lrow, L - 1);
+    const bf16 *qrow = (const bf16 *)a.q + ((tok0 + t) * NH + h) * (DN + DR) + lgrp * 8;
+#pragma unroll
+    for (int s = 0; s < QS; ++s) qf[qb][s] = *(const bf16x8 *)(qrow + s * 32);
+  }
+  f32x4 oacc[DVB][QB];
+#pragma unroll
+  for (int i = 0; i < DVB; ++i)
+#pragma unroll
+    for (int j = 0; j < QB; ++j) oacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mref[QB], lrun[QB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) { mref[j] = -1e30f; lrun[j] = 0.f; }
+
+  // copies of tile t into stage t % 3
+  const unsigned lds0 = (unsigned)(size_t)(lds_void_t *)stages;
+  auto issue = [&](int t) {
+    const int kvb = t * KVT;
+    const int last = min(KVT, L - kvb) - 1;
+    const unsigned dst = lds0 + (unsigned)((t % NS) * STAGE * 2) + wave * 1024;
+    const char *kn = (const char *)((const bf16 *)a.k + ((tok0 + kvb) * NH + h) * DN);
+    const char *kr = (const char *)((const bf16 *)a.kr + (tok0 + kvb) * DR);
+    const char *vt = (const char *)((const bf16 *)a.vt + (long)h * DV * ntok + tok0);
+#pragma unroll
+    for (int i = 0; i < LKN; ++i) {
+      const int sl = i * NT + tid, r = sl >> 4, c = (sl & 15) ^ (r & 15);
+      fp_dma16(kn, (unsigned)(min(r, last) * NH * DN + c * 8) * 2u, dst + i * NT * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < LKR; ++i) {
+      const int sl = i * NT + tid, r = sl >> 3, c = (sl & 7) ^ ((r >> 1) & 7);
+      fp_dma16(kr, (unsigned)(min(r, last) * DR + c * 8) * 2u, dst + (KN_E * 2) + i * NT * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < LV; ++i) {
+      const int sl = i * NT + tid, d = sl >> 3, c = (sl & 7) ^ ((d >> 1) & 7);
+      const int col = min(kvb + c * 8, L - 8);
+      fp_dma16(vt, (unsigned)((long)d * ntok + col) * 2u, dst + (KN_E + KR_E) * 2 + i * NT * 16);
+    }
+  };
+
+  const int ntiles = blk_qmax / KVT + 1;
+  fp_wait_vm<0>();   // queries in registers before the copies start
+  issue(0);
+  if (ntiles > 1) issue(1);
+  const lds_T *st0 = (const lds_T *)stages;
+  for (int t = 0; t < ntiles; ++t) {
+    const int kvb = t * KVT;
+    // every LDS read of tile t-1 done, tile t landed (tile t+1 may stay in flight)
+    if (t + 1 < ntiles) fp_wait_vm_lgkm<LOADS>();
+    else fp_wait_vm_lgkm<0>();
+    fp_bar();   // tile t landed for every wave; stage (t+2) % 3 was last read at tile t-1
+    if (t + 2 < ntiles) issue(t + 2);
+    if (kvb > wave_qmax) continue;   // every key of this tile is after every query of this wave
+    const lds_T *kn_p = st0 + (t % NS) * STAGE;
+    const lds_T *kr_p = kn_p + KN_E;
+    const lds_T *v_p = kr_p + KR_E;
+
+    // S^T = K . Q^T: key rows 16kb + lrow, head dims 32s + 8 lgrp (natural order)
+    f32x4 sacc[KVB][QB];
+#pragma unroll
+    for (int kb = 0; kb < KVB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < KVB; ++kb) {
+        const int r = kb * 16 + lrow;
+        bf16x8 ka;
+        if (s < DN / 32) ka = *(const lds_frag *)(kn_p + (r * 16 + ((4 * s + lgrp) ^ (r & 15))) * 8);
+        else ka = *(const lds_frag *)(kr_p + (r * 8 + ((4 * (s - DN / 32) + lgrp) ^ ((r >> 1) & 7))) * 8);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = Mma<bf16>::mma(ka, qf[qb][s], sacc[kb][qb]);
+      }
+    }
+
+    const bool diag = kvb + KVT - 1 > q0;
+    bf16x8 pf[QB][PS];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qpos = q0 + qb * 16 + lrow;
+      float sv[KVB][4];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KVB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kv = kvb + 16 * kb + 4 * lgrp + i;
+          float x = sacc[kb][qb][i] * sl2;
+          if (diag && kv > qpos) x = -INFINITY;
+          sv[kb][i] = x;
+          mt = fmaxf(mt, x);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      // the running reference max only moves when a tile exceeds it by 2^8
+      if (__any(mt > mref[qb] + 8.0f)) {
+        const float mnew = fmaxf(mref[qb], mt);
+        const float alpha = exp2f(mref[qb] - mnew);
+        mref[qb] = mnew;
+        lrun[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DVB; ++db) oacc[db][qb] *= alpha;
+      }
+      float psum = 0.f;
+      float p[KVB][4];
+#pragma unroll
+      for (int kb = 0; kb < KVB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[kb][i] = __builtin_amdgcn_exp2f(sv[kb][i] - mref[qb]);
+          psum += p[kb][i];
+        }
+      lrun[qb] += psum;
+      // slot j of lane group g in P.V step ps is key 32ps + 16(j/4) + 4g + (j%4)
+#pragma unroll
+      for (int ps = 0; ps < PS; ++ps) {
+        bf16x8 f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int jj = ps * 8 + j;
+          f[j] = (bf16)p[jj >> 2][jj & 3];
+        }
+        pf[qb][ps] = f;
+      }
+    }
+
+    // O^T += V^T . P^T: V^T rows d = 16db + lrow, the two 4-key runs of the
+    // lane group (keys 32ps + 4g.. and 32ps + 16 + 4g..)
+#pragma unroll
+    for (int ps = 0; ps < PS; ++ps)
+#pragma unroll
+      for (int db = 0; db < DVB; ++db) {
+        const int d = db * 16 + lrow, sw = (d >> 1) & 7;
+        const int k1 = 32 * ps + 4 * lgrp, k2 = k1 + 16;
+        const bf16x4 lo = *(const lds_bf16x4 *)(v_p + d * KVT + (((k1 >> 3) ^ sw) << 3) + (k1 & 7));
+        const bf16x4 hi = *(const lds_bf16x4 *)(v_p + d * KVT + (((k2 >> 3) ^ sw) << 3) + (k2 & 7));
+        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = Mma<bf16>::mma(va, pf[qb][ps], oacc[db][qb]);
+      }
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float l = lrun[qb];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int t = q0 + qb * 16 + lrow;
+    if (t < L) {
+      const float inv = 1.f / l;
+      bf16 *orow = (bf16 *)a.o + ((tok0 + t) * NH + h) * DV;
+#pragma unroll
+      for (int db = 0; db < DVB; ++db) {
+        float v[4] = {oacc[db][qb][0] * inv, oacc[db][qb][1] * inv, oacc[db][qb][2] * inv, oacc[db][qb][3] * inv};
+        store4<bf16>(orow, db * 16 + 4 * lgrp, v, 0);
+      }
+    }
+  }
+}
+
 template <typename T, int QB, int NW, int DN, int DR, int DV>
 static hipError_t launch_fp(const FlashArgs &a, hipStream_t st) {
   const int qtiles = (a.L + 16 * QB * NW - 1) / (16 * QB * NW);
@@ -290,6 +541,16 @@ static hipError_t launch_fp(const FlashArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_flash_prefill(int dtype, const FlashArgs &a, hipStream_t st) {
+  if (dtype == 1 && a.d_nope == 128 && a.d_rope == 64 && a.d_v == 128 && a.L % 8 == 0 && a.L >= 8 &&
+      (long)a.B * a.L * 2 * 128 < (1L << 31) && (long)a.n_h * 128 * 64 * 2 < (1L << 31)) {
+    constexpr int QB = FLASH_QB, NW = FLASH_NW;
+    const int qtiles = (a.L + 16 * QB * NW - 1) / (16 * QB * NW);
+    const long grid = (long)qtiles * a.B * a.n_h;
+    timing_before("flash_prefill", st);
+    hipLaunchKernelGGL((flash_prefill_dma_kernel<QB, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st, a);
+    timing_after("flash_prefill", st);
+    return hipGetLastError();
+  }
   if (dtype == 1 && a.d_nope == 128 && a.d_rope == 64 && a.d_v == 128) return launch_fp<bf16, FLASH_QB, FLASH_NW, 128, 64, 128>(a, st);
   if (dtype == 0 && a.d_nope == 32 && a.d_rope == 16 && a.d_v == 32) return launch_fp<float, 1, 4, 32, 16, 32>(a, st);
   return hipErrorInvalidValue;
