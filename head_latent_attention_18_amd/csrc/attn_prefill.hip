@@ -280,15 +280,21 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_kernel(FlashArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel for gfx950 (d_nope 128, d_R 64, d_v 128, L a multiple of 8).
-// Same work split and softmax as above; the K and V^T tiles go HBM -> LDS
-// with global_load_lds_dwordx4 into a three-stage ring (two tiles ahead, one
-// barrier per tile, no staging registers), as three sub-tiles per stage:
-// K_C rows (16 chunks of 16 bytes), k_R rows (8 chunks) and V^T rows (8
-// chunks of 8 keys).  Chunk indices are XORed with the row so that the
-// 16-row fragment reads hit distinct banks; the scores read the head
-// dimension in natural order.  Keys past the end of the sequence repeat valid
-// data (their probabilities are 0).
+// bf16 kernel for gfx950 (d_nope 128, d_R 64, d_v 128, L a multiple of 8):
+// causal flash attention over one (sequence, head, 256-query) block, 8 waves
+// of 32 queries on 32x32x16 MFMAs, with the softmax and the lazily moved
+// reference max of the kernel above.  The K_C, k_R and V^T tiles of 64 keys
+// go HBM -> LDS with global_load_lds_dwordx4 into a three-stage ring (copies
+// two tiles ahead, one barrier per tile, no staging registers); each row's
+// 16-byte chunks are XORed with the row index so that the 32-row fragment
+// reads of a quarter wave hit distinct banks.  Keys past the end of the
+// sequence repeat valid data (their probabilities are 0).
+//
+// S^T = K.Q^T for a 32-key block leaves lane (query l%32, half h = l/32)
+// holding rows 8j + 4h + i.  Loading key swap23(R) into K row R of the tile
+// (bits 2 and 3 of the row index exchanged) makes the 8 values a lane feeds
+// as P^T to P.V step m the contiguous keys 16m + 8h .. 16m + 8h + 7, so that
+// V^T is read in whole 16-byte chunks.
 // ---------------------------------------------------------------------------
 namespace {
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -318,39 +324,38 @@ __device__ inline void fp_bar() {
 }
 }  // namespace
 
-template <int QB, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void flash_prefill_dma_kernel(FlashArgs a) {
+__device__ inline int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void flash_prefill_m32_kernel(FlashArgs a) {
   constexpr int DN = 128, DR = 64, DV = 128, KVT = 64, NT = 64 * NW;
-  constexpr int KVB = KVT / 16, QS = (DN + DR) / 32, PS = KVT / 32, DVB = DV / 16;
+  constexpr int QS = (DN + DR) / 16, DVB = DV / 32;
   constexpr int KN_E = KVT * DN, KR_E = KVT * DR, V_E = DV * KVT;
   constexpr int STAGE = KN_E + KR_E + V_E;       // elements (40 KB)
   constexpr int NS = 3;
   constexpr int LKN = KN_E / 8 / NT, LKR = KR_E / 8 / NT, LV = V_E / 8 / NT;
-  constexpr int LOADS = LKN + LKR + LV;          // copy instructions per wave per tile
-  constexpr int BQ = 16 * QB * NW;
+  constexpr int LOADS = LKN + LKR + LV;
+  constexpr int BQ = 32 * NW;
   static_assert(KN_E % (8 * NT) == 0 && KR_E % (8 * NT) == 0 && V_E % (8 * NT) == 0, "");
   typedef __attribute__((address_space(3))) bf16 lds_T;
   typedef __attribute__((address_space(3))) bf16x8 lds_frag;
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
   __shared__ __attribute__((aligned(16))) bf16 stages[NS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lrow = lane & 15, lgrp = lane >> 4;
+  const int lc = lane & 31, hh = lane >> 5;
   const int L = a.L, NH = a.n_h;
   const int qtiles = (L + BQ - 1) / BQ;
 
-  // block -> (query tile, longest first; sequence; head), heads interleaved
-  // over the XCDs (see above)
   int bid = blockIdx.x, h, b, qt_rev;
   if ((NH & 7) == 0) {
     const int hx = bid & 7;
     int rest = bid >> 3;
-    const int hh = rest % (NH >> 3);
+    const int hq = rest % (NH >> 3);
     rest /= (NH >> 3);
     b = rest % a.B;
     qt_rev = rest / a.B;
-    h = hh * 8 + hx;
+    h = hq * 8 + hx;
   } else {
     h = bid % NH;
     int rest = bid / NH;
@@ -360,29 +365,25 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_dma_kernel(FlashArgs
   const int qt = qtiles - 1 - qt_rev;
   const long tok0 = (long)b * L;
   const long ntok = (long)a.B * L;
-  const int q0 = qt * BQ + wave * 16 * QB;
-  const int wave_qmax = min(q0 + 16 * QB - 1, L - 1);
+  const int q0 = qt * BQ + wave * 32;
+  const int qpos = q0 + lc;
+  const int wave_qmax = min(q0 + 31, L - 1);
   const int blk_qmax = min(qt * BQ + BQ - 1, L - 1);
   const float sl2 = a.scale_log2;
 
-  bf16x8 qf[QB][QS];
+  bf16x8 qf[QS];
+  {
+    const bf16 *qrow = (const bf16 *)a.q + ((tok0 + min(qpos, L - 1)) * NH + h) * (DN + DR) + hh * 8;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int t = min(q0 + qb * 16 + lrow, L - 1);
-    const bf16 *qrow = (const bf16 *)a.q + ((tok0 + t) * NH + h) * (DN + DR) + lgrp * 8;
-#pragma unroll
-    for (int s = 0; s < QS; ++s) qf[qb][s] = *(const bf16x8 *)(qrow + s * 32);
+    for (int s = 0; s < QS; ++s) qf[s] = *(const bf16x8 *)(qrow + s * 16);
   }
-  f32x4 oacc[DVB][QB];
+  f32x16 oacc[DVB];
 #pragma unroll
   for (int i = 0; i < DVB; ++i)
 #pragma unroll
-    for (int j = 0; j < QB; ++j) oacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mref[QB], lrun[QB];
-#pragma unroll
-  for (int j = 0; j < QB; ++j) { mref[j] = -1e30f; lrun[j] = 0.f; }
+    for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
+  float mref = -1e30f, lrun = 0.f;
 
-  // copies of tile t into stage t % 3
   const unsigned lds0 = (unsigned)(size_t)(lds_void_t *)stages;
   auto issue = [&](int t) {
     const int kvb = t * KVT;
@@ -394,12 +395,12 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_dma_kernel(FlashArgs
 #pragma unroll
     for (int i = 0; i < LKN; ++i) {
       const int sl = i * NT + tid, r = sl >> 4, c = (sl & 15) ^ (r & 15);
-      fp_dma16(kn, (unsigned)(min(r, last) * NH * DN + c * 8) * 2u, dst + i * NT * 16);
+      fp_dma16(kn, (unsigned)(min(swap23(r), last) * NH * DN + c * 8) * 2u, dst + i * NT * 16);
     }
 #pragma unroll
     for (int i = 0; i < LKR; ++i) {
       const int sl = i * NT + tid, r = sl >> 3, c = (sl & 7) ^ ((r >> 1) & 7);
-      fp_dma16(kr, (unsigned)(min(r, last) * DR + c * 8) * 2u, dst + (KN_E * 2) + i * NT * 16);
+      fp_dma16(kr, (unsigned)(min(swap23(r), last) * DR + c * 8) * 2u, dst + (KN_E * 2) + i * NT * 16);
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
@@ -410,123 +411,106 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_dma_kernel(FlashArgs
   };
 
   const int ntiles = blk_qmax / KVT + 1;
-  fp_wait_vm<0>();   // queries in registers before the copies start
+  fp_wait_vm<0>();
   issue(0);
   if (ntiles > 1) issue(1);
   const lds_T *st0 = (const lds_T *)stages;
   for (int t = 0; t < ntiles; ++t) {
     const int kvb = t * KVT;
-    // every LDS read of tile t-1 done, tile t landed (tile t+1 may stay in flight)
     if (t + 1 < ntiles) fp_wait_vm_lgkm<LOADS>();
     else fp_wait_vm_lgkm<0>();
-    fp_bar();   // tile t landed for every wave; stage (t+2) % 3 was last read at tile t-1
+    fp_bar();
     if (t + 2 < ntiles) issue(t + 2);
-    if (kvb > wave_qmax) continue;   // every key of this tile is after every query of this wave
+    if (kvb > wave_qmax) continue;
     const lds_T *kn_p = st0 + (t % NS) * STAGE;
     const lds_T *kr_p = kn_p + KN_E;
     const lds_T *v_p = kr_p + KR_E;
 
-    // S^T = K . Q^T: key rows 16kb + lrow, head dims 32s + 8 lgrp (natural order)
-    f32x4 sacc[KVB][QB];
+    f32x16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < KVB; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
 #pragma unroll
     for (int s = 0; s < QS; ++s) {
 #pragma unroll
-      for (int kb = 0; kb < KVB; ++kb) {
-        const int r = kb * 16 + lrow;
+      for (int kb = 0; kb < 2; ++kb) {
+        const int r = kb * 32 + lc;
         bf16x8 ka;
-        if (s < DN / 32) ka = *(const lds_frag *)(kn_p + (r * 16 + ((4 * s + lgrp) ^ (r & 15))) * 8);
-        else ka = *(const lds_frag *)(kr_p + (r * 8 + ((4 * (s - DN / 32) + lgrp) ^ ((r >> 1) & 7))) * 8);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = Mma<bf16>::mma(ka, qf[qb][s], sacc[kb][qb]);
+        if (s < DN / 16) ka = *(const lds_frag *)(kn_p + (r * 16 + ((2 * s + hh) ^ (r & 15))) * 8);
+        else ka = *(const lds_frag *)(kr_p + (r * 8 + ((2 * (s - DN / 16) + hh) ^ ((r >> 1) & 7))) * 8);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[kb], 0, 0, 0);
       }
     }
 
-    const bool diag = kvb + KVT - 1 > q0;
-    bf16x8 pf[QB][PS];
+    // sacc[kb][4j + i] is key kvb + 32kb + 16(j/2) + 8h + 4(j%2) + i
+    if (kvb + KVT - 1 > q0) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int qpos = q0 + qb * 16 + lrow;
-      float sv[KVB][4];
-      float mt = -INFINITY;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < KVB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kv = kvb + 16 * kb + 4 * lgrp + i;
-          float x = sacc[kb][qb][i] * sl2;
-          if (diag && kv > qpos) x = -INFINITY;
-          sv[kb][i] = x;
-          mt = fmaxf(mt, x);
+        for (int e = 0; e < 16; ++e) {
+          const int j = e >> 2, i = e & 3;
+          const int kv = kvb + 32 * kb + 16 * (j >> 1) + 8 * hh + 4 * (j & 1) + i;
+          if (kv > qpos) sacc[kb][e] = -INFINITY;
         }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      // the running reference max only moves when a tile exceeds it by 2^8
-      if (__any(mt > mref[qb] + 8.0f)) {
-        const float mnew = fmaxf(mref[qb], mt);
-        const float alpha = exp2f(mref[qb] - mnew);
-        mref[qb] = mnew;
-        lrun[qb] *= alpha;
+    }
+    float mx = sacc[0][0];
 #pragma unroll
-        for (int db = 0; db < DVB; ++db) oacc[db][qb] *= alpha;
-      }
-      float psum = 0.f;
-      float p[KVB][4];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < KVB; ++kb)
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    // the reference max only moves when a tile exceeds it by 2^8
+    if (__any(mx > mref + 8.0f)) {
+      const float mnew = fmaxf(mref, mx);
+      const float alpha = exp2f(mref - mnew);
+      mref = mnew;
+      lrun *= alpha;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[kb][i] = __builtin_amdgcn_exp2f(sv[kb][i] - mref[qb]);
-          psum += p[kb][i];
-        }
-      lrun[qb] += psum;
-      // slot j of lane group g in P.V step ps is key 32ps + 16(j/4) + 4g + (j%4)
+      for (int db = 0; db < DVB; ++db) oacc[db] *= alpha;
+    }
+    bf16x8 pf[2][2];
+    float psum = 0.f;
 #pragma unroll
-      for (int ps = 0; ps < PS; ++ps) {
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
         bf16x8 f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int jj = ps * 8 + j;
-          f[j] = (bf16)p[jj >> 2][jj & 3];
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * m + e], sl2, -mref));
+          psum += p;
+          f[e] = (bf16)p;
         }
-        pf[qb][ps] = f;
+        pf[kb][m] = f;
       }
-    }
+    lrun += psum;
 
-    // O^T += V^T . P^T: V^T rows d = 16db + lrow, the two 4-key runs of the
-    // lane group (keys 32ps + 4g.. and 32ps + 16 + 4g..)
+    // O^T += V^T . P^T over keys 32kb + 16m + 8h .. +7
 #pragma unroll
-    for (int ps = 0; ps < PS; ++ps)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int db = 0; db < DVB; ++db) {
-        const int d = db * 16 + lrow, sw = (d >> 1) & 7;
-        const int k1 = 32 * ps + 4 * lgrp, k2 = k1 + 16;
-        const bf16x4 lo = *(const lds_bf16x4 *)(v_p + d * KVT + (((k1 >> 3) ^ sw) << 3) + (k1 & 7));
-        const bf16x4 hi = *(const lds_bf16x4 *)(v_p + d * KVT + (((k2 >> 3) ^ sw) << 3) + (k2 & 7));
-        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = Mma<bf16>::mma(va, pf[qb][ps], oacc[db][qb]);
-      }
+        for (int db = 0; db < DVB; ++db) {
+          const int d = db * 32 + lc;
+          const bf16x8 va = *(const lds_frag *)(v_p + (d * 8 + ((4 * kb + 2 * m + hh) ^ ((d >> 1) & 7))) * 8);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kb][m], oacc[db], 0, 0, 0);
+        }
   }
 
+  float l = lrun + __shfl_xor(lrun, 32);
+  if (qpos < L) {
+    const float inv = 1.f / l;
+    bf16 *orow = (bf16 *)a.o + ((tok0 + qpos) * NH + h) * DV;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float l = lrun[qb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const int t = q0 + qb * 16 + lrow;
-    if (t < L) {
-      const float inv = 1.f / l;
-      bf16 *orow = (bf16 *)a.o + ((tok0 + t) * NH + h) * DV;
+    for (int db = 0; db < DVB; ++db)
 #pragma unroll
-      for (int db = 0; db < DVB; ++db) {
-        float v[4] = {oacc[db][qb][0] * inv, oacc[db][qb][1] * inv, oacc[db][qb][2] * inv, oacc[db][qb][3] * inv};
-        store4<bf16>(orow, db * 16 + 4 * lgrp, v, 0);
+      for (int j = 0; j < 4; ++j) {
+        float v[4] = {oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv, oacc[db][4 * j + 2] * inv,
+                      oacc[db][4 * j + 3] * inv};
+        store4<bf16>(orow, db * 32 + 8 * j + 4 * hh, v, 0);
       }
-    }
   }
 }
 
@@ -543,11 +527,11 @@ static hipError_t launch_fp(const FlashArgs &a, hipStream_t st) {
 hipError_t launch_flash_prefill(int dtype, const FlashArgs &a, hipStream_t st) {
   if (dtype == 1 && a.d_nope == 128 && a.d_rope == 64 && a.d_v == 128 && a.L % 8 == 0 && a.L >= 8 &&
       (long)a.B * a.L * 2 * 128 < (1L << 31) && (long)a.n_h * 128 * 64 * 2 < (1L << 31)) {
-    constexpr int QB = FLASH_QB, NW = FLASH_NW;
-    const int qtiles = (a.L + 16 * QB * NW - 1) / (16 * QB * NW);
+    constexpr int NW = 8;
+    const int qtiles = (a.L + 32 * NW - 1) / (32 * NW);
     const long grid = (long)qtiles * a.B * a.n_h;
     timing_before("flash_prefill", st);
-    hipLaunchKernelGGL((flash_prefill_dma_kernel<QB, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((flash_prefill_m32_kernel<NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st, a);
     timing_after("flash_prefill", st);
     return hipGetLastError();
   }

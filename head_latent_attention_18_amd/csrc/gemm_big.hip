@@ -29,7 +29,6 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) bf16 lds_bf16;
 typedef __attribute__((address_space(3))) float lds_float;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int GBM = 256, GBN = 256, GBK = 64;
 constexpr int GNT = 512;                        // threads (8 waves)
