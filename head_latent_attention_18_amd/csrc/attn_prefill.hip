@@ -298,6 +298,7 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_kernel(FlashArgs a) 
 // ---------------------------------------------------------------------------
 namespace {
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 template <int N>
 __device__ inline void fp_wait_vm() {
   static_assert(N >= 0 && N < 64, "");
@@ -332,17 +333,21 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_m32_kernel(FlashArgs
   constexpr int QS = (DN + DR) / 16, DVB = DV / 32;
   constexpr int KN_E = KVT * DN, KR_E = KVT * DR, V_E = DV * KVT;
   constexpr int STAGE = KN_E + KR_E + V_E;       // elements (40 KB)
-  constexpr int NS = 3;
+#ifndef FLASH_NS
+#define FLASH_NS 4
+#endif
+  constexpr int NS = FLASH_NS;   // stages (at most four fit)
+  static_assert(NS >= 2 && NS <= 4, "");
   constexpr int LKN = KN_E / 8 / NT, LKR = KR_E / 8 / NT, LV = V_E / 8 / NT;
   constexpr int LOADS = LKN + LKR + LV;
   constexpr int BQ = 32 * NW;
   static_assert(KN_E % (8 * NT) == 0 && KR_E % (8 * NT) == 0 && V_E % (8 * NT) == 0, "");
-  typedef __attribute__((address_space(3))) bf16 lds_T;
   typedef __attribute__((address_space(3))) bf16x8 lds_frag;
+  typedef __attribute__((address_space(3))) char lds_char;
 
-  __shared__ __attribute__((aligned(16))) bf16 stages[NS * STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16 stages[NS * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lc = lane & 31, hh = lane >> 5;
   const int L = a.L, NH = a.n_h;
   const int qtiles = (L + BQ - 1) / BQ;
@@ -371,27 +376,44 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_m32_kernel(FlashArgs
   const int blk_qmax = min(qt * BQ + BQ - 1, L - 1);
   const float sl2 = a.scale_log2;
 
+  // Q^T fragments with the softmax scale (in log2 units) folded in
   bf16x8 qf[QS];
   {
     const bf16 *qrow = (const bf16 *)a.q + ((tok0 + min(qpos, L - 1)) * NH + h) * (DN + DR) + hh * 8;
 #pragma unroll
-    for (int s = 0; s < QS; ++s) qf[s] = *(const bf16x8 *)(qrow + s * 16);
+    for (int s = 0; s < QS; ++s) {
+      const bf16x8 x = *(const bf16x8 *)(qrow + s * 16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[s][e] = (bf16)((float)x[e] * sl2);
+    }
   }
+  // One more (short) k-step subtracts the reference: K side all ones in k
+  // slot 0, Q side -mref (a bf16 value, so the subtraction is exact).
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  s16x4 kone = {0, 0, 0, 0}, qref = {0, 0, 0, 0};
+  if (hh == 0) kone[0] = (short)0x3f80;
   f32x16 oacc[DVB];
 #pragma unroll
   for (int i = 0; i < DVB; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
-  float mref = -1e30f, lrun = 0.f;
+  float lrun = 0.f;
+  bool bad = false;
 
+  // Copies.  Stage layout (bytes): K_C rows of 256 at 0, k_R rows of 128 at
+  // 16384, V^T rows of 128 at 24576; chunk c of row r sits at position
+  // c ^ (r & 15) (K_C) or c ^ ((r >> 1) & 7) (k_R, V^T).
   const unsigned lds0 = (unsigned)(size_t)(lds_void_t *)stages;
   auto issue = [&](int t) {
     const int kvb = t * KVT;
-    const int last = min(KVT, L - kvb) - 1;
     const unsigned dst = lds0 + (unsigned)((t % NS) * STAGE * 2) + wave * 1024;
     const char *kn = (const char *)((const bf16 *)a.k + ((tok0 + kvb) * NH + h) * DN);
     const char *kr = (const char *)((const bf16 *)a.kr + (tok0 + kvb) * DR);
-    const char *vt = (const char *)((const bf16 *)a.vt + (long)h * DV * ntok + tok0);
+    const char *vt = (const char *)((const bf16 *)a.vt + (long)h * DV * ntok + tok0 + kvb);
+    // rows past the end repeat the last key, V^T chunks past the end repeat
+    // the last 8 keys (their probabilities are 0)
+    const int last = min(KVT, L - kvb) - 1;
+    const int vlast = min(KVT, L - kvb) - 8;
 #pragma unroll
     for (int i = 0; i < LKN; ++i) {
       const int sl = i * NT + tid, r = sl >> 4, c = (sl & 15) ^ (r & 15);
@@ -400,48 +422,73 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_m32_kernel(FlashArgs
 #pragma unroll
     for (int i = 0; i < LKR; ++i) {
       const int sl = i * NT + tid, r = sl >> 3, c = (sl & 7) ^ ((r >> 1) & 7);
-      fp_dma16(kr, (unsigned)(min(swap23(r), last) * DR + c * 8) * 2u, dst + (KN_E * 2) + i * NT * 16);
+      fp_dma16(kr, (unsigned)(min(swap23(r), last) * DR + c * 8) * 2u, dst + KN_E * 2 + i * NT * 16);
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
       const int sl = i * NT + tid, d = sl >> 3, c = (sl & 7) ^ ((d >> 1) & 7);
-      const int col = min(kvb + c * 8, L - 8);
-      fp_dma16(vt, (unsigned)((long)d * ntok + col) * 2u, dst + (KN_E + KR_E) * 2 + i * NT * 16);
+      fp_dma16(vt, (unsigned)((long)d * ntok + min(c * 8, vlast)) * 2u, dst + (KN_E + KR_E) * 2 + i * NT * 16);
     }
   };
 
-  const int ntiles = blk_qmax / KVT + 1;
-  fp_wait_vm<0>();
-  issue(0);
-  if (ntiles > 1) issue(1);
-  const lds_T *st0 = (const lds_T *)stages;
-  for (int t = 0; t < ntiles; ++t) {
-    const int kvb = t * KVT;
-    if (t + 1 < ntiles) fp_wait_vm_lgkm<LOADS>();
-    else fp_wait_vm_lgkm<0>();
-    fp_bar();
-    if (t + 2 < ntiles) issue(t + 2);
-    if (kvb > wave_qmax) continue;
-    const lds_T *kn_p = st0 + (t % NS) * STAGE;
-    const lds_T *kr_p = kn_p + KN_E;
-    const lds_T *v_p = kr_p + KR_E;
+  // Fragment reads.  With the stage offset so, the K_C fragment of k-step s
+  // (chunk 2s + h) for key row kb*32 + lc is at ((so + lk) ^ 32s) + 8192kb,
+  // the k_R one of step 8 + s at ((so + lr) ^ 32s) + 4096kb, and the V^T
+  // fragment of P.V step (kb, m) for rows db*32 + lc at ((so + lv) ^ (64kb +
+  // 32m)) + 4096db: the XOR only touches the chunk bits of the row.
+  const lds_char *lbase = (const lds_char *)stages;
+  const unsigned lk = lc * 256 + ((unsigned)(hh ^ (lc & 15)) << 4);
+  const unsigned lr = 16384 + lc * 128 + ((unsigned)(hh ^ ((lc >> 1) & 7)) << 4);
+  const unsigned lv = 24576 + lc * 128 + ((unsigned)(hh ^ ((lc >> 1) & 7)) << 4);
+  auto kfrag = [&](unsigned so, int s, int kb) {
+    if (s < DN / 16) return *(const lds_frag *)(lbase + (((so + lk) ^ (32u * s)) + 8192u * kb));
+    return *(const lds_frag *)(lbase + (((so + lr) ^ (32u * (s - DN / 16))) + 4096u * kb));
+  };
+  auto vfrag = [&](unsigned so, int i) {
+    const int kb = i / (2 * DVB), m = (i / DVB) & 1, db = i % DVB;
+    return *(const lds_frag *)(lbase + (((so + lv) ^ (64u * kb + 32u * m)) + 4096u * db));
+  };
 
-    f32x16 sacc[2];
+  // S^T of tile t minus the reference, in log2 units: two accumulators (the
+  // two 32-key halves), K fragments read two k-steps ahead.
+  f32x16 sacc[2];
+  auto scores = [&](int t) {
+    const unsigned so = (unsigned)((t % NS) * STAGE * 2);
+    bf16x8 kf[3][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) kf[i][kb] = kfrag(so, i, kb);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(kone, qref, sacc[kb], 0, 0, 0);
+    }
 #pragma unroll
     for (int s = 0; s < QS; ++s) {
+      if (s + 2 < QS) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int r = kb * 32 + lc;
-        bf16x8 ka;
-        if (s < DN / 16) ka = *(const lds_frag *)(kn_p + (r * 16 + ((2 * s + hh) ^ (r & 15))) * 8);
-        else ka = *(const lds_frag *)(kr_p + (r * 8 + ((2 * (s - DN / 16) + hh) ^ ((r >> 1) & 7))) * 8);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[kb], 0, 0, 0);
+        for (int kb = 0; kb < 2; ++kb) kf[(s + 2) % 3][kb] = kfrag(so, s + 2, kb);
       }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % 3][kb], qf[s], sacc[kb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  // softmax of tile t (scores in sacc) and O^T += V^T . P^T
+  auto softmax_pv = [&](int t) {
+    const int kvb = t * KVT;
+    const unsigned so = (unsigned)((t % NS) * STAGE * 2);
+    // V^T fragments of the P.V steps, in order (kb, m, db); the first ones
+    // are read before the softmax
+    constexpr int PVN = 2 * 2 * DVB, VPF = 4;
+    bf16x8 vf[VPF + 1];
+#pragma unroll
+    for (int i = 0; i < VPF; ++i) vf[i] = vfrag(so, i);
+    __builtin_amdgcn_sched_barrier(0);
 
     // sacc[kb][4j + i] is key kvb + 32kb + 16(j/2) + 8h + 4(j%2) + i
     if (kvb + KVT - 1 > q0) {
@@ -454,52 +501,77 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_m32_kernel(FlashArgs
           if (kv > qpos) sacc[kb][e] = -INFINITY;
         }
     }
-    float mx = sacc[0][0];
+    // The reference is fixed on the first tile: its row maximum, rounded up
+    // to a bf16 value.  Later probabilities may exceed 1; a row whose lane
+    // sums pass 2^40 (or overflow) is marked for exact recomputation and its
+    // output here is not used.
+    if (t == 0) {
+      float mx = sacc[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-    // the reference max only moves when a tile exceeds it by 2^8
-    if (__any(mx > mref + 8.0f)) {
-      const float mnew = fmaxf(mref, mx);
-      const float alpha = exp2f(mref - mnew);
-      mref = mnew;
-      lrun *= alpha;
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      unsigned uu = __float_as_uint(mx);
+      uu = (uu & 0x80000000u) ? (uu & 0xffff0000u) : ((uu + 0xffffu) & 0xffff0000u);
+      const float mref = __uint_as_float(uu);
 #pragma unroll
-      for (int db = 0; db < DVB; ++db) oacc[db] *= alpha;
+      for (int kb = 0; kb < 2; ++kb) sacc[kb] -= mref;
+      if (hh == 0) qref[0] = (short)(__float_as_uint(-mref) >> 16);
     }
     bf16x8 pf[2][2];
-    float psum = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         bf16x8 f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * m + e], sl2, -mref));
-          psum += p;
-          f[e] = (bf16)p;
-        }
+        for (int e = 0; e < 8; ++e) f[e] = (bf16)__builtin_amdgcn_exp2f(sacc[kb][8 * m + e]);
         pf[kb][m] = f;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          ps[e / 2] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f[e], f[e + 1]}, bf16x2{(bf16)1.f, (bf16)1.f}, ps[e / 2], false);
       }
+    const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    bad |= !(psum <= 0x1p40f);
     lrun += psum;
 
-    // O^T += V^T . P^T over keys 32kb + 16m + 8h .. +7
+    // keys 32kb + 16m + 8h .. +7
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < PVN; ++i) {
+      if (i + VPF < PVN) vf[(i + VPF) % (VPF + 1)] = vfrag(so, i + VPF);
+      const int kb = i / (2 * DVB), m = (i / DVB) & 1, db = i % DVB;
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % (VPF + 1)], pf[kb][m], oacc[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Copies run NS-1 tiles ahead of the tile read.
+  const int ntiles = blk_qmax / KVT + 1;
+  const int wtiles = wave_qmax / KVT + 1;   // tiles with a key at or before one of this wave's queries
+  fp_wait_vm<0>();   // queries in registers before the copies start
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int db = 0; db < DVB; ++db) {
-          const int d = db * 32 + lc;
-          const bf16x8 va = *(const lds_frag *)(v_p + (d * 8 + ((4 * kb + 2 * m + hh) ^ ((d >> 1) & 7))) * 8);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kb][m], oacc[db], 0, 0, 0);
-        }
+  for (int i = 0; i < NS - 1; ++i)
+    if (i < ntiles) issue(i);
+  for (int t = 0; t < ntiles; ++t) {
+    // tile t landed for every wave (the next NS-2 may stay in flight);
+    // every LDS read of iteration t-1 done
+    const int ahead = min(ntiles - 1 - t, NS - 2);
+    if (ahead >= 2) fp_wait_vm_lgkm<2 * LOADS>();
+    else if (ahead == 1) fp_wait_vm_lgkm<LOADS>();
+    else fp_wait_vm_lgkm<0>();
+    fp_bar();
+    if (t + NS - 1 < ntiles) issue(t + NS - 1);
+    if (t < wtiles) {
+      scores(t);
+      softmax_pv(t);
+    }
   }
 
-  float l = lrun + __shfl_xor(lrun, 32);
+  const float l = lrun + __shfl_xor(lrun, 32);
+  const int flag = (int)bad | __shfl_xor((int)bad, 32);
+  if (qpos < L && hh == 0) a.flags[(tok0 + qpos) * NH + h] = (unsigned char)flag;
   if (qpos < L) {
     const float inv = 1.f / l;
     bf16 *orow = (bf16 *)a.o + ((tok0 + qpos) * NH + h) * DV;
@@ -514,6 +586,79 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_m32_kernel(FlashArgs
   }
 }
 
+// Exact recomputation of the (token, head) rows that the kernel above marked:
+// scores against every visible key in fp32, their maximum, then the
+// normalised weighted sum of values, keys taken 1024 at a time.  One
+// workgroup per marked row; the flags are scanned 256 at a time.
+__global__ __launch_bounds__(256) void flash_fixup_kernel(FlashArgs a) {
+  constexpr int DN = 128, DR = 64, DV = 128, DQK = DN + DR, CH = 1024;
+  __shared__ float qs[DQK];
+  __shared__ float pbuf[CH];
+  __shared__ float red[256];
+  __shared__ int list[256];
+  __shared__ int nlist;
+  const int tid = threadIdx.x, NH = a.n_h, L = a.L;
+  const long ntok = (long)a.B * L, rows = ntok * NH;
+  const bf16 *q = (const bf16 *)a.q, *k = (const bf16 *)a.k, *kr = (const bf16 *)a.kr, *vt = (const bf16 *)a.vt;
+  for (long base = (long)blockIdx.x * 256; base < rows; base += (long)gridDim.x * 256) {
+    if (tid == 0) nlist = 0;
+    __syncthreads();
+    if (base + tid < rows && a.flags[base + tid]) list[atomicAdd(&nlist, 1)] = tid;
+    __syncthreads();
+    const int n = nlist;
+    for (int j = 0; j < n; ++j) {
+      const long row = base + list[j], tok = row / NH;
+      const int h = (int)(row % NH), t = (int)(tok % L);
+      const long tok0 = tok - t;
+      if (tid < DQK) qs[tid] = (float)q[row * DQK + tid];
+      __syncthreads();
+      auto score = [&](int key) {
+        const bf16 *kc = k + ((tok0 + key) * NH + h) * DN, *krr = kr + (tok0 + key) * DR;
+        float acc = 0.f;
+        for (int i = 0; i < DN; ++i) acc += qs[i] * (float)kc[i];
+        for (int i = 0; i < DR; ++i) acc += qs[DN + i] * (float)krr[i];
+        return acc * a.scale_log2;
+      };
+      float mx = -INFINITY;
+      for (int key = tid; key <= t; key += 256) mx = fmaxf(mx, score(key));
+      red[tid] = mx;
+      __syncthreads();
+      for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+        __syncthreads();
+      }
+      const float m = red[0];
+      __syncthreads();
+      const int d = tid & (DV - 1), half = tid >> 7;
+      float lsum = 0.f, oacc = 0.f;
+      for (int c0 = 0; c0 <= t; c0 += CH) {
+        const int c1 = min(c0 + CH, t + 1);
+        for (int key = c0 + tid; key < c1; key += 256) {
+          const float pr = exp2f(score(key) - m);
+          pbuf[key - c0] = pr;
+          lsum += pr;
+        }
+        __syncthreads();
+        const bf16 *vrow = vt + (long)(h * DV + d) * ntok + tok0;
+        for (int key = c0 + half; key < c1; key += 2) oacc += pbuf[key - c0] * (float)vrow[key];
+        __syncthreads();
+      }
+      red[tid] = lsum;
+      __syncthreads();
+      for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) red[tid] += red[tid + w];
+        __syncthreads();
+      }
+      const float l = red[0];
+      __syncthreads();
+      red[tid] = oacc;
+      __syncthreads();
+      if (tid < DV) ((bf16 *)a.o)[row * DV + d] = (bf16)((red[tid] + red[tid + DV]) / l);
+      __syncthreads();
+    }
+  }
+}
+
 template <typename T, int QB, int NW, int DN, int DR, int DV>
 static hipError_t launch_fp(const FlashArgs &a, hipStream_t st) {
   const int qtiles = (a.L + 16 * QB * NW - 1) / (16 * QB * NW);
@@ -525,7 +670,7 @@ static hipError_t launch_fp(const FlashArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_flash_prefill(int dtype, const FlashArgs &a, hipStream_t st) {
-  if (dtype == 1 && a.d_nope == 128 && a.d_rope == 64 && a.d_v == 128 && a.L % 8 == 0 && a.L >= 8 &&
+  if (dtype == 1 && a.d_nope == 128 && a.d_rope == 64 && a.d_v == 128 && a.L % 8 == 0 && a.L >= 8 && a.flags &&
       (long)a.B * a.L * 2 * 128 < (1L << 31) && (long)a.n_h * 128 * 64 * 2 < (1L << 31)) {
     constexpr int NW = 8;
     const int qtiles = (a.L + 32 * NW - 1) / (32 * NW);
@@ -533,6 +678,13 @@ hipError_t launch_flash_prefill(int dtype, const FlashArgs &a, hipStream_t st) {
     timing_before("flash_prefill", st);
     hipLaunchKernelGGL((flash_prefill_m32_kernel<NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st, a);
     timing_after("flash_prefill", st);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long rows = (long)a.B * a.L * a.n_h;
+    const long fgrid = std::min<long>((rows + 255) / 256, 1024);
+    timing_before("flash_fixup", st);
+    hipLaunchKernelGGL(flash_fixup_kernel, dim3((unsigned)fgrid), dim3(256), 0, st, a);
+    timing_after("flash_fixup", st);
     return hipGetLastError();
   }
   if (dtype == 1 && a.d_nope == 128 && a.d_rope == 64 && a.d_v == 128) return launch_fp<bf16, FLASH_QB, FLASH_NW, 128, 64, 128>(a, st);

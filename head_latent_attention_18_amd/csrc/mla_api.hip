@@ -91,7 +91,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Workspace plans
 // ---------------------------------------------------------------------------
 struct PrefillPlan {
-  size_t c_q, ckv, kr, q, k, vt, o, total;
+  size_t c_q, ckv, kr, q, k, vt, o, flags, total;
 };
 PrefillPlan plan_prefill(const mla_config *c, int64_t T) {
   const size_t e = esize(c);
@@ -105,6 +105,7 @@ PrefillPlan plan_prefill(const mla_config *c, int64_t T) {
   p.k = take((size_t)T * c->n_heads * c->d_nope * e);
   p.vt = take((size_t)T * c->n_heads * c->d_v * e);
   p.o = take((size_t)T * c->n_heads * c->d_v * e);
+  p.flags = take((size_t)T * c->n_heads);
   p.total = off;
   return p;
 }
@@ -480,6 +481,7 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
     f.kr = ws + p.kr;
     f.vt = ws + p.vt;
     f.o = o;
+    f.flags = (unsigned char *)(ws + p.flags);
     f.B = batch;
     f.L = len;
     f.n_h = NH;
