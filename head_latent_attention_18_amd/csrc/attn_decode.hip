@@ -670,31 +670,44 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int nsp = len > 0 ? min(a.n_splits, (len + a.chunk - 1) / a.chunk) : 0;
   const long base = (long)b * a.n_splits * R + r;
   T *out = (T *)a.o_lat + row * DC;
+  // split weights: lane s holds split s (for up to 64 splits; more are
+  // read in rounds)
   float lmax = -INFINITY;
   bool flagged = false;
-  for (int s = 0; s < nsp; ++s) {
-    const float ls = a.lse_part[base + (long)s * R];
+  for (int s0 = 0; s0 < nsp; s0 += 64) {
+    const float ls = s0 + lane < nsp ? a.lse_part[base + (long)(s0 + lane) * R] : -INFINITY;
     flagged |= ls != ls;
     lmax = fmaxf(lmax, ls);
   }
-  if (flagged) {
+  if (__any(flagged)) {
     decode_row_exact<T, DC, DR>(a, b, r, len, out);
     return;
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, o));
   // lane owns PER consecutive latent columns (one 16-byte load per split for
-  // bf16 and d_c = 512)
+  // bf16 and d_c = 512); loads of 8 splits are issued together
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   float wsum = 0.f;
-  for (int s = 0; s < nsp; ++s) {
-    const float ls = a.lse_part[base + (long)s * R];
-    const float w = (ls == -INFINITY) ? 0.f : exp2f(ls - lmax);
-    wsum += w;
-    const T *op = (const T *)a.o_part + (base + (long)s * R) * DC + lane * PER;
-    const Pack<T, PER> v = *(const Pack<T, PER> *)op;
+  constexpr int SB = 8;
+  for (int s0 = 0; s0 < nsp; s0 += SB) {
+    Pack<T, PER> v[SB];
+    float w[SB];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += w * to_f32(v.x[i]);
+    for (int j = 0; j < SB; ++j) {
+      const int s = min(s0 + j, nsp - 1);
+      v[j] = *(const Pack<T, PER> *)((const T *)a.o_part + (base + (long)s * R) * DC + lane * PER);
+      const float ls = a.lse_part[base + (long)s * R];
+      w[j] = (s0 + j >= nsp || ls == -INFINITY) ? 0.f : exp2f(ls - lmax);
+    }
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      wsum += w[j];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] += w[j] * to_f32(v[j].x[i]);
+    }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   Pack<T, PER> o;
