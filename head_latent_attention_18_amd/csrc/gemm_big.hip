@@ -201,14 +201,70 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
       // a thread always handles the same 4 features (GNT is a multiple of
       // GBN / 4): their column plan is prepared once, outside the row loop
       const int f = (tid % (GBN / 4)) * 4, n = n0 + f;
+      constexpr int TS = GNT / (GBN / 4), IT = 128 / TS;   // rows between a thread's items, items
+      const int t0 = tid / (GBN / 4);
       if (n < a.N) {
         const ColPlan cp = col_plan(a.epi, n);
-        for (int t = tid / (GBN / 4); t < 128; t += GNT / (GBN / 4)) {
-          const int m = mh + t;
-          if (m < a.M) {
-            const f32x4 v4 = *(const lds_f32x4 *)(ep + t * EPI_LD + f);
+        if (cp.kind != SEG_CACHE && !cp.dst2 && !cp.out_f32 && (!cp.rope || a.epi.rows.mode == ROWS_DENSE)) {
+          // Plain and head-layout columns: all items are formed first and
+          // stored afterwards, each store with registers of its own (a store
+          // whose source registers are rewritten has to complete first, which
+          // would serialise the stores).  Rows advance by TS per item; the
+          // RoPE angles turn by TS positions per item (exact at the first row
+          // and wherever a new sequence starts).
+          bf16 *base = (bf16 *)cp.dst + cp.col;
+          int m = mh + t0, seq = 0, pos = 0;
+          float sn[2] = {0.f, 0.f}, cs[2] = {1.f, 1.f}, st[2] = {0.f, 0.f}, ct[2] = {1.f, 1.f};
+          const int per = a.epi.rows.per_seq;
+          if (cp.rope) {
+            seq = m / per;
+            pos = m - seq * per;
+            rope_sincos(pos, cp.inv0, sn[0], cs[0]);
+            rope_sincos(pos, cp.inv1, sn[1], cs[1]);
+            rope_sincos(TS, cp.inv0, st[0], ct[0]);
+            rope_sincos(TS, cp.inv1, st[1], ct[1]);
+          }
+          bf16x4 ov[IT];
+#pragma unroll
+          for (int i = 0; i < IT; ++i) {
+            const f32x4 v4 = *(const lds_f32x4 *)(ep + (t0 + i * TS) * EPI_LD + f);
             float v[4] = {v4[0], v4[1], v4[2], v4[3]};
-            col_store<bf16>(cp, a.epi, 0, m, v);
+            if (cp.rope) {
+#pragma unroll
+              for (int q = 0; q < 2; ++q) {
+                const float x0 = v[2 * q], x1 = v[2 * q + 1];
+                v[2 * q] = x0 * cs[q] - x1 * sn[q];
+                v[2 * q + 1] = x0 * sn[q] + x1 * cs[q];
+              }
+              pos += TS;
+              if (pos >= per) {
+                seq += pos / per;
+                pos %= per;
+                rope_sincos(pos, cp.inv0, sn[0], cs[0]);
+                rope_sincos(pos, cp.inv1, sn[1], cs[1]);
+              } else {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                  const float c = cs[q] * ct[q] - sn[q] * st[q];
+                  sn[q] = sn[q] * ct[q] + cs[q] * st[q];
+                  cs[q] = c;
+                }
+              }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ov[i][e] = (bf16)(v[e] * cp.scale);
+          }
+#pragma unroll
+          for (int i = 0; i < IT; ++i)
+            if (m + i * TS < a.M) *(bf16x4 *)(base + (long)(m + i * TS) * cp.ld) = ov[i];
+        } else {
+          for (int t = t0; t < 128; t += TS) {
+            const int m = mh + t;
+            if (m < a.M) {
+              const f32x4 v4 = *(const lds_f32x4 *)(ep + t * EPI_LD + f);
+              float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+              col_store<bf16>(cp, a.epi, 0, m, v);
+            }
           }
         }
       }
