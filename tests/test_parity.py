@@ -90,39 +90,41 @@ def test_dsv3_prefill_small(B, L):
     _prefill_check(wl, layer)
 
 
-def test_dsv3_prefill_large_logit_spread():
-    """The hidden state of token 100 scaled by 16: for later queries its key
-    scores far above the first 32 keys (by more than the flash kernel's
-    fixed-reference range in many heads), so those (query, head) rows take
-    the exact recomputation path; they match the oracle like every other
-    row.  Token 100's own query row is left out: scaled twice (query and
-    key), its scores reach magnitudes where rounding q and k to bf16 already
-    moves the softmax weights by more than the bf16 bounds, whatever the
-    attention kernel does."""
+@pytest.mark.parametrize("B,L,tb", [(1, 520, 100), (2, 264, 70)])
+def test_dsv3_prefill_large_logit_spread(B, L, tb):
+    """The hidden state of one token (tb, in the last sequence) scaled by 16:
+    for later queries its key scores far above the first keys (by more than
+    the flash kernel's fixed-reference range in many heads), so those
+    (query, head) rows take the exact recomputation path; they match the
+    oracle like every other row.  The scaled token's own query row is left
+    out: scaled twice (query and key), its scores reach magnitudes where
+    rounding q and k to bf16 already moves the softmax weights by more than
+    the bf16 bounds, whatever the attention kernel does."""
     from mla_inputs import bf16_bits_to_f32, bf16_round
-    wl = make_workload(3, batch=1, seq_len=520)
-    tb = 100
-    big = bf16_round(wl.h_f32[0][tb] * 16.0)
-    wl.h_bits[0][tb] = big
-    wl.h_f32[0][tb] = bf16_bits_to_f32(big)
+    wl = make_workload(3, batch=B, seq_len=L)
+    sb = B - 1   # the scaled token sits in the last sequence
+    big = bf16_round(wl.h_f32[sb][tb] * 16.0)
+    wl.h_bits[sb][tb] = big
+    wl.h_f32[sb][tb] = bf16_bits_to_f32(big)
     layer = layer_for(wl)
-    d, L = wl.dims, wl.seq_len
+    d = wl.dims
     h = upload(wl.h_f32, wl.h_bits, True)
-    say("prefill with large logit spread B=1 L=520")
-    u, o = layer.prefill(h, layer.new_cache(1, L), want_o=True)
+    say(f"prefill with large logit spread B={B} L={L} token {tb} of sequence {sb}")
+    u, o = layer.prefill(h, layer.new_cache(B, L), want_o=True)
     torch.cuda.synchronize()
-    keep = np.setdiff1d(np.arange(L), [tb])
-    with Timer("oracle prefill"):
-        ref = O.prefill(d, weights64(wl), wl.h_f32[0].astype(np.float64), rows=keep)
-    sel = torch.from_numpy(keep).cuda()
     from tests.gpu_harness import BF16_MAX_ABS, BF16_REL_FROB, err
-    for what, got, r in (("u", u[0, sel], ref["u"]), ("o", o.view(1, L, d.n_heads, d.d_v)[0, sel], ref["o"])):
-        # the scaled key raises the outputs' magnitude, so the max-abs bound
-        # is taken relative to max(1, max|oracle|)
-        e = err(got, r)
-        mag = max(1.0, float(np.max(np.abs(r))))
-        say(f"{what}: max_abs={e.max_abs:.3e} (max|ref|={mag:.1f}) rel_frob={e.rel_frob:.3e}")
-        assert e.rel_frob <= BF16_REL_FROB and e.max_abs <= BF16_MAX_ABS * mag, (what, e)
+    for b in range(B):
+        keep = np.setdiff1d(np.arange(L), [tb]) if b == sb else np.arange(L)
+        with Timer(f"oracle prefill b={b}"):
+            ref = O.prefill(d, weights64(wl), wl.h_f32[b].astype(np.float64), rows=keep)
+        sel = torch.from_numpy(keep).cuda()
+        for what, got, r in (("u", u[b, sel], ref["u"]), ("o", o.view(B, L, d.n_heads, d.d_v)[b, sel], ref["o"])):
+            # the scaled key raises the outputs' magnitude, so the max-abs
+            # bound is taken relative to max(1, max|oracle|)
+            e = err(got, r)
+            mag = max(1.0, float(np.max(np.abs(r))))
+            say(f"{what} b={b}: max_abs={e.max_abs:.3e} (max|ref|={mag:.1f}) rel_frob={e.rel_frob:.3e}")
+            assert e.rel_frob <= BF16_REL_FROB and e.max_abs <= BF16_MAX_ABS * mag, (what, b, e)
 
 
 def test_dsv3_prefill_paged():
