@@ -1,23 +1,31 @@
-// Causal MLA prefill attention, flash-style (tiled, exact online softmax),
-// in the up-projected form of section 2.1 of the DeepSeek-V3 paper-reading
-// notes: for head i, q = [q_C,i ; q_R,i] against k = [k_C,j,i ; k_R,j] (k_R
-// shared by all heads), values v_j,i, scale 1/sqrt(d_h + d_R).
+// Causal MLA prefill attention, flash-style (tiled, exact softmax), in the
+// up-projected form of section 2.1 of the DeepSeek-V3 paper-reading notes:
+// for head i, q = [q_C,i ; q_R,i] against k = [k_C,j,i ; k_R,j] (k_R shared
+// by all heads), values v_j,i, scale 1/sqrt(d_h + d_R).
 //
-// One workgroup = (sequence, head, 64*QB queries); four waves of 16*QB
-// queries each walk the 64-key tiles up to the diagonal.  Scores are formed
+// Common to the kernels here: one workgroup = (sequence, head, block of
+// queries), its waves walk the 64-key tiles up to the diagonal, query blocks
+// start from the longest (causal work imbalance).  Scores are formed
 // transposed (S^T = K . Q^T) so that each lane owns one query column: the
-// softmax max/sum are lane-local plus two shuffles, and after permuting the
-// key rows of the A operand the probabilities are already the B operand of
+// softmax max/sum are lane-local plus a shuffle, and after permuting the key
+// rows of the A operand the probabilities are already the B operand of
 // O^T += V^T . P^T.  V arrives transposed ([n_h*d_v][tokens], written that
-// way by the V up-projection), so both contractions read 16-byte runs from
-// LDS.  Tiles start from the longest query blocks (causal work imbalance).
+// way by the V up-projection), so both contractions read 16-byte runs.
+//
+//   flash_prefill_m32_kernel  bf16, lengths a multiple of 8: 32x32x16 MFMAs,
+//                             copy-fed LDS ring, softmax reference fixed on
+//                             the first tile (rows that outgrow it are
+//                             recomputed by flash_fixup_kernel);
+//   flash_prefill_kernel      fp32, and bf16 at other lengths: tiles staged
+//                             through registers, 16x16 MFMAs, reference
+//                             moved lazily.
 #include "mla_internal.h"
 
 namespace mla {
 
 #ifndef FLASH_QB
-#define FLASH_QB 2   // 16-query blocks per wave
-#define FLASH_NW 8   // waves per workgroup
+#define FLASH_QB 2   // 16-query blocks per wave (flash_prefill_kernel, bf16)
+#define FLASH_NW 8   // waves per workgroup (flash_prefill_kernel, bf16)
 #endif
 
 template <typename T, int QB, int NW, int DN, int DR, int DV>
