@@ -290,13 +290,13 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_kernel(FlashArgs a) 
 // ---------------------------------------------------------------------------
 // bf16 kernel for gfx950 (d_nope 128, d_R 64, d_v 128, L a multiple of 8):
 // causal flash attention over one (sequence, head, 256-query) block, 8 waves
-// of 32 queries on 32x32x16 MFMAs, with the softmax and the lazily moved
-// reference max of the kernel above.  The K_C, k_R and V^T tiles of 64 keys
-// go HBM -> LDS with global_load_lds_dwordx4 into a three-stage ring (copies
-// two tiles ahead, one barrier per tile, no staging registers); each row's
+// of 32 queries on 32x32x16 MFMAs.  The K_C, k_R and V^T tiles of 64 keys go
+// HBM -> LDS with global_load_lds_dwordx4 into a four-stage ring (copies
+// three tiles ahead, one barrier per tile, no staging registers); each row's
 // 16-byte chunks are XORed with the row index so that the 32-row fragment
 // reads of a quarter wave hit distinct banks.  Keys past the end of the
-// sequence repeat valid data (their probabilities are 0).
+// sequence repeat valid data (their probabilities are 0).  The softmax
+// reference of a row is fixed on the first tile (see the kernel body).
 //
 // S^T = K.Q^T for a 32-key block leaves lane (query l%32, half h = l/32)
 // holding rows 8j + 4h + i.  Loading key swap23(R) into K row R of the tile
