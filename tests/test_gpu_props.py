@@ -1,7 +1,7 @@
 """Properties of the GPU path that hold at any size: run-to-run determinism,
 paged == contiguous, independence of the split plan, causality, prefill +
-decode == one longer prefill, and the standalone cache-compression entry
-point."""
+decode == one longer prefill, chunked prefill over a ragged paged cache ==
+one longer prefill, and the standalone cache-compression entry point."""
 import numpy as np
 import pytest
 import torch
@@ -135,3 +135,40 @@ def test_compress_kv_entry_point(wid):
     c_kv, k_r = O.compress_kv(weights64(wl), hx[idx].astype(np.float64), pos[idx], d)
     got = torch.stack([cache.read_rows(int(seq[i]), [int(pos[i])])[0] for i in idx])
     assert_close(got, np.concatenate([c_kv, k_r], axis=1), wl.bf16, "compressed rows")
+
+
+def test_chunked_prefill_over_ragged_paged_cache():
+    """A chunk of new tokens per sequence against a cached prefix of a
+    different length per sequence (split-phase serving: the prefix rows
+    written by mla_compress_kv into a permuted paged cache, the chunk by
+    mla_decode with n_q = chunk, causal among its tokens) gives the rows of
+    one longer prefill of each sequence."""
+    P, C, bs = (96, 60), 40, 64
+    L = max(P) + C
+    wl = make_workload(3, batch=2, seq_len=L)
+    d = wl.dims
+    layer = layer_for(wl)
+    rng = np.random.Generator(np.random.PCG64(11))
+    nb = (L + bs - 1) // bs
+    table = rng.permutation(2 * nb).astype(np.int32).reshape(2, nb)
+    pool = torch.zeros(2 * nb * bs, d.d_row, dtype=layer.tdtype, device="cuda")
+    cache = CacheBuf.paged(pool, bs, table)
+    h = upload(wl.h_f32, wl.h_bits, True)   # [2][L][d_model]
+    # prefixes: sequence b, positions 0..P[b]-1
+    seq = np.concatenate([np.full(P[b], b, np.int32) for b in range(2)])
+    pos = np.concatenate([np.arange(P[b], dtype=np.int32) for b in range(2)])
+    hp = torch.cat([h[b, :P[b]] for b in range(2)]).contiguous()
+    layer.compress_kv(hp, torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), 2, cache)
+    # chunk: tokens P[b] .. P[b]+C-1 of each sequence
+    hc = torch.stack([h[b, P[b]:P[b] + C] for b in range(2)]).contiguous()
+    lens = torch.tensor([P[0] + C, P[1] + C], dtype=torch.int32, device="cuda")
+    say(f"chunked prefill: prefixes {P}, chunk {C}, paged block {bs}")
+    u = layer.decode(hc, lens, L, cache).clone()
+    torch.cuda.synchronize()
+    W = weights64(wl)
+    for b in range(2):
+        n = P[b] + C
+        ref = O.prefill(d, W, wl.h_f32[b, :n].astype(np.float64), rows=np.arange(P[b], n))
+        assert_close(u[b], ref["u"], True, f"chunk rows of sequence {b}")
+        got_rows = cache.read_rows(b, np.arange(n))
+        assert_close(got_rows, np.concatenate([ref["c_kv"], ref["k_r"]], axis=1), True, f"cache rows of sequence {b}")
