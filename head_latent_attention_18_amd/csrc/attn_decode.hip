@@ -57,11 +57,12 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 15, lgrp = lane >> 4;
 
-  // block -> (unit = (b, s), row group); the row groups of one unit share an XCD
+  // block -> (unit = (b, s), row group): the row groups of one unit, and the
+  // splits of one sequence, share an XCD (its L2 serves their common reads)
   const int units = a.B * a.n_splits;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int rg = slot % a.row_groups;
-  const int unit = (slot / a.row_groups) * 8 + xcd;
+  const int unit = xcd * ((units + 7) / 8) + slot / a.row_groups;
   if (unit >= units) return;
   const int b = unit / a.n_splits, s = unit % a.n_splits;
   // lengths beyond the plan or the cache are clamped, so no read leaves the cache
@@ -255,25 +256,26 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel for gfx950 (d_c = 512, d_R = 64).  The cache tile goes HBM ->
-// LDS with global_load_lds_dwordx4 (lane i's 16 bytes land at base + 16*i;
-// no staging registers) into a ring of three stages.  Per tile, two phases
-// separated by a barrier:
-//   A (scores): wave w owns query rows 32w..32w+31 and computes their scores
+// bf16 kernel for gfx950 (d_c = 512, d_R = 64), ROWS = 128 or 64 query rows
+// per workgroup.  The cache tile goes HBM -> LDS with global_load_lds_dwordx4
+// (lane i's 16 bytes land at base + 16*i; no staging registers) into a ring
+// of four stages, two tiles ahead.  Per tile, two phases separated by a
+// barrier:
+//   A (scores): wave w owns query rows (ROWS/4)w.. and computes their scores
 //     against the 32 cached rows, S^T = C . Q^T, from 16-byte row reads of the
 //     stage; the softmax is lane-local (each lane holds eight scores of one
 //     query row) plus two shuffles.  The bf16 probabilities go to LDS.
-//   B (P.V): wave w owns latent columns 128w..128w+127 for all 128 query rows:
+//   B (P.V): wave w owns latent columns 128w..128w+127 for all ROWS query rows:
 //     O^T[d][row] += C_lat^T[d][kv] . P^T[kv][row], with C_lat^T read by
 //     ds_read_b64_tr_b16 (lane i of a 16-lane group receives column i of the
 //     4x16 block of 16-bit elements the group addresses) and P^T from LDS.
 // So each wave reads the tile once as rows and only its own quarter of the
-// latent part transposed.  One wave per SIMD: 512 registers hold the queries
-// of 32 rows and the 128x128 O^T block (in AGPRs).  The softmax reference of a
-// row is the max of its first tile and never moves (no O rescale: numerator
-// and denominator share the reference, so the result is the same softmax);
-// a row whose scores later rise more than 2^32 above it is flagged and
-// recomputed exactly by the combine.
+// latent part transposed.  One wave per SIMD: at ROWS = 128, 512 registers
+// hold the queries of 32 rows and the 128x128 O^T block (in AGPRs).  The
+// softmax reference of a row is the max of its first tile and never moves (no
+// O rescale: numerator and denominator share the reference, so the result is
+// the same softmax); a row whose scores later rise more than 2^32 above it is
+// flagged and recomputed exactly by the combine.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 #ifndef DECODE_PF
@@ -326,7 +328,7 @@ __device__ inline void bar() {
   asm volatile("" ::: "memory");
 }
 
-template <int DC, int DR, bool PAGED>
+template <int DC, int DR, bool PAGED, int ROWS>
 __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
   constexpr int NW = 4, NT = 64 * NW;
   constexpr int D = DC + DR;
@@ -335,16 +337,16 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
   constexpr int STAGE = KVT * D;                     // elements per stage
   constexpr int NS = 4;                              // ring stages (two tiles ahead)
   constexpr int QS = D / 32;                         // 32-wide k steps of the scores
-  constexpr int ROWS = 128;                          // query rows per workgroup
   constexpr int HA = ROWS / (16 * NW);               // 16-row blocks per wave in the scores
   constexpr int DW = DC / NW, DBW = DW / 16;         // latent columns per wave in P.V
   constexpr int HBS = ROWS / 16;                     // 16-row blocks in P.V
   constexpr int PF = DECODE_PF;                      // score steps read ahead
-  constexpr int PVS = HBS - 2;                       // P.V row blocks interleaved with the scores
+  constexpr int PVS = HBS - HA;                      // P.V row blocks interleaved with the scores
   // P = exp2(score - reference) stays below 2^TAU, so P (bf16), l and O (fp32)
   // keep their range without ever rescaling O
   constexpr float TAU = 32.0f, MREF0 = -1e30f;
   static_assert(KVT * CH % NT == 0 && CH % 8 == 0 && DC % (16 * NW) == 0 && DBW == 8, "");
+  static_assert(ROWS % (16 * NW) == 0 && HA >= 1 && HA <= 2, "");
   static_assert(QS > PF && QS >= 2 * PVS && QS >= 2 * LOADS, "");
 
   // 4 x 36 KB stages + 2 x 8 KB of P = 160 KB.  Rows have no padding: the
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
   const int units = a.B * a.n_splits;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int rg = slot % a.row_groups;
-  const int unit = (slot / a.row_groups) * 8 + xcd;
+  const int unit = xcd * ((units + 7) / 8) + slot / a.row_groups;
   if (unit >= units) return;
   const int b = unit / a.n_splits, s = unit % a.n_splits;
   const int len = (int)min((long)a.lens[b], min((long)a.n_splits * a.chunk, a.cache.cap));
@@ -717,7 +719,15 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 }
 
 int decode_kv_tile(int) { return KVT; }
-int decode_rows_per_group(int dtype) { return dtype == 1 ? 128 : 64; }
+// Query rows per workgroup.  bf16 takes 128 (a quarter per wave), or 64 when
+// every sequence still gets at least four splits from one wave of workgroups
+// over the CUs: halving the partial results written per split, and the
+// combine's reads of them, then outweighs the second read of each cache tile
+// (an L2 hit) by the other row group.
+int decode_rows_per_group(int dtype, long B, long R, int cus) {
+  if (dtype != 1) return 64;
+  return (R <= 64 || (R <= 128 && B * 2 * 4 <= cus)) ? 64 : 128;
+}
 
 template <typename T, int NW, int HB, int DC, int DR>
 static hipError_t launch_attn(const DecodeArgs &a, hipStream_t st) {
@@ -735,14 +745,22 @@ hipError_t launch_decode_attn(int dtype, const DecodeArgs &a, hipStream_t st) {
     const int units = a.B * a.n_splits;
     const int grid = ((units + 7) / 8) * 8 * a.row_groups;
     timing_before("decode_attn", st);
-    if (a.cache.table)
-      hipLaunchKernelGGL((decode_attn_dma_kernel<512, 64, true>), dim3(grid), dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((decode_attn_dma_kernel<512, 64, false>), dim3(grid), dim3(256), 0, st, a);
+    if (a.rows == 64) {
+      if (a.cache.table)
+        hipLaunchKernelGGL((decode_attn_dma_kernel<512, 64, true, 64>), dim3(grid), dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((decode_attn_dma_kernel<512, 64, false, 64>), dim3(grid), dim3(256), 0, st, a);
+    } else {
+      if (a.cache.table)
+        hipLaunchKernelGGL((decode_attn_dma_kernel<512, 64, true, 128>), dim3(grid), dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((decode_attn_dma_kernel<512, 64, false, 128>), dim3(grid), dim3(256), 0, st, a);
+    }
     timing_after("decode_attn", st);
     return hipGetLastError();
   }
-  if (dtype == 1 && a.d_c == 512 && a.d_rope == 64) return launch_attn<bf16, 8, 1, 512, 64>(a, st);
+  if (dtype == 1 && a.d_c == 512 && a.d_rope == 64)
+    return a.rows == 64 ? launch_attn<bf16, 4, 1, 512, 64>(a, st) : launch_attn<bf16, 8, 1, 512, 64>(a, st);
   if (dtype == 0 && a.d_c == 64 && a.d_rope == 16) return launch_attn<float, 4, 1, 64, 16>(a, st);
   return hipErrorInvalidValue;
 }

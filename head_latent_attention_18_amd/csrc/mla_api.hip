@@ -144,7 +144,7 @@ SplitK choose_splitk(int dtype, int64_t M, int64_t N, int64_t K, int batch) {
 }
 
 struct DecodePlan {
-  int splits, chunk, row_groups;
+  int splits, chunk, row_groups, rows;
   SplitK sk1, sk2, sk5;
   size_t c_q, q_nope, q_abs, o_part, lse, o_lat, o, partial, total;
 };
@@ -153,8 +153,9 @@ DecodePlan plan_decode(const mla_config *c, int32_t B, int32_t n_q, int32_t max_
   const int dt = c->dtype;
   const int64_t T = (int64_t)B * n_q;
   const int64_t R = (int64_t)n_q * c->n_heads;
-  const int rows = decode_rows_per_group(dt == MLA_BF16 ? 1 : 0);
+  const int rows = decode_rows_per_group(dt == MLA_BF16 ? 1 : 0, B, R, kCUs);
   const int kvt = decode_kv_tile(dt);
+  p.rows = rows;
   p.row_groups = (int)((R + rows - 1) / rows);
   const int64_t per_seq_units = (int64_t)B * p.row_groups;
   int64_t s = (kCUs + per_seq_units - 1) / per_seq_units;
@@ -558,6 +559,7 @@ mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h
   d.chunk = p.chunk;
   d.n_splits = p.splits;
   d.row_groups = p.row_groups;
+  d.rows = p.rows;
   d.o_part = ws + p.o_part;
   d.lse_part = (float *)(ws + p.lse);
   d.o_lat = ws + p.o_lat;

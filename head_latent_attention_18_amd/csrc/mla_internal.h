@@ -333,11 +333,12 @@ struct DecodeArgs {
   int chunk;          // kv rows per split (multiple of the kv tile)
   int n_splits;       // splits per sequence in the grid
   int row_groups;     // groups of query rows (n_q*n_h rows per sequence)
+  int rows;           // query rows per group (the workgroup's share)
   void *o_part;       // [B][n_splits][n_q*n_h][d_c], normalised, in the layer's dtype
   float *lse_part;    // [B][n_splits][n_q*n_h]  (log2 units; NaN = recompute the row)
   void *o_lat;        // combine output [B*n_q][n_h][d_c]
 };
-int decode_rows_per_group(int dtype);
+int decode_rows_per_group(int dtype, long B, long R, int cus);
 int decode_kv_tile(int dtype);
 hipError_t launch_decode_attn(int dtype, const DecodeArgs &a, hipStream_t st);
 hipError_t launch_decode_combine(int dtype, const DecodeArgs &a, hipStream_t st);
