@@ -281,10 +281,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 #ifndef DECODE_PF
 #define DECODE_PF 2               // score steps of cache fragments read ahead
 #endif
-constexpr int DECODE_TBL = 256;   // block-table entries a split may span (staged in LDS)
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) bf16 lds_bf16;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
@@ -599,19 +599,28 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
+  // The normalised rows go through the (now idle) stages as bf16 [ROWS][DC],
+  // 16-byte chunk c of row r at chunk c ^ (r & 15), and leave one whole row
+  // per wave instruction: a lane's own four columns per 16-row block would
+  // make every store touch sixteen rows.
+  static_assert(ROWS * DC <= NS * STAGE && DC / 8 == 64, "");
+  lds_bf16 *ot = (lds_bf16 *)stages;
 #pragma unroll
   for (int hb = 0; hb < HBS; ++hb) {
-    const int r = rbase + hb * 16 + lrow;
-    if (r < R) {
-      const float inv = fac[hb * 16 + lrow];
-      bf16 *op = (bf16 *)a.o_part + (((long)b * a.n_splits + s) * R + r) * DC + wave * DW + 4 * lgrp;
+    const int rl = hb * 16 + lrow;
+    const float inv = fac[rl];
 #pragma unroll
-      for (int db = 0; db < DBW; ++db) {
-        const f32x4 o4 = oacc[db][hb] * inv;
-        *(bf16x4 *)(op + db * 16) = bf16x4{(bf16)o4[0], (bf16)o4[1], (bf16)o4[2], (bf16)o4[3]};
-      }
+    for (int db = 0; db < DBW; ++db) {
+      const f32x4 o4 = oacc[db][hb] * inv;
+      const int c = (wave * 16 + db * 2 + (lgrp >> 1)) ^ lrow;
+      *(lds_bf16x4 *)(ot + rl * DC + c * 8 + (lgrp & 1) * 4) =
+          bf16x4{(bf16)o4[0], (bf16)o4[1], (bf16)o4[2], (bf16)o4[3]};
     }
   }
+  __syncthreads();
+  bf16 *op = (bf16 *)a.o_part + (((long)b * a.n_splits + s) * R + rbase) * DC + lane * 8;
+  for (int rl = wave; rl < ROWS && rbase + rl < R; rl += NW)
+    *(bf16x8 *)(op + (long)rl * DC) = *(const lds_bf16x8 *)(ot + rl * DC + (lane ^ (rl & 15)) * 8);
 }
 
 // Exact attention of one query row over its whole sequence, straight from the
