@@ -623,6 +623,266 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
     *(bf16x8 *)(op + (long)rl * DC) = *(const lds_bf16x8 *)(ot + rl * DC + (lane ^ (rl & 15)) * 8);
 }
 
+// Two waves per SIMD: 64 query rows, 8 waves.  With one wave per SIMD the
+// waits of that wave (copies, LDS reads, the softmax's VALU chain) leave its
+// matrix core idle; here a second wave can issue meanwhile, and the registers
+// of each (queries of 16 rows, O^T of 64 columns x 64 rows) fit in 256.
+//   A (scores): waves w and w+4 hold the queries of rows 16(w&3)..+15; wave
+//     w scores them against cache rows 0..15 of the tile, wave w+4 against
+//     rows 16..31.  The reference of a row is the max over both halves of its
+//     first tile (exchanged once through LDS).  Each lane writes its four
+//     probabilities into its half's part of the P entry, so P has the layout
+//     of the kernel above.
+//   B (P.V): wave w owns latent columns 64w..64w+63 for all 64 rows.
+// Waves 0..3 issue the cache copies (the pattern of the kernel above).
+template <int DC, int DR, bool PAGED>
+__global__ __launch_bounds__(512, 1) void decode_attn_dma8_kernel(DecodeArgs a) {
+  constexpr int NW = 8, NC = 256;                    // waves; threads issuing copies
+  constexpr int D = DC + DR;
+  constexpr int CH = D / 8;                          // 16-byte chunks per cached row
+  constexpr int LOADS = KVT * CH / NC;               // copy instructions per copying wave per tile
+  constexpr int STAGE = KVT * D;
+  constexpr int NS = 4;                              // ring stages (two tiles ahead)
+  constexpr int QS = D / 32;
+  constexpr int ROWS = 64;
+  constexpr int DW = DC / NW, DBW = DW / 16;         // latent columns per wave in P.V
+  constexpr int HBS = ROWS / 16;
+  constexpr int PF = DECODE_PF;
+  constexpr int PVS = HBS - 1;                       // P.V row blocks interleaved with the scores
+  constexpr float TAU = 32.0f, MREF0 = -1e30f;
+  static_assert(KVT * CH % NC == 0 && DBW == 4 && QS > PF && QS >= 2 * PVS && QS >= 2 * LOADS, "");
+
+  __shared__ __attribute__((aligned(16))) bf16 stages[NS * STAGE];
+  __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2 * 4 * ROWS];   // P[buf][g][row]
+  __shared__ float xch[2][ROWS];                                       // per key half: row max, then row sum
+  __shared__ int xov[2][ROWS];                                         // per key half: row overflowed
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  const int rw = wave & 3, kh = wave >> 2;          // score roles: row block, key half
+  const int units = a.B * a.n_splits;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int rg = slot % a.row_groups;
+  const int unit = xcd * ((units + 7) / 8) + slot / a.row_groups;
+  if (unit >= units) return;
+  const int b = unit / a.n_splits, s = unit % a.n_splits;
+  const int len = (int)min((long)a.lens[b], min((long)a.n_splits * a.chunk, a.cache.cap));
+  const int kv_beg = s * a.chunk;
+  if (kv_beg >= len) return;
+  const int kv_end = min(len, kv_beg + a.chunk);
+  const int R = a.n_q * a.n_h;
+  const int rbase = rg * ROWS;
+  const float sl2 = a.scale_log2;
+  const bf16 *pool = (const bf16 *)a.cache.pool;
+  const long seq_row0 = (long)b * a.cache.max_len;
+  const unsigned lds_stages = (unsigned)(size_t)(lds_void *)stages;
+  const int ntiles = (kv_end - kv_beg + KVT - 1) / KVT;
+
+  static_assert(NC / CH == 3 && NC % CH == 40, "");
+  const int r0 = tid / CH, c0 = tid - (tid / CH) * CH;
+  auto tile_src = [&](int t) {
+    const int kvb = kv_beg + t * KVT;
+    long trow;
+    if constexpr (PAGED) {
+      const int q = block_of(a.cache, kvb);
+      const int blk = __builtin_amdgcn_readfirstlane(a.cache.table[(long)b * a.cache.max_blocks + q]);
+      trow = (long)blk * a.cache.block_size + (kvb - q * a.cache.block_size);
+    } else {
+      trow = seq_row0 + kvb;
+    }
+    return (const char *)(pool + trow * D);
+  };
+  // tile t's copies (waves 0..3 only: a wave-uniform branch)
+  auto copy_tile = [&](int t) {
+    if (wave >= NC / 64) return;
+    const char *src = tile_src(t);
+    const int last = min(KVT, kv_end - (kv_beg + t * KVT)) - 1;
+    int cr = r0, cc = c0;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int r = min(cr, last);
+      const unsigned dst = lds_stages + (unsigned)((t % NS) * STAGE * 2) + i * NC * 16 + wave * 1024;
+      dma16(src, (unsigned)(r * D + ((cc ^ (r & 7)) << 3)) * 2u, dst);
+      cc += NC % CH;
+      const bool wrap = cc >= CH;
+      cc -= wrap ? CH : 0;
+      cr += NC / CH + (wrap ? 1 : 0);
+    }
+  };
+
+  // score state: the queries of rows rbase + 16*rw..
+  bf16x8 qf[QS];
+  const int qr = min(rbase + rw * 16 + lrow, R - 1);
+  {
+    const bf16 *qrow = (const bf16 *)a.q + ((long)b * R + qr) * D + lgrp * 8;
+#pragma unroll
+    for (int q = 0; q < QS; ++q) qf[q] = *(const bf16x8 *)(qrow + q * 32);
+  }
+  const int limit = min(len - a.n_q + qr / a.n_h, kv_end - 1);
+  float mref = MREF0, lrun = 0.f;
+  bool ovf = false;
+
+  // P.V state: O^T for latent columns wave*DW.. and all ROWS rows
+  f32x4 oacc[DBW][HBS];
+#pragma unroll
+  for (int i = 0; i < DBW; ++i)
+#pragma unroll
+    for (int j = 0; j < HBS; ++j) oacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  wait_vmcnt<0>();
+  for (int t = 0; t < 2 && t < ntiles; ++t) copy_tile(t);
+
+  // score reads: the kernel above's addressing, in this wave's half of the tile
+  const int fq = (lrow >> 2) & 1, gq = lgrp ^ (lrow & 3);
+  const int a_even = (kh * 16 + lrow) * D + (4 * fq + gq) * 8;
+  const int a_odd = (kh * 16 + lrow) * D + (gq - 4 * fq) * 8;
+  // transposed reads of the wave's 64 columns (8 chunks): row r = 4*lgrp +
+  // (lrow >> 2) (and r + 16), physical chunk wave*8 + 2*(db ^ fh) + cl
+  int t_base, t_fh;
+  {
+    const int r = 4 * lgrp + (lrow >> 2), fr = r & 7;
+    const int cl = ((lrow & 3) >> 1) ^ (fr & 1), half = (lrow & 1) * 4;
+    t_base = r * D + (wave * 8 + cl) * 8 + half;
+    t_fh = fr >> 1;
+  }
+  constexpr int TRH = 16 * D;
+  const lds_bf16 *st_base = (const lds_bf16 *)stages;
+  lds_bf16x8 *pl = (lds_bf16x8 *)pbuf;
+
+  bf16x8 va[DBW];
+  auto load_v = [&](int u) {
+    const lds_bf16 *st = st_base + (u % NS) * STAGE;
+#pragma unroll
+    for (int db = 0; db < DBW; ++db) {
+      const int o = t_base + 16 * (db ^ t_fh);
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + o));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + o + TRH));
+      va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  auto pv_block = [&](int u, int hb) {
+    const bf16x8 pb = pl[((u & 1) * 4 + lgrp) * ROWS + hb * 16 + lrow];
+#pragma unroll
+    for (int db = 0; db < DBW; ++db) oacc[db][hb] = Mma<bf16>::mma(va[db], pb, oacc[db][hb]);
+  };
+
+  // Scores and softmax of tile t (stage t % NS) into P buffer t & 1, with the
+  // P.V of tile t-1 interleaved when WITH_PV; two accumulators (even and odd
+  // k steps) halve the dependent MFMA chain.
+  auto scores = [&](int t, auto with_pv_c) {
+    constexpr bool WITH_PV = decltype(with_pv_c)::value;
+    const lds_bf16 *ca_p = st_base + (t % NS) * STAGE;
+    const int kvb = kv_beg + t * KVT;
+    if (t + 2 < ntiles) copy_tile(t + 2);
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    auto rd = [&](int q) { return *(const lds_bf16x8 *)(ca_p + ((q & 1) ? a_odd : a_even) + q * 32); };
+    bf16x8 ca[PF + 1];
+#pragma unroll
+    for (int q = 0; q < PF; ++q) ca[q] = rd(q);
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      if (q + PF < QS) ca[(q + PF) % (PF + 1)] = rd(q + PF);
+      sacc[q & 1] = Mma<bf16>::mma(ca[q % (PF + 1)], qf[q], sacc[q & 1]);
+      if constexpr (WITH_PV) {
+        if (q % 2 == 1 && q / 2 < PVS) pv_block(t - 1, q / 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float sv[4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kv = kvb + 16 * kh + 4 * lgrp + i;
+      const float x = (sacc[0][i] + sacc[1][i]) * sl2;
+      sv[i] = (kv <= limit) ? x : -INFINITY;
+      mt = fmaxf(mt, sv[i]);
+    }
+    // the first tile fixes the reference of each row: the max over both key
+    // halves; later tiles only check, per lane, that they stay within TAU
+    if (t == 0) {
+      const float m16 = row_max(mt);
+      if (lgrp == 0) xch[kh][rw * 16 + lrow] = m16;
+      wait_lgkm0();
+      bar();
+      mref = fmaxf(fmaxf(xch[0][rw * 16 + lrow], xch[1][rw * 16 + lrow]), MREF0);
+    } else {
+      ovf |= mt > mref + TAU;
+    }
+    bf16x4 pf;
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float p = __builtin_amdgcn_exp2f(sv[j] - mref);
+      psum += p;
+      pf[j] = (bf16)p;
+    }
+    lrun += psum;
+    *(lds_bf16x4 *)((lds_bf16 *)(pl + ((t & 1) * 4 + lgrp) * ROWS + rw * 16 + lrow) + kh * 4) = pf;
+    if constexpr (WITH_PV) pv_block(t - 1, PVS);
+  };
+
+  auto sync = [&](int i) {
+    if (i + 1 < ntiles) wait_vmcnt<LOADS>();   // this wave's copies of tile i (none for waves 4..7)
+    else wait_vmcnt<0>();
+    wait_lgkm0();
+    bar();
+  };
+  sync(0);
+  scores(0, std::false_type());
+  for (int i = 1; i < ntiles; ++i) {
+    sync(i);
+    load_v(i - 1);
+    scores(i, std::true_type());
+  }
+  sync(ntiles);
+  load_v(ntiles - 1);
+#pragma unroll
+  for (int hb = 0; hb < HBS; ++hb) pv_block(ntiles - 1, hb);
+
+  // row sums and overflow marks of the two key halves meet in LDS
+  {
+    float l = lrun;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const bool rov = row_max(ovf ? 1.f : 0.f) > 0.f;   // any lane of the row
+    if (lgrp == 0) {
+      xch[kh][rw * 16 + lrow] = l;
+      xov[kh][rw * 16 + lrow] = rov ? 1 : 0;
+    }
+  }
+  __syncthreads();   // P no longer read: its space holds 1/l per row
+  float *fac = (float *)pbuf;
+  if (kh == 0 && lgrp == 0) {
+    const int rl = rw * 16 + lrow;
+    const float l = xch[0][rl] + xch[1][rl];
+    const bool ov = (xov[0][rl] | xov[1][rl]) != 0;
+    fac[rl] = l > 0.f ? 1.f / l : 0.f;
+    if (rbase + rl < R)
+      a.lse_part[((long)b * a.n_splits + s) * R + rbase + rl] =
+          ov ? __builtin_nanf("") : l > 0.f ? mref + log2f(l) : -INFINITY;
+  }
+  __syncthreads();
+  // normalised rows through the idle stages, then one whole row per store
+  static_assert(ROWS * DC <= NS * STAGE && DC / 8 == 64, "");
+  lds_bf16 *ot = (lds_bf16 *)stages;
+#pragma unroll
+  for (int hb = 0; hb < HBS; ++hb) {
+    const int rl = hb * 16 + lrow;
+    const float inv = fac[rl];
+#pragma unroll
+    for (int db = 0; db < DBW; ++db) {
+      const f32x4 o4 = oacc[db][hb] * inv;
+      const int c = (wave * 8 + db * 2 + (lgrp >> 1)) ^ lrow;
+      *(lds_bf16x4 *)(ot + rl * DC + c * 8 + (lgrp & 1) * 4) =
+          bf16x4{(bf16)o4[0], (bf16)o4[1], (bf16)o4[2], (bf16)o4[3]};
+    }
+  }
+  __syncthreads();
+  bf16 *op = (bf16 *)a.o_part + (((long)b * a.n_splits + s) * R + rbase) * DC + lane * 8;
+  for (int rl = wave; rl < ROWS && rbase + rl < R; rl += NW)
+    *(bf16x8 *)(op + (long)rl * DC) = *(const lds_bf16x8 *)(ot + rl * DC + (lane ^ (rl & 15)) * 8);
+}
+
 // Exact attention of one query row over its whole sequence, straight from the
 // cache, for rows an attention kernel flagged (lse = NaN): two passes, the
 // first for the max, the second for the sum and the weighted latent rows.
@@ -756,9 +1016,9 @@ hipError_t launch_decode_attn(int dtype, const DecodeArgs &a, hipStream_t st) {
     timing_before("decode_attn", st);
     if (a.rows == 64) {
       if (a.cache.table)
-        hipLaunchKernelGGL((decode_attn_dma_kernel<512, 64, true, 64>), dim3(grid), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((decode_attn_dma8_kernel<512, 64, true>), dim3(grid), dim3(512), 0, st, a);
       else
-        hipLaunchKernelGGL((decode_attn_dma_kernel<512, 64, false, 64>), dim3(grid), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((decode_attn_dma8_kernel<512, 64, false>), dim3(grid), dim3(512), 0, st, a);
     } else {
       if (a.cache.table)
         hipLaunchKernelGGL((decode_attn_dma_kernel<512, 64, true, 128>), dim3(grid), dim3(256), 0, st, a);
