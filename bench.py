@@ -47,6 +47,7 @@ def decode_kernel_bytes(d, B, n_q, sum_len, e=2):
         "decode_attn": e * (sum_len * D + T * nh * D),
         "decode_combine": e * T * nh * d.d_c,
         "unabsorb": e * (nh * d.d_v * d.d_c + T * nh * d.d_c + T * nh * d.d_v),
+        "decode_combine_uv": e * (nh * d.d_v * d.d_c + T * nh * d.d_c + T * nh * d.d_v),
         "o_proj": e * (d.d_model * nh * d.d_v + T * nh * d.d_v + T * d.d_model),
     }
 

@@ -886,9 +886,12 @@ __global__ __launch_bounds__(512, 1) void decode_attn_dma8_kernel(DecodeArgs a) 
 // Exact attention of one query row over its whole sequence, straight from the
 // cache, for rows an attention kernel flagged (lse = NaN): two passes, the
 // first for the max, the second for the sum and the weighted latent rows.
-template <typename T, int DC, int DR>
-__device__ void decode_row_exact(const DecodeArgs &a, int b, int r, int len, T *out) {
+// res[i] receives latent column col(i): lane + 64*i, or lane*PER + i when
+// CHUNKED (the lane's PER consecutive columns).
+template <typename T, int DC, int DR, bool CHUNKED>
+__device__ void decode_row_exact(const DecodeArgs &a, int b, int r, int len, float (&res)[(DC + 63) / 64]) {
   constexpr int D = DC + DR, PER = (DC + 63) / 64, QP = (D + 63) / 64;
+  static_assert(!CHUNKED || DC == 64 * PER, "");
   const int lane = threadIdx.x & 63;
   const int R = a.n_q * a.n_h;
   const T *qrow = (const T *)a.q + ((long)b * R + r) * D;
@@ -915,13 +918,14 @@ __device__ void decode_row_exact(const DecodeArgs &a, int b, int r, int len, T *
     const float p = exp2f(score(crow) - m);
     l += p;
 #pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (lane + 64 * i < DC) acc[i] += p * to_f32(crow[lane + 64 * i]);
+    for (int i = 0; i < PER; ++i) {
+      const int c = CHUNKED ? lane * PER + i : lane + 64 * i;
+      if (c < DC) acc[i] += p * to_f32(crow[c]);
+    }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-  for (int i = 0; i < PER; ++i)
-    if (lane + 64 * i < DC) out[lane + 64 * i] = from_f32<T>(acc[i] * inv);
+  for (int i = 0; i < PER; ++i) res[i] = acc[i] * inv;
 }
 
 template <typename T, int N>
@@ -951,7 +955,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     lmax = fmaxf(lmax, ls);
   }
   if (__any(flagged)) {
-    decode_row_exact<T, DC, DR>(a, b, r, len, out);
+    float res[PER];
+    decode_row_exact<T, DC, DR, false>(a, b, r, len, res);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) out[lane + 64 * i] = from_f32<T>(res[i]);
     return;
   }
 #pragma unroll
@@ -985,6 +992,158 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < PER; ++i) o.x[i] = from_f32<T>(acc[i] * inv);
   *(Pack<T, PER> *)(out + lane * PER) = o;
+}
+
+// Split combine fused with the value un-absorption o_t,i = W_UV,i o_lat,t,i
+// (W_UV applied after the attention, by the associativity of the products in
+// section 2.1 of the DeepSeek-V3 paper-reading notes), bf16, d_c = 512.  One
+// workgroup = (head i, 16 tokens): its four waves merge the splits of the 16
+// latent rows (a wave per four tokens, a lane per eight columns) into LDS,
+// rounded to bf16 as a stored o_lat would be, while W_UV,i (128 KB) streams
+// into registers; then O^T[v][t] = W_UV,i[v][:] . o_lat[t][:] on the matrix
+// cores, wave w taking features (DV/4)w...  The token groups of a head share
+// an XCD, whose L2 serves their common reads of W_UV,i.  Rows marked for
+// exact recomputation take the two-pass path of the combine kernel.
+template <int DC, int DR, int DV>
+__global__ __launch_bounds__(256, 1) void decode_combine_uv_kernel(DecodeArgs a, const bf16 *w_uv, bf16 *o) {
+  constexpr int TT = 16, NW = 4;         // tokens per workgroup, waves
+  constexpr int KS = DC / 32;            // k steps
+  constexpr int VB = DV / (16 * NW);     // 16-feature blocks per wave
+  constexpr int PER = DC / 64;           // latent columns per lane in the merge
+  constexpr int SB = 4;                  // splits per token requested up front
+  static_assert(DC == 512 && PER == 8 && VB >= 1 && DV % (16 * NW) == 0, "");
+  // token row tl of the group: 16-byte chunk c at chunk c ^ (tl & 15)
+  __shared__ __attribute__((aligned(16))) bf16 olat[TT * DC];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  const int T = a.B * a.n_q, R = a.n_q * a.n_h;
+  const int ntg = (T + TT - 1) / TT;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int h = (slot / ntg) * 8 + xcd, tg = slot % ntg;
+  if (h >= a.n_h) return;
+
+  // W_UV,i fragments (A operand): feature (wave*VB + vb)*16 + lrow, k = 32*ks + 8*lgrp..
+  bf16x8 wf[VB][KS];
+  const bf16 *wh = w_uv + (long)h * DV * DC;
+#pragma unroll
+  for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      wf[vb][ks] = *(const bf16x8 *)(wh + (long)((wave * VB + vb) * 16 + lrow) * DC + ks * 32 + lgrp * 8);
+
+  // merge: wave w takes tokens 4w..4w+3 of the group.  The log-sum-exps
+  // (lane s: split s) and the first SB partial rows of all four tokens are
+  // requested before any of them is used, so the merge costs one round trip
+  // (more splits than SB, or than 64, take extra rounds).
+  constexpr int TW = TT / NW;
+  int bq[TW], rq[TW], lq[TW], nsp[TW];
+  long base[TW];
+#pragma unroll
+  for (int j = 0; j < TW; ++j) {
+    const int t = tg * TT + wave * TW + j;
+    bq[j] = 0; rq[j] = 0; lq[j] = 0; nsp[j] = 0; base[j] = 0;
+    if (t < T) {
+      bq[j] = t / a.n_q;
+      rq[j] = (t % a.n_q) * a.n_h + h;
+      lq[j] = (int)min((long)a.lens[bq[j]], min((long)a.n_splits * a.chunk, a.cache.cap));
+      nsp[j] = lq[j] > 0 ? min(a.n_splits, (lq[j] + a.chunk - 1) / a.chunk) : 0;
+      base[j] = (long)bq[j] * a.n_splits * R + rq[j];
+    }
+  }
+  // addresses from the plan only (not from the lengths), so these loads do
+  // not wait for the length loads; splits past a sequence's end are masked
+  float ls[TW];
+  bf16x8 v[TW][SB];
+  const int lsp = min(lane, a.n_splits - 1);
+#pragma unroll
+  for (int j = 0; j < TW; ++j) ls[j] = a.lse_part[base[j] + (long)lsp * R];
+#pragma unroll
+  for (int j = 0; j < TW; ++j)
+#pragma unroll
+    for (int jj = 0; jj < SB; ++jj) {
+      const int sp = min(jj, a.n_splits - 1);
+      v[j][jj] = *(const bf16x8 *)((const bf16 *)a.o_part + (base[j] + (long)sp * R) * DC + lane * PER);
+    }
+#pragma unroll
+  for (int j = 0; j < TW; ++j) ls[j] = lane < nsp[j] ? ls[j] : -INFINITY;
+  lds_bf16 *ol = (lds_bf16 *)olat;
+#pragma unroll
+  for (int j = 0; j < TW; ++j) {
+    const int tl = wave * TW + j;
+    float res[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) res[i] = 0.f;
+    if (nsp[j] > 0) {
+      float lmax = ls[j];
+      bool flagged = ls[j] != ls[j];
+      for (int s0 = 64; s0 < nsp[j]; s0 += 64) {
+        const float x = s0 + lane < nsp[j] ? a.lse_part[base[j] + (long)(s0 + lane) * R] : -INFINITY;
+        flagged |= x != x;
+        lmax = fmaxf(lmax, x);
+      }
+      if (__any(flagged)) {
+        decode_row_exact<bf16, DC, DR, true>(a, bq[j], rq[j], lq[j], res);
+      } else {
+#pragma unroll
+        for (int o2 = 32; o2 > 0; o2 >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, o2));
+        float wsum = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < SB; ++jj) {
+          const float lsj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[j]), jj));
+          const float w = (jj < nsp[j] && lsj != -INFINITY) ? exp2f(lsj - lmax) : 0.f;
+          wsum += w;
+#pragma unroll
+          for (int i = 0; i < PER; ++i) res[i] += w * (float)v[j][jj][i];
+        }
+        for (int sp = SB; sp < nsp[j]; ++sp) {
+          const float lsj = a.lse_part[base[j] + (long)sp * R];
+          const bf16x8 vv = *(const bf16x8 *)((const bf16 *)a.o_part + (base[j] + (long)sp * R) * DC + lane * PER);
+          const float w = lsj != -INFINITY ? exp2f(lsj - lmax) : 0.f;
+          wsum += w;
+#pragma unroll
+          for (int i = 0; i < PER; ++i) res[i] += w * (float)vv[i];
+        }
+        const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) res[i] *= inv;
+      }
+    }
+    bf16x8 pk;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) pk[i] = (bf16)res[i];
+    *(lds_bf16x8 *)(ol + tl * DC + (lane ^ (tl & 15)) * 8) = pk;
+  }
+  __syncthreads();
+
+  f32x4 acc[VB];
+#pragma unroll
+  for (int vb = 0; vb < VB; ++vb) acc[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const bf16x8 xb = *(const lds_bf16x8 *)(ol + lrow * DC + (((4 * ks + lgrp) ^ lrow) * 8));
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) acc[vb] = Mma<bf16>::mma(wf[vb][ks], xb, acc[vb]);
+  }
+  // lane: features (wave*VB + vb)*16 + 4*lgrp + 0..3 of token lrow
+  const int t = tg * TT + lrow;
+  if (t < T) {
+    bf16 *orow = o + ((long)t * a.n_h + h) * DV + wave * VB * 16 + 4 * lgrp;
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb)
+      *(bf16x4 *)(orow + vb * 16) = bf16x4{(bf16)acc[vb][0], (bf16)acc[vb][1], (bf16)acc[vb][2], (bf16)acc[vb][3]};
+  }
+}
+
+hipError_t launch_decode_combine_uv(const DecodeArgs &a, int d_v, const void *w_uv, void *o, hipStream_t st) {
+  if (a.d_c != 512 || a.d_rope != 64 || d_v != 128) return hipErrorNotSupported;
+  const int T = a.B * a.n_q;
+  const int grid = ((a.n_h + 7) / 8) * 8 * ((T + 15) / 16);
+  timing_before("decode_combine_uv", st);
+  hipLaunchKernelGGL((decode_combine_uv_kernel<512, 64, 128>), dim3(grid), dim3(256), 0, st, a,
+                     (const bf16 *)w_uv, (bf16 *)o);
+  timing_after("decode_combine_uv", st);
+  return hipGetLastError();
 }
 
 int decode_kv_tile(int) { return KVT; }

@@ -565,9 +565,12 @@ mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h
   d.o_lat = ws + p.o_lat;
   e = launch_decode_attn(dt == MLA_BF16, d, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
-  e = launch_decode_combine(dt == MLA_BF16, d, st);
-  if (e != hipSuccess) return MLA_ERR_HIP;
-  {  // un-absorb: o[t][i] = W_UV,i o_lat[t][i]   (W_UV,i is [d_v][d_c])
+  e = dt == MLA_BF16 ? launch_decode_combine_uv(d, cfg->d_v, w->w_uv, o, st) : hipErrorNotSupported;
+  if (e != hipSuccess && e != hipErrorNotSupported) return MLA_ERR_HIP;
+  if (e == hipErrorNotSupported) {   // nothing was launched
+    e = launch_decode_combine(dt == MLA_BF16, d, st);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    // un-absorb: o[t][i] = W_UV,i o_lat[t][i]   (W_UV,i is [d_v][d_c])
     GemmArgs a = gemm_args(ws + p.o_lat, (long)NH * cfg->d_c, M, cfg->d_v, cfg->d_c);
     a.x_bs = cfg->d_c;
     a.w[0] = w->w_uv;

@@ -342,6 +342,9 @@ int decode_rows_per_group(int dtype, long B, long R, int cus);
 int decode_kv_tile(int dtype);
 hipError_t launch_decode_attn(int dtype, const DecodeArgs &a, hipStream_t st);
 hipError_t launch_decode_combine(int dtype, const DecodeArgs &a, hipStream_t st);
+// bf16 split combine fused with o = W_UV o_lat (hipErrorNotSupported outside
+// d_c = 512, d_R = 64, d_v = 128: then combine and un-absorb run separately)
+hipError_t launch_decode_combine_uv(const DecodeArgs &a, int d_v, const void *w_uv, void *o, hipStream_t st);
 
 // kernel timing hooks (implemented with the C ABI)
 void timing_before(const char *name, hipStream_t st);
