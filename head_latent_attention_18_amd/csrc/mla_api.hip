@@ -293,9 +293,9 @@ hipError_t run_compress(const mla_config *c, const mla_weights *w, const void *h
 
 // q = c_Q [W_UQ; W_QR]^T with RoPE on the q_R part.  The content part goes to
 // (qc, qc_ld, qc_head_ld, 0) and the rope part to (qr, qr_ld, qr_head_ld, qr_off).
-hipError_t run_query(const mla_config *c, const mla_weights *w, const void *c_q, int M, RowMap rows,
-                     void *qc, long qc_ld, long qc_head_ld, void *qr, long qr_ld, long qr_head_ld, int qr_off,
-                     SplitK sk, float *partial, hipStream_t st) {
+GemmArgs query_args(const mla_config *c, const mla_weights *w, const void *c_q, int M, RowMap rows,
+                    void *qc, long qc_ld, long qc_head_ld, void *qr, long qr_ld, long qr_head_ld, int qr_off,
+                    SplitK sk, float *partial) {
   const int dt = c->dtype;
   const int Nc = c->n_heads * c->d_nope, N = Nc + c->n_heads * c->d_rope;
   GemmArgs a = gemm_args(c_q, c->d_cq, M, N, c->d_cq);
@@ -325,7 +325,14 @@ hipError_t run_query(const mla_config *c, const mla_weights *w, const void *c_q,
   a.partial = partial;
   a.name = "q_up";
   a.reduce_name = "q_up.reduce";
-  return launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M), 1, 0, a, st);
+  return a;
+}
+
+hipError_t run_query(const mla_config *c, const mla_weights *w, const void *c_q, int M, RowMap rows,
+                     void *qc, long qc_ld, long qc_head_ld, void *qr, long qr_ld, long qr_head_ld, int qr_off,
+                     SplitK sk, float *partial, hipStream_t st) {
+  GemmArgs a = query_args(c, w, c_q, M, rows, qc, qc_ld, qc_head_ld, qr, qr_ld, qr_head_ld, qr_off, sk, partial);
+  return launch_gemm(c->dtype == MLA_BF16, gemm_tile_for(c->dtype, M), 1, 0, a, st);
 }
 
 // u = o W_O^T
@@ -525,25 +532,42 @@ mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h
 
   e = run_compress(cfg, w, h, M, rows, cache, batch, true, ws + p.c_q, nullptr, nullptr, p.sk1, partial, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
-  e = run_query(cfg, w, ws + p.c_q, M, rows, ws + p.q_nope, (long)NH * cfg->d_nope, cfg->d_nope, ws + p.q_abs,
-                (long)NH * D, D, cfg->d_c, p.sk2, partial, st);
-  if (e != hipSuccess) return MLA_ERR_HIP;
-  {  // absorption: q_abs[t][i][0:d_c] = W_UK,i^T q_C[t][i]   (W_UK,i is [d_nope][d_c])
-    GemmArgs a = gemm_args(ws + p.q_nope, (long)NH * cfg->d_nope, M, cfg->d_c, cfg->d_nope);
-    a.x_bs = cfg->d_nope;
-    a.w[0] = w->w_uk;
-    a.w_end[0] = cfg->d_c;
-    a.ldw = cfg->d_c;
-    a.w_bs = (long)cfg->d_nope * cfg->d_c;
-    a.batch = NH;
-    Seg sg = seg_plain(cfg->d_c, ws + p.q_abs, (long)NH * D);
-    sg.batch_stride = D;
-    a.epi.seg[0] = sg;
-    a.epi.nseg = 1;
-    a.partial = partial;
-    a.name = "absorb";
-    e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M), 1, 1, a, st);
+  if (dt == MLA_BF16 && decode_q_supported(cfg->d_cq, cfg->d_nope, cfg->d_rope, cfg->d_c, M)) {
+    // up-projection, RoPE and absorption in one launch
+    const GemmArgs qa = query_args(cfg, w, ws + p.c_q, M, rows, ws + p.q_nope, (long)NH * cfg->d_nope, cfg->d_nope,
+                                   ws + p.q_abs, (long)NH * D, D, cfg->d_c, p.sk2, partial);
+    DecodeQArgs q;
+    q.cq = (const bf16 *)(ws + p.c_q);
+    q.w_uq = (const bf16 *)w->w_uq;
+    q.w_qr = (const bf16 *)w->w_qr;
+    q.w_uk = (const bf16 *)w->w_uk;
+    q.q_abs = (bf16 *)(ws + p.q_abs);
+    q.T = M;
+    q.n_h = NH;
+    q.epi = qa.epi;
+    e = launch_decode_q(q, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
+  } else {
+    e = run_query(cfg, w, ws + p.c_q, M, rows, ws + p.q_nope, (long)NH * cfg->d_nope, cfg->d_nope, ws + p.q_abs,
+                  (long)NH * D, D, cfg->d_c, p.sk2, partial, st);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    {  // absorption: q_abs[t][i][0:d_c] = W_UK,i^T q_C[t][i]   (W_UK,i is [d_nope][d_c])
+      GemmArgs a = gemm_args(ws + p.q_nope, (long)NH * cfg->d_nope, M, cfg->d_c, cfg->d_nope);
+      a.x_bs = cfg->d_nope;
+      a.w[0] = w->w_uk;
+      a.w_end[0] = cfg->d_c;
+      a.ldw = cfg->d_c;
+      a.w_bs = (long)cfg->d_nope * cfg->d_c;
+      a.batch = NH;
+      Seg sg = seg_plain(cfg->d_c, ws + p.q_abs, (long)NH * D);
+      sg.batch_stride = D;
+      a.epi.seg[0] = sg;
+      a.epi.nseg = 1;
+      a.partial = partial;
+      a.name = "absorb";
+      e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M), 1, 1, a, st);
+      if (e != hipSuccess) return MLA_ERR_HIP;
+    }
   }
   DecodeArgs d;
   memset(&d, 0, sizeof(d));

@@ -312,6 +312,19 @@ hipError_t launch_gemm_big(GemmArgs &a, int swap, hipStream_t st);
 size_t gemm_stream_partial_bytes(int M);
 hipError_t launch_gemm_stream(GemmArgs &a, int wkn, hipStream_t st);
 
+// Decode query path in one launch (decode_q.hip): q_up with RoPE and the
+// absorption of W_UK, bf16 with d_cq 1536, d_nope 128, d_R 64, d_c 512 and
+// up to 32 tokens.
+struct DecodeQArgs {
+  const bf16 *cq;                     // c_Q [T][d_cq]
+  const bf16 *w_uq, *w_qr, *w_uk;     // [n_h*d_nope][d_cq], [n_h*d_R][d_cq], [n_h*d_nope][d_c]
+  bf16 *q_abs;                        // [T][n_h][d_c + d_R]: q_lat, then the roped q_R
+  int T, n_h;
+  Epi epi;                            // the up-projection's epilogue (its RoPE segment stores q_R)
+};
+bool decode_q_supported(int d_cq, int d_nope, int d_rope, int d_c, int T);
+hipError_t launch_decode_q(const DecodeQArgs &a, hipStream_t st);
+
 struct FlashArgs {
   const void *q;    // [B*L][n_h][d_nope + d_rope] (q_C, then roped q_R)
   const void *k;    // [B*L][n_h][d_nope]
