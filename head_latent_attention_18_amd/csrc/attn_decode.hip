@@ -692,16 +692,15 @@ __global__ __launch_bounds__(512, 1) void decode_attn_dma8_kernel(DecodeArgs a) 
     }
     return (const char *)(pool + trow * D);
   };
-  // tile t's copies (waves 0..3 only: a wave-uniform branch)
-  auto copy_tile = [&](int t) {
+  // copies of rows r_off..r_off+31 of src (rows past `last` repeat it) into
+  // stage st (waves 0..3 only: a wave-uniform branch)
+  auto copy_rows = [&](const char *src, int r_off, int last, int st) {
     if (wave >= NC / 64) return;
-    const char *src = tile_src(t);
-    const int last = min(KVT, kv_end - (kv_beg + t * KVT)) - 1;
     int cr = r0, cc = c0;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int r = min(cr, last);
-      const unsigned dst = lds_stages + (unsigned)((t % NS) * STAGE * 2) + i * NC * 16 + wave * 1024;
+      const int r = min(r_off + cr, last);
+      const unsigned dst = lds_stages + (unsigned)(st * STAGE * 2) + i * NC * 16 + wave * 1024;
       dma16(src, (unsigned)(r * D + ((cc ^ (r & 7)) << 3)) * 2u, dst);
       cc += NC % CH;
       const bool wrap = cc >= CH;
@@ -709,14 +708,31 @@ __global__ __launch_bounds__(512, 1) void decode_attn_dma8_kernel(DecodeArgs a) 
       cr += NC / CH + (wrap ? 1 : 0);
     }
   };
+  auto copy_tile = [&](int t) { copy_rows(tile_src(t), 0, min(KVT, kv_end - (kv_beg + t * KVT)) - 1, t % NS); };
 
-  // score state: the queries of rows rbase + 16*rw..
+  // the workgroup's 64 query rows reach LDS through stages 2 and 3 (whole
+  // rows per copy instruction; rows past the last query row repeat it) while
+  // tiles 0 and 1 are copied into stages 0 and 1
+  {
+    const char *qsrc = (const char *)((const bf16 *)a.q + ((long)b * R + rbase) * D);
+    copy_rows(qsrc, 0, R - 1 - rbase, 2);
+    copy_rows(qsrc, KVT, R - 1 - rbase, 3);
+  }
+  for (int t = 0; t < 2 && t < ntiles; ++t) copy_tile(t);
+  // this wave's query copies (the tiles may still be in flight)
+  if (ntiles >= 2) wait_vmcnt<2 * LOADS>();
+  else wait_vmcnt<LOADS>();
+  bar();
+  // score state: the queries of rows rbase + 16*rw.. (B operand), read with
+  // the tiles' chunk swizzle; stage 2 is next written by the copy of tile 2,
+  // after the barrier of sync(0), which follows these reads (lgkm wait)
   bf16x8 qf[QS];
   const int qr = min(rbase + rw * 16 + lrow, R - 1);
   {
-    const bf16 *qrow = (const bf16 *)a.q + ((long)b * R + qr) * D + lgrp * 8;
+    const int rr = (rw * 16 + lrow) & (KVT - 1);
+    const lds_bf16 *qs = (const lds_bf16 *)stages + (2 + (rw >> 1)) * STAGE + rr * D;
 #pragma unroll
-    for (int q = 0; q < QS; ++q) qf[q] = *(const bf16x8 *)(qrow + q * 32);
+    for (int q = 0; q < QS; ++q) qf[q] = *(const lds_bf16x8 *)(qs + (((4 * q + lgrp) ^ (rr & 7)) << 3));
   }
   const int limit = min(len - a.n_q + qr / a.n_h, kv_end - 1);
   float mref = MREF0, lrun = 0.f;
@@ -729,8 +745,6 @@ __global__ __launch_bounds__(512, 1) void decode_attn_dma8_kernel(DecodeArgs a) 
 #pragma unroll
     for (int j = 0; j < HBS; ++j) oacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  wait_vmcnt<0>();
-  for (int t = 0; t < 2 && t < ntiles; ++t) copy_tile(t);
 
   // score reads: the kernel above's addressing, in this wave's half of the tile
   const int fq = (lrow >> 2) & 1, gq = lgrp ^ (lrow & 3);
