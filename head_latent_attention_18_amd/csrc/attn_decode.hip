@@ -1028,6 +1028,8 @@ __global__ __launch_bounds__(256, 1) void decode_combine_uv_kernel(DecodeArgs a,
   static_assert(DC == 512 && PER == 8 && VB >= 1 && DV % (16 * NW) == 0, "");
   // token row tl of the group: 16-byte chunk c at chunk c ^ (tl & 15)
   __shared__ __attribute__((aligned(16))) bf16 olat[TT * DC];
+  // W_UV,i [DV][DC]: chunk c of row v at chunk c ^ (v & 15)
+  __shared__ __attribute__((aligned(16))) bf16 wuv[DV * DC];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lrow = lane & 15, lgrp = lane >> 4;
@@ -1037,14 +1039,19 @@ __global__ __launch_bounds__(256, 1) void decode_combine_uv_kernel(DecodeArgs a,
   const int h = (slot / ntg) * 8 + xcd, tg = slot % ntg;
   if (h >= a.n_h) return;
 
-  // W_UV,i fragments (A operand): feature (wave*VB + vb)*16 + lrow, k = 32*ks + 8*lgrp..
-  bf16x8 wf[VB][KS];
-  const bf16 *wh = w_uv + (long)h * DV * DC;
+  // W_UV,i -> LDS, whole rows per copy instruction (the merge's loads below
+  // return after these: the counter is in order)
+  {
+    constexpr int WLOADS = DV * DC / 8 / 256;
+    const unsigned lw = (unsigned)(size_t)(lds_void *)wuv;
+    const bf16 *wh = w_uv + (long)h * DV * DC;
 #pragma unroll
-  for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      wf[vb][ks] = *(const bf16x8 *)(wh + (long)((wave * VB + vb) * 16 + lrow) * DC + ks * 32 + lgrp * 8);
+    for (int j = 0; j < WLOADS; ++j) {
+      const int sl = j * 256 + threadIdx.x, v = sl / (DC / 8), pc = sl % (DC / 8);
+      const int c = pc ^ (v & 15);
+      dma16(wh, (unsigned)((v * DC + c * 8) * 2), lw + (unsigned)(j * 256 + wave * 64) * 16);
+    }
+  }
 
   // merge: wave w takes tokens 4w..4w+3 of the group.  The log-sum-exps
   // (lane s: split s) and the first SB partial rows of all four tokens are
@@ -1128,8 +1135,11 @@ __global__ __launch_bounds__(256, 1) void decode_combine_uv_kernel(DecodeArgs a,
     for (int i = 0; i < PER; ++i) pk[i] = (bf16)res[i];
     *(lds_bf16x8 *)(ol + tl * DC + (lane ^ (tl & 15)) * 8) = pk;
   }
+  wait_vmcnt<0>();   // this wave's W_UV copies
   __syncthreads();
 
+  // A operand: W_UV,i row (wave*VB + vb)*16 + lrow, k = 32*ks + 8*lgrp..
+  const lds_bf16 *wl = (const lds_bf16 *)wuv;
   f32x4 acc[VB];
 #pragma unroll
   for (int vb = 0; vb < VB; ++vb) acc[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1137,7 +1147,10 @@ __global__ __launch_bounds__(256, 1) void decode_combine_uv_kernel(DecodeArgs a,
   for (int ks = 0; ks < KS; ++ks) {
     const bf16x8 xb = *(const lds_bf16x8 *)(ol + lrow * DC + (((4 * ks + lgrp) ^ lrow) * 8));
 #pragma unroll
-    for (int vb = 0; vb < VB; ++vb) acc[vb] = Mma<bf16>::mma(wf[vb][ks], xb, acc[vb]);
+    for (int vb = 0; vb < VB; ++vb) {
+      const bf16x8 wf = *(const lds_bf16x8 *)(wl + ((wave * VB + vb) * 16 + lrow) * DC + (((4 * ks + lgrp) ^ lrow) * 8));
+      acc[vb] = Mma<bf16>::mma(wf, xb, acc[vb]);
+    }
   }
   // lane: features (wave*VB + vb)*16 + 4*lgrp + 0..3 of token lrow
   const int t = tg * TT + lrow;
