@@ -5,12 +5,13 @@
 // With 32 tokens every weight element feeds two MFMAs, so these products are
 // bound by streaming the weights from HBM.  The kernel is built for that:
 //   * the work is a flat list of units (matrix z, 64-row weight tile t,
-//     128-wide k step j) of 16 KB of weights each; a persistent grid of
-//     workgroups takes equal contiguous ranges of it (no tail wave);
+//     k step j, 256 wide up to 32 tokens, else 128) of 32 or 16 KB of
+//     weights; a persistent grid of workgroups takes equal contiguous ranges
+//     of it (no tail wave);
 //   * weights and the matching activation slice go HBM -> LDS with
-//     global_load_lds_dwordx4 into a ring of stages, whole rows per
-//     instruction (coalesced), several units ahead;
-//   * LDS rows are 16 chunks of 16 bytes with the chunk index XORed by the
+//     global_load_lds_dwordx4 into a ring of stages, each row's slice of a
+//     unit one contiguous run, several units ahead;
+//   * LDS rows are k/8 chunks of 16 bytes with the chunk index XORed by the
 //     row (no padding, no bank conflicts for the 16-row MFMA reads);
 //   * a tile finished inside one workgroup goes straight through the
 //     epilogue; a tile shared by several leaves fp32 partials that the reduce
@@ -28,12 +29,18 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) bf16 lds_bf16;
 
 constexpr int SBN = 64;          // weight rows (output features) per tile
-constexpr int SBK = 128;         // k per unit
 constexpr int SNT = 256;         // threads per workgroup
 constexpr int MAX_PARTS = 16;    // workgroups that may share one tile
 
-// ring stages: as many units in flight as LDS holds (24 KB per unit at 32 rows)
-template <int MB> constexpr int stream_stages() { return MB <= 2 ? 6 : 4; }
+// k per unit.  Each weight row contributes one contiguous run of 2*BK bytes
+// per unit: HBM serves 512-byte runs markedly faster than 256-byte ones
+// (W_O at 32 tokens: 48.5 -> 44.6 us), so up to 32 tokens take 256-wide
+// units; 64 tokens keep 128 (their activation slice would not fit beside).
+template <int MB> constexpr int stream_bk() { return MB <= 2 ? 256 : 128; }
+inline int stream_bk_for(int M) { return M <= 32 ? 256 : 128; }
+// ring stages: as many units in flight as LDS holds (48 KB per unit at 32
+// tokens, 32 KB at 64)
+template <int MB> constexpr int stream_stages() { return MB <= 2 ? 3 : 4; }
 
 template <int N>
 __device__ inline void wait_vm() {
@@ -70,8 +77,10 @@ __device__ __host__ inline int unit_owner(int u, int U, int G) { return ((u + 1)
 // MB: 16-row blocks of activations (M <= 16*MB).  WKN: W stored [K][N].
 template <int MB, bool WKN>
 __global__ __launch_bounds__(SNT, 1) void gemm_stream_kernel(GemmArgs a) {
+  constexpr int SBK = stream_bk<MB>();
+  constexpr int CPR = SBK / 8;                      // 16-byte chunks per row of a unit
   constexpr int SNS = stream_stages<MB>();
-  constexpr int WCH = SBN * SBK / 8;                // weight chunks per unit (1024)
+  constexpr int WCH = SBN * SBK / 8;                // weight chunks per unit
   constexpr int XCH = 16 * MB * SBK / 8;            // activation chunks per unit
   constexpr int WLD = WCH / SNT, XLD = XCH / SNT;   // copy instructions per unit
   constexpr int LOADS = WLD + XLD;
@@ -104,7 +113,7 @@ __global__ __launch_bounds__(SNT, 1) void gemm_stream_kernel(GemmArgs a) {
       const int rows = min(SBN, a.w_end[seg] - n0);
 #pragma unroll
       for (int i = 0; i < WLD; ++i) {
-        const int s = i * SNT + tid, r = s >> 4, pc = s & 15;
+        const int s = i * SNT + tid, r = s / CPR, pc = s % CPR;
         const unsigned off = (unsigned)(min(r, rows - 1) * a.ldw + ((pc ^ (r & 15)) << 3)) * 2u;
         dma16(wb, off, lst + i * SNT * 16);
       }
@@ -121,7 +130,7 @@ __global__ __launch_bounds__(SNT, 1) void gemm_stream_kernel(GemmArgs a) {
     const char *xb = (const char *)((const bf16 *)a.x + (long)z * a.x_bs + k0);
 #pragma unroll
     for (int i = 0; i < XLD; ++i) {
-      const int s = i * SNT + tid, r = s >> 4, pc = s & 15;
+      const int s = i * SNT + tid, r = s / CPR, pc = s % CPR;
       const unsigned off = (unsigned)(min(r, a.M - 1) * a.ldx + ((pc ^ (r & 15)) << 3)) * 2u;
       dma16(xb, off, lst + (WLD + i) * SNT * 16);
     }
@@ -172,7 +181,7 @@ __global__ __launch_bounds__(SNT, 1) void gemm_stream_kernel(GemmArgs a) {
       bf16x8 wf;
       if constexpr (!WKN) {
         const int r = wave * 16 + lrow;
-        wf = *(const lds_bf16x8 *)(ws + (r * 16 + (c ^ (r & 15))) * 8);
+        wf = *(const lds_bf16x8 *)(ws + (r * CPR + (c ^ (r & 15))) * 8);
       } else {
         // W^T fragment: k = 32s + 8*lgrp + 0..7 for feature wave*16 + lrow,
         // two transposed 4x16 reads of the [k][n] tile
@@ -189,7 +198,7 @@ __global__ __launch_bounds__(SNT, 1) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int r = mb * 16 + lrow;
-        const bf16x8 xf = *(const lds_bf16x8 *)(xs + (r * 16 + (c ^ (r & 15))) * 8);
+        const bf16x8 xf = *(const lds_bf16x8 *)(xs + (r * CPR + (c ^ (r & 15))) * 8);
         acc[mb] = Mma<bf16>::mma(wf, xf, acc[mb]);
       }
     }
@@ -203,7 +212,7 @@ __global__ __launch_bounds__(SNT, 1) void gemm_stream_kernel(GemmArgs a) {
 // are issued before the sum.
 template <int MB>
 __global__ __launch_bounds__(256) void gemm_stream_reduce_kernel(GemmArgs a, int G) {
-  const int KS = a.K / SBK;
+  const int KS = a.K / stream_bk<MB>();
   const int U = a.batch * a.tiles_n * KS;
   const int idx = blockIdx.x * 256 + threadIdx.x;
   const int per_tile = a.M * (SBN / 4);
@@ -246,11 +255,12 @@ bool gemm_stream_ok(const GemmArgs &a, int wkn) {
   // which shorter weight streams (q_up, W_UK, W_UV) do not amortise; those
   // keep the register-streaming kernels.
   if (wkn || a.K < 4096) return false;
-  if (a.M > 64 || a.K % SBK != 0 || !a.partial) return false;
-  const long units = (long)a.batch * ((a.N + SBN - 1) / SBN) * (a.K / SBK);
+  const int bk = stream_bk_for(a.M);
+  if (a.M > 64 || a.K % bk != 0 || !a.partial) return false;
+  const long units = (long)a.batch * ((a.N + SBN - 1) / SBN) * (a.K / bk);
   if (units * gemm_stream_grid() >= (1L << 31)) return false;
   // a tile is shared by at most MAX_PARTS workgroups
-  const long per = std::max<long>(1, units / gemm_stream_grid()), ks = a.K / SBK;
+  const long per = std::max<long>(1, units / gemm_stream_grid()), ks = a.K / bk;
   if (ks / per + 2 > MAX_PARTS) return false;
   if (wkn) return a.N % SBN == 0 && a.nw == 1;
   for (int s = 0; s < a.nw - 1; ++s)
@@ -272,7 +282,7 @@ template <int MB, bool WKN>
 static hipError_t launch_stream_t(GemmArgs &a, hipStream_t st) {
   a.tiles_m = 1;
   a.tiles_n = (a.N + SBN - 1) / SBN;
-  const int KS = a.K / SBK;
+  const int KS = a.K / stream_bk<MB>();
   const int tiles = a.batch * a.tiles_n;
   const int U = tiles * KS;
   const int G = stream_grid_for(U, KS, tiles);
