@@ -35,6 +35,7 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) bf16 lds_bf16;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 template <int N>
 __device__ inline void wait_vm() {
@@ -59,25 +60,34 @@ __device__ inline void bar() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+__device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4)); }
 
 constexpr int DQ = 1536, DN = 128, DRP = 64, DCL = 512;
-constexpr int TQ = 32;                 // tokens (two 16-row MFMA blocks)
-constexpr int BK = 256, NST = DQ / BK; // k stages of the up-projection
-constexpr int AH = 2;                  // stages in flight beyond the current one
-constexpr int STEPS = BK / 32;
-constexpr int XCH = DQ / 8;            // 16-byte chunks per c_Q row (192)
-constexpr int KCH = 256 / 8;           // chunks per row of the W_UK half (32)
-constexpr int XLOADS = TQ * XCH / 256; // copy instructions per copying wave
-constexpr int KLOADS = DN * KCH / 256;
+constexpr int TQ = 32;                   // tokens (two 16-row MFMA blocks)
+constexpr int ROWS = DN + 32;            // weight rows per workgroup: q_C (128) and half of q_R (32)
+constexpr int RB = ROWS / 16;            // 16-row blocks (10)
+constexpr int SKW = 512;                 // k per stage: a 1 KB run of every weight row
+constexpr int KC = DQ / SKW;             // k chunks (3)
+constexpr int NSTG = RB * KC;            // stages (30)
+constexpr int SCH = SKW / 8;             // 16-byte chunks per stage row (64)
+constexpr int SLOADS = 16 * SCH / 256;   // copy instructions per wave per stage (4)
+constexpr int RING = 4;                  // ring stages (three ahead)
+constexpr int XCH = DQ / 8;              // chunks per c_Q row (192)
+constexpr int XLOADS = TQ * XCH / 256;   // copy instructions per wave for c_Q (24)
+constexpr int KCH = 256 / 8;             // chunks per row of the W_UK half (32)
 
 }  // namespace
 
-__global__ __launch_bounds__(320, 1) void decode_q_kernel(DecodeQArgs a) {
-  static_assert(TQ * XCH % 256 == 0 && DN * KCH % 256 == 0 && XLOADS + 2 * 2 * STEPS < 64, "");
-  // c_Q [32][1536] (chunk c of row t at c ^ (t & 15)), later q_C [32][128]
+__global__ __launch_bounds__(256, 1) void decode_q_kernel(DecodeQArgs a) {
+  static_assert(16 * SCH % 256 == 0 && TQ * XCH % 256 == 0 && 32 * KCH / 256 == SLOADS, "");
+  static_assert(XLOADS + 3 * SLOADS < 64 && RING * 16 * SKW == DN * 256, "");
+  static_assert(4 * RB * 2 * 64 * 16 + TQ * DN * 2 <= TQ * DQ * 2, "");
+  // region A: c_Q [32][1536] (chunk c of token t at c ^ (t & 15)); after the
+  // up-projection, the waves' partial sums and then q_C [32][128] (bf16)
   __shared__ __attribute__((aligned(16))) bf16 xs[TQ * DQ];
-  // W_UK,i[f][256hf + 8c..] at chunk c ^ (f & 15) of row f
-  __shared__ __attribute__((aligned(16))) bf16 wk[DN * 256];
+  // region B: the ring of weight stages ([16][512], chunk c of row r at
+  // c ^ r); afterwards W_UK,i[f][256hf + 8c..] at chunk c ^ (f & 15) of row f
+  __shared__ __attribute__((aligned(16))) bf16 ring[RING * 16 * SKW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 15, lgrp = lane >> 4;
@@ -85,107 +95,108 @@ __global__ __launch_bounds__(320, 1) void decode_q_kernel(DecodeQArgs a) {
   const int h = (slot >> 1) * 8 + xcd, hf = slot & 1;
   if (h >= a.n_h) return;
   const int T = a.T;
-  const unsigned lxs = (unsigned)(size_t)(lds_void *)xs, lwk = (unsigned)(size_t)(lds_void *)wk;
+  const unsigned lxs = (unsigned)(size_t)(lds_void *)xs, lring = (unsigned)(size_t)(lds_void *)ring;
 
-  // c_Q -> LDS (waves 0..3); rows past the last token repeat it
-  if (wave < 4) {
+  // c_Q -> region A; rows past the last token repeat it
 #pragma unroll
-    for (int j = 0; j < XLOADS; ++j) {
-      const int s = j * 256 + tid, r = s / XCH, p = s - r * XCH;
-      const int c = p ^ (r & 15);
-      dma16(a.cq, (unsigned)((min(r, T - 1) * DQ + c * 8) * 2), lxs + (unsigned)(j * 256 + wave * 64) * 16);
-    }
+  for (int j = 0; j < XLOADS; ++j) {
+    const int sl = j * 256 + tid, r = sl / XCH, p = sl - r * XCH;
+    const int c = p ^ (r & 15);
+    dma16(a.cq, (unsigned)((min(r, T - 1) * DQ + c * 8) * 2), lxs + (unsigned)sl * 16);
   }
-
-  // weight rows of this lane: two 16-row blocks
-  const bf16 *wrow[2];
+  // stage s = (row block s / KC, k chunk s % KC) -> ring slot s % RING: each
+  // wave instruction copies one whole 1 KB run of one row
+  auto issue_stage = [&](int st) {
+    const int rb = st / KC, j = st % KC;
+    const bf16 *base = rb < DN / 16 ? a.w_uq + ((long)h * DN + rb * 16) * DQ
+                                    : a.w_qr + ((long)h * DRP + hf * 32 + (rb - DN / 16) * 16) * DQ;
+    base += j * SKW;
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
-    wrow[blk] = wave < 4 ? a.w_uq + ((long)h * DN + wave * 32 + blk * 16 + lrow) * DQ + lgrp * 8
-                         : a.w_qr + ((long)h * DRP + hf * 32 + blk * 16 + lrow) * DQ + lgrp * 8;
-  bf16x8 wr[AH + 1][2][STEPS];
-  auto wload = [&](int st) {
+    for (int i = 0; i < SLOADS; ++i) {
+      const int sl = i * 256 + tid, r = sl / SCH, p = sl - r * SCH;
+      dma16(base, (unsigned)((r * DQ + ((p ^ r) << 3)) * 2),
+            lring + (unsigned)((st % RING) * 16 * SKW * 2 + sl * 16));
+    }
+  };
+  // quarter q of the W_UK half (rows 32q..32q+31) -> ring slot q
+  auto issue_wuk = [&](int q) {
+    const bf16 *base = a.w_uk + ((long)h * DN + 32 * q) * DCL + hf * 256;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int s = 0; s < STEPS; ++s) wr[st % (AH + 1)][blk][s] = *(const bf16x8 *)(wrow[blk] + st * BK + s * 32);
+    for (int i = 0; i < SLOADS; ++i) {
+      const int sl = i * 256 + tid, fl = sl / KCH, p = sl - fl * KCH;
+      const int f = 32 * q + fl;
+      dma16(base, (unsigned)((fl * DCL + ((p ^ (f & 15)) << 3)) * 2), lring + (unsigned)((q * 1024 + sl) * 16));
+    }
   };
 #pragma unroll
-  for (int st = 0; st < AH; ++st) wload(st);
+  for (int st = 0; st < RING - 1; ++st) issue_stage(st);
 
-  f32x4 acc[2][2];
+  // the wave's partial sums over its k quarter of every stage
+  f32x4 acc[RB][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  wait_vm<2 * 2 * STEPS>();   // c_Q copies landed (the weight stages may not have)
-  bar();
-
   const lds_bf16 *xl = (const lds_bf16 *)xs;
+  const lds_bf16 *rl = (const lds_bf16 *)ring;
 #pragma unroll
-  for (int st = 0; st < NST; ++st) {
-    // the scheduler must not sink the next stage's loads below this stage's
-    // MFMAs (it does, to save registers, and the pipe then drains)
-    if (st + AH < NST) wload(st + AH);
-    __builtin_amdgcn_sched_barrier(0);
-    if (st == 3 && wave < 4) {
-      // W_UK,i half -> LDS, now that every weight load has been issued
-      const char *src = (const char *)(a.w_uk + (long)h * DN * DCL + hf * 256);
+  for (int st = 0; st < NSTG; ++st) {
+    // stage st landed (and, at st = 0, c_Q); the two after it may not have
+    wait_vm<2 * SLOADS>();
+    bar();   // every wave is done with the slot of stage st-1
+    // next copy into that slot: stage st+3, or a quarter of W_UK once the
+    // weight stages are all issued (quarters 2, 3, 0 here, 1 after the loop)
+    if (st + RING - 1 < NSTG) issue_stage(st + RING - 1);
+    else issue_wuk((st + RING - 1) % RING);
+    const int rb = st / KC, j = st % KC;
+    const lds_bf16 *ws = rl + (st % RING) * 16 * SKW;
 #pragma unroll
-      for (int j = 0; j < KLOADS; ++j) {
-        const int s = j * 256 + tid, f = s / KCH, p = s - f * KCH;
-        const int c = p ^ (f & 15);
-        dma16(src, (unsigned)((f * DCL + c * 8) * 2), lwk + (unsigned)(j * 256 + wave * 64) * 16);
+    for (int i = 0; i < 4; ++i) {
+      const int cw = 16 * wave + 4 * i + lgrp;           // chunk in the stage row
+      const int cx = j * SCH + cw;                       // chunk in the c_Q row
+      const bf16x8 wf = *(const lds_bf16x8 *)(ws + lrow * SKW + ((cw ^ lrow) << 3));
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const bf16x8 xb = *(const lds_bf16x8 *)(xl + (tb * 16 + lrow) * DQ + ((cx ^ lrow) << 3));
+        acc[rb][tb] = Mma<bf16>::mma(wf, xb, acc[rb][tb]);
       }
     }
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-      const int c = st * (BK / 8) + 4 * s + lgrp;
-      bf16x8 xb[2];
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) xb[tb] = *(const lds_bf16x8 *)(xl + (tb * 16 + lrow) * DQ + (c ^ lrow) * 8);
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) acc[blk][tb] = Mma<bf16>::mma(wr[st % (AH + 1)][blk][s], xb[tb], acc[blk][tb]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
   }
+  bar();             // stage 29 (slot 1) and c_Q no longer read
+  issue_wuk(1);
 
-  __syncthreads();   // c_Q no longer read
-  lds_bf16 *ql = (lds_bf16 *)xs;
-  if (wave < 4) {
-    // q_C features wave*32 + blk*16 + 4*lgrp + i of token tb*16 + lrow, as bf16
+  // sum the four waves' partials through region A
+  lds_f32x4 *pt = (lds_f32x4 *)xs;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const int t = tb * 16 + lrow;
-        const int c = wave * 4 + blk * 2 + (lgrp >> 1);
-        *(lds_bf16x4 *)(ql + t * DN + (c ^ lrow) * 8 + (lgrp & 1) * 4) =
-            bf16x4{(bf16)acc[blk][tb][0], (bf16)acc[blk][tb][1], (bf16)acc[blk][tb][2], (bf16)acc[blk][tb][3]};
-      }
-  } else {
-    // RoPE features: columns of the up-projection's output space
-    const int n0 = a.n_h * DN + h * DRP + hf * 32 + 4 * lgrp;
+    for (int tb = 0; tb < 2; ++tb) pt[((wave * RB + rb) * 2 + tb) * 64 + lane] = acc[rb][tb];
+  wait_lgkm0();
+  bar();
+  lds_bf16 *ql = (lds_bf16 *)xs + 4 * RB * 2 * 64 * 8;   // q_C [32][128] after the partials
+  for (int q = 0; q < RB * 2 / 4; ++q) {
+    const int pr = wave * (RB * 2 / 4) + q, rb = pr >> 1, tb = pr & 1;
+    f32x4 v = pt[(rb * 2 + tb) * 64 + lane];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const int t = tb * 16 + lrow;
-        if (t < T) {
-          float v[4] = {acc[blk][tb][0], acc[blk][tb][1], acc[blk][tb][2], acc[blk][tb][3]};
-          epi_store4<bf16>(a.epi, 0, t, n0 + blk * 16, v);
-        }
-      }
+    for (int w = 1; w < 4; ++w) v += pt[((w * RB + rb) * 2 + tb) * 64 + lane];
+    // rows 16rb + 4lgrp + 0..3 of token 16tb + lrow
+    const int t = tb * 16 + lrow;
+    if (rb < DN / 16) {
+      const int c = 2 * rb + (lgrp >> 1);
+      *(lds_bf16x4 *)(ql + t * DN + ((c ^ lrow) << 3) + (lgrp & 1) * 4) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+    } else if (t < T) {
+      // RoPE features: columns of the up-projection's output space
+      float vv[4] = {v[0], v[1], v[2], v[3]};
+      epi_store4<bf16>(a.epi, 0, t, a.n_h * DN + h * DRP + hf * 32 + (rb - DN / 16) * 16 + 4 * lgrp, vv);
+    }
   }
   wait_vm<0>();      // this wave's W_UK copies
-  __syncthreads();
-  if (wave >= 4) return;
+  wait_lgkm0();
+  bar();
 
   // q_lat[t][256hf + d] for the wave's 64 latent columns: 4 blocks of 16
-  const lds_bf16 *kl = (const lds_bf16 *)wk;
+  const lds_bf16 *kl = (const lds_bf16 *)ring;
   f32x4 lat[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -231,7 +242,7 @@ bool decode_q_supported(int d_cq, int d_nope, int d_rope, int d_c, int T) {
 hipError_t launch_decode_q(const DecodeQArgs &a, hipStream_t st) {
   const int grid = ((a.n_h + 7) / 8) * 16;
   timing_before("q_up_absorb", st);
-  hipLaunchKernelGGL(decode_q_kernel, dim3(grid), dim3(320), 0, st, a);
+  hipLaunchKernelGGL(decode_q_kernel, dim3(grid), dim3(256), 0, st, a);
   timing_after("q_up_absorb", st);
   return hipGetLastError();
 }
