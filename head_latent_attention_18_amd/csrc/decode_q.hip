@@ -11,17 +11,18 @@
 // Split in two launches, q_C would go to HBM and back and the absorption
 // would pay its own ramp; here workgroup (head i, half hf) keeps everything
 // on chip:
-//   1. c_Q (32 x 1536, 96 KB) is copied HBM -> LDS once; W_UQ,i and half of
-//      W_QR,i stream from HBM straight into MFMA A-operand registers (six
-//      256-wide k stages, three in flight).  Waves 0..3 compute 32 features
-//      of q_C,i each; wave 4 the 32 RoPE features 32hf.. (RoPE and the store
-//      go through the shared GEMM epilogue, so the values are those of the
-//      separate up-projection).  Both halves compute all of q_C,i: the
-//      absorption contracts over it; the second read of W_UQ,i hits L2 (the
-//      two halves of a head share an XCD).
-//   2. q_C,i, rounded to bf16 as a stored q_C would be, replaces c_Q in LDS;
-//      W_UK,i[:, 256hf..+256] (64 KB, copied to LDS during step 1) is read
-//      transposed (ds_read_b64_tr_b16) as the A operand of
+//   1. c_Q (32 x 1536, 96 KB) is copied HBM -> LDS once.  The 160 weight
+//      rows the workgroup needs (W_UQ,i and half of W_QR,i) go HBM -> LDS as
+//      stages of 16 rows x 512 k, one 1 KB run per row per copy instruction,
+//      through a four-slot ring; the four waves split the k steps of every
+//      stage and add their partial sums through LDS at the end.  Both halves
+//      compute all of q_C,i (the absorption contracts over it); the second
+//      read of W_UQ,i hits L2 (the two halves of a head share an XCD).  The
+//      RoPE features 32hf.. are rotated with the same fp64-reduced angles as
+//      the GEMM epilogue (positions and frequencies fetched at the start).
+//   2. q_C,i, rounded to bf16 as a stored q_C would be, replaces the partial
+//      sums in LDS; W_UK,i[:, 256hf..+256] (64 KB, copied into the freed ring
+//      slots) is read transposed (ds_read_b64_tr_b16) as the A operand of
 //      q_lat^T[d][t] = W_UK^T[d][f] q_C^T[f][t].
 #include "mla_internal.h"
 
@@ -131,6 +132,22 @@ __global__ __launch_bounds__(256, 1) void decode_q_kernel(DecodeQArgs a) {
 #pragma unroll
   for (int st = 0; st < RING - 1; ++st) issue_stage(st);
 
+  // RoPE inputs of the lane's rows, fetched now so that the epilogue waits
+  // for no load chain: positions of tokens lrow and 16 + lrow (decode rows:
+  // the last n_q positions of each sequence) and the frequencies of its
+  // pairs in RoPE blocks 0 and 1 (features 32hf + 16blk + 4lgrp..)
+  int rpos[2];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int t = min(tb * 16 + lrow, T - 1), nq = a.epi.rows.per_seq, sq = t / nq;
+    rpos[tb] = a.epi.rows.lens[sq] - nq + (t - sq * nq);
+  }
+  double rfreq[2][2];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) rfreq[blk][pp] = a.epi.inv_freq[hf * 16 + blk * 8 + 2 * lgrp + pp];
+
   // the wave's partial sums over its k quarter of every stage
   f32x4 acc[RB][2];
 #pragma unroll
@@ -186,9 +203,20 @@ __global__ __launch_bounds__(256, 1) void decode_q_kernel(DecodeQArgs a) {
       const int c = 2 * rb + (lgrp >> 1);
       *(lds_bf16x4 *)(ql + t * DN + ((c ^ lrow) << 3) + (lgrp & 1) * 4) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
     } else if (t < T) {
-      // RoPE features: columns of the up-projection's output space
+      // RoPE features 32hf + 16(rb - 8) + 4lgrp.. : pairs (2k, 2k+1) rotated
+      // by pos * inv_freq[k], stored after q_lat in the q_abs row
+      const int blk = rb - DN / 16;
       float vv[4] = {v[0], v[1], v[2], v[3]};
-      epi_store4<bf16>(a.epi, 0, t, a.n_h * DN + h * DRP + hf * 32 + (rb - DN / 16) * 16 + 4 * lgrp, vv);
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        float sn, cs;
+        rope_sincos(rpos[tb], blk ? rfreq[1][pp] : rfreq[0][pp], sn, cs);
+        const float x0 = vv[2 * pp], x1 = vv[2 * pp + 1];
+        vv[2 * pp] = x0 * cs - x1 * sn;
+        vv[2 * pp + 1] = x0 * sn + x1 * cs;
+      }
+      *(bf16x4 *)(a.q_abs + ((long)t * a.n_h + h) * (DCL + DRP) + DCL + hf * 32 + blk * 16 + 4 * lgrp) =
+          bf16x4{(bf16)vv[0], (bf16)vv[1], (bf16)vv[2], (bf16)vv[3]};
     }
   }
   wait_vm<0>();      // this wave's W_UK copies
