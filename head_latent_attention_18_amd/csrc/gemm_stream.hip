@@ -214,17 +214,19 @@ template <int MB>
 __global__ __launch_bounds__(256) void gemm_stream_reduce_kernel(GemmArgs a, int G) {
   const int KS = a.K / stream_bk<MB>();
   const int U = a.batch * a.tiles_n * KS;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
+  // workgroups of one tile: its segment and owners are uniform
   const int per_tile = a.M * (SBN / 4);
-  const int tt = idx / per_tile;
-  if (tt >= a.batch * a.tiles_n) return;
-  const int rem = idx - tt * per_tile;
+  const int wpt = (per_tile + 255) / 256;
+  const int tt = blockIdx.x / wpt;
+  const int rem = (blockIdx.x - tt * wpt) * 256 + threadIdx.x;
+  if (tt >= a.batch * a.tiles_n || rem >= per_tile) return;
   const int m = rem / (SBN / 4), c4 = (rem % (SBN / 4)) * 4;
   const int bf = unit_owner(tt * KS, U, G), bl = unit_owner((tt + 1) * KS - 1, U, G);
   if (bf == bl) return;   // stored by its only workgroup
   const int z = tt / a.tiles_n, t = tt - z * a.tiles_n;
   const int n = t * SBN + c4;
   if (n >= a.N) return;
+  const ColPlan cp = col_plan_tile(a.epi, t * SBN, n);
   // the first contributor holds the tile as its last one (slot 1) unless the
   // tile is also its first; every later contributor starts with it (slot 0)
   const int slot0 = unit_start(bf, U, G) / KS == tt ? 0 : 1;
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(256) void gemm_stream_reduce_kernel(GemmArgs a, int
   for (int i = 1; i < MAX_PARTS; ++i)
     if (bf + i <= bl) s += v[i];
   float o[4] = {s[0], s[1], s[2], s[3]};
-  epi_store4<bf16>(a.epi, z, m, n, o);
+  col_store<bf16>(cp, a.epi, z, m, o);
 }
 
 int gemm_stream_grid() { return 256; }
@@ -294,10 +296,10 @@ static hipError_t launch_stream_t(GemmArgs &a, hipStream_t st) {
   bool split = false;   // does a workgroup boundary fall inside a tile?
   for (int b = 1; b < G && !split; ++b) split = unit_start(b, U, G) % KS != 0;
   if (!split) return hipSuccess;
-  const long total = (long)tiles * a.M * (SBN / 4);
+  const long wgs = (long)tiles * ((a.M * (SBN / 4) + 255) / 256);
   const char *rn = a.reduce_name ? a.reduce_name : "gemm_stream.reduce";
   timing_before(rn, st);
-  hipLaunchKernelGGL((gemm_stream_reduce_kernel<MB>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a, G);
+  hipLaunchKernelGGL((gemm_stream_reduce_kernel<MB>), dim3((unsigned)wgs), dim3(256), 0, st, a, G);
   timing_after(rn, st);
   return hipGetLastError();
 }

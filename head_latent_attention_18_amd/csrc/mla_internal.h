@@ -218,9 +218,11 @@ __device__ inline int epi_segment(const Epi &e, int n, int &nb) {
   return s;
 }
 
-__device__ inline ColPlan col_plan(const Epi &e, int n) {
-  int nb;
-  const Seg &g = e.seg[epi_segment(e, n, nb)];
+// Plan for columns n..n+3 inside segment sg (starting at column nb).  With a
+// wave-uniform segment the kernel-argument reads are scalar loads; a per-lane
+// segment search reads them with dependent vector loads.
+__device__ inline ColPlan col_plan_in(const Epi &e, int sg, int nb, int n) {
+  const Seg &g = e.seg[sg];
   ColPlan p;
   p.c = n - nb;
   p.kind = g.kind;
@@ -245,6 +247,21 @@ __device__ inline ColPlan col_plan(const Epi &e, int n) {
     p.inv1 = e.inv_freq[k0 + 1];
   }
   return p;
+}
+
+__device__ inline ColPlan col_plan(const Epi &e, int n) {
+  int nb;
+  const int sg = epi_segment(e, n, nb);
+  return col_plan_in(e, sg, nb, n);
+}
+
+// Plan for a lane whose columns lie in the same segment as column n0, a
+// value the whole wave shares (the first column of a tile that never
+// straddles two segments).
+__device__ inline ColPlan col_plan_tile(const Epi &e, int n0, int n) {
+  int nb;
+  const int sg = epi_segment(e, __builtin_amdgcn_readfirstlane(n0), nb);
+  return col_plan_in(e, __builtin_amdgcn_readfirstlane(sg), __builtin_amdgcn_readfirstlane(nb), n);
 }
 
 template <typename T>
