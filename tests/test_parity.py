@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from mla_inputs import DSV3, make_workload
+from mla_inputs import Dims, DSV3, make_workload
 from oracle import mla_oracle as O
 
 from tests.gpu_harness import (CacheBuf, Timer, assert_close, decode_cache, layer_for, oracle_decode_seq,
@@ -152,6 +152,34 @@ def test_dsv3_decode_small(B, L, nq):
         assert_close(o.view(B, nq, d.n_heads, d.d_v)[b], ref["o"], True, f"o b={b}")
         got_new = cache.read_rows(b, np.arange(L - nq, L))
         assert_close(got_new, ref["row_new"], True, f"new cache rows b={b}")
+
+
+# DeepSeek-V3 latent and head widths with 20 heads and a narrower model:
+# head counts off the multiples of 8 that the workgroup-to-XCD maps assume,
+# fewer query rows (20) than a 64-row decode workgroup, a W_O input width
+# (2560) below the streaming GEMM's range, and the flash kernel's mapping for
+# head counts not divisible by 8.
+ODD_HEADS = Dims(d_model=1024, n_heads=20, d_nope=128, d_rope=64, d_v=128, d_c=512, d_cq=1536)
+
+
+@pytest.mark.parametrize("B,L,nq", [(5, 150, 1), (3, 90, 2)])
+def test_dsv3_widths_odd_head_count_decode(B, L, nq):
+    wl = make_workload(2, dims=ODD_HEADS, batch=B, uniform_len=L, n_q=nq)
+    layer = layer_for(wl)
+    cache = decode_cache(wl, layer)
+    say(f"decode 20 heads B={B} L={L} n_q={nq}")
+    u, o = run_decode(wl, layer, cache)
+    d = wl.dims
+    for b in range(B):
+        ref = oracle_decode_seq(wl, b)
+        assert_close(u[b], ref["u"], True, f"u b={b}")
+        assert_close(o.view(B, nq, d.n_heads, d.d_v)[b], ref["o"], True, f"o b={b}")
+
+
+def test_dsv3_widths_odd_head_count_prefill():
+    wl = make_workload(3, dims=ODD_HEADS, batch=2, seq_len=100)
+    layer = layer_for(wl)
+    _prefill_check(wl, layer)
 
 
 @pytest.mark.parametrize("block_size", [64, 32, 16, 96])
