@@ -634,7 +634,9 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
 //     probabilities into its half's part of the P entry, so P has the layout
 //     of the kernel above.
 //   B (P.V): wave w owns latent columns 64w..64w+63 for all 64 rows.
-// Waves 0..3 issue the cache copies (the pattern of the kernel above).
+// Waves 0..3 issue the cache copies (the pattern of the kernel above) and,
+// first, the copies of the 64 query rows, which reach registers through
+// stages 2 and 3 (whole rows per copy instead of sixteen-row register loads).
 template <int DC, int DR, bool PAGED>
 __global__ __launch_bounds__(512, 1) void decode_attn_dma8_kernel(DecodeArgs a) {
   constexpr int NW = 8, NC = 256;                    // waves; threads issuing copies
