@@ -48,6 +48,8 @@ def decode_kernel_bytes(d, B, n_q, sum_len, e=2):
         "decode_combine": e * T * nh * d.d_c,
         "unabsorb": e * (nh * d.d_v * d.d_c + T * nh * d.d_c + T * nh * d.d_v),
         "decode_combine_uv": e * (nh * d.d_v * d.d_c + T * nh * d.d_c + T * nh * d.d_v),
+        "q_up_absorb": e * (nh * (d.d_nope + d.d_rope) * d.d_cq + nh * d.d_nope * d.d_c + T * d.d_cq
+                            + T * nh * (d.d_c + d.d_rope)),
         "o_proj": e * (d.d_model * nh * d.d_v + T * nh * d.d_v + T * d.d_model),
     }
 
@@ -76,7 +78,9 @@ def measured_traffic(kernel_label):
     changed since the counters were taken."""
     import hashlib
     files = {"decode_attn": ("profiles/decode_attn_b32_len4096_traffic.txt",
-                             "head_latent_attention_18_amd/csrc/attn_decode.hip")}
+                             "head_latent_attention_18_amd/csrc/attn_decode.hip"),
+             "o_proj": ("profiles/o_proj_b32_traffic.txt",
+                        "head_latent_attention_18_amd/csrc/gemm_stream.hip")}
     if kernel_label not in files:
         return None
     summ, src = (os.path.join(ROOT, f) for f in files[kernel_label])
