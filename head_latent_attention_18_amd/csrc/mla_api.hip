@@ -36,6 +36,10 @@ const int kCUs = 256;  // MI355X compute units; the split plan targets one wave 
 
 size_t esize(const mla_config *c) { return c->dtype == MLA_BF16 ? 2 : 4; }
 
+// YaRN is on for any factor other than 0 and 1 (a zero-initialised config
+// keeps plain RoPE)
+bool yarn_on(const mla_config *c) { return c->yarn_factor != 0.0 && c->yarn_factor != 1.0; }
+
 mla_status check_config(const mla_config *c) {
   if (!c) return MLA_ERR_NULL;
   if (c->dtype != MLA_FP32 && c->dtype != MLA_BF16) return MLA_ERR_DTYPE;
@@ -44,6 +48,11 @@ mla_status check_config(const mla_config *c) {
     return MLA_ERR_SHAPE;
   if (c->d_rope % 2 != 0) return MLA_ERR_SHAPE;
   if (!(c->rope_base > 0.0) || !isfinite(c->rope_base)) return MLA_ERR_SHAPE;
+  if (yarn_on(c)) {
+    if (!(c->yarn_factor > 1.0) || !isfinite(c->yarn_factor) || c->yarn_orig_len <= 0) return MLA_ERR_SHAPE;
+    if (!(c->yarn_beta_slow > 0.0) || !(c->yarn_beta_fast > c->yarn_beta_slow) || !isfinite(c->yarn_beta_fast))
+      return MLA_ERR_SHAPE;
+  }
   if (c->d_rope / 2 > MLA_MAX_ROPE_PAIRS) return MLA_ERR_UNSUPPORTED;
   if ((long)c->n_heads * (c->d_nope + c->d_rope) > (1L << 24) || c->d_model > (1 << 20))
     return MLA_ERR_UNSUPPORTED;
@@ -194,9 +203,32 @@ DecodePlan plan_decode(const mla_config *c, int32_t B, int32_t n_q, int32_t max_
   return p;
 }
 
+// RoPE frequency of pair k (fp64, host).  With YaRN the pair's rotation
+// count over the original context, r = L * theta / (2 pi), blends the
+// interpolated frequency theta / s (r <= beta_slow) into the original one
+// (r >= beta_fast), linearly in r.
 void fill_inv_freq(const mla_config *c, Epi &e) {
-  for (int k = 0; k < MLA_MAX_ROPE_PAIRS; ++k)
-    e.inv_freq[k] = (2 * k < c->d_rope) ? pow(c->rope_base, -2.0 * k / c->d_rope) : 0.0;
+  const double two_pi = 6.283185307179586476925287;
+  for (int k = 0; k < MLA_MAX_ROPE_PAIRS; ++k) {
+    if (2 * k >= c->d_rope) { e.inv_freq[k] = 0.0; continue; }
+    const double theta = pow(c->rope_base, -2.0 * k / c->d_rope);
+    if (!yarn_on(c)) { e.inv_freq[k] = theta; continue; }
+    const double r = (double)c->yarn_orig_len * theta / two_pi;
+    double g = (r - c->yarn_beta_slow) / (c->yarn_beta_fast - c->yarn_beta_slow);
+    g = g < 0.0 ? 0.0 : g > 1.0 ? 1.0 : g;
+    e.inv_freq[k] = (1.0 - g) * (theta / c->yarn_factor) + g * theta;
+  }
+}
+
+// Softmax scale in log2 units: log2(e) / sqrt(d_nope + d_rope), times the
+// YaRN temperature factor (0.1 ln s + 1)^2 when enabled.
+float softmax_scale_log2(const mla_config *c) {
+  double s = 1.4426950408889634 / sqrt((double)(c->d_nope + c->d_rope));
+  if (yarn_on(c)) {
+    const double m = 0.1 * log(c->yarn_factor) + 1.0;
+    s *= m * m;
+  }
+  return (float)s;
 }
 
 CacheRef cache_ref(const mla_config *c, const mla_cache *k, int32_t batch) {
@@ -496,7 +528,7 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
     f.d_nope = cfg->d_nope;
     f.d_rope = cfg->d_rope;
     f.d_v = cfg->d_v;
-    f.scale_log2 = (float)(1.4426950408889634 / sqrt((double)DQK));
+    f.scale_log2 = softmax_scale_log2(cfg);
     e = launch_flash_prefill(dt == MLA_BF16, f, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
   }
@@ -579,7 +611,7 @@ mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h
   d.n_h = NH;
   d.d_c = cfg->d_c;
   d.d_rope = cfg->d_rope;
-  d.scale_log2 = (float)(1.4426950408889634 / sqrt((double)(cfg->d_nope + cfg->d_rope)));
+  d.scale_log2 = softmax_scale_log2(cfg);
   d.chunk = p.chunk;
   d.n_splits = p.splits;
   d.row_groups = p.row_groups;

@@ -31,7 +31,8 @@ class MlaError(RuntimeError):
 class mla_config(ctypes.Structure):
     _fields_ = [("d_model", c_int32), ("n_heads", c_int32), ("d_nope", c_int32), ("d_rope", c_int32),
                 ("d_v", c_int32), ("d_c", c_int32), ("d_cq", c_int32), ("dtype", c_int32),
-                ("rope_base", c_double)]
+                ("rope_base", c_double), ("yarn_factor", c_double), ("yarn_beta_slow", c_double),
+                ("yarn_beta_fast", c_double), ("yarn_orig_len", c_int32)]
 
 
 class mla_weights(ctypes.Structure):
@@ -112,7 +113,9 @@ def _stream(stream) -> Optional[int]:
 
 def make_config(dims, dtype: str) -> mla_config:
     return mla_config(dims.d_model, dims.n_heads, dims.d_nope, dims.d_rope, dims.d_v, dims.d_c, dims.d_cq,
-                      MLA_BF16 if dtype == "bf16" else MLA_FP32, float(dims.rope_base))
+                      MLA_BF16 if dtype == "bf16" else MLA_FP32, float(dims.rope_base),
+                      float(getattr(dims, "yarn_factor", 1.0)), float(getattr(dims, "yarn_beta_slow", 1.0)),
+                      float(getattr(dims, "yarn_beta_fast", 32.0)), int(getattr(dims, "yarn_orig_len", 4096)))
 
 
 def make_weights(w: Dict[str, object]) -> mla_weights:

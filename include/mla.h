@@ -78,6 +78,21 @@ typedef struct mla_config {
   int32_t d_cq;      /* query latent width */
   int32_t dtype;     /* mla_dtype */
   double rope_base;  /* RoPE base (10000 for DeepSeek-V3) */
+  /* YaRN context extension (the V3 highlights page, highlight 13, extends
+   * the context from 4K to 128K with YaRN and the constants 40, 1, 32).
+   * yarn_factor 0 or 1 leaves plain RoPE (the other three fields are then
+   * ignored).  Otherwise pair k, of frequency theta_k = base^(-2k/d_rope),
+   * turns r_k = yarn_orig_len * theta_k / (2 pi) times over the original
+   * context and rotates at (1 - g) theta_k / yarn_factor + g theta_k with
+   * g = clamp((r_k - beta_slow) / (beta_fast - beta_slow), 0, 1), and the
+   * softmax scale is multiplied by (0.1 ln yarn_factor + 1)^2.
+   * DeepSeek-V3 at 128K: 40, 4096, 1, 32.  MLA_ERR_SHAPE unless
+   * yarn_factor > 1, yarn_orig_len > 0 and 0 < beta_slow < beta_fast (all
+   * finite) when enabled. */
+  double yarn_factor;
+  double yarn_beta_slow;
+  double yarn_beta_fast;
+  int32_t yarn_orig_len;
 } mla_config;
 
 /* The eight projections, each row-major [out][in] in the config dtype:

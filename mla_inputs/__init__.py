@@ -47,6 +47,14 @@ class Dims:
     d_c: int      # KV latent width
     d_cq: int     # query latent width
     rope_base: float = 10000.0
+    # YaRN context extension (factor 1: plain RoPE).  The V3 highlights page
+    # (highlight 13) names YaRN with the constants 40, 1 and 32, read as the
+    # scale factor s, beta_slow and beta_fast, over the 4K pre-training
+    # context the same passage extends to 128K.
+    yarn_factor: float = 1.0
+    yarn_orig_len: int = 4096
+    yarn_beta_slow: float = 1.0
+    yarn_beta_fast: float = 32.0
 
     @property
     def d_row(self) -> int:

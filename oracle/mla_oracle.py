@@ -23,6 +23,11 @@ lost in extraction):
     0-based position in the sequence;
   * attention is causal: query at position t sees keys 0..t;
   * the softmax scale is 1/sqrt(d_h + d_R) (d_h the per-head content width);
+  * YaRN (V3 highlights page, highlight 13: "scale 40, base 1, factor 32"
+    with garbled names) is read as the YaRN method with s = 40,
+    beta_slow = 1, beta_fast = 32 over a 4K original context: per-pair
+    frequencies blended linearly in the pair's rotation count, and the
+    logits divided by the temperature t with sqrt(1/t) = 0.1 ln s + 1;
   * head i owns the i-th contiguous slice of each up-projection output and of
     W_O's input;
   * weights are stored [out][in] because the pages write W*h;
@@ -43,7 +48,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "rope", "compress_kv", "project_queries", "head_keys_values", "attend_head",
+    "rope", "rope_freqs", "yarn_on", "compress_kv", "project_queries", "head_keys_values", "attend_head",
     "output_projection", "prefill", "decode", "decode_absorbed",
     "cache_elements_per_token", "mha_elements_per_token", "softmax_scale",
 ]
@@ -57,15 +62,49 @@ def _f64(x):
 # RoPE (section 2.1: "ROPE(W_KR h)" and "ROPE(W_QR c_Q)")
 # ---------------------------------------------------------------------------
 
-def rope(x, pos, base):
-    """Rotate interleaved pairs (x[2k], x[2k+1]) by angle pos * base^(-2k/d_R).
+def yarn_on(dims):
+    return dims.yarn_factor not in (0.0, 1.0)
+
+
+def rope_freqs(dims):
+    """Angular frequency of each rotated pair k = 0..d_R/2-1.
+
+    Plain RoPE: theta_k = base^(-2k/d_R).  With YaRN (named, with its
+    constants, in highlight 13 of the V3 highlights page; the steps are those
+    of the YaRN method's "NTK-by-parts" interpolation): pair k turns
+    r_k = L_orig * theta_k / (2 pi) times over the original context; pairs
+    that turn fewer than beta_slow times are interpolated (theta_k / s), pairs
+    that turn more than beta_fast times are kept, and in between the two
+    frequencies are blended linearly in r_k."""
+    d_r = dims.d_rope
+    k = np.arange(d_r // 2, dtype=np.float64)
+    theta = np.power(float(dims.rope_base), -2.0 * k / d_r)
+    if not yarn_on(dims):
+        return theta
+    s = float(dims.yarn_factor)
+    r = float(dims.yarn_orig_len) * theta / (2.0 * np.pi)
+    lo, hi = float(dims.yarn_beta_slow), float(dims.yarn_beta_fast)
+    gamma = np.clip((r - lo) / (hi - lo), 0.0, 1.0)   # 0: interpolate, 1: keep
+    return (1.0 - gamma) * (theta / s) + gamma * theta
+
+
+def _yarn_theta(dims):
+    """The YaRN frequencies, or None for plain RoPE (rope() then forms
+    base^(-2k/d_R) itself)."""
+    return rope_freqs(dims) if yarn_on(dims) else None
+
+
+def rope(x, pos, base, theta=None):
+    """Rotate interleaved pairs (x[2k], x[2k+1]) by angle pos * theta_k, with
+    theta_k = base^(-2k/d_R) unless the frequencies are given.
 
     x: [..., d_R]; pos: integer array broadcastable to x.shape[:-1]."""
     x = _f64(x)
     d_r = x.shape[-1]
-    k = np.arange(d_r // 2, dtype=np.float64)
-    theta = np.power(float(base), -2.0 * k / d_r)
-    ang = _f64(pos)[..., None] * theta
+    if theta is None:
+        k = np.arange(d_r // 2, dtype=np.float64)
+        theta = np.power(float(base), -2.0 * k / d_r)
+    ang = _f64(pos)[..., None] * _f64(theta)
     c, s = np.cos(ang), np.sin(ang)
     xe, xo = x[..., 0::2], x[..., 1::2]
     out = np.empty_like(x)
@@ -75,8 +114,13 @@ def rope(x, pos, base):
 
 
 def softmax_scale(dims):
-    """1/sqrt(d_h + d_R): section 2.1, attention computation."""
-    return 1.0 / np.sqrt(dims.d_nope + dims.d_rope)
+    """1/sqrt(d_h + d_R): section 2.1, attention computation.  With YaRN the
+    logits are further divided by the method's temperature t, where
+    sqrt(1/t) = 0.1 ln(s) + 1."""
+    scale = 1.0 / np.sqrt(dims.d_nope + dims.d_rope)
+    if yarn_on(dims):
+        scale *= (0.1 * np.log(float(dims.yarn_factor)) + 1.0) ** 2
+    return scale
 
 
 # ---------------------------------------------------------------------------
@@ -88,7 +132,7 @@ def compress_kv(W, h, pos, dims):
     positions pos [T].  These two are the whole cached row."""
     h = _f64(h)
     c_kv = h @ _f64(W["w_dkv"]).T
-    k_r = rope(h @ _f64(W["w_kr"]).T, pos, dims.rope_base)
+    k_r = rope(h @ _f64(W["w_kr"]).T, pos, dims.rope_base, _yarn_theta(dims))
     return c_kv, k_r
 
 
@@ -113,7 +157,7 @@ def project_queries(W, h, pos, dims):
     c_q = h @ _f64(W["w_dq"]).T
     q_c = (c_q @ _f64(W["w_uq"]).T).reshape(T, dims.n_heads, dims.d_nope)
     q_r_raw = (c_q @ _f64(W["w_qr"]).T).reshape(T, dims.n_heads, dims.d_rope)
-    q_r = rope(q_r_raw, _f64(pos)[:, None], dims.rope_base)
+    q_r = rope(q_r_raw, _f64(pos)[:, None], dims.rope_base, _yarn_theta(dims))
     return q_c, q_r
 
 

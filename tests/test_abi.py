@@ -89,6 +89,13 @@ CONFIG_CASES = [
     (dict(rope_base=0.0), -2),
     (dict(d_model=7000), -7),   # not a multiple of 64 for bf16
     (dict(d_rope=256), -7),     # more RoPE pairs than supported
+    (dict(yarn_factor=40.0), 0),                                   # DeepSeek-V3 at 128K
+    (dict(yarn_factor=0.0), 0),                                    # off
+    (dict(yarn_factor=0.5), -2),                                   # shrinking the context
+    (dict(yarn_factor=float("inf")), -2),
+    (dict(yarn_factor=40.0, yarn_orig_len=0), -2),
+    (dict(yarn_factor=40.0, yarn_beta_slow=32.0, yarn_beta_fast=1.0), -2),
+    (dict(yarn_factor=40.0, yarn_beta_slow=0.0), -2),
 ]
 
 

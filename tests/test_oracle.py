@@ -192,6 +192,61 @@ def pin_rope_in_scores():
         assert abs(r["probs"][i][1, 0] - p0) <= 1e-14, (r["probs"][i][1, 0], p0)
 
 
+def pin_yarn_frequencies():
+    """YaRN (highlight 13 of the V3 highlights page): pairs that turn at most
+    beta_slow times over the original context rotate at theta/s, i.e. as
+    plain RoPE at position p/s; pairs that turn at least beta_fast times keep
+    theta; the blend in between lies between the two, and less interpolation
+    goes to faster pairs.  For DeepSeek-V3 (d_R 64, base 10^4, L 4096,
+    s 40, 1, 32) the pair k turns 4096 * 10^(-k/8) / (2 pi) times: pairs
+    0..10 turn at least 32 times, pairs 23..31 at most once."""
+    import dataclasses
+    rng = np.random.Generator(np.random.PCG64(31))
+    x = rng.standard_normal(16)
+    slow = dataclasses.replace(TINY, yarn_factor=40.0, yarn_orig_len=1)            # every pair slow
+    fast = dataclasses.replace(TINY, yarn_factor=40.0, yarn_orig_len=10 ** 12)     # every pair fast
+    for p in (0, 1, 7, 300, 5000):
+        got = O.rope(x, p, TINY.rope_base, O.rope_freqs(slow))
+        assert np.allclose(got, O.rope(x, p / 40.0, TINY.rope_base), rtol=0, atol=1e-12)
+        assert np.array_equal(O.rope(x, p, TINY.rope_base, O.rope_freqs(fast)), O.rope(x, p, TINY.rope_base))
+    ds = dataclasses.replace(DSV3, yarn_factor=40.0)
+    th = 10000.0 ** (-2.0 * np.arange(32) / 64)
+    ratio = O.rope_freqs(ds) / th
+    assert np.allclose(ratio[:11], 1.0, rtol=0, atol=1e-15)
+    assert np.allclose(ratio[23:], 1.0 / 40.0, rtol=1e-15, atol=0)
+    mid = ratio[11:23]
+    assert np.all((mid > 1.0 / 40.0) & (mid < 1.0)) and np.all(np.diff(ratio) <= 1e-15)
+    # relative-position property survives the new frequencies
+    y = rng.standard_normal(64)
+    z = rng.standard_normal(64)
+    f = O.rope_freqs(ds)
+    d1 = O.rope(y, 9000, 1.0, f) @ O.rope(z, 8000, 1.0, f)
+    d2 = O.rope(y, 131000, 1.0, f) @ O.rope(z, 130000, 1.0, f)
+    assert np.isclose(d1, d2, rtol=1e-8)
+
+
+def pin_yarn_in_scores():
+    """YaRN through the whole prefill: as pin_rope_in_scores, with every pair
+    slow (the angle per position becomes 1/s) and the logits multiplied by
+    the temperature factor (0.1 ln s + 1)^2."""
+    import dataclasses
+    d = dataclasses.replace(Dims(d_model=12, n_heads=2, d_nope=4, d_rope=2, d_v=3, d_c=5, d_cq=6),
+                            yarn_factor=40.0, yarn_orig_len=1)
+    W = _weights(d, 29)
+    W["w_uq"][:] = 0
+    x = _h(1, d, 30)[0]
+    r = O.prefill(d, W, np.stack([x, x]), return_probs=True)
+    scale = (0.1 * math.log(40.0) + 1.0) ** 2 / math.sqrt(d.d_nope + d.d_rope)
+    b = W["w_kr"] @ x
+    rot = lambda ang: np.array([[math.cos(ang), -math.sin(ang)], [math.sin(ang), math.cos(ang)]])
+    for i in range(d.n_heads):
+        a = W["w_qr"][2 * i:2 * i + 2] @ (W["w_dq"] @ x)
+        s0 = a @ rot(-1.0 / 40.0) @ b * scale
+        s1 = a @ b * scale
+        p0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        assert abs(r["probs"][i][1, 0] - p0) <= 1e-14, (r["probs"][i][1, 0], p0)
+
+
 def pin_prefill_decode_agree(dims=TINY, L=24, steps=5):
     """P9: a prefill of L followed by decode steps equals one longer prefill."""
     W = _weights(dims, 23)
@@ -255,7 +310,7 @@ def pin_brute_force(dims=SMALL, L=4):
 
 ALL_PINS = [pin_absorbed_equals_plain, pin_softmax_rows, pin_causal, pin_single_key,
             pin_zero_query, pin_head_isolation, pin_mha_special_case, pin_rope_rotation, pin_rope_in_scores,
-            pin_prefill_decode_agree, pin_brute_force]
+            pin_yarn_frequencies, pin_yarn_in_scores, pin_prefill_decode_agree, pin_brute_force]
 
 
 # ---------------------------------------------------------------------------

@@ -1,5 +1,7 @@
 """Plant plausible mistakes in the oracle (on the CPU) and check that the pins
 in test_oracle.py catch every one of them."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -14,21 +16,41 @@ _out = O.output_projection
 _ckv = O.compress_kv
 
 
-def _rope_sign(x, pos, base):
-    return _rope(x, -np.asarray(pos), base)
+_freqs = O.rope_freqs
+_scale = O.softmax_scale
 
 
-def _rope_freq(x, pos, base):
+def _rope_sign(x, pos, base, theta=None):
+    return _rope(x, -np.asarray(pos), base, theta)
+
+
+def _rope_freq(x, pos, base, theta=None):
     # frequency base^(-k/d_R) instead of base^(-2k/d_R)
     d = np.asarray(x).shape[-1]
-    return _rope(x, pos, base ** 0.5) if d > 2 else _rope(x, pos, base)
+    return _rope(x, pos, base ** 0.5, theta) if d > 2 else _rope(x, pos, base, theta)
 
 
-def _rope_halfsplit_pairs_wrong(x, pos, base):
+def _yarn_ramp_inverted(dims):
+    # interpolate the fast pairs and keep the slow ones
+    th = _freqs(dataclasses.replace(dims, yarn_factor=1.0))
+    got = _freqs(dims)
+    return th * th / got if O.yarn_on(dims) else got
+
+
+def _yarn_no_temperature(dims):
+    return 1.0 / np.sqrt(dims.d_nope + dims.d_rope)
+
+
+def _yarn_temperature_unsquared(dims):
+    s = _scale(dims)
+    return s / (0.1 * np.log(dims.yarn_factor) + 1.0) if O.yarn_on(dims) else s
+
+
+def _rope_halfsplit_pairs_wrong(x, pos, base, theta=None):
     # rotate (x[k], x[k+1]) over overlapping pairs: a wrong index
     x = np.asarray(x, dtype=np.float64)
     y = np.roll(x, 1, axis=-1)
-    return np.roll(_rope(y, pos, base), -1, axis=-1)
+    return np.roll(_rope(y, pos, base, theta), -1, axis=-1)
 
 
 def _attend_drop_rope(q_c_i, q_r_i, qpos, k_c_i, k_r, v_i, scale, return_probs=False):
@@ -117,6 +139,10 @@ MUTATIONS = {
     "q_no_rope": ("project_queries", _pq_no_rope),
     "output_head_order": ("output_projection", _out_head_order),
     "k_no_rope": ("compress_kv", _ckv_kr_unroped),
+    "yarn_ramp_inverted": ("rope_freqs", _yarn_ramp_inverted),
+    "yarn_no_interpolation": ("rope_freqs", lambda d: _freqs(dataclasses.replace(d, yarn_factor=1.0))),
+    "yarn_no_temperature": ("softmax_scale", _yarn_no_temperature),
+    "yarn_temperature_unsquared": ("softmax_scale", _yarn_temperature_unsquared),
 }
 
 

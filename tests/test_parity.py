@@ -1,11 +1,13 @@
 """GPU parity: libmla (through the C ABI) against the CPU oracle on the same
 seeded inputs, element by element.  fp32: max-abs <= 1e-4; bf16: relative
 Frobenius <= 2e-2 and max-abs <= 5e-2."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
 
-from mla_inputs import Dims, DSV3, make_workload
+from mla_inputs import Dims, DSV3, TINY, make_workload
 from oracle import mla_oracle as O
 
 from tests.gpu_harness import (CacheBuf, Timer, assert_close, decode_cache, layer_for, oracle_decode_seq,
@@ -222,3 +224,48 @@ def test_dsv3_decode_large_logit_spread():
             mag = max(1.0, float(np.max(np.abs(r))))
             say(f"{what} b={b}: max_abs={e.max_abs:.3e} (max|ref|={mag:.1f}) rel_frob={e.rel_frob:.3e}")
             assert e.rel_frob <= BF16_REL_FROB and e.max_abs <= BF16_MAX_ABS * mag, (what, b, e)
+
+
+# YaRN long-context RoPE (highlight 13 of the V3 highlights page: s = 40,
+# beta_slow = 1, beta_fast = 32 over the 4K original context).  The library
+# forms the blended frequencies and the softmax temperature on the host; the
+# kernels are the plain-RoPE ones.
+YARN_DS = dataclasses.replace(DSV3, yarn_factor=40.0)
+YARN_TINY = dataclasses.replace(TINY, yarn_factor=40.0, yarn_orig_len=32)
+
+
+def test_yarn_tiny_fp32_prefill():
+    """fp32, 64 positions over a 32-token original context (every regime of
+    the blend occurs among the 8 pairs)."""
+    wl = make_workload(1, dims=YARN_TINY)
+    layer = layer_for(wl)
+    W = weights64(wl)
+    h = wl.h_f32[0, :wl.seq_len].astype(np.float64)
+    plain = O.prefill(TINY, W, h)["u"]
+    assert not np.allclose(O.prefill(YARN_TINY, W, h)["u"], plain, rtol=1e-3, atol=1e-3)
+    wl.h_f32, wl.h_bits = wl.h_f32[:, :wl.seq_len], (None if wl.h_bits is None else wl.h_bits[:, :wl.seq_len])
+    _prefill_check(wl, layer)
+
+
+def test_yarn_dsv3_prefill_small():
+    wl = make_workload(3, dims=YARN_DS, batch=1, seq_len=300)
+    layer = layer_for(wl)
+    _prefill_check(wl, layer)
+
+
+@pytest.mark.parametrize("B,L,nq", [(1, 4600, 2), (3, 700, 1)])
+def test_yarn_dsv3_decode(B, L, nq):
+    """Decode with positions past the 4K original context (the new tokens'
+    RoPE key and query rotate at the blended frequencies)."""
+    wl = make_workload(2, dims=YARN_DS, batch=B, uniform_len=L, n_q=nq)
+    layer = layer_for(wl)
+    cache = decode_cache(wl, layer)
+    say(f"yarn decode B={B} L={L} n_q={nq}")
+    u, o = run_decode(wl, layer, cache)
+    d = wl.dims
+    for b in range(B):
+        ref = oracle_decode_seq(wl, b)
+        assert_close(u[b], ref["u"], True, f"u b={b}")
+        assert_close(o.view(B, nq, d.n_heads, d.d_v)[b], ref["o"], True, f"o b={b}")
+        got_new = cache.read_rows(b, np.arange(L - nq, L))
+        assert_close(got_new, ref["row_new"], True, f"new cache rows b={b}")

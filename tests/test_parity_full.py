@@ -3,11 +3,13 @@ configuration bench.py times, on outputs the oracle can compute one by one:
 whole sequences (decode), sampled rows (prefill) and sampled heads (128K
 decode).  Same tolerances as test_parity (bf16: relative Frobenius <= 2e-2,
 max-abs <= 5e-2)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
 
-from mla_inputs import make_workload
+from mla_inputs import DSV3, make_workload
 from oracle import mla_oracle as O
 
 from tests.gpu_harness import Timer, assert_close, decode_cache, layer_for, run_decode, say, upload, weights64
@@ -83,11 +85,14 @@ def test_full_decode_ragged_paged_b128():
     _decode_seq_check(wl, u, o, cache, seqs=seqs)
 
 
-def test_full_decode_len131072_nq2():
+@pytest.mark.parametrize("yarn", [False, True], ids=["rope", "yarn40"])
+def test_full_decode_len131072_nq2(yarn):
     """Four sequences of 128K, two new tokens each (causal between them): one
-    sequence in full, sampled heads of the others."""
+    sequence in full, sampled heads of the others.  The YaRN case is the
+    configuration the V3 highlights page runs at 128K (highlight 13: s = 40,
+    beta_slow = 1, beta_fast = 32 over the 4K original context)."""
     with Timer("draw 128K workload"):
-        wl = make_workload(5)
+        wl = make_workload(5, dims=dataclasses.replace(DSV3, yarn_factor=40.0) if yarn else None)
     layer = layer_for(wl)
     cache = decode_cache(wl, layer)
     say("128K decode n_q=2")
