@@ -661,7 +661,7 @@ const char *mla_status_string(mla_status s) {
   return "unknown status";
 }
 
-const char *mla_version(void) { return "libmla 0.1 (gfx950)"; }
+const char *mla_version(void) { return "libmla 0.2 (gfx950)"; }
 
 mla_status mla_timing_enable(int32_t on) {
   g_timing = on != 0;

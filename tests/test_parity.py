@@ -136,12 +136,13 @@ def test_dsv3_prefill_paged():
 
 
 @pytest.mark.parametrize("B,L,nq", [(4, 300, 1), (2, 33, 1), (3, 1, 1), (2, 500, 2), (2, 2, 2), (1, 97, 3),
-                                     (20, 50, 1), (11, 40, 3)])
+                                     (20, 50, 1), (11, 40, 3), (4, 260, 4), (2, 900, 8)])
 def test_dsv3_decode_small(B, L, nq):
     """DeepSeek-V3 shapes, bf16 decode against a contiguous latent cache.  20
     tokens leave the second 16-token block of the one-launch query path and of
     the combine partly empty; 33 tokens take the separate up-projection and
-    absorption GEMMs."""
+    absorption GEMMs; 4 and 8 query tokens per sequence are multi-token
+    verification steps (causal among the new tokens)."""
     wl = make_workload(2, batch=B, uniform_len=L, n_q=nq)
     layer = layer_for(wl)
     cache = decode_cache(wl, layer)
