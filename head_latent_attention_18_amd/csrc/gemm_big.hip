@@ -40,9 +40,14 @@ constexpr int GLOADS = (XCHK + WCHK) / GNT;     // copy instructions per wave pe
 constexpr int GSTAGE = (XCHK + WCHK) * 8;       // elements per stage (32768 = 64 KB)
 constexpr int NSTEP = GBK / 16;                 // MFMA k steps per slab (4)
 constexpr int EPI_LD = GBN + 4;                 // fp32 row pitch of the epilogue staging
+// feature-major staging of the transposed store: 128 tokens per feature row,
+// pitch 136 floats (4 rows apart = 32 banks apart, so the two lane halves of
+// a 32x32 accumulator write disjoint banks)
+constexpr int EPI_LDT = GBM / 2 + 8;
 static_assert(GNT % (GBN / 4) == 0, "");
 // LDS: the ring, reused for half a tile of fp32 results in the epilogue
-constexpr int RING_ELEMS = (GNS * GSTAGE > GBM / 2 * EPI_LD * 2) ? GNS * GSTAGE : GBM / 2 * EPI_LD * 2;
+constexpr int cmax(int x, int y) { return x > y ? x : y; }
+constexpr int RING_ELEMS = cmax(GNS * GSTAGE, cmax(GBM / 2 * EPI_LD * 2, GBN * EPI_LDT * 2));
 
 template <int N>
 __device__ inline void wait_vm() {
@@ -183,7 +188,9 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
     wait_lgkm0();
     __syncthreads();
     if (wm == half) {
-      // acc[i][j]: features wn*64 + 32i + 8q + 4fh + 0..3, token 32j + fr
+      // acc[i][j]: features wn*64 + 32i + 8q + 4fh + 0..3, token 32j + fr;
+      // rows [token][feature] for the row-major store, [feature][token] for
+      // the transposed one
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -191,8 +198,13 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int f = wn * 64 + i * 32 + 8 * q + 4 * fh, t = j * 32 + fr;
-            *(lds_f32x4 *)(ep + t * EPI_LD + f) =
-                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            if constexpr (SWAP) {
+              *(lds_f32x4 *)(ep + t * EPI_LD + f) =
+                  f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ep[(f + e) * EPI_LDT + t] = acc[i][j][4 * q + e];
+            }
           }
     }
     __syncthreads();
@@ -269,22 +281,26 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
         }
       }
     } else {
-      // transposed plain store dst[n * ld + m]: items of 4 consecutive tokens
+      // transposed plain store dst[n * ld + m]: items of 8 consecutive
+      // tokens of one feature (two 16-byte LDS reads, one 16-byte store;
+      // 16 lanes cover a feature's 128 tokens)
       const Seg &g = a.epi.seg[0];
-      for (int it = tid; it < GBN * (128 / 4); it += GNT) {
-        const int f = it / 32, t = (it % 32) * 4;
+      const bool vec = (g.ld & 7) == 0 && (((size_t)g.dst) & 15) == 0;
+      for (int it = tid; it < GBN * (128 / 8); it += GNT) {
+        const int f = it / 16, t = (it % 16) * 8;
         const int n = n0 + f, m = mh + t;
         if (n < a.N && m < a.M) {
-          bf16 *dst = (bf16 *)g.dst + (long)n * g.ld;
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = ep[(t + e) * EPI_LD + f];
-          if (m + 3 < a.M && (g.ld & 3) == 0) {
-            store4<bf16>(dst, m, v, 0);
+          bf16 *dst = (bf16 *)g.dst + (long)n * g.ld + m;
+          const f32x4 lo = *(const lds_f32x4 *)(ep + f * EPI_LDT + t);
+          const f32x4 hi = *(const lds_f32x4 *)(ep + f * EPI_LDT + t + 4);
+          if (m + 7 < a.M && vec) {
+            *(bf16x8 *)dst = bf16x8{(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3],
+                                    (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
           } else {
+            const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (m + e < a.M) dst[m + e] = (bf16)v[e];
+            for (int e = 0; e < 8; ++e)
+              if (m + e < a.M) dst[e] = (bf16)v[e];
           }
         }
       }
