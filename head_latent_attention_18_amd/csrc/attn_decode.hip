@@ -895,8 +895,11 @@ __global__ __launch_bounds__(512, 1) void decode_attn_dma8_kernel(DecodeArgs a) 
   }
   __syncthreads();
   bf16 *op = (bf16 *)a.o_part + (((long)b * a.n_splits + s) * R + rbase) * DC + lane * 8;
+  // streaming stores: the partials are read once, by the combine, from
+  // other XCDs (47.1 -> 45.2 us against write-allocating stores)
   for (int rl = wave; rl < ROWS && rbase + rl < R; rl += NW)
-    *(bf16x8 *)(op + (long)rl * DC) = *(const lds_bf16x8 *)(ot + rl * DC + (lane ^ (rl & 15)) * 8);
+    __builtin_nontemporal_store(*(const lds_bf16x8 *)(ot + rl * DC + (lane ^ (rl & 15)) * 8),
+                                (bf16x8 *)(op + (long)rl * DC));
 }
 
 // Exact attention of one query row over its whole sequence, straight from the
