@@ -254,6 +254,20 @@ def test_yarn_dsv3_prefill_small():
     _prefill_check(wl, layer)
 
 
+def test_yarn_dsv3_decode_ragged_paged():
+    """YaRN with ragged lengths over a paged cache in a permuted block order."""
+    wl = make_workload(4, dims=YARN_DS, batch=5, ragged_max=5000, block_size=64)
+    layer = layer_for(wl)
+    cache = decode_cache(wl, layer)
+    say(f"yarn ragged paged decode lens={wl.lens.tolist()}")
+    u, o = run_decode(wl, layer, cache)
+    for b in range(wl.batch):
+        ref = oracle_decode_seq(wl, b)
+        assert_close(u[b], ref["u"], True, f"u b={b} len={wl.lens[b]}")
+        L = int(wl.lens[b])
+        assert_close(cache.read_rows(b, np.arange(L - 1, L)), ref["row_new"], True, f"new row b={b}")
+
+
 @pytest.mark.parametrize("B,L,nq", [(1, 4600, 2), (3, 700, 1)])
 def test_yarn_dsv3_decode(B, L, nq):
     """Decode with positions past the 4K original context (the new tokens'
