@@ -139,6 +139,49 @@ def run_prefill(args, dev):
                         for k, v in pk_times.items()}}
 
 
+def chunk_flops(d, C, P):
+    """Algorithmic flops of a chunk of C new tokens against P cached ones in
+    the pages' (non-absorbed) form: projections of the chunk, K/V
+    up-projection of all P + C keys, causal attention, W_O."""
+    pairs = C * P + C * (C + 1) // 2
+    return (2 * C * d.d_model * (d.d_cq + d.d_c + d.d_rope)
+            + 2 * C * d.d_cq * d.n_heads * (d.d_nope + d.d_rope)
+            + 2 * (P + C) * d.d_c * d.n_heads * (d.d_nope + d.d_v)
+            + pairs * d.n_heads * 2 * (d.d_nope + d.d_rope + d.d_v)
+            + 2 * C * d.n_heads * d.d_v * d.d_model)
+
+
+def run_chunk(args, dev, C=512, P=4096):
+    """Chunked prefill: 512 new tokens of one sequence against a 4096-token
+    cached prefix (mla_decode with n_q = 512, causal among the chunk)."""
+    import numpy as np
+    import torch
+    from head_latent_attention_18_amd.layer import MlaLayer, cache_from_rows, upload
+    from mla_inputs import make_workload
+    wc = make_workload(2, batch=1, uniform_len=P + C, n_q=C)
+    lc = MlaLayer.from_host(wc.dims, "bf16", wc.weights_f32, wc.weights_bits)
+    cc = cache_from_rows(wc.cache_bits, wc.lens, wc.dims.d_row, True)
+    hc = upload(wc.h_f32, wc.h_bits, True)
+    lens = torch.from_numpy(wc.lens.astype(np.int32)).to(dev)
+    run = lambda i: lc.decode(hc, lens, P + C, cc)
+    for i in range(3):
+        run(i)
+    torch.cuda.synchronize()
+    k = max(3, args.steps // 5)
+    t0 = time.perf_counter()
+    for i in range(k):
+        run(i)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / k
+    times = kernel_times(run, k)
+    fl = chunk_flops(wc.dims, C, P)
+    log(f"chunk: {dt * 1e3:.3f} ms, {C / dt:.0f} tokens/s, {fl / dt / 1e12:.1f} TFLOPS (non-absorbed flops)")
+    return {"workload": f"dsv3-chunk{C}-prefix{P}", "ms": round(dt * 1e3, 4), "tokens_per_s": round(C / dt, 1),
+            "TFLOPS_nonabsorbed": round(fl / dt / 1e12, 1), "alg_flops": fl,
+            "kernels": {k2: {"avg_us": round(v["avg_ms"] * 1e3, 2), "launches_per_step": v["launches_per_step"]}
+                        for k2, v in times.items()}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,7 +192,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the oracle's first (parity) pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="least CPU time of the timed oracle sample")
-    ap.add_argument("--only", choices=["all", "decode", "prefill"], default="all",
+    ap.add_argument("--only", choices=["all", "decode", "prefill", "chunk"], default="all",
                     help="profiling runs: time one path only (the JSON line is printed for 'all' and 'decode')")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only copy a buffer of this many MB three times (scale for HBM byte counters)")
@@ -180,6 +223,9 @@ def main():
 
     if args.only == "prefill":
         print(json.dumps(run_prefill(args, dev)), flush=True)
+        return
+    if args.only == "chunk":
+        print(json.dumps(run_chunk(args, dev)), flush=True)
         return
 
     # ------------------------------------------------------------ decode

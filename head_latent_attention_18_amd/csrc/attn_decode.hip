@@ -27,6 +27,22 @@
 
 namespace mla {
 
+// Block -> work item (unit = (sequence, split), row group).  Items in unit
+// order, a contiguous eighth of them per XCD (blocks x, x+8, x+16, .. run on
+// XCD x): with eight units or more the row groups of a unit and the splits of
+// a sequence share an XCD, whose L2 serves their common reads (queries, cache
+// tiles); with fewer units (one long sequence, many query rows) the row
+// groups still spread over all eight XCDs.
+__device__ inline bool decode_item(const DecodeArgs &a, int &unit, int &rg) {
+  const int W = a.B * a.n_splits * a.row_groups, per = (W + 7) / 8;
+  const int slot = blockIdx.x >> 3, item = (blockIdx.x & 7) * per + slot;
+  if (slot >= per || item >= W) return false;
+  unit = item / a.row_groups;
+  rg = item - unit * a.row_groups;
+  return true;
+}
+inline int decode_grid(const DecodeArgs &a) { return 8 * ((a.B * a.n_splits * a.row_groups + 7) / 8); }
+
 constexpr int KVT = 32;  // cache rows per tile (two 16-row MFMA blocks)
 
 template <typename T, int NW, int HB, int DC, int DR>
@@ -57,13 +73,9 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 15, lgrp = lane >> 4;
 
-  // block -> (unit = (b, s), row group): the row groups of one unit, and the
-  // splits of one sequence, share an XCD (its L2 serves their common reads)
-  const int units = a.B * a.n_splits;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int rg = slot % a.row_groups;
-  const int unit = xcd * ((units + 7) / 8) + slot / a.row_groups;
-  if (unit >= units) return;
+  // block -> (unit = (b, s), row group)
+  int unit, rg;
+  if (!decode_item(a, unit, rg)) return;
   const int b = unit / a.n_splits, s = unit % a.n_splits;
   // lengths beyond the plan or the cache are clamped, so no read leaves the cache
   const int len = (int)min((long)a.lens[b], min((long)a.n_splits * a.chunk, a.cache.cap));
@@ -357,11 +369,8 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 15, lgrp = lane >> 4;
-  const int units = a.B * a.n_splits;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int rg = slot % a.row_groups;
-  const int unit = xcd * ((units + 7) / 8) + slot / a.row_groups;
-  if (unit >= units) return;
+  int unit, rg;
+  if (!decode_item(a, unit, rg)) return;
   const int b = unit / a.n_splits, s = unit % a.n_splits;
   const int len = (int)min((long)a.lens[b], min((long)a.n_splits * a.chunk, a.cache.cap));
   const int kv_beg = s * a.chunk;
@@ -662,11 +671,8 @@ __global__ __launch_bounds__(512, 1) void decode_attn_dma8_kernel(DecodeArgs a) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int rw = wave & 3, kh = wave >> 2;          // score roles: row block, key half
-  const int units = a.B * a.n_splits;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int rg = slot % a.row_groups;
-  const int unit = xcd * ((units + 7) / 8) + slot / a.row_groups;
-  if (unit >= units) return;
+  int unit, rg;
+  if (!decode_item(a, unit, rg)) return;
   const int b = unit / a.n_splits, s = unit % a.n_splits;
   const int len = (int)min((long)a.lens[b], min((long)a.n_splits * a.chunk, a.cache.cap));
   const int kv_beg = s * a.chunk;
@@ -1191,8 +1197,7 @@ int decode_rows_per_group(int dtype, long B, long R, int cus) {
 
 template <typename T, int NW, int HB, int DC, int DR>
 static hipError_t launch_attn(const DecodeArgs &a, hipStream_t st) {
-  const int units = a.B * a.n_splits;
-  const int grid = ((units + 7) / 8) * 8 * a.row_groups;
+  const int grid = decode_grid(a);
   timing_before("decode_attn", st);
   hipLaunchKernelGGL((decode_attn_kernel<T, NW, HB, DC, DR>), dim3(grid), dim3(64 * NW), 0, st, a);
   timing_after("decode_attn", st);
@@ -1202,8 +1207,7 @@ static hipError_t launch_attn(const DecodeArgs &a, hipStream_t st) {
 hipError_t launch_decode_attn(int dtype, const DecodeArgs &a, hipStream_t st) {
   const bool tile_in_block = !a.cache.table || (a.cache.block_size % KVT == 0);
   if (dtype == 1 && a.d_c == 512 && a.d_rope == 64 && tile_in_block) {
-    const int units = a.B * a.n_splits;
-    const int grid = ((units + 7) / 8) * 8 * a.row_groups;
+    const int grid = decode_grid(a);
     timing_before("decode_attn", st);
     if (a.rows == 64) {
       if (a.cache.table)
