@@ -368,8 +368,11 @@ static hipError_t launch_t(GemmArgs &a, hipStream_t st, const char *name) {
   a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + BN - 1) / BN;
   a.grouped = a.tiles_m >= 8 && a.tiles_n >= 8;
-  dim3 grid(a.grouped ? ((a.tiles_m + 7) / 8) * ((a.tiles_n + 7) / 8) * 64 : a.tiles_m * a.tiles_n,
-            a.batch * a.splits);
+  // grouped: 8x8-tile groups dealt to the XCDs in rows of eight groups
+  // (block -> group (block >> 9) * 8 + (block & 7)), so the grid covers whole
+  // rows of groups even when the group count is not a multiple of eight
+  const int groups = ((a.tiles_m + 7) / 8) * ((a.tiles_n + 7) / 8);
+  dim3 grid(a.grouped ? ((groups + 7) / 8) * 8 * 64 : a.tiles_m * a.tiles_n, a.batch * a.splits);
   if (a.name) name = a.name;
   timing_before(name, st);
   hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, SWAP, WKN>), grid, dim3(64 * WM * WN), 0, st, a);

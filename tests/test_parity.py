@@ -84,7 +84,7 @@ def test_tiny_fp32_prefill_then_decode():
         assert_close(cache.read_rows(0, np.arange(total)), ref_rows, False, "tiny cache after decode")
 
 
-@pytest.mark.parametrize("B,L", [(1, 64), (2, 200), (1, 1), (3, 37), (2, 8), (1, 520), (1, 261)])
+@pytest.mark.parametrize("B,L", [(1, 64), (2, 200), (1, 1), (3, 37), (2, 8), (1, 520), (1, 261), (1, 200), (1, 150), (1, 240)])
 def test_dsv3_prefill_small(B, L):
     """DeepSeek-V3 shapes, bf16, small sequences with ragged tiles."""
     wl = make_workload(3, batch=B, seq_len=L)
