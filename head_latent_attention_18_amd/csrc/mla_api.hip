@@ -121,7 +121,15 @@ PrefillPlan plan_prefill(const mla_config *c, int64_t T) {
 
 struct SplitK { int splits, k_chunk; };
 
-int gemm_tile_for(int dtype, int64_t M) { return (dtype == MLA_BF16 && M >= 256) ? TILE_BIG : TILE_SKINNY; }
+// 256x256 tiles (bf16) unless they would leave all but a few CUs idle: a
+// few hundred tokens against a narrow weight (a 512-token chunk: 18 tiles for
+// the down projection) go to the 32x64-tile kernel, which spreads over every
+// CU (180 -> 90 us there); from 32 tiles on the big tiles win (W_O at 512
+// tokens, 56 tiles: 362 against 393 us).
+int gemm_tile_for(int dtype, int64_t M, int64_t N, int64_t batch) {
+  if (dtype != MLA_BF16 || M < 256) return TILE_SKINNY;
+  return ((M + 255) / 256) * ((N + 255) / 256) * batch >= kCUs / 8 ? TILE_BIG : TILE_SKINNY;
+}
 
 // Split K only as far as needed for about two workgroups per CU: the
 // weight-streaming kernel (bf16, up to 128 tokens) works on 64-feature tiles
@@ -130,7 +138,7 @@ SplitK choose_splitk(int dtype, int64_t M, int64_t N, int64_t K, int batch) {
   SplitK r;
   r.splits = 1;
   r.k_chunk = (int)K;
-  const int tile = gemm_tile_for(dtype, M);
+  const int tile = gemm_tile_for(dtype, M, N, batch);
   if (tile != TILE_SKINNY) return r;
   int bk, bn;
   if (dtype == MLA_BF16 && M <= 128) {
@@ -320,7 +328,7 @@ hipError_t run_compress(const mla_config *c, const mla_weights *w, const void *h
   a.partial = partial;
   a.name = with_q ? "q_kv_down" : "kv_compress";
   a.reduce_name = "q_kv_down.reduce";
-  return launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M), 1, 0, a, st);
+  return launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 1, 0, a, st);
 }
 
 // q = c_Q [W_UQ; W_QR]^T with RoPE on the q_R part.  The content part goes to
@@ -364,7 +372,7 @@ hipError_t run_query(const mla_config *c, const mla_weights *w, const void *c_q,
                      void *qc, long qc_ld, long qc_head_ld, void *qr, long qr_ld, long qr_head_ld, int qr_off,
                      SplitK sk, float *partial, hipStream_t st) {
   GemmArgs a = query_args(c, w, c_q, M, rows, qc, qc_ld, qc_head_ld, qr, qr_ld, qr_head_ld, qr_off, sk, partial);
-  return launch_gemm(c->dtype == MLA_BF16, gemm_tile_for(c->dtype, M), 1, 0, a, st);
+  return launch_gemm(c->dtype == MLA_BF16, gemm_tile_for(c->dtype, M, a.N, a.batch), 1, 0, a, st);
 }
 
 // u = o W_O^T
@@ -382,7 +390,7 @@ hipError_t run_output(const mla_config *c, const mla_weights *w, const void *o, 
   a.partial = partial;
   a.name = "o_proj";
   a.reduce_name = "o_proj.reduce";
-  return launch_gemm(c->dtype == MLA_BF16, gemm_tile_for(c->dtype, M), 1, 0, a, st);
+  return launch_gemm(c->dtype == MLA_BF16, gemm_tile_for(c->dtype, M, a.N, a.batch), 1, 0, a, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -500,7 +508,7 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
     a.epi.seg[0] = seg_plain(NH * cfg->d_nope, ws + p.k, (long)NH * cfg->d_nope);
     a.epi.nseg = 1;
     a.name = "k_up";
-    e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M), 1, 0, a, st);
+    e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 1, 0, a, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
   }
   {  // V^T = (c_KV W_UV^T)^T -> [n_h*d_v][T]
@@ -511,7 +519,7 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
     a.epi.seg[0] = seg_plain(NH * cfg->d_v, ws + p.vt, (long)T);
     a.epi.nseg = 1;
     a.name = "v_up";
-    e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M), 0, 0, a, st);
+    e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 0, 0, a, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
   }
   {
@@ -597,7 +605,7 @@ mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h
       a.epi.nseg = 1;
       a.partial = partial;
       a.name = "absorb";
-      e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M), 1, 1, a, st);
+      e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 1, 1, a, st);
       if (e != hipSuccess) return MLA_ERR_HIP;
     }
   }
@@ -640,7 +648,7 @@ mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h
     a.epi.nseg = 1;
     a.partial = partial;
     a.name = "unabsorb";
-    e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M), 1, 0, a, st);
+    e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 1, 0, a, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
   }
   e = run_output(cfg, w, o, M, u, p.sk5, partial, st);
