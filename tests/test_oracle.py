@@ -247,6 +247,24 @@ def pin_yarn_in_scores():
         assert abs(r["probs"][i][1, 0] - p0) <= 1e-14, (r["probs"][i][1, 0], p0)
 
 
+def pin_yarn_blend_hand_worked():
+    """YaRN's blend inside the ramp, against values worked by hand from the
+    method's definition (tests/golden/yarn_blend_hand_worked.json, V3
+    highlights page, highlight 13): pairs 11 and 16 of DeepSeek-V3 (d_R 64,
+    base 10^4, 4K original context, s 40) and one pair over a 100-token
+    original context.  A ramp linear in the pair index instead of in the
+    rotation count r_k moves pair 16 from 0.00199 to 0.0055."""
+    import dataclasses
+    g = json.load(open(os.path.join(GOLDEN, "yarn_blend_hand_worked.json")))
+    for c in g["cases"]:
+        d = dataclasses.replace(Dims(d_model=8, n_heads=1, d_nope=2, d_rope=c["d_rope"], d_v=2, d_c=4, d_cq=4),
+                                rope_base=c["rope_base"], yarn_factor=c["yarn_factor"],
+                                yarn_orig_len=c["yarn_orig_len"], yarn_beta_slow=c["yarn_beta_slow"],
+                                yarn_beta_fast=c["yarn_beta_fast"])
+        got = O.rope_freqs(d)[c["pair"]]
+        assert abs(got - c["theta_blended"]) <= 1e-8 * c["theta_blended"], (c["name"], got, c["theta_blended"])
+
+
 def pin_prefill_decode_agree(dims=TINY, L=24, steps=5):
     """P9: a prefill of L followed by decode steps equals one longer prefill."""
     W = _weights(dims, 23)
@@ -310,7 +328,8 @@ def pin_brute_force(dims=SMALL, L=4):
 
 ALL_PINS = [pin_absorbed_equals_plain, pin_softmax_rows, pin_causal, pin_single_key,
             pin_zero_query, pin_head_isolation, pin_mha_special_case, pin_rope_rotation, pin_rope_in_scores,
-            pin_yarn_frequencies, pin_yarn_in_scores, pin_prefill_decode_agree, pin_brute_force]
+            pin_yarn_frequencies, pin_yarn_in_scores, pin_yarn_blend_hand_worked, pin_prefill_decode_agree,
+            pin_brute_force]
 
 
 # ---------------------------------------------------------------------------

@@ -37,6 +37,21 @@ def _yarn_ramp_inverted(dims):
     return th * th / got if O.yarn_on(dims) else got
 
 
+def _yarn_ramp_in_index(dims):
+    # the blend weight linear in the pair index k between the (real-valued)
+    # pairs that turn beta_fast and beta_slow times, instead of linear in r_k
+    if not O.yarn_on(dims):
+        return _freqs(dims)
+    d_r = dims.d_rope
+    k = np.arange(d_r // 2, dtype=np.float64)
+    theta = np.power(float(dims.rope_base), -2.0 * k / d_r)
+    L = float(dims.yarn_orig_len)
+    k_at = lambda r: (d_r / 2.0) * np.log(L / (2.0 * np.pi * r)) / np.log(float(dims.rope_base))
+    k_fast, k_slow = k_at(float(dims.yarn_beta_fast)), k_at(float(dims.yarn_beta_slow))
+    gamma = np.clip((k_slow - k) / (k_slow - k_fast), 0.0, 1.0)
+    return (1.0 - gamma) * theta / float(dims.yarn_factor) + gamma * theta
+
+
 def _yarn_no_temperature(dims):
     return 1.0 / np.sqrt(dims.d_nope + dims.d_rope)
 
@@ -140,6 +155,7 @@ MUTATIONS = {
     "output_head_order": ("output_projection", _out_head_order),
     "k_no_rope": ("compress_kv", _ckv_kr_unroped),
     "yarn_ramp_inverted": ("rope_freqs", _yarn_ramp_inverted),
+    "yarn_ramp_in_index": ("rope_freqs", _yarn_ramp_in_index),
     "yarn_no_interpolation": ("rope_freqs", lambda d: _freqs(dataclasses.replace(d, yarn_factor=1.0))),
     "yarn_no_temperature": ("softmax_scale", _yarn_no_temperature),
     "yarn_temperature_unsquared": ("softmax_scale", _yarn_temperature_unsquared),
