@@ -112,8 +112,34 @@ def kernel_times(run, steps):
     return {k: {"avg_ms": ms / max(n, 1), "launches_per_step": n / steps} for k, (ms, n) in t.items()}
 
 
+def event_times(run, calls):
+    """Per-call durations (ms) from torch events on the current stream (every
+    kernel of a call is launched on that stream)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for i in range(calls):
+        ev[i][0].record()
+        run(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def spread(ms):
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"ms_median": round(float(np.median(a)), 5), "ms_p10": round(float(np.percentile(a, 10)), 5),
+            "ms_p90": round(float(np.percentile(a, 90)), 5), "calls": int(a.size)}
+
+
+def event_kernels(ktimes):
+    return {k: {"avg_us_event_timed": round(v["avg_ms"] * 1e3, 2), "launches_per_step": v["launches_per_step"]}
+            for k, v in ktimes.items()}
+
+
 def run_prefill(args, dev):
-    """Causal prefill of the DeepSeek-V3 layer, batch 1 x 4096 tokens, bf16."""
+    """Causal prefill of the DeepSeek-V3 layer, batch 1 x 4096 tokens, bf16:
+    per-call event times of at least 20 calls (median, p10, p90)."""
     import torch
     from head_latent_attention_18_amd.layer import MlaLayer, upload
     from mla_inputs import make_workload
@@ -124,19 +150,101 @@ def run_prefill(args, dev):
     for _ in range(3):
         lp.prefill(hp, cp)
     torch.cuda.synchronize()
-    pk = max(3, args.steps // 5)
-    t0 = time.perf_counter()
-    for _ in range(pk):
-        lp.prefill(hp, cp)
-    torch.cuda.synchronize()
-    pdt = (time.perf_counter() - t0) / pk
+    pk = max(20, args.steps // 10)
+    st = spread(event_times(lambda i: lp.prefill(hp, cp), pk))
+    pdt = st["ms_median"] * 1e-3
     pk_times = kernel_times(lambda i: lp.prefill(hp, cp), pk)
     fl = prefill_flops(wp.dims, wp.batch, wp.seq_len)
-    log(f"prefill: {pdt * 1e3:.3f} ms, {fl / pdt / 1e12:.1f} TFLOPS")
-    return {"workload": wp.name, "ms": round(pdt * 1e3, 4), "TFLOPS": round(fl / pdt / 1e12, 1),
+    log(f"prefill: median {pdt * 1e3:.3f} ms (p10 {st['ms_p10']:.3f}, p90 {st['ms_p90']:.3f}), "
+        f"{fl / pdt / 1e12:.1f} TFLOPS")
+    return {"workload": wp.name, "ms": st["ms_median"], **st, "TFLOPS": round(fl / pdt / 1e12, 1),
             "mfma_frac": round(fl / pdt / 1e12 / BF16_PEAK_TFLOPS, 4), "alg_flops": fl,
-            "kernels": {k: {"avg_us": round(v["avg_ms"] * 1e3, 2), "launches_per_step": v["launches_per_step"]}
-                        for k, v in pk_times.items()}}
+            "kernels": event_kernels(pk_times)}
+
+
+def decode_attn_flops(d, lens, n_q):
+    """Absorbed attention flops: 2*(d_c + d_R) for the score and 2*d_c for
+    P.V per (query, visible key, head)."""
+    import numpy as np
+    L = np.asarray(lens, dtype=np.int64)
+    vis = int(np.sum(n_q * (L - n_q) + n_q * (n_q + 1) // 2))
+    return vis * d.n_heads * 2 * ((d.d_c + d.d_rope) + d.d_c)
+
+
+def run_decode_workload(args, dev, wid):
+    """Decode step of workload 4 (batch 128, lengths U{1..32768}, paged
+    64-row blocks in a permuted order) or 5 (batch 4, 128K cache, two query
+    tokens).  Lengths, block order, weights and h come from the workload's
+    seed; the cached rows (2.5 GB and 0.6 GB) are drawn N(0,1) on the device
+    from a seeded torch generator and rounded to bf16."""
+    import numpy as np
+    import torch
+    from head_latent_attention_18_amd import libmla as L
+    from head_latent_attention_18_amd.layer import CacheBuf, MlaLayer, upload
+    from mla_inputs import make_workload
+    t0 = time.perf_counter()
+    wl = make_workload(wid, cache_rows=False)
+    d = wl.dims
+    B, nq = wl.batch, wl.n_q
+    lens_np = wl.lens.astype(np.int32)
+    layer = MlaLayer.from_host(d, "bf16", wl.weights_f32, wl.weights_bits)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 + wid)
+    if wl.paged:
+        bs = wl.block_size
+        nblk = int(sum((int(l) + bs - 1) // bs for l in lens_np))
+        maxb = int(max((int(l) + bs - 1) // bs for l in lens_np))
+        table = np.full((B, maxb), -1, dtype=np.int32)
+        off = 0
+        for b in range(B):
+            n = (int(lens_np[b]) + bs - 1) // bs
+            table[b, :n] = wl.block_perm[off:off + n]
+            off += n
+        pool = torch.empty(nblk * bs, d.d_row, dtype=torch.float32, device=dev).normal_(generator=gen)
+        cache = CacheBuf.paged(pool.to(torch.bfloat16), bs, table)
+        del pool
+    else:
+        ml = int(lens_np.max())
+        pool = torch.empty(B * ml, d.d_row, dtype=torch.float32, device=dev).normal_(generator=gen)
+        cache = CacheBuf(pool.to(torch.bfloat16), None, max_len=ml)
+        cache.desc = L.make_cache(cache.pool, max_len=ml)
+        del pool
+    h = upload(wl.h_f32, wl.h_bits, True)
+    lens = torch.from_numpy(lens_np).to(dev)
+    Lmax = int(lens_np.max())
+    u = torch.empty(B, nq, d.d_model, dtype=torch.bfloat16, device=dev)
+    run = lambda i: layer.decode(h, lens, Lmax, cache, u=u, lens_host=lens_np)
+    torch.cuda.synchronize()
+    log(f"workload {wl.name}: set up in {time.perf_counter() - t0:.1f}s, sum of lengths {int(lens_np.sum())}")
+    for i in range(5):
+        run(i)
+    torch.cuda.synchronize()
+    k = max(20, args.steps // 10)
+    st = spread(event_times(run, k))
+    dt = st["ms_median"] * 1e-3
+    kt = kernel_times(run, k)
+    sum_len = int(lens_np.sum())
+    step_bytes = decode_step_bytes(d, B, nq, sum_len)
+    kb = decode_kernel_bytes(d, B, nq, sum_len)["decode_attn"]
+    attn_fl = decode_attn_flops(d, lens_np, nq)
+    attn_ms = kt["decode_attn"]["avg_ms"]
+    t_hbm = kb / (HBM_PEAK_GBS * 1e9)
+    t_mfma = attn_fl / (BF16_PEAK_TFLOPS * 1e12)
+    bound = "mfma" if t_mfma > t_hbm else "hbm"
+    log(f"{wl.name}: median {dt * 1e6:.1f} us/step, attention {attn_ms * 1e3:.1f} us (event-timed), "
+        f"bound {bound} {max(t_hbm, t_mfma) * 1e6:.1f} us")
+    del cache, layer
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "batch": B, "n_q": nq, "sum_len": sum_len, "max_len": Lmax, "paged": wl.paged,
+            **st, "tokens_per_s": round(B * nq / dt, 1),
+            "step_hbm": {"alg_bytes": step_bytes, "GBps": round(step_bytes / dt / 1e9, 1),
+                         "frac": round(step_bytes / dt / 1e9 / HBM_PEAK_GBS, 4)},
+            "attention": {"alg_bytes": kb, "alg_flops": attn_fl, "us_event_timed": round(attn_ms * 1e3, 2),
+                          "hbm_frac": round(kb / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "mfma_frac": round(attn_fl / (attn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                          "bound": bound, "bound_us": round(max(t_hbm, t_mfma) * 1e6, 2),
+                          "frac_of_bound": round(max(t_hbm, t_mfma) / (attn_ms * 1e-3), 4)},
+            "kernels": event_kernels(kt)}
 
 
 def chunk_flops(d, C, P):
@@ -190,9 +298,10 @@ def main():
     ap.add_argument("--sets", type=int, default=3, help="rotated input copies (defeat the Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the ragged and 128K decode workloads")
     ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the oracle's first (parity) pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="least CPU time of the timed oracle sample")
-    ap.add_argument("--only", choices=["all", "decode", "prefill", "chunk"], default="all",
+    ap.add_argument("--only", choices=["all", "decode", "prefill", "chunk", "ragged", "long"], default="all",
                     help="profiling runs: time one path only (the JSON line is printed for 'all' and 'decode')")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only copy a buffer of this many MB three times (scale for HBM byte counters)")
@@ -227,6 +336,9 @@ def main():
     if args.only == "chunk":
         print(json.dumps(run_chunk(args, dev)), flush=True)
         return
+    if args.only in ("ragged", "long"):
+        print(json.dumps(run_decode_workload(args, dev, 4 if args.only == "ragged" else 5)), flush=True)
+        return
 
     # ------------------------------------------------------------ decode
     t0 = time.perf_counter()
@@ -238,7 +350,8 @@ def main():
     layer0 = MlaLayer.from_host(d, "bf16", wl.weights_f32, wl.weights_bits)
     cache0 = cache_from_rows(wl.cache_bits, wl.lens, d.d_row, True)
     h0 = upload(wl.h_f32, wl.h_bits, True)
-    lens = torch.from_numpy(wl.lens.astype(np.int32)).to(dev)
+    lens_np = wl.lens.astype(np.int32)
+    lens = torch.from_numpy(lens_np).to(dev)
     sets = [(layer0, cache0, h0)]
     for _ in range(args.sets - 1):
         lw = MlaLayer(d, "bf16", {k: v.clone() for k, v in layer0.weights.items()})
@@ -249,7 +362,7 @@ def main():
 
     def step(i):
         lw, c, h = sets[i % len(sets)]
-        lw.decode(h, lens, Lmax, c, u=outs[i % len(sets)])
+        lw.decode(h, lens, Lmax, c, u=outs[i % len(sets)], lens_host=lens_np)
 
     for i in range(args.warmup):
         step(i)
@@ -322,6 +435,10 @@ def main():
     torch.cuda.empty_cache()
 
     prefill = None if (args.no_prefill or args.only == "decode") else run_prefill(args, dev)
+    ragged = long_ctx = None
+    if args.only == "all" and not args.no_extra:
+        ragged = run_decode_workload(args, dev, 4)
+        long_ctx = run_decode_workload(args, dev, 5)
 
     out = {
         "metric": "MLA decode tokens/s (DeepSeek-V3 layer, batch 32, cache 4096)",
@@ -344,8 +461,12 @@ def main():
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom),
                      "alg_bytes": kbytes[dom]},
         "kernels": kernels,
+        "kernel_timing": "HIP events recorded around each launch on its stream (about 2 us per launch above the "
+                         "kernel's own duration; rocprofv3 kernel traces under profiles/ give the durations alone)",
         "parity": parity,
         "prefill": prefill,
+        "decode_ragged": ragged,
+        "decode_long": long_ctx,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

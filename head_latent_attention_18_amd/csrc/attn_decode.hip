@@ -27,23 +27,163 @@
 
 namespace mla {
 
-// Block -> work item (unit = (sequence, split), row group).  Items in unit
-// order, a contiguous eighth of them per XCD (blocks x, x+8, x+16, .. run on
-// XCD x): with eight units or more the row groups of a unit and the splits of
-// a sequence share an XCD, whose L2 serves their common reads (queries, cache
-// tiles); with fewer units (one long sequence, many query rows) the row
-// groups still spread over all eight XCDs.
-__device__ inline bool decode_item(const DecodeArgs &a, int &unit, int &rg) {
-  const int W = a.B * a.n_splits * a.row_groups, per = (W + 7) / 8;
+constexpr int KVT = 32;  // cache rows per tile (two 16-row MFMA blocks)
+
+// Block -> work item (w, row group), w-major, a contiguous eighth of the
+// items per XCD (blocks x, x+8, x+16, .. run on XCD x): the row groups of a
+// range of tiles, and the neighbouring ranges (the rest of the same
+// sequence), share an XCD, whose L2 serves their common reads (cache tiles,
+// queries).
+__device__ inline bool decode_item(const DecodeArgs &a, int &w, int &rg) {
+  const int n = a.W * a.row_groups, per = (n + 7) / 8;
   const int slot = blockIdx.x >> 3, item = (blockIdx.x & 7) * per + slot;
-  if (slot >= per || item >= W) return false;
-  unit = item / a.row_groups;
-  rg = item - unit * a.row_groups;
+  if (slot >= per || item >= n) return false;
+  w = item / a.row_groups;
+  rg = item - w * a.row_groups;
   return true;
 }
-inline int decode_grid(const DecodeArgs &a) { return 8 * ((a.B * a.n_splits * a.row_groups + 7) / 8); }
+inline int decode_grid(const DecodeArgs &a) { return 8 * ((a.W * a.row_groups + 7) / 8); }
 
-constexpr int KVT = 32;  // cache rows per tile (two 16-row MFMA blocks)
+// ---------------------------------------------------------------------------
+// Split plan (DecodeArgs): the cached rows of every sequence, in KVT-row
+// tiles, end to end in sequence order; workgroup w of a row group takes
+// tiles [w*P, (w+1)*P) with P = ceil(total / W), i.e. the rows are divided
+// over the compute units in proportion to each sequence's length.  Every
+// wave computes the plan from the lengths with wave-wide scans, so the
+// results are wave-uniform and identical in every kernel that needs them.
+// ---------------------------------------------------------------------------
+// cache rows of sequence b the plan covers: its length, clamped to the cache
+__device__ inline int plan_len(const DecodeArgs &a, int b) {
+  return (int)max(0L, min((long)a.lens[b], a.cache.cap));
+}
+__device__ inline int plan_tiles(int len) { return (len + KVT - 1) / KVT; }
+
+__device__ inline int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ inline int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// total tiles over all sequences, and tiles per workgroup
+__device__ inline void plan_totals(const DecodeArgs &a, int &total, int &P) {
+  const int lane = threadIdx.x & 63;
+  int sum = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64)
+    sum += b0 + lane < a.B ? plan_tiles(plan_len(a, b0 + lane)) : 0;
+  total = __builtin_amdgcn_readfirstlane(wave_sum_i(sum));
+  P = (total + a.W - 1) / a.W;
+}
+
+struct SeqSpan { int b, t0, tiles, len; };   // sequence, its first tile, its tiles, its rows
+
+// The sequence holding global tile g (g < total), or {B, total, 0, 0}.
+__device__ inline SeqSpan plan_locate(const DecodeArgs &a, int g) {
+  const int lane = threadIdx.x & 63;
+  int carry = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const bool in = b0 + lane < a.B;
+    const int len = in ? plan_len(a, b0 + lane) : 0, t = plan_tiles(len);
+    const int incl = wave_incl_scan(t) + carry;
+    const unsigned long long m = __ballot(in && incl > g);
+    if (m) {
+      const int l = __builtin_ctzll(m);
+      const int tl = __shfl(t, l);
+      return SeqSpan{b0 + l, __shfl(incl, l) - tl, tl, __shfl(len, l)};
+    }
+    carry = __shfl(incl, 63);
+  }
+  return SeqSpan{a.B, carry, 0, 0};
+}
+
+// The span of sequence b (0 <= b < B).
+__device__ inline SeqSpan plan_seq(const DecodeArgs &a, int b) {
+  const int lane = threadIdx.x & 63;
+  int carry = 0;
+  for (int b0 = 0;; b0 += 64) {
+    const bool in = b0 + lane < a.B;
+    const int len = in ? plan_len(a, b0 + lane) : 0, t = plan_tiles(len);
+    const int incl = wave_incl_scan(t) + carry;
+    if (b < b0 + 64) {
+      const int l = b - b0, tl = __shfl(t, l);
+      return SeqSpan{b, __shfl(incl, l) - tl, tl, __shfl(len, l)};
+    }
+    carry = __shfl(incl, 63);
+  }
+}
+
+// Partial slots of sequence sp: the first, and how many (workgroups
+// sp.t0/P .. (sp.t0 + tiles - 1)/P hold its tiles).
+__device__ inline void plan_slots(const SeqSpan &sp, int P, int &slot0, int &n) {
+  if (sp.tiles <= 0 || P <= 0) { slot0 = sp.b; n = 0; return; }
+  const int w0 = sp.t0 / P, w1 = (sp.t0 + sp.tiles - 1) / P;
+  slot0 = w0 + sp.b;
+  n = w1 - w0 + 1;
+}
+
+// The spans of N sequences bs[] (0 <= bs[j] < B) and the total tiles, in
+// one pass over the lengths.
+template <int N>
+__device__ inline void plan_spans(const DecodeArgs &a, const int (&bs)[N], SeqSpan (&sp)[N], int &total) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < N; ++j) sp[j] = SeqSpan{bs[j], 0, 0, 0};
+  int carry = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const bool in = b0 + lane < a.B;
+    const int len = in ? plan_len(a, b0 + lane) : 0, t = plan_tiles(len);
+    const int incl = wave_incl_scan(t) + carry;
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+      if (bs[j] >= b0 && bs[j] < b0 + 64) {
+        const int l = bs[j] - b0, tl = __shfl(t, l);
+        sp[j] = SeqSpan{bs[j], __shfl(incl, l) - tl, tl, __shfl(len, l)};
+      }
+    carry = __shfl(incl, 63);
+  }
+  total = carry;
+}
+
+// Run seg(b, len, kv_beg, kv_end, slot) for each part of a sequence that
+// workgroup w holds, in order (kv_beg < kv_end <= len).
+template <typename F>
+__device__ inline void for_each_segment(const DecodeArgs &a, int w, F &&seg) {
+  int total, P;
+  plan_totals(a, total, P);
+  int g = w * P;
+  const int g_end = min(g + P, total);
+  while (g < g_end) {
+    const SeqSpan sp = plan_locate(a, g);
+    if (sp.b >= a.B) break;
+    const int end = __builtin_amdgcn_readfirstlane(min(g_end, sp.t0 + sp.tiles));
+    const int kv_beg = (g - sp.t0) * KVT, kv_end = min(sp.len, (end - sp.t0) * KVT);
+    // wave-uniform values the compiler cannot prove uniform (they come out
+    // of cross-lane operations): put them in scalar registers
+    if (kv_beg < kv_end)
+      seg(__builtin_amdgcn_readfirstlane(sp.b), __builtin_amdgcn_readfirstlane(sp.len),
+          __builtin_amdgcn_readfirstlane(kv_beg), __builtin_amdgcn_readfirstlane(kv_end),
+          __builtin_amdgcn_readfirstlane(w + sp.b));
+    g = end;
+  }
+}
+
+// Lane and wave indices, formed afresh for each part a workgroup processes:
+// the opaque copy of threadIdx.x keeps the compiler from hoisting every
+// lane-dependent address out of the loop over parts, which would hold them
+// in registers across the whole kernel (and spill).
+#define LANE_IDS_PER_PART                                                      \
+  int tid = threadIdx.x;                                                       \
+  asm volatile("" : "+v"(tid));                                                \
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  \
+  const int lrow = lane & 15, lgrp = lane >> 4
 
 template <typename T, int NW, int HB, int DC, int DR>
 __global__ __launch_bounds__(64 * NW, 1) void decode_attn_kernel(DecodeArgs a) {
@@ -73,15 +213,12 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 15, lgrp = lane >> 4;
 
-  // block -> (unit = (b, s), row group)
-  int unit, rg;
-  if (!decode_item(a, unit, rg)) return;
-  const int b = unit / a.n_splits, s = unit % a.n_splits;
-  // lengths beyond the plan or the cache are clamped, so no read leaves the cache
-  const int len = (int)min((long)a.lens[b], min((long)a.n_splits * a.chunk, a.cache.cap));
-  const int kv_beg = s * a.chunk;
-  if (kv_beg >= len) return;
-  const int kv_end = min(len, kv_beg + a.chunk);
+  int w_item, rg;
+  if (!decode_item(a, w_item, rg)) return;
+  bool first_seg = true;
+  for_each_segment(a, w_item, [&](const int b, const int len, const int kv_beg, const int kv_end, const int slot) {
+  if (!first_seg) __syncthreads();   // the previous part's LDS reads are done
+  first_seg = false;
   const int R = a.n_q * a.n_h;
   const int row0 = rg * ROWS + wave * 16 * HB;
   const float sl2 = a.scale_log2;
@@ -255,7 +392,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_kernel(DecodeArgs a) {
     const int r = row0 + hb * 16 + lrow;
     if (r < R) {
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      const long pbase = ((long)b * a.n_splits + s) * R + r;
+      const long pbase = (long)slot * R + r;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const f32x4 o4 = oacc[db][hb] * inv;
@@ -265,6 +402,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_kernel(DecodeArgs a) {
       if (lgrp == 0) a.lse_part[pbase] = l > 0.f ? mrun[hb] + log2f(l) : -INFINITY;
     }
   }
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -367,15 +505,18 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 stages[NS * STAGE];
   __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2 * 4 * ROWS];   // P[buf][g][row]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lrow = lane & 15, lgrp = lane >> 4;
-  int unit, rg;
-  if (!decode_item(a, unit, rg)) return;
-  const int b = unit / a.n_splits, s = unit % a.n_splits;
-  const int len = (int)min((long)a.lens[b], min((long)a.n_splits * a.chunk, a.cache.cap));
-  const int kv_beg = s * a.chunk;
-  if (kv_beg >= len) return;
-  const int kv_end = min(len, kv_beg + a.chunk);
+  int w_item, rg;
+  if (!decode_item(a, w_item, rg)) return;
+  bool first_seg = true;
+  for_each_segment(a, w_item, [&](const int b, const int len, const int kv_beg, const int kv_end, const int slot) {
+  LANE_IDS_PER_PART;
+  if (!first_seg) {
+    // the previous part's partial stores have left and every wave is done
+    // with the stages it staged them in
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  first_seg = false;
   const int R = a.n_q * a.n_h;
   const int rbase = rg * ROWS;
   const float sl2 = a.scale_log2;
@@ -603,7 +744,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
     if (lgrp == 0) {
       fac[rl] = l > 0.f ? 1.f / l : 0.f;
       if (rbase + rl < R)
-        a.lse_part[((long)b * a.n_splits + s) * R + rbase + rl] =
+        a.lse_part[(long)slot * R + rbase + rl] =
             ovf ? __builtin_nanf("") : l > 0.f ? mref[ha] + log2f(l) : -INFINITY;
     }
   }
@@ -627,9 +768,10 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  bf16 *op = (bf16 *)a.o_part + (((long)b * a.n_splits + s) * R + rbase) * DC + lane * 8;
+  bf16 *op = (bf16 *)a.o_part + ((long)slot * R + rbase) * DC + lane * 8;
   for (int rl = wave; rl < ROWS && rbase + rl < R; rl += NW)
     *(bf16x8 *)(op + (long)rl * DC) = *(const lds_bf16x8 *)(ot + rl * DC + (lane ^ (rl & 15)) * 8);
+  });
 }
 
 // Two waves per SIMD: 64 query rows, 8 waves.  With one wave per SIMD the
@@ -668,16 +810,19 @@ __global__ __launch_bounds__(512, 1) void decode_attn_dma8_kernel(DecodeArgs a) 
   __shared__ float xch[2][ROWS];                                       // per key half: row max, then row sum
   __shared__ int xov[2][ROWS];                                         // per key half: row overflowed
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lrow = lane & 15, lgrp = lane >> 4;
+  int w_item, rg;
+  if (!decode_item(a, w_item, rg)) return;
+  bool first_seg = true;
+  for_each_segment(a, w_item, [&](const int b, const int len, const int kv_beg, const int kv_end, const int slot) {
+  LANE_IDS_PER_PART;
   const int rw = wave & 3, kh = wave >> 2;          // score roles: row block, key half
-  int unit, rg;
-  if (!decode_item(a, unit, rg)) return;
-  const int b = unit / a.n_splits, s = unit % a.n_splits;
-  const int len = (int)min((long)a.lens[b], min((long)a.n_splits * a.chunk, a.cache.cap));
-  const int kv_beg = s * a.chunk;
-  if (kv_beg >= len) return;
-  const int kv_end = min(len, kv_beg + a.chunk);
+  if (!first_seg) {
+    // the previous part's partial stores have left and every wave is done
+    // with the stages it staged them in
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  first_seg = false;
   const int R = a.n_q * a.n_h;
   const int rbase = rg * ROWS;
   const float sl2 = a.scale_log2;
@@ -880,7 +1025,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_dma8_kernel(DecodeArgs a) 
     const bool ov = (xov[0][rl] | xov[1][rl]) != 0;
     fac[rl] = l > 0.f ? 1.f / l : 0.f;
     if (rbase + rl < R)
-      a.lse_part[((long)b * a.n_splits + s) * R + rbase + rl] =
+      a.lse_part[(long)slot * R + rbase + rl] =
           ov ? __builtin_nanf("") : l > 0.f ? mref + log2f(l) : -INFINITY;
   }
   __syncthreads();
@@ -900,12 +1045,13 @@ __global__ __launch_bounds__(512, 1) void decode_attn_dma8_kernel(DecodeArgs a) 
     }
   }
   __syncthreads();
-  bf16 *op = (bf16 *)a.o_part + (((long)b * a.n_splits + s) * R + rbase) * DC + lane * 8;
+  bf16 *op = (bf16 *)a.o_part + ((long)slot * R + rbase) * DC + lane * 8;
   // streaming stores: the partials are read once, by the combine, from
   // other XCDs (47.1 -> 45.2 us against write-allocating stores)
   for (int rl = wave; rl < ROWS && rbase + rl < R; rl += NW)
     __builtin_nontemporal_store(*(const lds_bf16x8 *)(ot + rl * DC + (lane ^ (rl & 15)) * 8),
                                 (bf16x8 *)(op + (long)rl * DC));
+  });
 }
 
 // Exact attention of one query row over its whole sequence, straight from the
@@ -966,9 +1112,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= (long)a.B * R) return;
   const int b = (int)(row / R), r = (int)(row % R);
-  const int len = (int)min((long)a.lens[b], min((long)a.n_splits * a.chunk, a.cache.cap));
-  const int nsp = len > 0 ? min(a.n_splits, (len + a.chunk - 1) / a.chunk) : 0;
-  const long base = (long)b * a.n_splits * R + r;
+  int total, P, slot0, nsp;
+  plan_totals(a, total, P);
+  const SeqSpan sp = plan_seq(a, b);
+  plan_slots(sp, P, slot0, nsp);
+  const int len = sp.len;
+  const long base = (long)slot0 * R + r;
   T *out = (T *)a.o_lat + row * DC;
   // split weights: lane s holds split s (for up to 64 splits; more are
   // read in rounds)
@@ -1073,28 +1222,36 @@ __global__ __launch_bounds__(256, 1) void decode_combine_uv_kernel(DecodeArgs a,
   long base[TW];
 #pragma unroll
   for (int j = 0; j < TW; ++j) {
-    const int t = tg * TT + wave * TW + j;
-    bq[j] = 0; rq[j] = 0; lq[j] = 0; nsp[j] = 0; base[j] = 0;
-    if (t < T) {
-      bq[j] = t / a.n_q;
-      rq[j] = (t % a.n_q) * a.n_h + h;
-      lq[j] = (int)min((long)a.lens[bq[j]], min((long)a.n_splits * a.chunk, a.cache.cap));
-      nsp[j] = lq[j] > 0 ? min(a.n_splits, (lq[j] + a.chunk - 1) / a.chunk) : 0;
-      base[j] = (long)bq[j] * a.n_splits * R + rq[j];
+    const int t = min(tg * TT + wave * TW + j, T - 1);
+    bq[j] = t / a.n_q;
+    rq[j] = (t % a.n_q) * a.n_h + h;
+  }
+  {
+    SeqSpan sp[TW];
+    int total;
+    plan_spans<TW>(a, bq, sp, total);
+    const int P = (total + a.W - 1) / a.W;
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+      int slot0;
+      plan_slots(sp[j], P, slot0, nsp[j]);
+      if (tg * TT + wave * TW + j >= T) nsp[j] = 0;
+      lq[j] = sp[j].len;
+      base[j] = (long)slot0 * R + rq[j];
     }
   }
-  // addresses from the plan only (not from the lengths), so these loads do
-  // not wait for the length loads; splits past a sequence's end are masked
+  // the log-sum-exps (lane s: split s) and the first SB partial rows of each
+  // token are requested before any is used; splits past a sequence's own
+  // count are masked (loads clamped to its last split)
   float ls[TW];
   bf16x8 v[TW][SB];
-  const int lsp = min(lane, a.n_splits - 1);
 #pragma unroll
-  for (int j = 0; j < TW; ++j) ls[j] = a.lse_part[base[j] + (long)lsp * R];
+  for (int j = 0; j < TW; ++j) ls[j] = a.lse_part[base[j] + (long)min(lane, max(nsp[j] - 1, 0)) * R];
 #pragma unroll
   for (int j = 0; j < TW; ++j)
 #pragma unroll
     for (int jj = 0; jj < SB; ++jj) {
-      const int sp = min(jj, a.n_splits - 1);
+      const int sp = min(jj, max(nsp[j] - 1, 0));
       v[j][jj] = *(const bf16x8 *)((const bf16 *)a.o_part + (base[j] + (long)sp * R) * DC + lane * PER);
     }
 #pragma unroll
@@ -1122,16 +1279,23 @@ __global__ __launch_bounds__(256, 1) void decode_combine_uv_kernel(DecodeArgs a,
         float wsum = 0.f;
 #pragma unroll
         for (int jj = 0; jj < SB; ++jj) {
+          // splits at or past the sequence's own count were not written by
+          // this call (their rows hold whatever the workspace held, possibly
+          // NaN bits), so they are skipped, not weighted by zero; the
+          // condition is wave-uniform
           const float lsj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[j]), jj));
-          const float w = (jj < nsp[j] && lsj != -INFINITY) ? exp2f(lsj - lmax) : 0.f;
-          wsum += w;
+          if (jj < nsp[j] && lsj != -INFINITY) {
+            const float w = exp2f(lsj - lmax);
+            wsum += w;
 #pragma unroll
-          for (int i = 0; i < PER; ++i) res[i] += w * (float)v[j][jj][i];
+            for (int i = 0; i < PER; ++i) res[i] += w * (float)v[j][jj][i];
+          }
         }
         for (int sp = SB; sp < nsp[j]; ++sp) {
           const float lsj = a.lse_part[base[j] + (long)sp * R];
+          if (lsj == -INFINITY) continue;
           const bf16x8 vv = *(const bf16x8 *)((const bf16 *)a.o_part + (base[j] + (long)sp * R) * DC + lane * PER);
-          const float w = lsj != -INFINITY ? exp2f(lsj - lmax) : 0.f;
+          const float w = exp2f(lsj - lmax);
           wsum += w;
 #pragma unroll
           for (int i = 0; i < PER; ++i) res[i] += w * (float)vv[i];
@@ -1185,14 +1349,10 @@ hipError_t launch_decode_combine_uv(const DecodeArgs &a, int d_v, const void *w_
 }
 
 int decode_kv_tile(int) { return KVT; }
-// Query rows per workgroup.  bf16 takes 128 (a quarter per wave), or 64 when
-// every sequence still gets at least four splits from one wave of workgroups
-// over the CUs: halving the partial results written per split, and the
-// combine's reads of them, then outweighs the second read of each cache tile
-// (an L2 hit) by the other row group.
+// Query rows per workgroup: 64 (the two-waves-per-SIMD kernel for bf16).
 int decode_rows_per_group(int dtype, long B, long R, int cus) {
-  if (dtype != 1) return 64;
-  return (R <= 64 || (R <= 128 && B * 2 * 4 <= cus)) ? 64 : 128;
+  (void)dtype; (void)B; (void)R; (void)cus;
+  return 64;
 }
 
 template <typename T, int NW, int HB, int DC, int DR>

@@ -161,28 +161,25 @@ SplitK choose_splitk(int dtype, int64_t M, int64_t N, int64_t K, int batch) {
 }
 
 struct DecodePlan {
-  int splits, chunk, row_groups, rows;
+  int W, slots, row_groups, rows;
   SplitK sk1, sk2, sk5;
   size_t c_q, q_nope, q_abs, o_part, lse, o_lat, o, partial, total;
 };
+// The attention's split plan: W workgroups per row group (one wave of
+// workgroups over the CUs), each taking an equal share of the batch's cached
+// tiles (computed on the device from the lengths), and at most W + B partial
+// slots; neither depends on the lengths, so the workspace size does not.
 DecodePlan plan_decode(const mla_config *c, int32_t B, int32_t n_q, int32_t max_len) {
   DecodePlan p;
   const int dt = c->dtype;
   const int64_t T = (int64_t)B * n_q;
   const int64_t R = (int64_t)n_q * c->n_heads;
   const int rows = decode_rows_per_group(dt == MLA_BF16 ? 1 : 0, B, R, kCUs);
-  const int kvt = decode_kv_tile(dt);
   p.rows = rows;
   p.row_groups = (int)((R + rows - 1) / rows);
-  const int64_t per_seq_units = (int64_t)B * p.row_groups;
-  int64_t s = (kCUs + per_seq_units - 1) / per_seq_units;
-  const int64_t max_tiles = (max_len + kvt - 1) / kvt;
-  if (s > max_tiles) s = max_tiles;
-  if (s < 1) s = 1;
-  int64_t chunk = (max_len + s - 1) / s;
-  chunk = ((chunk + kvt - 1) / kvt) * kvt;
-  p.chunk = (int)chunk;
-  p.splits = (int)((max_len + chunk - 1) / chunk);
+  p.W = std::max(1, kCUs / p.row_groups);
+  p.slots = p.W + B;
+  (void)max_len;
   const int64_t N1 = c->d_cq + c->d_c + c->d_rope;
   p.sk1 = choose_splitk(dt, T, N1, c->d_model, 1);
   p.sk2 = choose_splitk(dt, T, (int64_t)c->n_heads * (c->d_nope + c->d_rope), c->d_cq, 1);
@@ -194,8 +191,8 @@ DecodePlan plan_decode(const mla_config *c, int32_t B, int32_t n_q, int32_t max_
   p.c_q = take((size_t)T * c->d_cq * e);
   p.q_nope = take((size_t)T * c->n_heads * c->d_nope * e);
   p.q_abs = take((size_t)T * c->n_heads * D * e);
-  p.o_part = take((size_t)B * p.splits * R * c->d_c * e);
-  p.lse = take((size_t)B * p.splits * R * 4);
+  p.o_part = take((size_t)p.slots * R * c->d_c * e);
+  p.lse = take((size_t)p.slots * R * 4);
   p.o_lat = take((size_t)T * c->n_heads * c->d_c * e);
   p.o = take((size_t)T * c->n_heads * c->d_v * e);
   size_t part = 0;
@@ -546,13 +543,17 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
 }
 
 mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h, int32_t batch, int32_t n_q,
-                      const int32_t *cache_lens, int32_t max_cache_len, const mla_cache *cache, void *u,
-                      void *o_heads, void *workspace, size_t workspace_bytes, void *stream) {
+                      const int32_t *cache_lens, const int32_t *cache_lens_host, int32_t max_cache_len,
+                      const mla_cache *cache, void *u, void *o_heads, void *workspace, size_t workspace_bytes,
+                      void *stream) {
   mla_status s = check_config(cfg);
   if (s != MLA_OK) return s;
   if ((s = check_weights(w)) != MLA_OK) return s;
   if (!h || !u || !cache_lens) return MLA_ERR_NULL;
   if (batch <= 0 || n_q <= 0 || max_cache_len < n_q) return MLA_ERR_SHAPE;
+  if (cache_lens_host)
+    for (int32_t b = 0; b < batch; ++b)
+      if (cache_lens_host[b] < n_q || cache_lens_host[b] > max_cache_len) return MLA_ERR_SHAPE;
   if ((int64_t)batch * n_q > (1L << 20) || (int64_t)n_q * cfg->n_heads > (1L << 20)) return MLA_ERR_UNSUPPORTED;
   if (!attention_supported(cfg, MLA_OP_DECODE)) return MLA_ERR_UNSUPPORTED;
   if ((s = check_cache(cache, batch, max_cache_len)) != MLA_OK) return s;
@@ -620,8 +621,8 @@ mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h
   d.d_c = cfg->d_c;
   d.d_rope = cfg->d_rope;
   d.scale_log2 = softmax_scale_log2(cfg);
-  d.chunk = p.chunk;
-  d.n_splits = p.splits;
+  d.W = p.W;
+  d.slots = p.slots;
   d.row_groups = p.row_groups;
   d.rows = p.rows;
   d.o_part = ws + p.o_part;

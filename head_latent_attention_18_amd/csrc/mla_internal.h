@@ -360,12 +360,18 @@ struct DecodeArgs {
   const int *lens;    // [B]
   int B, n_q, n_h, d_c, d_rope;
   float scale_log2;   // softmax scale * log2(e)
-  int chunk;          // kv rows per split (multiple of the kv tile)
-  int n_splits;       // splits per sequence in the grid
+  // Split plan.  The cached rows of all sequences, in KV tiles, are laid end
+  // to end in sequence order; each row group's W workgroups take equal
+  // contiguous ranges of ceil(total tiles / W) tiles, so a workgroup may hold
+  // the end of one sequence and the start of the next.  The part of sequence
+  // b that workgroup w holds writes partial slot w + b (unique, and a
+  // sequence's slots are consecutive); slots = W + B bounds them.
+  int W;              // workgroups per row group
+  int slots;          // partial slots: W + B
   int row_groups;     // groups of query rows (n_q*n_h rows per sequence)
   int rows;           // query rows per group (the workgroup's share)
-  void *o_part;       // [B][n_splits][n_q*n_h][d_c], normalised, in the layer's dtype
-  float *lse_part;    // [B][n_splits][n_q*n_h]  (log2 units; NaN = recompute the row)
+  void *o_part;       // [slots][n_q*n_h][d_c], normalised, in the layer's dtype
+  float *lse_part;    // [slots][n_q*n_h]  (log2 units; NaN = recompute the row)
   void *o_lat;        // combine output [B*n_q][n_h][d_c]
 };
 int decode_rows_per_group(int dtype, long B, long R, int cus);

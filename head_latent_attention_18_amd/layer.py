@@ -88,14 +88,15 @@ class MlaLayer:
         return (u, o) if want_o else u
 
     def decode(self, h: torch.Tensor, lens: torch.Tensor, max_len: int, cache: CacheBuf, want_o: bool = False,
-               stream=None, u: Optional[torch.Tensor] = None):
+               stream=None, u: Optional[torch.Tensor] = None, lens_host=None):
         B, nq, _ = h.shape
         if u is None:
             u = torch.empty(B, nq, self.dims.d_model, dtype=self.tdtype, device=h.device)
         o = torch.empty(B * nq, self.dims.n_heads, self.dims.d_v, dtype=self.tdtype, device=h.device) if want_o else None
         nbytes = L.mla_workspace_size(self.cfg, L.MLA_OP_DECODE, B, nq, max_len)
         ws = self.workspace("decode", nbytes, h.device)
-        L.mla_decode(self.cfg, self.cw, h, B, nq, lens, max_len, cache.desc, u, o, ws, ws.numel(), stream)
+        L.mla_decode(self.cfg, self.cw, h, B, nq, lens, max_len, cache.desc, u, o, ws, ws.numel(), stream,
+                     cache_lens_host=lens_host)
         return (u, o) if want_o else u
 
     def compress_kv(self, h: torch.Tensor, seq_idx: torch.Tensor, pos: torch.Tensor, batch: int, cache: CacheBuf,

@@ -67,8 +67,8 @@ def _lib():
         lib.mla_prefill.argtypes = [P(mla_config), P(mla_weights), c_void_p, c_int32, c_int32, P(mla_cache),
                                     c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
         lib.mla_prefill.restype = c_int32
-        lib.mla_decode.argtypes = [P(mla_config), P(mla_weights), c_void_p, c_int32, c_int32, c_void_p, c_int32,
-                                   P(mla_cache), c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        lib.mla_decode.argtypes = [P(mla_config), P(mla_weights), c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                   c_int32, P(mla_cache), c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
         lib.mla_decode.restype = c_int32
         lib.mla_status_string.argtypes = [c_int32]
         lib.mla_status_string.restype = c_char_p
@@ -159,11 +159,23 @@ def mla_prefill(cfg, w: mla_weights, h, batch: int, length: int, cache: mla_cach
                                              workspace_bytes, _stream(stream)))
 
 
+def _host_i32(a):
+    """A host int32 array for a *_host argument: (ctypes pointer, keep-alive
+    object), or (None, None)."""
+    if a is None:
+        return None, None
+    import numpy as np
+    arr = np.ascontiguousarray(a, dtype=np.int32)
+    return arr.ctypes.data_as(c_void_p), arr
+
+
 def mla_decode(cfg, w: mla_weights, h, batch: int, n_q: int, cache_lens, max_cache_len: int, cache: mla_cache,
-               u, o_heads, workspace, workspace_bytes: int, stream=None):
+               u, o_heads, workspace, workspace_bytes: int, stream=None, cache_lens_host=None):
+    lens_host, _keep = _host_i32(cache_lens_host)
     _check("mla_decode", _lib().mla_decode(ctypes.byref(cfg), ctypes.byref(w), _ptr(h), batch, n_q,
-                                           _ptr(cache_lens), max_cache_len, ctypes.byref(cache), _ptr(u),
-                                           _ptr(o_heads), _ptr(workspace), workspace_bytes, _stream(stream)))
+                                           _ptr(cache_lens), lens_host, max_cache_len, ctypes.byref(cache),
+                                           _ptr(u), _ptr(o_heads), _ptr(workspace), workspace_bytes,
+                                           _stream(stream)))
 
 
 def mla_status_string(code: int) -> str:

@@ -122,9 +122,12 @@ typedef struct mla_cache {
   int32_t max_len;             /* contiguous: rows per sequence; paged: ignored */
 } mla_cache;
 
-/* Elements cached per token and layer, times the dtype size:
- * (d_c + d_rope) * sizeof(dtype).  1152 bytes for DeepSeek-V3 in BF16.
- * Returns 0 for an invalid config. */
+/* Bytes one cached token occupies per layer.  The DeepSeek-V3 paper-reading
+ * notes (hk.pswp.cn), section 2.1, "advantages of MLA": inference caches only
+ * the latent c_KV and the decoupled key k_R, so a row is (d_c + d_rope)
+ * elements of the cache's element type: 1152 bytes for DeepSeek-V3 in BF16
+ * (against 2 * n_heads * d_nope elements for standard multi-head attention,
+ * mla_mha_cache_elements_per_token).  Returns 0 for an invalid config. */
 size_t mla_cache_bytes_per_token(const mla_config *cfg);
 
 /* Elements a standard multi-head attention would cache per token:
@@ -165,21 +168,36 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
                        int32_t batch, int32_t len, const mla_cache *cache, void *u,
                        void *o_heads, void *workspace, size_t workspace_bytes, void *stream);
 
-/* Decode `n_q` new tokens per sequence against the latent cache.
+/* Decode `n_q` new tokens per sequence against the latent cache: the
+ * decoding phase of the split prefill/decode serving in the DeepSeek V3
+ * paper-reading notes (hk.pswp.cn), section 5 "Inference and Deployment",
+ * computing the equations of section 2.1 ("Key and Value compression",
+ * "Query compression", "attention computation") for the new tokens, with
+ * the keys and values of earlier tokens taken from their cached
+ * [c_KV || k_R] rows ("advantages of MLA").
  *   h [batch][n_q][d_model] -> u [batch][n_q][d_model];
  *   cache_lens [batch] int32 device: sequence lengths AFTER appending the new
  *     tokens (1 <= n_q <= cache_lens[b] <= max_cache_len).  The new tokens
  *     take positions cache_lens[b]-n_q .. cache_lens[b]-1 and query i sees
  *     keys 0..cache_lens[b]-n_q+i (causal among the new tokens);
- *   max_cache_len: host-side bound on cache_lens, also used for the split plan;
+ *   cache_lens_host: NULL, or the same lengths in host memory.  When given,
+ *     every length is checked on the host before any GPU work
+ *     (MLA_ERR_SHAPE if one lies outside [n_q, max_cache_len]); the call
+ *     reads them before it returns and keeps no pointer to them;
+ *   max_cache_len: host-side bound on cache_lens, used for validation and to
+ *     size the workspace;
  *   o_heads: optional [batch*n_q][n_heads][d_v], or NULL.
  * Queries are absorbed into the latent space (W_UK folded into q, W_UV applied
  * after the softmax-weighted latent sum), so attention reads each cached row
- * once for all heads.  Workspace: mla_workspace_size(cfg, MLA_OP_DECODE,
- * batch, n_q, max_cache_len). */
+ * once for all heads.  The cached rows are divided among the compute units
+ * in proportion to each sequence's length (read from cache_lens on the
+ * device), and the order of every reduction is fixed by the lengths alone,
+ * so results are bitwise reproducible.  Workspace: mla_workspace_size(cfg,
+ * MLA_OP_DECODE, batch, n_q, max_cache_len). */
 mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h,
                       int32_t batch, int32_t n_q, const int32_t *cache_lens,
-                      int32_t max_cache_len, const mla_cache *cache, void *u, void *o_heads,
+                      const int32_t *cache_lens_host, int32_t max_cache_len,
+                      const mla_cache *cache, void *u, void *o_heads,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /* Human-readable name of a status code (static string). */

@@ -9,7 +9,10 @@ Recipe (shared by every workload):
   * one numpy ``Generator(PCG64(1000 + workload_id))`` per workload;
   * draw order: W_DQ, W_UQ, W_QR, W_DKV, W_KR, W_UK, W_UV, W_O, then h, then
     the per-sequence cache lengths (ragged workload only), then the cached
-    latent rows, then the block permutation (paged workload only);
+    latent rows; the block permutation (paged workload only) comes from a
+    stream of its own, ``PCG64(1000 + workload_id + 7919)``, so it is the
+    same whether or not the rows are drawn on the host (the benchmark draws
+    the rows of its large workloads on the device: ``cache_rows=False``);
   * weights are N(0, 1/fan_in) with fan_in the input dimension, hidden states
     N(0, 1), cached latent rows N(0, 1) for both the c_KV and the k_R columns;
   * values are drawn as float32 and rounded to bfloat16 with
@@ -191,9 +194,11 @@ def make_workload(wid: int, *, dims: Optional[Dims] = None, batch: Optional[int]
                   ragged_max: Optional[int] = None, n_q: Optional[int] = None,
                   paged: Optional[bool] = None, block_size: Optional[int] = None,
                   dtype: Optional[str] = None, seed: Optional[int] = None,
-                  n_steps: Optional[int] = None) -> Workload:
+                  n_steps: Optional[int] = None, lengths=None, cache_rows: bool = True) -> Workload:
     """Build workload ``wid`` (1..5).  Keyword overrides shrink or reshape it
-    for tests; the seed stays 1000 + wid unless given."""
+    for tests; the seed stays 1000 + wid unless given.  ``lengths`` (decode
+    workloads) fixes every sequence's cache length after the append (and the
+    batch)."""
     spec = dict(WORKLOADS[wid])
     d = dims or spec["dims"]
     dt = dtype or spec["dtype"]
@@ -201,6 +206,8 @@ def make_workload(wid: int, *, dims: Optional[Dims] = None, batch: Optional[int]
     kind = spec["kind"]
     rng = np.random.Generator(np.random.PCG64(1000 + wid if seed is None else seed))
     B = batch if batch is not None else spec["batch"]
+    if lengths is not None:
+        B = len(lengths)
     wl = Workload(wid=wid, name=spec["name"], dims=d, dtype=dt, kind=kind, batch=B)
     wl.weights_f32, wl.weights_bits = draw_weights(rng, d, bf16)
 
@@ -225,24 +232,28 @@ def make_workload(wid: int, *, dims: Optional[Dims] = None, batch: Optional[int]
     wl.h_f32, wl.h_bits = _normal(rng, (B, nq, d.d_model), 1.0, bf16)
     rmax = ragged_max if ragged_max is not None else spec.get("ragged_max")
     ulen = uniform_len if uniform_len is not None else spec.get("uniform_len")
-    if rmax is not None and uniform_len is None:
+    if lengths is not None:
+        lens = np.maximum(np.asarray(lengths, dtype=np.int64), nq)
+    elif rmax is not None and uniform_len is None:
         # integers, both ends inclusive; at least n_q so the new tokens fit
         lens = rng.integers(low=1, high=rmax, size=B, endpoint=True).astype(np.int64)
         lens = np.maximum(lens, nq)
     else:
         lens = np.full(B, ulen, dtype=np.int64)
     wl.lens = lens.astype(np.int32)
-    cf, cb = [], []
-    for b in range(B):
-        v, bb = _normal(rng, (int(lens[b]) - nq, d.d_row), 1.0, bf16)
-        cf.append(v)
-        cb.append(bb)
-    wl.cache_f32, wl.cache_bits = cf, cb
+    if cache_rows:
+        cf, cb = [], []
+        for b in range(B):
+            v, bb = _normal(rng, (int(lens[b]) - nq, d.d_row), 1.0, bf16)
+            cf.append(v)
+            cb.append(bb)
+        wl.cache_f32, wl.cache_bits = cf, cb
     wl.paged = bool(spec.get("paged", False)) if paged is None else bool(paged)
     wl.block_size = block_size or spec.get("block_size", 64)
     if wl.paged:
         nblk = int(sum((int(l) + wl.block_size - 1) // wl.block_size for l in lens))
-        wl.block_perm = rng.permutation(nblk).astype(np.int32)
+        prng = np.random.Generator(np.random.PCG64((1000 + wid if seed is None else seed) + 7919))
+        wl.block_perm = prng.permutation(nblk).astype(np.int32)
     return wl
 
 

@@ -114,12 +114,14 @@ def _prefill(cfg=None, w=None, h=FAKE, B=1, S=16, cache=None, u=FAKE, ws=FAKE, w
                                wsb, None)
 
 
-def _decode(cfg=None, w=None, h=FAKE, B=2, nq=1, lens=FAKE, ml=64, cache=None, u=FAKE, ws=FAKE, wsb=1 << 40):
+def _decode(cfg=None, w=None, h=FAKE, B=2, nq=1, lens=FAKE, ml=64, cache=None, u=FAKE, ws=FAKE, wsb=1 << 40,
+            lens_host=None):
     cfg = cfg or _cfg()
     w = w or _weights()
     cache = cache if cache is not None else L.make_cache(FAKE, max_len=64)
-    return L.lib().mla_decode(ctypes.byref(cfg), ctypes.byref(w), h, B, nq, lens, ml, ctypes.byref(cache), u, None,
-                              ws, wsb, None)
+    lh = None if lens_host is None else (ctypes.c_int32 * len(lens_host))(*lens_host)
+    return L.lib().mla_decode(ctypes.byref(cfg), ctypes.byref(w), h, B, nq, lens, lh, ml, ctypes.byref(cache), u,
+                              None, ws, wsb, None)
 
 
 def test_prefill_validation():
@@ -157,6 +159,11 @@ def test_decode_validation():
     assert _decode(ws=None) == -4
     assert _decode(wsb=100) == -4
     assert _decode(cfg=_cfg(d_c=256)) == -7  # no decode kernel for this latent width
+    # host lengths, when given, are checked against [n_q, max_cache_len]
+    assert _decode(lens_host=[5, 65]) == -2            # beyond max_cache_len
+    assert _decode(nq=2, lens_host=[1, 64]) == -2      # shorter than the new tokens
+    assert _decode(lens_host=[0, 3]) == -2
+    assert _decode(lens_host=[5, 64], ws=None) == -4   # valid lengths: the next check fails
 
 
 def test_compress_validation():

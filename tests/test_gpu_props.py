@@ -137,36 +137,41 @@ def test_compress_kv_entry_point(wid):
     assert_close(got, np.concatenate([c_kv, k_r], axis=1), wl.bf16, "compressed rows")
 
 
-def test_chunked_prefill_over_ragged_paged_cache():
+@pytest.mark.parametrize("P,C", [((96, 60), 40), ((200, 333), 300), ((500,), 300)])
+def test_chunked_prefill_over_ragged_paged_cache(P, C):
     """A chunk of new tokens per sequence against a cached prefix of a
     different length per sequence (split-phase serving: the prefix rows
     written by mla_compress_kv into a permuted paged cache, the chunk by
     mla_decode with n_q = chunk, causal among its tokens) gives the rows of
-    one longer prefill of each sequence."""
-    P, C, bs = (96, 60), 40, 64
+    one longer prefill of each sequence.  Chunks of 300 tokens take the
+    projection kernels of a few hundred rows (32x64 tiles, with the cache
+    append in their epilogue) and many query row groups per sequence."""
+    bs = 64
+    B = len(P)
     L = max(P) + C
-    wl = make_workload(3, batch=2, seq_len=L)
+    wl = make_workload(3, batch=B, seq_len=L)
     d = wl.dims
     layer = layer_for(wl)
     rng = np.random.Generator(np.random.PCG64(11))
     nb = (L + bs - 1) // bs
-    table = rng.permutation(2 * nb).astype(np.int32).reshape(2, nb)
-    pool = torch.zeros(2 * nb * bs, d.d_row, dtype=layer.tdtype, device="cuda")
+    table = rng.permutation(B * nb).astype(np.int32).reshape(B, nb)
+    pool = torch.zeros(B * nb * bs, d.d_row, dtype=layer.tdtype, device="cuda")
     cache = CacheBuf.paged(pool, bs, table)
-    h = upload(wl.h_f32, wl.h_bits, True)   # [2][L][d_model]
+    h = upload(wl.h_f32, wl.h_bits, True)   # [B][L][d_model]
     # prefixes: sequence b, positions 0..P[b]-1
-    seq = np.concatenate([np.full(P[b], b, np.int32) for b in range(2)])
-    pos = np.concatenate([np.arange(P[b], dtype=np.int32) for b in range(2)])
-    hp = torch.cat([h[b, :P[b]] for b in range(2)]).contiguous()
-    layer.compress_kv(hp, torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), 2, cache)
+    seq = np.concatenate([np.full(P[b], b, np.int32) for b in range(B)])
+    pos = np.concatenate([np.arange(P[b], dtype=np.int32) for b in range(B)])
+    hp = torch.cat([h[b, :P[b]] for b in range(B)]).contiguous()
+    layer.compress_kv(hp, torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), B, cache)
     # chunk: tokens P[b] .. P[b]+C-1 of each sequence
-    hc = torch.stack([h[b, P[b]:P[b] + C] for b in range(2)]).contiguous()
-    lens = torch.tensor([P[0] + C, P[1] + C], dtype=torch.int32, device="cuda")
+    hc = torch.stack([h[b, P[b]:P[b] + C] for b in range(B)]).contiguous()
+    lens_host = np.array([P[b] + C for b in range(B)], dtype=np.int32)
+    lens = torch.from_numpy(lens_host).cuda()
     say(f"chunked prefill: prefixes {P}, chunk {C}, paged block {bs}")
-    u = layer.decode(hc, lens, L, cache).clone()
+    u = layer.decode(hc, lens, L, cache, lens_host=lens_host).clone()
     torch.cuda.synchronize()
     W = weights64(wl)
-    for b in range(2):
+    for b in range(B):
         n = P[b] + C
         ref = O.prefill(d, W, wl.h_f32[b, :n].astype(np.float64), rows=np.arange(P[b], n))
         assert_close(u[b], ref["u"], True, f"chunk rows of sequence {b}")
