@@ -8,19 +8,13 @@
 // paper-reading notes: "Key and Value compression", "attention
 // computation").  Every cached row is therefore read once for all heads.
 //
-// One workgroup = (sequence b, split s, group of 16*NW*HB query rows); a query
-// row is a (new token, head) pair; each wave owns 16*HB rows.  Per 32-row cache tile:
-//   * the tile is staged in LDS twice: as rows ([kv][d_c+d_R], for the
-//     scores) and transposed ([d][kv], latent part only, for P.V), so both
-//     MFMA contractions read 16-byte runs;
-//   * S^T = C . Q^T on the matrix cores: each lane ends with the scores of
-//     one query row for eight cache rows, so the running max and sum are
-//     lane-local plus two cross-lane-group shuffles;
-//   * the cache rows feeding the A operand are permuted so that those eight
-//     rows are consecutive, and the probabilities become the B operand of
-//     O^T += C_lat^T . P^T straight from registers.
-// Split results are stored normalised with their log2-sum-exp; the combine
-// weights them by exp2(lse_s - max lse).
+// One workgroup = (its share of the batch's cached tiles, group of query
+// rows); a query row is a (new token, head) pair.  The bf16 kernel for the
+// DeepSeek-V3 widths (decode_attn_ws_kernel) stages tiles in LDS by DMA and
+// runs both contractions on the matrix cores; decode_attn_kernel is the
+// register-staged form for the other shapes (fp32, block sizes that do not
+// hold whole 32-row tiles).  Split results are stored normalised with their
+// log2-sum-exp; the combine weights them by exp2(lse_s - max lse).
 #include <type_traits>
 
 #include "mla_internal.h"
@@ -406,30 +400,25 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel for gfx950 (d_c = 512, d_R = 64), ROWS = 128 or 64 query rows
-// per workgroup.  The cache tile goes HBM -> LDS with global_load_lds_dwordx4
+// bf16 kernel for gfx950 (d_c = 512, d_R = 64), 64 query rows per
+// workgroup.  The cache tile goes HBM -> LDS with global_load_lds_dwordx4
 // (lane i's 16 bytes land at base + 16*i; no staging registers) into a ring
-// of four stages, two tiles ahead.  Per tile, two phases separated by a
-// barrier:
-//   A (scores): wave w owns query rows (ROWS/4)w.. and computes their scores
-//     against the 32 cached rows, S^T = C . Q^T, from 16-byte row reads of the
-//     stage; the softmax is lane-local (each lane holds eight scores of one
-//     query row) plus two shuffles.  The bf16 probabilities go to LDS.
-//   B (P.V): wave w owns latent columns 128w..128w+127 for all ROWS query rows:
-//     O^T[d][row] += C_lat^T[d][kv] . P^T[kv][row], with C_lat^T read by
-//     ds_read_b64_tr_b16 (lane i of a 16-lane group receives column i of the
-//     4x16 block of 16-bit elements the group addresses) and P^T from LDS.
-// So each wave reads the tile once as rows and only its own quarter of the
-// latent part transposed.  One wave per SIMD: at ROWS = 128, 512 registers
-// hold the queries of 32 rows and the 128x128 O^T block (in AGPRs).  The
-// softmax reference of a row is the max of its first tile and never moves (no
-// O rescale: numerator and denominator share the reference, so the result is
-// the same softmax); a row whose scores later rise more than 2^32 above it is
-// flagged and recomputed exactly by the combine.
+// of four stages, two tiles ahead.  Per tile, two phases:
+//   A (scores): S^T = C . Q^T against the 32 cached rows of the tile, from
+//     16-byte row reads of the stage; the softmax is lane-local (each lane
+//     holds the scores of one query row for four cached rows) plus cross-lane
+//     swaps.  The bf16 probabilities go to LDS.
+//   B (P.V): O^T[d][row] += C_lat^T[d][kv] . P^T[kv][row], with C_lat^T read
+//     by ds_read_b64_tr_b16 (lane i of a 16-lane group receives column i of
+//     the 4x16 block of 16-bit elements the group addresses) and P^T from LDS.
+// The softmax reference of a row is the max of its first tile and never
+// moves (no O rescale: numerator and denominator share the reference, so the
+// result is the same softmax); a row whose scores later rise more than 2^32
+// above it is flagged and recomputed exactly by the combine.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
-#ifndef DECODE_PF
-#define DECODE_PF 2               // score steps of cache fragments read ahead
+#ifndef DECODE_WS_PF
+#define DECODE_WS_PF 6            // score steps of cache fragments read ahead
 #endif
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -478,347 +467,51 @@ __device__ inline void bar() {
   asm volatile("" ::: "memory");
 }
 
-template <int DC, int DR, bool PAGED, int ROWS>
-__global__ __launch_bounds__(256, 1) void decode_attn_dma_kernel(DecodeArgs a) {
-  constexpr int NW = 4, NT = 64 * NW;
-  constexpr int D = DC + DR;
-  constexpr int CH = D / 8;                          // 16-byte chunks per cached row
-  constexpr int LOADS = KVT * CH / NT;               // copy instructions per wave per tile
-  constexpr int STAGE = KVT * D;                     // elements per stage
-  constexpr int NS = 4;                              // ring stages (two tiles ahead)
-  constexpr int QS = D / 32;                         // 32-wide k steps of the scores
-  constexpr int HA = ROWS / (16 * NW);               // 16-row blocks per wave in the scores
-  constexpr int DW = DC / NW, DBW = DW / 16;         // latent columns per wave in P.V
-  constexpr int HBS = ROWS / 16;                     // 16-row blocks in P.V
-  constexpr int PF = DECODE_PF;                      // score steps read ahead
-  constexpr int PVS = HBS - HA;                      // P.V row blocks interleaved with the scores
-  // P = exp2(score - reference) stays below 2^TAU, so P (bf16), l and O (fp32)
-  // keep their range without ever rescaling O
-  constexpr float TAU = 32.0f, MREF0 = -1e30f;
-  static_assert(KVT * CH % NT == 0 && CH % 8 == 0 && DC % (16 * NW) == 0 && DBW == 8, "");
-  static_assert(ROWS % (16 * NW) == 0 && HA >= 1 && HA <= 2, "");
-  static_assert(QS > PF && QS >= 2 * PVS && QS >= 2 * LOADS, "");
-
-  // 4 x 36 KB stages + 2 x 8 KB of P = 160 KB.  Rows have no padding: the
-  // 16-byte chunk index is XORed with (row & 7), which keeps both the 16-byte
-  // score reads and the transposed reads free of bank conflicts.
-  __shared__ __attribute__((aligned(16))) bf16 stages[NS * STAGE];
-  __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2 * 4 * ROWS];   // P[buf][g][row]
-
-  int w_item, rg;
-  if (!decode_item(a, w_item, rg)) return;
-  bool first_seg = true;
-  for_each_segment(a, w_item, [&](const int b, const int len, const int kv_beg, const int kv_end, const int slot) {
-  LANE_IDS_PER_PART;
-  if (!first_seg) {
-    // the previous part's partial stores have left and every wave is done
-    // with the stages it staged them in
-    wait_vmcnt<0>();
-    __syncthreads();
-  }
-  first_seg = false;
-  const int R = a.n_q * a.n_h;
-  const int rbase = rg * ROWS;
-  const float sl2 = a.scale_log2;
-  const bf16 *pool = (const bf16 *)a.cache.pool;
-  const long seq_row0 = (long)b * a.cache.max_len;
-  const unsigned lds_stages = (unsigned)(size_t)(lds_void *)stages;
-  const int ntiles = (kv_end - kv_beg + KVT - 1) / KVT;
-
-  // Copies.  Stage slot (row, c) holds cache chunk (row, c ^ (row & 7)); a
-  // tile lies inside one cache block (block_size is a multiple of the tile),
-  // so its rows are contiguous: a uniform base plus 32-bit lane offsets.  The
-  // lane's slot of instruction i is i*NT + tid; its (row, chunk) advances by
-  // NT = 3*CH + 40 per instruction.  Rows past the end of a partial last tile
-  // repeat its last row (finite values; their probabilities are 0).
-  static_assert(NT / CH == 3 && NT % CH == 40, "");
-  const int r0 = tid / CH, c0 = tid - (tid / CH) * CH;
-  auto tile_src = [&](int t) {
-    const int kvb = kv_beg + t * KVT;
-    long trow;
-    if constexpr (PAGED) {
-      const int q = block_of(a.cache, kvb);
-      const int blk = __builtin_amdgcn_readfirstlane(a.cache.table[(long)b * a.cache.max_blocks + q]);
-      trow = (long)blk * a.cache.block_size + (kvb - q * a.cache.block_size);
-    } else {
-      trow = seq_row0 + kvb;
-    }
-    return (const char *)(pool + trow * D);
-  };
-  struct Cursor { int r, c; };
-  auto copy_next = [&](const char *src, int t, int i, Cursor &cu) {
-    const int last = min(KVT, kv_end - (kv_beg + t * KVT)) - 1;
-    const int r = min(cu.r, last);
-    const unsigned dst = lds_stages + (unsigned)((t % NS) * STAGE * 2) + i * NT * 16 + wave * 1024;
-    dma16(src, (unsigned)(r * D + ((cu.c ^ (r & 7)) << 3)) * 2u, dst);
-    cu.c += NT % CH;
-    const bool wrap = cu.c >= CH;
-    cu.c -= wrap ? CH : 0;
-    cu.r += NT / CH + (wrap ? 1 : 0);
-  };
-
-  // score state: this wave's HA blocks of 16 query rows
-  bf16x8 qf[HA][QS];
-  int limit[HA];
-  float mref[HA], lrun[HA];
-#pragma unroll
-  for (int ha = 0; ha < HA; ++ha) {
-    const int r = min(rbase + (wave * HA + ha) * 16 + lrow, R - 1);
-    const bf16 *qrow = (const bf16 *)a.q + ((long)b * R + r) * D + lgrp * 8;
-#pragma unroll
-    for (int q = 0; q < QS; ++q) qf[ha][q] = *(const bf16x8 *)(qrow + q * 32);
-    limit[ha] = min(len - a.n_q + r / a.n_h, kv_end - 1);
-    mref[ha] = MREF0;
-    lrun[ha] = 0.f;
-  }
-  bool ovf = false;
-
-  // P.V state: O^T for latent columns wave*DW.. and all ROWS rows
-  f32x4 oacc[DBW][HBS];
-#pragma unroll
-  for (int i = 0; i < DBW; ++i)
-#pragma unroll
-    for (int j = 0; j < HBS; ++j) oacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // the queries are in registers before the first copy is issued, so no wait
-  // for them is left inside the loop (where it would also wait for copies)
-  wait_vmcnt<0>();
-  for (int t = 0; t < 2 && t < ntiles; ++t) {
-    const char *src = tile_src(t);
-    Cursor cu = {r0, c0};
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) copy_next(src, t, i, cu);
-  }
-
-  // Score reads: rows lrow and 16+lrow, logical chunk 4q+lgrp (natural k
-  // order), physical chunk (4q+lgrp) ^ (lrow & 7) = 4(q ^ fq) + (lgrp ^ (lrow & 3))
-  // with fq = (lrow >> 2) & 1: even and odd steps use two base offsets.
-  // Lane group g then holds the scores of rows 4g..4g+3 and 16+4g..16+4g+3,
-  // and the transposed reads of P.V fetch exactly those rows (any four rows
-  // can form the 4x16 block), so P keeps that key order in LDS.
-  const int fq = (lrow >> 2) & 1, gq = lgrp ^ (lrow & 3);
-  const int a_even = lrow * D + (4 * fq + gq) * 8, a_odd = lrow * D + (gq - 4 * fq) * 8;
-  // Transposed reads: row r = 4*lgrp + (lrow >> 2) (and r + 16), elements
-  // 4*(lrow & 3).. of the wave's 16-column block db: physical chunk
-  // wave*16 + 2*(db ^ fh) + cl, fh = (r & 7) >> 1, cl = ((lrow & 3) >> 1) ^ (r & 1).
-  int t_base, t_fh;
-  {
-    const int r = 4 * lgrp + (lrow >> 2), fr = r & 7;
-    const int cl = ((lrow & 3) >> 1) ^ (fr & 1), half = (lrow & 1) * 4;
-    t_base = r * D + (wave * 16 + cl) * 8 + half;
-    t_fh = fr >> 1;
-  }
-  constexpr int TRH = 16 * D;   // sixteen rows further
-  const lds_bf16 *st_base = (const lds_bf16 *)stages;
-  lds_bf16x8 *pl = (lds_bf16x8 *)pbuf;
-
-  // P.V of tile u (stage u % NS, P buffer u & 1); the V^T fragments of the
-  // wave's columns are read once per tile
-  bf16x8 va[DBW];
-  auto load_v = [&](int u) {
-    const lds_bf16 *st = st_base + (u % NS) * STAGE;
-#pragma unroll
-    for (int db = 0; db < DBW; ++db) {
-      const int o = t_base + 16 * ((db & 3) ^ t_fh) + 64 * (db >> 2);
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + o));
-      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + o + TRH));
-      va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-  };
-  auto pv_block = [&](int u, int hb) {
-    const bf16x8 pb = pl[((u & 1) * 4 + lgrp) * ROWS + hb * 16 + lrow];
-#pragma unroll
-    for (int db = 0; db < DBW; ++db) oacc[db][hb] = Mma<bf16>::mma(va[db], pb, oacc[db][hb]);
-  };
-
-  // Scores and softmax of tile t (stage t % NS) into P buffer t & 1.  When
-  // WITH_PV, the P.V of tile t-1 is interleaved: row blocks 0..PVS-1 between
-  // the score steps, the last two with the softmax.  The copy of tile t+2 is
-  // spread over the odd score steps (one instruction each).
-  auto scores = [&](int t, auto with_pv_c) {
-    constexpr bool WITH_PV = decltype(with_pv_c)::value;
-    const lds_bf16 *ca_p = st_base + (t % NS) * STAGE;
-    const int kvb = kv_beg + t * KVT;
-    if (t + 2 < ntiles) {
-      const char *src = tile_src(t + 2);
-      Cursor cu = {r0, c0};
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) copy_next(src, t + 2, i, cu);
-    }
-    f32x4 sacc[2][HA];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ha = 0; ha < HA; ++ha) sacc[kb][ha] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto rd = [&](int q, int kb) {
-      return *(const lds_bf16x8 *)(ca_p + ((q & 1) ? a_odd : a_even) + q * 32 + kb * 16 * D);
-    };
-    bf16x8 ca[PF + 1][2];
-#pragma unroll
-    for (int q = 0; q < PF; ++q) {
-      ca[q][0] = rd(q, 0);
-      ca[q][1] = rd(q, 1);
-    }
-#pragma unroll
-    for (int q = 0; q < QS; ++q) {
-      if (q + PF < QS) {
-        ca[(q + PF) % (PF + 1)][0] = rd(q + PF, 0);
-        ca[(q + PF) % (PF + 1)][1] = rd(q + PF, 1);
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int ha = 0; ha < HA; ++ha) sacc[kb][ha] = Mma<bf16>::mma(ca[q % (PF + 1)][kb], qf[ha][q], sacc[kb][ha]);
-      if constexpr (WITH_PV) {
-        if (q % 2 == 1 && q / 2 < PVS) pv_block(t - 1, q / 2);
-      }
-
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int ha = 0; ha < HA; ++ha) {
-      float sv[2][4];
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kv = kvb + 16 * kb + 4 * lgrp + i;
-          const float x = sacc[kb][ha][i] * sl2;
-          sv[kb][i] = (kv <= limit[ha]) ? x : -INFINITY;
-          mt = fmaxf(mt, sv[kb][i]);
-        }
-      // The first tile fixes the reference of each row (max over the four
-      // lane groups that share it).  Later tiles only check, per lane, that
-      // their scores stay within TAU of it; the flags are merged at the end.
-      if (t == 0) mref[ha] = fmaxf(row_max(mt), MREF0);
-      else ovf |= mt > mref[ha] + TAU;
-      bf16x8 pf;
-      float psum = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = __builtin_amdgcn_exp2f(sv[j >> 2][j & 3] - mref[ha]);
-        psum += p;
-        pf[j] = (bf16)p;
-      }
-      lrun[ha] += psum;
-      pl[((t & 1) * 4 + lgrp) * ROWS + (wave * HA + ha) * 16 + lrow] = pf;
-      if constexpr (WITH_PV) pv_block(t - 1, PVS + ha);
-    }
-  };
-
-  // Iteration i: tile i has landed (tile i+1 may still be in flight); the
-  // scores of tile i run with the P.V of tile i-1 (whose P every wave wrote in
-  // iteration i-1) and the copy of tile i+2 into stage (i+2) % 4, last read by
-  // the P.V of tile i-2 in the previous iteration.  One barrier per iteration.
-  auto sync = [&](int i) {
-    if (i + 1 < ntiles) wait_vmcnt<LOADS>();   // this wave's copies of tile i
-    else wait_vmcnt<0>();
-    wait_lgkm0();                              // this wave's P of tile i-1
-    bar();
-  };
-  sync(0);
-  scores(0, std::false_type());
-  for (int i = 1; i < ntiles; ++i) {
-    sync(i);
-    load_v(i - 1);
-    scores(i, std::true_type());
-  }
-  sync(ntiles);
-  load_v(ntiles - 1);
-#pragma unroll
-  for (int hb = 0; hb < HBS; ++hb) pv_block(ntiles - 1, hb);
-
-  // normalise and store this split's partial result: the score lanes hold l
-  // and the reference of their rows, the P.V lanes the O columns.  A row
-  // marked in overflow gets lse = NaN; the combine recomputes it exactly.
-  ovf = row_max(ovf ? 1.f : 0.f) > 0.f;
-  __syncthreads();   // P no longer read: its space holds 1/l per row
-  float *fac = (float *)pbuf;
-#pragma unroll
-  for (int ha = 0; ha < HA; ++ha) {
-    float l = lrun[ha];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const int rl = (wave * HA + ha) * 16 + lrow;
-    if (lgrp == 0) {
-      fac[rl] = l > 0.f ? 1.f / l : 0.f;
-      if (rbase + rl < R)
-        a.lse_part[(long)slot * R + rbase + rl] =
-            ovf ? __builtin_nanf("") : l > 0.f ? mref[ha] + log2f(l) : -INFINITY;
-    }
-  }
-  __syncthreads();
-  // The normalised rows go through the (now idle) stages as bf16 [ROWS][DC],
-  // 16-byte chunk c of row r at chunk c ^ (r & 15), and leave one whole row
-  // per wave instruction: a lane's own four columns per 16-row block would
-  // make every store touch sixteen rows.
-  static_assert(ROWS * DC <= NS * STAGE && DC / 8 == 64, "");
-  lds_bf16 *ot = (lds_bf16 *)stages;
-#pragma unroll
-  for (int hb = 0; hb < HBS; ++hb) {
-    const int rl = hb * 16 + lrow;
-    const float inv = fac[rl];
-#pragma unroll
-    for (int db = 0; db < DBW; ++db) {
-      const f32x4 o4 = oacc[db][hb] * inv;
-      const int c = (wave * 16 + db * 2 + (lgrp >> 1)) ^ lrow;
-      *(lds_bf16x4 *)(ot + rl * DC + c * 8 + (lgrp & 1) * 4) =
-          bf16x4{(bf16)o4[0], (bf16)o4[1], (bf16)o4[2], (bf16)o4[3]};
-    }
-  }
-  __syncthreads();
-  bf16 *op = (bf16 *)a.o_part + ((long)slot * R + rbase) * DC + lane * 8;
-  for (int rl = wave; rl < ROWS && rbase + rl < R; rl += NW)
-    *(bf16x8 *)(op + (long)rl * DC) = *(const lds_bf16x8 *)(ot + rl * DC + (lane ^ (rl & 15)) * 8);
-  });
-}
-
-// Two waves per SIMD: 64 query rows, 8 waves.  With one wave per SIMD the
-// waits of that wave (copies, LDS reads, the softmax's VALU chain) leave its
-// matrix core idle; here a second wave can issue meanwhile, and the registers
-// of each (queries of 16 rows, O^T of 64 columns x 64 rows) fit in 256.
-//   A (scores): waves w and w+4 hold the queries of rows 16(w&3)..+15; wave
-//     w scores them against cache rows 0..15 of the tile, wave w+4 against
-//     rows 16..31.  The reference of a row is the max over both halves of its
-//     first tile (exchanged once through LDS).  Each lane writes its four
-//     probabilities into its half's part of the P entry, so P has the layout
-//     of the kernel above.
-//   B (P.V): wave w owns latent columns 64w..64w+63 for all 64 rows.
-// Waves 0..3 issue the cache copies (the pattern of the kernel above) and,
-// first, the copies of the 64 query rows, which reach registers through
-// stages 2 and 3 (whole rows per copy instead of sixteen-row register loads).
+// 64 query rows, 8 waves, and on each SIMD one score wave and one P.V wave
+// (waves w and w+4 share SIMD w).  Earlier forms in which every wave did
+// both phases (one or two waves per SIMD, each reading every cache fragment
+// for one 16-row query block) spent longer per tile: the score reads of each
+// tile were four full passes over it.
+//   score waves s = 0..3: query rows 32(s>>1)..+31 (two 16-row blocks in
+//     registers), cache rows 16(s&1)..+15 of each tile.  Every 16-byte cache
+//     fragment read from LDS feeds two MFMAs (one per query block): the
+//     scores read each tile from LDS twice in all, not four times.
+//   P.V waves p = 0..3 (waves 4..7): latent columns 128p..128p+127 for all
+//     64 rows (O^T in 128 registers); they also issue the tile copies.
+// In iteration i the score waves process tile i while the P.V waves process
+// tile i-1 (its P written in iteration i-1); one barrier per iteration.
 template <int DC, int DR, bool PAGED>
-__global__ __launch_bounds__(512, 1) void decode_attn_dma8_kernel(DecodeArgs a) {
-  constexpr int NW = 8, NC = 256;                    // waves; threads issuing copies
+__global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
+  constexpr int NC = 256;                            // threads issuing copies (the P.V waves)
   constexpr int D = DC + DR;
   constexpr int CH = D / 8;                          // 16-byte chunks per cached row
   constexpr int LOADS = KVT * CH / NC;               // copy instructions per copying wave per tile
   constexpr int STAGE = KVT * D;
   constexpr int NS = 4;                              // ring stages (two tiles ahead)
-  constexpr int QS = D / 32;
+  constexpr int QS = D / 32;                         // 32-wide k steps of the scores
   constexpr int ROWS = 64;
-  constexpr int DW = DC / NW, DBW = DW / 16;         // latent columns per wave in P.V
-  constexpr int HBS = ROWS / 16;
-  constexpr int PF = DECODE_PF;
-  constexpr int PVS = HBS - 1;                       // P.V row blocks interleaved with the scores
+  constexpr int DBW = DC / 4 / 16;                   // 16-column blocks per P.V wave
+  constexpr int HBS = ROWS / 16;                     // 16-row blocks in P.V
+  constexpr int PF = DECODE_WS_PF;                   // score steps read ahead
   constexpr float TAU = 32.0f, MREF0 = -1e30f;
-  static_assert(KVT * CH % NC == 0 && DBW == 4 && QS > PF && QS >= 2 * PVS && QS >= 2 * LOADS, "");
+  static_assert(KVT * CH % NC == 0 && DBW == 8 && QS > PF && DC / 8 == 64, "");
 
   __shared__ __attribute__((aligned(16))) bf16 stages[NS * STAGE];
   __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2 * 4 * ROWS];   // P[buf][g][row]
   __shared__ float xch[2][ROWS];                                       // per key half: row max, then row sum
   __shared__ int xov[2][ROWS];                                         // per key half: row overflowed
+  constexpr int BTAB = PAGED ? 1024 : 1;
+  __shared__ int btab[BTAB];
 
   int w_item, rg;
   if (!decode_item(a, w_item, rg)) return;
   bool first_seg = true;
   for_each_segment(a, w_item, [&](const int b, const int len, const int kv_beg, const int kv_end, const int slot) {
   LANE_IDS_PER_PART;
-  const int rw = wave & 3, kh = wave >> 2;          // score roles: row block, key half
+  const bool pv_wave = wave >= 4;                    // wave-uniform role
+  const int sw = wave & 3;                           // score wave index / P.V wave index
+  const int qb = sw >> 1, kh = sw & 1;               // score roles: 32-row query block, key half
   if (!first_seg) {
-    // the previous part's partial stores have left and every wave is done
-    // with the stages it staged them in
     wait_vmcnt<0>();
     __syncthreads();
   }
@@ -830,30 +523,50 @@ __global__ __launch_bounds__(512, 1) void decode_attn_dma8_kernel(DecodeArgs a) 
   const long seq_row0 = (long)b * a.cache.max_len;
   const unsigned lds_stages = (unsigned)(size_t)(lds_void *)stages;
   const int ntiles = (kv_end - kv_beg + KVT - 1) / KVT;
+  int q0 = 0;
+  bool tab_lds = false;
+  if constexpr (PAGED) {
+    q0 = block_of(a.cache, kv_beg);
+    const int nbq = block_of(a.cache, kv_end - 1) - q0 + 1;
+    tab_lds = nbq <= BTAB;
+    if (tab_lds) {
+      const int *trow = a.cache.table + (long)b * a.cache.max_blocks + q0;
+      for (int i = tid; i < nbq; i += 512) btab[i] = trow[i];
+      __syncthreads();
+    }
+  }
 
+  // Copies (P.V waves; copying thread index ct = tid - 256).  Stage slot
+  // (row, c) holds cache chunk (row, c ^ (row & 7)) (no padding; the XOR
+  // keeps the 16-byte score reads and the transposed reads free of bank
+  // conflicts).  A tile lies inside one cache block (block_size is a multiple
+  // of the tile), so its rows are contiguous: a uniform base plus 32-bit lane
+  // offsets.  The lane's slot of instruction i is i*NC + ct; its (row, chunk)
+  // advances by NC = 3*CH + 40 per instruction.  Rows past the end of a
+  // partial last tile repeat its last row (finite values; their
+  // probabilities are 0).
   static_assert(NC / CH == 3 && NC % CH == 40, "");
-  const int r0 = tid / CH, c0 = tid - (tid / CH) * CH;
+  const int ct = tid - NC;
+  const int r0 = ct / CH, c0 = ct - (ct / CH) * CH;
   auto tile_src = [&](int t) {
     const int kvb = kv_beg + t * KVT;
     long trow;
     if constexpr (PAGED) {
       const int q = block_of(a.cache, kvb);
-      const int blk = __builtin_amdgcn_readfirstlane(a.cache.table[(long)b * a.cache.max_blocks + q]);
+      const int blk = __builtin_amdgcn_readfirstlane(tab_lds ? btab[q - q0]
+                                                             : a.cache.table[(long)b * a.cache.max_blocks + q]);
       trow = (long)blk * a.cache.block_size + (kvb - q * a.cache.block_size);
     } else {
       trow = seq_row0 + kvb;
     }
     return (const char *)(pool + trow * D);
   };
-  // copies of rows r_off..r_off+31 of src (rows past `last` repeat it) into
-  // stage st (waves 0..3 only: a wave-uniform branch)
   auto copy_rows = [&](const char *src, int r_off, int last, int st) {
-    if (wave >= NC / 64) return;
     int cr = r0, cc = c0;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int r = min(r_off + cr, last);
-      const unsigned dst = lds_stages + (unsigned)(st * STAGE * 2) + i * NC * 16 + wave * 1024;
+      const unsigned dst = lds_stages + (unsigned)(st * STAGE * 2) + i * NC * 16 + (wave - 4) * 1024;
       dma16(src, (unsigned)(r * D + ((cc ^ (r & 7)) << 3)) * 2u, dst);
       cc += NC % CH;
       const bool wrap = cc >= CH;
@@ -863,192 +576,224 @@ __global__ __launch_bounds__(512, 1) void decode_attn_dma8_kernel(DecodeArgs a) 
   };
   auto copy_tile = [&](int t) { copy_rows(tile_src(t), 0, min(KVT, kv_end - (kv_beg + t * KVT)) - 1, t % NS); };
 
-  // the workgroup's 64 query rows reach LDS through stages 2 and 3 (whole
-  // rows per copy instruction; rows past the last query row repeat it) while
-  // tiles 0 and 1 are copied into stages 0 and 1
-  {
+  // the 64 query rows reach LDS through stages 2 and 3 while tiles 0 and 1
+  // are copied into stages 0 and 1
+  if (pv_wave) {
     const char *qsrc = (const char *)((const bf16 *)a.q + ((long)b * R + rbase) * D);
     copy_rows(qsrc, 0, R - 1 - rbase, 2);
     copy_rows(qsrc, KVT, R - 1 - rbase, 3);
+    for (int t = 0; t < 2 && t < ntiles; ++t) copy_tile(t);
+    if (ntiles >= 2) wait_vmcnt<2 * LOADS>();   // the query copies
+    else wait_vmcnt<LOADS>();
   }
-  for (int t = 0; t < 2 && t < ntiles; ++t) copy_tile(t);
-  // this wave's query copies (the tiles may still be in flight)
-  if (ntiles >= 2) wait_vmcnt<2 * LOADS>();
-  else wait_vmcnt<LOADS>();
   bar();
-  // score state: the queries of rows rbase + 16*rw.. (B operand), read with
-  // the tiles' chunk swizzle; stage 2 is next written by the copy of tile 2,
-  // after the barrier of sync(0), which follows these reads (lgkm wait)
-  bf16x8 qf[QS];
-  const int qr = min(rbase + rw * 16 + lrow, R - 1);
-  {
-    const int rr = (rw * 16 + lrow) & (KVT - 1);
-    const lds_bf16 *qs = (const lds_bf16 *)stages + (2 + (rw >> 1)) * STAGE + rr * D;
-#pragma unroll
-    for (int q = 0; q < QS; ++q) qf[q] = *(const lds_bf16x8 *)(qs + (((4 * q + lgrp) ^ (rr & 7)) << 3));
-  }
-  const int limit = min(len - a.n_q + qr / a.n_h, kv_end - 1);
-  float mref = MREF0, lrun = 0.f;
-  bool ovf = false;
 
-  // P.V state: O^T for latent columns wave*DW.. and all ROWS rows
-  f32x4 oacc[DBW][HBS];
-#pragma unroll
-  for (int i = 0; i < DBW; ++i)
-#pragma unroll
-    for (int j = 0; j < HBS; ++j) oacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-
-  // score reads: the kernel above's addressing, in this wave's half of the tile
-  const int fq = (lrow >> 2) & 1, gq = lgrp ^ (lrow & 3);
-  const int a_even = (kh * 16 + lrow) * D + (4 * fq + gq) * 8;
-  const int a_odd = (kh * 16 + lrow) * D + (gq - 4 * fq) * 8;
-  // transposed reads of the wave's 64 columns (8 chunks): row r = 4*lgrp +
-  // (lrow >> 2) (and r + 16), physical chunk wave*8 + 2*(db ^ fh) + cl
-  int t_base, t_fh;
-  {
-    const int r = 4 * lgrp + (lrow >> 2), fr = r & 7;
-    const int cl = ((lrow & 3) >> 1) ^ (fr & 1), half = (lrow & 1) * 4;
-    t_base = r * D + (wave * 8 + cl) * 8 + half;
-    t_fh = fr >> 1;
-  }
   constexpr int TRH = 16 * D;
   const lds_bf16 *st_base = (const lds_bf16 *)stages;
   lds_bf16x8 *pl = (lds_bf16x8 *)pbuf;
+  float *fac = (float *)pbuf;                // after the loop: 1/l per row
+  lds_bf16 *ot = (lds_bf16 *)stages;         // after the loop: normalised rows
+  static_assert(ROWS * DC <= NS * STAGE, "");
 
-  bf16x8 va[DBW];
-  auto load_v = [&](int u) {
-    const lds_bf16 *st = st_base + (u % NS) * STAGE;
+  // The two roles run separate code (their register state differs); both
+  // pass the same barriers in the same order:
+  //   B0 (tile 0 visible, query reads done), per iteration i: [i == 0: the
+  //   reference exchange] + end of iteration, then E1, E2, E3 around the
+  //   epilogue.
+  if (!pv_wave) {
+    // ------------------------------------------------------------ score waves
+    bf16x8 qf[2][QS];
+    int limit[2];
+    float mref[2] = {MREF0, MREF0}, lrun[2] = {0.f, 0.f};
+    bool ovf[2] = {false, false};
 #pragma unroll
-    for (int db = 0; db < DBW; ++db) {
-      const int o = t_base + 16 * (db ^ t_fh);
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + o));
-      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + o + TRH));
-      va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    for (int j = 0; j < 2; ++j) {
+      const int rl = qb * 32 + j * 16 + lrow;          // row within the group
+      const int rr = rl & (KVT - 1);
+      const lds_bf16 *qs = (const lds_bf16 *)stages + (2 + (rl >> 5)) * STAGE + rr * D;
+#pragma unroll
+      for (int q = 0; q < QS; ++q) qf[j][q] = *(const lds_bf16x8 *)(qs + (((4 * q + lgrp) ^ (rr & 7)) << 3));
+      const int qr = min(rbase + rl, R - 1);
+      limit[j] = min(len - a.n_q + qr / a.n_h, kv_end - 1);
     }
-  };
-  auto pv_block = [&](int u, int hb) {
-    const bf16x8 pb = pl[((u & 1) * 4 + lgrp) * ROWS + hb * 16 + lrow];
-#pragma unroll
-    for (int db = 0; db < DBW; ++db) oacc[db][hb] = Mma<bf16>::mma(va[db], pb, oacc[db][hb]);
-  };
-
-  // Scores and softmax of tile t (stage t % NS) into P buffer t & 1, with the
-  // P.V of tile t-1 interleaved when WITH_PV; two accumulators (even and odd
-  // k steps) halve the dependent MFMA chain.
-  auto scores = [&](int t, auto with_pv_c) {
-    constexpr bool WITH_PV = decltype(with_pv_c)::value;
-    const lds_bf16 *ca_p = st_base + (t % NS) * STAGE;
-    const int kvb = kv_beg + t * KVT;
-    if (t + 2 < ntiles) copy_tile(t + 2);
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    auto rd = [&](int q) { return *(const lds_bf16x8 *)(ca_p + ((q & 1) ? a_odd : a_even) + q * 32); };
-    bf16x8 ca[PF + 1];
-#pragma unroll
-    for (int q = 0; q < PF; ++q) ca[q] = rd(q);
-#pragma unroll
-    for (int q = 0; q < QS; ++q) {
-      if (q + PF < QS) ca[(q + PF) % (PF + 1)] = rd(q + PF);
-      sacc[q & 1] = Mma<bf16>::mma(ca[q % (PF + 1)], qf[q], sacc[q & 1]);
-      if constexpr (WITH_PV) {
-        if (q % 2 == 1 && q / 2 < PVS) pv_block(t - 1, q / 2);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    float sv[4];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kv = kvb + 16 * kh + 4 * lgrp + i;
-      const float x = (sacc[0][i] + sacc[1][i]) * sl2;
-      sv[i] = (kv <= limit) ? x : -INFINITY;
-      mt = fmaxf(mt, sv[i]);
-    }
-    // the first tile fixes the reference of each row: the max over both key
-    // halves; later tiles only check, per lane, that they stay within TAU
-    if (t == 0) {
-      const float m16 = row_max(mt);
-      if (lgrp == 0) xch[kh][rw * 16 + lrow] = m16;
-      wait_lgkm0();
-      bar();
-      mref = fmaxf(fmaxf(xch[0][rw * 16 + lrow], xch[1][rw * 16 + lrow]), MREF0);
-    } else {
-      ovf |= mt > mref + TAU;
-    }
-    bf16x4 pf;
-    float psum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float p = __builtin_amdgcn_exp2f(sv[j] - mref);
-      psum += p;
-      pf[j] = (bf16)p;
-    }
-    lrun += psum;
-    *(lds_bf16x4 *)((lds_bf16 *)(pl + ((t & 1) * 4 + lgrp) * ROWS + rw * 16 + lrow) + kh * 4) = pf;
-    if constexpr (WITH_PV) pv_block(t - 1, PVS);
-  };
-
-  auto sync = [&](int i) {
-    if (i + 1 < ntiles) wait_vmcnt<LOADS>();   // this wave's copies of tile i (none for waves 4..7)
-    else wait_vmcnt<0>();
+    // Score reads: row kh*16 + lrow of the tile, logical chunk 4q+lgrp
+    // (natural k order), physical chunk (4q+lgrp) ^ (lrow & 7) =
+    // 4(q ^ fq) + (lgrp ^ (lrow & 3)) with fq = (lrow >> 2) & 1: even and odd
+    // steps use two base offsets.  Lane group g then holds the scores of
+    // rows 4g..4g+3 of the half, and the transposed reads of P.V fetch exactly
+    // those rows (any four rows can form the 4x16 block), so P keeps that key
+    // order in LDS: entry (g, row) holds keys 4g..4g+3 of the first half and
+    // 16+4g..16+4g+3 of the second.
+    const int fq = (lrow >> 2) & 1, gq = lgrp ^ (lrow & 3);
+    const int a_even = (kh * 16 + lrow) * D + (4 * fq + gq) * 8;
+    const int a_odd = (kh * 16 + lrow) * D + (gq - 4 * fq) * 8;
     wait_lgkm0();
-    bar();
-  };
-  sync(0);
-  scores(0, std::false_type());
-  for (int i = 1; i < ntiles; ++i) {
-    sync(i);
-    load_v(i - 1);
-    scores(i, std::true_type());
-  }
-  sync(ntiles);
-  load_v(ntiles - 1);
-#pragma unroll
-  for (int hb = 0; hb < HBS; ++hb) pv_block(ntiles - 1, hb);
+    bar();                                             // B0
 
-  // row sums and overflow marks of the two key halves meet in LDS
-  {
-    float l = lrun;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const bool rov = row_max(ovf ? 1.f : 0.f) > 0.f;   // any lane of the row
-    if (lgrp == 0) {
-      xch[kh][rw * 16 + lrow] = l;
-      xov[kh][rw * 16 + lrow] = rov ? 1 : 0;
-    }
-  }
-  __syncthreads();   // P no longer read: its space holds 1/l per row
-  float *fac = (float *)pbuf;
-  if (kh == 0 && lgrp == 0) {
-    const int rl = rw * 16 + lrow;
-    const float l = xch[0][rl] + xch[1][rl];
-    const bool ov = (xov[0][rl] | xov[1][rl]) != 0;
-    fac[rl] = l > 0.f ? 1.f / l : 0.f;
-    if (rbase + rl < R)
-      a.lse_part[(long)slot * R + rbase + rl] =
-          ov ? __builtin_nanf("") : l > 0.f ? mref + log2f(l) : -INFINITY;
-  }
-  __syncthreads();
-  // normalised rows through the idle stages, then one whole row per store
-  static_assert(ROWS * DC <= NS * STAGE && DC / 8 == 64, "");
-  lds_bf16 *ot = (lds_bf16 *)stages;
+    for (int t = 0; t <= ntiles; ++t) {
+      if (t < ntiles) {
+        // scores and softmax of tile t into P buffer t & 1
+        const lds_bf16 *ca_p = st_base + (t % NS) * STAGE;
+        const int kvb = kv_beg + t * KVT;
+        f32x4 sacc[2][2];
 #pragma unroll
-  for (int hb = 0; hb < HBS; ++hb) {
-    const int rl = hb * 16 + lrow;
-    const float inv = fac[rl];
+        for (int j = 0; j < 2; ++j) sacc[j][0] = sacc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto rd = [&](int q) { return *(const lds_bf16x8 *)(ca_p + ((q & 1) ? a_odd : a_even) + q * 32); };
+        bf16x8 ca[PF + 1];
 #pragma unroll
-    for (int db = 0; db < DBW; ++db) {
-      const f32x4 o4 = oacc[db][hb] * inv;
-      const int c = (wave * 8 + db * 2 + (lgrp >> 1)) ^ lrow;
-      *(lds_bf16x4 *)(ot + rl * DC + c * 8 + (lgrp & 1) * 4) =
-          bf16x4{(bf16)o4[0], (bf16)o4[1], (bf16)o4[2], (bf16)o4[3]};
+        for (int q = 0; q < PF; ++q) ca[q] = rd(q);
+#pragma unroll
+        for (int q = 0; q < QS; ++q) {
+          if (q + PF < QS) ca[(q + PF) % (PF + 1)] = rd(q + PF);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) sacc[j][q & 1] = Mma<bf16>::mma(ca[q % (PF + 1)], qf[j][q], sacc[j][q & 1]);
+          __builtin_amdgcn_sched_barrier(0);   // keep the read-ahead distance as written
+        }
+        float sv[2][4], mt[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          mt[j] = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kv = kvb + 16 * kh + 4 * lgrp + i;
+            const float x = (sacc[j][0][i] + sacc[j][1][i]) * sl2;
+            sv[j][i] = (kv <= limit[j]) ? x : -INFINITY;
+            mt[j] = fmaxf(mt[j], sv[j][i]);
+          }
+        }
+        // the first tile fixes the reference of each row (max over both key
+        // halves, exchanged through LDS); later tiles only check that they
+        // stay within TAU of it
+        if (t == 0) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const float m16 = row_max(mt[j]);
+            if (lgrp == 0) xch[kh][qb * 32 + j * 16 + lrow] = m16;
+          }
+          wait_lgkm0();
+          bar();                                       // reference exchange
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int rl = qb * 32 + j * 16 + lrow;
+            mref[j] = fmaxf(fmaxf(xch[0][rl], xch[1][rl]), MREF0);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) ovf[j] |= mt[j] > mref[j] + TAU;
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          bf16x4 pf;
+          float psum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = __builtin_amdgcn_exp2f(sv[j][i] - mref[j]);
+            psum += p;
+            pf[i] = (bf16)p;
+          }
+          lrun[j] += psum;
+          *(lds_bf16x4 *)((lds_bf16 *)(pl + ((t & 1) * 4 + lgrp) * ROWS + qb * 32 + j * 16 + lrow) + kh * 4) = pf;
+        }
+      }
+      wait_lgkm0();
+      bar();                                           // end of iteration t
     }
+
+    // row sums and overflow marks of the two key halves meet in LDS
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool rov = row_max(ovf[j] ? 1.f : 0.f) > 0.f;
+      float l = lrun[j];
+      l += __shfl_xor(l, 16);
+      l += __shfl_xor(l, 32);
+      if (lgrp == 0) {
+        xch[kh][qb * 32 + j * 16 + lrow] = l;
+        xov[kh][qb * 32 + j * 16 + lrow] = rov ? 1 : 0;
+      }
+    }
+    __syncthreads();                                   // E1 (P no longer read)
+    if (kh == 0 && lgrp == 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int rl = qb * 32 + j * 16 + lrow;
+        const float l = xch[0][rl] + xch[1][rl];
+        const bool ov = (xov[0][rl] | xov[1][rl]) != 0;
+        fac[rl] = l > 0.f ? 1.f / l : 0.f;
+        if (rbase + rl < R)
+          a.lse_part[(long)slot * R + rbase + rl] =
+              ov ? __builtin_nanf("") : l > 0.f ? mref[j] + log2f(l) : -INFINITY;
+      }
+    }
+    __syncthreads();                                   // E2
+    __syncthreads();                                   // E3
+  } else {
+    // ------------------------------------------------------------ P.V waves
+    // tile 0 has landed (tile 1 may still be in flight)
+    if (ntiles >= 2) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+    f32x4 oacc[DBW][HBS];
+#pragma unroll
+    for (int i = 0; i < DBW; ++i)
+#pragma unroll
+      for (int j = 0; j < HBS; ++j) oacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // transposed reads of the wave's 128 columns (16 chunks): row r = 4*lgrp
+    // + (lrow >> 2) (and r + 16), logical chunk 16p + 2db + ((lrow & 3) >> 1),
+    // physical chunk 16p + 8(db >> 2) + 2((db & 3) ^ fh) + cl
+    const int r = 4 * lgrp + (lrow >> 2), fr = r & 7;
+    const int cl = ((lrow & 3) >> 1) ^ (fr & 1), half = (lrow & 1) * 4;
+    const int t_base = r * D + (sw * 16 + cl) * 8 + half;
+    const int t_fh = fr >> 1;
+    bar();                                             // B0
+
+    for (int i = 0; i <= ntiles; ++i) {
+      // the copy of tile i+2 goes into the stage of tile i-2, whose last
+      // readers (this wave's P.V in iteration i-1) are past the barrier
+      if (i + 2 < ntiles) copy_tile(i + 2);
+      if (i == 0) bar();                               // the score waves' reference exchange
+      if (i >= 1) {
+        const int u = i - 1;
+        const lds_bf16 *st = st_base + (u % NS) * STAGE;
+        bf16x8 va[DBW], pb[HBS];
+#pragma unroll
+        for (int hb = 0; hb < HBS; ++hb) pb[hb] = pl[((u & 1) * 4 + lgrp) * ROWS + hb * 16 + lrow];
+#pragma unroll
+        for (int db = 0; db < DBW; ++db) {
+          const int o = t_base + 16 * ((db & 3) ^ t_fh) + 64 * (db >> 2);
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + o));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + o + TRH));
+          va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int db = 0; db < DBW; ++db)
+#pragma unroll
+          for (int hb = 0; hb < HBS; ++hb) oacc[db][hb] = Mma<bf16>::mma(va[db], pb[hb], oacc[db][hb]);
+      }
+      // this wave's copies of tile i+1 (tile i+2 may stay in flight)
+      if (i + 2 < ntiles) wait_vmcnt<LOADS>();
+      else wait_vmcnt<0>();
+      wait_lgkm0();
+      bar();                                           // end of iteration i
+    }
+    __syncthreads();                                   // E1
+    __syncthreads();                                   // E2 (1/l per row is in LDS)
+    // normalised rows through the idle stages: chunk c of row r at c ^ (r & 15)
+#pragma unroll
+    for (int hb = 0; hb < HBS; ++hb) {
+      const int rl = hb * 16 + lrow;
+      const float inv = fac[rl];
+#pragma unroll
+      for (int db = 0; db < DBW; ++db) {
+        const f32x4 o4 = oacc[db][hb] * inv;
+        const int c = (sw * 16 + db * 2 + (lgrp >> 1)) ^ lrow;
+        *(lds_bf16x4 *)(ot + rl * DC + c * 8 + (lgrp & 1) * 4) =
+            bf16x4{(bf16)o4[0], (bf16)o4[1], (bf16)o4[2], (bf16)o4[3]};
+      }
+    }
+    __syncthreads();                                   // E3
   }
-  __syncthreads();
+  // one whole row per store instruction
   bf16 *op = (bf16 *)a.o_part + ((long)slot * R + rbase) * DC + lane * 8;
-  // streaming stores: the partials are read once, by the combine, from
-  // other XCDs (47.1 -> 45.2 us against write-allocating stores)
-  for (int rl = wave; rl < ROWS && rbase + rl < R; rl += NW)
+  for (int rl = wave; rl < ROWS && rbase + rl < R; rl += 8)
     __builtin_nontemporal_store(*(const lds_bf16x8 *)(ot + rl * DC + (lane ^ (rl & 15)) * 8),
                                 (bf16x8 *)(op + (long)rl * DC));
   });
@@ -1184,7 +929,7 @@ __global__ __launch_bounds__(256, 1) void decode_combine_uv_kernel(DecodeArgs a,
   constexpr int KS = DC / 32;            // k steps
   constexpr int VB = DV / (16 * NW);     // 16-feature blocks per wave
   constexpr int PER = DC / 64;           // latent columns per lane in the merge
-  constexpr int SB = 4;                  // splits per token requested up front
+  constexpr int SB = 8;                  // splits per token requested up front
   static_assert(DC == 512 && PER == 8 && VB >= 1 && DV % (16 * NW) == 0, "");
   // token row tl of the group: 16-byte chunk c at chunk c ^ (tl & 15)
   __shared__ __attribute__((aligned(16))) bf16 olat[TT * DC];
@@ -1291,14 +1036,26 @@ __global__ __launch_bounds__(256, 1) void decode_combine_uv_kernel(DecodeArgs a,
             for (int i = 0; i < PER; ++i) res[i] += w * (float)v[j][jj][i];
           }
         }
-        for (int sp = SB; sp < nsp[j]; ++sp) {
-          const float lsj = a.lse_part[base[j] + (long)sp * R];
-          if (lsj == -INFINITY) continue;
-          const bf16x8 vv = *(const bf16x8 *)((const bf16 *)a.o_part + (base[j] + (long)sp * R) * DC + lane * PER);
-          const float w = exp2f(lsj - lmax);
-          wsum += w;
+        // the remaining splits in batches of eight, every load of a batch
+        // issued before any is used (one round trip per batch)
+        for (int s0 = SB; s0 < nsp[j]; s0 += 8) {
+          bf16x8 vv[8];
+          float lsv[8];
 #pragma unroll
-          for (int i = 0; i < PER; ++i) res[i] += w * (float)vv[i];
+          for (int jj = 0; jj < 8; ++jj) {
+            const int sp = min(s0 + jj, nsp[j] - 1);
+            vv[jj] = *(const bf16x8 *)((const bf16 *)a.o_part + (base[j] + (long)sp * R) * DC + lane * PER);
+            lsv[jj] = sp < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[j]), sp))
+                              : a.lse_part[base[j] + (long)sp * R];
+          }
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj)
+            if (s0 + jj < nsp[j] && lsv[jj] != -INFINITY) {
+              const float w = exp2f(lsv[jj] - lmax);
+              wsum += w;
+#pragma unroll
+              for (int i = 0; i < PER; ++i) res[i] += w * (float)vv[jj][i];
+            }
         }
         const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
@@ -1366,25 +1123,18 @@ static hipError_t launch_attn(const DecodeArgs &a, hipStream_t st) {
 
 hipError_t launch_decode_attn(int dtype, const DecodeArgs &a, hipStream_t st) {
   const bool tile_in_block = !a.cache.table || (a.cache.block_size % KVT == 0);
-  if (dtype == 1 && a.d_c == 512 && a.d_rope == 64 && tile_in_block) {
+  if (dtype == 1 && a.d_c == 512 && a.d_rope == 64 && tile_in_block && a.rows == 64) {
     const int grid = decode_grid(a);
     timing_before("decode_attn", st);
-    if (a.rows == 64) {
-      if (a.cache.table)
-        hipLaunchKernelGGL((decode_attn_dma8_kernel<512, 64, true>), dim3(grid), dim3(512), 0, st, a);
-      else
-        hipLaunchKernelGGL((decode_attn_dma8_kernel<512, 64, false>), dim3(grid), dim3(512), 0, st, a);
-    } else {
-      if (a.cache.table)
-        hipLaunchKernelGGL((decode_attn_dma_kernel<512, 64, true, 128>), dim3(grid), dim3(256), 0, st, a);
-      else
-        hipLaunchKernelGGL((decode_attn_dma_kernel<512, 64, false, 128>), dim3(grid), dim3(256), 0, st, a);
-    }
+    if (a.cache.table)
+      hipLaunchKernelGGL((decode_attn_ws_kernel<512, 64, true>), dim3(grid), dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_attn_ws_kernel<512, 64, false>), dim3(grid), dim3(512), 0, st, a);
     timing_after("decode_attn", st);
     return hipGetLastError();
   }
   if (dtype == 1 && a.d_c == 512 && a.d_rope == 64)
-    return a.rows == 64 ? launch_attn<bf16, 4, 1, 512, 64>(a, st) : launch_attn<bf16, 8, 1, 512, 64>(a, st);
+    return launch_attn<bf16, 4, 1, 512, 64>(a, st);
   if (dtype == 0 && a.d_c == 64 && a.d_rope == 16) return launch_attn<float, 4, 1, 64, 16>(a, st);
   return hipErrorInvalidValue;
 }

@@ -1,4 +1,4 @@
-// Weight-streaming GEMM for few tokens (bf16, up to 64 rows of activations):
+// Weight-streaming GEMM for few tokens (bf16, up to 128 rows of activations):
 // Y[z][m][n] = sum_k X[z][m][k] W[z][n][k]   (W stored [N][K]: the down/up
 // projections, W_UV and W_O), or W stored [K][N] (W_UK in the absorption).
 //
@@ -39,8 +39,8 @@ constexpr int MAX_PARTS = 16;    // workgroups that may share one tile
 template <int MB> constexpr int stream_bk() { return MB <= 2 ? 256 : 128; }
 inline int stream_bk_for(int M) { return M <= 32 ? 256 : 128; }
 // ring stages: as many units in flight as LDS holds (48 KB per unit at 32
-// tokens, 32 KB at 64)
-template <int MB> constexpr int stream_stages() { return MB <= 2 ? 3 : 4; }
+// tokens, 32 KB at 64, 48 KB at 128)
+template <int MB> constexpr int stream_stages() { return MB <= 2 ? 3 : MB <= 4 ? 4 : 3; }
 
 template <int N>
 __device__ inline void wait_vm() {
@@ -248,17 +248,18 @@ __global__ __launch_bounds__(256) void gemm_stream_reduce_kernel(GemmArgs a, int
 int gemm_stream_grid() { return 256; }
 
 size_t gemm_stream_partial_bytes(int M) {
-  const int mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+  const int mb = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
   return (size_t)gemm_stream_grid() * 2 * 16 * mb * SBN * sizeof(float);
 }
 
 bool gemm_stream_ok(const GemmArgs &a, int wkn) {
-  // Long products only: the ring's fill and drain cost a few microseconds,
-  // which shorter weight streams (q_up, W_UK, W_UV) do not amortise; those
-  // keep the register-streaming kernels.
-  if (wkn || a.K < 4096) return false;
+  // Up to 32 tokens, long products only: the ring's fill and drain cost a
+  // few microseconds, which shorter weight streams (q_up, W_UK, W_UV) do not
+  // amortise; those keep the register-streaming kernels.  From 33 tokens on
+  // every product whose k is a whole number of units streams here.
+  if (wkn || (a.M <= 32 && a.K < 4096)) return false;
   const int bk = stream_bk_for(a.M);
-  if (a.M > 64 || a.K % bk != 0 || !a.partial) return false;
+  if (a.M > 128 || a.K % bk != 0 || !a.partial) return false;
   const long units = (long)a.batch * ((a.N + SBN - 1) / SBN) * (a.K / bk);
   if (units * gemm_stream_grid() >= (1L << 31)) return false;
   // a tile is shared by at most MAX_PARTS workgroups
@@ -307,7 +308,8 @@ static hipError_t launch_stream_t(GemmArgs &a, hipStream_t st) {
 hipError_t launch_gemm_stream(GemmArgs &a, int wkn, hipStream_t st) {
   if (a.M <= 16) return wkn ? launch_stream_t<1, true>(a, st) : launch_stream_t<1, false>(a, st);
   if (a.M <= 32) return wkn ? launch_stream_t<2, true>(a, st) : launch_stream_t<2, false>(a, st);
-  return wkn ? launch_stream_t<4, true>(a, st) : launch_stream_t<4, false>(a, st);
+  if (a.M <= 64) return wkn ? launch_stream_t<4, true>(a, st) : launch_stream_t<4, false>(a, st);
+  return wkn ? launch_stream_t<8, true>(a, st) : launch_stream_t<8, false>(a, st);
 }
 
 }  // namespace mla

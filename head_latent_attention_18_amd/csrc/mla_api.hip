@@ -202,7 +202,7 @@ DecodePlan plan_decode(const mla_config *c, int32_t B, int32_t n_q, int32_t max_
   need(p.sk1, N1);
   need(p.sk2, (int64_t)c->n_heads * (c->d_nope + c->d_rope));
   need(p.sk5, c->d_model);
-  if (dt == MLA_BF16 && T <= 64) part = std::max(part, gemm_stream_partial_bytes((int)T));
+  if (dt == MLA_BF16 && T <= 128) part = std::max(part, gemm_stream_partial_bytes((int)T));
   p.partial = take(part);
   p.total = off;
   return p;
