@@ -16,6 +16,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -542,10 +543,14 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
   return hip_status(e);
 }
 
-mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h, int32_t batch, int32_t n_q,
-                      const int32_t *cache_lens, const int32_t *cache_lens_host, int32_t max_cache_len,
-                      const mla_cache *cache, void *u, void *o_heads, void *workspace, size_t workspace_bytes,
-                      void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the decode entry points (no HIP call).
+mla_status check_decode(const mla_config *cfg, const mla_weights *w, const void *h, int32_t batch, int32_t n_q,
+                        const int32_t *cache_lens, const int32_t *cache_lens_host, int32_t max_cache_len,
+                        const mla_cache *cache, const void *u, DecodePlan *plan) {
   mla_status s = check_config(cfg);
   if (s != MLA_OK) return s;
   if ((s = check_weights(w)) != MLA_OK) return s;
@@ -557,12 +562,15 @@ mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h
   if ((int64_t)batch * n_q > (1L << 20) || (int64_t)n_q * cfg->n_heads > (1L << 20)) return MLA_ERR_UNSUPPORTED;
   if (!attention_supported(cfg, MLA_OP_DECODE)) return MLA_ERR_UNSUPPORTED;
   if ((s = check_cache(cache, batch, max_cache_len)) != MLA_OK) return s;
-  const DecodePlan p = plan_decode(cfg, batch, n_q, max_cache_len);
-  if (!workspace) return MLA_ERR_WORKSPACE;
-  if (workspace_bytes < p.total) return MLA_ERR_WORKSPACE;
+  *plan = plan_decode(cfg, batch, n_q, max_cache_len);
+  return MLA_OK;
+}
 
+// The decode kernel sequence on a validated call, with its workspace at ws.
+mla_status decode_steps(const mla_config *cfg, const mla_weights *w, const void *h, int32_t batch, int32_t n_q,
+                        const int32_t *cache_lens, const mla_cache *cache, void *u, void *o_heads, char *ws,
+                        const DecodePlan &p, void *stream) {
   hipStream_t st = (hipStream_t)stream;
-  char *ws = (char *)workspace;
   const int dt = cfg->dtype;
   const int M = batch * n_q;
   const int NH = cfg->n_heads, D = cfg->d_c + cfg->d_rope;
@@ -654,6 +662,58 @@ mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h
   }
   e = run_output(cfg, w, o, M, u, p.sk5, partial, st);
   return hip_status(e);
+}
+
+// The allocation-free decode's workspace: one array per device, its device
+// address looked up once per device (the array's host-side name is only a
+// stand-in and never reaches a kernel).
+static __device__ __align__(256) unsigned char scratch[MLA_NOALLOC_WORKSPACE_BYTES];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[256];
+
+hipError_t scratch_for_current_device(char **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 256) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = (char *)g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h, int32_t batch, int32_t n_q,
+                      const int32_t *cache_lens, const int32_t *cache_lens_host, int32_t max_cache_len,
+                      const mla_cache *cache, void *u, void *o_heads, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+  DecodePlan p;
+  mla_status s = check_decode(cfg, w, h, batch, n_q, cache_lens, cache_lens_host, max_cache_len, cache, u, &p);
+  if (s != MLA_OK) return s;
+  if (!workspace) return MLA_ERR_WORKSPACE;
+  if (workspace_bytes < p.total) return MLA_ERR_WORKSPACE;
+  return decode_steps(cfg, w, h, batch, n_q, cache_lens, cache, u, o_heads, (char *)workspace, p, stream);
+}
+
+mla_status mla_decode_noalloc(const mla_config *cfg, const mla_weights *w, const void *h, int32_t batch, int32_t n_q,
+                              const int32_t *cache_lens, const int32_t *cache_lens_host, int32_t max_cache_len,
+                              const mla_cache *cache, void *u, void *o_heads, void *stream) {
+  DecodePlan p;
+  mla_status s = check_decode(cfg, w, h, batch, n_q, cache_lens, cache_lens_host, max_cache_len, cache, u, &p);
+  if (s != MLA_OK) return s;
+  if (p.total > (size_t)MLA_NOALLOC_WORKSPACE_BYTES) return MLA_ERR_WORKSPACE;
+  char *ws = nullptr;
+  if (scratch_for_current_device(&ws) != hipSuccess) return MLA_ERR_HIP;
+  return decode_steps(cfg, w, h, batch, n_q, cache_lens, cache, u, o_heads, ws, p, stream);
 }
 
 const char *mla_status_string(mla_status s) {

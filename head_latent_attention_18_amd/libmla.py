@@ -70,6 +70,9 @@ def _lib():
         lib.mla_decode.argtypes = [P(mla_config), P(mla_weights), c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                    c_int32, P(mla_cache), c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
         lib.mla_decode.restype = c_int32
+        lib.mla_decode_noalloc.argtypes = [P(mla_config), P(mla_weights), c_void_p, c_int32, c_int32, c_void_p,
+                                           c_void_p, c_int32, P(mla_cache), c_void_p, c_void_p, c_void_p]
+        lib.mla_decode_noalloc.restype = c_int32
         lib.mla_status_string.argtypes = [c_int32]
         lib.mla_status_string.restype = c_char_p
         lib.mla_version.argtypes = []
@@ -176,6 +179,18 @@ def mla_decode(cfg, w: mla_weights, h, batch: int, n_q: int, cache_lens, max_cac
                                            _ptr(cache_lens), lens_host, max_cache_len, ctypes.byref(cache),
                                            _ptr(u), _ptr(o_heads), _ptr(workspace), workspace_bytes,
                                            _stream(stream)))
+
+
+MLA_NOALLOC_WORKSPACE_BYTES = 96 << 20
+
+
+def mla_decode_noalloc(cfg, w: mla_weights, h, batch: int, n_q: int, cache_lens, max_cache_len: int,
+                       cache: mla_cache, u, o_heads, stream=None, cache_lens_host=None):
+    lens_host, _keep = _host_i32(cache_lens_host)
+    _check("mla_decode_noalloc", _lib().mla_decode_noalloc(ctypes.byref(cfg), ctypes.byref(w), _ptr(h), batch, n_q,
+                                                           _ptr(cache_lens), lens_host, max_cache_len,
+                                                           ctypes.byref(cache), _ptr(u), _ptr(o_heads),
+                                                           _stream(stream)))
 
 
 def mla_status_string(code: int) -> str:

@@ -200,6 +200,28 @@ mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h
                       const mla_cache *cache, void *u, void *o_heads,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* Largest workspace mla_decode_noalloc can use: 96 MiB (DeepSeek-V3 widths:
+ * batch 128 x one new token at cache lengths up to 32768 needs 90.5 MiB,
+ * batch 32 at 4096 needs 35 MiB). */
+#define MLA_NOALLOC_WORKSPACE_BYTES (96u << 20)
+
+/* mla_decode for callers that cannot allocate device memory or bring a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Arguments, results and errors are those of
+ * mla_decode, without the workspace.  The workspace is a device array of
+ * MLA_NOALLOC_WORKSPACE_BYTES built into the library: each GPU the library
+ * runs on holds its own copy from the library's load until the process ends,
+ * and the call never allocates or frees memory.  A call whose workspace
+ * (mla_workspace_size for MLA_OP_DECODE) exceeds that size returns
+ * MLA_ERR_WORKSPACE before any GPU work.  Every call on one GPU uses that
+ * GPU's array: calls that overlap in time on one GPU (other streams, other
+ * host threads) race and give wrong results; serialise them.  Nothing in the
+ * array needs to be zero, and its contents after a call are unspecified. */
+mla_status mla_decode_noalloc(const mla_config *cfg, const mla_weights *w, const void *h,
+                              int32_t batch, int32_t n_q, const int32_t *cache_lens,
+                              const int32_t *cache_lens_host, int32_t max_cache_len,
+                              const mla_cache *cache, void *u, void *o_heads, void *stream);
+
 /* Human-readable name of a status code (static string). */
 const char *mla_status_string(mla_status s);
 

@@ -166,6 +166,26 @@ def test_decode_validation():
     assert _decode(lens_host=[5, 64], ws=None) == -4   # valid lengths: the next check fails
 
 
+def test_decode_noalloc_validation():
+    """The allocation-free decode validates like mla_decode and rejects a
+    call whose workspace exceeds its built-in array, before any GPU work."""
+    cfg, w = _cfg(), _weights()
+    def call(**k):
+        cache = k.get("cache", L.make_cache(FAKE, max_len=k.get("ml", 64)))
+        return L.lib().mla_decode_noalloc(ctypes.byref(k.get("cfg", cfg)), ctypes.byref(w), k.get("h", FAKE),
+                                          k.get("B", 2), k.get("nq", 1), k.get("lens", FAKE), None, k.get("ml", 64),
+                                          ctypes.byref(cache), FAKE, None, None)
+    assert call(cfg=_cfg(dtype=7)) == -3
+    assert call(h=None) == -1
+    assert call(lens=None) == -1
+    assert call(nq=0) == -2
+    assert call(cfg=_cfg(d_c=256)) == -7
+    # 2 sequences x 300 new tokens: about 312 MB of workspace, over the 96 MiB array
+    big = L.mla_workspace_size(cfg, L.MLA_OP_DECODE, 2, 300, 633)
+    assert big > L.MLA_NOALLOC_WORKSPACE_BYTES
+    assert call(B=2, nq=300, ml=633) == -4
+
+
 def test_compress_validation():
     cfg = _cfg()
     w = _weights()
