@@ -426,6 +426,7 @@ typedef __attribute__((address_space(3))) bf16 lds_bf16;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 template <int N>
 __device__ inline void wait_vmcnt() {
@@ -480,7 +481,14 @@ __device__ inline void bar() {
 //     64 rows (O^T in 128 registers); they also issue the tile copies.
 // In iteration i the score waves process tile i while the P.V waves process
 // tile i-1 (its P written in iteration i-1); one barrier per iteration.
-template <int DC, int DR, bool PAGED>
+// FP8: the cache holds FP8 rows (d_c E4M3 codes | d_R bf16 | d_c/128 fp32
+// scales); the P.V waves load each tile into registers and write it to the
+// stage already converted to bf16 (each code decoded exactly to fp32, times
+// its group's fp32 scale, rounded to bf16; the hardware's scaled fp8
+// conversion is not used: its scale operand is an MX power-of-two scale), so
+// the stage layout, and every read of it, is that of a bf16 cache.  HBM then carries 656 bytes per cached row
+// instead of 1152.
+template <int DC, int DR, bool PAGED, bool FP8>
 __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
   constexpr int NC = 256;                            // threads issuing copies (the P.V waves)
   constexpr int D = DC + DR;
@@ -519,7 +527,6 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
   const int R = a.n_q * a.n_h;
   const int rbase = rg * ROWS;
   const float sl2 = a.scale_log2;
-  const bf16 *pool = (const bf16 *)a.cache.pool;
   const long seq_row0 = (long)b * a.cache.max_len;
   const unsigned lds_stages = (unsigned)(size_t)(lds_void *)stages;
   const int ntiles = (kv_end - kv_beg + KVT - 1) / KVT;
@@ -548,6 +555,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
   static_assert(NC / CH == 3 && NC % CH == 40, "");
   const int ct = tid - NC;
   const int r0 = ct / CH, c0 = ct - (ct / CH) * CH;
+  constexpr int RBYTES = FP8 ? DC + 2 * DR + 4 * (DC / 128) : 2 * D;   // bytes per cached row
   auto tile_src = [&](int t) {
     const int kvb = kv_beg + t * KVT;
     long trow;
@@ -559,7 +567,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
     } else {
       trow = seq_row0 + kvb;
     }
-    return (const char *)(pool + trow * D);
+    return (const char *)a.cache.pool + trow * RBYTES;
   };
   auto copy_rows = [&](const char *src, int r_off, int last, int st) {
     int cr = r0, cc = c0;
@@ -576,15 +584,63 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
   };
   auto copy_tile = [&](int t) { copy_rows(tile_src(t), 0, min(KVT, kv_end - (kv_beg + t * KVT)) - 1, t % NS); };
 
+  // FP8 tiles: copying thread ct converts row ct >> 3 of a tile, part
+  // j = ct & 7: codes 64j..64j+63 (logical chunks 8j..8j+7 of the bf16 row),
+  // k_R values 8j..8j+7 (chunk 64 + j) and the scale of group j >> 1.  The
+  // loads of tile t are issued one iteration before the conversion writes it.
+  static_assert(!FP8 || (DC == 512 && DR == 64 && NC == 8 * KVT), "");
+  u32x4 f8c[4], f8r;
+  float f8s = 0.f;
+  auto fp8_load = [&](int t) {
+    const int r = min(ct >> 3, min(KVT, kv_end - (kv_beg + t * KVT)) - 1), j = ct & 7;
+    const char *row = tile_src(t) + (long)r * RBYTES;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f8c[i] = *(const u32x4 *)(row + 64 * j + 16 * i);
+    f8r = *(const u32x4 *)(row + DC + 16 * j);
+    f8s = *(const float *)(row + DC + 2 * DR + 4 * (j >> 1));
+  };
+  auto fp8_store = [&](int t) {
+    const int r = ct >> 3, j = ct & 7;
+    lds_bf16 *st = (lds_bf16 *)stages + (t % NS) * STAGE + r * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // 16 codes -> two 8-element chunks (logical 8j + 2i, 8j + 2i + 1)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        bf16x8 v;
+#pragma unroll
+        for (int w2 = 0; w2 < 2; ++w2) {
+          const int word = (int)f8c[i][2 * h2 + w2];
+          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+          v[4 * w2] = (bf16)(lo[0] * f8s);
+          v[4 * w2 + 1] = (bf16)(lo[1] * f8s);
+          v[4 * w2 + 2] = (bf16)(hi[0] * f8s);
+          v[4 * w2 + 3] = (bf16)(hi[1] * f8s);
+        }
+        const int c = 8 * j + 2 * i + h2;
+        *(lds_bf16x8 *)(st + ((c ^ (r & 7)) << 3)) = v;
+      }
+    }
+    *(lds_u32x4 *)(st + (((64 + j) ^ (r & 7)) << 3)) = f8r;
+  };
+
   // the 64 query rows reach LDS through stages 2 and 3 while tiles 0 and 1
-  // are copied into stages 0 and 1
+  // are copied into stages 0 and 1 (FP8: tile 0 converted, tile 1 loaded)
   if (pv_wave) {
     const char *qsrc = (const char *)((const bf16 *)a.q + ((long)b * R + rbase) * D);
     copy_rows(qsrc, 0, R - 1 - rbase, 2);
     copy_rows(qsrc, KVT, R - 1 - rbase, 3);
-    for (int t = 0; t < 2 && t < ntiles; ++t) copy_tile(t);
-    if (ntiles >= 2) wait_vmcnt<2 * LOADS>();   // the query copies
-    else wait_vmcnt<LOADS>();
+    if constexpr (FP8) {
+      fp8_load(0);
+      wait_vmcnt<0>();
+      fp8_store(0);
+      if (ntiles >= 2) fp8_load(1);
+    } else {
+      for (int t = 0; t < 2 && t < ntiles; ++t) copy_tile(t);
+      if (ntiles >= 2) wait_vmcnt<2 * LOADS>();   // the query copies
+      else wait_vmcnt<LOADS>();
+    }
   }
   bar();
 
@@ -729,8 +785,10 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
   } else {
     // ------------------------------------------------------------ P.V waves
     // tile 0 has landed (tile 1 may still be in flight)
-    if (ntiles >= 2) wait_vmcnt<LOADS>();
-    else wait_vmcnt<0>();
+    if constexpr (!FP8) {
+      if (ntiles >= 2) wait_vmcnt<LOADS>();
+      else wait_vmcnt<0>();
+    }
     f32x4 oacc[DBW][HBS];
 #pragma unroll
     for (int i = 0; i < DBW; ++i)
@@ -743,12 +801,23 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
     const int cl = ((lrow & 3) >> 1) ^ (fr & 1), half = (lrow & 1) * 4;
     const int t_base = r * D + (sw * 16 + cl) * 8 + half;
     const int t_fh = fr >> 1;
+    wait_lgkm0();                                      // FP8: this wave's writes of tile 0
     bar();                                             // B0
 
     for (int i = 0; i <= ntiles; ++i) {
       // the copy of tile i+2 goes into the stage of tile i-2, whose last
       // readers (this wave's P.V in iteration i-1) are past the barrier
-      if (i + 2 < ntiles) copy_tile(i + 2);
+      // (FP8: tile i+1, loaded in iteration i-1, is converted into the stage
+      // of tile i-3, and the loads of tile i+2 go out)
+      if constexpr (FP8) {
+        if (i + 1 < ntiles) {
+          wait_vmcnt<0>();
+          fp8_store(i + 1);
+          if (i + 2 < ntiles) fp8_load(i + 2);
+        }
+      } else if (i + 2 < ntiles) {
+        copy_tile(i + 2);
+      }
       if (i == 0) bar();                               // the score waves' reference exchange
       if (i >= 1) {
         const int u = i - 1;
@@ -769,8 +838,10 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
           for (int hb = 0; hb < HBS; ++hb) oacc[db][hb] = Mma<bf16>::mma(va[db], pb[hb], oacc[db][hb]);
       }
       // this wave's copies of tile i+1 (tile i+2 may stay in flight)
-      if (i + 2 < ntiles) wait_vmcnt<LOADS>();
-      else wait_vmcnt<0>();
+      if constexpr (!FP8) {
+        if (i + 2 < ntiles) wait_vmcnt<LOADS>();
+        else wait_vmcnt<0>();
+      }
       wait_lgkm0();
       bar();                                           // end of iteration i
     }
@@ -815,28 +886,40 @@ __device__ void decode_row_exact(const DecodeArgs &a, int b, int r, int len, flo
 #pragma unroll
   for (int i = 0; i < QP; ++i) qv[i] = (lane + 64 * i < D) ? to_f32(qrow[lane + 64 * i]) : 0.f;
   const int limit = min(len - a.n_q + r / a.n_h, len - 1);
-  auto score = [&](const T *crow) {
+  // element c of a cached row (FP8 rows: code times its group's scale, or
+  // the bf16 k_R)
+  const bool f8 = a.cache.fp8 != 0;
+  auto elem = [&](const unsigned char *row, int c) -> float {
+    if (!f8) return to_f32(((const T *)row)[c]);
+    if (c >= DC) return (float)((const bf16 *)(row + DC))[c - DC];
+    const float sc = ((const float *)(row + DC + 2 * DR))[c / 128];
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)row[c], false)[0] * sc;
+  };
+  auto row_at = [&](int kv) {
+    return (const unsigned char *)a.cache.pool + cache_row(a.cache, b, kv) * (long)a.cache.row_bytes;
+  };
+  auto score = [&](const unsigned char *crow) {
     float dot = 0.f;
 #pragma unroll
     for (int i = 0; i < QP; ++i)
-      if (lane + 64 * i < D) dot += qv[i] * to_f32(crow[lane + 64 * i]);
+      if (lane + 64 * i < D) dot += qv[i] * elem(crow, lane + 64 * i);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
     return dot * a.scale_log2;
   };
   float m = -INFINITY;
-  for (int kv = 0; kv <= limit; ++kv) m = fmaxf(m, score((const T *)a.cache.pool + cache_row(a.cache, b, kv) * D));
+  for (int kv = 0; kv <= limit; ++kv) m = fmaxf(m, score(row_at(kv)));
   float l = 0.f, acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   for (int kv = 0; kv <= limit; ++kv) {
-    const T *crow = (const T *)a.cache.pool + cache_row(a.cache, b, kv) * D;
+    const unsigned char *crow = row_at(kv);
     const float p = exp2f(score(crow) - m);
     l += p;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = CHUNKED ? lane * PER + i : lane + 64 * i;
-      if (c < DC) acc[i] += p * to_f32(crow[c]);
+      if (c < DC) acc[i] += p * elem(crow, c);
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -1126,13 +1209,21 @@ hipError_t launch_decode_attn(int dtype, const DecodeArgs &a, hipStream_t st) {
   if (dtype == 1 && a.d_c == 512 && a.d_rope == 64 && tile_in_block && a.rows == 64) {
     const int grid = decode_grid(a);
     timing_before("decode_attn", st);
-    if (a.cache.table)
-      hipLaunchKernelGGL((decode_attn_ws_kernel<512, 64, true>), dim3(grid), dim3(512), 0, st, a);
-    else
-      hipLaunchKernelGGL((decode_attn_ws_kernel<512, 64, false>), dim3(grid), dim3(512), 0, st, a);
+    if (a.cache.fp8) {
+      if (a.cache.table)
+        hipLaunchKernelGGL((decode_attn_ws_kernel<512, 64, true, true>), dim3(grid), dim3(512), 0, st, a);
+      else
+        hipLaunchKernelGGL((decode_attn_ws_kernel<512, 64, false, true>), dim3(grid), dim3(512), 0, st, a);
+    } else {
+      if (a.cache.table)
+        hipLaunchKernelGGL((decode_attn_ws_kernel<512, 64, true, false>), dim3(grid), dim3(512), 0, st, a);
+      else
+        hipLaunchKernelGGL((decode_attn_ws_kernel<512, 64, false, false>), dim3(grid), dim3(512), 0, st, a);
+    }
     timing_after("decode_attn", st);
     return hipGetLastError();
   }
+  if (a.cache.fp8) return hipErrorInvalidValue;   // FP8 rows: the DeepSeek-V3 kernel only
   if (dtype == 1 && a.d_c == 512 && a.d_rope == 64)
     return launch_attn<bf16, 4, 1, 512, 64>(a, st);
   if (dtype == 0 && a.d_c == 64 && a.d_rope == 16) return launch_attn<float, 4, 1, 64, 16>(a, st);

@@ -37,6 +37,15 @@ const int kCUs = 256;  // MI355X compute units; the split plan targets one wave 
 
 size_t esize(const mla_config *c) { return c->dtype == MLA_BF16 ? 2 : 4; }
 
+bool cache_fp8(const mla_config *c) { return c->cache_dtype == MLA_CACHE_FP8_E4M3; }
+
+// bytes of one cached row: (d_c + d_R) elements, or the FP8 row (codes,
+// bf16 k_R, a float32 scale per 128 columns)
+size_t row_bytes(const mla_config *c) {
+  if (cache_fp8(c)) return (size_t)c->d_c + 2 * (size_t)c->d_rope + 4 * (size_t)(c->d_c / 128);
+  return (size_t)(c->d_c + c->d_rope) * esize(c);
+}
+
 // YaRN is on for any factor other than 0 and 1 (a zero-initialised config
 // keeps plain RoPE)
 bool yarn_on(const mla_config *c) { return c->yarn_factor != 0.0 && c->yarn_factor != 1.0; }
@@ -54,6 +63,9 @@ mla_status check_config(const mla_config *c) {
     if (!(c->yarn_beta_slow > 0.0) || !(c->yarn_beta_fast > c->yarn_beta_slow) || !isfinite(c->yarn_beta_fast))
       return MLA_ERR_SHAPE;
   }
+  if (c->cache_dtype != MLA_CACHE_LAYER && c->cache_dtype != MLA_CACHE_FP8_E4M3) return MLA_ERR_DTYPE;
+  if (c->cache_dtype == MLA_CACHE_FP8_E4M3 && (c->dtype != MLA_BF16 || c->d_c % 128 || c->d_rope % 8))
+    return MLA_ERR_UNSUPPORTED;
   if (c->d_rope / 2 > MLA_MAX_ROPE_PAIRS) return MLA_ERR_UNSUPPORTED;
   if ((long)c->n_heads * (c->d_nope + c->d_rope) > (1L << 24) || c->d_model > (1 << 20))
     return MLA_ERR_UNSUPPORTED;
@@ -164,7 +176,7 @@ SplitK choose_splitk(int dtype, int64_t M, int64_t N, int64_t K, int batch) {
 struct DecodePlan {
   int W, slots, row_groups, rows;
   SplitK sk1, sk2, sk5;
-  size_t c_q, q_nope, q_abs, o_part, lse, o_lat, o, partial, total;
+  size_t c_q, q_nope, q_abs, o_part, lse, o_lat, o, ckv, kr, partial, total;
 };
 // The attention's split plan: W workgroups per row group (one wave of
 // workgroups over the CUs), each taking an equal share of the batch's cached
@@ -196,6 +208,9 @@ DecodePlan plan_decode(const mla_config *c, int32_t B, int32_t n_q, int32_t max_
   p.lse = take((size_t)p.slots * R * 4);
   p.o_lat = take((size_t)T * c->n_heads * c->d_c * e);
   p.o = take((size_t)T * c->n_heads * c->d_v * e);
+  // FP8 cache: the new tokens' c_KV and k_R before quantisation
+  p.ckv = take(cache_fp8(c) ? (size_t)T * c->d_c * e : 0);
+  p.kr = take(cache_fp8(c) ? (size_t)T * c->d_rope * e : 0);
   size_t part = 0;
   auto need = [&](SplitK sk, int64_t N) {
     if (sk.splits > 1) part = std::max(part, (size_t)sk.splits * T * N * 4);
@@ -247,6 +262,8 @@ CacheRef cache_ref(const mla_config *c, const mla_cache *k, int32_t batch) {
   r.max_blocks = k->max_blocks_per_seq;
   r.max_len = k->max_len;
   r.d_row = c->d_c + c->d_rope;
+  r.row_bytes = (int)row_bytes(c);
+  r.fp8 = cache_fp8(c) ? 1 : 0;
   r.bs_shift = -1;
   for (int sh = 0; sh < 31; ++sh)
     if ((1 << sh) == r.block_size) r.bs_shift = sh;
@@ -303,6 +320,7 @@ hipError_t run_compress(const mla_config *c, const mla_weights *w, const void *h
   a.w_end[nw++] = N;
   a.nw = nw;
   a.ldw = c->d_model;
+  const bool fp8 = cache_fp8(c);
   Seg s1 = seg_plain(off + c->d_c, nullptr, 0);
   s1.kind = SEG_CACHE;
   s1.col_off = 0;
@@ -315,6 +333,14 @@ hipError_t run_compress(const mla_config *c, const mla_weights *w, const void *h
   s2.col_off = c->d_c;
   s2.dst2 = kr_mirror;
   s2.ld2 = c->d_rope;
+  if (fp8) {
+    // the FP8 row needs its group maxima first: c_KV and k_R go to the
+    // mirrors, and the append kernel quantises and writes the rows
+    s1 = seg_plain(off + c->d_c, ckv_mirror, c->d_c);
+    s2 = seg_plain(N, kr_mirror, c->d_rope);
+    s2.rope = 1;
+    s2.head_w = c->d_rope;
+  }
   a.epi.seg[ns++] = s1;
   a.epi.seg[ns++] = s2;
   a.epi.nseg = ns;
@@ -326,7 +352,17 @@ hipError_t run_compress(const mla_config *c, const mla_weights *w, const void *h
   a.partial = partial;
   a.name = with_q ? "q_kv_down" : "kv_compress";
   a.reduce_name = "q_kv_down.reduce";
-  return launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 1, 0, a, st);
+  hipError_t e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 1, 0, a, st);
+  if (e != hipSuccess || !fp8) return e;
+  CacheAppendArgs ap;
+  ap.ckv = (const bf16 *)ckv_mirror;
+  ap.kr = (const bf16 *)kr_mirror;
+  ap.T = M;
+  ap.d_c = c->d_c;
+  ap.d_rope = c->d_rope;
+  ap.rows = rows;
+  ap.cache = a.epi.cache;
+  return launch_cache_append_fp8(ap, st);
 }
 
 // q = c_Q [W_UQ; W_QR]^T with RoPE on the q_R part.  The content part goes to
@@ -424,7 +460,7 @@ extern "C" {
 
 size_t mla_cache_bytes_per_token(const mla_config *cfg) {
   if (check_config(cfg) != MLA_OK) return 0;
-  return (size_t)(cfg->d_c + cfg->d_rope) * esize(cfg);
+  return row_bytes(cfg);
 }
 
 size_t mla_mha_cache_elements_per_token(const mla_config *cfg) {
@@ -459,6 +495,7 @@ mla_status mla_compress_kv(const mla_config *cfg, const mla_weights *w, const vo
   if (!h || !seq_idx || !pos) return MLA_ERR_NULL;
   if (n <= 0 || batch <= 0) return MLA_ERR_SHAPE;
   if ((s = check_cache(cache, batch, 1)) != MLA_OK) return s;
+  if (cache_fp8(cfg)) return MLA_ERR_UNSUPPORTED;
   RowMap rows = {ROWS_EXPLICIT, 1, nullptr, seq_idx, pos};
   SplitK sk = {1, cfg->d_model};
   return hip_status(run_compress(cfg, w, h, n, rows, cache, batch, false, nullptr, nullptr, nullptr, sk, nullptr,
@@ -477,6 +514,7 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
   if (T > (1L << 24)) return MLA_ERR_UNSUPPORTED;
   if (!attention_supported(cfg, MLA_OP_PREFILL)) return MLA_ERR_UNSUPPORTED;
   if ((s = check_cache(cache, batch, len)) != MLA_OK) return s;
+  if (cache_fp8(cfg) && cache->block_table && cache->block_size % 32) return MLA_ERR_UNSUPPORTED;
   const PrefillPlan p = plan_prefill(cfg, T);
   if (!workspace) return MLA_ERR_WORKSPACE;
   if (workspace_bytes < p.total) return MLA_ERR_WORKSPACE;
@@ -562,6 +600,7 @@ mla_status check_decode(const mla_config *cfg, const mla_weights *w, const void 
   if ((int64_t)batch * n_q > (1L << 20) || (int64_t)n_q * cfg->n_heads > (1L << 20)) return MLA_ERR_UNSUPPORTED;
   if (!attention_supported(cfg, MLA_OP_DECODE)) return MLA_ERR_UNSUPPORTED;
   if ((s = check_cache(cache, batch, max_cache_len)) != MLA_OK) return s;
+  if (cache_fp8(cfg) && cache->block_table && cache->block_size % 32) return MLA_ERR_UNSUPPORTED;
   *plan = plan_decode(cfg, batch, n_q, max_cache_len);
   return MLA_OK;
 }
@@ -579,7 +618,9 @@ mla_status decode_steps(const mla_config *cfg, const mla_weights *w, const void 
   void *o = o_heads ? o_heads : (void *)(ws + p.o);
   hipError_t e;
 
-  e = run_compress(cfg, w, h, M, rows, cache, batch, true, ws + p.c_q, nullptr, nullptr, p.sk1, partial, st);
+  const bool fp8 = cache_fp8(cfg);
+  e = run_compress(cfg, w, h, M, rows, cache, batch, true, ws + p.c_q, fp8 ? ws + p.ckv : nullptr,
+                   fp8 ? ws + p.kr : nullptr, p.sk1, partial, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
   if (dt == MLA_BF16 && decode_q_supported(cfg->d_cq, cfg->d_nope, cfg->d_rope, cfg->d_c, M)) {
     // up-projection, RoPE and absorption in one launch

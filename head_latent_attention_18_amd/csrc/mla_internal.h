@@ -81,10 +81,12 @@ struct CacheRef {
   int block_size;
   int max_blocks;
   int max_len;
-  int d_row;          // elements per cached row
+  int d_row;          // elements per cached row (layer-dtype rows)
   int batch;          // sequences the descriptor covers
   long cap;           // positions per sequence: max_len, or max_blocks * block_size
   int bs_shift;       // log2(block_size) when it is a power of two, else -1
+  int row_bytes;      // bytes per cached row
+  int fp8;            // rows in the FP8 layout: d_c E4M3 codes | d_R bf16 | d_c/128 fp32 scales
 };
 
 __device__ inline int block_of(const CacheRef &c, int pos) {
@@ -381,6 +383,18 @@ hipError_t launch_decode_combine(int dtype, const DecodeArgs &a, hipStream_t st)
 // bf16 split combine fused with o = W_UV o_lat (hipErrorNotSupported outside
 // d_c = 512, d_R = 64, d_v = 128: then combine and un-absorb run separately)
 hipError_t launch_decode_combine_uv(const DecodeArgs &a, int d_v, const void *w_uv, void *o, hipStream_t st);
+
+// FP8 cache append: token m's c_KV (ckv[m][0:d_c], bf16) and RoPE key
+// (kr[m][0:d_rope], bf16) are quantised (a scale per 128 columns) and written
+// to row (seq, pos) of the cache as the RowMap gives it.
+struct CacheAppendArgs {
+  const bf16 *ckv;
+  const bf16 *kr;
+  int T, d_c, d_rope;
+  RowMap rows;
+  CacheRef cache;
+};
+hipError_t launch_cache_append_fp8(const CacheAppendArgs &a, hipStream_t st);
 
 // kernel timing hooks (implemented with the C ABI)
 void timing_before(const char *name, hipStream_t st);

@@ -27,6 +27,7 @@ class CacheBuf:
 
     @staticmethod
     def contiguous(d_row: int, tdtype, batch: int, max_len: int, device="cuda") -> "CacheBuf":
+        """d_row: elements per row of tdtype (FP8 rows: bytes, tdtype uint8)."""
         pool = torch.zeros(batch * max_len, d_row, dtype=tdtype, device=device)
         return CacheBuf(pool, L.make_cache(pool, max_len=max_len), max_len=max_len)
 
@@ -53,20 +54,23 @@ class CacheBuf:
 class MlaLayer:
     """One MLA layer's weights on the device and the libmla calls on them."""
 
-    def __init__(self, dims, dtype: str, weights: Dict[str, torch.Tensor]):
-        self.dims, self.dtype = dims, dtype
+    def __init__(self, dims, dtype: str, weights: Dict[str, torch.Tensor], cache: str = "layer"):
+        self.dims, self.dtype, self.cache = dims, dtype, cache
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.weights = weights
-        self.cfg = L.make_config(dims, dtype)
+        self.cfg = L.make_config(dims, dtype, cache)
+        # a cache row: d_row elements of the layer dtype, or the FP8 row's bytes
+        self.row_width = L.mla_cache_bytes_per_token(self.cfg) if cache == "fp8" else dims.d_row
+        self.cache_tdtype = torch.uint8 if cache == "fp8" else self.tdtype
         self.cw = L.make_weights(weights)
         self._ws: Dict[str, torch.Tensor] = {}
 
     @classmethod
     def from_host(cls, dims, dtype: str, weights_f32: Dict[str, np.ndarray],
-                  weights_bits: Dict[str, Optional[np.ndarray]], device="cuda") -> "MlaLayer":
+                  weights_bits: Dict[str, Optional[np.ndarray]], device="cuda", cache: str = "layer") -> "MlaLayer":
         bf16 = dtype == "bf16"
         w = {k: upload(weights_f32[k], weights_bits.get(k), bf16, device) for k in L.WEIGHT_NAMES}
-        return cls(dims, dtype, w)
+        return cls(dims, dtype, w, cache)
 
     def workspace(self, key: str, nbytes: int, device) -> torch.Tensor:
         ws = self._ws.get(key)
@@ -76,7 +80,7 @@ class MlaLayer:
         return ws
 
     def new_cache(self, batch: int, max_len: int, device="cuda") -> CacheBuf:
-        return CacheBuf.contiguous(self.dims.d_row, self.tdtype, batch, max_len, device)
+        return CacheBuf.contiguous(self.row_width, self.cache_tdtype, batch, max_len, device)
 
     def prefill(self, h: torch.Tensor, cache: CacheBuf, want_o: bool = False, stream=None):
         B, S, _ = h.shape
@@ -108,17 +112,19 @@ class MlaLayer:
 def cache_from_rows(rows_per_seq, lens, d_row: int, bf16: bool, paged: bool = False, block_size: int = 64,
                     perm=None, max_len: Optional[int] = None, device="cuda") -> CacheBuf:
     """Device cache whose sequence b starts with the given rows (host arrays:
-    bf16 bit patterns as uint16, or float32).  Positions after them are zero.
-    Paged: logical block k of sequence b is physical block perm[offset_b + k]."""
+    bf16 bit patterns as uint16, float32, or FP8 rows as uint8 bytes with
+    d_row the row's bytes).  Positions after them are zero.  Paged: logical
+    block k of sequence b is physical block perm[offset_b + k]."""
     lens = np.asarray(lens, dtype=np.int64)
     B = len(rows_per_seq)
-    np_dtype = np.uint16 if bf16 else np.float32
+    raw = rows_per_seq[0].dtype == np.uint8
+    np_dtype = np.uint8 if raw else (np.uint16 if bf16 else np.float32)
     if not paged:
         ml = int(max_len or lens.max())
         pool = np.zeros((B * ml, d_row), dtype=np_dtype)
         for b in range(B):
             pool[b * ml: b * ml + rows_per_seq[b].shape[0]] = rows_per_seq[b]
-        t = upload(pool, pool, bf16, device)
+        t = torch.from_numpy(pool).to(device) if raw else upload(pool, pool, bf16, device)
         return CacheBuf(t, L.make_cache(t, max_len=ml), max_len=ml)
     bs = block_size
     nblk = [(int(l) + bs - 1) // bs for l in lens]
@@ -138,5 +144,5 @@ def cache_from_rows(rows_per_seq, lens, d_row: int, bf16: bool, paged: bool = Fa
         pos = np.arange(n)
         phys = table[b, pos // bs].astype(np.int64) * bs + pos % bs
         pool[phys] = rows_per_seq[b]
-    t = upload(pool, pool, bf16, device)
+    t = torch.from_numpy(pool).to(device) if raw else upload(pool, pool, bf16, device)
     return CacheBuf.paged(t, bs, table, device)

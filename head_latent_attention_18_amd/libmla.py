@@ -16,6 +16,7 @@ LIB_PATH = os.environ.get("MLA_LIBRARY") or os.path.join(os.path.dirname(os.path
                                                          "libmla.so")
 
 MLA_FP32, MLA_BF16 = 0, 1
+MLA_CACHE_LAYER, MLA_CACHE_FP8_E4M3 = 0, 1
 MLA_OP_PREFILL, MLA_OP_DECODE = 0, 1
 STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTYPE",
           -4: "MLA_ERR_WORKSPACE", -5: "MLA_ERR_CACHE", -6: "MLA_ERR_HIP", -7: "MLA_ERR_UNSUPPORTED"}
@@ -32,7 +33,7 @@ class mla_config(ctypes.Structure):
     _fields_ = [("d_model", c_int32), ("n_heads", c_int32), ("d_nope", c_int32), ("d_rope", c_int32),
                 ("d_v", c_int32), ("d_c", c_int32), ("d_cq", c_int32), ("dtype", c_int32),
                 ("rope_base", c_double), ("yarn_factor", c_double), ("yarn_beta_slow", c_double),
-                ("yarn_beta_fast", c_double), ("yarn_orig_len", c_int32)]
+                ("yarn_beta_fast", c_double), ("yarn_orig_len", c_int32), ("cache_dtype", c_int32)]
 
 
 class mla_weights(ctypes.Structure):
@@ -114,11 +115,12 @@ def _stream(stream) -> Optional[int]:
 # Struct builders
 # ---------------------------------------------------------------------------
 
-def make_config(dims, dtype: str) -> mla_config:
+def make_config(dims, dtype: str, cache: str = "layer") -> mla_config:
     return mla_config(dims.d_model, dims.n_heads, dims.d_nope, dims.d_rope, dims.d_v, dims.d_c, dims.d_cq,
                       MLA_BF16 if dtype == "bf16" else MLA_FP32, float(dims.rope_base),
                       float(getattr(dims, "yarn_factor", 1.0)), float(getattr(dims, "yarn_beta_slow", 1.0)),
-                      float(getattr(dims, "yarn_beta_fast", 32.0)), int(getattr(dims, "yarn_orig_len", 4096)))
+                      float(getattr(dims, "yarn_beta_fast", 32.0)), int(getattr(dims, "yarn_orig_len", 4096)),
+                      MLA_CACHE_FP8_E4M3 if cache == "fp8" else MLA_CACHE_LAYER)
 
 
 def make_weights(w: Dict[str, object]) -> mla_weights:

@@ -64,6 +64,27 @@ typedef enum mla_dtype {
   MLA_BF16 = 1   /* bfloat16 storage, float32 accumulation */
 } mla_dtype;
 
+/* Element format of the latent cache (mla_config.cache_dtype).
+ *   MLA_CACHE_LAYER: rows of (d_c + d_rope) elements in the layer dtype.
+ *   MLA_CACHE_FP8_E4M3: fine-grained FP8 (the FP8 framework of the V3
+ *     technical-report summary, "FP8 training framework" paragraph and
+ *     figure 7; the 18-highlights page, highlight 5): c_KV as E4M3 codes
+ *     (OCP 8-bit floating point) with one float32 scale per group of 128
+ *     consecutive columns, k_R in bf16.  A row is
+ *       d_c bytes of codes | d_rope bf16 values of k_R | d_c/128 float32 scales
+ *     (little-endian; 656 bytes for DeepSeek-V3 against 1152 in bf16), and
+ *     column c of c_KV is code[c] * scale[c/128].  Rows are written with
+ *     scale = (largest magnitude of the group) / 448 (1 for an all-zero
+ *     group) and each code the E4M3 value nearest to x / scale (ties to even).
+ *     Needs dtype MLA_BF16, d_c a multiple of 128 and d_rope of 8; a paged
+ *     cache's block_size must be a multiple of 32.  mla_compress_kv does not
+ *     support it (it has no workspace to stage a row before its scales are
+ *     known). */
+typedef enum mla_cache_dtype {
+  MLA_CACHE_LAYER = 0,
+  MLA_CACHE_FP8_E4M3 = 1
+} mla_cache_dtype;
+
 /* Layer dimensions.  Supported envelope (checked, MLA_ERR_UNSUPPORTED
  * otherwise): d_rope even; for BF16 d_model, d_cq, d_c multiples of 64,
  * d_nope, d_rope, d_v multiples of 32, n_heads*d_v a multiple of 64; for FP32
@@ -93,6 +114,7 @@ typedef struct mla_config {
   double yarn_beta_slow;
   double yarn_beta_fast;
   int32_t yarn_orig_len;
+  int32_t cache_dtype;  /* mla_cache_dtype; 0 (a zero-initialised config) = layer dtype */
 } mla_config;
 
 /* The eight projections, each row-major [out][in] in the config dtype:
@@ -104,8 +126,9 @@ typedef struct mla_weights {
   const void *w_dq, *w_uq, *w_qr, *w_dkv, *w_kr, *w_uk, *w_uv, *w_o;
 } mla_weights;
 
-/* Latent cache.  pool holds n_blocks*block_size rows of (d_c + d_rope)
- * elements in the config dtype.
+/* Latent cache.  pool holds n_blocks*block_size rows of
+ * mla_cache_bytes_per_token(cfg) bytes each ((d_c + d_rope) elements in the
+ * config dtype, or the FP8 row of mla_cache_dtype).
  *   Contiguous (block_table == NULL): position t of sequence b is row
  *     b*max_len + t; the pool must hold batch*max_len rows.
  *   Paged (block_table != NULL): block_table is int32 [batch][max_blocks_per_seq]
@@ -127,7 +150,8 @@ typedef struct mla_cache {
  * the latent c_KV and the decoupled key k_R, so a row is (d_c + d_rope)
  * elements of the cache's element type: 1152 bytes for DeepSeek-V3 in BF16
  * (against 2 * n_heads * d_nope elements for standard multi-head attention,
- * mla_mha_cache_elements_per_token).  Returns 0 for an invalid config. */
+ * mla_mha_cache_elements_per_token), 656 in MLA_CACHE_FP8_E4M3.  Returns 0
+ * for an invalid config. */
 size_t mla_cache_bytes_per_token(const mla_config *cfg);
 
 /* Elements a standard multi-head attention would cache per token:

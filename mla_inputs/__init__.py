@@ -169,6 +169,8 @@ class Workload:
     paged: bool = False
     block_size: int = 64
     block_perm: Optional[np.ndarray] = None        # physical block id of logical block k
+    cache_fp8: bool = False                        # cached rows in the FP8 layout
+    cache_fp8_rows: Optional[List[np.ndarray]] = None   # per sequence [lens[b]-n_q][row bytes] uint8
 
     @property
     def bf16(self) -> bool:
@@ -189,16 +191,46 @@ WORKLOADS = {
 }
 
 
+FP8_GROUP = 128   # columns of c_KV per scale in the FP8 cache rows
+
+
+def fp8_cache_rows(rng: np.random.Generator, n: int, d_c: int, d_rope: int, chunk: int = 1 << 16) -> np.ndarray:
+    """n cached rows in the FP8 cache layout, [n][d_c + 2*d_rope + 4*d_c/128]
+    uint8: E4M3 codes of c_KV, k_R as bf16 bits, then one float32 scale per
+    128 columns (little-endian).  Input data only: per row and group a scale
+    is drawn uniformly from [0.5, 1.5)/64 and the codes are those of N(0,1)
+    draws divided by it (clamped to +-448), cast by PyTorch's float8_e4m3fn
+    conversion; k_R is N(0,1) rounded to bf16.  The dequantised c_KV is then
+    close to N(0,1), as in the bf16 workloads."""
+    import torch
+    G = d_c // FP8_GROUP
+    out = np.empty((n, d_c + 2 * d_rope + 4 * G), dtype=np.uint8)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        m = e - s
+        x = rng.standard_normal((m, d_c), dtype=np.float32)
+        sc = ((0.5 + rng.random((m, G), dtype=np.float32)) / np.float32(64.0)).astype(np.float32)
+        q = np.clip(x.reshape(m, G, FP8_GROUP) / sc[:, :, None], -448.0, 448.0).reshape(m, d_c)
+        out[s:e, :d_c] = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float32)).to(
+            torch.float8_e4m3fn).view(torch.uint8).numpy()
+        _, kr_bits = _normal(rng, (m, d_rope), 1.0, True)
+        out[s:e, d_c:d_c + 2 * d_rope] = kr_bits.view(np.uint8).reshape(m, 2 * d_rope)
+        out[s:e, d_c + 2 * d_rope:] = sc.view(np.uint8).reshape(m, 4 * G)
+    return out
+
+
 def make_workload(wid: int, *, dims: Optional[Dims] = None, batch: Optional[int] = None,
                   seq_len: Optional[int] = None, uniform_len: Optional[int] = None,
                   ragged_max: Optional[int] = None, n_q: Optional[int] = None,
                   paged: Optional[bool] = None, block_size: Optional[int] = None,
                   dtype: Optional[str] = None, seed: Optional[int] = None,
-                  n_steps: Optional[int] = None, lengths=None, cache_rows: bool = True) -> Workload:
+                  n_steps: Optional[int] = None, lengths=None, cache_rows: bool = True,
+                  cache_fp8: bool = False) -> Workload:
     """Build workload ``wid`` (1..5).  Keyword overrides shrink or reshape it
     for tests; the seed stays 1000 + wid unless given.  ``lengths`` (decode
     workloads) fixes every sequence's cache length after the append (and the
-    batch)."""
+    batch).  ``cache_fp8`` (decode workloads) gives the cached rows in the
+    FP8 cache layout (``cache_fp8_rows``, fp8_cache_rows) instead of bf16."""
     spec = dict(WORKLOADS[wid])
     d = dims or spec["dims"]
     dt = dtype or spec["dtype"]
@@ -241,7 +273,10 @@ def make_workload(wid: int, *, dims: Optional[Dims] = None, batch: Optional[int]
     else:
         lens = np.full(B, ulen, dtype=np.int64)
     wl.lens = lens.astype(np.int32)
-    if cache_rows:
+    wl.cache_fp8 = cache_fp8
+    if cache_rows and cache_fp8:
+        wl.cache_fp8_rows = [fp8_cache_rows(rng, int(lens[b]) - nq, d.d_c, d.d_rope) for b in range(B)]
+    elif cache_rows:
         cf, cb = [], []
         for b in range(B):
             v, bb = _normal(rng, (int(lens[b]) - nq, d.d_row), 1.0, bf16)

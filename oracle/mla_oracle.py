@@ -51,6 +51,8 @@ __all__ = [
     "rope", "rope_freqs", "yarn_on", "compress_kv", "project_queries", "head_keys_values", "attend_head",
     "output_projection", "prefill", "decode", "decode_absorbed",
     "cache_elements_per_token", "mha_elements_per_token", "softmax_scale",
+    "E4M3_MAX", "FP8_GROUP", "e4m3_decode", "e4m3_encode", "quantize_latent", "fp8_row_bytes",
+    "dequantize_fp8_rows",
 ]
 
 
@@ -227,19 +229,27 @@ def prefill(dims, W, h, rows=None, heads=None, return_probs=False):
     return out
 
 
-def decode(dims, W, h, cache_rows, heads=None):
+def decode(dims, W, h, cache_rows, heads=None, cache_fp8=False):
     """n_q new tokens h [n_q][d_model] appended to one sequence whose first
     cached rows ``cache_rows`` [L-n_q][d_c+d_R] (each [c_KV || k_R]) are given.
     The new tokens take positions L-n_q..L-1 and query i sees keys
     0..L-n_q+i.  Returns u [n_q][d_model] (None when heads is a subset),
-    o [n_q][n_h][d_v] and the new cache rows [n_q][d_c+d_R]."""
+    o [n_q][n_h][d_v] and the new cache rows [n_q][d_c+d_R] (before any
+    quantisation).  cache_fp8: the cache holds c_KV in FP8 (E4M3 with a scale
+    per group of FP8_GROUP columns), so the new tokens' c_KV is attended in
+    its quantised form, as every cached row is (``cache_rows`` are then the
+    dequantised rows, dequantize_fp8_rows)."""
     h = _f64(h)
     cache_rows = _f64(cache_rows)
     n_q = h.shape[0]
     L = cache_rows.shape[0] + n_q
     qpos = np.arange(L - n_q, L)
     c_new, kr_new = compress_kv(W, h, qpos, dims)
-    c_kv = np.concatenate([cache_rows[:, :dims.d_c], c_new], axis=0)
+    c_att = c_new
+    if cache_fp8:
+        codes, scales = quantize_latent(c_new)
+        c_att = _dequantize_latent(codes, scales)
+    c_kv = np.concatenate([cache_rows[:, :dims.d_c], c_att], axis=0)
     k_r = np.concatenate([cache_rows[:, dims.d_c:], kr_new], axis=0)
     q_c, q_r = project_queries(W, h, qpos, dims)
     scale = softmax_scale(dims)
@@ -293,3 +303,92 @@ def cache_elements_per_token(dims):
 def mha_elements_per_token(dims):
     """Elements a standard multi-head attention caches: a key and a value per head."""
     return 2 * dims.n_heads * dims.d_nope
+
+
+# ---------------------------------------------------------------------------
+# FP8 latent cache (the FP8 framework of the V3 technical-report summary,
+# "FP8 training framework" paragraph and figure 7: values kept in FP8 with
+# fine-grained scaling, a scale per small group of elements, the group of 128
+# elements the figure's accumulation interval gives; the 18-highlights page,
+# highlight 5, FP8 for computation and storage).  Reading: a cached row keeps
+# c_KV as E4M3 codes with one fp32 scale per FP8_GROUP consecutive columns
+# (scale = the group's largest magnitude / 448, so that value maps to +-448;
+# an all-zero group takes scale 1), and k_R in the layer dtype.
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+FP8_GROUP = 128
+
+
+def e4m3_decode(codes):
+    """Values of E4M3 codes (OCP 8-bit floating point, E4M3: 1 sign, 4
+    exponent bits with bias 7, 3 mantissa bits; exponent field 0 encodes
+    subnormals m/8 * 2^-6; S.1111.111 is NaN; there is no infinity)."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.power(2.0, e - 7))
+    mag = np.where((e == 15) & ((c & 7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def _e4m3_magnitudes():
+    return e4m3_decode(np.arange(127))   # codes 0..126: every finite non-negative value, increasing
+
+
+def e4m3_encode(x):
+    """Nearest E4M3 code to each value, ties to the even code (round to
+    nearest even); magnitudes beyond 448 saturate to 448 (reading: the
+    format has no infinity and the quantiser never exceeds 448); NaN maps to
+    the NaN code; the sign of zero is kept."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    mags = _e4m3_magnitudes()
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 126)   # first value >= a
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    code = np.where(d_lo < d_hi, lo, hi)
+    tie = (d_lo == d_hi) & (lo != hi)
+    code = np.where(tie, np.where(lo % 2 == 0, lo, hi), code)
+    code = np.where(np.signbit(x), code | 0x80, code)
+    code = np.where(np.isnan(x), 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def quantize_latent(c_kv):
+    """c_KV rows [T][d_c] -> (codes [T][d_c] uint8, scales [T][d_c/FP8_GROUP]):
+    per group, scale = max|x| / 448 (1 for an all-zero group) and each value
+    takes the E4M3 code nearest to x / scale."""
+    c = _f64(c_kv)
+    T, d_c = c.shape
+    g = c.reshape(T, d_c // FP8_GROUP, FP8_GROUP)
+    amax = np.max(np.abs(g), axis=2)
+    scales = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+    codes = e4m3_encode(g / scales[:, :, None]).reshape(T, d_c)
+    return codes, scales
+
+
+def _dequantize_latent(codes, scales):
+    T, d_c = codes.shape
+    v = e4m3_decode(codes).reshape(T, d_c // FP8_GROUP, FP8_GROUP) * _f64(scales)[:, :, None]
+    return v.reshape(T, d_c)
+
+
+def fp8_row_bytes(dims):
+    """Bytes of one FP8 cache row: d_c codes, d_R bf16 values of k_R, and
+    d_c / FP8_GROUP fp32 scales, in that order."""
+    return dims.d_c + 2 * dims.d_rope + 4 * (dims.d_c // FP8_GROUP)
+
+
+def dequantize_fp8_rows(rows, dims):
+    """Cache rows as stored ([T][fp8_row_bytes] uint8, little-endian) ->
+    [T][d_c + d_R] float64: codes times their group's scale, then k_R."""
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.uint8))
+    T = r.shape[0]
+    d_c, d_r = dims.d_c, dims.d_rope
+    codes = r[:, :d_c]
+    kr_bits = r[:, d_c:d_c + 2 * d_r].copy().view(np.uint16).astype(np.uint32)
+    k_r = (kr_bits << np.uint32(16)).view(np.float32).astype(np.float64)
+    scales = r[:, d_c + 2 * d_r:].copy().view(np.float32).astype(np.float64)
+    return np.concatenate([_dequantize_latent(codes, scales), k_r.reshape(T, d_r)], axis=1)

@@ -62,19 +62,23 @@ def weights64(wl: Workload):
 
 
 def layer_for(wl: Workload) -> MlaLayer:
-    return MlaLayer.from_host(wl.dims, wl.dtype, wl.weights_f32, wl.weights_bits)
+    return MlaLayer.from_host(wl.dims, wl.dtype, wl.weights_f32, wl.weights_bits,
+                              cache="fp8" if getattr(wl, "cache_fp8", False) else "layer")
 
 
 def decode_cache(wl: Workload, layer: MlaLayer, max_len: int = None, paged: bool = None):
     """Device cache holding the workload's given rows; positions of the new
     tokens are left zero (the call writes them)."""
     paged = wl.paged if paged is None else paged
-    rows = [(wl.cache_bits[b] if wl.bf16 else wl.cache_f32[b]) for b in range(wl.batch)]
+    if getattr(wl, "cache_fp8", False):
+        rows = wl.cache_fp8_rows
+    else:
+        rows = [(wl.cache_bits[b] if wl.bf16 else wl.cache_f32[b]) for b in range(wl.batch)]
     perm = wl.block_perm
     if paged and perm is None:
         nblk = int(sum((int(l) + wl.block_size - 1) // wl.block_size for l in wl.lens))
         perm = np.random.Generator(np.random.PCG64(7)).permutation(nblk).astype(np.int32)
-    return cache_from_rows(rows, wl.lens, wl.dims.d_row, wl.bf16, paged=paged, block_size=wl.block_size,
+    return cache_from_rows(rows, wl.lens, layer.row_width, wl.bf16, paged=paged, block_size=wl.block_size,
                            perm=perm, max_len=max_len)
 
 
@@ -88,9 +92,37 @@ def run_decode(wl: Workload, layer: MlaLayer, cache: CacheBuf, max_len: int = No
     return out
 
 
+def oracle_cache_rows(wl: Workload, b: int):
+    """The cached rows of sequence b as the oracle takes them (float64; FP8
+    rows dequantised by the oracle)."""
+    if getattr(wl, "cache_fp8", False):
+        return O.dequantize_fp8_rows(wl.cache_fp8_rows[b], wl.dims)
+    return wl.cache_f32[b].astype(np.float64)
+
+
 def oracle_decode_seq(wl: Workload, b: int, heads=None):
     h = wl.h_f32[b].astype(np.float64)
-    return O.decode(wl.dims, weights64(wl), h, wl.cache_f32[b].astype(np.float64), heads=heads)
+    return O.decode(wl.dims, weights64(wl), h, oracle_cache_rows(wl, b), heads=heads,
+                    cache_fp8=getattr(wl, "cache_fp8", False))
+
+
+def assert_fp8_rows(got_bytes, ref_rows, dims, what: str):
+    """FP8 cache rows written by the GPU against the oracle's unquantised
+    rows [n][d_c + d_R]: every c_KV value within half an E4M3 step at its
+    group's scale (scale = group max / 448) of the oracle's value, plus the
+    bf16 rounding of the value before quantisation and of the scale's
+    computation (2^-8 relative); k_R within the bf16 bounds."""
+    got = O.dequantize_fp8_rows(got_bytes.detach().cpu().numpy(), dims)
+    ref = np.asarray(ref_rows, dtype=np.float64)
+    d_c = dims.d_c
+    g = ref[:, :d_c].reshape(ref.shape[0], -1, O.FP8_GROUP)
+    sc = np.max(np.abs(g), axis=2, keepdims=True) / O.E4M3_MAX
+    bound = sc * np.maximum(2.0 ** -4 * np.abs(g) / np.maximum(sc, 1e-300), 2.0 ** -10) + 2.0 ** -8 * np.abs(g) + 1e-6
+    diff = np.abs(got[:, :d_c].reshape(g.shape) - g)
+    worst = float(np.max(diff / bound)) if diff.size else 0.0
+    say(f"{what}: c_KV worst error / bound = {worst:.3f}")
+    assert worst <= 1.0, f"{what}: FP8 c_KV beyond the quantisation bound ({worst})"
+    assert_close(got[:, d_c:], ref[:, d_c:], True, f"{what} k_R")
 
 
 class Timer:

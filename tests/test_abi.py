@@ -40,6 +40,8 @@ def test_version_and_status_strings():
 
 def test_cache_bytes_closed_form():
     assert L.mla_cache_bytes_per_token(L.make_config(DSV3, "bf16")) == 1152
+    # FP8 rows: 512 codes + 64 bf16 k_R + 4 float32 scales
+    assert L.mla_cache_bytes_per_token(L.make_config(DSV3, "bf16", "fp8")) == 656
     assert L.mla_cache_bytes_per_token(L.make_config(DSV3, "fp32")) == 2304
     assert L.mla_cache_bytes_per_token(L.make_config(TINY, "fp32")) == 320
     assert L.mla_mha_cache_elements_per_token(L.make_config(DSV3, "bf16")) == 32768
@@ -96,6 +98,9 @@ CONFIG_CASES = [
     (dict(yarn_factor=40.0, yarn_orig_len=0), -2),
     (dict(yarn_factor=40.0, yarn_beta_slow=32.0, yarn_beta_fast=1.0), -2),
     (dict(yarn_factor=40.0, yarn_beta_slow=0.0), -2),
+    (dict(cache_dtype=1), 0),                                      # FP8 cache
+    (dict(cache_dtype=2), -3),
+    (dict(cache_dtype=1, d_c=576), -7),                            # not a multiple of 128
 ]
 
 
@@ -184,6 +189,22 @@ def test_decode_noalloc_validation():
     big = L.mla_workspace_size(cfg, L.MLA_OP_DECODE, 2, 300, 633)
     assert big > L.MLA_NOALLOC_WORKSPACE_BYTES
     assert call(B=2, nq=300, ml=633) == -4
+
+
+def test_fp8_cache_validation():
+    fp8 = L.make_config(DSV3, "bf16", "fp8")
+    f32 = L.make_config(TINY, "fp32", "fp8")
+    out = ctypes.c_size_t(0)
+    assert L.lib().mla_workspace_size(ctypes.byref(f32), 1, 1, 1, 8, ctypes.byref(out)) == -7   # fp32 layer
+    # paged blocks must hold whole 32-row tiles
+    assert _decode(cfg=fp8, cache=L.make_cache(FAKE, block_size=16, n_blocks=8, block_table=FAKE,
+                                               max_blocks_per_seq=8)) == -7
+    assert _prefill(cfg=fp8, cache=L.make_cache(FAKE, block_size=48, n_blocks=8, block_table=FAKE,
+                                                max_blocks_per_seq=8)) == -7
+    # the standalone compression has no workspace for the row's scales
+    w = _weights()
+    assert L.lib().mla_compress_kv(ctypes.byref(fp8), ctypes.byref(w), FAKE, 4, FAKE, FAKE, 1,
+                                   ctypes.byref(L.make_cache(FAKE, max_len=16)), None) == -7
 
 
 def test_compress_validation():

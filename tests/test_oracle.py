@@ -326,10 +326,123 @@ def pin_brute_force(dims=SMALL, L=4):
         assert np.allclose(got[t], u, rtol=1e-11, atol=1e-12)
 
 
+# ---------------------------------------------------------------------------
+# FP8 latent cache
+# ---------------------------------------------------------------------------
+
+def pin_e4m3_definition():
+    """E4M3 values from the OCP 8-bit floating-point definition, worked by
+    hand: bias 7, three mantissa bits, exponent field 0 for subnormals,
+    S.1111.111 the only NaN, largest finite 448."""
+    table = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x0F: 1.875 * 2.0 ** -6,
+             0x30: 0.5, 0x38: 1.0, 0x39: 1.125, 0x3F: 1.875, 0x40: 2.0, 0x58: 16.0, 0x7E: 448.0,
+             0x80: -0.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in table.items():
+        got = O.e4m3_decode(c)
+        assert got == v and np.signbit(got) == np.signbit(v), (hex(c), got, v)
+    vals = O.e4m3_decode(np.arange(256))
+    assert np.isnan(vals[0x7F]) and np.isnan(vals[0xFF]) and np.sum(np.isnan(vals)) == 2
+    assert np.max(vals[~np.isnan(vals)]) == O.E4M3_MAX
+
+
+def pin_e4m3_rounding():
+    """Encoding: every finite code round-trips; a value halfway between two
+    neighbours goes to the one with the even code; just off the midpoint it
+    goes to the nearer; beyond 448 it saturates."""
+    vals = O.e4m3_decode(np.arange(256))
+    fin = np.where(~np.isnan(vals))[0]
+    assert np.array_equal(O.e4m3_encode(vals[fin]), fin.astype(np.uint8))
+    mags = O.e4m3_decode(np.arange(127))
+    mid = (mags[:-1] + mags[1:]) / 2
+    even = np.where(np.arange(126) % 2 == 0, np.arange(126), np.arange(1, 127))
+    assert np.array_equal(O.e4m3_encode(mid), even.astype(np.uint8))
+    assert np.array_equal(O.e4m3_encode(mid * (1 - 1e-9)), np.arange(126).astype(np.uint8))
+    assert np.array_equal(O.e4m3_encode(mid * (1 + 1e-9)), np.arange(1, 127).astype(np.uint8))
+    assert O.e4m3_encode(1000.0) == 0x7E and O.e4m3_encode(-470.0) == 0xFE
+    # 1.0625 lies halfway between 1 (0x38) and 1.125 (0x39): the even code
+    assert O.e4m3_encode(1.0625) == 0x38 and O.e4m3_encode(1.1875) == 0x3A
+
+
+def pin_e4m3_library():
+    """The codec against PyTorch's float8_e4m3fn (a library implementation
+    of the same format): every code's value, and the codes of random values
+    within range."""
+    codes = np.arange(256)
+    ref = torch.tensor(codes, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = O.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)) and np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    x = np.random.Generator(np.random.PCG64(41)).standard_normal(20000).astype(np.float32) * 60
+    x = np.clip(x, -448, 448)
+    ref_codes = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(x.astype(np.float64)), ref_codes)
+
+
+def pin_quantize_latent_bound():
+    """Per group of 128 columns the largest magnitude maps to +-448 exactly,
+    and every dequantised value lies within half a code step of the input:
+    |x' - x| <= s * max(2^-4 |x/s|, 2^-10) (normal and subnormal spacing);
+    an all-zero group stays zero."""
+    rng = np.random.Generator(np.random.PCG64(43))
+    c = rng.standard_normal((7, 256)) * np.exp(rng.standard_normal((7, 1)) * 3)
+    c[3, 128:] = 0.0
+    codes, scales = O.quantize_latent(c)
+    assert codes.shape == (7, 256) and scales.shape == (7, 2)
+    deq = O.e4m3_decode(codes).reshape(7, 2, 128) * scales[:, :, None]
+    g = c.reshape(7, 2, 128)
+    bound = scales[:, :, None] * np.maximum(2.0 ** -4 * np.abs(g) / scales[:, :, None], 2.0 ** -10)
+    assert np.all(np.abs(deq - g) <= bound * (1 + 1e-12))
+    for t in range(7):
+        for k in range(2):
+            if np.any(g[t, k]):
+                j = np.argmax(np.abs(g[t, k]))
+                assert abs(deq[t, k, j]) == abs(g[t, k, j])   # the group's extreme is exact
+    assert np.all(deq[3, 1] == 0.0)
+
+
+def pin_fp8_row_layout():
+    """A stored FP8 row, assembled byte by byte here: codes, k_R in bf16,
+    then the little-endian fp32 scales; 656 bytes for DeepSeek-V3 widths."""
+    assert O.fp8_row_bytes(DSV3) == 512 + 128 + 16
+    d = Dims(d_model=8, n_heads=1, d_nope=2, d_rope=2, d_v=2, d_c=128, d_cq=4)
+    row = np.zeros(O.fp8_row_bytes(d), dtype=np.uint8)
+    row[0] = 0x38          # 1.0
+    row[127] = 0xC0        # -2.0
+    row[128:130] = np.frombuffer(np.float32(3.0).tobytes()[2:], dtype=np.uint8)     # bf16 3.0
+    row[130:132] = np.frombuffer(np.float32(-0.5).tobytes()[2:], dtype=np.uint8)    # bf16 -0.5
+    row[132:136] = np.frombuffer(np.float32(0.25).tobytes(), dtype=np.uint8)        # scale
+    got = O.dequantize_fp8_rows(row[None], d)[0]
+    assert got.shape == (130,)
+    assert got[0] == 0.25 and got[127] == -0.5 and np.all(got[1:127] == 0)
+    assert got[128] == 3.0 and got[129] == -0.5
+
+
+def pin_decode_fp8_new_rows():
+    """With an FP8 cache the new tokens attend to their own c_KV in quantised
+    form: a one-token sequence (only its own key) gives o_i = W_UV,i c_KV',
+    c_KV' the quantise-dequantise of c_KV."""
+    d = dataclasses_replace(TINY, d_c=128)
+    W = _weights(d, 44)
+    x = _h(1, d, 45)
+    r = O.decode(d, W, x, np.zeros((0, d.d_row)), cache_fp8=True)
+    c = x @ W["w_dkv"].T
+    codes, scales = O.quantize_latent(c)
+    cq = O.e4m3_decode(codes) * np.repeat(scales, 128, axis=1)
+    for i in range(d.n_heads):
+        v = W["w_uv"][i * d.d_v:(i + 1) * d.d_v] @ cq[0]
+        assert np.allclose(r["o"][0, i], v, rtol=1e-13, atol=1e-13)
+    assert not np.allclose(cq, c, rtol=1e-6, atol=0)   # the quantisation is visible
+
+
+def dataclasses_replace(d, **kw):
+    import dataclasses
+    return dataclasses.replace(d, **kw)
+
+
 ALL_PINS = [pin_absorbed_equals_plain, pin_softmax_rows, pin_causal, pin_single_key,
             pin_zero_query, pin_head_isolation, pin_mha_special_case, pin_rope_rotation, pin_rope_in_scores,
             pin_yarn_frequencies, pin_yarn_in_scores, pin_yarn_blend_hand_worked, pin_prefill_decode_agree,
-            pin_brute_force]
+            pin_e4m3_definition, pin_e4m3_rounding, pin_e4m3_library, pin_quantize_latent_bound,
+            pin_fp8_row_layout, pin_decode_fp8_new_rows, pin_brute_force]
 
 
 # ---------------------------------------------------------------------------

@@ -137,6 +137,42 @@ def _ckv_kr_unroped(W, h, pos, dims):
     return c, np.asarray(h, dtype=np.float64) @ np.asarray(W["w_kr"], dtype=np.float64).T
 
 
+_dec8 = O.e4m3_decode
+_enc8 = O.e4m3_encode
+_quant = O.quantize_latent
+
+
+def _e4m3_bias8(codes):
+    # the exponent bias of the other common 8-bit format (8 instead of 7)
+    return _dec8(codes) / 2.0
+
+
+def _e4m3_truncate(x):
+    # truncation towards zero instead of round to nearest even
+    x = np.asarray(x, dtype=np.float64)
+    mags = O.e4m3_decode(np.arange(127))
+    a = np.minimum(np.abs(x), O.E4M3_MAX)
+    code = np.clip(np.searchsorted(mags, a, side="right") - 1, 0, 126)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+def _quant_scale_240(c_kv):
+    # scale against 240 (another format's largest value) instead of 448
+    codes, scales = _quant(np.asarray(c_kv) * (240.0 / 448.0))
+    return codes, scales * (448.0 / 240.0)
+
+
+def _quant_group_64(c_kv):
+    # groups of 64 columns, one scale each, but the stored scale of the first
+    c = np.asarray(c_kv, dtype=np.float64)
+    T, d_c = c.shape
+    g = c.reshape(T, d_c // 64, 64)
+    amax = np.max(np.abs(g), axis=2)
+    sc = np.where(amax > 0, amax / 448.0, 1.0)
+    codes = _enc8(g / sc[:, :, None]).reshape(T, d_c)
+    return codes, sc[:, ::2]
+
+
 MUTATIONS = {
     "rope_sign": ("rope", _rope_sign),
     "rope_frequency": ("rope", _rope_freq),
@@ -159,6 +195,10 @@ MUTATIONS = {
     "yarn_no_interpolation": ("rope_freqs", lambda d: _freqs(dataclasses.replace(d, yarn_factor=1.0))),
     "yarn_no_temperature": ("softmax_scale", _yarn_no_temperature),
     "yarn_temperature_unsquared": ("softmax_scale", _yarn_temperature_unsquared),
+    "e4m3_bias8": ("e4m3_decode", _e4m3_bias8),
+    "e4m3_truncate": ("e4m3_encode", _e4m3_truncate),
+    "fp8_scale_240": ("quantize_latent", _quant_scale_240),
+    "fp8_group_64": ("quantize_latent", _quant_group_64),
 }
 
 

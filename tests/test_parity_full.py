@@ -99,3 +99,41 @@ def test_full_decode_len131072_nq2(yarn):
     u, o = run_decode(wl, layer, cache)
     _decode_seq_check(wl, u, o, cache, seqs=[3])
     _decode_seq_check(wl, u, o, cache, seqs=[0, 1, 2], heads=[0, 57, 127])
+
+
+def _fp8_full(wid, seqs, heads_seqs=(), heads=None):
+    with Timer(f"draw workload {wid} (FP8 cache)"):
+        wl = make_workload(wid, cache_fp8=True)
+    layer = layer_for(wl)
+    with Timer("build cache"):
+        cache = decode_cache(wl, layer)
+    say(f"fp8 full decode workload {wid}")
+    u, o = run_decode(wl, layer, cache)
+    d = wl.dims
+    B, nq = wl.batch, wl.n_q
+    for b in list(seqs) + list(heads_seqs):
+        hs = heads if b in heads_seqs else None
+        with Timer(f"oracle fp8 decode b={b} len={wl.lens[b]}"):
+            ref = O.decode(d, weights64(wl), wl.h_f32[b].astype(np.float64),
+                           O.dequantize_fp8_rows(wl.cache_fp8_rows[b], d), heads=hs, cache_fp8=True)
+        ob = o.view(B, nq, d.n_heads, d.d_v)[b]
+        if hs is None:
+            assert_close(u[b], ref["u"], True, f"fp8 u b={b}")
+            assert_close(ob, ref["o"], True, f"fp8 o b={b}")
+        else:
+            hsel = torch.tensor(hs, device=ob.device)
+            assert_close(ob.index_select(1, hsel), ref["o"][:, hs], True, f"fp8 o b={b} heads={hs}")
+
+
+def test_full_fp8_decode_b32_len4096():
+    _fp8_full(2, seqs=[0, 31])
+
+
+def test_full_fp8_decode_ragged_paged_b128():
+    wl_lens = make_workload(4, cache_rows=False).lens
+    order = np.argsort(wl_lens)
+    _fp8_full(4, seqs=sorted({int(order[0]), int(order[-1]), 64}))
+
+
+def test_full_fp8_decode_len131072_nq2():
+    _fp8_full(5, seqs=[1], heads_seqs=[0, 3], heads=[0, 127])
