@@ -12,8 +12,10 @@ Infinity Cache.
 
 Also reported: per-kernel times from HIP events recorded by the library on
 the launch stream, the roofline of the dominant kernel, a causal prefill of
-4096 tokens (TFLOPS against the bf16 MFMA peak), a sampled parity check, and
-the CPU oracle's throughput on a bounded sample (cpu_baseline).
+4096 tokens (TFLOPS against the bf16 MFMA peak), the ragged paged batch-128
+and 128K two-token decode workloads, the three decode workloads again with
+the FP8 (E4M3 + per-128-column scale) latent cache, a sampled parity check,
+and the CPU oracle's throughput on a bounded sample (cpu_baseline).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -34,17 +36,20 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def decode_kernel_bytes(d, B, n_q, sum_len, e=2):
+def decode_kernel_bytes(d, B, n_q, sum_len, e=2, row_bytes=None):
     """Algorithmic HBM bytes per launch of each decode kernel (weights and
-    cache read once, activations read/written once)."""
+    cache read once, activations read/written once); row_bytes is the size
+    of a cached row (e * (d_c + d_R) for a cache in the layer dtype, 656 for
+    the FP8 cache)."""
     T = B * n_q
     nh = d.n_heads
     D = d.d_c + d.d_rope
+    rb = e * D if row_bytes is None else row_bytes
     return {
         "q_kv_down": e * ((d.d_cq + D) * d.d_model + T * d.d_model + T * d.d_cq + T * D),
         "q_up": e * (nh * (d.d_nope + d.d_rope) * d.d_cq + T * d.d_cq + T * nh * (d.d_nope + d.d_rope)),
         "absorb": e * (nh * d.d_nope * d.d_c + T * nh * d.d_nope + T * nh * d.d_c),
-        "decode_attn": e * (sum_len * D + T * nh * D),
+        "decode_attn": sum_len * rb + e * T * nh * D,
         "decode_combine": e * T * nh * d.d_c,
         "unabsorb": e * (nh * d.d_v * d.d_c + T * nh * d.d_c + T * nh * d.d_v),
         "decode_combine_uv": e * (nh * d.d_v * d.d_c + T * nh * d.d_c + T * nh * d.d_v),
@@ -54,11 +59,12 @@ def decode_kernel_bytes(d, B, n_q, sum_len, e=2):
     }
 
 
-def decode_step_bytes(d, B, n_q, sum_len, e=2):
+def decode_step_bytes(d, B, n_q, sum_len, e=2, row_bytes=None):
     """Whole decode step: every weight once, every cached row once, h in, u out."""
     nparams = (d.d_cq * d.d_model + d.n_heads * (d.d_nope + d.d_rope) * d.d_cq + (d.d_c + d.d_rope) * d.d_model
                + d.n_heads * (d.d_nope + d.d_v) * d.d_c + d.d_model * d.n_heads * d.d_v)
-    return e * (nparams + sum_len * (d.d_c + d.d_rope) + 2 * B * n_q * d.d_model)
+    rb = e * (d.d_c + d.d_rope) if row_bytes is None else row_bytes
+    return e * (nparams + 2 * B * n_q * d.d_model) + sum_len * rb
 
 
 def prefill_flops(d, B, L):
@@ -171,51 +177,91 @@ def decode_attn_flops(d, lens, n_q):
     return vis * d.n_heads * 2 * ((d.d_c + d.d_rope) + d.d_c)
 
 
-def run_decode_workload(args, dev, wid):
-    """Decode step of workload 4 (batch 128, lengths U{1..32768}, paged
-    64-row blocks in a permuted order) or 5 (batch 4, 128K cache, two query
-    tokens).  Lengths, block order, weights and h come from the workload's
-    seed; the cached rows (2.5 GB and 0.6 GB) are drawn N(0,1) on the device
-    from a seeded torch generator and rounded to bf16."""
+def device_cache_rows(d, n, gen, dev, fp8):
+    """n cached rows drawn on the device from a seeded generator: bf16
+    N(0,1) rows, or FP8 rows by the recipe of mla_inputs.fp8_cache_rows
+    (scales 2^-7, 2^-6 or 2^-5 per row and 128-column group, codes of N(0,1)
+    draws divided by the scale, clamped to +-448; k_R N(0,1) in bf16)."""
+    import torch
+    if not fp8:
+        out = torch.empty(n, d.d_row, dtype=torch.bfloat16, device=dev)
+        for s in range(0, n, 1 << 18):
+            e = min(n, s + (1 << 18))
+            out[s:e] = torch.empty(e - s, d.d_row, device=dev).normal_(generator=gen).to(torch.bfloat16)
+        return out
+    G = d.d_c // 128
+    out = torch.empty(n, d.d_c + 2 * d.d_rope + 4 * G, dtype=torch.uint8, device=dev)
+    for s in range(0, n, 1 << 18):
+        e = min(n, s + (1 << 18))
+        m = e - s
+        x = torch.empty(m, G, 128, device=dev).normal_(generator=gen)
+        sc = torch.ldexp(torch.ones(m, G, device=dev),
+                         torch.randint(-7, -4, (m, G), generator=gen, device=dev)).contiguous()
+        q = (x / sc[:, :, None]).clamp_(-448.0, 448.0).reshape(m, d.d_c)
+        out[s:e, :d.d_c] = q.to(torch.float8_e4m3fn).view(torch.uint8)
+        kr = torch.empty(m, d.d_rope, device=dev).normal_(generator=gen).to(torch.bfloat16).contiguous()
+        out[s:e, d.d_c:d.d_c + 2 * d.d_rope] = kr.view(torch.uint8)
+        out[s:e, d.d_c + 2 * d.d_rope:] = sc.view(torch.uint8)
+    return out
+
+
+def run_decode_workload(args, dev, wid, cache_kind="layer"):
+    """Decode step of workload 2 (batch 32, cache 4096), 4 (batch 128,
+    lengths U{1..32768}, paged 64-row blocks in a permuted order) or 5
+    (batch 4, 128K cache, two query tokens), with a bf16 or an FP8 latent
+    cache.  Lengths, block order, weights and h come from the workload's
+    seed; the cached rows (workload 4: 2.5 GB bf16, 1.4 GB FP8) are drawn on
+    the device from a seeded torch generator (device_cache_rows).  Workload 2
+    rotates --sets copies of weights and cache so that neither stays in the
+    Infinity Cache."""
     import numpy as np
     import torch
     from head_latent_attention_18_amd import libmla as L
     from head_latent_attention_18_amd.layer import CacheBuf, MlaLayer, upload
     from mla_inputs import make_workload
     t0 = time.perf_counter()
+    fp8 = cache_kind == "fp8"
     wl = make_workload(wid, cache_rows=False)
     d = wl.dims
     B, nq = wl.batch, wl.n_q
     lens_np = wl.lens.astype(np.int32)
-    layer = MlaLayer.from_host(d, "bf16", wl.weights_f32, wl.weights_bits)
+    layer = MlaLayer.from_host(d, "bf16", wl.weights_f32, wl.weights_bits, cache=cache_kind)
     gen = torch.Generator(device=dev)
-    gen.manual_seed(1000 + wid)
-    if wl.paged:
-        bs = wl.block_size
-        nblk = int(sum((int(l) + bs - 1) // bs for l in lens_np))
-        maxb = int(max((int(l) + bs - 1) // bs for l in lens_np))
-        table = np.full((B, maxb), -1, dtype=np.int32)
-        off = 0
-        for b in range(B):
-            n = (int(lens_np[b]) + bs - 1) // bs
-            table[b, :n] = wl.block_perm[off:off + n]
-            off += n
-        pool = torch.empty(nblk * bs, d.d_row, dtype=torch.float32, device=dev).normal_(generator=gen)
-        cache = CacheBuf.paged(pool.to(torch.bfloat16), bs, table)
-        del pool
-    else:
+    gen.manual_seed(1000 + wid + (500 if fp8 else 0))
+
+    def new_cache():
+        if wl.paged:
+            bs = wl.block_size
+            nblk = int(sum((int(l) + bs - 1) // bs for l in lens_np))
+            maxb = int(max((int(l) + bs - 1) // bs for l in lens_np))
+            table = np.full((B, maxb), -1, dtype=np.int32)
+            off = 0
+            for b in range(B):
+                n = (int(lens_np[b]) + bs - 1) // bs
+                table[b, :n] = wl.block_perm[off:off + n]
+                off += n
+            return CacheBuf.paged(device_cache_rows(d, nblk * bs, gen, dev, fp8), bs, table)
         ml = int(lens_np.max())
-        pool = torch.empty(B * ml, d.d_row, dtype=torch.float32, device=dev).normal_(generator=gen)
-        cache = CacheBuf(pool.to(torch.bfloat16), None, max_len=ml)
-        cache.desc = L.make_cache(cache.pool, max_len=ml)
-        del pool
+        c = CacheBuf(device_cache_rows(d, B * ml, gen, dev, fp8), None, max_len=ml)
+        c.desc = L.make_cache(c.pool, max_len=ml)
+        return c
+
     h = upload(wl.h_f32, wl.h_bits, True)
+    sets = [(layer, new_cache(), h)]
+    for _ in range((args.sets if wid == 2 else 1) - 1):
+        lw = MlaLayer(d, "bf16", {k: v.clone() for k, v in layer.weights.items()}, cache=cache_kind)
+        sets.append((lw, new_cache(), h.clone()))
     lens = torch.from_numpy(lens_np).to(dev)
     Lmax = int(lens_np.max())
     u = torch.empty(B, nq, d.d_model, dtype=torch.bfloat16, device=dev)
-    run = lambda i: layer.decode(h, lens, Lmax, cache, u=u, lens_host=lens_np)
+
+    def run(i):
+        lw, c, hh = sets[i % len(sets)]
+        lw.decode(hh, lens, Lmax, c, u=u, lens_host=lens_np)
+
     torch.cuda.synchronize()
-    log(f"workload {wl.name}: set up in {time.perf_counter() - t0:.1f}s, sum of lengths {int(lens_np.sum())}")
+    name = wl.name + ("-fp8cache" if fp8 else "")
+    log(f"workload {name}: set up in {time.perf_counter() - t0:.1f}s, sum of lengths {int(lens_np.sum())}")
     for i in range(5):
         run(i)
     torch.cuda.synchronize()
@@ -224,18 +270,20 @@ def run_decode_workload(args, dev, wid):
     dt = st["ms_median"] * 1e-3
     kt = kernel_times(run, k)
     sum_len = int(lens_np.sum())
-    step_bytes = decode_step_bytes(d, B, nq, sum_len)
-    kb = decode_kernel_bytes(d, B, nq, sum_len)["decode_attn"]
+    rb = layer.row_width * (1 if fp8 else 2)
+    step_bytes = decode_step_bytes(d, B, nq, sum_len, row_bytes=rb)
+    kb = decode_kernel_bytes(d, B, nq, sum_len, row_bytes=rb)["decode_attn"]
     attn_fl = decode_attn_flops(d, lens_np, nq)
     attn_ms = kt["decode_attn"]["avg_ms"]
     t_hbm = kb / (HBM_PEAK_GBS * 1e9)
     t_mfma = attn_fl / (BF16_PEAK_TFLOPS * 1e12)
     bound = "mfma" if t_mfma > t_hbm else "hbm"
-    log(f"{wl.name}: median {dt * 1e6:.1f} us/step, attention {attn_ms * 1e3:.1f} us (event-timed), "
+    log(f"{name}: median {dt * 1e6:.1f} us/step, attention {attn_ms * 1e3:.1f} us (event-timed), "
         f"bound {bound} {max(t_hbm, t_mfma) * 1e6:.1f} us")
-    del cache, layer
+    del sets, layer
     torch.cuda.empty_cache()
-    return {"workload": wl.name, "batch": B, "n_q": nq, "sum_len": sum_len, "max_len": Lmax, "paged": wl.paged,
+    return {"workload": name, "batch": B, "n_q": nq, "sum_len": sum_len, "max_len": Lmax, "paged": wl.paged,
+            "cache": cache_kind, "cache_row_bytes": rb,
             **st, "tokens_per_s": round(B * nq / dt, 1),
             "step_hbm": {"alg_bytes": step_bytes, "GBps": round(step_bytes / dt / 1e9, 1),
                          "frac": round(step_bytes / dt / 1e9 / HBM_PEAK_GBS, 4)},
@@ -303,6 +351,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="least CPU time of the timed oracle sample")
     ap.add_argument("--only", choices=["all", "decode", "prefill", "chunk", "ragged", "long"], default="all",
                     help="profiling runs: time one path only (the JSON line is printed for 'all' and 'decode')")
+    ap.add_argument("--cache", choices=["layer", "fp8"], default="layer",
+                    help="latent cache of the --only decode/ragged/long runs (fp8: E4M3 codes + group scales)")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache decode workloads")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only copy a buffer of this many MB three times (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -336,8 +387,9 @@ def main():
     if args.only == "chunk":
         print(json.dumps(run_chunk(args, dev)), flush=True)
         return
-    if args.only in ("ragged", "long"):
-        print(json.dumps(run_decode_workload(args, dev, 4 if args.only == "ragged" else 5)), flush=True)
+    if args.only in ("ragged", "long") or (args.only == "decode" and args.cache == "fp8"):
+        wid = {"decode": 2, "ragged": 4, "long": 5}[args.only]
+        print(json.dumps(run_decode_workload(args, dev, wid, args.cache)), flush=True)
         return
 
     # ------------------------------------------------------------ decode
@@ -436,9 +488,15 @@ def main():
 
     prefill = None if (args.no_prefill or args.only == "decode") else run_prefill(args, dev)
     ragged = long_ctx = None
+    fp8 = None
     if args.only == "all" and not args.no_extra:
         ragged = run_decode_workload(args, dev, 4)
         long_ctx = run_decode_workload(args, dev, 5)
+    if args.only == "all" and not args.no_fp8:
+        fp8 = {"b32_len4096": run_decode_workload(args, dev, 2, "fp8")}
+        if not args.no_extra:
+            fp8["ragged"] = run_decode_workload(args, dev, 4, "fp8")
+            fp8["long"] = run_decode_workload(args, dev, 5, "fp8")
 
     out = {
         "metric": "MLA decode tokens/s (DeepSeek-V3 layer, batch 32, cache 4096)",
@@ -467,6 +525,7 @@ def main():
         "prefill": prefill,
         "decode_ragged": ragged,
         "decode_long": long_ctx,
+        "decode_fp8_cache": fp8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

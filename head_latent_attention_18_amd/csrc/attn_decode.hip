@@ -483,10 +483,10 @@ __device__ inline void bar() {
 // tile i-1 (its P written in iteration i-1); one barrier per iteration.
 // FP8: the cache holds FP8 rows (d_c E4M3 codes | d_R bf16 | d_c/128 fp32
 // scales); the P.V waves load each tile into registers and write it to the
-// stage already converted to bf16 (each code decoded exactly to fp32, times
-// its group's fp32 scale, rounded to bf16; the hardware's scaled fp8
-// conversion is not used: its scale operand is an MX power-of-two scale), so
-// the stage layout, and every read of it, is that of a bf16 cache.  HBM then carries 656 bytes per cached row
+// stage already converted to bf16 (codes times their group's scale, a power
+// of two, by the hardware's scaled conversion: two codes per instruction,
+// exact), so the stage layout, and every read of it, is that of a bf16
+// cache.  HBM then carries 656 bytes per cached row
 // instead of 1152.
 template <int DC, int DR, bool PAGED, bool FP8>
 __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
@@ -610,13 +610,15 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
         bf16x8 v;
 #pragma unroll
         for (int w2 = 0; w2 < 2; ++w2) {
-          const int word = (int)f8c[i][2 * h2 + w2];
-          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-          v[4 * w2] = (bf16)(lo[0] * f8s);
-          v[4 * w2 + 1] = (bf16)(lo[1] * f8s);
-          v[4 * w2 + 2] = (bf16)(hi[0] * f8s);
-          v[4 * w2 + 3] = (bf16)(hi[1] * f8s);
+          // the scaled conversion applies the power of two of its scale
+          // operand (an MX-style scale), which is the whole of f8s
+          const unsigned word = f8c[i][2 * h2 + w2];
+          const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, f8s, false);
+          const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, f8s, true);
+          v[4 * w2] = lo[0];
+          v[4 * w2 + 1] = lo[1];
+          v[4 * w2 + 2] = hi[0];
+          v[4 * w2 + 3] = hi[1];
         }
         const int c = 8 * j + 2 * i + h2;
         *(lds_bf16x8 *)(st + ((c ^ (r & 7)) << 3)) = v;

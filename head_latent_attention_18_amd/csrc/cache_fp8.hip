@@ -3,10 +3,12 @@
 //
 // The format follows the fine-grained FP8 scaling of the V3 technical-report
 // summary ("FP8 training framework" paragraph and figure 7: values in FP8
-// with a scale per small group of elements): per group, scale = max|x| / 448
-// (1 for an all-zero group), and each value takes the E4M3 code nearest to
-// x / scale, ties to even (the hardware conversion rounds so; values are
-// clamped to +-448 first because it maps larger ones to NaN).
+// with a scale per small group of elements).  Per group the scale is the
+// smallest power of two s with 448 s >= max|x| (1 for an all-zero group;
+// exponents below -126 are raised to -126), so x / s is exact, lies in
+// [-448, 448], and the dequantised value code * s is exact in bf16 (when it
+// is a bf16 normal number); each value takes the E4M3 code nearest to x / s,
+// ties to even (the hardware conversion rounds so).
 #include "mla_internal.h"
 
 namespace mla {
@@ -42,13 +44,20 @@ __global__ __launch_bounds__(256) void cache_append_fp8_kernel(CacheAppendArgs a
     }
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-    const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+    // amax = f * 2^e with 0.5 <= f < 1: 448 * 2^(e-9) = 0.875 * 2^e, and
+    // 448 * 2^(e-10) < 0.5 * 2^e <= amax, so k = e - 9, or e - 8 when f > 0.875
+    int k = 0;
+    if (amax > 0.f) {
+      int e;
+      const float f = frexpf(amax, &e);
+      k = max(e - 9 + (f > 0.875f ? 1 : 0), -126);
+    }
+    const float scale = ldexpf(1.f, k), inv = ldexpf(1.f, -k);
     if (c < a.d_c) {
       unsigned w[2] = {0u, 0u};
 #pragma unroll
       for (int i = 0; i < 8; i += 2) {
-        const float q0 = fminf(fmaxf(v[i] / scale, -448.f), 448.f);
-        const float q1 = fminf(fmaxf(v[i + 1] / scale, -448.f), 448.f);
+        const float q0 = v[i] * inv, q1 = v[i + 1] * inv;
         const unsigned p = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false) & 0xFFFFu;
         w[i >> 2] |= p << (16 * ((i >> 1) & 1));
       }

@@ -73,9 +73,13 @@ typedef enum mla_dtype {
  *     consecutive columns, k_R in bf16.  A row is
  *       d_c bytes of codes | d_rope bf16 values of k_R | d_c/128 float32 scales
  *     (little-endian; 656 bytes for DeepSeek-V3 against 1152 in bf16), and
- *     column c of c_KV is code[c] * scale[c/128].  Rows are written with
- *     scale = (largest magnitude of the group) / 448 (1 for an all-zero
- *     group) and each code the E4M3 value nearest to x / scale (ties to even).
+ *     column c of c_KV is code[c] * scale[c/128].  Every scale is a power
+ *     of two 2^k, -126 <= k <= 127 (the attention applies only the power of
+ *     two of a stored scale, by gfx950's scaled FP8 conversion: a row written
+ *     by another producer must keep to this).  Rows are written with the
+ *     smallest such scale for which 448 * scale >= the group's largest
+ *     magnitude (1 for an all-zero group) and each code the E4M3 value
+ *     nearest to x / scale (ties to even), so no code saturates.
  *     Needs dtype MLA_BF16, d_c a multiple of 128 and d_rope of 8; a paged
  *     cache's block_size must be a multiple of 32.  mla_compress_kv does not
  *     support it (it has no workspace to stage a row before its scales are

@@ -198,10 +198,11 @@ def fp8_cache_rows(rng: np.random.Generator, n: int, d_c: int, d_rope: int, chun
     """n cached rows in the FP8 cache layout, [n][d_c + 2*d_rope + 4*d_c/128]
     uint8: E4M3 codes of c_KV, k_R as bf16 bits, then one float32 scale per
     128 columns (little-endian).  Input data only: per row and group a scale
-    is drawn uniformly from [0.5, 1.5)/64 and the codes are those of N(0,1)
-    draws divided by it (clamped to +-448), cast by PyTorch's float8_e4m3fn
-    conversion; k_R is N(0,1) rounded to bf16.  The dequantised c_KV is then
-    close to N(0,1), as in the bf16 workloads."""
+    2^-7, 2^-6 or 2^-5 is drawn uniformly (scales of the FP8 cache are powers
+    of two) and the codes are those of N(0,1) draws divided by it (clamped
+    to +-448), cast by PyTorch's float8_e4m3fn conversion; k_R is N(0,1)
+    rounded to bf16.  The dequantised c_KV is then close to N(0,1), as in
+    the bf16 workloads."""
     import torch
     G = d_c // FP8_GROUP
     out = np.empty((n, d_c + 2 * d_rope + 4 * G), dtype=np.uint8)
@@ -209,7 +210,7 @@ def fp8_cache_rows(rng: np.random.Generator, n: int, d_c: int, d_rope: int, chun
         e = min(n, s + chunk)
         m = e - s
         x = rng.standard_normal((m, d_c), dtype=np.float32)
-        sc = ((0.5 + rng.random((m, G), dtype=np.float32)) / np.float32(64.0)).astype(np.float32)
+        sc = np.ldexp(np.float32(1.0), rng.integers(-7, -4, (m, G))).astype(np.float32)
         q = np.clip(x.reshape(m, G, FP8_GROUP) / sc[:, :, None], -448.0, 448.0).reshape(m, d_c)
         out[s:e, :d_c] = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float32)).to(
             torch.float8_e4m3fn).view(torch.uint8).numpy()

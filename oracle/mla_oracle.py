@@ -51,7 +51,8 @@ __all__ = [
     "rope", "rope_freqs", "yarn_on", "compress_kv", "project_queries", "head_keys_values", "attend_head",
     "output_projection", "prefill", "decode", "decode_absorbed",
     "cache_elements_per_token", "mha_elements_per_token", "softmax_scale",
-    "E4M3_MAX", "FP8_GROUP", "e4m3_decode", "e4m3_encode", "quantize_latent", "fp8_row_bytes",
+    "E4M3_MAX", "FP8_GROUP", "e4m3_decode", "e4m3_encode", "round_bf16", "fp8_group_scale", "quantize_latent",
+    "fp8_row_bytes",
     "dequantize_fp8_rows",
 ]
 
@@ -238,7 +239,10 @@ def decode(dims, W, h, cache_rows, heads=None, cache_fp8=False):
     quantisation).  cache_fp8: the cache holds c_KV in FP8 (E4M3 with a scale
     per group of FP8_GROUP columns), so the new tokens' c_KV is attended in
     its quantised form, as every cached row is (``cache_rows`` are then the
-    dequantised rows, dequantize_fp8_rows)."""
+    dequantised rows, dequantize_fp8_rows).  The quantiser reads c_KV
+    rounded to bfloat16, the type the compression produces in a bf16 layer
+    (the FP8 cache exists for bf16 layers only), so that a code is decided
+    from the value the layer holds, not from its float64 form."""
     h = _f64(h)
     cache_rows = _f64(cache_rows)
     n_q = h.shape[0]
@@ -247,7 +251,7 @@ def decode(dims, W, h, cache_rows, heads=None, cache_fp8=False):
     c_new, kr_new = compress_kv(W, h, qpos, dims)
     c_att = c_new
     if cache_fp8:
-        codes, scales = quantize_latent(c_new)
+        codes, scales = quantize_latent(round_bf16(c_new))
         c_att = _dequantize_latent(codes, scales)
     c_kv = np.concatenate([cache_rows[:, :dims.d_c], c_att], axis=0)
     k_r = np.concatenate([cache_rows[:, dims.d_c:], kr_new], axis=0)
@@ -311,9 +315,11 @@ def mha_elements_per_token(dims):
 # fine-grained scaling, a scale per small group of elements, the group of 128
 # elements the figure's accumulation interval gives; the 18-highlights page,
 # highlight 5, FP8 for computation and storage).  Reading: a cached row keeps
-# c_KV as E4M3 codes with one fp32 scale per FP8_GROUP consecutive columns
-# (scale = the group's largest magnitude / 448, so that value maps to +-448;
-# an all-zero group takes scale 1), and k_R in the layer dtype.
+# c_KV as E4M3 codes with one fp32 scale per FP8_GROUP consecutive columns,
+# and k_R in the layer dtype.  The pages do not say how a scale is chosen;
+# here it is the smallest power of two s with 448 s >= the group's largest
+# magnitude (an all-zero group takes 1; s is kept at or above 2^-126, the
+# smallest normal fp32), so that no value saturates and code * s is exact.
 # ---------------------------------------------------------------------------
 
 E4M3_MAX = 448.0
@@ -356,15 +362,35 @@ def e4m3_encode(x):
     return code.astype(np.uint8)
 
 
+def round_bf16(x):
+    """Nearest bfloat16 value (8 significant bits) to each value, ties to
+    even (values in bfloat16's normal range)."""
+    f, e = np.frexp(_f64(x))                 # x = f * 2^e, 0.5 <= |f| < 1
+    return np.ldexp(np.round(f * 256.0) / 256.0, e)   # np.round: half to even
+
+
+def fp8_group_scale(amax):
+    """Smallest power of two s >= 2^-126 with 448 s >= amax (1 when amax is
+    0), for each group maximum in ``amax``."""
+    a = _f64(amax)
+    # amax = f * 2^e with 0.5 <= f < 1; 448 * 2^(e-10) = 0.4375 * 2^e < amax,
+    # so s is 2^(e-9) (448 * 2^(e-9) = 0.875 * 2^e) or, if that is short, 2^(e-8)
+    f, e = np.frexp(a)
+    s = np.ldexp(1.0, e - 9)
+    s = np.where(E4M3_MAX * s >= a, s, 2.0 * s)
+    s = np.maximum(s, 2.0 ** -126)
+    return np.where(a > 0, s, 1.0)
+
+
 def quantize_latent(c_kv):
     """c_KV rows [T][d_c] -> (codes [T][d_c] uint8, scales [T][d_c/FP8_GROUP]):
-    per group, scale = max|x| / 448 (1 for an all-zero group) and each value
-    takes the E4M3 code nearest to x / scale."""
+    per group, scale = fp8_group_scale(max|x|) and each value takes the
+    E4M3 code nearest to x / scale."""
     c = _f64(c_kv)
     T, d_c = c.shape
     g = c.reshape(T, d_c // FP8_GROUP, FP8_GROUP)
     amax = np.max(np.abs(g), axis=2)
-    scales = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+    scales = fp8_group_scale(amax)
     codes = e4m3_encode(g / scales[:, :, None]).reshape(T, d_c)
     return codes, scales
 

@@ -108,16 +108,22 @@ def oracle_decode_seq(wl: Workload, b: int, heads=None):
 
 def assert_fp8_rows(got_bytes, ref_rows, dims, what: str):
     """FP8 cache rows written by the GPU against the oracle's unquantised
-    rows [n][d_c + d_R]: every c_KV value within half an E4M3 step at its
-    group's scale (scale = group max / 448) of the oracle's value, plus the
-    bf16 rounding of the value before quantisation and of the scale's
-    computation (2^-8 relative); k_R within the bf16 bounds."""
-    got = O.dequantize_fp8_rows(got_bytes.detach().cpu().numpy(), dims)
+    rows [n][d_c + d_R].  Each stored scale is the oracle's group scale
+    (fp8_group_scale) of the group maximum, give or take the bf16 rounding
+    of that maximum (2^-8 relative) before quantisation; every c_KV value
+    lies within half an E4M3 step at its stored scale of the oracle's value,
+    plus that bf16 rounding; k_R within the bf16 bounds."""
+    raw = got_bytes.detach().cpu().numpy()
+    got = O.dequantize_fp8_rows(raw, dims)
     ref = np.asarray(ref_rows, dtype=np.float64)
-    d_c = dims.d_c
-    g = ref[:, :d_c].reshape(ref.shape[0], -1, O.FP8_GROUP)
-    sc = np.max(np.abs(g), axis=2, keepdims=True) / O.E4M3_MAX
-    bound = sc * np.maximum(2.0 ** -4 * np.abs(g) / np.maximum(sc, 1e-300), 2.0 ** -10) + 2.0 ** -8 * np.abs(g) + 1e-6
+    d_c, n = dims.d_c, ref.shape[0]
+    g = ref[:, :d_c].reshape(n, -1, O.FP8_GROUP)
+    sc = np.ascontiguousarray(raw[:, d_c + 2 * dims.d_rope:]).view(np.float32).astype(np.float64).reshape(n, -1)
+    amax = np.max(np.abs(g), axis=2)
+    ok = (sc == O.fp8_group_scale(amax * (1 - 2.0 ** -8))) | (sc == O.fp8_group_scale(amax * (1 + 2.0 ** -8)))
+    assert np.all(ok), f"{what}: FP8 scales differ from the group rule at {np.argwhere(~ok)[:4].tolist()}"
+    scb = sc[:, :, None]
+    bound = scb * np.maximum(2.0 ** -4 * np.abs(g) / scb, 2.0 ** -10) + 2.0 ** -8 * np.abs(g) + 1e-6
     diff = np.abs(got[:, :d_c].reshape(g.shape) - g)
     worst = float(np.max(diff / bound)) if diff.size else 0.0
     say(f"{what}: c_KV worst error / bound = {worst:.3f}")

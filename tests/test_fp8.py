@@ -66,7 +66,8 @@ def test_fp8_decode_mixed_lengths_deterministic():
 def test_fp8_prefill_then_decode():
     """Prefill of 300 tokens into an FP8 cache (the attention of the prefill
     itself uses the unquantised latent), then three decode steps reading the
-    FP8 rows the prefill wrote.  The oracle quantises its own rows."""
+    FP8 rows the prefill wrote.  The oracle quantises its own rows, from
+    their bf16 values as the layer does."""
     L0, steps = 300, 3
     wl = make_workload(3, batch=1, seq_len=L0 + steps)
     wl.cache_fp8 = True
@@ -83,7 +84,7 @@ def test_fp8_prefill_then_decode():
     assert_close(u[0], full["u"][:L0], True, "prefill u")
     assert_fp8_rows(cache.read_rows(0, np.arange(L0)), np.concatenate([full["c_kv"], full["k_r"]], axis=1)[:L0],
                     d, "prefill rows")
-    codes, scales = O.quantize_latent(full["c_kv"])
+    codes, scales = O.quantize_latent(O.round_bf16(full["c_kv"]))   # codes decided from the bf16 latent
     cq = O.e4m3_decode(codes) * np.repeat(scales, O.FP8_GROUP, axis=1)
     rows_oracle = np.concatenate([cq, full["k_r"]], axis=1)
     for s in range(steps):

@@ -167,10 +167,43 @@ def _quant_group_64(c_kv):
     c = np.asarray(c_kv, dtype=np.float64)
     T, d_c = c.shape
     g = c.reshape(T, d_c // 64, 64)
-    amax = np.max(np.abs(g), axis=2)
-    sc = np.where(amax > 0, amax / 448.0, 1.0)
+    sc = O.fp8_group_scale(np.max(np.abs(g), axis=2))
     codes = _enc8(g / sc[:, :, None]).reshape(T, d_c)
     return codes, sc[:, ::2]
+
+
+def _quant_scale_amax(c_kv):
+    # scale = max|x| / 448 (the group maximum maps to 448 exactly), not a
+    # power of two
+    c = np.asarray(c_kv, dtype=np.float64)
+    T, d_c = c.shape
+    g = c.reshape(T, d_c // 128, 128)
+    amax = np.max(np.abs(g), axis=2)
+    sc = np.where(amax > 0, amax / 448.0, 1.0)
+    return _enc8(g / sc[:, :, None]).reshape(T, d_c), sc
+
+
+def _quant_scale_floor(c_kv):
+    # the power of two at or below max|x| / 448 (the group maximum can then
+    # exceed 448 and saturates)
+    c = np.asarray(c_kv, dtype=np.float64)
+    T, d_c = c.shape
+    g = c.reshape(T, d_c // 128, 128)
+    amax = np.max(np.abs(g), axis=2)
+    with np.errstate(divide="ignore"):
+        sc = np.where(amax > 0, 2.0 ** np.floor(np.log2(np.where(amax > 0, amax, 1.0) / 448.0)), 1.0)
+    return _enc8(g / sc[:, :, None]).reshape(T, d_c), sc
+
+
+def _bf16_truncate(x):
+    # drop the low bits instead of rounding to nearest
+    f, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.trunc(f * 256.0) / 256.0, e)
+
+
+def _bf16_skipped(x):
+    # quantise the float64 value (no bf16 rounding first)
+    return np.asarray(x, dtype=np.float64)
 
 
 MUTATIONS = {
@@ -199,6 +232,10 @@ MUTATIONS = {
     "e4m3_truncate": ("e4m3_encode", _e4m3_truncate),
     "fp8_scale_240": ("quantize_latent", _quant_scale_240),
     "fp8_group_64": ("quantize_latent", _quant_group_64),
+    "fp8_scale_amax_over_448": ("quantize_latent", _quant_scale_amax),
+    "fp8_scale_rounded_down": ("quantize_latent", _quant_scale_floor),
+    "bf16_truncate": ("round_bf16", _bf16_truncate),
+    "fp8_input_not_bf16": ("round_bf16", _bf16_skipped),
 }
 
 
