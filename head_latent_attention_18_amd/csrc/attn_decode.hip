@@ -585,42 +585,50 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
   auto copy_tile = [&](int t) { copy_rows(tile_src(t), 0, min(KVT, kv_end - (kv_beg + t * KVT)) - 1, t % NS); };
 
   // FP8 tiles: copying thread ct converts row ct >> 3 of a tile, part
-  // j = ct & 7: codes 64j..64j+63 (logical chunks 8j..8j+7 of the bf16 row),
-  // k_R values 8j..8j+7 (chunk 64 + j) and the scale of group j >> 1.  The
-  // loads of tile t are issued one iteration before the conversion writes it.
+  // j = ct & 7: the 16-code pieces j + 8i (i = 0..3; codes 16(j + 8i) ..
+  // +15, logical chunks 2(j + 8i) and 2(j + 8i) + 1 of the bf16 row), k_R
+  // values 8j..8j+7 (chunk 64 + j) and the four group scales (piece j + 8i
+  // lies in group i).  Interleaving the pieces over the lanes keeps each
+  // row's loads 128 contiguous bytes and the 16-byte LDS writes free of bank
+  // conflicts (a row's eight lanes hit eight distinct 4-bank groups of one
+  // parity, the next row's swizzle the other parity).  The loads of tile t
+  // are issued one iteration before the conversion writes it.
   static_assert(!FP8 || (DC == 512 && DR == 64 && NC == 8 * KVT), "");
-  u32x4 f8c[4], f8r;
-  float f8s = 0.f;
+  u32x4 f8c[4], f8r, f8s;
   auto fp8_load = [&](int t) {
     const int r = min(ct >> 3, min(KVT, kv_end - (kv_beg + t * KVT)) - 1), j = ct & 7;
     const char *row = tile_src(t) + (long)r * RBYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f8c[i] = *(const u32x4 *)(row + 64 * j + 16 * i);
+    for (int i = 0; i < 4; ++i) f8c[i] = *(const u32x4 *)(row + 16 * (j + 8 * i));
     f8r = *(const u32x4 *)(row + DC + 16 * j);
-    f8s = *(const float *)(row + DC + 2 * DR + 4 * (j >> 1));
+    f8s = *(const u32x4 *)(row + DC + 2 * DR);   // the four group scales
   };
   auto fp8_store = [&](int t) {
     const int r = ct >> 3, j = ct & 7;
     lds_bf16 *st = (lds_bf16 *)stages + (t % NS) * STAGE + r * D;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // 16 codes -> two 8-element chunks (logical 8j + 2i, 8j + 2i + 1)
+      // 16 codes -> two 8-element chunks (logical 2(j + 8i), 2(j + 8i) + 1)
+      // columns 16(j + 8i).. lie in group i (the element is copied out first:
+      // a bit cast of the vector element itself reads element 0)
+      const unsigned sbits = f8s[i];
+      const float scale = __builtin_bit_cast(float, sbits);
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         bf16x8 v;
 #pragma unroll
         for (int w2 = 0; w2 < 2; ++w2) {
           // the scaled conversion applies the power of two of its scale
-          // operand (an MX-style scale), which is the whole of f8s
+          // operand (an MX-style scale), which is the whole of the scale
           const unsigned word = f8c[i][2 * h2 + w2];
-          const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, f8s, false);
-          const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, f8s, true);
+          const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, scale, false);
+          const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, scale, true);
           v[4 * w2] = lo[0];
           v[4 * w2 + 1] = lo[1];
           v[4 * w2 + 2] = hi[0];
           v[4 * w2 + 3] = hi[1];
         }
-        const int c = 8 * j + 2 * i + h2;
+        const int c = 2 * (j + 8 * i) + h2;
         *(lds_bf16x8 *)(st + ((c ^ (r & 7)) << 3)) = v;
       }
     }
