@@ -1009,21 +1009,24 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 // Split combine fused with the value un-absorption o_t,i = W_UV,i o_lat,t,i
 // (W_UV applied after the attention, by the associativity of the products in
 // section 2.1 of the DeepSeek-V3 paper-reading notes), bf16, d_c = 512.  One
-// workgroup = (head i, 16 tokens): its four waves merge the splits of the 16
-// latent rows (a wave per four tokens, a lane per eight columns) into LDS,
-// rounded to bf16 as a stored o_lat would be, while W_UV,i (128 KB) streams
-// into registers; then O^T[v][t] = W_UV,i[v][:] . o_lat[t][:] on the matrix
-// cores, wave w taking features (DV/4)w...  The token groups of a head share
-// an XCD, whose L2 serves their common reads of W_UV,i.  Rows marked for
-// exact recomputation take the two-pass path of the combine kernel.
+// workgroup = (head i, 16 tokens), eight waves in two roles whose memory
+// counters are separate, so neither waits for the other's loads:
+//   waves 0..3 merge the splits of four tokens each (a lane per eight latent
+//     columns) into LDS, rounded to bf16 as a stored o_lat would be; only
+//     the splits a token has are loaded, all of them before any is used;
+//   waves 4..7 copy W_UV,i (128 KB) into LDS.
+// Then O^T[v][t] = W_UV,i[v][:] . o_lat[t][:] on the matrix cores, wave w
+// taking features 16w..16w+15.  The token groups of a head share an XCD,
+// whose L2 serves their common reads of W_UV,i.  Rows marked for exact
+// recomputation take the two-pass path of the combine kernel.
 template <int DC, int DR, int DV>
-__global__ __launch_bounds__(256, 1) void decode_combine_uv_kernel(DecodeArgs a, const bf16 *w_uv, bf16 *o) {
-  constexpr int TT = 16, NW = 4;         // tokens per workgroup, waves
+__global__ __launch_bounds__(512, 1) void decode_combine_uv_kernel(DecodeArgs a, const bf16 *w_uv, bf16 *o) {
+  constexpr int TT = 16, NM = 4;         // tokens per workgroup, merging waves
+  constexpr int NW = 8;                  // waves
   constexpr int KS = DC / 32;            // k steps
-  constexpr int VB = DV / (16 * NW);     // 16-feature blocks per wave
   constexpr int PER = DC / 64;           // latent columns per lane in the merge
   constexpr int SB = 8;                  // splits per token requested up front
-  static_assert(DC == 512 && PER == 8 && VB >= 1 && DV % (16 * NW) == 0, "");
+  static_assert(DC == 512 && PER == 8 && DV == 16 * NW, "");
   // token row tl of the group: 16-byte chunk c at chunk c ^ (tl & 15)
   __shared__ __attribute__((aligned(16))) bf16 olat[TT * DC];
   // W_UV,i [DV][DC]: chunk c of row v at chunk c ^ (v & 15)
@@ -1037,153 +1040,142 @@ __global__ __launch_bounds__(256, 1) void decode_combine_uv_kernel(DecodeArgs a,
   const int h = (slot / ntg) * 8 + xcd, tg = slot % ntg;
   if (h >= a.n_h) return;
 
-  // W_UV,i -> LDS, whole rows per copy instruction (the merge's loads below
-  // return after these: the counter is in order)
-  {
-    constexpr int WLOADS = DV * DC / 8 / 256;
+  if (wave >= NM) {
+    // W_UV,i -> LDS, whole rows per copy instruction
+    constexpr int NC = 64 * (NW - NM);
+    constexpr int WLOADS = DV * DC / 8 / NC;
+    const int ct = threadIdx.x - 64 * NM;
     const unsigned lw = (unsigned)(size_t)(lds_void *)wuv;
     const bf16 *wh = w_uv + (long)h * DV * DC;
 #pragma unroll
     for (int j = 0; j < WLOADS; ++j) {
-      const int sl = j * 256 + threadIdx.x, v = sl / (DC / 8), pc = sl % (DC / 8);
+      const int sl = j * NC + ct, v = sl / (DC / 8), pc = sl % (DC / 8);
       const int c = pc ^ (v & 15);
-      dma16(wh, (unsigned)((v * DC + c * 8) * 2), lw + (unsigned)(j * 256 + wave * 64) * 16);
+      dma16(wh, (unsigned)((v * DC + c * 8) * 2), lw + (unsigned)(j * NC + (wave - NM) * 64) * 16);
     }
-  }
-
-  // merge: wave w takes tokens 4w..4w+3 of the group.  The log-sum-exps
-  // (lane s: split s) and the first SB partial rows of all four tokens are
-  // requested before any of them is used, so the merge costs one round trip
-  // (more splits than SB, or than 64, take extra rounds).
-  constexpr int TW = TT / NW;
-  int bq[TW], rq[TW], lq[TW], nsp[TW];
-  long base[TW];
-#pragma unroll
-  for (int j = 0; j < TW; ++j) {
-    const int t = min(tg * TT + wave * TW + j, T - 1);
-    bq[j] = t / a.n_q;
-    rq[j] = (t % a.n_q) * a.n_h + h;
-  }
-  {
-    SeqSpan sp[TW];
-    int total;
-    plan_spans<TW>(a, bq, sp, total);
-    const int P = (total + a.W - 1) / a.W;
+    wait_vmcnt<0>();
+  } else {
+    // merge: wave w takes tokens 4w..4w+3 of the group
+    constexpr int TW = TT / NM;
+    int bq[TW], rq[TW], lq[TW], nsp[TW];
+    long base[TW];
 #pragma unroll
     for (int j = 0; j < TW; ++j) {
-      int slot0;
-      plan_slots(sp[j], P, slot0, nsp[j]);
-      if (tg * TT + wave * TW + j >= T) nsp[j] = 0;
-      lq[j] = sp[j].len;
-      base[j] = (long)slot0 * R + rq[j];
+      const int t = min(tg * TT + wave * TW + j, T - 1);
+      bq[j] = t / a.n_q;
+      rq[j] = (t % a.n_q) * a.n_h + h;
     }
-  }
-  // the log-sum-exps (lane s: split s) and the first SB partial rows of each
-  // token are requested before any is used; splits past a sequence's own
-  // count are masked (loads clamped to its last split)
-  float ls[TW];
-  bf16x8 v[TW][SB];
+    {
+      SeqSpan sp[TW];
+      int total;
+      plan_spans<TW>(a, bq, sp, total);
+      const int P = (total + a.W - 1) / a.W;
 #pragma unroll
-  for (int j = 0; j < TW; ++j) ls[j] = a.lse_part[base[j] + (long)min(lane, max(nsp[j] - 1, 0)) * R];
-#pragma unroll
-  for (int j = 0; j < TW; ++j)
-#pragma unroll
-    for (int jj = 0; jj < SB; ++jj) {
-      const int sp = min(jj, max(nsp[j] - 1, 0));
-      v[j][jj] = *(const bf16x8 *)((const bf16 *)a.o_part + (base[j] + (long)sp * R) * DC + lane * PER);
-    }
-#pragma unroll
-  for (int j = 0; j < TW; ++j) ls[j] = lane < nsp[j] ? ls[j] : -INFINITY;
-  lds_bf16 *ol = (lds_bf16 *)olat;
-#pragma unroll
-  for (int j = 0; j < TW; ++j) {
-    const int tl = wave * TW + j;
-    float res[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) res[i] = 0.f;
-    if (nsp[j] > 0) {
-      float lmax = ls[j];
-      bool flagged = ls[j] != ls[j];
-      for (int s0 = 64; s0 < nsp[j]; s0 += 64) {
-        const float x = s0 + lane < nsp[j] ? a.lse_part[base[j] + (long)(s0 + lane) * R] : -INFINITY;
-        flagged |= x != x;
-        lmax = fmaxf(lmax, x);
+      for (int j = 0; j < TW; ++j) {
+        int slot0;
+        plan_slots(sp[j], P, slot0, nsp[j]);
+        if (tg * TT + wave * TW + j >= T) nsp[j] = 0;
+        nsp[j] = __builtin_amdgcn_readfirstlane(nsp[j]);
+        lq[j] = sp[j].len;
+        base[j] = (long)slot0 * R + rq[j];
       }
-      if (__any(flagged)) {
-        decode_row_exact<bf16, DC, DR, true>(a, bq[j], rq[j], lq[j], res);
-      } else {
+    }
+    // the log-sum-exps (lane s: split s) and the first SB partial rows of
+    // each token are requested before any is used; splits at or past a
+    // sequence's own count are neither loaded nor used (this call did not
+    // write them: they hold whatever the workspace held, possibly NaN bits)
+    float ls[TW];
+    bf16x8 v[TW][SB];
 #pragma unroll
-        for (int o2 = 32; o2 > 0; o2 >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, o2));
-        float wsum = 0.f;
+    for (int j = 0; j < TW; ++j) ls[j] = a.lse_part[base[j] + (long)min(lane, max(nsp[j] - 1, 0)) * R];
 #pragma unroll
-        for (int jj = 0; jj < SB; ++jj) {
-          // splits at or past the sequence's own count were not written by
-          // this call (their rows hold whatever the workspace held, possibly
-          // NaN bits), so they are skipped, not weighted by zero; the
-          // condition is wave-uniform
-          const float lsj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[j]), jj));
-          if (jj < nsp[j] && lsj != -INFINITY) {
-            const float w = exp2f(lsj - lmax);
-            wsum += w;
+    for (int j = 0; j < TW; ++j)
 #pragma unroll
-            for (int i = 0; i < PER; ++i) res[i] += w * (float)v[j][jj][i];
-          }
+      for (int jj = 0; jj < SB; ++jj)
+        if (jj < nsp[j]) v[j][jj] = *(const bf16x8 *)((const bf16 *)a.o_part + (base[j] + (long)jj * R) * DC + lane * PER);
+#pragma unroll
+    for (int j = 0; j < TW; ++j) ls[j] = lane < nsp[j] ? ls[j] : -INFINITY;
+    lds_bf16 *ol = (lds_bf16 *)olat;
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+      const int tl = wave * TW + j;
+      float res[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) res[i] = 0.f;
+      if (nsp[j] > 0) {
+        float lmax = ls[j];
+        bool flagged = ls[j] != ls[j];
+        for (int s0 = 64; s0 < nsp[j]; s0 += 64) {
+          const float x = s0 + lane < nsp[j] ? a.lse_part[base[j] + (long)(s0 + lane) * R] : -INFINITY;
+          flagged |= x != x;
+          lmax = fmaxf(lmax, x);
         }
-        // the remaining splits in batches of eight, every load of a batch
-        // issued before any is used (one round trip per batch)
-        for (int s0 = SB; s0 < nsp[j]; s0 += 8) {
-          bf16x8 vv[8];
-          float lsv[8];
+        if (__any(flagged)) {
+          decode_row_exact<bf16, DC, DR, true>(a, bq[j], rq[j], lq[j], res);
+        } else {
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            const int sp = min(s0 + jj, nsp[j] - 1);
-            vv[jj] = *(const bf16x8 *)((const bf16 *)a.o_part + (base[j] + (long)sp * R) * DC + lane * PER);
-            lsv[jj] = sp < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[j]), sp))
-                              : a.lse_part[base[j] + (long)sp * R];
-          }
+          for (int o2 = 32; o2 > 0; o2 >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, o2));
+          float wsum = 0.f;
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj)
-            if (s0 + jj < nsp[j] && lsv[jj] != -INFINITY) {
-              const float w = exp2f(lsv[jj] - lmax);
+          for (int jj = 0; jj < SB; ++jj) {
+            // the condition is wave-uniform
+            const float lsj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[j]), jj));
+            if (jj < nsp[j] && lsj != -INFINITY) {
+              const float w = exp2f(lsj - lmax);
               wsum += w;
 #pragma unroll
-              for (int i = 0; i < PER; ++i) res[i] += w * (float)vv[jj][i];
+              for (int i = 0; i < PER; ++i) res[i] += w * (float)v[j][jj][i];
             }
+          }
+          // the remaining splits in batches of eight, every load of a batch
+          // issued before any is used (one round trip per batch)
+          for (int s0 = SB; s0 < nsp[j]; s0 += 8) {
+            bf16x8 vv[8];
+            float lsv[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+              const int sp = min(s0 + jj, nsp[j] - 1);
+              vv[jj] = *(const bf16x8 *)((const bf16 *)a.o_part + (base[j] + (long)sp * R) * DC + lane * PER);
+              lsv[jj] = sp < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[j]), sp))
+                                : a.lse_part[base[j] + (long)sp * R];
+            }
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+              if (s0 + jj < nsp[j] && lsv[jj] != -INFINITY) {
+                const float w = exp2f(lsv[jj] - lmax);
+                wsum += w;
+#pragma unroll
+                for (int i = 0; i < PER; ++i) res[i] += w * (float)vv[jj][i];
+              }
+          }
+          const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+          for (int i = 0; i < PER; ++i) res[i] *= inv;
         }
-        const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) res[i] *= inv;
       }
-    }
-    bf16x8 pk;
+      bf16x8 pk;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) pk[i] = (bf16)res[i];
-    *(lds_bf16x8 *)(ol + tl * DC + (lane ^ (tl & 15)) * 8) = pk;
+      for (int i = 0; i < PER; ++i) pk[i] = (bf16)res[i];
+      *(lds_bf16x8 *)(ol + tl * DC + (lane ^ (tl & 15)) * 8) = pk;
+    }
   }
-  wait_vmcnt<0>();   // this wave's W_UV copies
   __syncthreads();
 
-  // A operand: W_UV,i row (wave*VB + vb)*16 + lrow, k = 32*ks + 8*lgrp..
+  // A operand: W_UV,i row 16*wave + lrow, k = 32*ks + 8*lgrp..
   const lds_bf16 *wl = (const lds_bf16 *)wuv;
-  f32x4 acc[VB];
-#pragma unroll
-  for (int vb = 0; vb < VB; ++vb) acc[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const lds_bf16 *ol = (const lds_bf16 *)olat;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const bf16x8 xb = *(const lds_bf16x8 *)(ol + lrow * DC + (((4 * ks + lgrp) ^ lrow) * 8));
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb) {
-      const bf16x8 wf = *(const lds_bf16x8 *)(wl + ((wave * VB + vb) * 16 + lrow) * DC + (((4 * ks + lgrp) ^ lrow) * 8));
-      acc[vb] = Mma<bf16>::mma(wf, xb, acc[vb]);
-    }
+    const bf16x8 wf = *(const lds_bf16x8 *)(wl + (wave * 16 + lrow) * DC + (((4 * ks + lgrp) ^ lrow) * 8));
+    acc = Mma<bf16>::mma(wf, xb, acc);
   }
-  // lane: features (wave*VB + vb)*16 + 4*lgrp + 0..3 of token lrow
+  // lane: features 16*wave + 4*lgrp + 0..3 of token lrow
   const int t = tg * TT + lrow;
   if (t < T) {
-    bf16 *orow = o + ((long)t * a.n_h + h) * DV + wave * VB * 16 + 4 * lgrp;
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb)
-      *(bf16x4 *)(orow + vb * 16) = bf16x4{(bf16)acc[vb][0], (bf16)acc[vb][1], (bf16)acc[vb][2], (bf16)acc[vb][3]};
+    bf16 *orow = o + ((long)t * a.n_h + h) * DV + wave * 16 + 4 * lgrp;
+    *(bf16x4 *)orow = bf16x4{(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
   }
 }
 
@@ -1192,7 +1184,7 @@ hipError_t launch_decode_combine_uv(const DecodeArgs &a, int d_v, const void *w_
   const int T = a.B * a.n_q;
   const int grid = ((a.n_h + 7) / 8) * 8 * ((T + 15) / 16);
   timing_before("decode_combine_uv", st);
-  hipLaunchKernelGGL((decode_combine_uv_kernel<512, 64, 128>), dim3(grid), dim3(256), 0, st, a,
+  hipLaunchKernelGGL((decode_combine_uv_kernel<512, 64, 128>), dim3(grid), dim3(512), 0, st, a,
                      (const bf16 *)w_uv, (bf16 *)o);
   timing_after("decode_combine_uv", st);
   return hipGetLastError();
