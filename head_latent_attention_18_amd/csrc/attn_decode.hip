@@ -413,8 +413,11 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_kernel(DecodeArgs a) {
 //     the 4x16 block of 16-bit elements the group addresses) and P^T from LDS.
 // The softmax reference of a row is the max of its first tile and never
 // moves (no O rescale: numerator and denominator share the reference, so the
-// result is the same softmax); a row whose scores later rise more than 2^32
-// above it is flagged and recomputed exactly by the combine.
+// result is the same softmax).  Scores that later rise more than 2^32 above
+// it would overflow the probabilities: the workgroup then runs its segment a
+// second time, with each row's reference set to the row's maximum over the
+// segment, which the first pass tracked (the same MFMA path, at most twice
+// the work, and no probability above 1).
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 #ifndef DECODE_WS_PF
@@ -508,6 +511,8 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2 * 4 * ROWS];   // P[buf][g][row]
   __shared__ float xch[2][ROWS];                                       // per key half: row max, then row sum
   __shared__ int xov[2][ROWS];                                         // per key half: row overflowed
+  __shared__ float xmx[2][ROWS];                                       // per key half: row max over the segment
+  __shared__ int xredo;                                                // a row overflowed: second pass
   constexpr int BTAB = PAGED ? 1024 : 1;
   __shared__ int btab[BTAB];
 
@@ -635,6 +640,11 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
     *(lds_u32x4 *)(st + (((64 + j) ^ (r & 7)) << 3)) = f8r;
   };
 
+  // pass 1 (only after a row overflowed in pass 0): each row's reference
+  // is its maximum over the segment (score waves)
+  float mfix[2] = {MREF0, MREF0};
+  // returns true when pass 0 found an overflow (pass 1 must follow)
+  auto run_pass = [&](const int pass) -> bool {
   // the 64 query rows reach LDS through stages 2 and 3 while tiles 0 and 1
   // are copied into stages 0 and 1 (FP8: tile 0 converted, tile 1 loaded)
   if (pv_wave) {
@@ -671,6 +681,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
     bf16x8 qf[2][QS];
     int limit[2];
     float mref[2] = {MREF0, MREF0}, lrun[2] = {0.f, 0.f};
+    float mx[2] = {-INFINITY, -INFINITY};              // the lane's maximum so far (pass 0)
     bool ovf[2] = {false, false};
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -695,6 +706,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
     const int a_odd = (kh * 16 + lrow) * D + (gq - 4 * fq) * 8;
     wait_lgkm0();
     bar();                                             // B0
+    if (tid == 0) xredo = 0;   // every read of the last pass's flag is behind B0
 
     for (int t = 0; t <= ntiles; ++t) {
       if (t < ntiles) {
@@ -726,6 +738,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
             sv[j][i] = (kv <= limit[j]) ? x : -INFINITY;
             mt[j] = fmaxf(mt[j], sv[j][i]);
           }
+          mx[j] = fmaxf(mx[j], mt[j]);
         }
         // the first tile fixes the reference of each row (max over both key
         // halves, exchanged through LDS); later tiles only check that they
@@ -741,9 +754,9 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const int rl = qb * 32 + j * 16 + lrow;
-            mref[j] = fmaxf(fmaxf(xch[0][rl], xch[1][rl]), MREF0);
+            mref[j] = pass ? mfix[j] : fmaxf(fmaxf(xch[0][rl], xch[1][rl]), MREF0);
           }
-        } else {
+        } else if (pass == 0) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) ovf[j] |= mt[j] > mref[j] + TAU;
         }
@@ -765,29 +778,39 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
       bar();                                           // end of iteration t
     }
 
-    // row sums and overflow marks of the two key halves meet in LDS
+    // row sums, overflow marks and row maxima of the two key halves meet in
+    // LDS
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const bool rov = row_max(ovf[j] ? 1.f : 0.f) > 0.f;
+      const float rmx = row_max(mx[j]);
       float l = lrun[j];
       l += __shfl_xor(l, 16);
       l += __shfl_xor(l, 32);
       if (lgrp == 0) {
         xch[kh][qb * 32 + j * 16 + lrow] = l;
         xov[kh][qb * 32 + j * 16 + lrow] = rov ? 1 : 0;
+        xmx[kh][qb * 32 + j * 16 + lrow] = rmx;
       }
     }
     __syncthreads();                                   // E1 (P no longer read)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int rl = qb * 32 + j * 16 + lrow;
+      mfix[j] = fmaxf(fmaxf(xmx[0][rl], xmx[1][rl]), MREF0);
+    }
     if (kh == 0 && lgrp == 0) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int rl = qb * 32 + j * 16 + lrow;
         const float l = xch[0][rl] + xch[1][rl];
-        const bool ov = (xov[0][rl] | xov[1][rl]) != 0;
+        // overflow in pass 0 sends the whole workgroup through pass 1 (rows
+        // of the group past R repeat the scores of row R - 1); the sums of
+        // pass 0 are then overwritten
+        if (pass == 0 && (xov[0][rl] | xov[1][rl]) != 0) xredo = 1;
         fac[rl] = l > 0.f ? 1.f / l : 0.f;
         if (rbase + rl < R)
-          a.lse_part[(long)slot * R + rbase + rl] =
-              ov ? __builtin_nanf("") : l > 0.f ? mref[j] + log2f(l) : -INFINITY;
+          a.lse_part[(long)slot * R + rbase + rl] = l > 0.f ? mref[j] + log2f(l) : -INFINITY;
       }
     }
     __syncthreads();                                   // E2
@@ -872,69 +895,21 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
     }
     __syncthreads();                                   // E3
   }
+  // the flag was written before E2 and is reset after the next B0
+  if (pass == 0 && xredo != 0) return true;
   // one whole row per store instruction
   bf16 *op = (bf16 *)a.o_part + ((long)slot * R + rbase) * DC + lane * 8;
   for (int rl = wave; rl < ROWS && rbase + rl < R; rl += 8)
     __builtin_nontemporal_store(*(const lds_bf16x8 *)(ot + rl * DC + (lane ^ (rl & 15)) * 8),
                                 (bf16x8 *)(op + (long)rl * DC));
-  });
-}
-
-// Exact attention of one query row over its whole sequence, straight from the
-// cache, for rows an attention kernel flagged (lse = NaN): two passes, the
-// first for the max, the second for the sum and the weighted latent rows.
-// res[i] receives latent column col(i): lane + 64*i, or lane*PER + i when
-// CHUNKED (the lane's PER consecutive columns).
-template <typename T, int DC, int DR, bool CHUNKED>
-__device__ void decode_row_exact(const DecodeArgs &a, int b, int r, int len, float (&res)[(DC + 63) / 64]) {
-  constexpr int D = DC + DR, PER = (DC + 63) / 64, QP = (D + 63) / 64;
-  static_assert(!CHUNKED || DC == 64 * PER, "");
-  const int lane = threadIdx.x & 63;
-  const int R = a.n_q * a.n_h;
-  const T *qrow = (const T *)a.q + ((long)b * R + r) * D;
-  float qv[QP];
-#pragma unroll
-  for (int i = 0; i < QP; ++i) qv[i] = (lane + 64 * i < D) ? to_f32(qrow[lane + 64 * i]) : 0.f;
-  const int limit = min(len - a.n_q + r / a.n_h, len - 1);
-  // element c of a cached row (FP8 rows: code times its group's scale, or
-  // the bf16 k_R)
-  const bool f8 = a.cache.fp8 != 0;
-  auto elem = [&](const unsigned char *row, int c) -> float {
-    if (!f8) return to_f32(((const T *)row)[c]);
-    if (c >= DC) return (float)((const bf16 *)(row + DC))[c - DC];
-    const float sc = ((const float *)(row + DC + 2 * DR))[c / 128];
-    return __builtin_amdgcn_cvt_pk_f32_fp8((int)row[c], false)[0] * sc;
+  return false;
   };
-  auto row_at = [&](int kv) {
-    return (const unsigned char *)a.cache.pool + cache_row(a.cache, b, kv) * (long)a.cache.row_bytes;
-  };
-  auto score = [&](const unsigned char *crow) {
-    float dot = 0.f;
-#pragma unroll
-    for (int i = 0; i < QP; ++i)
-      if (lane + 64 * i < D) dot += qv[i] * elem(crow, lane + 64 * i);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
-    return dot * a.scale_log2;
-  };
-  float m = -INFINITY;
-  for (int kv = 0; kv <= limit; ++kv) m = fmaxf(m, score(row_at(kv)));
-  float l = 0.f, acc[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  for (int kv = 0; kv <= limit; ++kv) {
-    const unsigned char *crow = row_at(kv);
-    const float p = exp2f(score(crow) - m);
-    l += p;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = CHUNKED ? lane * PER + i : lane + 64 * i;
-      if (c < DC) acc[i] += p * elem(crow, c);
-    }
+  if (run_pass(0)) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    run_pass(1);
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) res[i] = acc[i] * inv;
+  });
 }
 
 template <typename T, int N>
@@ -954,24 +929,14 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   plan_totals(a, total, P);
   const SeqSpan sp = plan_seq(a, b);
   plan_slots(sp, P, slot0, nsp);
-  const int len = sp.len;
   const long base = (long)slot0 * R + r;
   T *out = (T *)a.o_lat + row * DC;
   // split weights: lane s holds split s (for up to 64 splits; more are
   // read in rounds)
   float lmax = -INFINITY;
-  bool flagged = false;
   for (int s0 = 0; s0 < nsp; s0 += 64) {
     const float ls = s0 + lane < nsp ? a.lse_part[base + (long)(s0 + lane) * R] : -INFINITY;
-    flagged |= ls != ls;
     lmax = fmaxf(lmax, ls);
-  }
-  if (__any(flagged)) {
-    float res[PER];
-    decode_row_exact<T, DC, DR, false>(a, b, r, len, res);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) out[lane + 64 * i] = from_f32<T>(res[i]);
-    return;
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, o));
@@ -1017,8 +982,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 //   waves 4..7 copy W_UV,i (128 KB) into LDS.
 // Then O^T[v][t] = W_UV,i[v][:] . o_lat[t][:] on the matrix cores, wave w
 // taking features 16w..16w+15.  The token groups of a head share an XCD,
-// whose L2 serves their common reads of W_UV,i.  Rows marked for exact
-// recomputation take the two-pass path of the combine kernel.
+// whose L2 serves their common reads of W_UV,i.
 template <int DC, int DR, int DV>
 __global__ __launch_bounds__(512, 1) void decode_combine_uv_kernel(DecodeArgs a, const bf16 *w_uv, bf16 *o) {
   constexpr int TT = 16, NM = 4;         // tokens per workgroup, merging waves
@@ -1057,7 +1021,7 @@ __global__ __launch_bounds__(512, 1) void decode_combine_uv_kernel(DecodeArgs a,
   } else {
     // merge: wave w takes tokens 4w..4w+3 of the group
     constexpr int TW = TT / NM;
-    int bq[TW], rq[TW], lq[TW], nsp[TW];
+    int bq[TW], rq[TW], nsp[TW];
     long base[TW];
 #pragma unroll
     for (int j = 0; j < TW; ++j) {
@@ -1076,7 +1040,6 @@ __global__ __launch_bounds__(512, 1) void decode_combine_uv_kernel(DecodeArgs a,
         plan_slots(sp[j], P, slot0, nsp[j]);
         if (tg * TT + wave * TW + j >= T) nsp[j] = 0;
         nsp[j] = __builtin_amdgcn_readfirstlane(nsp[j]);
-        lq[j] = sp[j].len;
         base[j] = (long)slot0 * R + rq[j];
       }
     }
@@ -1104,15 +1067,11 @@ __global__ __launch_bounds__(512, 1) void decode_combine_uv_kernel(DecodeArgs a,
       for (int i = 0; i < PER; ++i) res[i] = 0.f;
       if (nsp[j] > 0) {
         float lmax = ls[j];
-        bool flagged = ls[j] != ls[j];
         for (int s0 = 64; s0 < nsp[j]; s0 += 64) {
           const float x = s0 + lane < nsp[j] ? a.lse_part[base[j] + (long)(s0 + lane) * R] : -INFINITY;
-          flagged |= x != x;
           lmax = fmaxf(lmax, x);
         }
-        if (__any(flagged)) {
-          decode_row_exact<bf16, DC, DR, true>(a, bq[j], rq[j], lq[j], res);
-        } else {
+        {
 #pragma unroll
           for (int o2 = 32; o2 > 0; o2 >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, o2));
           float wsum = 0.f;

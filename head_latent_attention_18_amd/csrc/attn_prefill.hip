@@ -14,8 +14,9 @@
 //
 //   flash_prefill_m32_kernel  bf16, lengths a multiple of 8: 32x32x16 MFMAs,
 //                             copy-fed LDS ring, softmax reference fixed on
-//                             the first tile (rows that outgrow it are
-//                             recomputed by flash_fixup_kernel);
+//                             the first tile (a workgroup with a row that
+//                             outgrows it runs a second pass with each row's
+//                             maximum as the reference);
 //   flash_prefill_kernel      fp32, and bf16 at other lengths: tiles staged
 //                             through registers, 16x16 MFMAs, reference
 //                             moved lazily.
@@ -401,12 +402,11 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_m32_kernel(FlashArgs
   s16x4 kone = {0, 0, 0, 0}, qref = {0, 0, 0, 0};
   if (hh == 0) kone[0] = (short)0x3f80;
   f32x16 oacc[DVB];
-#pragma unroll
-  for (int i = 0; i < DVB; ++i)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
   float lrun = 0.f;
   bool bad = false;
+  // pass 0: the lane's largest score relative to the reference (the row's
+  // maximum minus the reference, once the lane pair is combined)
+  float smax = -INFINITY, mref0 = 0.f;
 
   // Copies.  Stage layout (bytes): K_C rows of 256 at 0, k_R rows of 128 at
   // 16384, V^T rows of 128 at 24576; chunk c of row r sits at position
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_m32_kernel(FlashArgs
   };
 
   // softmax of tile t (scores in sacc) and O^T += V^T . P^T
-  auto softmax_pv = [&](int t) {
+  auto softmax_pv = [&](int t, int pass) {
     const int kvb = t * KVT;
     const unsigned so = (unsigned)((t % NS) * STAGE * 2);
     // V^T fragments of the P.V steps, in order (kb, m, db); the first ones
@@ -511,9 +511,9 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_m32_kernel(FlashArgs
     }
     // The reference is fixed on the first tile: its row maximum, rounded up
     // to a bf16 value.  Later probabilities may exceed 1; a row whose lane
-    // sums pass 2^40 (or overflow) is marked for exact recomputation and its
-    // output here is not used.
-    if (t == 0) {
+    // sums pass 2^40 (or overflow) sends the workgroup through pass 1, whose
+    // reference is the row's maximum (set before the first tile).
+    if (t == 0 && pass == 0) {
       float mx = sacc[0][0];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -526,6 +526,15 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_m32_kernel(FlashArgs
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) sacc[kb] -= mref;
       if (hh == 0) qref[0] = (short)(__float_as_uint(-mref) >> 16);
+      mref0 = mref;
+    }
+    if (pass == 0) {
+      float tm = sacc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) tm = fmaxf(tm, sacc[kb][e]);
+      smax = fmaxf(smax, tm);
     }
     bf16x8 pf[2][2];
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
@@ -558,6 +567,15 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_m32_kernel(FlashArgs
   // Copies run NS-1 tiles ahead of the tile read.
   const int ntiles = blk_qmax / KVT + 1;
   const int wtiles = wave_qmax / KVT + 1;   // tiles with a key at or before one of this wave's queries
+  // returns true when pass 0 found a row that outgrew its reference (the
+  // workgroup then runs pass 1; nothing of pass 0 is stored)
+  auto run = [&](const int pass) -> bool {
+#pragma unroll
+  for (int i = 0; i < DVB; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
+  lrun = 0.f;
+  bad = false;
   fp_wait_vm<0>();   // queries in registers before the copies start
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i)
@@ -573,13 +591,33 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_m32_kernel(FlashArgs
     if (t + NS - 1 < ntiles) issue(t + NS - 1);
     if (t < wtiles) {
       scores(t);
-      softmax_pv(t);
+      softmax_pv(t, pass);
+    }
+  }
+  if (pass == 0) {
+    // one bit per wave in the last stage (every copy has landed and, past
+    // this barrier, every read of the stages is done; the next pass writes
+    // that stage only after its first barrier)
+    fp_bar();
+    volatile int *wbad = (volatile int *)(stages + (NS - 1) * STAGE);
+    const bool any_bad = __any(bad);
+    if (lane == 0) wbad[wave] = any_bad ? 1 : 0;
+    fp_wait_vm_lgkm<0>();
+    fp_bar();
+    int redo = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) redo |= wbad[w];
+    if (redo) {
+      // pass 1's reference: the row's maximum, rounded up to a bf16 value
+      const float m = mref0 + fmaxf(smax, __shfl_xor(smax, 32));
+      unsigned uu = __float_as_uint(m);
+      uu = (uu & 0x80000000u) ? (uu & 0xffff0000u) : ((uu + 0xffffu) & 0xffff0000u);
+      if (hh == 0) qref[0] = (short)(__float_as_uint(-__uint_as_float(uu)) >> 16);
+      return true;
     }
   }
 
   const float l = lrun + __shfl_xor(lrun, 32);
-  const int flag = (int)bad | __shfl_xor((int)bad, 32);
-  if (qpos < L && hh == 0) a.flags[(tok0 + qpos) * NH + h] = (unsigned char)flag;
   if (qpos < L) {
     const float inv = 1.f / l;
     bf16 *orow = (bf16 *)a.o + ((tok0 + qpos) * NH + h) * DV;
@@ -592,79 +630,9 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_m32_kernel(FlashArgs
         store4<bf16>(orow, db * 32 + 8 * j + 4 * hh, v, 0);
       }
   }
-}
-
-// Exact recomputation of the (token, head) rows that the kernel above marked:
-// scores against every visible key in fp32, their maximum, then the
-// normalised weighted sum of values, keys taken 1024 at a time.  One
-// workgroup per marked row; the flags are scanned 256 at a time.
-__global__ __launch_bounds__(256) void flash_fixup_kernel(FlashArgs a) {
-  constexpr int DN = 128, DR = 64, DV = 128, DQK = DN + DR, CH = 1024;
-  __shared__ float qs[DQK];
-  __shared__ float pbuf[CH];
-  __shared__ float red[256];
-  __shared__ int list[256];
-  __shared__ int nlist;
-  const int tid = threadIdx.x, NH = a.n_h, L = a.L;
-  const long ntok = (long)a.B * L, rows = ntok * NH;
-  const bf16 *q = (const bf16 *)a.q, *k = (const bf16 *)a.k, *kr = (const bf16 *)a.kr, *vt = (const bf16 *)a.vt;
-  for (long base = (long)blockIdx.x * 256; base < rows; base += (long)gridDim.x * 256) {
-    if (tid == 0) nlist = 0;
-    __syncthreads();
-    if (base + tid < rows && a.flags[base + tid]) list[atomicAdd(&nlist, 1)] = tid;
-    __syncthreads();
-    const int n = nlist;
-    for (int j = 0; j < n; ++j) {
-      const long row = base + list[j], tok = row / NH;
-      const int h = (int)(row % NH), t = (int)(tok % L);
-      const long tok0 = tok - t;
-      if (tid < DQK) qs[tid] = (float)q[row * DQK + tid];
-      __syncthreads();
-      auto score = [&](int key) {
-        const bf16 *kc = k + ((tok0 + key) * NH + h) * DN, *krr = kr + (tok0 + key) * DR;
-        float acc = 0.f;
-        for (int i = 0; i < DN; ++i) acc += qs[i] * (float)kc[i];
-        for (int i = 0; i < DR; ++i) acc += qs[DN + i] * (float)krr[i];
-        return acc * a.scale_log2;
-      };
-      float mx = -INFINITY;
-      for (int key = tid; key <= t; key += 256) mx = fmaxf(mx, score(key));
-      red[tid] = mx;
-      __syncthreads();
-      for (int w = 128; w > 0; w >>= 1) {
-        if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-        __syncthreads();
-      }
-      const float m = red[0];
-      __syncthreads();
-      const int d = tid & (DV - 1), half = tid >> 7;
-      float lsum = 0.f, oacc = 0.f;
-      for (int c0 = 0; c0 <= t; c0 += CH) {
-        const int c1 = min(c0 + CH, t + 1);
-        for (int key = c0 + tid; key < c1; key += 256) {
-          const float pr = exp2f(score(key) - m);
-          pbuf[key - c0] = pr;
-          lsum += pr;
-        }
-        __syncthreads();
-        const bf16 *vrow = vt + (long)(h * DV + d) * ntok + tok0;
-        for (int key = c0 + half; key < c1; key += 2) oacc += pbuf[key - c0] * (float)vrow[key];
-        __syncthreads();
-      }
-      red[tid] = lsum;
-      __syncthreads();
-      for (int w = 128; w > 0; w >>= 1) {
-        if (tid < w) red[tid] += red[tid + w];
-        __syncthreads();
-      }
-      const float l = red[0];
-      __syncthreads();
-      red[tid] = oacc;
-      __syncthreads();
-      if (tid < DV) ((bf16 *)a.o)[row * DV + d] = (bf16)((red[tid] + red[tid + DV]) / l);
-      __syncthreads();
-    }
-  }
+  return false;
+  };
+  if (run(0)) run(1);
 }
 
 template <typename T, int QB, int NW, int DN, int DR, int DV>
@@ -678,7 +646,7 @@ static hipError_t launch_fp(const FlashArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_flash_prefill(int dtype, const FlashArgs &a, hipStream_t st) {
-  if (dtype == 1 && a.d_nope == 128 && a.d_rope == 64 && a.d_v == 128 && a.L % 8 == 0 && a.L >= 8 && a.flags &&
+  if (dtype == 1 && a.d_nope == 128 && a.d_rope == 64 && a.d_v == 128 && a.L % 8 == 0 && a.L >= 8 &&
       (long)a.B * a.L * 2 * 128 < (1L << 31) && (long)a.n_h * 128 * 64 * 2 < (1L << 31)) {
     constexpr int NW = 8;
     const int qtiles = (a.L + 32 * NW - 1) / (32 * NW);
@@ -686,13 +654,6 @@ hipError_t launch_flash_prefill(int dtype, const FlashArgs &a, hipStream_t st) {
     timing_before("flash_prefill", st);
     hipLaunchKernelGGL((flash_prefill_m32_kernel<NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st, a);
     timing_after("flash_prefill", st);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const long rows = (long)a.B * a.L * a.n_h;
-    const long fgrid = std::min<long>((rows + 255) / 256, 1024);
-    timing_before("flash_fixup", st);
-    hipLaunchKernelGGL(flash_fixup_kernel, dim3((unsigned)fgrid), dim3(256), 0, st, a);
-    timing_after("flash_fixup", st);
     return hipGetLastError();
   }
   if (dtype == 1 && a.d_nope == 128 && a.d_rope == 64 && a.d_v == 128) return launch_fp<bf16, FLASH_QB, FLASH_NW, 128, 64, 128>(a, st);

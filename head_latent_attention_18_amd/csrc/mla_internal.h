@@ -350,7 +350,6 @@ struct FlashArgs {
   const void *kr;   // [B*L][d_rope]
   const void *vt;   // [n_h*d_v][B*L]
   void *o;          // [B*L][n_h][d_v]
-  unsigned char *flags;  // [B*L][n_h] scratch: rows left to exact recomputation
   int B, L, n_h, d_nope, d_rope, d_v;
   float scale_log2;  // softmax scale * log2(e)
 };

@@ -96,9 +96,9 @@ def test_dsv3_prefill_small(B, L):
 def test_dsv3_prefill_large_logit_spread(B, L, tb):
     """The hidden state of one token (tb, in the last sequence) scaled by 16:
     for later queries its key scores far above the first keys (by more than
-    the flash kernel's fixed-reference range in many heads), so those
-    (query, head) rows take the exact recomputation path; they match the
-    oracle like every other row.  The scaled token's own query row is left
+    the flash kernel's fixed-reference range in many heads), so their
+    workgroups run the second pass (reference = each row's maximum); they
+    match the oracle like every other row.  The scaled token's own query row is left
     out: scaled twice (query and key), its scores reach magnitudes where
     rounding q and k to bf16 already moves the softmax weights by more than
     the bf16 bounds, whatever the attention kernel does."""
@@ -201,9 +201,9 @@ def test_dsv3_decode_ragged_paged_small(block_size):
 
 def test_dsv3_decode_large_logit_spread():
     """Cached rows scaled by 64 late in a split: their scores exceed the
-    split's first-tile reference by far more than the kernel's fixed-reference
-    range, so those query rows take the exact recomputation path; all rows
-    still match the oracle."""
+    split's first-tile reference by far more than 2^32, so those workgroups
+    run their second pass (reference = each row's maximum); all rows still
+    match the oracle."""
     from mla_inputs import bf16_bits_to_f32, bf16_round
     wl = make_workload(2, batch=32, uniform_len=300)
     for b, pos, src in ((0, 40, 3), (5, 100, 7), (9, 250, 2)):
