@@ -57,6 +57,11 @@ mla_status check_config(const mla_config *c) {
       c->d_c <= 0 || c->d_cq <= 0)
     return MLA_ERR_SHAPE;
   if (c->d_rope % 2 != 0) return MLA_ERR_SHAPE;
+  // every width within 2^20 (n_heads 2^16), so sums and products of widths
+  // below stay far inside int32 / int64
+  if (c->d_model > (1 << 20) || c->d_cq > (1 << 20) || c->d_c > (1 << 20) || c->d_nope > (1 << 20) ||
+      c->d_rope > (1 << 20) || c->d_v > (1 << 20) || c->n_heads > (1 << 16))
+    return MLA_ERR_UNSUPPORTED;
   if (!(c->rope_base > 0.0) || !isfinite(c->rope_base)) return MLA_ERR_SHAPE;
   if (yarn_on(c)) {
     if (!(c->yarn_factor > 1.0) || !isfinite(c->yarn_factor) || c->yarn_orig_len <= 0) return MLA_ERR_SHAPE;
@@ -67,8 +72,7 @@ mla_status check_config(const mla_config *c) {
   if (c->cache_dtype == MLA_CACHE_FP8_E4M3 && (c->dtype != MLA_BF16 || c->d_c % 128 || c->d_rope % 8))
     return MLA_ERR_UNSUPPORTED;
   if (c->d_rope / 2 > MLA_MAX_ROPE_PAIRS) return MLA_ERR_UNSUPPORTED;
-  if ((long)c->n_heads * (c->d_nope + c->d_rope) > (1L << 24) || c->d_model > (1 << 20))
-    return MLA_ERR_UNSUPPORTED;
+  if ((long)c->n_heads * ((long)c->d_nope + c->d_rope) > (1L << 24)) return MLA_ERR_UNSUPPORTED;
   const int big = c->dtype == MLA_BF16 ? 64 : 32, small = c->dtype == MLA_BF16 ? 32 : 16;
   if (c->d_model % big || c->d_cq % big || c->d_c % big || c->d_nope % big ||
       ((long)c->n_heads * c->d_v) % big || c->d_rope % small || c->d_v % small)
@@ -170,6 +174,12 @@ SplitK choose_splitk(int dtype, int64_t M, int64_t N, int64_t K, int batch) {
     if (nkt % s == 0 && s <= want && (!stream || skinny_nst_supported((int)(nkt / s)))) r.splits = (int)s;
   r.k_chunk = (int)(K / r.splits);
   return r;
+}
+
+// decode size envelope: at most 2^20 new tokens and 2^20 query rows per
+// sequence, so every product in the plan stays far inside int64 / size_t
+bool decode_sizes_ok(const mla_config *c, int32_t batch, int32_t n_q) {
+  return (int64_t)batch * n_q <= (1L << 20) && (int64_t)n_q * c->n_heads <= (1L << 20);
 }
 
 struct DecodePlan {
@@ -473,12 +483,16 @@ mla_status mla_workspace_size(const mla_config *cfg, int32_t op, int32_t batch, 
   if (s != MLA_OK) return s;
   if (!bytes) return MLA_ERR_NULL;
   if (batch <= 0 || len_or_nq <= 0) return MLA_ERR_SHAPE;
+  // the same size envelopes as the entry points (they bound every product
+  // in the plans)
   if (op == MLA_OP_PREFILL) {
+    if ((int64_t)batch * len_or_nq > (1L << 24)) return MLA_ERR_UNSUPPORTED;
     *bytes = plan_prefill(cfg, (int64_t)batch * len_or_nq).total;
     return MLA_OK;
   }
   if (op == MLA_OP_DECODE) {
     if (max_cache_len < len_or_nq) return MLA_ERR_SHAPE;
+    if (!decode_sizes_ok(cfg, batch, len_or_nq)) return MLA_ERR_UNSUPPORTED;
     *bytes = plan_decode(cfg, batch, len_or_nq, max_cache_len).total;
     return MLA_OK;
   }
@@ -595,7 +609,7 @@ mla_status check_decode(const mla_config *cfg, const mla_weights *w, const void 
   if (cache_lens_host)
     for (int32_t b = 0; b < batch; ++b)
       if (cache_lens_host[b] < n_q || cache_lens_host[b] > max_cache_len) return MLA_ERR_SHAPE;
-  if ((int64_t)batch * n_q > (1L << 20) || (int64_t)n_q * cfg->n_heads > (1L << 20)) return MLA_ERR_UNSUPPORTED;
+  if (!decode_sizes_ok(cfg, batch, n_q)) return MLA_ERR_UNSUPPORTED;
   if (!attention_supported(cfg, MLA_OP_DECODE)) return MLA_ERR_UNSUPPORTED;
   if ((s = check_cache(cache, batch, max_cache_len)) != MLA_OK) return s;
   if (cache_fp8(cfg) && cache->block_table && cache->block_size % 32) return MLA_ERR_UNSUPPORTED;
@@ -756,7 +770,11 @@ mla_status mla_decode_noalloc(const mla_config *cfg, const mla_weights *w, const
 }
 
 const char *mla_status_string(mla_status s) {
-  switch (s) {
+  // callers may pass any int: its bytes are read as an int (loading an enum
+  // value outside the enumerators' range is undefined in C++)
+  int code;
+  memcpy(&code, &s, sizeof code);
+  switch (code) {
     case MLA_OK: return "ok";
     case MLA_ERR_NULL: return "required pointer is NULL";
     case MLA_ERR_SHAPE: return "size or dimension out of range";

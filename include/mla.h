@@ -92,7 +92,8 @@ typedef enum mla_cache_dtype {
 /* Layer dimensions.  Supported envelope (checked, MLA_ERR_UNSUPPORTED
  * otherwise): d_rope even; for BF16 d_model, d_cq, d_c multiples of 64,
  * d_nope, d_rope, d_v multiples of 32, n_heads*d_v a multiple of 64; for FP32
- * the same with 32 and 16.  DeepSeek-V3: 7168, 128, 128, 64, 128, 512, 1536. */
+ * the same with 32 and 16; every width at most 2^20 and n_heads at most
+ * 2^16.  DeepSeek-V3: 7168, 128, 128, 64, 128, 512, 1536. */
 typedef struct mla_config {
   int32_t d_model;   /* hidden width of h and u */
   int32_t n_heads;   /* n_h */
@@ -171,7 +172,10 @@ size_t mla_mha_cache_elements_per_token(const mla_config *cfg);
  *   MLA_OP_DECODE : batch sequences of len_or_nq new tokens each, whose
  *     cache lengths (after appending) are at most max_cache_len; the split
  *     plan, and with it the size, depends only on these numbers.
- * The decode call must be given the same max_cache_len. */
+ * The decode call must be given the same max_cache_len.  Sizes outside the
+ * entry points' envelopes (prefill: batch * len_or_nq > 2^24; decode:
+ * batch * len_or_nq or len_or_nq * n_heads > 2^20) return
+ * MLA_ERR_UNSUPPORTED, as those calls would. */
 mla_status mla_workspace_size(const mla_config *cfg, int32_t op, int32_t batch,
                               int32_t len_or_nq, int32_t max_cache_len, size_t *bytes);
 
