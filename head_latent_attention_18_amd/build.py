@@ -1,9 +1,10 @@
 """Build libmla.so (gfx950) in place with hipcc.
 
-    python -m head_latent_attention_18_amd.build [--verbose]
+    python -m head_latent_attention_18_amd.build [--verbose] [--debug-checks]
 
 Every .hip file under csrc/ is compiled to an object in parallel and the
-objects are linked into head_latent_attention_18_amd/libmla.so.
+objects are linked into head_latent_attention_18_amd/lib/libmla.so
+(--debug-checks: lib/libmla_debug.so, with the device range checks).
 """
 from __future__ import annotations
 
@@ -19,6 +20,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "lib", "libmla.so")
+# debug library: device range checks of block-table entries, cache lengths and
+# positions (MLA_DEBUG_CHECKS), reported as MLA_ERR_CACHE after the call
+LIB_DEBUG = os.path.join(PKG, "lib", "libmla_debug.so")
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -44,8 +48,10 @@ def _compile(src: str, obj: str, extra) -> str:
     return "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
 
 
-def build(verbose: bool = False, extra=()) -> str:
+def build(verbose: bool = False, extra=(), debug: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    lib = LIB_DEBUG if debug else LIB
+    extra = list(extra) + (["-DMLA_DEBUG_CHECKS=1"] if debug else [])
     tmp = tempfile.mkdtemp(prefix="libmla_")
     try:
         objs = [os.path.join(tmp, os.path.basename(s) + ".o") for s in srcs]
@@ -55,19 +61,19 @@ def build(verbose: bool = False, extra=()) -> str:
             for s, l in zip(srcs, logs):
                 if l.strip():
                     print(f"== {os.path.basename(s)}\n{l}")
-        os.makedirs(os.path.dirname(LIB), exist_ok=True)
-        out = LIB + ".tmp"
+        os.makedirs(os.path.dirname(lib), exist_ok=True)
+        out = lib + ".tmp"
         r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out],
                            capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{r.stderr}")
-        os.replace(out, LIB)
+        os.replace(out, lib)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB
+    return lib
 
 
 if __name__ == "__main__":
     v = "--verbose" in sys.argv
     extra = ["-Rpass-analysis=kernel-resource-usage"] if "--resources" in sys.argv else []
-    print(build(verbose=v or bool(extra), extra=extra))
+    print(build(verbose=v or bool(extra), extra=extra, debug="--debug-checks" in sys.argv))

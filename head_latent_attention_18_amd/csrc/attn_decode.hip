@@ -48,7 +48,11 @@ inline int decode_grid(const DecodeArgs &a) { return 8 * ((a.W * a.row_groups + 
 // ---------------------------------------------------------------------------
 // cache rows of sequence b the plan covers: its length, clamped to the cache
 __device__ inline int plan_len(const DecodeArgs &a, int b) {
-  return (int)max(0L, min((long)a.lens[b], a.cache.cap));
+  const int len = a.lens[b];
+  // a length outside [n_q, cache capacity] is clamped (and reported in
+  // debug builds)
+  if (len < a.n_q || len > a.cache.cap) dbg_flag(a.cache, MLA_DBG_LENGTH);
+  return (int)max(0L, min((long)len, a.cache.cap));
 }
 __device__ inline int plan_tiles(int len) { return (len + KVT - 1) / KVT; }
 
@@ -566,8 +570,8 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
     long trow;
     if constexpr (PAGED) {
       const int q = block_of(a.cache, kvb);
-      const int blk = __builtin_amdgcn_readfirstlane(tab_lds ? btab[q - q0]
-                                                             : a.cache.table[(long)b * a.cache.max_blocks + q]);
+      const int blk = checked_block(a.cache, __builtin_amdgcn_readfirstlane(
+                                                 tab_lds ? btab[q - q0] : a.cache.table[(long)b * a.cache.max_blocks + q]));
       trow = (long)blk * a.cache.block_size + (kvb - q * a.cache.block_size);
     } else {
       trow = seq_row0 + kvb;

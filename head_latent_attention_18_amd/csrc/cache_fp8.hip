@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void cache_append_fp8_kernel(CacheAppendArgs a
   int seq = 0, pos = 0;
   row_seq_pos(a.rows, m, seq, pos);
   // rows outside the described cache are never written
-  if (seq < 0 || seq >= a.cache.batch || pos < 0 || pos >= a.cache.cap) return;
+  if (!cache_row_ok(a.cache, seq, pos)) return;
   unsigned char *row = (unsigned char *)a.cache.pool + cache_row(a.cache, seq, pos) * (long)a.cache.row_bytes;
   float *scales = (float *)(row + a.d_c + 2 * a.d_rope);
   const bf16 *x = a.ckv + (long)m * a.d_c;

@@ -261,8 +261,51 @@ float softmax_scale_log2(const mla_config *c) {
   return (float)s;
 }
 
+#ifdef MLA_DEBUG_CHECKS
+// Debug builds: one error word per device (its device address fetched once
+// per device, like the allocation-free decode's array), cleared before a
+// call's kernels and read after them.
+static __device__ unsigned dbg_word;
+std::mutex g_dbg_mu;
+unsigned *g_dbg_ptr[256];
+
+unsigned *debug_word() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return nullptr;
+  std::lock_guard<std::mutex> lock(g_dbg_mu);
+  if (!g_dbg_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(dbg_word)) != hipSuccess || !ptr) return nullptr;
+    g_dbg_ptr[dev] = (unsigned *)ptr;
+  }
+  return g_dbg_ptr[dev];
+}
+
+mla_status debug_begin(hipStream_t st) {
+  unsigned *d = debug_word();
+  if (!d) return MLA_ERR_HIP;
+  return hipMemsetAsync(d, 0, sizeof(unsigned), st) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+// after the call's kernels: wait for them and report what they recorded
+mla_status debug_end(hipStream_t st, mla_status s) {
+  if (s != MLA_OK) return s;
+  unsigned hv = 0;
+  if (hipMemcpyAsync(&hv, debug_word(), sizeof hv, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return MLA_ERR_HIP;
+  return hv ? MLA_ERR_CACHE : MLA_OK;
+}
+#else
+unsigned *debug_word() { return nullptr; }
+mla_status debug_begin(hipStream_t) { return MLA_OK; }
+mla_status debug_end(hipStream_t, mla_status s) { return s; }
+#endif
+
 CacheRef cache_ref(const mla_config *c, const mla_cache *k, int32_t batch) {
   CacheRef r;
+  r.n_blocks = k->block_table ? k->n_blocks : 0;
+  r.dbg = debug_word();
   r.batch = batch;
   r.cap = k->block_table ? (long)k->max_blocks_per_seq * k->block_size : (long)k->max_len;
   r.pool = k->pool;
@@ -511,8 +554,10 @@ mla_status mla_compress_kv(const mla_config *cfg, const mla_weights *w, const vo
   if (cache_fp8(cfg)) return MLA_ERR_UNSUPPORTED;
   RowMap rows = {ROWS_EXPLICIT, 1, nullptr, seq_idx, pos};
   SplitK sk = {1, cfg->d_model};
-  return hip_status(run_compress(cfg, w, h, n, rows, cache, batch, false, nullptr, nullptr, nullptr, sk, nullptr,
-                                 (hipStream_t)stream));
+  const hipStream_t st = (hipStream_t)stream;
+  if ((s = debug_begin(st)) != MLA_OK) return s;
+  return debug_end(st, hip_status(run_compress(cfg, w, h, n, rows, cache, batch, false, nullptr, nullptr, nullptr,
+                                               sk, nullptr, st)));
 }
 
 mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *h, int32_t batch, int32_t len,
@@ -533,6 +578,7 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
   if (workspace_bytes < p.total) return MLA_ERR_WORKSPACE;
 
   hipStream_t st = (hipStream_t)stream;
+  if ((s = debug_begin(st)) != MLA_OK) return s;
   char *ws = (char *)workspace;
   const int dt = cfg->dtype;
   const int M = (int)T;
@@ -590,7 +636,7 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
   }
   one.k_chunk = NH * cfg->d_v;
   e = run_output(cfg, w, o, M, u, one, nullptr, st);
-  return hip_status(e);
+  return debug_end(st, hip_status(e));
 }
 
 }  // extern "C"
@@ -754,7 +800,9 @@ mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h
   if (s != MLA_OK) return s;
   if (!workspace) return MLA_ERR_WORKSPACE;
   if (workspace_bytes < p.total) return MLA_ERR_WORKSPACE;
-  return decode_steps(cfg, w, h, batch, n_q, cache_lens, cache, u, o_heads, (char *)workspace, p, stream);
+  if ((s = debug_begin((hipStream_t)stream)) != MLA_OK) return s;
+  return debug_end((hipStream_t)stream,
+                   decode_steps(cfg, w, h, batch, n_q, cache_lens, cache, u, o_heads, (char *)workspace, p, stream));
 }
 
 mla_status mla_decode_noalloc(const mla_config *cfg, const mla_weights *w, const void *h, int32_t batch, int32_t n_q,
@@ -766,7 +814,8 @@ mla_status mla_decode_noalloc(const mla_config *cfg, const mla_weights *w, const
   if (p.total > (size_t)MLA_NOALLOC_WORKSPACE_BYTES) return MLA_ERR_WORKSPACE;
   char *ws = nullptr;
   if (scratch_for_current_device(&ws) != hipSuccess) return MLA_ERR_HIP;
-  return decode_steps(cfg, w, h, batch, n_q, cache_lens, cache, u, o_heads, ws, p, stream);
+  if ((s = debug_begin((hipStream_t)stream)) != MLA_OK) return s;
+  return debug_end((hipStream_t)stream, decode_steps(cfg, w, h, batch, n_q, cache_lens, cache, u, o_heads, ws, p, stream));
 }
 
 const char *mla_status_string(mla_status s) {

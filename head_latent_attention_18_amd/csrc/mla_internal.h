@@ -87,7 +87,37 @@ struct CacheRef {
   int bs_shift;       // log2(block_size) when it is a power of two, else -1
   int row_bytes;      // bytes per cached row
   int fp8;            // rows in the FP8 layout: d_c E4M3 codes | d_R bf16 | d_c/128 fp32 scales
+  int n_blocks;       // blocks in the pool (paged)
+  unsigned *dbg;      // debug builds: error word (bits MLA_DBG_*), else unused
 };
+
+// Debug builds (MLA_DEBUG_CHECKS) check on the device every block-table
+// entry a kernel uses and every cache length it is given, and record what
+// they find in the error word; the host reads it after the call.
+#define MLA_DBG_BLOCK 1u    // a block-table entry outside [0, n_blocks)
+#define MLA_DBG_LENGTH 2u   // a cache length or position outside the cache
+
+__device__ inline void dbg_flag(const CacheRef &c, unsigned bit) {
+#ifdef MLA_DEBUG_CHECKS
+  atomicOr(c.dbg, bit);
+#else
+  (void)c;
+  (void)bit;
+#endif
+}
+
+// A block-table entry as used: in debug builds one outside the pool is
+// reported and replaced by block 0 (in bounds), so a read stays inside the
+// pool; writers ask cache_row_ok first and skip such a row.
+__device__ inline int checked_block(const CacheRef &c, int blk) {
+#ifdef MLA_DEBUG_CHECKS
+  if (blk < 0 || blk >= c.n_blocks) {
+    dbg_flag(c, MLA_DBG_BLOCK);
+    return 0;
+  }
+#endif
+  return blk;
+}
 
 __device__ inline int block_of(const CacheRef &c, int pos) {
   return c.bs_shift >= 0 ? (pos >> c.bs_shift) : pos / c.block_size;
@@ -96,10 +126,30 @@ __device__ inline int block_of(const CacheRef &c, int pos) {
 __device__ inline long cache_row(const CacheRef &c, int seq, int pos) {
   if (c.table) {
     const int q = block_of(c, pos);
-    const int blk = c.table[(long)seq * c.max_blocks + q];
+    const int blk = checked_block(c, c.table[(long)seq * c.max_blocks + q]);
     return (long)blk * c.block_size + (pos - q * c.block_size);
   }
   return (long)seq * c.max_len + pos;
+}
+
+// May a writer store position pos of sequence seq?  Rows outside the
+// described cache are never written (silently in release builds; debug
+// builds report them, and a block-table entry outside the pool).
+__device__ inline bool cache_row_ok(const CacheRef &c, int seq, int pos) {
+  if (seq < 0 || seq >= c.batch || pos < 0 || pos >= c.cap) {
+    dbg_flag(c, MLA_DBG_LENGTH);
+    return false;
+  }
+#ifdef MLA_DEBUG_CHECKS
+  if (c.table) {
+    const int blk = c.table[(long)seq * c.max_blocks + block_of(c, pos)];
+    if (blk < 0 || blk >= c.n_blocks) {
+      dbg_flag(c, MLA_DBG_BLOCK);
+      return false;
+    }
+  }
+#endif
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -190,7 +240,7 @@ __device__ inline void epi_store4(const Epi &e, int z, int m, int n, float v[4])
     off = (long)z * g.batch_stride + (long)m * g.ld + (long)hh * g.head_ld + g.col_off + d;
   } else {
     // rows outside the described cache are never written
-    if (seq < 0 || seq >= e.cache.batch || pos < 0 || pos >= e.cache.cap) return;
+    if (!cache_row_ok(e.cache, seq, pos)) return;
     base = e.cache.pool;
     off = cache_row(e.cache, seq, pos) * e.cache.d_row + g.col_off + c;
   }
@@ -289,7 +339,7 @@ __device__ inline void col_store(const ColPlan &p, const Epi &e, int z, int m, f
   if (p.kind != SEG_CACHE) {
     off = (long)z * p.batch_stride + (long)m * p.ld + p.col;
   } else {
-    if (seq < 0 || seq >= e.cache.batch || pos < 0 || pos >= e.cache.cap) return;
+    if (!cache_row_ok(e.cache, seq, pos)) return;
     base = e.cache.pool;
     off = cache_row(e.cache, seq, pos) * e.cache.d_row + p.col;
   }
@@ -372,7 +422,7 @@ struct DecodeArgs {
   int row_groups;     // groups of query rows (n_q*n_h rows per sequence)
   int rows;           // query rows per group (the workgroup's share)
   void *o_part;       // [slots][n_q*n_h][d_c], normalised, in the layer's dtype
-  float *lse_part;    // [slots][n_q*n_h]  (log2 units; NaN = recompute the row)
+  float *lse_part;    // [slots][n_q*n_h]  (log2 units)
   void *o_lat;        // combine output [B*n_q][n_h][d_c]
 };
 int decode_rows_per_group(int dtype, long B, long R, int cus);

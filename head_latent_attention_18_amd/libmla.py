@@ -48,41 +48,47 @@ class mla_cache(ctypes.Structure):
 _LIB = None
 
 
+def load(path: str) -> ctypes.CDLL:
+    """A libmla build at `path` (e.g. lib/libmla_debug.so) with every
+    function's argument and result types declared."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"libmla is not built ({path} missing); run "
+                           "`python -m head_latent_attention_18_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = POINTER
+    lib.mla_cache_bytes_per_token.argtypes = [P(mla_config)]
+    lib.mla_cache_bytes_per_token.restype = c_size_t
+    lib.mla_mha_cache_elements_per_token.argtypes = [P(mla_config)]
+    lib.mla_mha_cache_elements_per_token.restype = c_size_t
+    lib.mla_workspace_size.argtypes = [P(mla_config), c_int32, c_int32, c_int32, c_int32, P(c_size_t)]
+    lib.mla_workspace_size.restype = c_int32
+    lib.mla_compress_kv.argtypes = [P(mla_config), P(mla_weights), c_void_p, c_int32, c_void_p, c_void_p,
+                                    c_int32, P(mla_cache), c_void_p]
+    lib.mla_compress_kv.restype = c_int32
+    lib.mla_prefill.argtypes = [P(mla_config), P(mla_weights), c_void_p, c_int32, c_int32, P(mla_cache),
+                                c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.mla_prefill.restype = c_int32
+    lib.mla_decode.argtypes = [P(mla_config), P(mla_weights), c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                               c_int32, P(mla_cache), c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.mla_decode.restype = c_int32
+    lib.mla_decode_noalloc.argtypes = [P(mla_config), P(mla_weights), c_void_p, c_int32, c_int32, c_void_p,
+                                       c_void_p, c_int32, P(mla_cache), c_void_p, c_void_p, c_void_p]
+    lib.mla_decode_noalloc.restype = c_int32
+    lib.mla_status_string.argtypes = [c_int32]
+    lib.mla_status_string.restype = c_char_p
+    lib.mla_version.argtypes = []
+    lib.mla_version.restype = c_char_p
+    lib.mla_timing_enable.argtypes = [c_int32]
+    lib.mla_timing_enable.restype = c_int32
+    lib.mla_timing_read.argtypes = [P(c_char_p), P(c_double), P(c_int64), c_int32]
+    lib.mla_timing_read.restype = c_int32
+    return lib
+
+
 def _lib():
     global _LIB
     if _LIB is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"libmla is not built ({LIB_PATH} missing); run "
-                               "`python -m head_latent_attention_18_amd.build`")
-        lib = ctypes.CDLL(LIB_PATH)
-        P = POINTER
-        lib.mla_cache_bytes_per_token.argtypes = [P(mla_config)]
-        lib.mla_cache_bytes_per_token.restype = c_size_t
-        lib.mla_mha_cache_elements_per_token.argtypes = [P(mla_config)]
-        lib.mla_mha_cache_elements_per_token.restype = c_size_t
-        lib.mla_workspace_size.argtypes = [P(mla_config), c_int32, c_int32, c_int32, c_int32, P(c_size_t)]
-        lib.mla_workspace_size.restype = c_int32
-        lib.mla_compress_kv.argtypes = [P(mla_config), P(mla_weights), c_void_p, c_int32, c_void_p, c_void_p,
-                                        c_int32, P(mla_cache), c_void_p]
-        lib.mla_compress_kv.restype = c_int32
-        lib.mla_prefill.argtypes = [P(mla_config), P(mla_weights), c_void_p, c_int32, c_int32, P(mla_cache),
-                                    c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
-        lib.mla_prefill.restype = c_int32
-        lib.mla_decode.argtypes = [P(mla_config), P(mla_weights), c_void_p, c_int32, c_int32, c_void_p, c_void_p,
-                                   c_int32, P(mla_cache), c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
-        lib.mla_decode.restype = c_int32
-        lib.mla_decode_noalloc.argtypes = [P(mla_config), P(mla_weights), c_void_p, c_int32, c_int32, c_void_p,
-                                           c_void_p, c_int32, P(mla_cache), c_void_p, c_void_p, c_void_p]
-        lib.mla_decode_noalloc.restype = c_int32
-        lib.mla_status_string.argtypes = [c_int32]
-        lib.mla_status_string.restype = c_char_p
-        lib.mla_version.argtypes = []
-        lib.mla_version.restype = c_char_p
-        lib.mla_timing_enable.argtypes = [c_int32]
-        lib.mla_timing_enable.restype = c_int32
-        lib.mla_timing_read.argtypes = [P(c_char_p), P(c_double), P(c_int64), c_int32]
-        lib.mla_timing_read.restype = c_int32
-        _LIB = lib
+        _LIB = load(LIB_PATH)
     return _LIB
 
 

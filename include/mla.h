@@ -139,8 +139,14 @@ typedef struct mla_weights {
  *   Paged (block_table != NULL): block_table is int32 [batch][max_blocks_per_seq]
  *     on the device; position t of sequence b is row
  *     block_table[b*max_blocks_per_seq + t/block_size]*block_size + t%block_size.
- *     The caller allocates the blocks a call writes or reads; entries are
- *     not range-checked on the device. */
+ *     The caller allocates the blocks a call writes or reads.  The release
+ *     library does not range-check entries on the device (an entry outside
+ *     the pool sends a kernel outside it).  The debug library
+ *     (libmla_debug.so, built with MLA_DEBUG_CHECKS) checks on the device
+ *     every entry, cache length and position a call uses, skips the
+ *     accesses it rejects, waits for the call on its stream and returns
+ *     MLA_ERR_CACHE if any check failed (it clears a word of device memory
+ *     with hipMemsetAsync first: not for graph capture). */
 typedef struct mla_cache {
   void *pool;
   int32_t block_size;          /* rows per block (paged); any value >= 1 */

@@ -1,0 +1,132 @@
+"""The debug library (lib/libmla_debug.so, MLA_DEBUG_CHECKS): device range
+checks of block-table entries, cache lengths and positions, reported as
+MLA_ERR_CACHE once the call has finished.  A valid call gives the release
+library's results bit for bit; each invalid case below goes to the debug
+library only, which checks every entry, length and position before using
+it (the release library would read or write outside the pool)."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from head_latent_attention_18_amd import libmla as L
+from head_latent_attention_18_amd.layer import CacheBuf
+from mla_inputs import make_workload
+
+from tests.gpu_harness import decode_cache, layer_for, say, upload
+
+pytestmark = pytest.mark.gpu
+
+DEBUG_LIB = os.path.join(os.path.dirname(L.LIB_PATH), "libmla_debug.so")
+ERR_CACHE = -5
+
+
+@pytest.fixture(scope="module")
+def dbg():
+    if not os.path.exists(DEBUG_LIB):
+        pytest.skip("debug library not built")
+    return L.load(DEBUG_LIB)
+
+
+def _paged_setup(cache_fp8=False):
+    wl = make_workload(4, batch=3, ragged_max=300, block_size=64, cache_fp8=cache_fp8)
+    layer = layer_for(wl)
+    cache = decode_cache(wl, layer)
+    h = upload(wl.h_f32, wl.h_bits, True)
+    return wl, layer, cache, h
+
+
+def _decode(lib, wl, layer, cache, h, lens_dev, max_len):
+    B, nq = wl.batch, wl.n_q
+    u = torch.zeros(B, nq, wl.dims.d_model, dtype=torch.bfloat16, device="cuda")
+    nbytes = L.mla_workspace_size(layer.cfg, L.MLA_OP_DECODE, B, nq, max_len)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    code = lib.mla_decode(ctypes.byref(layer.cfg), ctypes.byref(layer.cw), h.data_ptr(), B, nq, lens_dev.data_ptr(),
+                          None, max_len, ctypes.byref(cache.desc), u.data_ptr(), None, ws.data_ptr(), nbytes, None)
+    torch.cuda.synchronize()
+    return code, u
+
+
+def _with_table(cache, table_host):
+    """The same pool under a modified block table (a new descriptor)."""
+    return CacheBuf.paged(cache.pool, cache.block_size, table_host)
+
+
+def test_debug_valid_call_matches_release(dbg):
+    wl, layer, cache, h = _paged_setup()
+    lens = torch.from_numpy(wl.lens.astype(np.int32)).cuda()
+    ml = int(wl.lens.max())
+    pool0 = cache.pool.clone()
+    code, u_dbg = _decode(dbg, wl, layer, cache, h, lens, ml)
+    assert code == 0
+    cache.pool.copy_(pool0)
+    code, u_rel = _decode(L.lib(), wl, layer, cache, h, lens, ml)
+    assert code == 0
+    assert torch.equal(u_dbg, u_rel)
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("bad", ["past_pool", "negative"])
+def test_debug_bad_block_entry(dbg, fp8, bad):
+    wl, layer, cache, h = _paged_setup(cache_fp8=fp8)
+    t = cache.table_host.copy()
+    nblk = cache.pool.shape[0] // cache.block_size
+    # a block the longest sequence reads (its first), and one the append writes
+    b = int(np.argmax(wl.lens))
+    t[b, 0] = nblk + 7 if bad == "past_pool" else -3
+    last = (int(wl.lens[0]) - 1) // cache.block_size
+    t[0, last] = nblk + 11 if bad == "past_pool" else -1
+    lens = torch.from_numpy(wl.lens.astype(np.int32)).cuda()
+    say(f"debug decode, bad block entries ({bad}, fp8={fp8})")
+    code, _ = _decode(dbg, wl, layer, _with_table(cache, t), h, lens, int(wl.lens.max()))
+    assert code == ERR_CACHE
+
+
+def test_debug_bad_device_lengths(dbg):
+    """Device lengths are checked against the cache's capacity (table width
+    times block size: the bound that keeps accesses inside the pool)."""
+    wl, layer, cache, h = _paged_setup()
+    ml = int(wl.lens.max())
+    cap = cache.table_host.shape[1] * cache.block_size
+    for bad_len in (cap + 40, 0):   # past the cache, and shorter than the new token
+        lens_np = wl.lens.astype(np.int32).copy()
+        lens_np[1] = bad_len
+        say(f"debug decode, device length {bad_len} (capacity {cap})")
+        code, _ = _decode(dbg, wl, layer, cache, h, torch.from_numpy(lens_np).cuda(), ml)
+        assert code == ERR_CACHE
+
+
+def test_debug_prefill_bad_block_entry(dbg):
+    wl = make_workload(3, batch=1, seq_len=256)
+    layer = layer_for(wl)
+    h = upload(wl.h_f32, wl.h_bits, True)
+    nblk = 4
+    pool = torch.zeros(nblk * 64, wl.dims.d_row, dtype=torch.bfloat16, device="cuda")
+    table = np.array([[0, 1, nblk + 2, 3]], dtype=np.int32)
+    cache = CacheBuf.paged(pool, 64, table)
+    u = torch.empty(1, 256, wl.dims.d_model, dtype=torch.bfloat16, device="cuda")
+    nbytes = L.mla_workspace_size(layer.cfg, L.MLA_OP_PREFILL, 1, 256)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    say("debug prefill, bad block entry")
+    code = dbg.mla_prefill(ctypes.byref(layer.cfg), ctypes.byref(layer.cw), h.data_ptr(), 1, 256,
+                           ctypes.byref(cache.desc), u.data_ptr(), None, ws.data_ptr(), nbytes, None)
+    torch.cuda.synchronize()
+    assert code == ERR_CACHE
+    # the rows of the valid blocks were written, the pool past them untouched
+    assert torch.count_nonzero(pool[:64]) > 0
+
+
+def test_debug_compress_position_outside_cache(dbg):
+    wl = make_workload(3, batch=1, seq_len=8)
+    layer = layer_for(wl)
+    h = upload(wl.h_f32, wl.h_bits, True)[0]
+    cache = layer.new_cache(1, 16)
+    seq = torch.zeros(8, dtype=torch.int32, device="cuda")
+    pos = torch.tensor([0, 1, 2, 3, 4, 5, 6, 16], dtype=torch.int32, device="cuda")   # 16 is past max_len
+    say("debug compress, position past the cache")
+    code = dbg.mla_compress_kv(ctypes.byref(layer.cfg), ctypes.byref(layer.cw), h.data_ptr(), 8, seq.data_ptr(),
+                               pos.data_ptr(), 1, ctypes.byref(cache.desc), None)
+    torch.cuda.synchronize()
+    assert code == ERR_CACHE
