@@ -591,7 +591,32 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
       cr += NC / CH + (wrap ? 1 : 0);
     }
   };
-  auto copy_tile = [&](int t) { copy_rows(tile_src(t), 0, min(KVT, kv_end - (kv_beg + t * KVT)) - 1, t % NS); };
+  // A full tile's per-lane source offsets are the same for every tile (only
+  // the tile's base, a scalar, changes): formed once, they leave the copy of
+  // a full tile with no vector arithmetic; a partial last tile clamps.
+  unsigned full_off[LOADS];
+  {
+    int cr = r0, cc = c0;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      full_off[i] = (unsigned)(cr * D + ((cc ^ (cr & 7)) << 3)) * 2u;
+      cc += NC % CH;
+      const bool wrap = cc >= CH;
+      cc -= wrap ? CH : 0;
+      cr += NC / CH + (wrap ? 1 : 0);
+    }
+  }
+  auto copy_tile = [&](int t) {
+    const int last = min(KVT, kv_end - (kv_beg + t * KVT)) - 1;
+    if (last == KVT - 1) {
+      const char *src = tile_src(t);
+      const unsigned dst0 = lds_stages + (unsigned)((t % NS) * STAGE * 2) + (wave - 4) * 1024;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) dma16(src, full_off[i], dst0 + i * NC * 16);
+    } else {
+      copy_rows(tile_src(t), 0, last, t % NS);
+    }
+  };
 
   // FP8 tiles: copying thread ct converts row ct >> 3 of a tile, part
   // j = ct & 7: the 16-code pieces j + 8i (i = 0..3; codes 16(j + 8i) ..
@@ -697,6 +722,11 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
       const int qr = min(rbase + rl, R - 1);
       limit[j] = min(len - a.n_q + qr / a.n_h, kv_end - 1);
     }
+    // the wave's smallest limit: tiles ending at or below it need no mask
+    int lim_all = min(limit[0], limit[1]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) lim_all = min(lim_all, __shfl_xor(lim_all, o));
+    lim_all = __builtin_amdgcn_readfirstlane(lim_all);
     // Score reads: row kh*16 + lrow of the tile, logical chunk 4q+lgrp
     // (natural k order), physical chunk (4q+lgrp) ^ (lrow & 7) =
     // 4(q ^ fq) + (lgrp ^ (lrow & 3)) with fq = (lrow >> 2) & 1: even and odd
@@ -733,15 +763,19 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
         }
         float sv[2][4], mt[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          mt[j] = -INFINITY;
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kv = kvb + 16 * kh + 4 * lgrp + i;
-            const float x = (sacc[j][0][i] + sacc[j][1][i]) * sl2;
-            sv[j][i] = (kv <= limit[j]) ? x : -INFINITY;
-            mt[j] = fmaxf(mt[j], sv[j][i]);
-          }
+          for (int i = 0; i < 4; ++i) sv[j][i] = (sacc[j][0][i] + sacc[j][1][i]) * sl2;
+        if (kvb + KVT - 1 > lim_all) {                 // wave-uniform: a key past some row's limit
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (kvb + 16 * kh + 4 * lgrp + i > limit[j]) sv[j][i] = -INFINITY;
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          mt[j] = fmaxf(fmaxf(sv[j][0], sv[j][1]), fmaxf(sv[j][2], sv[j][3]));
           mx[j] = fmaxf(mx[j], mt[j]);
         }
         // the first tile fixes the reference of each row (max over both key
