@@ -482,29 +482,51 @@ hipError_t run_output(const mla_config *c, const mla_weights *w, const void *o, 
 // ---------------------------------------------------------------------------
 // Kernel timing
 // ---------------------------------------------------------------------------
-struct TimedLaunch { const char *name; hipEvent_t start, stop; };
+// One slot per timed launch.  The slots, the count and the session number are
+// guarded by g_timing_mu; a bracket opened by timing_before is closed by the
+// same host thread's timing_after (t_open), so launches from several threads
+// get their own slots.  A slot counts once its stop event is recorded in the
+// session that opened it.
+struct TimedLaunch { const char *name; hipEvent_t start, stop; bool done; };
+std::mutex g_timing_mu;
 bool g_timing = false;
 std::vector<TimedLaunch> g_events;
 size_t g_used = 0;
+unsigned long g_session = 0;
+struct OpenBracket { long slot = -1; unsigned long session = 0; };
+thread_local OpenBracket t_open;
 
 }  // namespace
 
 namespace mla {
 void timing_before(const char *name, hipStream_t st) {
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  t_open.slot = -1;
   if (!g_timing) return;
   if (g_used == g_events.size()) {
-    TimedLaunch t;
-    t.name = name;
-    if (hipEventCreate(&t.start) != hipSuccess || hipEventCreate(&t.stop) != hipSuccess) return;
+    TimedLaunch t{name, nullptr, nullptr, false};
+    if (hipEventCreate(&t.start) != hipSuccess) return;
+    if (hipEventCreate(&t.stop) != hipSuccess) {
+      (void)hipEventDestroy(t.start);
+      return;
+    }
     g_events.push_back(t);
   }
-  g_events[g_used].name = name;
-  (void)hipEventRecord(g_events[g_used].start, st);
+  TimedLaunch &t = g_events[g_used];
+  t.name = name;
+  t.done = false;
+  if (hipEventRecord(t.start, st) != hipSuccess) return;
+  t_open.slot = (long)g_used++;
+  t_open.session = g_session;
 }
 void timing_after(const char *name, hipStream_t st) {
-  if (!g_timing || g_used >= g_events.size() || g_events[g_used].name != name) return;
-  (void)hipEventRecord(g_events[g_used].stop, st);
-  ++g_used;
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  const OpenBracket o = t_open;
+  t_open.slot = -1;
+  if (!g_timing || o.slot < 0 || o.session != g_session || (size_t)o.slot >= g_used) return;
+  TimedLaunch &t = g_events[o.slot];
+  if (strcmp(t.name, name) != 0) return;
+  t.done = hipEventRecord(t.stop, st) == hipSuccess;
 }
 }  // namespace mla
 
@@ -839,37 +861,41 @@ const char *mla_status_string(mla_status s) {
 const char *mla_version(void) { return "libmla 0.2 (gfx950)"; }
 
 mla_status mla_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lock(g_timing_mu);
   g_timing = on != 0;
   g_used = 0;
+  ++g_session;
   return MLA_OK;
 }
 
 int32_t mla_timing_read(const char **names, double *total_ms, int64_t *launches, int32_t cap) {
-  std::vector<std::string> keys;
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  std::vector<const char *> keys;   // the static strings the launchers pass
   std::vector<double> ms;
   std::vector<int64_t> cnt;
   for (size_t i = 0; i < g_used; ++i) {
-    float t = 0.f;
-    if (hipEventSynchronize(g_events[i].stop) != hipSuccess) return MLA_ERR_HIP;
-    if (hipEventElapsedTime(&t, g_events[i].start, g_events[i].stop) != hipSuccess) return MLA_ERR_HIP;
+    const TimedLaunch &t = g_events[i];
+    if (!t.done) continue;
+    float el = 0.f;
+    if (hipEventSynchronize(t.stop) != hipSuccess) return MLA_ERR_HIP;
+    if (hipEventElapsedTime(&el, t.start, t.stop) != hipSuccess) return MLA_ERR_HIP;
     size_t k = 0;
-    while (k < keys.size() && keys[k] != g_events[i].name) ++k;
+    while (k < keys.size() && strcmp(keys[k], t.name) != 0) ++k;
     if (k == keys.size()) {
-      keys.push_back(g_events[i].name);
+      keys.push_back(t.name);
       ms.push_back(0.0);
       cnt.push_back(0);
     }
-    ms[k] += t;
+    ms[k] += el;
     cnt[k] += 1;
   }
   for (size_t k = 0; k < keys.size() && (int32_t)k < cap; ++k) {
-    // names point at the static strings the launchers pass
-    for (size_t i = 0; i < g_used; ++i)
-      if (keys[k] == g_events[i].name) { if (names) names[k] = g_events[i].name; break; }
+    if (names) names[k] = keys[k];
     if (total_ms) total_ms[k] = ms[k];
     if (launches) launches[k] = cnt[k];
   }
   g_used = 0;
+  ++g_session;
   return (int32_t)keys.size();
 }
 

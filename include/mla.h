@@ -269,7 +269,10 @@ const char *mla_version(void);
 /* Kernel timing, for profiling.  While enabled, every kernel the library
  * launches is bracketed by two HIP events recorded on the stream it is
  * launched on; mla_timing_read synchronises those events and accumulates the
- * elapsed milliseconds per kernel name.  Not thread-safe; off by default.
+ * elapsed milliseconds per kernel name.  Off by default.  The session is
+ * process-wide and guarded by a lock: calls from several host threads each
+ * time their own launches; a read (or a new session) while another thread is
+ * inside a call leaves that call's open launch uncounted.
  *   mla_timing_enable(1) starts (and clears) a session, 0 stops it.
  *   mla_timing_read fills up to `cap` entries (names are static strings) and
  *   returns the number of distinct kernel names, or a negative mla_status. */
