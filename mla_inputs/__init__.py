@@ -36,7 +36,7 @@ import numpy as np
 __all__ = [
     "Dims", "TINY", "DSV3", "Workload", "WORKLOADS", "make_workload",
     "bf16_round", "bf16_bits_to_f32", "WEIGHT_NAMES", "weight_shapes",
-    "draw_weights", "scatter_paged", "block_table_rows",
+    "draw_weights", "scatter_paged", "block_table_rows", "FP8_WEIGHT_NAMES", "fp8_weight_blocks",
 ]
 
 
@@ -171,6 +171,9 @@ class Workload:
     block_perm: Optional[np.ndarray] = None        # physical block id of logical block k
     cache_fp8: bool = False                        # cached rows in the FP8 layout
     cache_fp8_rows: Optional[List[np.ndarray]] = None   # per sequence [lens[b]-n_q][row bytes] uint8
+    # block-scaled FP8 projections: (E4M3 codes [out][in] uint8, float32
+    # scales [ceil(out/128)][in/128]) by weight name (FP8_WEIGHT_NAMES)
+    weights_fp8: Optional[Dict[str, tuple]] = None
 
     @property
     def bf16(self) -> bool:
@@ -220,18 +223,48 @@ def fp8_cache_rows(rng: np.random.Generator, n: int, d_c: int, d_rope: int, chun
     return out
 
 
+FP8_WEIGHT_NAMES = ("w_dq", "w_dkv", "w_kr", "w_o")   # the projections that may be block-scaled FP8
+
+
+def fp8_weight_blocks(rng: np.random.Generator, shape, std: float, chunk_rows: int = 1024):
+    """A weight [out][in] as E4M3 codes with one float32 scale per block of
+    128 rows by 128 columns.  Input data only: per block a scale
+    2^(e0 + d), d drawn uniformly from {-1, 0, 1} and 2^e0 the power of two
+    nearest to std/32 (scales of FP8 weights are powers of two), and the
+    codes are those of N(0, std^2) draws divided by their block's scale
+    (clamped to +-448), cast by PyTorch's float8_e4m3fn conversion.  The
+    dequantised weight is then close to N(0, std^2)."""
+    import torch
+    N, K = shape
+    nb, kb = (N + 127) // 128, K // 128
+    e0 = int(np.round(np.log2(std / 32.0)))
+    scales = np.ldexp(np.float32(1.0), e0 + rng.integers(-1, 2, (nb, kb))).astype(np.float32)
+    codes = np.empty((N, K), dtype=np.uint8)
+    for r0 in range(0, N, chunk_rows):
+        r1 = min(N, r0 + chunk_rows)
+        x = rng.standard_normal((r1 - r0, K), dtype=np.float32) * np.float32(std)
+        sc = np.repeat(scales, 128, axis=0)[r0:r1]            # each row's block scales [rows][kb]
+        q = np.clip(x.reshape(r1 - r0, kb, 128) / sc[:, :, None], -448.0, 448.0).reshape(r1 - r0, K)
+        codes[r0:r1] = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float32)).to(
+            torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scales
+
+
 def make_workload(wid: int, *, dims: Optional[Dims] = None, batch: Optional[int] = None,
                   seq_len: Optional[int] = None, uniform_len: Optional[int] = None,
                   ragged_max: Optional[int] = None, n_q: Optional[int] = None,
                   paged: Optional[bool] = None, block_size: Optional[int] = None,
                   dtype: Optional[str] = None, seed: Optional[int] = None,
                   n_steps: Optional[int] = None, lengths=None, cache_rows: bool = True,
-                  cache_fp8: bool = False) -> Workload:
+                  cache_fp8: bool = False, weights_fp8: bool = False) -> Workload:
     """Build workload ``wid`` (1..5).  Keyword overrides shrink or reshape it
     for tests; the seed stays 1000 + wid unless given.  ``lengths`` (decode
     workloads) fixes every sequence's cache length after the append (and the
     batch).  ``cache_fp8`` (decode workloads) gives the cached rows in the
-    FP8 cache layout (``cache_fp8_rows``, fp8_cache_rows) instead of bf16."""
+    FP8 cache layout (``cache_fp8_rows``, fp8_cache_rows) instead of bf16.
+    ``weights_fp8`` adds the FP8 projections (``weights_fp8``,
+    fp8_weight_blocks) from a stream of their own,
+    ``PCG64(1000 + workload_id + 4481)``, so every other draw is unchanged."""
     spec = dict(WORKLOADS[wid])
     d = dims or spec["dims"]
     dt = dtype or spec["dtype"]
@@ -243,6 +276,10 @@ def make_workload(wid: int, *, dims: Optional[Dims] = None, batch: Optional[int]
         B = len(lengths)
     wl = Workload(wid=wid, name=spec["name"], dims=d, dtype=dt, kind=kind, batch=B)
     wl.weights_f32, wl.weights_bits = draw_weights(rng, d, bf16)
+    if weights_fp8:
+        frng = np.random.Generator(np.random.PCG64((1000 + wid if seed is None else seed) + 4481))
+        shp = weight_shapes(d)
+        wl.weights_fp8 = {n: fp8_weight_blocks(frng, shp[n], 1.0 / np.sqrt(shp[n][1])) for n in FP8_WEIGHT_NAMES}
 
     if kind == "prefill":
         L = seq_len if seq_len is not None else spec["seq_len"]

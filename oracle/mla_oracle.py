@@ -54,6 +54,7 @@ __all__ = [
     "E4M3_MAX", "FP8_GROUP", "e4m3_decode", "e4m3_encode", "round_bf16", "fp8_group_scale", "quantize_latent",
     "fp8_row_bytes",
     "dequantize_fp8_rows",
+    "FP8_WEIGHTS", "quantize_groups", "dequantize_groups", "fp8_activation", "dequantize_weight_blocks",
 ]
 
 
@@ -200,19 +201,23 @@ def _heads(dims, heads):
     return range(dims.n_heads) if heads is None else heads
 
 
-def prefill(dims, W, h, rows=None, heads=None, return_probs=False):
+def prefill(dims, W, h, rows=None, heads=None, return_probs=False, weights_fp8=False):
     """Causal MLA over one whole sequence h [L][d_model] (positions 0..L-1).
 
     rows: query positions to evaluate (default all); heads: heads to evaluate
     (default all; u is only formed when all heads are).  Returns a dict with
     u [R][d_model] (or None), o [R][n_h][d_v] (zeros for skipped heads),
-    and the cache rows c_kv [L][d_c], k_r [L][d_R]."""
+    and the cache rows c_kv [L][d_c], k_r [L][d_R].  weights_fp8: the
+    projections of FP8_WEIGHTS are FP8 products (W holds their dequantised
+    weights, dequantize_weight_blocks); their inputs, h and the attention
+    output o, enter as fp8_activation of themselves."""
     h = _f64(h)
     L = h.shape[0]
     pos = np.arange(L)
-    c_kv, k_r = compress_kv(W, h, pos, dims)
+    hp = fp8_activation(h) if weights_fp8 else h
+    c_kv, k_r = compress_kv(W, hp, pos, dims)
     qpos = pos if rows is None else np.asarray(rows)
-    q_c, q_r = project_queries(W, h[qpos], qpos, dims)
+    q_c, q_r = project_queries(W, hp[qpos], qpos, dims)
     scale = softmax_scale(dims)
     o = np.zeros((len(qpos), dims.n_heads, dims.d_v))
     probs = {}
@@ -223,14 +228,16 @@ def prefill(dims, W, h, rows=None, heads=None, return_probs=False):
             o[:, i], probs[i] = res
         else:
             o[:, i] = res
-    u = output_projection(W, o) if heads is None else None
+    u = None
+    if heads is None:
+        u = output_projection(W, fp8_activation(round_bf16(o.reshape(o.shape[0], -1))) if weights_fp8 else o)
     out = dict(u=u, o=o, c_kv=c_kv, k_r=k_r)
     if return_probs:
         out["probs"] = probs
     return out
 
 
-def decode(dims, W, h, cache_rows, heads=None, cache_fp8=False):
+def decode(dims, W, h, cache_rows, heads=None, cache_fp8=False, weights_fp8=False):
     """n_q new tokens h [n_q][d_model] appended to one sequence whose first
     cached rows ``cache_rows`` [L-n_q][d_c+d_R] (each [c_KV || k_R]) are given.
     The new tokens take positions L-n_q..L-1 and query i sees keys
@@ -242,12 +249,16 @@ def decode(dims, W, h, cache_rows, heads=None, cache_fp8=False):
     dequantised rows, dequantize_fp8_rows).  The quantiser reads c_KV
     rounded to bfloat16, the type the compression produces in a bf16 layer
     (the FP8 cache exists for bf16 layers only), so that a code is decided
-    from the value the layer holds, not from its float64 form."""
+    from the value the layer holds, not from its float64 form.
+    weights_fp8: as in prefill, the FP8_WEIGHTS projections read
+    fp8_activation(h) and fp8_activation(o rounded to bfloat16)."""
     h = _f64(h)
     cache_rows = _f64(cache_rows)
     n_q = h.shape[0]
     L = cache_rows.shape[0] + n_q
     qpos = np.arange(L - n_q, L)
+    if weights_fp8:
+        h = fp8_activation(h)
     c_new, kr_new = compress_kv(W, h, qpos, dims)
     c_att = c_new
     if cache_fp8:
@@ -261,7 +272,9 @@ def decode(dims, W, h, cache_rows, heads=None, cache_fp8=False):
     for i in _heads(dims, heads):
         k_c_i, v_i = head_keys_values(W, c_kv, i, dims)
         o[:, i] = attend_head(q_c[:, i], q_r[:, i], qpos, k_c_i, k_r, v_i, scale)
-    u = output_projection(W, o) if heads is None else None
+    u = None
+    if heads is None:
+        u = output_projection(W, fp8_activation(round_bf16(o.reshape(o.shape[0], -1))) if weights_fp8 else o)
     return dict(u=u, o=o, row_new=np.concatenate([c_new, kr_new], axis=1))
 
 
@@ -382,23 +395,35 @@ def fp8_group_scale(amax):
     return np.where(a > 0, s, 1.0)
 
 
-def quantize_latent(c_kv):
-    """c_KV rows [T][d_c] -> (codes [T][d_c] uint8, scales [T][d_c/FP8_GROUP]):
-    per group, scale = fp8_group_scale(max|x|) and each value takes the
-    E4M3 code nearest to x / scale."""
-    c = _f64(c_kv)
-    T, d_c = c.shape
-    g = c.reshape(T, d_c // FP8_GROUP, FP8_GROUP)
+def quantize_groups(x):
+    """Rows [T][K] (K a multiple of FP8_GROUP) -> (codes [T][K] uint8,
+    scales [T][K/FP8_GROUP]): per group of FP8_GROUP consecutive columns of
+    a row, scale = fp8_group_scale(max|x|) and each value takes the E4M3
+    code nearest to x / scale."""
+    c = _f64(x)
+    T, K = c.shape
+    g = c.reshape(T, K // FP8_GROUP, FP8_GROUP)
     amax = np.max(np.abs(g), axis=2)
     scales = fp8_group_scale(amax)
-    codes = e4m3_encode(g / scales[:, :, None]).reshape(T, d_c)
+    codes = e4m3_encode(g / scales[:, :, None]).reshape(T, K)
     return codes, scales
 
 
+def dequantize_groups(codes, scales):
+    """Inverse of quantize_groups: each code's value times its group's scale."""
+    T, K = codes.shape
+    v = e4m3_decode(codes).reshape(T, K // FP8_GROUP, FP8_GROUP) * _f64(scales)[:, :, None]
+    return v.reshape(T, K)
+
+
+def quantize_latent(c_kv):
+    """c_KV rows [T][d_c] -> (codes, scales): quantize_groups over the latent
+    columns (a scale per FP8_GROUP columns of each row)."""
+    return quantize_groups(c_kv)
+
+
 def _dequantize_latent(codes, scales):
-    T, d_c = codes.shape
-    v = e4m3_decode(codes).reshape(T, d_c // FP8_GROUP, FP8_GROUP) * _f64(scales)[:, :, None]
-    return v.reshape(T, d_c)
+    return dequantize_groups(codes, scales)
 
 
 def fp8_row_bytes(dims):
@@ -418,3 +443,46 @@ def dequantize_fp8_rows(rows, dims):
     k_r = (kr_bits << np.uint32(16)).view(np.float32).astype(np.float64)
     scales = r[:, d_c + 2 * d_r:].copy().view(np.float32).astype(np.float64)
     return np.concatenate([_dequantize_latent(codes, scales), k_r.reshape(T, d_r)], axis=1)
+
+
+# ---------------------------------------------------------------------------
+# FP8 projections: block-scaled GEMMs (the FP8 framework of the V3
+# technical-report summary, "FP8 training framework" paragraph and figures 6
+# and 7; the CSDN blog, "FP8 mixed-precision training framework": the GEMMs
+# take FP8 inputs and produce higher-precision outputs, activations and
+# weights are scaled in blocks, and figure 7 gives 128 elements as the
+# interval of high-precision accumulation).  Readings: an activation is
+# scaled per token and per group of FP8_GROUP consecutive input columns (one
+# scale per accumulation interval of each row); a weight per block of
+# FP8_GROUP output rows by FP8_GROUP input columns; scales are powers of two
+# chosen as for the latent cache (fp8_group_scale); the products are exact
+# and accumulate in at least fp32, so the result is the plain product of the
+# dequantised operands.  The FP8 projections are those between the model's
+# hidden width and the latent or head space that read the hidden state or
+# write the layer output: W_DQ, W_DKV, W_KR and W_O (FP8_WEIGHTS); the
+# up-projections W_UQ, W_QR, W_UK and W_UV, which act inside the latent and
+# head space, keep the layer dtype.  An activation is quantised from the
+# value the layer holds in bfloat16 (h as given; o rounded to bfloat16), as
+# for the latent cache.
+# ---------------------------------------------------------------------------
+
+FP8_WEIGHTS = ("w_dq", "w_dkv", "w_kr", "w_o")
+
+
+def fp8_activation(x):
+    """The values an FP8 product reads for activations x [T][K]: the
+    dequantised quantize_groups(x)."""
+    codes, scales = quantize_groups(x)
+    return dequantize_groups(codes, scales)
+
+
+def dequantize_weight_blocks(codes, scales):
+    """Weight codes [N][K] (uint8 E4M3) with one scale per block of FP8_GROUP
+    rows by FP8_GROUP columns (scales [ceil(N/FP8_GROUP)][K/FP8_GROUP];
+    the last row block may be short) -> [N][K] float64 values."""
+    c = np.asarray(codes)
+    N, K = c.shape
+    sc = _f64(scales)
+    rb = np.arange(N) // FP8_GROUP
+    cb = np.arange(K) // FP8_GROUP
+    return e4m3_decode(c) * sc[rb[:, None], cb[None, :]]

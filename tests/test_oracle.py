@@ -489,12 +489,136 @@ def dataclasses_replace(d, **kw):
     return dataclasses.replace(d, **kw)
 
 
+# ---------------------------------------------------------------------------
+# Block-scaled FP8 projections
+# ---------------------------------------------------------------------------
+
+def _torch_e4m3_values(codes):
+    """Values of E4M3 codes by PyTorch's float8_e4m3fn."""
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def pin_weight_blocks_layout():
+    """A [130][256] weight of codes 0x38 (1.0) under scales [[1, 2], [4, 8]]:
+    element (r, c) takes the scale of block (r // 128, c // 128), the last
+    row block holding two rows; and random codes and scales against
+    PyTorch's E4M3 values times a scale expanded block by block here."""
+    codes = np.full((130, 256), 0x38, dtype=np.uint8)
+    sc = np.array([[1.0, 2.0], [4.0, 8.0]])
+    w = O.dequantize_weight_blocks(codes, sc)
+    assert w[0, 0] == 1 and w[127, 127] == 1 and w[0, 128] == 2 and w[0, 255] == 2
+    assert w[128, 0] == 4 and w[129, 127] == 4 and w[128, 128] == 8 and w[129, 255] == 8
+    rng = np.random.Generator(np.random.PCG64(51))
+    codes = rng.integers(0, 256, (200, 384)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38        # no NaN codes
+    sc = np.ldexp(1.0, rng.integers(-12, 3, (2, 3)))
+    ref = _torch_e4m3_values(codes)
+    for rb in range(2):
+        for cb in range(3):
+            ref[rb * 128:(rb + 1) * 128, cb * 128:(cb + 1) * 128] *= sc[rb, cb]
+    assert np.array_equal(O.dequantize_weight_blocks(codes, sc), ref)
+
+
+def pin_activation_groups_per_row():
+    """Activation groups run along a token's row: row 0 is 1e-3 in columns
+    0..127 and 100 in 128..255, row 1 the other way round.  Worked by hand:
+    100 = 0.78125 * 2^7 needs 2^-2 (448 / 4 = 112 >= 100, 448 / 8 = 56 <
+    100); 1e-3 = 0.512 * 2^-9 needs 2^-18 (448 * 2^-18 = 1.709e-3, half that
+    falls short).  Each value is then a multiple of a code: 100 / 2^-2 = 400
+    lies halfway between the codes 384 (mantissa 100) and 416 (101) and goes
+    to the even 384, so 100 -> 96; 1e-3 / 2^-18 = 262.144 -> 256, so
+    1e-3 -> 2^-10."""
+    x = np.zeros((2, 256))
+    x[0, :128], x[0, 128:] = 1e-3, 100.0
+    x[1, :128], x[1, 128:] = 100.0, 1e-3
+    codes, scales = O.quantize_groups(x)
+    assert scales.tolist() == [[2.0 ** -18, 0.25], [0.25, 2.0 ** -18]]
+    deq = O.fp8_activation(x)
+    assert np.all(deq[0, :128] == 2.0 ** -10) and np.all(deq[0, 128:] == 96.0)
+    assert np.all(deq[1, :128] == 96.0) and np.all(deq[1, 128:] == 2.0 ** -10)
+
+
+def _brute_quant(row):
+    """Quantise-dequantise one row in groups of 128 without the oracle: the
+    scale 2^ceil(log2(max|x| / 448)) (the smallest power of two s with
+    448 s >= max|x|), codes by PyTorch's E4M3 cast of x / s."""
+    out = []
+    for g in range(0, len(row), 128):
+        grp = row[g:g + 128]
+        amax = max(abs(v) for v in grp)
+        s = 2.0 ** math.ceil(math.log2(amax / 448.0)) if amax > 0 else 1.0
+        q = torch.tensor([v / s for v in grp], dtype=torch.float64).to(torch.float32).to(torch.float8_e4m3fn)
+        out += [float(v) * s for v in q.double().tolist()]
+    return out
+
+
+def pin_fp8_projections_brute_force(dims=TINY, L=3):
+    """FP8 projections on a micro case by scalar loops: W_DQ, W_DKV, W_KR
+    and W_O from E4M3 codes and block scales (PyTorch's E4M3 values), the
+    hidden state quantised per token and 128 columns before the down
+    projections, the attention output rounded to bfloat16 (PyTorch) and
+    quantised the same way before W_O; the other projections in float64.
+    Then the decode of the last token against a cache of the first L-1 rows
+    gives the prefill's last row."""
+    W = _weights(dims, 52)
+    wl = make_workload(1, dims=dims, weights_fp8=True)
+    for n, (codes, sc) in wl.weights_fp8.items():
+        vals = _torch_e4m3_values(codes)
+        for r in range(vals.shape[0]):
+            for cb in range(vals.shape[1] // 128):
+                vals[r, cb * 128:(cb + 1) * 128] *= sc[r // 128, cb]
+        W[n] = vals
+    h = _h(L, dims, 53) * 3.0
+    got = O.prefill(dims, W, h, weights_fp8=True)
+
+    def mv(M, x):
+        return [sum(M[r][c] * x[c] for c in range(len(x))) for r in range(len(M))]
+
+    def rot(x, p):
+        out = list(x)
+        for k in range(len(x) // 2):
+            a = p * dims.rope_base ** (-2.0 * k / len(x))
+            out[2 * k] = x[2 * k] * math.cos(a) - x[2 * k + 1] * math.sin(a)
+            out[2 * k + 1] = x[2 * k] * math.sin(a) + x[2 * k + 1] * math.cos(a)
+        return out
+
+    Wl = {k: v.tolist() for k, v in W.items()}
+    hq = [_brute_quant(h[t].tolist()) for t in range(L)]
+    ckv = [mv(Wl["w_dkv"], hq[t]) for t in range(L)]
+    kr = [rot(mv(Wl["w_kr"], hq[t]), t) for t in range(L)]
+    for t in range(L):
+        cq = mv(Wl["w_dq"], hq[t])
+        qc_all, qr_all = mv(Wl["w_uq"], cq), mv(Wl["w_qr"], cq)
+        ocat = []
+        for i in range(dims.n_heads):
+            qc = qc_all[i * dims.d_nope:(i + 1) * dims.d_nope]
+            qr = rot(qr_all[i * dims.d_rope:(i + 1) * dims.d_rope], t)
+            scores, vals = [], []
+            for j in range(t + 1):
+                kc = mv(Wl["w_uk"][i * dims.d_nope:(i + 1) * dims.d_nope], ckv[j])
+                v = mv(Wl["w_uv"][i * dims.d_v:(i + 1) * dims.d_v], ckv[j])
+                scores.append(sum(a * b for a, b in zip(qc + qr, kc + kr[j])) / math.sqrt(dims.d_nope + dims.d_rope))
+                vals.append(v)
+            mx = max(scores)
+            ex = [math.exp(s - mx) for s in scores]
+            z = sum(ex)
+            ocat += [sum(ex[j] / z * vals[j][c] for j in range(t + 1)) for c in range(dims.d_v)]
+        o16 = torch.tensor(ocat, dtype=torch.float64).to(torch.bfloat16).double().tolist()
+        u = mv(Wl["w_o"], _brute_quant(o16))
+        assert np.allclose(got["u"][t], u, rtol=1e-10, atol=1e-12)
+        assert np.allclose(got["c_kv"][t], ckv[t], rtol=1e-11, atol=1e-12)
+    rows = np.concatenate([got["c_kv"][:L - 1], got["k_r"][:L - 1]], axis=1)
+    dec = O.decode(dims, W, h[L - 1:], rows, weights_fp8=True)
+    assert np.allclose(dec["u"][0], got["u"][L - 1], rtol=1e-10, atol=1e-12)
+
+
 ALL_PINS = [pin_absorbed_equals_plain, pin_softmax_rows, pin_causal, pin_single_key,
             pin_zero_query, pin_head_isolation, pin_mha_special_case, pin_rope_rotation, pin_rope_in_scores,
             pin_yarn_frequencies, pin_yarn_in_scores, pin_yarn_blend_hand_worked, pin_prefill_decode_agree,
             pin_e4m3_definition, pin_e4m3_rounding, pin_e4m3_library, pin_quantize_latent_hand_worked,
             pin_quantize_latent_bound,
-            pin_fp8_row_layout, pin_round_bf16, pin_decode_fp8_new_rows, pin_brute_force]
+            pin_fp8_row_layout, pin_round_bf16, pin_decode_fp8_new_rows, pin_brute_force,
+            pin_weight_blocks_layout, pin_activation_groups_per_row, pin_fp8_projections_brute_force]
 
 
 # ---------------------------------------------------------------------------

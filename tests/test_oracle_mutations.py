@@ -206,6 +206,26 @@ def _bf16_skipped(x):
     return np.asarray(x, dtype=np.float64)
 
 
+_qgroups = O.quantize_groups
+_deqw = O.dequantize_weight_blocks
+
+
+def _quant_scale_per_token(x):
+    # one scale per token row (its largest magnitude) instead of one per group
+    x = np.asarray(x, dtype=np.float64)
+    codes, scales = _qgroups(x)
+    amax = np.max(np.abs(x), axis=1, keepdims=True)
+    sc = np.repeat(O.fp8_group_scale(amax), scales.shape[1], axis=1)
+    g = x.reshape(x.shape[0], -1, 128)
+    return _enc8(g / sc[:, :, None]).reshape(x.shape), sc
+
+
+def _weight_scale_row_blocks_only(codes, scales):
+    # the first column block's scale for the whole row block
+    sc = np.asarray(scales, dtype=np.float64)
+    return _deqw(codes, np.repeat(sc[:, :1], sc.shape[1], axis=1))
+
+
 MUTATIONS = {
     "rope_sign": ("rope", _rope_sign),
     "rope_frequency": ("rope", _rope_freq),
@@ -236,6 +256,9 @@ MUTATIONS = {
     "fp8_scale_rounded_down": ("quantize_latent", _quant_scale_floor),
     "bf16_truncate": ("round_bf16", _bf16_truncate),
     "fp8_input_not_bf16": ("round_bf16", _bf16_skipped),
+    "fp8_act_scale_per_token": ("quantize_groups", _quant_scale_per_token),
+    "fp8_weight_scale_per_row_block": ("dequantize_weight_blocks", _weight_scale_row_blocks_only),
+    "fp8_activation_unquantised": ("fp8_activation", lambda x: np.asarray(x, dtype=np.float64)),
 }
 
 
