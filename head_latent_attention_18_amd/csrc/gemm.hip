@@ -448,6 +448,14 @@ int gemm_bm(int dtype, int tile) {
 #define BIG_WN 4
 #endif
 hipError_t launch_gemm(int dtype, int tile, int swap, int wkn, GemmArgs &a, hipStream_t st) {
+  if (a.fp8) {
+    // block-scaled FP8: up to 128 tokens stream the weights, more take the
+    // 256x256 tiles
+    if (dtype != 1 || wkn || !swap) return hipErrorNotSupported;
+    if (a.M <= 128 && gemm_stream_ok(a, 0)) return launch_gemm_stream(a, 0, st);
+    if (a.M > 128 && gemm_big_ok(a)) return launch_gemm_big(a, 1, st);
+    return hipErrorNotSupported;
+  }
   if (dtype == 1) {
     if (tile == TILE_BIG) {
       if (!wkn && gemm_big_ok(a)) return launch_gemm_big(a, swap, st);

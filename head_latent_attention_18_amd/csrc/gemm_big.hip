@@ -18,7 +18,13 @@
 //     epilogue is compiled once instead of once per accumulator; the plain
 //     outputs leave by streaming (non-temporal) stores of whole rows, since
 //     the next kernel reads them from other XCDs (measured 5-10 us faster
-//     per prefill than write-allocating stores).
+//     per prefill than write-allocating stores);
+//   * block-scaled FP8 (F8): E4M3 operands, a slab row is the same 128 bytes
+//     (128 k instead of 64), each 64-wide k step a scaled 32x32x64 MFMA
+//     taking the weight block's power-of-two scale (uniform over a wave's
+//     64 features) and each token's as 8-bit exponents; a slab is one 128-k
+//     scale block, and its token exponents are loaded with the next slab's
+//     copies.
 #include <type_traits>
 
 #include "mla_internal.h"
@@ -32,8 +38,10 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) bf16 lds_bf16;
 typedef __attribute__((address_space(3))) float lds_float;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int GBM = 256, GBN = 256, GBK = 64;
+constexpr int GBM = 256, GBN = 256, GBK = 64;   // GBK: bf16 k per slab (FP8: 2 * GBK)
 constexpr int GNT = 512;                        // threads (8 waves)
 constexpr int GNS = 2;                          // ring stages
 constexpr int RCH = GBK / 8;                    // 16-byte chunks per row of a slab (8)
@@ -84,10 +92,12 @@ __device__ inline int swz(int row) { return (row >> 1) & 7; }
 
 }  // namespace
 
-template <bool SWAP>
+template <bool SWAP, bool F8>
 __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
+  constexpr int ESZ = F8 ? 1 : 2;               // bytes per operand element
+  constexpr int SK = GBK * 2 / ESZ;             // k per slab (128 bytes of each row)
   __shared__ __attribute__((aligned(16))) bf16 ring[RING_ELEMS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;      // 128-token x 64-feature block of the wave
 
   // tile of this workgroup: GxG groups of tiles, one group per XCD at a time
@@ -103,9 +113,9 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
 
   int seg = 0, beg = 0;
   while (seg < a.nw - 1 && n0 >= a.w_end[seg]) { beg = a.w_end[seg]; ++seg; }
-  const bf16 *wsrc = (const bf16 *)a.w[seg] + (long)(n0 - beg) * a.ldw;
+  const char *wsrc = (const char *)a.w[seg] + (long)(n0 - beg) * a.ldw * ESZ;
   const int wrows = min(GBN, a.w_end[seg] - n0);
-  const bf16 *xsrc = (const bf16 *)a.x + (long)m0 * a.ldx;
+  const char *xsrc = (const char *)a.x + (long)m0 * a.ldx * ESZ;
   const int xrows = min(GBM, a.M - m0);
   const unsigned lring = (unsigned)(size_t)(lds_void *)ring;
 
@@ -116,12 +126,12 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < GLOADS; ++i) {
     const int s = (i < XL ? i : i - XL) * GNT + tid, r = s / RCH, c = (s % RCH) ^ swz(r);
-    coff[i] = i < XL ? (unsigned)(min(r, xrows - 1) * a.ldx + c * 8) * 2u
-                     : (unsigned)(min(r, wrows - 1) * a.ldw + c * 8) * 2u;
+    coff[i] = i < XL ? (unsigned)(min(r, xrows - 1) * a.ldx * ESZ + c * 16)
+                     : (unsigned)(min(r, wrows - 1) * a.ldw * ESZ + c * 16);
   }
   auto issue = [&](int kt, int st) {
     const unsigned dst = lring + (unsigned)(st * GSTAGE * 2) + wave * 1024;
-    const char *xb = (const char *)(xsrc + kt * GBK), *wb = (const char *)(wsrc + kt * GBK);
+    const char *xb = xsrc + kt * SK * ESZ, *wb = wsrc + kt * SK * ESZ;
 #pragma unroll
     for (int i = 0; i < GLOADS; ++i) dma16(i < XL ? xb : wb, coff[i], dst + i * GNT * 16);
   };
@@ -162,7 +172,64 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][i], xf[buf][j], acc[i][j], 0, 0, 0);
   };
 
-  const int nkt = a.K / GBK;
+  const int nkt = a.K / SK;
+  if constexpr (F8) {
+    // fragments of the two 64-wide k steps of a slab: lane group fh holds
+    // logical chunks 4s + 2fh and 4s + 2fh + 1 of its row (both operands
+    // alike, so the instruction's k order does not matter)
+    i32x8 wq[2][2], xq[2][4];
+    auto rd8 = [&](int st, int s) {
+      const lds_bf16 *xs = rl + st * GSTAGE;
+      const lds_bf16 *ws = xs + XCHK * 8;
+      const int c = 4 * s + 2 * fh;
+      auto frag = [&](const lds_bf16 *base, int r) {
+        const lds_u32x4 *row = (const lds_u32x4 *)(base + r * RCH * 8);
+        const u32x4 p0 = row[c ^ swz(r)], p1 = row[(c + 1) ^ swz(r)];
+        return i32x8{(int)p0[0], (int)p0[1], (int)p0[2], (int)p0[3], (int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]};
+      };
+#pragma unroll
+      for (int b = 0; b < 2; ++b) wq[s][b] = frag(ws, wn * 64 + b * 32 + fr);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) xq[s][b] = frag(xs, wm * 128 + b * 32 + fr);
+    };
+    // the weight block's exponent (uniform over the wave's 64 features) and
+    // each of the lane's four tokens' exponent, per 128-k slab
+    // (a wave past the segment's last row reads the last block's scales;
+    // its rows are never stored)
+    const int wblk = min((n0 - beg + wn * 64) >> 7, (a.w_end[seg] - beg - 1) >> 7);
+    const float *wsp = a.wsc[seg] + (long)wblk * a.wsc_ld;
+    const unsigned char *xsp = a.xs + m0 + wm * 128 + fr;
+    int sx[4], sxn[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sxn[j] = xsp[j * 32];
+    issue(0, 0);
+    for (int kt = 0; kt < nkt; ++kt) {
+      wait_vm<0>();     // this wave's copies of slab kt (and its token exponents)
+      wait_lgkm0();     // its reads of slab kt-1 are in registers
+      bar();            // slab kt landed for every wave; stage (kt+1) % 2 is free
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sx[j] = sxn[j];
+      if (kt + 1 < nkt) {
+        issue(kt + 1, (kt + 1) % GNS);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sxn[j] = xsp[(long)(kt + 1) * a.xs_ld + j * 32];
+      }
+      const int sw = (int)((__builtin_bit_cast(unsigned, wsp[kt]) >> 23) & 0xFFu);
+      const int st = kt % GNS;
+      rd8(st, 0);
+      rd8(st, 1);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wq[s][i], xq[s][j], acc[i][j], 0, 0, 0, sw,
+                                                                        0, sx[j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else {
   issue(0, 0);
   // slab kt: wait for it, free the other stage for slab kt+1, multiply with
   // the fragments read two steps ahead (ring of three fragment buffers)
@@ -180,6 +247,7 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
       mm(s % 3);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
   }
 
   // Epilogue through LDS, half a tile (128 tokens) at a time: the waves of
@@ -313,11 +381,15 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
 }
 
 bool gemm_big_ok(const GemmArgs &a) {
-  if (a.batch != 1 || a.M < GBM || a.K % GBK != 0) return false;
+  // bf16 from 256 tokens on; FP8 products of more than 128 tokens all come
+  // here (fewer stream), the tile's surplus rows clamped and not stored
+  if (a.fp8 ? (a.batch != 1 || a.K % (2 * GBK) != 0 || !a.xs) : (a.batch != 1 || a.M < GBM || a.K % GBK != 0))
+    return false;
   for (int s = 0; s < a.nw - 1; ++s)
     if (a.w_end[s] % GBN != 0) return false;   // a tile never straddles two weight segments
   // 32-bit lane offsets
-  if ((long)GBM * a.ldx * 2 >= (1L << 31) || (long)GBN * a.ldw * 2 >= (1L << 31)) return false;
+  const int esz = a.fp8 ? 1 : 2;
+  if ((long)GBM * a.ldx * esz >= (1L << 31) || (long)GBN * a.ldw * esz >= (1L << 31)) return false;
   return true;
 }
 
@@ -333,8 +405,14 @@ hipError_t launch_gemm_big(GemmArgs &a, int swap, hipStream_t st) {
   const int grid = ((groups + 7) / 8) * 8 * G * G;
   const char *name = a.name ? a.name : "gemm_big";
   timing_before(name, st);
-  if (swap) hipLaunchKernelGGL((gemm_big_kernel<true>), dim3(grid), dim3(GNT), 0, st, a);
-  else hipLaunchKernelGGL((gemm_big_kernel<false>), dim3(grid), dim3(GNT), 0, st, a);
+  if (a.fp8) {
+    if (!swap) return hipErrorNotSupported;
+    hipLaunchKernelGGL((gemm_big_kernel<true, true>), dim3(grid), dim3(GNT), 0, st, a);
+  } else if (swap) {
+    hipLaunchKernelGGL((gemm_big_kernel<true, false>), dim3(grid), dim3(GNT), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((gemm_big_kernel<false, false>), dim3(grid), dim3(GNT), 0, st, a);
+  }
   timing_after(name, st);
   return hipGetLastError();
 }

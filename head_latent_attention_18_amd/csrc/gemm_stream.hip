@@ -15,7 +15,12 @@
 //     row (no padding, no bank conflicts for the 16-row MFMA reads);
 //   * a tile finished inside one workgroup goes straight through the
 //     epilogue; a tile shared by several leaves fp32 partials that the reduce
-//     kernel adds up in workgroup order (deterministic).
+//     kernel adds up in workgroup order (deterministic);
+//   * block-scaled FP8 (F8): weights and activations are E4M3 codes, a unit
+//     holds twice the k in the same bytes, and each 128-wide k step is one
+//     scaled 16x16x128 MFMA taking the weight block's and the token's
+//     power-of-two scales as 8-bit exponents (the activation exponents of
+//     every k block sit in LDS from the start).
 #include "mla_internal.h"
 
 namespace mla {
@@ -27,10 +32,14 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) bf16 lds_bf16;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int SBN = 64;          // weight rows (output features) per tile
 constexpr int SNT = 256;         // threads per workgroup
 constexpr int MAX_PARTS = 16;    // workgroups that may share one tile
+constexpr int F8_MAX_KB = 128;   // FP8: k blocks of 128 whose activation exponents LDS holds
 
 // k per unit.  Each weight row contributes one contiguous run of 2*BK bytes
 // per unit: HBM serves 512-byte runs markedly faster than 256-byte ones
@@ -75,18 +84,23 @@ __device__ __host__ inline int unit_owner(int u, int U, int G) { return ((u + 1)
 }  // namespace
 
 // MB: 16-row blocks of activations (M <= 16*MB).  WKN: W stored [K][N].
-template <int MB, bool WKN>
+// F8: block-scaled E4M3 operands (GemmArgs fp8 fields).
+template <int MB, bool WKN, bool F8>
 __global__ __launch_bounds__(SNT, 1) void gemm_stream_kernel(GemmArgs a) {
-  constexpr int SBK = stream_bk<MB>();
-  constexpr int CPR = SBK / 8;                      // 16-byte chunks per row of a unit
+  static_assert(!(F8 && WKN), "");
+  constexpr int ESZ = F8 ? 1 : 2;                   // bytes per element
+  constexpr int SBK = stream_bk<MB>() * 2 / ESZ;    // k per unit (the same bytes either way)
+  constexpr int CPR = SBK * ESZ / 16;               // 16-byte chunks per row of a unit
   constexpr int SNS = stream_stages<MB>();
-  constexpr int WCH = SBN * SBK / 8;                // weight chunks per unit
-  constexpr int XCH = 16 * MB * SBK / 8;            // activation chunks per unit
+  constexpr int WCH = SBN * CPR;                    // weight chunks per unit
+  constexpr int XCH = 16 * MB * CPR;                // activation chunks per unit
   constexpr int WLD = WCH / SNT, XLD = XCH / SNT;   // copy instructions per unit
   constexpr int LOADS = WLD + XLD;
-  constexpr int STAGE = (WCH + XCH) * 8;            // elements per stage
+  constexpr int STAGE = (WCH + XCH) * 8;            // bf16 elements per stage
   static_assert(WCH % SNT == 0 && XCH % SNT == 0 && LOADS * (SNS - 2) < 64, "");
   __shared__ __attribute__((aligned(16))) bf16 ring[SNS * STAGE];
+  // FP8: activation scale exponents [k block][token]
+  __shared__ unsigned char xsc[F8 ? F8_MAX_KB * 16 * MB : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 15, lgrp = lane >> 4;
@@ -109,12 +123,12 @@ __global__ __launch_bounds__(SNT, 1) void gemm_stream_kernel(GemmArgs a) {
     if constexpr (!WKN) {
       int seg = 0, beg = 0;
       while (seg < a.nw - 1 && n0 >= a.w_end[seg]) { beg = a.w_end[seg]; ++seg; }
-      const char *wb = (const char *)((const bf16 *)a.w[seg] + (long)z * a.w_bs + (long)(n0 - beg) * a.ldw + k0);
+      const char *wb = (const char *)a.w[seg] + ((long)z * a.w_bs + (long)(n0 - beg) * a.ldw + k0) * ESZ;
       const int rows = min(SBN, a.w_end[seg] - n0);
 #pragma unroll
       for (int i = 0; i < WLD; ++i) {
         const int s = i * SNT + tid, r = s / CPR, pc = s % CPR;
-        const unsigned off = (unsigned)(min(r, rows - 1) * a.ldw + ((pc ^ (r & 15)) << 3)) * 2u;
+        const unsigned off = (unsigned)(min(r, rows - 1) * a.ldw * ESZ + ((pc ^ (r & 15)) << 4));
         dma16(wb, off, lst + i * SNT * 16);
       }
     } else {
@@ -127,11 +141,11 @@ __global__ __launch_bounds__(SNT, 1) void gemm_stream_kernel(GemmArgs a) {
       }
     }
     // activations
-    const char *xb = (const char *)((const bf16 *)a.x + (long)z * a.x_bs + k0);
+    const char *xb = (const char *)a.x + ((long)z * a.x_bs + k0) * ESZ;
 #pragma unroll
     for (int i = 0; i < XLD; ++i) {
       const int s = i * SNT + tid, r = s / CPR, pc = s % CPR;
-      const unsigned off = (unsigned)(min(r, a.M - 1) * a.ldx + ((pc ^ (r & 15)) << 3)) * 2u;
+      const unsigned off = (unsigned)(min(r, a.M - 1) * a.ldx * ESZ + ((pc ^ (r & 15)) << 4));
       dma16(xb, off, lst + (WLD + i) * SNT * 16);
     }
   };
@@ -168,6 +182,15 @@ __global__ __launch_bounds__(SNT, 1) void gemm_stream_kernel(GemmArgs a) {
   };
 
   for (int i = 0; i < SNS - 1 && i < nu; ++i) issue(u0 + i, i);
+  if constexpr (F8) {
+    // every k block's activation exponents, [k block][token] (visible after
+    // the loop's first barrier)
+    const int nkb = a.K / 128;
+    for (int i = tid; i < nkb * 16 * MB; i += SNT) {
+      const int kb = i / (16 * MB), m = i - kb * 16 * MB;
+      xsc[i] = a.xs[(long)kb * a.xs_ld + min(m, a.M - 1)];
+    }
+  }
   for (int k = 0; k < nu; ++k) {
     if (k + SNS - 2 < nu) wait_vm<LOADS * (SNS - 2)>();
     else wait_vm<0>();
@@ -175,6 +198,38 @@ __global__ __launch_bounds__(SNT, 1) void gemm_stream_kernel(GemmArgs a) {
     if (k + SNS - 1 < nu) issue(u0 + k + SNS - 1, (k + SNS - 1) % SNS);
     const lds_bf16 *ws = rl + (k % SNS) * STAGE;
     const lds_bf16 *xs = ws + WCH * 8;
+    if constexpr (F8) {
+      // 128-wide k steps: lane group g holds logical chunks 8s + 2g and
+      // 8s + 2g + 1 of its row (both operands alike); the weight block's
+      // exponent is uniform over the unit's 64 rows, the token's comes from LDS
+      const int u = u0 + k;
+      const int tt = u / KS;
+      const int j = u - tt * KS;
+      const int z = tt / a.tiles_n, t = tt - z * a.tiles_n;
+      const int n0 = t * SBN;
+      int seg = 0, beg = 0;
+      while (seg < a.nw - 1 && n0 >= a.w_end[seg]) { beg = a.w_end[seg]; ++seg; }
+      const float *wsp = a.wsc[seg] + (long)((n0 - beg) >> 7) * a.wsc_ld + j * (SBK / 128);
+      const lds_u8 *xsl = (const lds_u8 *)xsc;
+#pragma unroll
+      for (int s = 0; s < SBK / 128; ++s) {
+        const int sw = (int)((__builtin_bit_cast(unsigned, wsp[s]) >> 23) & 0xFFu);
+        const int c0 = 8 * s + 2 * lgrp;
+        const int r = wave * 16 + lrow;
+        const lds_u32x4 *wrow = (const lds_u32x4 *)((const lds_u8 *)ws + r * CPR * 16);
+        const u32x4 w0 = wrow[c0 ^ (r & 15)], w1 = wrow[(c0 + 1) ^ (r & 15)];
+        const i32x8 wf = {(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3], (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int rx = mb * 16 + lrow;
+          const lds_u32x4 *xrow = (const lds_u32x4 *)((const lds_u8 *)xs + rx * CPR * 16);
+          const u32x4 x0 = xrow[c0 ^ (rx & 15)], x1 = xrow[(c0 + 1) ^ (rx & 15)];
+          const i32x8 xf = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+          const int sx = xsl[(j * (SBK / 128) + s) * 16 * MB + rx];
+          acc[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf, xf, acc[mb], 0, 0, 0, sw, 0, sx);
+        }
+      }
+    } else {
 #pragma unroll
     for (int s = 0; s < SBK / 32; ++s) {
       const int c = 4 * s + lgrp;                  // logical 16-byte chunk of the k step
@@ -202,6 +257,7 @@ __global__ __launch_bounds__(SNT, 1) void gemm_stream_kernel(GemmArgs a) {
         acc[mb] = Mma<bf16>::mma(wf, xf, acc[mb]);
       }
     }
+    }
     const int u = u0 + k;
     if ((u + 1) % KS == 0 || k == nu - 1) flush(u);
   }
@@ -211,8 +267,7 @@ __global__ __launch_bounds__(SNT, 1) void gemm_stream_kernel(GemmArgs a) {
 // then the epilogue.  One thread per (tile, row, 4 columns); all partial loads
 // are issued before the sum.
 template <int MB>
-__global__ __launch_bounds__(256) void gemm_stream_reduce_kernel(GemmArgs a, int G) {
-  const int KS = a.K / stream_bk<MB>();
+__global__ __launch_bounds__(256) void gemm_stream_reduce_kernel(GemmArgs a, int G, int KS) {
   const int U = a.batch * a.tiles_n * KS;
   // workgroups of one tile: its segment and owners are uniform
   const int per_tile = a.M * (SBN / 4);
@@ -256,9 +311,11 @@ bool gemm_stream_ok(const GemmArgs &a, int wkn) {
   // Up to 32 tokens, long products only: the ring's fill and drain cost a
   // few microseconds, which shorter weight streams (q_up, W_UK, W_UV) do not
   // amortise; those keep the register-streaming kernels.  From 33 tokens on
-  // every product whose k is a whole number of units streams here.
-  if (wkn || (a.M <= 32 && a.K < 4096)) return false;
-  const int bk = stream_bk_for(a.M);
+  // every product whose k is a whole number of units streams here.  FP8
+  // products always stream here (the only FP8 kernel for up to 128 tokens).
+  if (a.fp8 && (wkn || a.K / 128 > F8_MAX_KB || !a.xs)) return false;
+  if (wkn || (!a.fp8 && a.M <= 32 && a.K < 4096)) return false;
+  const int bk = stream_bk_for(a.M) * (a.fp8 ? 2 : 1);
   if (a.M > 128 || a.K % bk != 0 || !a.partial) return false;
   const long units = (long)a.batch * ((a.N + SBN - 1) / SBN) * (a.K / bk);
   if (units * gemm_stream_grid() >= (1L << 31)) return false;
@@ -281,16 +338,16 @@ static int stream_grid_for(int U, int KS, int tiles) {
   return full;
 }
 
-template <int MB, bool WKN>
+template <int MB, bool WKN, bool F8>
 static hipError_t launch_stream_t(GemmArgs &a, hipStream_t st) {
   a.tiles_m = 1;
   a.tiles_n = (a.N + SBN - 1) / SBN;
-  const int KS = a.K / stream_bk<MB>();
+  const int KS = a.K / (stream_bk<MB>() * (F8 ? 2 : 1));
   const int tiles = a.batch * a.tiles_n;
   const int U = tiles * KS;
   const int G = stream_grid_for(U, KS, tiles);
   timing_before(a.name ? a.name : "gemm_stream", st);
-  hipLaunchKernelGGL((gemm_stream_kernel<MB, WKN>), dim3(G), dim3(SNT), 0, st, a);
+  hipLaunchKernelGGL((gemm_stream_kernel<MB, WKN, F8>), dim3(G), dim3(SNT), 0, st, a);
   timing_after(a.name ? a.name : "gemm_stream", st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -300,16 +357,23 @@ static hipError_t launch_stream_t(GemmArgs &a, hipStream_t st) {
   const long wgs = (long)tiles * ((a.M * (SBN / 4) + 255) / 256);
   const char *rn = a.reduce_name ? a.reduce_name : "gemm_stream.reduce";
   timing_before(rn, st);
-  hipLaunchKernelGGL((gemm_stream_reduce_kernel<MB>), dim3((unsigned)wgs), dim3(256), 0, st, a, G);
+  hipLaunchKernelGGL((gemm_stream_reduce_kernel<MB>), dim3((unsigned)wgs), dim3(256), 0, st, a, G, KS);
   timing_after(rn, st);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_stream(GemmArgs &a, int wkn, hipStream_t st) {
-  if (a.M <= 16) return wkn ? launch_stream_t<1, true>(a, st) : launch_stream_t<1, false>(a, st);
-  if (a.M <= 32) return wkn ? launch_stream_t<2, true>(a, st) : launch_stream_t<2, false>(a, st);
-  if (a.M <= 64) return wkn ? launch_stream_t<4, true>(a, st) : launch_stream_t<4, false>(a, st);
-  return wkn ? launch_stream_t<8, true>(a, st) : launch_stream_t<8, false>(a, st);
+  if (a.fp8) {
+    if (wkn) return hipErrorNotSupported;
+    if (a.M <= 16) return launch_stream_t<1, false, true>(a, st);
+    if (a.M <= 32) return launch_stream_t<2, false, true>(a, st);
+    if (a.M <= 64) return launch_stream_t<4, false, true>(a, st);
+    return launch_stream_t<8, false, true>(a, st);
+  }
+  if (a.M <= 16) return wkn ? launch_stream_t<1, true, false>(a, st) : launch_stream_t<1, false, false>(a, st);
+  if (a.M <= 32) return wkn ? launch_stream_t<2, true, false>(a, st) : launch_stream_t<2, false, false>(a, st);
+  if (a.M <= 64) return wkn ? launch_stream_t<4, true, false>(a, st) : launch_stream_t<4, false, false>(a, st);
+  return wkn ? launch_stream_t<8, true, false>(a, st) : launch_stream_t<8, false, false>(a, st);
 }
 
 }  // namespace mla

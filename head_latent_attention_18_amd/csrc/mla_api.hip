@@ -39,6 +39,14 @@ size_t esize(const mla_config *c) { return c->dtype == MLA_BF16 ? 2 : 4; }
 
 bool cache_fp8(const mla_config *c) { return c->cache_dtype == MLA_CACHE_FP8_E4M3; }
 
+// block-scaled FP8 projections (W_DQ, W_DKV, W_KR, W_O)
+bool weights_fp8(const mla_config *c) { return c->weight_dtype == MLA_WEIGHTS_FP8_BLOCK; }
+
+// widest input of an FP8 projection (h, or the attention output o)
+int64_t fp8_act_width(const mla_config *c) { return std::max<int64_t>(c->d_model, (int64_t)c->n_heads * c->d_v); }
+// tokens per row of the activation scale exponents (whole 256-token tiles)
+int64_t fp8_scale_ld(int64_t T) { return (T + 255) / 256 * 256; }
+
 // bytes of one cached row: (d_c + d_R) elements, or the FP8 row (codes,
 // bf16 k_R, a float32 scale per 128 columns)
 size_t row_bytes(const mla_config *c) {
@@ -71,6 +79,11 @@ mla_status check_config(const mla_config *c) {
   if (c->cache_dtype != MLA_CACHE_LAYER && c->cache_dtype != MLA_CACHE_FP8_E4M3) return MLA_ERR_DTYPE;
   if (c->cache_dtype == MLA_CACHE_FP8_E4M3 && (c->dtype != MLA_BF16 || c->d_c % 128 || c->d_rope % 8))
     return MLA_ERR_UNSUPPORTED;
+  if (c->weight_dtype != MLA_WEIGHTS_LAYER && c->weight_dtype != MLA_WEIGHTS_FP8_BLOCK) return MLA_ERR_DTYPE;
+  if (c->weight_dtype == MLA_WEIGHTS_FP8_BLOCK &&
+      (c->dtype != MLA_BF16 || c->d_model % 512 || ((long)c->n_heads * c->d_v) % 512 ||
+       c->d_model > 16384 || (long)c->n_heads * c->d_v > 16384))
+    return MLA_ERR_UNSUPPORTED;
   if (c->d_rope / 2 > MLA_MAX_ROPE_PAIRS) return MLA_ERR_UNSUPPORTED;
   if ((long)c->n_heads * ((long)c->d_nope + c->d_rope) > (1L << 24)) return MLA_ERR_UNSUPPORTED;
   const int big = c->dtype == MLA_BF16 ? 64 : 32, small = c->dtype == MLA_BF16 ? 32 : 16;
@@ -89,10 +102,11 @@ bool attention_supported(const mla_config *c, int op) {
   return c->d_c == 64 && c->d_rope == 16;
 }
 
-mla_status check_weights(const mla_weights *w) {
+mla_status check_weights(const mla_config *c, const mla_weights *w) {
   if (!w) return MLA_ERR_NULL;
   if (!w->w_dq || !w->w_uq || !w->w_qr || !w->w_dkv || !w->w_kr || !w->w_uk || !w->w_uv || !w->w_o)
     return MLA_ERR_NULL;
+  if (weights_fp8(c) && (!w->s_dq || !w->s_dkv || !w->s_kr || !w->s_o)) return MLA_ERR_NULL;
   return MLA_OK;
 }
 
@@ -117,7 +131,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Workspace plans
 // ---------------------------------------------------------------------------
 struct PrefillPlan {
-  size_t c_q, ckv, kr, q, k, vt, o, total;
+  size_t c_q, ckv, kr, q, k, vt, o, x8, xs, partial, total;
 };
 PrefillPlan plan_prefill(const mla_config *c, int64_t T) {
   const size_t e = esize(c);
@@ -131,6 +145,12 @@ PrefillPlan plan_prefill(const mla_config *c, int64_t T) {
   p.k = take((size_t)T * c->n_heads * c->d_nope * e);
   p.vt = take((size_t)T * c->n_heads * c->d_v * e);
   p.o = take((size_t)T * c->n_heads * c->d_v * e);
+  // FP8 projections: the quantised h / o (codes and scale exponents), and
+  // up to 128 tokens the streaming kernel's partial sums
+  const bool f8 = weights_fp8(c);
+  p.x8 = take(f8 ? (size_t)T * fp8_act_width(c) : 0);
+  p.xs = take(f8 ? (size_t)(fp8_act_width(c) / 128) * fp8_scale_ld(T) : 0);
+  p.partial = take(f8 && T <= 128 ? gemm_stream_partial_bytes((int)T) : 0);
   p.total = off;
   return p;
 }
@@ -185,7 +205,7 @@ bool decode_sizes_ok(const mla_config *c, int32_t batch, int32_t n_q) {
 struct DecodePlan {
   int W, slots, row_groups, rows;
   SplitK sk1, sk2, sk5;
-  size_t c_q, q_nope, q_abs, o_part, lse, o_lat, o, ckv, kr, partial, total;
+  size_t c_q, q_nope, q_abs, o_part, lse, o_lat, o, ckv, kr, x8, xs, partial, total;
 };
 // The attention's split plan: W workgroups per row group (one wave of
 // workgroups over the CUs), each taking an equal share of the batch's cached
@@ -220,6 +240,9 @@ DecodePlan plan_decode(const mla_config *c, int32_t B, int32_t n_q, int32_t max_
   // FP8 cache: the new tokens' c_KV and k_R before quantisation
   p.ckv = take(cache_fp8(c) ? (size_t)T * c->d_c * e : 0);
   p.kr = take(cache_fp8(c) ? (size_t)T * c->d_rope * e : 0);
+  // FP8 projections: the quantised h / o
+  p.x8 = take(weights_fp8(c) ? (size_t)T * fp8_act_width(c) : 0);
+  p.xs = take(weights_fp8(c) ? (size_t)(fp8_act_width(c) / 128) * fp8_scale_ld(T) : 0);
   size_t part = 0;
   auto need = [&](SplitK sk, int64_t N) {
     if (sk.splits > 1) part = std::max(part, (size_t)sk.splits * T * N * 4);
@@ -351,11 +374,34 @@ GemmArgs gemm_args(const void *x, long ldx, int M, int N, int K) {
 
 mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+// Workspace of the FP8 projections' quantised input: E4M3 codes [T][K] and
+// the scale exponents [K/128][ld_s].
+struct Fp8Act {
+  unsigned char *codes, *scales;
+  long ld_s;
+};
+
+// Quantise x [M][K] (bf16, row stride K) into f and point the product's
+// activation operand at it; the weights are E4M3 with the scales wsc.
+hipError_t fp8_operands(const Fp8Act &f, const void *x, int M, int K, GemmArgs &a, hipStream_t st) {
+  hipError_t e = launch_quant_act_fp8((const bf16 *)x, K, M, K, f.codes, f.scales, f.ld_s, st);
+  if (e != hipSuccess) return e;
+  a.x = f.codes;
+  a.ldx = K;
+  a.fp8 = 1;
+  a.xs = f.scales;
+  a.xs_ld = f.ld_s;
+  a.wsc_ld = K / 128;
+  a.splits = 1;
+  a.k_chunk = K;
+  return hipSuccess;
+}
+
 // [c_Q | c_KV | k_R] = h [W_DQ; W_DKV; W_KR]^T with RoPE on k_R and the cache write.
 // with_q = false drops the W_DQ segment (plain cache compression).
 hipError_t run_compress(const mla_config *c, const mla_weights *w, const void *h, int M, RowMap rows,
                         const mla_cache *cache, int32_t batch, bool with_q, void *c_q, void *ckv_mirror, void *kr_mirror,
-                        SplitK sk, float *partial, hipStream_t st) {
+                        SplitK sk, float *partial, const Fp8Act *f8, hipStream_t st) {
   const int dt = c->dtype;
   const int N = (with_q ? c->d_cq : 0) + c->d_c + c->d_rope;
   GemmArgs a = gemm_args(h, c->d_model, M, N, c->d_model);
@@ -404,6 +450,14 @@ hipError_t run_compress(const mla_config *c, const mla_weights *w, const void *h
   a.partial = partial;
   a.name = with_q ? "q_kv_down" : "kv_compress";
   a.reduce_name = "q_kv_down.reduce";
+  if (f8) {
+    int i = 0;
+    if (with_q) a.wsc[i++] = w->s_dq;
+    a.wsc[i++] = w->s_dkv;
+    a.wsc[i++] = w->s_kr;
+    hipError_t e = fp8_operands(*f8, h, M, c->d_model, a, st);
+    if (e != hipSuccess) return e;
+  }
   hipError_t e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 1, 0, a, st);
   if (e != hipSuccess || !fp8) return e;
   CacheAppendArgs ap;
@@ -463,7 +517,7 @@ hipError_t run_query(const mla_config *c, const mla_weights *w, const void *c_q,
 
 // u = o W_O^T
 hipError_t run_output(const mla_config *c, const mla_weights *w, const void *o, int M, void *u, SplitK sk,
-                      float *partial, hipStream_t st) {
+                      float *partial, const Fp8Act *f8, hipStream_t st) {
   const int K = c->n_heads * c->d_v;
   GemmArgs a = gemm_args(o, K, M, c->d_model, K);
   a.w[0] = w->w_o;
@@ -476,6 +530,11 @@ hipError_t run_output(const mla_config *c, const mla_weights *w, const void *o, 
   a.partial = partial;
   a.name = "o_proj";
   a.reduce_name = "o_proj.reduce";
+  if (f8) {
+    a.wsc[0] = w->s_o;
+    hipError_t e = fp8_operands(*f8, o, M, K, a, st);
+    if (e != hipSuccess) return e;
+  }
   return launch_gemm(c->dtype == MLA_BF16, gemm_tile_for(c->dtype, M, a.N, a.batch), 1, 0, a, st);
 }
 
@@ -573,13 +632,13 @@ mla_status mla_compress_kv(const mla_config *cfg, const mla_weights *w, const vo
   if (!h || !seq_idx || !pos) return MLA_ERR_NULL;
   if (n <= 0 || batch <= 0) return MLA_ERR_SHAPE;
   if ((s = check_cache(cache, batch, 1)) != MLA_OK) return s;
-  if (cache_fp8(cfg)) return MLA_ERR_UNSUPPORTED;
+  if (cache_fp8(cfg) || weights_fp8(cfg)) return MLA_ERR_UNSUPPORTED;
   RowMap rows = {ROWS_EXPLICIT, 1, nullptr, seq_idx, pos};
   SplitK sk = {1, cfg->d_model};
   const hipStream_t st = (hipStream_t)stream;
   if ((s = debug_begin(st)) != MLA_OK) return s;
   return debug_end(st, hip_status(run_compress(cfg, w, h, n, rows, cache, batch, false, nullptr, nullptr, nullptr,
-                                               sk, nullptr, st)));
+                                               sk, nullptr, nullptr, st)));
 }
 
 mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *h, int32_t batch, int32_t len,
@@ -587,7 +646,7 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
                        void *stream) {
   mla_status s = check_config(cfg);
   if (s != MLA_OK) return s;
-  if ((s = check_weights(w)) != MLA_OK) return s;
+  if ((s = check_weights(cfg, w)) != MLA_OK) return s;
   if (!h || !u) return MLA_ERR_NULL;
   if (batch <= 0 || len <= 0) return MLA_ERR_SHAPE;
   const int64_t T = (int64_t)batch * len;
@@ -610,8 +669,11 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
   void *o = o_heads ? o_heads : (void *)(ws + p.o);
   hipError_t e;
 
+  const Fp8Act f8 = {(unsigned char *)(ws + p.x8), (unsigned char *)(ws + p.xs), (long)fp8_scale_ld(T)};
+  const Fp8Act *f8p = weights_fp8(cfg) ? &f8 : nullptr;
+  float *partial = weights_fp8(cfg) && T <= 128 ? (float *)(ws + p.partial) : nullptr;
   one.k_chunk = cfg->d_model;
-  e = run_compress(cfg, w, h, M, rows, cache, batch, true, ws + p.c_q, ws + p.ckv, ws + p.kr, one, nullptr, st);
+  e = run_compress(cfg, w, h, M, rows, cache, batch, true, ws + p.c_q, ws + p.ckv, ws + p.kr, one, partial, f8p, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
   one.k_chunk = cfg->d_cq;
   e = run_query(cfg, w, ws + p.c_q, M, rows, ws + p.q, (long)NH * DQK, DQK, ws + p.q, (long)NH * DQK, DQK,
@@ -657,7 +719,7 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
     if (e != hipSuccess) return MLA_ERR_HIP;
   }
   one.k_chunk = NH * cfg->d_v;
-  e = run_output(cfg, w, o, M, u, one, nullptr, st);
+  e = run_output(cfg, w, o, M, u, one, partial, f8p, st);
   return debug_end(st, hip_status(e));
 }
 
@@ -671,7 +733,7 @@ mla_status check_decode(const mla_config *cfg, const mla_weights *w, const void 
                         const mla_cache *cache, const void *u, DecodePlan *plan) {
   mla_status s = check_config(cfg);
   if (s != MLA_OK) return s;
-  if ((s = check_weights(w)) != MLA_OK) return s;
+  if ((s = check_weights(cfg, w)) != MLA_OK) return s;
   if (!h || !u || !cache_lens) return MLA_ERR_NULL;
   if (batch <= 0 || n_q <= 0 || max_cache_len < n_q) return MLA_ERR_SHAPE;
   if (cache_lens_host)
@@ -699,8 +761,10 @@ mla_status decode_steps(const mla_config *cfg, const mla_weights *w, const void 
   hipError_t e;
 
   const bool fp8 = cache_fp8(cfg);
+  const Fp8Act f8 = {(unsigned char *)(ws + p.x8), (unsigned char *)(ws + p.xs), (long)fp8_scale_ld(M)};
+  const Fp8Act *f8p = weights_fp8(cfg) ? &f8 : nullptr;
   e = run_compress(cfg, w, h, M, rows, cache, batch, true, ws + p.c_q, fp8 ? ws + p.ckv : nullptr,
-                   fp8 ? ws + p.kr : nullptr, p.sk1, partial, st);
+                   fp8 ? ws + p.kr : nullptr, p.sk1, partial, f8p, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
   if (dt == MLA_BF16 && decode_q_supported(cfg->d_cq, cfg->d_nope, cfg->d_rope, cfg->d_c, M)) {
     // up-projection, RoPE and absorption in one launch
@@ -781,7 +845,7 @@ mla_status decode_steps(const mla_config *cfg, const mla_weights *w, const void 
     e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 1, 0, a, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
   }
-  e = run_output(cfg, w, o, M, u, p.sk5, partial, st);
+  e = run_output(cfg, w, o, M, u, p.sk5, partial, f8p, st);
   return hip_status(e);
 }
 

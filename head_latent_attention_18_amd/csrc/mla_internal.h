@@ -365,6 +365,16 @@ struct GemmArgs {
   const char *name;          // timing labels (static strings)
   const char *reduce_name;
   Epi epi;
+  // Block-scaled FP8 operands (bf16 layers with FP8 projections): x holds
+  // E4M3 codes [M][K] (ldx counts bytes), xs the activation scales as
+  // biased 8-bit exponents [K/128][xs_ld] (xs_ld >= M rounded up to 256),
+  // w[] E4M3 codes with power-of-two float32 scales wsc[] per block of 128
+  // rows by 128 columns ([rows/128][wsc_ld], wsc_ld = K/128)
+  int fp8;
+  const unsigned char *xs;
+  long xs_ld;
+  const float *wsc[4];
+  int wsc_ld;
 };
 
 // dtype: 0 fp32, 1 bf16.  swap: 1 -> output rows are tokens (segment
@@ -444,6 +454,12 @@ struct CacheAppendArgs {
   CacheRef cache;
 };
 hipError_t launch_cache_append_fp8(const CacheAppendArgs &a, hipStream_t st);
+
+// Activations of the FP8 projections (quant_fp8.hip): x [T][K] bf16 (row
+// stride ldx) -> E4M3 codes [T][K] and per token and 128 columns the scale's
+// biased exponent, stored [K/128][ld_s].  K a multiple of 512.
+hipError_t launch_quant_act_fp8(const bf16 *x, long ldx, int T, int K, unsigned char *codes, unsigned char *scales,
+                                long ld_s, hipStream_t st);
 
 // kernel timing hooks (implemented with the C ABI)
 void timing_before(const char *name, hipStream_t st);

@@ -54,23 +54,35 @@ class CacheBuf:
 class MlaLayer:
     """One MLA layer's weights on the device and the libmla calls on them."""
 
-    def __init__(self, dims, dtype: str, weights: Dict[str, torch.Tensor], cache: str = "layer"):
+    def __init__(self, dims, dtype: str, weights: Dict[str, torch.Tensor], cache: str = "layer",
+                 scales: Optional[Dict[str, torch.Tensor]] = None):
+        """scales (by weight name): the block scales of FP8 projections,
+        whose weights are then E4M3 codes (MLA_WEIGHTS_FP8_BLOCK)."""
         self.dims, self.dtype, self.cache = dims, dtype, cache
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
-        self.weights = weights
-        self.cfg = L.make_config(dims, dtype, cache)
+        self.weights, self.scales = weights, scales
+        self.cfg = L.make_config(dims, dtype, cache, "fp8" if scales else "layer")
         # a cache row: d_row elements of the layer dtype, or the FP8 row's bytes
         self.row_width = L.mla_cache_bytes_per_token(self.cfg) if cache == "fp8" else dims.d_row
         self.cache_tdtype = torch.uint8 if cache == "fp8" else self.tdtype
-        self.cw = L.make_weights(weights)
+        self.cw = L.make_weights(weights, scales)
         self._ws: Dict[str, torch.Tensor] = {}
 
     @classmethod
     def from_host(cls, dims, dtype: str, weights_f32: Dict[str, np.ndarray],
-                  weights_bits: Dict[str, Optional[np.ndarray]], device="cuda", cache: str = "layer") -> "MlaLayer":
+                  weights_bits: Dict[str, Optional[np.ndarray]], device="cuda", cache: str = "layer",
+                  weights_fp8: Optional[Dict[str, tuple]] = None) -> "MlaLayer":
+        """weights_fp8: (E4M3 codes, block scales) by weight name for the FP8
+        projections; those replace the layer-dtype weights of the same name."""
         bf16 = dtype == "bf16"
         w = {k: upload(weights_f32[k], weights_bits.get(k), bf16, device) for k in L.WEIGHT_NAMES}
-        return cls(dims, dtype, w, cache)
+        scales = None
+        if weights_fp8:
+            scales = {}
+            for k, (codes, sc) in weights_fp8.items():
+                w[k] = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).to(device)
+                scales[k] = torch.from_numpy(np.ascontiguousarray(sc, dtype=np.float32)).to(device)
+        return cls(dims, dtype, w, cache, scales)
 
     def workspace(self, key: str, nbytes: int, device) -> torch.Tensor:
         ws = self._ws.get(key)

@@ -17,10 +17,13 @@ LIB_PATH = os.environ.get("MLA_LIBRARY") or os.path.join(os.path.dirname(os.path
 
 MLA_FP32, MLA_BF16 = 0, 1
 MLA_CACHE_LAYER, MLA_CACHE_FP8_E4M3 = 0, 1
+MLA_WEIGHTS_LAYER, MLA_WEIGHTS_FP8_BLOCK = 0, 1
 MLA_OP_PREFILL, MLA_OP_DECODE = 0, 1
 STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTYPE",
           -4: "MLA_ERR_WORKSPACE", -5: "MLA_ERR_CACHE", -6: "MLA_ERR_HIP", -7: "MLA_ERR_UNSUPPORTED"}
 WEIGHT_NAMES = ("w_dq", "w_uq", "w_qr", "w_dkv", "w_kr", "w_uk", "w_uv", "w_o")
+# the block scales of the FP8 projections (MLA_WEIGHTS_FP8_BLOCK), by weight
+SCALE_NAMES = ("w_dq", "w_dkv", "w_kr", "w_o")
 
 
 class MlaError(RuntimeError):
@@ -33,11 +36,12 @@ class mla_config(ctypes.Structure):
     _fields_ = [("d_model", c_int32), ("n_heads", c_int32), ("d_nope", c_int32), ("d_rope", c_int32),
                 ("d_v", c_int32), ("d_c", c_int32), ("d_cq", c_int32), ("dtype", c_int32),
                 ("rope_base", c_double), ("yarn_factor", c_double), ("yarn_beta_slow", c_double),
-                ("yarn_beta_fast", c_double), ("yarn_orig_len", c_int32), ("cache_dtype", c_int32)]
+                ("yarn_beta_fast", c_double), ("yarn_orig_len", c_int32), ("cache_dtype", c_int32),
+                ("weight_dtype", c_int32)]
 
 
 class mla_weights(ctypes.Structure):
-    _fields_ = [(n, c_void_p) for n in WEIGHT_NAMES]
+    _fields_ = [(n, c_void_p) for n in WEIGHT_NAMES] + [("s_" + n[2:], c_void_p) for n in SCALE_NAMES]
 
 
 class mla_cache(ctypes.Structure):
@@ -121,16 +125,20 @@ def _stream(stream) -> Optional[int]:
 # Struct builders
 # ---------------------------------------------------------------------------
 
-def make_config(dims, dtype: str, cache: str = "layer") -> mla_config:
+def make_config(dims, dtype: str, cache: str = "layer", weights: str = "layer") -> mla_config:
     return mla_config(dims.d_model, dims.n_heads, dims.d_nope, dims.d_rope, dims.d_v, dims.d_c, dims.d_cq,
                       MLA_BF16 if dtype == "bf16" else MLA_FP32, float(dims.rope_base),
                       float(getattr(dims, "yarn_factor", 1.0)), float(getattr(dims, "yarn_beta_slow", 1.0)),
                       float(getattr(dims, "yarn_beta_fast", 32.0)), int(getattr(dims, "yarn_orig_len", 4096)),
-                      MLA_CACHE_FP8_E4M3 if cache == "fp8" else MLA_CACHE_LAYER)
+                      MLA_CACHE_FP8_E4M3 if cache == "fp8" else MLA_CACHE_LAYER,
+                      MLA_WEIGHTS_FP8_BLOCK if weights == "fp8" else MLA_WEIGHTS_LAYER)
 
 
-def make_weights(w: Dict[str, object]) -> mla_weights:
-    return mla_weights(*[_ptr(w.get(n)) for n in WEIGHT_NAMES])
+def make_weights(w: Dict[str, object], scales: Optional[Dict[str, object]] = None) -> mla_weights:
+    """Weight pointers by name; `scales` (by weight name) gives the block
+    scales of the FP8 projections."""
+    scales = scales or {}
+    return mla_weights(*[_ptr(w.get(n)) for n in WEIGHT_NAMES], *[_ptr(scales.get(n)) for n in SCALE_NAMES])
 
 
 def make_cache(pool, *, max_len: int = 0, block_size: int = 0, n_blocks: int = 0, block_table=None,

@@ -89,6 +89,36 @@ typedef enum mla_cache_dtype {
   MLA_CACHE_FP8_E4M3 = 1
 } mla_cache_dtype;
 
+/* Format of the projections between the hidden width and the latent and head
+ * space that read h or write u: W_DQ, W_DKV, W_KR and W_O
+ * (mla_config.weight_dtype).
+ *   MLA_WEIGHTS_LAYER: every weight in the layer dtype.
+ *   MLA_WEIGHTS_FP8_BLOCK: block-scaled FP8 GEMMs (the FP8 framework of the
+ *     V3 technical-report summary, "FP8 training framework" paragraph and
+ *     figures 6 and 7; the CSDN blog, "FP8 mixed-precision training
+ *     framework": FP8 inputs, higher-precision outputs, activations and
+ *     weights scaled in blocks, 128 elements per accumulation interval).
+ *     w_dq, w_dkv, w_kr and w_o then hold E4M3 codes (OCP 8-bit floating
+ *     point, one byte each, row-major [out][in]) and s_dq, s_dkv, s_kr and
+ *     s_o one float32 scale per block of 128 output rows by 128 input
+ *     columns, row-major [ceil(out/128)][in/128]: element (r, c) is
+ *     code[r][c] * scale[r/128][c/128].  Every scale is a power of two
+ *     2^k, -126 <= k <= 127 (only its power of two is applied: the gfx950
+ *     scaled FP8 MFMAs take 8-bit exponents).  The library quantises what
+ *     enters these products, h and the attention output o as held in bf16,
+ *     per token and group of 128 columns, with the smallest power-of-two
+ *     scale s for which 448 s >= the group's largest magnitude (1 for an
+ *     all-zero group) and each value the E4M3 code nearest to x / s (ties
+ *     to even); products of codes are exact, the scales are applied exactly
+ *     and the sums accumulate in float32; outputs are bf16.  w_uq, w_qr,
+ *     w_uk and w_uv stay in the layer dtype.  Needs dtype MLA_BF16 and
+ *     d_model and n_heads*d_v multiples of 512; mla_compress_kv does not
+ *     support it (it has no workspace for the quantised h). */
+typedef enum mla_weight_dtype {
+  MLA_WEIGHTS_LAYER = 0,
+  MLA_WEIGHTS_FP8_BLOCK = 1
+} mla_weight_dtype;
+
 /* Layer dimensions.  Supported envelope (checked, MLA_ERR_UNSUPPORTED
  * otherwise): d_rope even; for BF16 d_model, d_cq, d_c multiples of 64,
  * d_nope, d_rope, d_v multiples of 32, n_heads*d_v a multiple of 64; for FP32
@@ -120,15 +150,20 @@ typedef struct mla_config {
   double yarn_beta_fast;
   int32_t yarn_orig_len;
   int32_t cache_dtype;  /* mla_cache_dtype; 0 (a zero-initialised config) = layer dtype */
+  int32_t weight_dtype; /* mla_weight_dtype; 0 = layer dtype */
 } mla_config;
 
-/* The eight projections, each row-major [out][in] in the config dtype:
+/* The eight projections, each row-major [out][in] in the config dtype
+ * (w_dq, w_dkv, w_kr and w_o as E4M3 codes under MLA_WEIGHTS_FP8_BLOCK):
  *   w_dq [d_cq][d_model]            w_uq [n_heads*d_nope][d_cq]
  *   w_qr [n_heads*d_rope][d_cq]     w_dkv [d_c][d_model]
  *   w_kr [d_rope][d_model]          w_uk [n_heads*d_nope][d_c]
- *   w_uv [n_heads*d_v][d_c]         w_o  [d_model][n_heads*d_v]            */
+ *   w_uv [n_heads*d_v][d_c]         w_o  [d_model][n_heads*d_v]
+ * s_dq, s_dkv, s_kr, s_o: the block scales of MLA_WEIGHTS_FP8_BLOCK
+ * (float32 [ceil(out/128)][in/128]); ignored, and may be NULL, otherwise. */
 typedef struct mla_weights {
   const void *w_dq, *w_uq, *w_qr, *w_dkv, *w_kr, *w_uk, *w_uv, *w_o;
+  const float *s_dq, *s_dkv, *s_kr, *s_o;
 } mla_weights;
 
 /* Latent cache.  pool holds n_blocks*block_size rows of

@@ -54,7 +54,9 @@ mla_config dsv3() {
 
 mla_weights fake_weights() {
   mla_weights w;
+  std::memset(&w, 0, sizeof w);
   w.w_dq = w.w_uq = w.w_qr = w.w_dkv = w.w_kr = w.w_uk = w.w_uv = w.w_o = FAKE;
+  w.s_dq = w.s_dkv = w.s_kr = w.s_o = (const float *)FAKE;
   return w;
 }
 
@@ -168,6 +170,20 @@ void fixed_cases() {
   c.cache_dtype = MLA_CACHE_FP8_E4M3;
   EXPECT_EQ(mla_compress_kv(&c, &w, FAKE, 4, (const int32_t *)FAKE, (const int32_t *)FAKE, 1, &k16, nullptr),
             MLA_ERR_UNSUPPORTED);
+  // block-scaled FP8 projections
+  c = dsv3();
+  c.weight_dtype = MLA_WEIGHTS_FP8_BLOCK;
+  EXPECT_EQ(mla_workspace_size(&c, 1, 32, 1, 4096, &bytes), MLA_OK);
+  mla_weights wns = w;
+  wns.s_o = nullptr;
+  EXPECT_EQ(mla_prefill(&c, &wns, FAKE, 1, 16, &k16, FAKE, nullptr, FAKE, 1ull << 40, nullptr), MLA_ERR_NULL);
+  EXPECT_EQ(mla_compress_kv(&c, &w, FAKE, 4, (const int32_t *)FAKE, (const int32_t *)FAKE, 1, &k16, nullptr),
+            MLA_ERR_UNSUPPORTED);
+  c.weight_dtype = 5;
+  EXPECT_EQ(mla_workspace_size(&c, 1, 32, 1, 4096, &bytes), MLA_ERR_DTYPE);
+  c.weight_dtype = MLA_WEIGHTS_FP8_BLOCK;
+  c.d_model = 7168 + 64;
+  EXPECT_EQ(mla_workspace_size(&c, 1, 32, 1, 4096, &bytes), MLA_ERR_UNSUPPORTED);
 }
 
 // Random configurations and sizes: any status is acceptable, but no call may
@@ -186,6 +202,7 @@ void sweeps(int n) {
     }
     if (next_u64() % 3 == 0) c.dtype = pick_i32() & 3;
     if (next_u64() % 3 == 0) c.cache_dtype = pick_i32() & 3;
+    if (next_u64() % 3 == 0) c.weight_dtype = pick_i32() & 3;
     if (next_u64() % 4 == 0) {
       c.yarn_factor = pick_f64();
       c.yarn_beta_slow = pick_f64();

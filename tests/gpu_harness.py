@@ -58,12 +58,18 @@ def assert_close(got, ref, bf16: bool, what: str):
 
 
 def weights64(wl: Workload):
-    return {k: v.astype(np.float64) for k, v in wl.weights_f32.items()}
+    """The weights as the oracle takes them (float64); FP8 projections
+    dequantised by the oracle."""
+    W = {k: v.astype(np.float64) for k, v in wl.weights_f32.items()}
+    for k, (codes, sc) in (wl.weights_fp8 or {}).items():
+        W[k] = O.dequantize_weight_blocks(codes, sc)
+    return W
 
 
 def layer_for(wl: Workload) -> MlaLayer:
     return MlaLayer.from_host(wl.dims, wl.dtype, wl.weights_f32, wl.weights_bits,
-                              cache="fp8" if getattr(wl, "cache_fp8", False) else "layer")
+                              cache="fp8" if getattr(wl, "cache_fp8", False) else "layer",
+                              weights_fp8=wl.weights_fp8)
 
 
 def decode_cache(wl: Workload, layer: MlaLayer, max_len: int = None, paged: bool = None):
@@ -103,7 +109,7 @@ def oracle_cache_rows(wl: Workload, b: int):
 def oracle_decode_seq(wl: Workload, b: int, heads=None):
     h = wl.h_f32[b].astype(np.float64)
     return O.decode(wl.dims, weights64(wl), h, oracle_cache_rows(wl, b), heads=heads,
-                    cache_fp8=getattr(wl, "cache_fp8", False))
+                    cache_fp8=getattr(wl, "cache_fp8", False), weights_fp8=wl.weights_fp8 is not None)
 
 
 def assert_fp8_rows(got_bytes, ref_rows, dims, what: str):

@@ -207,6 +207,39 @@ def test_fp8_cache_validation():
                                    ctypes.byref(L.make_cache(FAKE, max_len=16)), None) == -7
 
 
+def test_fp8_weights_validation():
+    """Block-scaled FP8 projections: the scale pointers are required, the
+    layer must be bf16 with d_model and n_heads*d_v multiples of 512, and
+    the standalone compression (no workspace for the quantised h) refuses."""
+    fp8 = L.make_config(DSV3, "bf16", weights="fp8")
+    out = ctypes.c_size_t(0)
+    ws = lambda cfg: L.lib().mla_workspace_size(ctypes.byref(cfg), 1, 32, 1, 4096, ctypes.byref(out))
+    assert ws(fp8) == 0
+    base = ws(L.make_config(DSV3, "bf16")) == 0 and out.value
+    ws(fp8)
+    assert out.value > base                      # room for the quantised activations
+    scales = {n: FAKE for n in L.SCALE_NAMES}
+    w = L.make_weights({n: FAKE for n in L.WEIGHT_NAMES}, scales)
+    w_no_so = L.make_weights({n: FAKE for n in L.WEIGHT_NAMES}, dict(scales, w_o=None))
+    cache = L.make_cache(FAKE, max_len=16)
+    # a 1 KiB workspace: every call below stops at validation, before any HIP call
+    call = lambda cfg, ww: L.lib().mla_prefill(ctypes.byref(cfg), ctypes.byref(ww), FAKE, 1, 16, ctypes.byref(cache),
+                                                FAKE, None, FAKE, 1024, None)
+    assert call(fp8, w_no_so) == -1
+    assert call(fp8, w) == -4
+    assert call(L.make_config(DSV3, "bf16"), w_no_so) == -4    # scales ignored without FP8 weights
+    f32 = L.make_config(TINY, "fp32", weights="fp8")
+    assert L.lib().mla_workspace_size(ctypes.byref(f32), 1, 1, 1, 8, ctypes.byref(out)) == -7
+    odd = L.make_config(DSV3, "bf16", weights="fp8")
+    odd.d_model = 7168 + 64
+    assert ws(odd) == -7
+    bad = L.make_config(DSV3, "bf16")
+    bad.weight_dtype = 9
+    assert ws(bad) == -3
+    assert L.lib().mla_compress_kv(ctypes.byref(fp8), ctypes.byref(w), FAKE, 4, FAKE, FAKE, 1,
+                                   ctypes.byref(cache), None) == -7
+
+
 def test_compress_validation():
     cfg = _cfg()
     w = _weights()
