@@ -30,21 +30,33 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def decode_kernel_bytes(d, B, n_q, sum_len, e=2, row_bytes=None):
+def decode_kernel_bytes(d, B, n_q, sum_len, e=2, row_bytes=None, fp8_weights=False):
     """Algorithmic HBM bytes per launch of each decode kernel (weights and
     cache read once, activations read/written once); row_bytes is the size
     of a cached row (e * (d_c + d_R) for a cache in the layer dtype, 656 for
-    the FP8 cache)."""
+    the FP8 cache).  fp8_weights: W_DQ, W_DKV, W_KR and W_O are one byte per
+    element plus a 4-byte scale per 128x128 block, and their products read
+    the quantised activations (a byte per element, a byte per 128)."""
     T = B * n_q
     nh = d.n_heads
     D = d.d_c + d.d_rope
     rb = e * D if row_bytes is None else row_bytes
+    if fp8_weights:
+        w_down = (d.d_cq + D) * d.d_model * (1 + 4 / 16384)
+        w_o = d.d_model * nh * d.d_v * (1 + 4 / 16384)
+        return {
+            "quant_fp8": int(e * T * (d.d_model + nh * d.d_v) + T * (d.d_model + nh * d.d_v) * (1 + 1 / 128)),
+            "q_kv_down": int(w_down + T * d.d_model * (1 + 1 / 128) + e * (T * d.d_cq + T * D)),
+            "o_proj": int(w_o + T * nh * d.d_v * (1 + 1 / 128) + e * T * d.d_model),
+        } | {k: v for k, v in decode_kernel_bytes(d, B, n_q, sum_len, e, row_bytes).items()
+             if k not in ("q_kv_down", "o_proj")}
     return {
         "q_kv_down": e * ((d.d_cq + D) * d.d_model + T * d.d_model + T * d.d_cq + T * D),
         "q_up": e * (nh * (d.d_nope + d.d_rope) * d.d_cq + T * d.d_cq + T * nh * (d.d_nope + d.d_rope)),
@@ -59,12 +71,23 @@ def decode_kernel_bytes(d, B, n_q, sum_len, e=2, row_bytes=None):
     }
 
 
-def decode_step_bytes(d, B, n_q, sum_len, e=2, row_bytes=None):
-    """Whole decode step: every weight once, every cached row once, h in, u out."""
+def decode_step_bytes(d, B, n_q, sum_len, e=2, row_bytes=None, fp8_weights=False):
+    """Whole decode step: every weight once, every cached row once, h in, u
+    out.  fp8_weights: W_DQ, W_DKV, W_KR and W_O at one byte per element
+    plus their block scales."""
+    nfp8 = (d.d_cq + d.d_c + d.d_rope) * d.d_model + d.d_model * d.n_heads * d.d_v
     nparams = (d.d_cq * d.d_model + d.n_heads * (d.d_nope + d.d_rope) * d.d_cq + (d.d_c + d.d_rope) * d.d_model
                + d.n_heads * (d.d_nope + d.d_v) * d.d_c + d.d_model * d.n_heads * d.d_v)
     rb = e * (d.d_c + d.d_rope) if row_bytes is None else row_bytes
-    return e * (nparams + 2 * B * n_q * d.d_model) + sum_len * rb
+    wbytes = e * nparams if not fp8_weights else e * (nparams - nfp8) + int(nfp8 * (1 + 4 / 16384))
+    return wbytes + e * 2 * B * n_q * d.d_model + sum_len * rb
+
+
+def prefill_fp8_flops(d, B, L):
+    """The part of prefill_flops done by the FP8 projections (W_DQ, W_DKV,
+    W_KR, W_O)."""
+    T = B * L
+    return 2 * T * d.d_model * (d.d_cq + d.d_c + d.d_rope) + 2 * T * d.n_heads * d.d_v * d.d_model
 
 
 def prefill_flops(d, B, L):
@@ -143,14 +166,16 @@ def event_kernels(ktimes):
             for k, v in ktimes.items()}
 
 
-def run_prefill(args, dev):
-    """Causal prefill of the DeepSeek-V3 layer, batch 1 x 4096 tokens, bf16:
-    per-call event times of at least 20 calls (median, p10, p90)."""
+def run_prefill(args, dev, weights_kind="layer"):
+    """Causal prefill of the DeepSeek-V3 layer, batch 1 x 4096 tokens, bf16
+    (weights_kind "fp8": block-scaled FP8 projections): per-call event times
+    of at least 20 calls (median, p10, p90)."""
     import torch
     from head_latent_attention_18_amd.layer import MlaLayer, upload
     from mla_inputs import make_workload
-    wp = make_workload(3)
-    lp = MlaLayer.from_host(wp.dims, "bf16", wp.weights_f32, wp.weights_bits)
+    f8 = weights_kind == "fp8"
+    wp = make_workload(3, weights_fp8=f8)
+    lp = MlaLayer.from_host(wp.dims, "bf16", wp.weights_f32, wp.weights_bits, weights_fp8=wp.weights_fp8)
     hp = upload(wp.h_f32, wp.h_bits, True)
     cp = lp.new_cache(wp.batch, wp.seq_len)
     for _ in range(3):
@@ -161,11 +186,18 @@ def run_prefill(args, dev):
     pdt = st["ms_median"] * 1e-3
     pk_times = kernel_times(lambda i: lp.prefill(hp, cp), pk)
     fl = prefill_flops(wp.dims, wp.batch, wp.seq_len)
-    log(f"prefill: median {pdt * 1e3:.3f} ms (p10 {st['ms_p10']:.3f}, p90 {st['ms_p90']:.3f}), "
-        f"{fl / pdt / 1e12:.1f} TFLOPS")
-    return {"workload": wp.name, "ms": st["ms_median"], **st, "TFLOPS": round(fl / pdt / 1e12, 1),
-            "mfma_frac": round(fl / pdt / 1e12 / BF16_PEAK_TFLOPS, 4), "alg_flops": fl,
-            "kernels": event_kernels(pk_times)}
+    log(f"prefill{' (FP8 projections)' if f8 else ''}: median {pdt * 1e3:.3f} ms (p10 {st['ms_p10']:.3f}, "
+        f"p90 {st['ms_p90']:.3f}), {fl / pdt / 1e12:.1f} TFLOPS")
+    out = {"workload": wp.name + ("-fp8weights" if f8 else ""), "ms": st["ms_median"], **st,
+           "TFLOPS": round(fl / pdt / 1e12, 1), "mfma_frac": round(fl / pdt / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "alg_flops": fl, "kernels": event_kernels(pk_times)}
+    if f8:
+        # the FP8 projections' flops at the FP8 MFMA peak, the rest at bf16
+        f8fl = prefill_fp8_flops(wp.dims, wp.batch, wp.seq_len)
+        bound = f8fl / (FP8_PEAK_TFLOPS * 1e12) + (fl - f8fl) / (BF16_PEAK_TFLOPS * 1e12)
+        out.update({"fp8_flops": f8fl, "mfma_bound_ms": round(bound * 1e3, 4),
+                    "mfma_frac": round(bound / pdt, 4)})
+    return out
 
 
 def decode_attn_flops(d, lens, n_q):
@@ -205,7 +237,7 @@ def device_cache_rows(d, n, gen, dev, fp8):
     return out
 
 
-def run_decode_workload(args, dev, wid, cache_kind="layer"):
+def run_decode_workload(args, dev, wid, cache_kind="layer", weights_kind="layer"):
     """Decode step of workload 2 (batch 32, cache 4096), 4 (batch 128,
     lengths U{1..32768}, paged 64-row blocks in a permuted order) or 5
     (batch 4, 128K cache, two query tokens), with a bf16 or an FP8 latent
@@ -221,11 +253,13 @@ def run_decode_workload(args, dev, wid, cache_kind="layer"):
     from mla_inputs import make_workload
     t0 = time.perf_counter()
     fp8 = cache_kind == "fp8"
-    wl = make_workload(wid, cache_rows=False)
+    w8 = weights_kind == "fp8"
+    wl = make_workload(wid, cache_rows=False, weights_fp8=w8)
     d = wl.dims
     B, nq = wl.batch, wl.n_q
     lens_np = wl.lens.astype(np.int32)
-    layer = MlaLayer.from_host(d, "bf16", wl.weights_f32, wl.weights_bits, cache=cache_kind)
+    layer = MlaLayer.from_host(d, "bf16", wl.weights_f32, wl.weights_bits, cache=cache_kind,
+                               weights_fp8=wl.weights_fp8)
     gen = torch.Generator(device=dev)
     gen.manual_seed(1000 + wid + (500 if fp8 else 0))
 
@@ -249,7 +283,8 @@ def run_decode_workload(args, dev, wid, cache_kind="layer"):
     h = upload(wl.h_f32, wl.h_bits, True)
     sets = [(layer, new_cache(), h)]
     for _ in range((args.sets if wid == 2 else 1) - 1):
-        lw = MlaLayer(d, "bf16", {k: v.clone() for k, v in layer.weights.items()}, cache=cache_kind)
+        lw = MlaLayer(d, "bf16", {k: v.clone() for k, v in layer.weights.items()}, cache=cache_kind,
+                      scales={k: v.clone() for k, v in layer.scales.items()} if layer.scales else None)
         sets.append((lw, new_cache(), h.clone()))
     lens = torch.from_numpy(lens_np).to(dev)
     Lmax = int(lens_np.max())
@@ -260,7 +295,7 @@ def run_decode_workload(args, dev, wid, cache_kind="layer"):
         lw.decode(hh, lens, Lmax, c, u=u, lens_host=lens_np)
 
     torch.cuda.synchronize()
-    name = wl.name + ("-fp8cache" if fp8 else "")
+    name = wl.name + ("-fp8cache" if fp8 else "") + ("-fp8weights" if w8 else "")
     log(f"workload {name}: set up in {time.perf_counter() - t0:.1f}s, sum of lengths {int(lens_np.sum())}")
     for i in range(5):
         run(i)
@@ -271,7 +306,7 @@ def run_decode_workload(args, dev, wid, cache_kind="layer"):
     kt = kernel_times(run, k)
     sum_len = int(lens_np.sum())
     rb = layer.row_width * (1 if fp8 else 2)
-    step_bytes = decode_step_bytes(d, B, nq, sum_len, row_bytes=rb)
+    step_bytes = decode_step_bytes(d, B, nq, sum_len, row_bytes=rb, fp8_weights=w8)
     kb = decode_kernel_bytes(d, B, nq, sum_len, row_bytes=rb)["decode_attn"]
     attn_fl = decode_attn_flops(d, lens_np, nq)
     attn_ms = kt["decode_attn"]["avg_ms"]
@@ -283,7 +318,7 @@ def run_decode_workload(args, dev, wid, cache_kind="layer"):
     del sets, layer
     torch.cuda.empty_cache()
     return {"workload": name, "batch": B, "n_q": nq, "sum_len": sum_len, "max_len": Lmax, "paged": wl.paged,
-            "cache": cache_kind, "cache_row_bytes": rb,
+            "cache": cache_kind, "cache_row_bytes": rb, "weights": weights_kind,
             **st, "tokens_per_s": round(B * nq / dt, 1),
             "step_hbm": {"alg_bytes": step_bytes, "GBps": round(step_bytes / dt / 1e9, 1),
                          "frac": round(step_bytes / dt / 1e9 / HBM_PEAK_GBS, 4)},
@@ -353,7 +388,9 @@ def main():
                     help="profiling runs: time one path only (the JSON line is printed for 'all' and 'decode')")
     ap.add_argument("--cache", choices=["layer", "fp8"], default="layer",
                     help="latent cache of the --only decode/ragged/long runs (fp8: E4M3 codes + group scales)")
-    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache decode workloads")
+    ap.add_argument("--weights", choices=["layer", "fp8"], default="layer",
+                    help="projections of the --only runs (fp8: W_DQ, W_DKV, W_KR, W_O block-scaled E4M3)")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache and FP8-weight workloads")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only copy a buffer of this many MB three times (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -382,14 +419,14 @@ def main():
         args.no_cpu_baseline = True
 
     if args.only == "prefill":
-        print(json.dumps(run_prefill(args, dev)), flush=True)
+        print(json.dumps(run_prefill(args, dev, args.weights)), flush=True)
         return
     if args.only == "chunk":
         print(json.dumps(run_chunk(args, dev)), flush=True)
         return
-    if args.only in ("ragged", "long") or (args.only == "decode" and args.cache == "fp8"):
+    if args.only in ("ragged", "long") or (args.only == "decode" and (args.cache == "fp8" or args.weights == "fp8")):
         wid = {"decode": 2, "ragged": 4, "long": 5}[args.only]
-        print(json.dumps(run_decode_workload(args, dev, wid, args.cache)), flush=True)
+        print(json.dumps(run_decode_workload(args, dev, wid, args.cache, args.weights)), flush=True)
         return
 
     # ------------------------------------------------------------ decode
@@ -492,11 +529,16 @@ def main():
     if args.only == "all" and not args.no_extra:
         ragged = run_decode_workload(args, dev, 4)
         long_ctx = run_decode_workload(args, dev, 5)
+    fp8w = None
     if args.only == "all" and not args.no_fp8:
         fp8 = {"b32_len4096": run_decode_workload(args, dev, 2, "fp8")}
         if not args.no_extra:
             fp8["ragged"] = run_decode_workload(args, dev, 4, "fp8")
             fp8["long"] = run_decode_workload(args, dev, 5, "fp8")
+        fp8w = {"decode_b32_len4096": run_decode_workload(args, dev, 2, "layer", "fp8"),
+                "decode_b32_len4096_fp8cache": run_decode_workload(args, dev, 2, "fp8", "fp8")}
+        if not args.no_prefill:
+            fp8w["prefill_len4096"] = run_prefill(args, dev, "fp8")
 
     out = {
         "metric": "MLA decode tokens/s (DeepSeek-V3 layer, batch 32, cache 4096)",
@@ -526,6 +568,7 @@ def main():
         "decode_ragged": ragged,
         "decode_long": long_ctx,
         "decode_fp8_cache": fp8,
+        "fp8_weights": fp8w,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

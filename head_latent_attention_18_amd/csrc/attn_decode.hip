@@ -1022,7 +1022,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 // taking features 16w..16w+15.  The token groups of a head share an XCD,
 // whose L2 serves their common reads of W_UV,i.
 template <int DC, int DR, int DV>
-__global__ __launch_bounds__(512, 1) void decode_combine_uv_kernel(DecodeArgs a, const bf16 *w_uv, bf16 *o) {
+__global__ __launch_bounds__(512, 1) void decode_combine_uv_kernel(DecodeArgs a, const bf16 *w_uv, bf16 *o,
+                                                                    Fp8Out q8) {
   constexpr int TT = 16, NM = 4;         // tokens per workgroup, merging waves
   constexpr int NW = 8;                  // waves
   constexpr int KS = DC / 32;            // k steps
@@ -1170,19 +1171,51 @@ __global__ __launch_bounds__(512, 1) void decode_combine_uv_kernel(DecodeArgs a,
   }
   // lane: features 16*wave + 4*lgrp + 0..3 of token lrow
   const int t = tg * TT + lrow;
-  if (t < T) {
-    bf16 *orow = o + ((long)t * a.n_h + h) * DV + wave * 16 + 4 * lgrp;
-    *(bf16x4 *)orow = bf16x4{(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
+  const bf16x4 ob = bf16x4{(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
+  if (t < T) *(bf16x4 *)(o + ((long)t * a.n_h + h) * DV + wave * 16 + 4 * lgrp) = ob;
+  if (q8.codes) {
+    // FP8 projections: the head's 128 outputs of a token (its bf16 values)
+    // are one quantisation group; their maximum magnitude is gathered from
+    // the lane's four, the token's four lane groups and the eight waves
+    __shared__ float gmax[NW][TT];
+    float v[4], m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = (float)ob[e];
+      m = fmaxf(m, fabsf(v[e]));
+    }
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    if (lgrp == 0) gmax[wave][lrow] = m;
+    __syncthreads();
+    float amax = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) amax = fmaxf(amax, gmax[w][lrow]);
+    // smallest power of two 2^k with 448 * 2^k >= amax (as the activation quantiser)
+    int k = 0;
+    if (amax > 0.f) {
+      int e;
+      const float f = frexpf(amax, &e);
+      k = max(e - 9 + (f > 0.875f ? 1 : 0), -126);
+    }
+    const float inv = ldexpf(1.f, -k);
+    const unsigned lo = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(v[0] * inv, v[1] * inv, 0, false) & 0xFFFFu;
+    const unsigned hi = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(v[2] * inv, v[3] * inv, 0, false) & 0xFFFFu;
+    if (t < T) {
+      *(unsigned *)(q8.codes + ((long)t * a.n_h + h) * DV + wave * 16 + 4 * lgrp) = lo | (hi << 16);
+      if (wave == 0 && lgrp == 0) q8.scales[(long)h * q8.ld_s + t] = (unsigned char)(k + 127);
+    }
   }
 }
 
-hipError_t launch_decode_combine_uv(const DecodeArgs &a, int d_v, const void *w_uv, void *o, hipStream_t st) {
+hipError_t launch_decode_combine_uv(const DecodeArgs &a, int d_v, const void *w_uv, void *o, Fp8Out q8,
+                                    hipStream_t st) {
   if (a.d_c != 512 || a.d_rope != 64 || d_v != 128) return hipErrorNotSupported;
   const int T = a.B * a.n_q;
   const int grid = ((a.n_h + 7) / 8) * 8 * ((T + 15) / 16);
   timing_before("decode_combine_uv", st);
   hipLaunchKernelGGL((decode_combine_uv_kernel<512, 64, 128>), dim3(grid), dim3(512), 0, st, a,
-                     (const bf16 *)w_uv, (bf16 *)o);
+                     (const bf16 *)w_uv, (bf16 *)o, q8);
   timing_after("decode_combine_uv", st);
   return hipGetLastError();
 }

@@ -202,6 +202,7 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
     int sx[4], sxn[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) sxn[j] = xsp[j * 32];
+    float wsn = wsp[0];   // the next slab's weight scale, loaded a slab ahead
     issue(0, 0);
     for (int kt = 0; kt < nkt; ++kt) {
       wait_vm<0>();     // this wave's copies of slab kt (and its token exponents)
@@ -209,12 +210,13 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
       bar();            // slab kt landed for every wave; stage (kt+1) % 2 is free
 #pragma unroll
       for (int j = 0; j < 4; ++j) sx[j] = sxn[j];
+      const int sw = (int)((__builtin_bit_cast(unsigned, wsn) >> 23) & 0xFFu);
       if (kt + 1 < nkt) {
         issue(kt + 1, (kt + 1) % GNS);
 #pragma unroll
         for (int j = 0; j < 4; ++j) sxn[j] = xsp[(long)(kt + 1) * a.xs_ld + j * 32];
+        wsn = wsp[kt + 1];
       }
-      const int sw = (int)((__builtin_bit_cast(unsigned, wsp[kt]) >> 23) & 0xFFu);
       const int st = kt % GNS;
       rd8(st, 0);
       rd8(st, 1);

@@ -374,18 +374,14 @@ GemmArgs gemm_args(const void *x, long ldx, int M, int N, int K) {
 
 mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
-// Workspace of the FP8 projections' quantised input: E4M3 codes [T][K] and
-// the scale exponents [K/128][ld_s].
-struct Fp8Act {
-  unsigned char *codes, *scales;
-  long ld_s;
-};
-
-// Quantise x [M][K] (bf16, row stride K) into f and point the product's
-// activation operand at it; the weights are E4M3 with the scales wsc.
-hipError_t fp8_operands(const Fp8Act &f, const void *x, int M, int K, GemmArgs &a, hipStream_t st) {
-  hipError_t e = launch_quant_act_fp8((const bf16 *)x, K, M, K, f.codes, f.scales, f.ld_s, st);
-  if (e != hipSuccess) return e;
+// Quantise x [M][K] (bf16, row stride K) into f, unless its producer already
+// wrote it there, and point the product's activation operand at it; the
+// weights are E4M3 with the scales wsc.
+hipError_t fp8_operands(const Fp8Out &f, const void *x, int M, int K, GemmArgs &a, bool quantised, hipStream_t st) {
+  if (!quantised) {
+    hipError_t e = launch_quant_act_fp8((const bf16 *)x, K, M, K, f.codes, f.scales, f.ld_s, st);
+    if (e != hipSuccess) return e;
+  }
   a.x = f.codes;
   a.ldx = K;
   a.fp8 = 1;
@@ -401,7 +397,7 @@ hipError_t fp8_operands(const Fp8Act &f, const void *x, int M, int K, GemmArgs &
 // with_q = false drops the W_DQ segment (plain cache compression).
 hipError_t run_compress(const mla_config *c, const mla_weights *w, const void *h, int M, RowMap rows,
                         const mla_cache *cache, int32_t batch, bool with_q, void *c_q, void *ckv_mirror, void *kr_mirror,
-                        SplitK sk, float *partial, const Fp8Act *f8, hipStream_t st) {
+                        SplitK sk, float *partial, const Fp8Out *f8, hipStream_t st) {
   const int dt = c->dtype;
   const int N = (with_q ? c->d_cq : 0) + c->d_c + c->d_rope;
   GemmArgs a = gemm_args(h, c->d_model, M, N, c->d_model);
@@ -455,7 +451,7 @@ hipError_t run_compress(const mla_config *c, const mla_weights *w, const void *h
     if (with_q) a.wsc[i++] = w->s_dq;
     a.wsc[i++] = w->s_dkv;
     a.wsc[i++] = w->s_kr;
-    hipError_t e = fp8_operands(*f8, h, M, c->d_model, a, st);
+    hipError_t e = fp8_operands(*f8, h, M, c->d_model, a, false, st);
     if (e != hipSuccess) return e;
   }
   hipError_t e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 1, 0, a, st);
@@ -516,8 +512,9 @@ hipError_t run_query(const mla_config *c, const mla_weights *w, const void *c_q,
 }
 
 // u = o W_O^T
+// f8_ready: the attention already wrote o's quantised form into *f8
 hipError_t run_output(const mla_config *c, const mla_weights *w, const void *o, int M, void *u, SplitK sk,
-                      float *partial, const Fp8Act *f8, hipStream_t st) {
+                      float *partial, const Fp8Out *f8, bool f8_ready, hipStream_t st) {
   const int K = c->n_heads * c->d_v;
   GemmArgs a = gemm_args(o, K, M, c->d_model, K);
   a.w[0] = w->w_o;
@@ -532,7 +529,7 @@ hipError_t run_output(const mla_config *c, const mla_weights *w, const void *o, 
   a.reduce_name = "o_proj.reduce";
   if (f8) {
     a.wsc[0] = w->s_o;
-    hipError_t e = fp8_operands(*f8, o, M, K, a, st);
+    hipError_t e = fp8_operands(*f8, o, M, K, a, f8_ready, st);
     if (e != hipSuccess) return e;
   }
   return launch_gemm(c->dtype == MLA_BF16, gemm_tile_for(c->dtype, M, a.N, a.batch), 1, 0, a, st);
@@ -669,8 +666,8 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
   void *o = o_heads ? o_heads : (void *)(ws + p.o);
   hipError_t e;
 
-  const Fp8Act f8 = {(unsigned char *)(ws + p.x8), (unsigned char *)(ws + p.xs), (long)fp8_scale_ld(T)};
-  const Fp8Act *f8p = weights_fp8(cfg) ? &f8 : nullptr;
+  const Fp8Out f8 = {(unsigned char *)(ws + p.x8), (unsigned char *)(ws + p.xs), (long)fp8_scale_ld(T)};
+  const Fp8Out *f8p = weights_fp8(cfg) ? &f8 : nullptr;
   float *partial = weights_fp8(cfg) && T <= 128 ? (float *)(ws + p.partial) : nullptr;
   one.k_chunk = cfg->d_model;
   e = run_compress(cfg, w, h, M, rows, cache, batch, true, ws + p.c_q, ws + p.ckv, ws + p.kr, one, partial, f8p, st);
@@ -719,7 +716,7 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
     if (e != hipSuccess) return MLA_ERR_HIP;
   }
   one.k_chunk = NH * cfg->d_v;
-  e = run_output(cfg, w, o, M, u, one, partial, f8p, st);
+  e = run_output(cfg, w, o, M, u, one, partial, f8p, false, st);
   return debug_end(st, hip_status(e));
 }
 
@@ -761,8 +758,8 @@ mla_status decode_steps(const mla_config *cfg, const mla_weights *w, const void 
   hipError_t e;
 
   const bool fp8 = cache_fp8(cfg);
-  const Fp8Act f8 = {(unsigned char *)(ws + p.x8), (unsigned char *)(ws + p.xs), (long)fp8_scale_ld(M)};
-  const Fp8Act *f8p = weights_fp8(cfg) ? &f8 : nullptr;
+  const Fp8Out f8 = {(unsigned char *)(ws + p.x8), (unsigned char *)(ws + p.xs), (long)fp8_scale_ld(M)};
+  const Fp8Out *f8p = weights_fp8(cfg) ? &f8 : nullptr;
   e = run_compress(cfg, w, h, M, rows, cache, batch, true, ws + p.c_q, fp8 ? ws + p.ckv : nullptr,
                    fp8 ? ws + p.kr : nullptr, p.sk1, partial, f8p, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
@@ -823,8 +820,13 @@ mla_status decode_steps(const mla_config *cfg, const mla_weights *w, const void 
   d.o_lat = ws + p.o_lat;
   e = launch_decode_attn(dt == MLA_BF16, d, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
-  e = dt == MLA_BF16 ? launch_decode_combine_uv(d, cfg->d_v, w->w_uv, o, st) : hipErrorNotSupported;
+  // with FP8 projections the combine also writes o's quantised form (when
+  // its group of 128 columns is one head: d_v = 128)
+  const bool o8 = f8p && cfg->d_v == 128;
+  e = dt == MLA_BF16 ? launch_decode_combine_uv(d, cfg->d_v, w->w_uv, o, o8 ? f8 : Fp8Out{nullptr, nullptr, 0}, st)
+                     : hipErrorNotSupported;
   if (e != hipSuccess && e != hipErrorNotSupported) return MLA_ERR_HIP;
+  const bool o_ready = o8 && e == hipSuccess;
   if (e == hipErrorNotSupported) {   // nothing was launched
     e = launch_decode_combine(dt == MLA_BF16, d, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
@@ -845,7 +847,7 @@ mla_status decode_steps(const mla_config *cfg, const mla_weights *w, const void 
     e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 1, 0, a, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
   }
-  e = run_output(cfg, w, o, M, u, p.sk5, partial, f8p, st);
+  e = run_output(cfg, w, o, M, u, p.sk5, partial, f8p, o_ready, st);
   return hip_status(e);
 }
 

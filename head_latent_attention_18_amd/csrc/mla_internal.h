@@ -441,7 +441,16 @@ hipError_t launch_decode_attn(int dtype, const DecodeArgs &a, hipStream_t st);
 hipError_t launch_decode_combine(int dtype, const DecodeArgs &a, hipStream_t st);
 // bf16 split combine fused with o = W_UV o_lat (hipErrorNotSupported outside
 // d_c = 512, d_R = 64, d_v = 128: then combine and un-absorb run separately)
-hipError_t launch_decode_combine_uv(const DecodeArgs &a, int d_v, const void *w_uv, void *o, hipStream_t st);
+// The quantised copy of an activation that feeds an FP8 projection: E4M3
+// codes [T][K] and the scales' biased exponents [K/128][ld_s]; codes ==
+// nullptr: none.
+struct Fp8Out {
+  unsigned char *codes, *scales;
+  long ld_s;
+};
+// q8: also write o in that form (the W_O input of the FP8 projections)
+hipError_t launch_decode_combine_uv(const DecodeArgs &a, int d_v, const void *w_uv, void *o, Fp8Out q8,
+                                    hipStream_t st);
 
 // FP8 cache append: token m's c_KV (ckv[m][0:d_c], bf16) and RoPE key
 // (kr[m][0:d_rope], bf16) are quantised (a scale per 128 columns) and written
