@@ -404,6 +404,14 @@ struct DecodeQArgs {
 bool decode_q_supported(int d_cq, int d_nope, int d_rope, int d_c, int T);
 hipError_t launch_decode_q(const DecodeQArgs &a, hipStream_t st);
 
+// The quantised copy of an activation that feeds an FP8 projection: E4M3
+// codes [T][K] and the scales' biased exponents [K/128][ld_s]; codes ==
+// nullptr: none.
+struct Fp8Out {
+  unsigned char *codes, *scales;
+  long ld_s;
+};
+
 struct FlashArgs {
   const void *q;    // [B*L][n_h][d_nope + d_rope] (q_C, then roped q_R)
   const void *k;    // [B*L][n_h][d_nope]
@@ -441,13 +449,6 @@ hipError_t launch_decode_attn(int dtype, const DecodeArgs &a, hipStream_t st);
 hipError_t launch_decode_combine(int dtype, const DecodeArgs &a, hipStream_t st);
 // bf16 split combine fused with o = W_UV o_lat (hipErrorNotSupported outside
 // d_c = 512, d_R = 64, d_v = 128: then combine and un-absorb run separately)
-// The quantised copy of an activation that feeds an FP8 projection: E4M3
-// codes [T][K] and the scales' biased exponents [K/128][ld_s]; codes ==
-// nullptr: none.
-struct Fp8Out {
-  unsigned char *codes, *scales;
-  long ld_s;
-};
 // q8: also write o in that form (the W_O input of the FP8 projections)
 hipError_t launch_decode_combine_uv(const DecodeArgs &a, int d_v, const void *w_uv, void *o, Fp8Out q8,
                                     hipStream_t st);
