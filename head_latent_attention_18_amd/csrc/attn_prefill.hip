@@ -359,7 +359,8 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_m32_kernel(FlashArgs
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lc = lane & 31, hh = lane >> 5;
   const int L = a.L, NH = a.n_h;
-  const int qtiles = (L + BQ - 1) / BQ;
+  const int Lq = a.lens ? a.Lq : L;   // queries per sequence
+  const int qtiles = (Lq + BQ - 1) / BQ;
 
   int bid = blockIdx.x, h, b, qt_rev;
   if ((NH & 7) == 0) {
@@ -377,18 +378,22 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_m32_kernel(FlashArgs
     qt_rev = rest / a.B;
   }
   const int qt = qtiles - 1 - qt_rev;
-  const long tok0 = (long)b * L;
+  const long tok0 = (long)b * L;      // first key row of the sequence
+  const long tok0q = (long)b * Lq;    // first query row
   const long ntok = (long)a.B * L;
-  const int q0 = qt * BQ + wave * 32;
-  const int qpos = q0 + lc;
-  const int wave_qmax = min(q0 + 31, L - 1);
-  const int blk_qmax = min(qt * BQ + BQ - 1, L - 1);
+  // position of query 0: after a prefix of lens[b] - Lq keys (lens clamped
+  // into [Lq, L], so that no access leaves the sequence's rows)
+  const int pos0 = a.lens ? min(max(a.lens[b], Lq), L) - Lq : 0;
+  const int q0 = qt * BQ + wave * 32;                         // query index
+  const int qpos = pos0 + q0 + lc;                            // its position
+  const int wave_qmax = pos0 + min(q0 + 31, Lq - 1);
+  const int blk_qmax = pos0 + min(qt * BQ + BQ - 1, Lq - 1);
   const float sl2 = a.scale_log2;
 
   // Q^T fragments with the softmax scale (in log2 units) folded in
   bf16x8 qf[QS];
   {
-    const bf16 *qrow = (const bf16 *)a.q + ((tok0 + min(qpos, L - 1)) * NH + h) * (DN + DR) + hh * 8;
+    const bf16 *qrow = (const bf16 *)a.q + ((tok0q + min(q0 + lc, Lq - 1)) * NH + h) * (DN + DR) + hh * 8;
 #pragma unroll
     for (int s = 0; s < QS; ++s) {
       const bf16x8 x = *(const bf16x8 *)(qrow + s * 16);
@@ -499,7 +504,7 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_m32_kernel(FlashArgs
     __builtin_amdgcn_sched_barrier(0);
 
     // sacc[kb][4j + i] is key kvb + 32kb + 16(j/2) + 8h + 4(j%2) + i
-    if (kvb + KVT - 1 > q0) {
+    if (kvb + KVT - 1 > pos0 + q0) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -618,9 +623,9 @@ __global__ __launch_bounds__(64 * NW, 1) void flash_prefill_m32_kernel(FlashArgs
   }
 
   const float l = lrun + __shfl_xor(lrun, 32);
-  if (qpos < L) {
+  if (q0 + lc < Lq) {
     const float inv = 1.f / l;
-    bf16 *orow = (bf16 *)a.o + ((tok0 + qpos) * NH + h) * DV;
+    bf16 *orow = (bf16 *)a.o + ((tok0q + q0 + lc) * NH + h) * DV;
 #pragma unroll
     for (int db = 0; db < DVB; ++db)
 #pragma unroll
@@ -645,11 +650,61 @@ static hipError_t launch_fp(const FlashArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// A cached prefix as dense rows for the up-projections and the flash kernel:
+// rows 0..Lpad-1 of every sequence, c_KV into ckv [B*Lpad][d_c] and k_R into
+// kr [B*Lpad][d_rope] (bf16).  Rows at or past the sequence's length
+// (clamped to the cache's capacity) are zero, so that the keys the flash
+// kernel masks out still hold finite values.  One wave per row.
+__global__ __launch_bounds__(256) void prefix_gather_kernel(CacheRef c, const int *lens, int B, int Lpad, int d_c,
+                                                            int d_rope, bf16 *ckv, bf16 *kr) {
+  const int lane = threadIdx.x & 63;
+  const long g = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nr = Lpad;
+  if (g >= (long)B * nr) return;
+  const int b = (int)(g / nr), r = (int)(g - (long)b * nr);
+  const int len = (int)min((long)max(lens[b], 0), min((long)Lpad, c.cap));
+  const int nch = d_c / 8, rch = d_rope / 8;   // 16-byte chunks
+  bf16 *dc = ckv + g * d_c, *dr = kr + g * d_rope;
+  if (r < len) {
+    const bf16 *row = (const bf16 *)c.pool + cache_row(c, b, r) * c.d_row;
+    for (int i = lane; i < nch + rch; i += 64) {
+      const bf16x8 v = *(const bf16x8 *)(row + 8 * i);
+      if (i < nch) *(bf16x8 *)(dc + 8 * i) = v;
+      else *(bf16x8 *)(dr + 8 * (i - nch)) = v;
+    }
+  } else {
+    const bf16x8 z = {};
+    for (int i = lane; i < nch + rch; i += 64) {
+      if (i < nch) *(bf16x8 *)(dc + 8 * i) = z;
+      else *(bf16x8 *)(dr + 8 * (i - nch)) = z;
+    }
+  }
+}
+
+hipError_t launch_prefix_gather(const CacheRef &c, const int *lens, int B, int Lpad, int d_c, int d_rope, void *ckv,
+                                void *kr, hipStream_t st) {
+  if (c.fp8 || d_c % 8 || d_rope % 8) return hipErrorNotSupported;
+  const long rows = (long)B * Lpad;
+  if ((rows + 3) / 4 > 0x7fffffffL) return hipErrorInvalidValue;
+  timing_before("prefix_gather", st);
+  hipLaunchKernelGGL(prefix_gather_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, c, lens, B, Lpad, d_c,
+                     d_rope, (bf16 *)ckv, (bf16 *)kr);
+  timing_after("prefix_gather", st);
+  return hipGetLastError();
+}
+
+bool flash_prefix_supported(int dtype, int d_nope, int d_rope, int d_v) {
+  return dtype == 1 && d_nope == 128 && d_rope == 64 && d_v == 128;
+}
+
 hipError_t launch_flash_prefill(int dtype, const FlashArgs &a, hipStream_t st) {
-  if (dtype == 1 && a.d_nope == 128 && a.d_rope == 64 && a.d_v == 128 && a.L % 8 == 0 && a.L >= 8 &&
-      (long)a.B * a.L * 2 * 128 < (1L << 31) && (long)a.n_h * 128 * 64 * 2 < (1L << 31)) {
+  const bool m32 = dtype == 1 && a.d_nope == 128 && a.d_rope == 64 && a.d_v == 128 && a.L % 8 == 0 && a.L >= 8 &&
+                   (long)a.B * a.L * 2 * 128 < (1L << 31) && (long)a.n_h * 128 * 64 * 2 < (1L << 31);
+  // queries after a prefix: the 32x32 kernel only
+  if (a.lens && (!m32 || a.Lq < 1 || a.Lq > a.L)) return hipErrorNotSupported;
+  if (m32) {
     constexpr int NW = 8;
-    const int qtiles = (a.L + 32 * NW - 1) / (32 * NW);
+    const int qtiles = ((a.lens ? a.Lq : a.L) + 32 * NW - 1) / (32 * NW);
     const long grid = (long)qtiles * a.B * a.n_h;
     timing_before("flash_prefill", st);
     hipLaunchKernelGGL((flash_prefill_m32_kernel<NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st, a);

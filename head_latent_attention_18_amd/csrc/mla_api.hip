@@ -206,15 +206,35 @@ struct DecodePlan {
   int W, slots, row_groups, rows;
   SplitK sk1, sk2, sk5;
   size_t c_q, q_nope, q_abs, o_part, lse, o_lat, o, ckv, kr, x8, xs, partial, total;
+  // many new tokens per sequence (a chunk after a cached prefix): the
+  // up-projected form, the prefix gathered into Lpad dense rows per sequence
+  bool flash;
+  int Lpad;
+  size_t qf, ckvd, krd, kf, vtf;
 };
+
+// New tokens per sequence from which decode takes the up-projected (flash)
+// form: its flops per cached row, 2*n_h*d_c*(d_nope + d_v) for the
+// up-projections plus 2*n_q*n_h*(d_nope + d_rope + d_v) for the attention,
+// fall below the absorbed form's 2*n_q*n_h*(2 d_c + d_rope) from about 170
+// tokens on (DeepSeek-V3 widths), and its kernels run faster.
+const int kFlashMinNq = 256;
+// ... while its dense keys and values stay within 4 GiB
+const int64_t kFlashMaxKvBytes = 1LL << 32;
 // The attention's split plan: W workgroups per row group (one wave of
 // workgroups over the CUs), each taking an equal share of the batch's cached
 // tiles (computed on the device from the lengths), and at most W + B partial
 // slots; neither depends on the lengths, so the workspace size does not.
-DecodePlan plan_decode(const mla_config *c, int32_t B, int32_t n_q, int32_t max_len) {
+DecodePlan plan_decode(const mla_config *c, int32_t B, int32_t n_q, int32_t max_len, bool allow_flash = true) {
   DecodePlan p;
   const int dt = c->dtype;
   const int64_t T = (int64_t)B * n_q;
+  const int64_t Lpad = ((int64_t)max_len + 63) / 64 * 64;
+  // bytes of K_C and V^T per dense row (each factor within 2^21, so no overflow)
+  const int64_t kv_row = (int64_t)c->n_heads * (c->d_nope + c->d_v) * 2;
+  p.flash = allow_flash && dt == MLA_BF16 && !cache_fp8(c) && n_q >= kFlashMinNq &&
+            flash_prefix_supported(1, c->d_nope, c->d_rope, c->d_v) && (int64_t)B * Lpad <= kFlashMaxKvBytes / kv_row;
+  p.Lpad = (int)Lpad;
   const int64_t R = (int64_t)n_q * c->n_heads;
   const int rows = decode_rows_per_group(dt == MLA_BF16 ? 1 : 0, B, R, kCUs);
   p.rows = rows;
@@ -230,13 +250,21 @@ DecodePlan plan_decode(const mla_config *c, int32_t B, int32_t n_q, int32_t max_
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off += align256(bytes); return at; };
   const int64_t D = c->d_c + c->d_rope;
+  const bool ab = !p.flash;   // the absorbed form's buffers
   p.c_q = take((size_t)T * c->d_cq * e);
-  p.q_nope = take((size_t)T * c->n_heads * c->d_nope * e);
-  p.q_abs = take((size_t)T * c->n_heads * D * e);
-  p.o_part = take((size_t)p.slots * R * c->d_c * e);
-  p.lse = take((size_t)p.slots * R * 4);
-  p.o_lat = take((size_t)T * c->n_heads * c->d_c * e);
+  p.q_nope = take(ab ? (size_t)T * c->n_heads * c->d_nope * e : 0);
+  p.q_abs = take(ab ? (size_t)T * c->n_heads * D * e : 0);
+  p.o_part = take(ab ? (size_t)p.slots * R * c->d_c * e : 0);
+  p.lse = take(ab ? (size_t)p.slots * R * 4 : 0);
+  p.o_lat = take(ab ? (size_t)T * c->n_heads * c->d_c * e : 0);
   p.o = take((size_t)T * c->n_heads * c->d_v * e);
+  // the up-projected form: q [T][n_h][d_nope + d_rope], the prefix's dense
+  // c_KV and k_R, K_C [B*Lpad][n_h][d_nope] and V^T [n_h*d_v][B*Lpad]
+  p.qf = take(p.flash ? (size_t)T * c->n_heads * (c->d_nope + c->d_rope) * e : 0);
+  p.ckvd = take(p.flash ? (size_t)B * Lpad * c->d_c * e : 0);
+  p.krd = take(p.flash ? (size_t)B * Lpad * c->d_rope * e : 0);
+  p.kf = take(p.flash ? (size_t)B * Lpad * c->n_heads * c->d_nope * e : 0);
+  p.vtf = take(p.flash ? (size_t)B * Lpad * c->n_heads * c->d_v * e : 0);
   // FP8 cache: the new tokens' c_KV and k_R before quantisation
   p.ckv = take(cache_fp8(c) ? (size_t)T * c->d_c * e : 0);
   p.kr = take(cache_fp8(c) ? (size_t)T * c->d_rope * e : 0);
@@ -700,6 +728,7 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
   }
   {
     FlashArgs f;
+    memset(&f, 0, sizeof(f));   // lens = nullptr: queries are positions 0..len-1
     f.q = ws + p.q;
     f.k = ws + p.k;
     f.kr = ws + p.kr;
@@ -727,7 +756,7 @@ namespace {
 // Validation shared by the decode entry points (no HIP call).
 mla_status check_decode(const mla_config *cfg, const mla_weights *w, const void *h, int32_t batch, int32_t n_q,
                         const int32_t *cache_lens, const int32_t *cache_lens_host, int32_t max_cache_len,
-                        const mla_cache *cache, const void *u, DecodePlan *plan) {
+                        const mla_cache *cache, const void *u, DecodePlan *plan, bool noalloc) {
   mla_status s = check_config(cfg);
   if (s != MLA_OK) return s;
   if ((s = check_weights(cfg, w)) != MLA_OK) return s;
@@ -741,6 +770,10 @@ mla_status check_decode(const mla_config *cfg, const mla_weights *w, const void 
   if ((s = check_cache(cache, batch, max_cache_len)) != MLA_OK) return s;
   if (cache_fp8(cfg) && cache->block_table && cache->block_size % 32) return MLA_ERR_UNSUPPORTED;
   *plan = plan_decode(cfg, batch, n_q, max_cache_len);
+  // the allocation-free decode keeps to its array: the absorbed form when
+  // the up-projected one would not fit
+  if (noalloc && plan->total > (size_t)MLA_NOALLOC_WORKSPACE_BYTES)
+    *plan = plan_decode(cfg, batch, n_q, max_cache_len, false);
   return MLA_OK;
 }
 
@@ -763,6 +796,62 @@ mla_status decode_steps(const mla_config *cfg, const mla_weights *w, const void 
   e = run_compress(cfg, w, h, M, rows, cache, batch, true, ws + p.c_q, fp8 ? ws + p.ckv : nullptr,
                    fp8 ? ws + p.kr : nullptr, p.sk1, partial, f8p, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
+  if (p.flash) {
+    // Many new tokens per sequence (a chunk after its cached prefix): the
+    // up-projected form of p5 section 2.1, as in prefill.  Queries with RoPE
+    // at their positions; every cached row (the chunk's own just appended)
+    // gathered densely and up-projected to K_C and V^T; the flash kernel
+    // with each sequence's queries after its prefix; then W_O.
+    const int DQK = cfg->d_nope + cfg->d_rope;
+    e = run_query(cfg, w, ws + p.c_q, M, rows, ws + p.qf, (long)NH * DQK, DQK, ws + p.qf, (long)NH * DQK, DQK,
+                  cfg->d_nope, p.sk2, partial, st);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    e = launch_prefix_gather(cache_ref(cfg, cache, batch), cache_lens, batch, p.Lpad, cfg->d_c, cfg->d_rope,
+                             ws + p.ckvd, ws + p.krd, st);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    const int MK = batch * p.Lpad;
+    {  // K_C = c_KV W_UK^T -> [B*Lpad][n_h][d_nope]
+      GemmArgs a = gemm_args(ws + p.ckvd, cfg->d_c, MK, NH * cfg->d_nope, cfg->d_c);
+      a.w[0] = w->w_uk;
+      a.w_end[0] = NH * cfg->d_nope;
+      a.ldw = cfg->d_c;
+      a.epi.seg[0] = seg_plain(NH * cfg->d_nope, ws + p.kf, (long)NH * cfg->d_nope);
+      a.epi.nseg = 1;
+      a.name = "k_up";
+      e = launch_gemm(1, gemm_tile_for(dt, MK, a.N, 1), 1, 0, a, st);
+      if (e != hipSuccess) return MLA_ERR_HIP;
+    }
+    {  // V^T = (c_KV W_UV^T)^T -> [n_h*d_v][B*Lpad]
+      GemmArgs a = gemm_args(ws + p.ckvd, cfg->d_c, MK, NH * cfg->d_v, cfg->d_c);
+      a.w[0] = w->w_uv;
+      a.w_end[0] = NH * cfg->d_v;
+      a.ldw = cfg->d_c;
+      a.epi.seg[0] = seg_plain(NH * cfg->d_v, ws + p.vtf, (long)MK);
+      a.epi.nseg = 1;
+      a.name = "v_up";
+      e = launch_gemm(1, gemm_tile_for(dt, MK, a.N, 1), 0, 0, a, st);
+      if (e != hipSuccess) return MLA_ERR_HIP;
+    }
+    FlashArgs f;
+    memset(&f, 0, sizeof(f));
+    f.q = ws + p.qf;
+    f.k = ws + p.kf;
+    f.kr = ws + p.krd;
+    f.vt = ws + p.vtf;
+    f.o = o;
+    f.B = batch;
+    f.L = p.Lpad;
+    f.n_h = NH;
+    f.d_nope = cfg->d_nope;
+    f.d_rope = cfg->d_rope;
+    f.d_v = cfg->d_v;
+    f.scale_log2 = softmax_scale_log2(cfg);
+    f.lens = cache_lens;
+    f.Lq = n_q;
+    e = launch_flash_prefill(1, f, st);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    return hip_status(run_output(cfg, w, o, M, u, p.sk5, partial, f8p, false, st));
+  }
   if (dt == MLA_BF16 && decode_q_supported(cfg->d_cq, cfg->d_nope, cfg->d_rope, cfg->d_c, M)) {
     // up-projection, RoPE and absorption in one launch
     const GemmArgs qa = query_args(cfg, w, ws + p.c_q, M, rows, ws + p.q_nope, (long)NH * cfg->d_nope, cfg->d_nope,
@@ -884,7 +973,7 @@ mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h
                       const mla_cache *cache, void *u, void *o_heads, void *workspace, size_t workspace_bytes,
                       void *stream) {
   DecodePlan p;
-  mla_status s = check_decode(cfg, w, h, batch, n_q, cache_lens, cache_lens_host, max_cache_len, cache, u, &p);
+  mla_status s = check_decode(cfg, w, h, batch, n_q, cache_lens, cache_lens_host, max_cache_len, cache, u, &p, false);
   if (s != MLA_OK) return s;
   if (!workspace) return MLA_ERR_WORKSPACE;
   if (workspace_bytes < p.total) return MLA_ERR_WORKSPACE;
@@ -897,7 +986,7 @@ mla_status mla_decode_noalloc(const mla_config *cfg, const mla_weights *w, const
                               const int32_t *cache_lens, const int32_t *cache_lens_host, int32_t max_cache_len,
                               const mla_cache *cache, void *u, void *o_heads, void *stream) {
   DecodePlan p;
-  mla_status s = check_decode(cfg, w, h, batch, n_q, cache_lens, cache_lens_host, max_cache_len, cache, u, &p);
+  mla_status s = check_decode(cfg, w, h, batch, n_q, cache_lens, cache_lens_host, max_cache_len, cache, u, &p, true);
   if (s != MLA_OK) return s;
   if (p.total > (size_t)MLA_NOALLOC_WORKSPACE_BYTES) return MLA_ERR_WORKSPACE;
   char *ws = nullptr;

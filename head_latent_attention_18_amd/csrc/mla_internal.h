@@ -413,15 +413,27 @@ struct Fp8Out {
 };
 
 struct FlashArgs {
-  const void *q;    // [B*L][n_h][d_nope + d_rope] (q_C, then roped q_R)
+  const void *q;    // [B*Lq][n_h][d_nope + d_rope] (q_C, then roped q_R)
   const void *k;    // [B*L][n_h][d_nope]
   const void *kr;   // [B*L][d_rope]
   const void *vt;   // [n_h*d_v][B*L]
-  void *o;          // [B*L][n_h][d_v]
+  void *o;          // [B*Lq][n_h][d_v]
   int B, L, n_h, d_nope, d_rope, d_v;
   float scale_log2;  // softmax scale * log2(e)
+  // Queries after a cached prefix (lens != nullptr): sequence b holds
+  // lens[b] keys (rows b*L ..), and its Lq queries are its last Lq
+  // positions, lens[b]-Lq .. lens[b]-1.  lens == nullptr: Lq = L and the
+  // queries are positions 0..L-1 (plain prefill).
+  const int *lens;
+  int Lq;
 };
 hipError_t launch_flash_prefill(int dtype, const FlashArgs &a, hipStream_t st);
+// the widths the queries-after-a-prefix form runs at (bf16 128/64/128)
+bool flash_prefix_supported(int dtype, int d_nope, int d_rope, int d_v);
+// rows 0..Lpad-1 of every sequence's cache (bf16 layout) as dense c_KV
+// [B*Lpad][d_c] and k_R [B*Lpad][d_rope], zero past each length
+hipError_t launch_prefix_gather(const CacheRef &c, const int *lens, int B, int Lpad, int d_c, int d_rope, void *ckv,
+                                void *kr, hipStream_t st);
 
 struct DecodeArgs {
   const void *q;      // absorbed queries [B*n_q][n_h][d_c + d_rope]

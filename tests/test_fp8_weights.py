@@ -20,8 +20,10 @@ pytestmark = pytest.mark.gpu
 
 
 # B * n_q tokens: 4 and 6 (16-row blocks), 20 (32), 64 (64), 128 (128 rows),
-# 132 (the 256x256 tiles with a partial tile)
-@pytest.mark.parametrize("B,L,nq", [(4, 300, 1), (3, 97, 2), (20, 50, 1), (64, 40, 1), (128, 20, 1), (33, 70, 4)])
+# 132 (the 256x256 tiles with a partial tile), 600 (a 300-token chunk per
+# sequence: the up-projected form)
+@pytest.mark.parametrize("B,L,nq", [(4, 300, 1), (3, 97, 2), (20, 50, 1), (64, 40, 1), (128, 20, 1), (33, 70, 4),
+                                    (2, 700, 300)])
 def test_fp8w_decode(B, L, nq):
     wl = make_workload(2, batch=B, uniform_len=L, n_q=nq, weights_fp8=True)
     layer = layer_for(wl)

@@ -137,15 +137,17 @@ def test_compress_kv_entry_point(wid):
     assert_close(got, np.concatenate([c_kv, k_r], axis=1), wl.bf16, "compressed rows")
 
 
-@pytest.mark.parametrize("P,C", [((96, 60), 40), ((200, 333), 300), ((500,), 300)])
+@pytest.mark.parametrize("P,C", [((96, 60), 40), ((200, 333), 300), ((500,), 300), ((1000, 37), 256)])
 def test_chunked_prefill_over_ragged_paged_cache(P, C):
     """A chunk of new tokens per sequence against a cached prefix of a
     different length per sequence (split-phase serving: the prefix rows
     written by mla_compress_kv into a permuted paged cache, the chunk by
     mla_decode with n_q = chunk, causal among its tokens) gives the rows of
-    one longer prefill of each sequence.  Chunks of 300 tokens take the
-    projection kernels of a few hundred rows (32x64 tiles, with the cache
-    append in their epilogue) and many query row groups per sequence."""
+    one longer prefill of each sequence.  Chunks of 40 tokens take the
+    absorbed form; chunks of 256 and more the up-projected one (the cached
+    rows gathered and up-projected, the flash kernel with each sequence's
+    queries after its own prefix), 300 also the projection kernels of a few
+    hundred rows (32x64 tiles, with the cache append in their epilogue)."""
     bs = 64
     B = len(P)
     L = max(P) + C
