@@ -390,6 +390,16 @@ static hipError_t launch_t(GemmArgs &a, hipStream_t st, const char *name) {
   return e;
 }
 
+// the ordered split-K reduce for the 256x256 kernel's splits (bf16 outputs)
+hipError_t launch_splitk_reduce_bf16(GemmArgs &a, hipStream_t st) {
+  const long total = (long)a.batch * a.M * (a.N / 4);
+  const char *rname = a.reduce_name ? a.reduce_name : "splitk_reduce";
+  timing_before(rname, st);
+  hipLaunchKernelGGL(splitk_reduce_kernel<bf16>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a);
+  timing_after(rname, st);
+  return hipGetLastError();
+}
+
 template <int MB, int BK, int NST>
 static void launch_skinny_nst(GemmArgs &a, hipStream_t st, dim3 grid) {
   hipLaunchKernelGGL((gemm_skinny_kernel<MB, BK, NST>), grid, dim3(256), 0, st, a);
@@ -448,6 +458,9 @@ int gemm_bm(int dtype, int tile) {
 #define BIG_WN 4
 #endif
 hipError_t launch_gemm(int dtype, int tile, int swap, int wkn, GemmArgs &a, hipStream_t st) {
+  // split-K partials [batch][splits][M][N] must fit the buffer given
+  if (a.splits > 1 && (!a.partial || a.partial_bytes < (size_t)a.batch * a.splits * a.M * a.N * sizeof(float)))
+    return hipErrorInvalidValue;
   if (a.fp8) {
     // block-scaled FP8: up to 128 tokens stream the weights, more take the
     // 256x256 tiles

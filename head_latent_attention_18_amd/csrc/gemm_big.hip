@@ -19,6 +19,8 @@
 //     outputs leave by streaming (non-temporal) stores of whole rows, since
 //     the next kernel reads them from other XCDs (measured 5-10 us faster
 //     per prefill than write-allocating stores);
+//   * few tiles (a few hundred tokens against a wide weight): split-K over
+//     blockIdx.y, each split writing its fp32 sums for the ordered reduce;
 //   * block-scaled FP8 (F8): E4M3 operands, a slab row is the same 128 bytes
 //     (128 k instead of 64), each 64-wide k step a scaled 32x32x64 MFMA
 //     taking the weight block's power-of-two scale (uniform over a wave's
@@ -110,12 +112,13 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
   const int tn = (group / groups_m) * G + ti / G;
   if (tm >= a.tiles_m || tn >= a.tiles_n) return;
   const int m0 = tm * GBM, n0 = tn * GBN;
+  const int split = blockIdx.y, kofs = split * a.k_chunk;   // this split's k range
 
   int seg = 0, beg = 0;
   while (seg < a.nw - 1 && n0 >= a.w_end[seg]) { beg = a.w_end[seg]; ++seg; }
-  const char *wsrc = (const char *)a.w[seg] + (long)(n0 - beg) * a.ldw * ESZ;
+  const char *wsrc = (const char *)a.w[seg] + ((long)(n0 - beg) * a.ldw + kofs) * ESZ;
   const int wrows = min(GBN, a.w_end[seg] - n0);
-  const char *xsrc = (const char *)a.x + (long)m0 * a.ldx * ESZ;
+  const char *xsrc = (const char *)a.x + ((long)m0 * a.ldx + kofs) * ESZ;
   const int xrows = min(GBM, a.M - m0);
   const unsigned lring = (unsigned)(size_t)(lds_void *)ring;
 
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][i], xf[buf][j], acc[i][j], 0, 0, 0);
   };
 
-  const int nkt = a.K / SK;
+  const int nkt = a.k_chunk / SK;
   if constexpr (F8) {
     // fragments of the two 64-wide k steps of a slab: lane group fh holds
     // logical chunks 4s + 2fh and 4s + 2fh + 1 of its row (both operands
@@ -197,8 +200,8 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
     // (a wave past the segment's last row reads the last block's scales;
     // its rows are never stored)
     const int wblk = min((n0 - beg + wn * 64) >> 7, (a.w_end[seg] - beg - 1) >> 7);
-    const float *wsp = a.wsc[seg] + (long)wblk * a.wsc_ld;
-    const unsigned char *xsp = a.xs + m0 + wm * 128 + fr;
+    const float *wsp = a.wsc[seg] + (long)wblk * a.wsc_ld + kofs / 128;
+    const unsigned char *xsp = a.xs + (long)(kofs / 128) * a.xs_ld + m0 + wm * 128 + fr;
     int sx[4], sxn[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) sxn[j] = xsp[j * 32];
@@ -288,7 +291,14 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
       const int f = (tid % (GBN / 4)) * 4, n = n0 + f;
       constexpr int TS = GNT / (GBN / 4), IT = 128 / TS;   // rows between a thread's items, items
       const int t0 = tid / (GBN / 4);
-      if (n < a.N) {
+      if (a.splits > 1) {
+        // this split's fp32 sums, [split][M][N] (the reduce adds the splits
+        // in order and runs the epilogue)
+        if (n < a.N)
+          for (int t = t0; t < 128; t += TS)
+            if (mh + t < a.M)
+              *(f32x4 *)(a.partial + ((long)split * a.M + mh + t) * a.N + n) = *(const lds_f32x4 *)(ep + t * EPI_LD + f);
+      } else if (n < a.N) {
         const ColPlan cp = col_plan(a.epi, n);
         if (cp.kind != SEG_CACHE && !cp.dst2 && !cp.out_f32 && (!cp.rope || a.epi.rows.mode == ROWS_DENSE)) {
           // Plain and head-layout columns: all items are formed first and
@@ -382,6 +392,8 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
   }
 }
 
+hipError_t launch_splitk_reduce_bf16(GemmArgs &a, hipStream_t st);
+
 bool gemm_big_ok(const GemmArgs &a) {
   // bf16 from 256 tokens on; FP8 products of more than 128 tokens all come
   // here (fewer stream), the tile's surplus rows clamped and not stored
@@ -391,6 +403,10 @@ bool gemm_big_ok(const GemmArgs &a) {
     if (a.w_end[s] % GBN != 0) return false;   // a tile never straddles two weight segments
   // 32-bit lane offsets
   const int esz = a.fp8 ? 1 : 2;
+  // split-K: whole slabs per split, fp32 partials, row-major outputs only
+  if (a.splits > 1 && (a.k_chunk % (2 * GBK) != 0 || (long)a.splits * a.k_chunk != a.K || !a.partial || a.N % 4 ||
+                       a.partial_bytes < (size_t)a.splits * a.M * a.N * sizeof(float)))
+    return false;
   if ((long)GBM * a.ldx * esz >= (1L << 31) || (long)GBN * a.ldw * esz >= (1L << 31)) return false;
   return true;
 }
@@ -406,17 +422,21 @@ hipError_t launch_gemm_big(GemmArgs &a, int swap, hipStream_t st) {
   a.grouped = G;
   const int grid = ((groups + 7) / 8) * 8 * G * G;
   const char *name = a.name ? a.name : "gemm_big";
+  if (a.splits > 1 && !swap) return hipErrorNotSupported;
+  const dim3 g3(grid, a.splits);
   timing_before(name, st);
   if (a.fp8) {
     if (!swap) return hipErrorNotSupported;
-    hipLaunchKernelGGL((gemm_big_kernel<true, true>), dim3(grid), dim3(GNT), 0, st, a);
+    hipLaunchKernelGGL((gemm_big_kernel<true, true>), g3, dim3(GNT), 0, st, a);
   } else if (swap) {
-    hipLaunchKernelGGL((gemm_big_kernel<true, false>), dim3(grid), dim3(GNT), 0, st, a);
+    hipLaunchKernelGGL((gemm_big_kernel<true, false>), g3, dim3(GNT), 0, st, a);
   } else {
-    hipLaunchKernelGGL((gemm_big_kernel<false, false>), dim3(grid), dim3(GNT), 0, st, a);
+    hipLaunchKernelGGL((gemm_big_kernel<false, false>), g3, dim3(GNT), 0, st, a);
   }
   timing_after(name, st);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits <= 1) return e;
+  return launch_splitk_reduce_bf16(a, st);
 }
 
 }  // namespace mla

@@ -317,6 +317,7 @@ bool gemm_stream_ok(const GemmArgs &a, int wkn) {
   if (wkn || (!a.fp8 && a.M <= 32 && a.K < 4096)) return false;
   const int bk = stream_bk_for(a.M) * (a.fp8 ? 2 : 1);
   if (a.M > 128 || a.K % bk != 0 || !a.partial) return false;
+  if (a.partial_bytes < gemm_stream_partial_bytes(a.M)) return false;   // the partials' layout must fit
   const long units = (long)a.batch * ((a.N + SBN - 1) / SBN) * (a.K / bk);
   if (units * gemm_stream_grid() >= (1L << 31)) return false;
   // a tile is shared by at most MAX_PARTS workgroups

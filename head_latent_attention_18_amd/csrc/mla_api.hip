@@ -130,9 +130,12 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // ---------------------------------------------------------------------------
 // Workspace plans
 // ---------------------------------------------------------------------------
+struct SplitK { int splits, k_chunk; };
 struct PrefillPlan {
   size_t c_q, ckv, kr, q, k, vt, o, x8, xs, partial, total;
+  SplitK sko;   // W_O's split over k
 };
+SplitK choose_splitk(int dtype, int64_t M, int64_t N, int64_t K, int batch);
 PrefillPlan plan_prefill(const mla_config *c, int64_t T) {
   const size_t e = esize(c);
   PrefillPlan p;
@@ -150,12 +153,16 @@ PrefillPlan plan_prefill(const mla_config *c, int64_t T) {
   const bool f8 = weights_fp8(c);
   p.x8 = take(f8 ? (size_t)T * fp8_act_width(c) : 0);
   p.xs = take(f8 ? (size_t)(fp8_act_width(c) / 128) * fp8_scale_ld(T) : 0);
-  p.partial = take(f8 && T <= 128 ? gemm_stream_partial_bytes((int)T) : 0);
+  // W_O split over k (few 256x256 tiles): fp32 partials [splits][T][d_model]
+  p.sko = choose_splitk(c->dtype, T, c->d_model, (int64_t)c->n_heads * c->d_v, 1);
+  size_t part = p.sko.splits > 1 ? (size_t)p.sko.splits * T * c->d_model * 4 : 0;
+  // a partial buffer lets products of up to 128 tokens stream (they need
+  // the streaming kernel's layout); FP8 products of that size always do
+  if ((part || f8) && T <= 128 && c->dtype == MLA_BF16) part = std::max(part, gemm_stream_partial_bytes((int)T));
+  p.partial = take(part);
   p.total = off;
   return p;
 }
-
-struct SplitK { int splits, k_chunk; };
 
 // 256x256 tiles (bf16) unless they would leave all but a few CUs idle: a
 // few hundred tokens against a narrow weight (a 512-token chunk: 18 tiles for
@@ -175,7 +182,22 @@ SplitK choose_splitk(int dtype, int64_t M, int64_t N, int64_t K, int batch) {
   r.splits = 1;
   r.k_chunk = (int)K;
   const int tile = gemm_tile_for(dtype, M, N, batch);
-  if (tile != TILE_SKINNY) return r;
+  if (tile != TILE_SKINNY) {
+    // 256x256 tiles filling at most half the CUs (a few hundred tokens
+    // against a wide weight): split k so that about one wave of workgroups
+    // runs, at least 1024 k per split, then the ordered reduce
+    if (dtype == MLA_BF16 && batch == 1) {
+      const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+      if (tiles <= kCUs / 2)
+        for (int s = 8; s >= 2; --s)
+          if (s * tiles <= kCUs && K % (128 * s) == 0 && K / s >= 1024) {
+            r.splits = s;
+            r.k_chunk = (int)(K / s);
+            break;
+          }
+    }
+    return r;
+  }
   int bk, bn;
   if (dtype == MLA_BF16 && M <= 128) {
     bk = M <= 64 ? 256 : 128;
@@ -402,6 +424,12 @@ GemmArgs gemm_args(const void *x, long ldx, int M, int N, int K) {
 
 mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+// A partial-sum buffer of the workspace and its size in bytes.
+struct Part {
+  float *p;
+  size_t bytes;
+};
+
 // Quantise x [M][K] (bf16, row stride K) into f, unless its producer already
 // wrote it there, and point the product's activation operand at it; the
 // weights are E4M3 with the scales wsc.
@@ -416,8 +444,6 @@ hipError_t fp8_operands(const Fp8Out &f, const void *x, int M, int K, GemmArgs &
   a.xs = f.scales;
   a.xs_ld = f.ld_s;
   a.wsc_ld = K / 128;
-  a.splits = 1;
-  a.k_chunk = K;
   return hipSuccess;
 }
 
@@ -425,7 +451,7 @@ hipError_t fp8_operands(const Fp8Out &f, const void *x, int M, int K, GemmArgs &
 // with_q = false drops the W_DQ segment (plain cache compression).
 hipError_t run_compress(const mla_config *c, const mla_weights *w, const void *h, int M, RowMap rows,
                         const mla_cache *cache, int32_t batch, bool with_q, void *c_q, void *ckv_mirror, void *kr_mirror,
-                        SplitK sk, float *partial, const Fp8Out *f8, hipStream_t st) {
+                        SplitK sk, Part partial, const Fp8Out *f8, hipStream_t st) {
   const int dt = c->dtype;
   const int N = (with_q ? c->d_cq : 0) + c->d_c + c->d_rope;
   GemmArgs a = gemm_args(h, c->d_model, M, N, c->d_model);
@@ -471,7 +497,8 @@ hipError_t run_compress(const mla_config *c, const mla_weights *w, const void *h
   fill_inv_freq(c, a.epi);
   a.splits = sk.splits;
   a.k_chunk = sk.k_chunk;
-  a.partial = partial;
+  a.partial = partial.p;
+  a.partial_bytes = partial.bytes;
   a.name = with_q ? "q_kv_down" : "kv_compress";
   a.reduce_name = "q_kv_down.reduce";
   if (f8) {
@@ -499,7 +526,7 @@ hipError_t run_compress(const mla_config *c, const mla_weights *w, const void *h
 // (qc, qc_ld, qc_head_ld, 0) and the rope part to (qr, qr_ld, qr_head_ld, qr_off).
 GemmArgs query_args(const mla_config *c, const mla_weights *w, const void *c_q, int M, RowMap rows,
                     void *qc, long qc_ld, long qc_head_ld, void *qr, long qr_ld, long qr_head_ld, int qr_off,
-                    SplitK sk, float *partial) {
+                    SplitK sk, Part partial) {
   const int dt = c->dtype;
   const int Nc = c->n_heads * c->d_nope, N = Nc + c->n_heads * c->d_rope;
   GemmArgs a = gemm_args(c_q, c->d_cq, M, N, c->d_cq);
@@ -526,7 +553,8 @@ GemmArgs query_args(const mla_config *c, const mla_weights *w, const void *c_q, 
   fill_inv_freq(c, a.epi);
   a.splits = sk.splits;
   a.k_chunk = sk.k_chunk;
-  a.partial = partial;
+  a.partial = partial.p;
+  a.partial_bytes = partial.bytes;
   a.name = "q_up";
   a.reduce_name = "q_up.reduce";
   return a;
@@ -534,7 +562,7 @@ GemmArgs query_args(const mla_config *c, const mla_weights *w, const void *c_q, 
 
 hipError_t run_query(const mla_config *c, const mla_weights *w, const void *c_q, int M, RowMap rows,
                      void *qc, long qc_ld, long qc_head_ld, void *qr, long qr_ld, long qr_head_ld, int qr_off,
-                     SplitK sk, float *partial, hipStream_t st) {
+                     SplitK sk, Part partial, hipStream_t st) {
   GemmArgs a = query_args(c, w, c_q, M, rows, qc, qc_ld, qc_head_ld, qr, qr_ld, qr_head_ld, qr_off, sk, partial);
   return launch_gemm(c->dtype == MLA_BF16, gemm_tile_for(c->dtype, M, a.N, a.batch), 1, 0, a, st);
 }
@@ -542,7 +570,7 @@ hipError_t run_query(const mla_config *c, const mla_weights *w, const void *c_q,
 // u = o W_O^T
 // f8_ready: the attention already wrote o's quantised form into *f8
 hipError_t run_output(const mla_config *c, const mla_weights *w, const void *o, int M, void *u, SplitK sk,
-                      float *partial, const Fp8Out *f8, bool f8_ready, hipStream_t st) {
+                      Part partial, const Fp8Out *f8, bool f8_ready, hipStream_t st) {
   const int K = c->n_heads * c->d_v;
   GemmArgs a = gemm_args(o, K, M, c->d_model, K);
   a.w[0] = w->w_o;
@@ -552,7 +580,8 @@ hipError_t run_output(const mla_config *c, const mla_weights *w, const void *o, 
   a.epi.nseg = 1;
   a.splits = sk.splits;
   a.k_chunk = sk.k_chunk;
-  a.partial = partial;
+  a.partial = partial.p;
+  a.partial_bytes = partial.bytes;
   a.name = "o_proj";
   a.reduce_name = "o_proj.reduce";
   if (f8) {
@@ -663,7 +692,7 @@ mla_status mla_compress_kv(const mla_config *cfg, const mla_weights *w, const vo
   const hipStream_t st = (hipStream_t)stream;
   if ((s = debug_begin(st)) != MLA_OK) return s;
   return debug_end(st, hip_status(run_compress(cfg, w, h, n, rows, cache, batch, false, nullptr, nullptr, nullptr,
-                                               sk, nullptr, nullptr, st)));
+                                               sk, Part{nullptr, 0}, nullptr, st)));
 }
 
 mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *h, int32_t batch, int32_t len,
@@ -696,13 +725,15 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
 
   const Fp8Out f8 = {(unsigned char *)(ws + p.x8), (unsigned char *)(ws + p.xs), (long)fp8_scale_ld(T)};
   const Fp8Out *f8p = weights_fp8(cfg) ? &f8 : nullptr;
-  float *partial = weights_fp8(cfg) && T <= 128 ? (float *)(ws + p.partial) : nullptr;
+  // partial sums: the FP8 streaming kernel (up to 128 tokens) or W_O's split
+  const bool has_part = p.total > p.partial;
+  const Part partial = {has_part ? (float *)(ws + p.partial) : nullptr, p.total - p.partial};
   one.k_chunk = cfg->d_model;
   e = run_compress(cfg, w, h, M, rows, cache, batch, true, ws + p.c_q, ws + p.ckv, ws + p.kr, one, partial, f8p, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
   one.k_chunk = cfg->d_cq;
   e = run_query(cfg, w, ws + p.c_q, M, rows, ws + p.q, (long)NH * DQK, DQK, ws + p.q, (long)NH * DQK, DQK,
-                cfg->d_nope, one, nullptr, st);
+                cfg->d_nope, one, Part{nullptr, 0}, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
   {  // K_C = c_KV W_UK^T  -> [T][n_h][d_nope]
     GemmArgs a = gemm_args(ws + p.ckv, cfg->d_c, M, NH * cfg->d_nope, cfg->d_c);
@@ -744,8 +775,7 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
     e = launch_flash_prefill(dt == MLA_BF16, f, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
   }
-  one.k_chunk = NH * cfg->d_v;
-  e = run_output(cfg, w, o, M, u, one, partial, f8p, false, st);
+  e = run_output(cfg, w, o, M, u, p.sko, partial, f8p, false, st);
   return debug_end(st, hip_status(e));
 }
 
@@ -785,7 +815,7 @@ mla_status decode_steps(const mla_config *cfg, const mla_weights *w, const void 
   const int dt = cfg->dtype;
   const int M = batch * n_q;
   const int NH = cfg->n_heads, D = cfg->d_c + cfg->d_rope;
-  float *partial = (float *)(ws + p.partial);
+  const Part partial = {(float *)(ws + p.partial), p.total - p.partial};
   RowMap rows = {ROWS_DECODE, n_q, cache_lens, nullptr, nullptr};
   void *o = o_heads ? o_heads : (void *)(ws + p.o);
   hipError_t e;
@@ -883,7 +913,8 @@ mla_status decode_steps(const mla_config *cfg, const mla_weights *w, const void 
       sg.batch_stride = D;
       a.epi.seg[0] = sg;
       a.epi.nseg = 1;
-      a.partial = partial;
+      a.partial = partial.p;
+      a.partial_bytes = partial.bytes;
       a.name = "absorb";
       e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 1, 1, a, st);
       if (e != hipSuccess) return MLA_ERR_HIP;
@@ -931,7 +962,8 @@ mla_status decode_steps(const mla_config *cfg, const mla_weights *w, const void 
     sg.batch_stride = cfg->d_v;
     a.epi.seg[0] = sg;
     a.epi.nseg = 1;
-    a.partial = partial;
+    a.partial = partial.p;
+    a.partial_bytes = partial.bytes;
     a.name = "unabsorb";
     e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 1, 0, a, st);
     if (e != hipSuccess) return MLA_ERR_HIP;

@@ -360,6 +360,7 @@ struct GemmArgs {
   int splits, k_chunk;                          // split-K: K = splits * k_chunk
   int batch;
   float *partial;                               // splits > 1: [batch][splits][M][N]
+  size_t partial_bytes;                         // its size: launchers refuse a layout that does not fit
   int tiles_m, tiles_n;
   int grouped;               // 8x8 tile groups per XCD (set by the launcher)
   const char *name;          // timing labels (static strings)
