@@ -69,6 +69,28 @@ def test_full_prefill_len4096_sampled_rows():
                  "all cache rows")
 
 
+@pytest.mark.parametrize("fp8w", [False, True])
+def test_prefill_len4000_sampled_rows(fp8w):
+    """4000 tokens, bf16 and FP8 projections: every 256x256-tile product has
+    a partial last row of tiles (3840..3999) and the flash kernel a partial
+    last query block; rows of the first and last row tiles and random ones."""
+    wl = make_workload(3, seq_len=4000, weights_fp8=fp8w)
+    d = wl.dims
+    layer = layer_for(wl)
+    L = wl.seq_len
+    h = upload(wl.h_f32, wl.h_bits, True)
+    cache = layer.new_cache(1, L)
+    say(f"prefill len4000 fp8w={fp8w}")
+    u = layer.prefill(h, cache)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(78))
+    rows = sorted(set([0, 255, 256, 3839, 3840, 3841, 3998, 3999] + rng.integers(0, L, 8).tolist()))
+    with Timer("oracle prefill (sampled rows)"):
+        ref = O.prefill(d, weights64(wl), wl.h_f32[0].astype(np.float64), rows=rows, weights_fp8=fp8w)
+    sel = torch.tensor(rows, device="cuda")
+    assert_close(u[0].index_select(0, sel), ref["u"], True, "u sampled rows")
+
+
 def test_full_decode_ragged_paged_b128():
     """128 sequences, lengths uniform in [1, 32768], paged 64-row blocks in a
     permuted order: the shortest, the longest and random sequences in full."""
