@@ -407,7 +407,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_attn_kernel(DecodeArgs a) {
 // bf16 kernel for gfx950 (d_c = 512, d_R = 64), 64 query rows per
 // workgroup.  The cache tile goes HBM -> LDS with global_load_lds_dwordx4
 // (lane i's 16 bytes land at base + 16*i; no staging registers) into a ring
-// of four stages, two tiles ahead.  Per tile, two phases:
+// of four stages, three tiles ahead (two with an FP8 cache).  Per tile, two
+// phases:
 //   A (scores): S^T = C . Q^T against the 32 cached rows of the tile, from
 //     16-byte row reads of the stage; the softmax is lane-local (each lane
 //     holds the scores of one query row for four cached rows) plus cross-lane
@@ -502,7 +503,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
   constexpr int CH = D / 8;                          // 16-byte chunks per cached row
   constexpr int LOADS = KVT * CH / NC;               // copy instructions per copying wave per tile
   constexpr int STAGE = KVT * D;
-  constexpr int NS = 4;                              // ring stages (two tiles ahead)
+  constexpr int NS = 4;                              // ring stages
   constexpr int QS = D / 32;                         // 32-wide k steps of the scores
   constexpr int ROWS = 64;
   constexpr int DBW = DC / 4 / 16;                   // 16-column blocks per P.V wave
@@ -875,25 +876,58 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
     wait_lgkm0();                                      // FP8: this wave's writes of tile 0
     bar();                                             // B0
 
+    // bf16: the V^T fragments of tile i are read in iteration i, beside its
+    // scores, and multiplied in iteration i+1 (with P of tile i), so a stage
+    // is free one iteration after its tile arrives and the copies run three
+    // tiles ahead
+    bf16x8 va[DBW];
     for (int i = 0; i <= ntiles; ++i) {
-      // the copy of tile i+2 goes into the stage of tile i-2, whose last
-      // readers (this wave's P.V in iteration i-1) are past the barrier
-      // (FP8: tile i+1, loaded in iteration i-1, is converted into the stage
-      // of tile i-3, and the loads of tile i+2 go out)
+      // FP8: tile i+1, loaded in iteration i-1, is converted into the stage
+      // of tile i-3, and the loads of tile i+2 go out.  bf16: tile i+3 goes
+      // into the stage of tile i-1, which every wave finished reading in
+      // iteration i-1 (iteration 0 also issues tile 2: stages 2 and 3 held
+      // the query rows until B0)
       if constexpr (FP8) {
         if (i + 1 < ntiles) {
           wait_vmcnt<0>();
           fp8_store(i + 1);
           if (i + 2 < ntiles) fp8_load(i + 2);
         }
-      } else if (i + 2 < ntiles) {
-        copy_tile(i + 2);
+      } else {
+        if (i == 0 && 2 < ntiles) copy_tile(2);
+        if (i + 3 < ntiles) copy_tile(i + 3);
       }
       if (i == 0) bar();                               // the score waves' reference exchange
-      if (i >= 1) {
+      if constexpr (!FP8) {
+        if (i >= 1) {
+          const int u = i - 1;
+          bf16x8 pb[HBS];
+#pragma unroll
+          for (int hb = 0; hb < HBS; ++hb) pb[hb] = pl[((u & 1) * 4 + lgrp) * ROWS + hb * 16 + lrow];
+#pragma unroll
+          for (int db = 0; db < DBW; ++db)
+#pragma unroll
+            for (int hb = 0; hb < HBS; ++hb) oacc[db][hb] = Mma<bf16>::mma(va[db], pb[hb], oacc[db][hb]);
+        }
+        // then this tile's fragments replace them
+        if (i < ntiles) {
+          const lds_bf16 *st = st_base + (i % NS) * STAGE;
+#pragma unroll
+          for (int db = 0; db < DBW; ++db) {
+            const int o = t_base + 16 * ((db & 3) ^ t_fh) + 64 * (db >> 2);
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + o));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + o + TRH));
+            va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+        }
+        // tile i+1 has landed (tiles i+2 and i+3 may stay in flight)
+        if (i + 3 < ntiles) wait_vmcnt<2 * LOADS>();
+        else if (i + 2 < ntiles) wait_vmcnt<LOADS>();
+        else wait_vmcnt<0>();
+      } else if (i >= 1) {
         const int u = i - 1;
         const lds_bf16 *st = st_base + (u % NS) * STAGE;
-        bf16x8 va[DBW], pb[HBS];
+        bf16x8 vb[DBW], pb[HBS];
 #pragma unroll
         for (int hb = 0; hb < HBS; ++hb) pb[hb] = pl[((u & 1) * 4 + lgrp) * ROWS + hb * 16 + lrow];
 #pragma unroll
@@ -901,17 +935,12 @@ __global__ __launch_bounds__(512, 1) void decode_attn_ws_kernel(DecodeArgs a) {
           const int o = t_base + 16 * ((db & 3) ^ t_fh) + 64 * (db >> 2);
           const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + o));
           const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + o + TRH));
-          va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          vb[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
 #pragma unroll
         for (int db = 0; db < DBW; ++db)
 #pragma unroll
-          for (int hb = 0; hb < HBS; ++hb) oacc[db][hb] = Mma<bf16>::mma(va[db], pb[hb], oacc[db][hb]);
-      }
-      // this wave's copies of tile i+1 (tile i+2 may stay in flight)
-      if constexpr (!FP8) {
-        if (i + 2 < ntiles) wait_vmcnt<LOADS>();
-        else wait_vmcnt<0>();
+          for (int hb = 0; hb < HBS; ++hb) oacc[db][hb] = Mma<bf16>::mma(vb[db], pb[hb], oacc[db][hb]);
       }
       wait_lgkm0();
       bar();                                           // end of iteration i
