@@ -302,6 +302,23 @@ __global__ __launch_bounds__(256) void gemm_stream_reduce_kernel(GemmArgs a, int
 
 int gemm_stream_grid() { return 256; }
 
+// Workgroups: whole tiles per workgroup when that keeps at least 3/4 of the
+// CUs busy (no partials, no reduce); otherwise an even split of the units
+// over at most one workgroup per CU, and fewer when a product has few tiles
+// of many units (the cache compression alone: 9 tiles of 28), so that no
+// tile is shared by more than MAX_PARTS workgroups (a workgroup holds
+// floor(U/G) or one more units, so a tile of KS units meets at most
+// KS / floor(U/G) + 2 of them).
+static int stream_grid_for(int U, int KS, int tiles) {
+  const int full = gemm_stream_grid();
+  if (U > full)
+    for (int g = full; g * 4 >= full * 3; --g)
+      if (tiles % g == 0) return g;
+  int g = std::min(U, full);
+  while (g > 1 && KS / std::max(1, U / g) + 2 > MAX_PARTS) --g;
+  return g;
+}
+
 size_t gemm_stream_partial_bytes(int M) {
   const int mb = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
   return (size_t)gemm_stream_grid() * 2 * 16 * mb * SBN * sizeof(float);
@@ -320,24 +337,13 @@ bool gemm_stream_ok(const GemmArgs &a, int wkn) {
   if (a.partial_bytes < gemm_stream_partial_bytes(a.M)) return false;   // the partials' layout must fit
   const long units = (long)a.batch * ((a.N + SBN - 1) / SBN) * (a.K / bk);
   if (units * gemm_stream_grid() >= (1L << 31)) return false;
-  // a tile is shared by at most MAX_PARTS workgroups
-  const long per = std::max<long>(1, units / gemm_stream_grid()), ks = a.K / bk;
-  if (ks / per + 2 > MAX_PARTS) return false;
+  // (the grid keeps the workgroups sharing a tile within MAX_PARTS)
   if (wkn) return a.N % SBN == 0 && a.nw == 1;
   for (int s = 0; s < a.nw - 1; ++s)
     if (a.w_end[s] % SBN != 0) return false;   // a tile never straddles two weight segments
   return true;
 }
 
-// Workgroups: whole tiles per workgroup when that keeps at least 3/4 of the
-// CUs busy (no partials, no reduce); otherwise an even split of the units.
-static int stream_grid_for(int U, int KS, int tiles) {
-  const int full = gemm_stream_grid();
-  if (U <= full) return U;
-  for (int g = full; g * 4 >= full * 3; --g)
-    if (tiles % g == 0) return g;
-  return full;
-}
 
 template <int MB, bool WKN, bool F8>
 static hipError_t launch_stream_t(GemmArgs &a, hipStream_t st) {

@@ -164,6 +164,26 @@ PrefillPlan plan_prefill(const mla_config *c, int64_t T) {
   return p;
 }
 
+// Standalone cache compression of n tokens: with an FP8 cache the rows'
+// c_KV and k_R before quantisation; with FP8 projections the quantised h and,
+// up to 128 tokens, the streaming kernel's partial sums.  Nothing otherwise.
+struct CompressPlan {
+  size_t ckv, kr, x8, xs, partial, total;
+};
+CompressPlan plan_compress(const mla_config *c, int64_t n) {
+  CompressPlan p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += align256(bytes); return at; };
+  const bool f8 = weights_fp8(c), c8 = cache_fp8(c);
+  p.ckv = take(c8 ? (size_t)n * c->d_c * esize(c) : 0);
+  p.kr = take(c8 ? (size_t)n * c->d_rope * esize(c) : 0);
+  p.x8 = take(f8 ? (size_t)n * c->d_model : 0);
+  p.xs = take(f8 ? (size_t)(c->d_model / 128) * fp8_scale_ld(n) : 0);
+  p.partial = take(f8 && n <= 128 ? gemm_stream_partial_bytes((int)n) : 0);
+  p.total = off;
+  return p;
+}
+
 // 256x256 tiles (bf16) unless they would leave all but a few CUs idle: a
 // few hundred tokens against a narrow weight (a 512-token chunk: 18 tiles for
 // the down projection) go to the 32x64-tile kernel, which spreads over every
@@ -674,25 +694,40 @@ mla_status mla_workspace_size(const mla_config *cfg, int32_t op, int32_t batch, 
     *bytes = plan_decode(cfg, batch, len_or_nq, max_cache_len).total;
     return MLA_OK;
   }
+  if (op == MLA_OP_COMPRESS) {
+    if (len_or_nq > (1 << 24)) return MLA_ERR_UNSUPPORTED;
+    *bytes = plan_compress(cfg, len_or_nq).total;
+    return MLA_OK;
+  }
   return MLA_ERR_SHAPE;
 }
 
 mla_status mla_compress_kv(const mla_config *cfg, const mla_weights *w, const void *h, int32_t n,
                            const int32_t *seq_idx, const int32_t *pos, int32_t batch, const mla_cache *cache,
-                           void *stream) {
+                           void *workspace, size_t workspace_bytes, void *stream) {
   mla_status s = check_config(cfg);
   if (s != MLA_OK) return s;
   if (!w || !w->w_dkv || !w->w_kr) return MLA_ERR_NULL;
+  if (weights_fp8(cfg) && (!w->s_dkv || !w->s_kr)) return MLA_ERR_NULL;
   if (!h || !seq_idx || !pos) return MLA_ERR_NULL;
   if (n <= 0 || batch <= 0) return MLA_ERR_SHAPE;
+  if (n > (1 << 24)) return MLA_ERR_UNSUPPORTED;
   if ((s = check_cache(cache, batch, 1)) != MLA_OK) return s;
-  if (cache_fp8(cfg) || weights_fp8(cfg)) return MLA_ERR_UNSUPPORTED;
+  if (cache_fp8(cfg) && cache->block_table && cache->block_size % 32) return MLA_ERR_UNSUPPORTED;
+  const CompressPlan p = plan_compress(cfg, n);
+  if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return MLA_ERR_WORKSPACE;
   RowMap rows = {ROWS_EXPLICIT, 1, nullptr, seq_idx, pos};
   SplitK sk = {1, cfg->d_model};
+  char *ws = (char *)workspace;
+  const Fp8Out f8 = {p.x8 < p.total ? (unsigned char *)(ws + p.x8) : nullptr,
+                     p.xs < p.total ? (unsigned char *)(ws + p.xs) : nullptr, (long)fp8_scale_ld(n)};
+  const bool c8 = cache_fp8(cfg), w8 = weights_fp8(cfg);
+  const Part part = {w8 && n <= 128 ? (float *)(ws + p.partial) : nullptr, w8 && n <= 128 ? p.total - p.partial : 0};
   const hipStream_t st = (hipStream_t)stream;
   if ((s = debug_begin(st)) != MLA_OK) return s;
-  return debug_end(st, hip_status(run_compress(cfg, w, h, n, rows, cache, batch, false, nullptr, nullptr, nullptr,
-                                               sk, Part{nullptr, 0}, nullptr, st)));
+  return debug_end(st, hip_status(run_compress(cfg, w, h, n, rows, cache, batch, false, nullptr,
+                                               c8 ? ws + p.ckv : nullptr, c8 ? ws + p.kr : nullptr, sk, part,
+                                               w8 ? &f8 : nullptr, st)));
 }
 
 mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *h, int32_t batch, int32_t len,

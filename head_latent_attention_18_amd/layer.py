@@ -118,7 +118,10 @@ class MlaLayer:
     def compress_kv(self, h: torch.Tensor, seq_idx: torch.Tensor, pos: torch.Tensor, batch: int, cache: CacheBuf,
                     stream=None):
         n = h.shape[0]
-        L.mla_compress_kv(self.cfg, self.cw, h, n, seq_idx, pos, batch, cache.desc, stream)
+        nbytes = L.mla_workspace_size(self.cfg, L.MLA_OP_COMPRESS, 1, n, 0)
+        ws = self.workspace("compress", nbytes, h.device) if nbytes else None
+        L.mla_compress_kv(self.cfg, self.cw, h, n, seq_idx, pos, batch, cache.desc, ws,
+                          ws.numel() if ws is not None else 0, stream)
 
 
 def cache_from_rows(rows_per_seq, lens, d_row: int, bf16: bool, paged: bool = False, block_size: int = 64,

@@ -18,7 +18,7 @@ LIB_PATH = os.environ.get("MLA_LIBRARY") or os.path.join(os.path.dirname(os.path
 MLA_FP32, MLA_BF16 = 0, 1
 MLA_CACHE_LAYER, MLA_CACHE_FP8_E4M3 = 0, 1
 MLA_WEIGHTS_LAYER, MLA_WEIGHTS_FP8_BLOCK = 0, 1
-MLA_OP_PREFILL, MLA_OP_DECODE = 0, 1
+MLA_OP_PREFILL, MLA_OP_DECODE, MLA_OP_COMPRESS = 0, 1, 2
 STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTYPE",
           -4: "MLA_ERR_WORKSPACE", -5: "MLA_ERR_CACHE", -6: "MLA_ERR_HIP", -7: "MLA_ERR_UNSUPPORTED"}
 WEIGHT_NAMES = ("w_dq", "w_uq", "w_qr", "w_dkv", "w_kr", "w_uk", "w_uv", "w_o")
@@ -67,7 +67,7 @@ def load(path: str) -> ctypes.CDLL:
     lib.mla_workspace_size.argtypes = [P(mla_config), c_int32, c_int32, c_int32, c_int32, P(c_size_t)]
     lib.mla_workspace_size.restype = c_int32
     lib.mla_compress_kv.argtypes = [P(mla_config), P(mla_weights), c_void_p, c_int32, c_void_p, c_void_p,
-                                    c_int32, P(mla_cache), c_void_p]
+                                    c_int32, P(mla_cache), c_void_p, c_size_t, c_void_p]
     lib.mla_compress_kv.restype = c_int32
     lib.mla_prefill.argtypes = [P(mla_config), P(mla_weights), c_void_p, c_int32, c_int32, P(mla_cache),
                                 c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
@@ -165,10 +165,11 @@ def mla_workspace_size(cfg: mla_config, op: int, batch: int, len_or_nq: int, max
     return out.value
 
 
-def mla_compress_kv(cfg, w: mla_weights, h, n: int, seq_idx, pos, batch: int, cache: mla_cache, stream=None):
+def mla_compress_kv(cfg, w: mla_weights, h, n: int, seq_idx, pos, batch: int, cache: mla_cache, workspace=None,
+                    workspace_bytes: int = 0, stream=None):
     _check("mla_compress_kv", _lib().mla_compress_kv(ctypes.byref(cfg), ctypes.byref(w), _ptr(h), n,
                                                      _ptr(seq_idx), _ptr(pos), batch, ctypes.byref(cache),
-                                                     _stream(stream)))
+                                                     _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def mla_prefill(cfg, w: mla_weights, h, batch: int, length: int, cache: mla_cache, u, o_heads, workspace,

@@ -162,14 +162,23 @@ void fixed_cases() {
   EXPECT_EQ(mla_decode_noalloc(&c, &w, FAKE, 2, 300, (const int32_t *)FAKE, nullptr, 633, &k633, FAKE, nullptr,
                                nullptr), MLA_ERR_WORKSPACE);
   // compression
-  EXPECT_EQ(mla_compress_kv(&c, &w, FAKE, 0, (const int32_t *)FAKE, (const int32_t *)FAKE, 1, &k16, nullptr),
+  EXPECT_EQ(mla_compress_kv(&c, &w, FAKE, 0, (const int32_t *)FAKE, (const int32_t *)FAKE, 1, &k16, nullptr, 0,
+                            nullptr),
             MLA_ERR_SHAPE);
   mla_cache k0 = contiguous(0);
-  EXPECT_EQ(mla_compress_kv(&c, &w, FAKE, 4, (const int32_t *)FAKE, (const int32_t *)FAKE, 1, &k0, nullptr),
+  EXPECT_EQ(mla_compress_kv(&c, &w, FAKE, 4, (const int32_t *)FAKE, (const int32_t *)FAKE, 1, &k0, nullptr, 0,
+                            nullptr),
             MLA_ERR_CACHE);
   c.cache_dtype = MLA_CACHE_FP8_E4M3;
-  EXPECT_EQ(mla_compress_kv(&c, &w, FAKE, 4, (const int32_t *)FAKE, (const int32_t *)FAKE, 1, &k16, nullptr),
-            MLA_ERR_UNSUPPORTED);
+  // the FP8 cache's rows are staged in the workspace: none, or too small
+  EXPECT_EQ(mla_workspace_size(&c, MLA_OP_COMPRESS, 1, 4, 0, &bytes), MLA_OK);
+  EXPECT_TRUE(bytes > 0);
+  EXPECT_EQ(mla_compress_kv(&c, &w, FAKE, 4, (const int32_t *)FAKE, (const int32_t *)FAKE, 1, &k16, nullptr, 0,
+                            nullptr),
+            MLA_ERR_WORKSPACE);
+  EXPECT_EQ(mla_compress_kv(&c, &w, FAKE, 4, (const int32_t *)FAKE, (const int32_t *)FAKE, 1, &k16, FAKE, bytes - 1,
+                            nullptr),
+            MLA_ERR_WORKSPACE);
   // block-scaled FP8 projections
   c = dsv3();
   c.weight_dtype = MLA_WEIGHTS_FP8_BLOCK;
@@ -177,8 +186,14 @@ void fixed_cases() {
   mla_weights wns = w;
   wns.s_o = nullptr;
   EXPECT_EQ(mla_prefill(&c, &wns, FAKE, 1, 16, &k16, FAKE, nullptr, FAKE, 1ull << 40, nullptr), MLA_ERR_NULL);
-  EXPECT_EQ(mla_compress_kv(&c, &w, FAKE, 4, (const int32_t *)FAKE, (const int32_t *)FAKE, 1, &k16, nullptr),
-            MLA_ERR_UNSUPPORTED);
+  EXPECT_EQ(mla_compress_kv(&c, &w, FAKE, 4, (const int32_t *)FAKE, (const int32_t *)FAKE, 1, &k16, nullptr, 0,
+                            nullptr),
+            MLA_ERR_WORKSPACE);
+  mla_weights wnk = w;
+  wnk.s_kr = nullptr;   // the compression reads W_KR's scales
+  EXPECT_EQ(mla_compress_kv(&c, &wnk, FAKE, 4, (const int32_t *)FAKE, (const int32_t *)FAKE, 1, &k16, FAKE,
+                            1ull << 40, nullptr),
+            MLA_ERR_NULL);
   c.weight_dtype = 5;
   EXPECT_EQ(mla_workspace_size(&c, 1, 32, 1, 4096, &bytes), MLA_ERR_DTYPE);
   c.weight_dtype = MLA_WEIGHTS_FP8_BLOCK;
@@ -230,7 +245,7 @@ void sweeps(int n) {
                                              kk, nullptr, nullptr, nullptr);
     EXPECT_TRUE(sn != MLA_OK && sn != MLA_ERR_HIP);
     // compression with a NULL position array
-    const mla_status sc = mla_compress_kv(&c, &w, FAKE, n, (const int32_t *)FAKE, nullptr, b, kk, nullptr);
+    const mla_status sc = mla_compress_kv(&c, &w, FAKE, n, (const int32_t *)FAKE, nullptr, b, kk, nullptr, 0, nullptr);
     EXPECT_TRUE(sc != MLA_OK && sc != MLA_ERR_HIP);
   }
 }

@@ -201,16 +201,25 @@ def test_fp8_cache_validation():
                                                max_blocks_per_seq=8)) == -7
     assert _prefill(cfg=fp8, cache=L.make_cache(FAKE, block_size=48, n_blocks=8, block_table=FAKE,
                                                 max_blocks_per_seq=8)) == -7
-    # the standalone compression has no workspace for the row's scales
+    # the standalone compression stages the rows before their scales are
+    # known: it needs the workspace mla_workspace_size names for it
     w = _weights()
+    out = ctypes.c_size_t(0)
+    assert L.lib().mla_workspace_size(ctypes.byref(fp8), L.MLA_OP_COMPRESS, 1, 4, 0, ctypes.byref(out)) == 0
+    assert out.value >= 4 * (512 + 64) * 2
+    comp = lambda ws, nb: L.lib().mla_compress_kv(ctypes.byref(fp8), ctypes.byref(w), FAKE, 4, FAKE, FAKE, 1,
+                                                 ctypes.byref(L.make_cache(FAKE, max_len=16)), ws, nb, None)
+    assert comp(None, 0) == -4
+    assert comp(FAKE, out.value - 1) == -4
     assert L.lib().mla_compress_kv(ctypes.byref(fp8), ctypes.byref(w), FAKE, 4, FAKE, FAKE, 1,
-                                   ctypes.byref(L.make_cache(FAKE, max_len=16)), None) == -7
+                                   ctypes.byref(L.make_cache(FAKE, block_size=16, n_blocks=8, block_table=FAKE,
+                                                             max_blocks_per_seq=8)), FAKE, 1 << 30, None) == -7
 
 
 def test_fp8_weights_validation():
     """Block-scaled FP8 projections: the scale pointers are required, the
     layer must be bf16 with d_model and n_heads*d_v multiples of 512, and
-    the standalone compression (no workspace for the quantised h) refuses."""
+    the standalone compression needs a workspace for the quantised h."""
     fp8 = L.make_config(DSV3, "bf16", weights="fp8")
     out = ctypes.c_size_t(0)
     ws = lambda cfg: L.lib().mla_workspace_size(ctypes.byref(cfg), 1, 32, 1, 4096, ctypes.byref(out))
@@ -236,8 +245,16 @@ def test_fp8_weights_validation():
     bad = L.make_config(DSV3, "bf16")
     bad.weight_dtype = 9
     assert ws(bad) == -3
-    assert L.lib().mla_compress_kv(ctypes.byref(fp8), ctypes.byref(w), FAKE, 4, FAKE, FAKE, 1,
-                                   ctypes.byref(cache), None) == -7
+    comp = lambda ww, ws, nb: L.lib().mla_compress_kv(ctypes.byref(fp8), ctypes.byref(ww), FAKE, 4, FAKE, FAKE, 1,
+                                                     ctypes.byref(cache), ws, nb, None)
+    assert L.lib().mla_workspace_size(ctypes.byref(fp8), L.MLA_OP_COMPRESS, 1, 4, 0, ctypes.byref(out)) == 0
+    need = out.value
+    assert need >= 7168 * 4                      # the quantised h of 4 tokens
+    assert L.lib().mla_workspace_size(ctypes.byref(L.make_config(DSV3, "bf16")), L.MLA_OP_COMPRESS, 1, 4, 0,
+                                      ctypes.byref(out)) == 0 and out.value == 0
+    assert comp(w, None, 0) == -4
+    assert comp(w, FAKE, need - 1) == -4
+    assert comp(L.make_weights({n: FAKE for n in L.WEIGHT_NAMES}, dict(scales, w_kr=None)), FAKE, need) == -1
 
 
 def test_compress_validation():
@@ -247,7 +264,8 @@ def test_compress_validation():
     call = lambda **k: L.lib().mla_compress_kv(ctypes.byref(k.get("cfg", cfg)), ctypes.byref(k.get("w", w)),
                                                k.get("h", FAKE), k.get("n", 4), k.get("seq", FAKE),
                                                k.get("pos", FAKE), k.get("batch", 1),
-                                               ctypes.byref(k.get("cache", cache)), None)
+                                               ctypes.byref(k.get("cache", cache)), k.get("ws", None),
+                                               k.get("nb", 0), None)
     assert call(h=None) == -1
     assert call(seq=None) == -1
     assert call(pos=None) == -1
@@ -255,6 +273,11 @@ def test_compress_validation():
     assert call(batch=0) == -2
     assert call(w=_weights(w_kr=None)) == -1
     assert call(cache=L.make_cache(FAKE, max_len=0)) == -5
+    assert call(n=(1 << 24) + 1) == -7
+    # layer-dtype cache and projections need no workspace (any given is ignored)
+    out = ctypes.c_size_t(7)
+    assert L.lib().mla_workspace_size(ctypes.byref(cfg), L.MLA_OP_COMPRESS, 1, 4, 0, ctypes.byref(out)) == 0
+    assert out.value == 0
 
 
 def test_binding_raises():

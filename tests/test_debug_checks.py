@@ -127,6 +127,6 @@ def test_debug_compress_position_outside_cache(dbg):
     pos = torch.tensor([0, 1, 2, 3, 4, 5, 6, 16], dtype=torch.int32, device="cuda")   # 16 is past max_len
     say("debug compress, position past the cache")
     code = dbg.mla_compress_kv(ctypes.byref(layer.cfg), ctypes.byref(layer.cw), h.data_ptr(), 8, seq.data_ptr(),
-                               pos.data_ptr(), 1, ctypes.byref(cache.desc), None)
+                               pos.data_ptr(), 1, ctypes.byref(cache.desc), None, 0, None)
     torch.cuda.synchronize()
     assert code == ERR_CACHE

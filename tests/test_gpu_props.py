@@ -10,7 +10,8 @@ from head_latent_attention_18_amd.layer import CacheBuf
 from mla_inputs import make_workload
 from oracle import mla_oracle as O
 
-from tests.gpu_harness import assert_close, decode_cache, layer_for, run_decode, say, upload, weights64
+from tests.gpu_harness import (assert_close, assert_fp8_rows, decode_cache, fp8_product_bound, layer_for, run_decode, say,
+                               upload, weights64)
 
 pytestmark = pytest.mark.gpu
 
@@ -135,6 +136,52 @@ def test_compress_kv_entry_point(wid):
     c_kv, k_r = O.compress_kv(weights64(wl), hx[idx].astype(np.float64), pos[idx], d)
     got = torch.stack([cache.read_rows(int(seq[i]), [int(pos[i])])[0] for i in idx])
     assert_close(got, np.concatenate([c_kv, k_r], axis=1), wl.bf16, "compressed rows")
+
+
+@pytest.mark.parametrize("cache_fp8,weights_fp8,n", [(True, False, 37), (False, True, 37), (True, False, 300),
+                                                     (False, True, 300), (True, True, 300)])
+def test_compress_kv_fp8(cache_fp8, weights_fp8, n):
+    """mla_compress_kv with an FP8 cache (rows staged in its workspace, then
+    quantised with their group scales) and with FP8 projections (h quantised
+    per token and 128 columns; 37 tokens stream the weights, 300 take the
+    256x256 tiles), into a permuted paged cache, positions in any order."""
+    wl = make_workload(2, batch=4, uniform_len=40, cache_fp8=cache_fp8, weights_fp8=weights_fp8)
+    d = wl.dims
+    layer = layer_for(wl)
+    rng = np.random.Generator(np.random.PCG64(19))
+    B, maxlen, bs = 3, 5000, 64
+    seq = rng.integers(0, B, n).astype(np.int32)
+    pos = rng.integers(0, maxlen, n).astype(np.int32)
+    slots = {}
+    for i, (s_, p_) in enumerate(zip(seq, pos)):
+        slots.setdefault((int(s_), int(p_)), []).append(i)
+    idx = sorted(v[0] for v in slots.values() if len(v) == 1)   # slots written by exactly one token
+    from mla_inputs import bf16_bits_to_f32, bf16_round
+    bits = bf16_round(rng.standard_normal((n, d.d_model)).astype(np.float32))
+    hx = bf16_bits_to_f32(bits)
+    h = upload(hx, bits, True)
+    nb = (maxlen + bs - 1) // bs
+    table = rng.permutation(B * nb).astype(np.int32).reshape(B, nb)
+    pool = torch.zeros(B * nb * bs, layer.row_width, dtype=layer.cache_tdtype, device="cuda")
+    cache = CacheBuf.paged(pool, bs, table)
+    say(f"compress_kv cache_fp8={cache_fp8} weights_fp8={weights_fp8} n={n}")
+    layer.compress_kv(h, torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), B, cache)
+    torch.cuda.synchronize()
+    # FP8 projections: the oracle's reading applies them to the quantised h
+    # and the dequantised weights, as its prefill does
+    hin = hx[idx].astype(np.float64)
+    if weights_fp8:
+        hin = O.fp8_activation(hin)
+    c_kv, k_r = O.compress_kv(weights64(wl), hin, pos[idx], d)
+    ref = np.concatenate([c_kv, k_r], axis=1)
+    got = torch.stack([cache.read_rows(int(seq[i]), [int(pos[i])])[0] for i in idx])
+    if cache_fp8:
+        # with FP8 projections the c_KV values carry the FP8 products' grouped
+        # accumulation error besides the bf16 rounding
+        extra = fp8_product_bound(hin, weights64(wl)["w_dkv"]) * 1.01 if weights_fp8 else None
+        assert_fp8_rows(got, ref, d, "compressed FP8 rows", extra=extra)
+    else:
+        assert_close(got, ref, True, "compressed rows")
 
 
 @pytest.mark.parametrize("P,C", [((96, 60), 40), ((200, 333), 300), ((500,), 300), ((1000, 37), 256)])
