@@ -43,6 +43,10 @@ typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+#ifndef MLA_GEMM_PINGPONG
+#define MLA_GEMM_PINGPONG 1
+#endif
+constexpr bool GEMM_PINGPONG = MLA_GEMM_PINGPONG != 0;
 constexpr int GBM = 256, GBN = 256, GBK = 64;   // GBK: bf16 k per slab (FP8: 2 * GBK)
 constexpr int GNT = 512;                        // threads (8 waves)
 constexpr int GNS = 2;                          // ring stages
@@ -231,6 +235,94 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
           for (int i = 0; i < 2; ++i)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wq[s][i], xq[s][j], acc[i][j], 0, 0, 0, sw,
                                                                         0, sx[j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else if constexpr (GEMM_PINGPONG) {
+    // Two wave groups take turns on each SIMD (waves w and w+4 share SIMD
+    // w): while one group runs a slab's 32 MFMAs from registers, the other
+    // reads all of its fragments of that slab from LDS, so every matrix core
+    // always has one wave's burst to run.  Group 0 also issues the copies,
+    // one slab ahead, into the stage that both groups have finished reading.
+    //   interval 2k:   group 0 copies slab k+1 and reads slab k
+    //   interval 2k+1: group 0 multiplies slab k and waits for its copies;
+    //                  group 1 reads slab k
+    //   interval 2k+2: group 1 multiplies slab k
+    // Each interval ends at a workgroup barrier; group 1 passes one more
+    // barrier before its loop and group 0 one after its loop, so both pass
+    // 2 nkt + 2 barriers.
+    const int grp = wave >> 2;
+    const int tr = tid >> 3;                                  // group 0: row of the lane's chunks
+    const unsigned cb = (unsigned)(((tid & 7) ^ ((tid >> 4) & 7)) * 16);   // its (swizzled) chunk
+    auto issue_pp = [&](int kt, int st) {
+      const unsigned dst = lring + (unsigned)(st * GSTAGE * 2) + wave * 1024;
+      const char *xb = xsrc + kt * SK * ESZ, *wb = wsrc + kt * SK * ESZ;
+#pragma unroll
+      for (int i = 0; i < XCHK / 256; ++i)
+        dma16(xb, (unsigned)(min(i * 32 + tr, xrows - 1) * a.ldx * ESZ) + cb, dst + i * 256 * 16);
+#pragma unroll
+      for (int i = 0; i < WCHK / 256; ++i)
+        dma16(wb, (unsigned)(min(i * 32 + tr, wrows - 1) * a.ldw * ESZ) + cb, dst + (XCHK / 256 + i) * 256 * 16);
+    };
+    bf16x8 pw[NSTEP][2], px[NSTEP][4];
+    auto rd_all = [&](int st) {
+      const lds_bf16 *xs = rl + st * GSTAGE;
+      const lds_bf16 *ws = xs + XCHK * 8;
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) {
+        const int c = 2 * s + fh;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int wr = wn * 64 + b * 32 + fr;
+          pw[s][b] = *(const lds_bf16x8 *)(ws + (wr * RCH + (c ^ swz(wr))) * 8);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int xr = wm * 128 + b * 32 + fr;
+          px[s][b] = *(const lds_bf16x8 *)(xs + (xr * RCH + (c ^ swz(xr))) * 8);
+        }
+      }
+    };
+    auto mm_all = [&]() {
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pw[s][i], px[s][j], acc[i][j], 0, 0, 0);
+    };
+    if (grp == 0) {
+      issue_pp(0, 0);
+      wait_vm<0>();
+      bar();                                   // slab 0 landed
+      for (int kt = 0; kt < nkt; ++kt) {
+        if (kt + 1 < nkt) issue_pp(kt + 1, (kt + 1) % GNS);
+        rd_all(kt % GNS);
+        wait_lgkm0();
+        __builtin_amdgcn_sched_barrier(0);
+        bar();                                 // end of interval 2kt
+        __builtin_amdgcn_sched_barrier(0);
+        mm_all();
+        __builtin_amdgcn_sched_barrier(0);     // the wait stays behind the burst
+        wait_vm<0>();                          // slab kt+1 (this wave's copies)
+        __builtin_amdgcn_sched_barrier(0);
+        bar();                                 // end of interval 2kt+1
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      bar();                                   // end of interval 2nkt
+    } else {
+      bar();                                   // slab 0 landed
+      bar();                                   // end of interval 0
+      for (int kt = 0; kt < nkt; ++kt) {
+        rd_all(kt % GNS);
+        wait_lgkm0();
+        __builtin_amdgcn_sched_barrier(0);
+        bar();                                 // end of interval 2kt+1
+        __builtin_amdgcn_sched_barrier(0);
+        mm_all();
+        __builtin_amdgcn_sched_barrier(0);
+        bar();                                 // end of interval 2kt+2
         __builtin_amdgcn_sched_barrier(0);
       }
     }
