@@ -98,7 +98,7 @@ __device__ inline int swz(int row) { return (row >> 1) & 7; }
 
 }  // namespace
 
-template <bool SWAP, bool F8>
+template <bool SWAP, bool F8, bool SPLIT_COPY = false>
 __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
   constexpr int ESZ = F8 ? 1 : 2;               // bytes per operand element
   constexpr int SK = GBK * 2 / ESZ;             // k per slab (128 bytes of each row)
@@ -251,9 +251,30 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
     // Each interval ends at a workgroup barrier; group 1 passes one more
     // barrier before its loop and group 0 one after its loop, so both pass
     // 2 nkt + 2 barriers.
+    // SPLIT_COPY (chosen by the launcher when the grid is one wave of
+    // workgroups, a tile per CU at most): group 1 issues the weight half of
+    // slab k+1 at the start of interval 2k+1 instead (into the same free
+    // stage) and waits for it before that interval's barrier; measured
+    // faster there (fewer CUs share the L2, so a copy lands within the
+    // interval), slower with several tiles per CU.
     const int grp = wave >> 2;
-    const int tr = tid >> 3;                                  // group 0: row of the lane's chunks
-    const unsigned cb = (unsigned)(((tid & 7) ^ ((tid >> 4) & 7)) * 16);   // its (swizzled) chunk
+    const int ct = tid & 255;                                 // the lane's slot within its group
+    const int tr = ct >> 3;                                   // row of the lane's chunks
+    const unsigned cb = (unsigned)(((ct & 7) ^ ((ct >> 4) & 7)) * 16);     // its (swizzled) chunk
+    // half h (0: activation rows, 1: weight rows) of slab kt into stage st,
+    // by the 256 threads of one group
+    auto issue_half = [&](int kt, int st, int h) {
+      const unsigned dst = lring + (unsigned)(st * GSTAGE * 2) + (wave & 3) * 1024 + h * XCHK * 16;
+      const char *b = (h ? wsrc : xsrc) + kt * SK * ESZ;
+      // row pitch in bytes: 256 rows of it stay below 2^31 (checked by the launcher)
+      const unsigned ldb = (unsigned)((h ? a.ldw : a.ldx) * ESZ);
+      const int rows = h ? wrows : xrows;
+#pragma unroll
+      for (int i = 0; i < XCHK / 256; ++i)
+        dma16(b, (unsigned)min(i * 32 + tr, rows - 1) * ldb + cb, dst + i * 256 * 16);
+    };
+    static_assert(XCHK == WCHK && XCHK % 256 == 0, "");
+    // both halves by group 0
     auto issue_pp = [&](int kt, int st) {
       const unsigned dst = lring + (unsigned)(st * GSTAGE * 2) + wave * 1024;
       const char *xb = xsrc + kt * SK * ESZ, *wb = wsrc + kt * SK * ESZ;
@@ -297,7 +318,10 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
       wait_vm<0>();
       bar();                                   // slab 0 landed
       for (int kt = 0; kt < nkt; ++kt) {
-        if (kt + 1 < nkt) issue_pp(kt + 1, (kt + 1) % GNS);
+        if (kt + 1 < nkt) {
+          if constexpr (SPLIT_COPY) issue_half(kt + 1, (kt + 1) % GNS, 0);
+          else issue_pp(kt + 1, (kt + 1) % GNS);
+        }
         rd_all(kt % GNS);
         wait_lgkm0();
         __builtin_amdgcn_sched_barrier(0);
@@ -315,8 +339,12 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
       bar();                                   // slab 0 landed
       bar();                                   // end of interval 0
       for (int kt = 0; kt < nkt; ++kt) {
+        if constexpr (SPLIT_COPY) {
+          if (kt + 1 < nkt) issue_half(kt + 1, (kt + 1) % GNS, 1);
+        }
         rd_all(kt % GNS);
         wait_lgkm0();
+        if constexpr (SPLIT_COPY) wait_vm<0>();   // the weight half of slab kt+1
         __builtin_amdgcn_sched_barrier(0);
         bar();                                 // end of interval 2kt+1
         __builtin_amdgcn_sched_barrier(0);
@@ -520,6 +548,9 @@ hipError_t launch_gemm_big(GemmArgs &a, int swap, hipStream_t st) {
   if (a.fp8) {
     if (!swap) return hipErrorNotSupported;
     hipLaunchKernelGGL((gemm_big_kernel<true, true>), g3, dim3(GNT), 0, st, a);
+  } else if (swap && GEMM_PINGPONG && (long)a.tiles_m * a.tiles_n * a.splits <= 256) {
+    // the grid is one wave of workgroups: both wave groups issue copies
+    hipLaunchKernelGGL((gemm_big_kernel<true, false, true>), g3, dim3(GNT), 0, st, a);
   } else if (swap) {
     hipLaunchKernelGGL((gemm_big_kernel<true, false>), g3, dim3(GNT), 0, st, a);
   } else {
