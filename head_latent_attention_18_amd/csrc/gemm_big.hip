@@ -251,12 +251,12 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
     // Each interval ends at a workgroup barrier; group 1 passes one more
     // barrier before its loop and group 0 one after its loop, so both pass
     // 2 nkt + 2 barriers.
-    // SPLIT_COPY (chosen by the launcher when the grid is one wave of
-    // workgroups, a tile per CU at most): group 1 issues the weight half of
-    // slab k+1 at the start of interval 2k+1 instead (into the same free
-    // stage) and waits for it before that interval's barrier; measured
-    // faster there (fewer CUs share the L2, so a copy lands within the
-    // interval), slower with several tiles per CU.
+    // SPLIT_COPY (chosen by the launcher when the grid leaves most CUs of
+    // each XCD idle): group 1 issues the weight half of slab k+1 at the
+    // start of interval 2k+1 instead (into the same free stage) and waits
+    // for it before that interval's barrier; measured faster there (fewer
+    // CUs share the L2, so a copy lands within the interval), slower when
+    // three quarters of the CUs or more are busy.
     const int grp = wave >> 2;
     const int ct = tid & 255;                                 // the lane's slot within its group
     const int tr = ct >> 3;                                   // row of the lane's chunks
@@ -548,8 +548,9 @@ hipError_t launch_gemm_big(GemmArgs &a, int swap, hipStream_t st) {
   if (a.fp8) {
     if (!swap) return hipErrorNotSupported;
     hipLaunchKernelGGL((gemm_big_kernel<true, true>), g3, dim3(GNT), 0, st, a);
-  } else if (swap && GEMM_PINGPONG && (long)a.tiles_m * a.tiles_n * a.splits <= 256) {
-    // the grid is one wave of workgroups: both wave groups issue copies
+  } else if (swap && GEMM_PINGPONG && (long)a.tiles_m * a.tiles_n * a.splits <= 160) {
+    // at most 5/8 of the CUs busy: both wave groups issue copies (measured:
+    // 144 workgroups faster, 192 and 224 slower)
     hipLaunchKernelGGL((gemm_big_kernel<true, false, true>), g3, dim3(GNT), 0, st, a);
   } else if (swap) {
     hipLaunchKernelGGL((gemm_big_kernel<true, false>), g3, dim3(GNT), 0, st, a);
