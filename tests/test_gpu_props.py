@@ -226,3 +226,36 @@ def test_chunked_prefill_over_ragged_paged_cache(P, C):
         assert_close(u[b], ref["u"], True, f"chunk rows of sequence {b}")
         got_rows = cache.read_rows(b, np.arange(n))
         assert_close(got_rows, np.concatenate([ref["c_kv"], ref["k_r"]], axis=1), True, f"cache rows of sequence {b}")
+
+
+def test_chunked_prefill_2048_tokens_sampled_rows():
+    """A chunk of 2048 new tokens after a 1000-token cached prefix (paged):
+    the down-projection of 2048 tokens splits k in two (72 tiles of 256x256,
+    144 workgroups, each wave group issuing half of every slab copy) and its
+    ordered reduce writes the cache rows; sampled chunk rows of u against
+    the oracle, and every cache row."""
+    bs, P, C = 64, 1000, 2048
+    L = P + C
+    wl = make_workload(3, batch=1, seq_len=L)
+    d = wl.dims
+    layer = layer_for(wl)
+    rng = np.random.Generator(np.random.PCG64(12))
+    nb = (L + bs - 1) // bs
+    table = rng.permutation(nb).astype(np.int32).reshape(1, nb)
+    pool = torch.zeros(nb * bs, d.d_row, dtype=layer.tdtype, device="cuda")
+    cache = CacheBuf.paged(pool, bs, table)
+    h = upload(wl.h_f32, wl.h_bits, True)   # [1][L][d_model]
+    layer.compress_kv(h[0, :P].contiguous(), torch.zeros(P, dtype=torch.int32, device="cuda"),
+                      torch.arange(P, dtype=torch.int32, device="cuda"), 1, cache)
+    lens_host = np.array([L], dtype=np.int32)
+    say(f"chunked prefill: prefix {P}, chunk {C}, paged block {bs}")
+    u = layer.decode(h[:, P:].contiguous(), torch.from_numpy(lens_host).cuda(), L, cache,
+                     lens_host=lens_host).clone()
+    torch.cuda.synchronize()
+    rows = sorted(set([P, P + 1, P + 255, P + 256, P + 1023, P + 1024, L - 2, L - 1]
+                      + (P + rng.integers(0, C, 8)).tolist()))
+    ref = O.prefill(d, weights64(wl), wl.h_f32[0].astype(np.float64), rows=np.array(rows))
+    sel = torch.tensor([r - P for r in rows], device="cuda")
+    assert_close(u[0].index_select(0, sel), ref["u"], True, "sampled chunk rows")
+    assert_close(cache.read_rows(0, np.arange(L)), np.concatenate([ref["c_kv"], ref["k_r"]], axis=1), True,
+                 "all cache rows")
