@@ -3,11 +3,16 @@
 //
 //   * tile 256 tokens x 256 features, k slabs of 64; 8 waves (two per SIMD),
 //     each computing a 128-token x 64-feature block of Y^T with 32x32x16
-//     MFMAs; operand fragments are read two k steps ahead of their MFMAs;
+//     MFMAs;
 //   * X and W slabs go HBM/L2 -> LDS with global_load_lds_dwordx4 into a
 //     two-stage ring (no staging registers), one slab ahead: 64 KB per slab
-//     for 8.4 MFLOP keeps the L2 -> LDS stream (about 90 GB/s per CU) below
-//     what the matrix cores consume;
+//     for 8.4 MFLOP, so at the full MFMA rate a CU needs about 66 GB/s from
+//     L2, close to what the L2 delivers with this access pattern (about
+//     75 GB/s per CU with every CU copying);
+//   * bf16 main loop, ping-pong: the two waves of each SIMD alternate a
+//     slab's MFMA burst (all fragments in registers) and the LDS reads of
+//     their next fragments, turns separated by workgroup barriers; FP8 main
+//     loop: every wave reads fragments ahead of its MFMAs;
 //   * LDS rows are 8 chunks of 16 bytes with the chunk index XORed by
 //     (row >> 1) & 7, so the 16-row fragment reads hit 16 distinct bank groups;
 //   * tiles are handed out in GxG groups per XCD (G = 8, 4, 2 or 1, the
