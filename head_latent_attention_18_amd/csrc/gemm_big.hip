@@ -520,9 +520,10 @@ __global__ __launch_bounds__(GNT, 1) void gemm_big_kernel(GemmArgs a) {
 hipError_t launch_splitk_reduce_bf16(GemmArgs &a, hipStream_t st);
 
 bool gemm_big_ok(const GemmArgs &a) {
-  // bf16 from 256 tokens on; FP8 products of more than 128 tokens all come
-  // here (fewer stream), the tile's surplus rows clamped and not stored
-  if (a.fp8 ? (a.batch != 1 || a.K % (2 * GBK) != 0 || !a.xs) : (a.batch != 1 || a.M < GBM || a.K % GBK != 0))
+  // any number of tokens (the host sends bf16 products of 96 tokens or
+  // more, FP8 ones of more than 128): a tile's surplus rows are clamped
+  // copies of its last row and are not stored
+  if (a.fp8 ? (a.batch != 1 || a.K % (2 * GBK) != 0 || !a.xs) : (a.batch != 1 || a.K % GBK != 0))
     return false;
   for (int s = 0; s < a.nw - 1; ++s)
     if (a.w_end[s] % GBN != 0) return false;   // a tile never straddles two weight segments

@@ -184,12 +184,30 @@ CompressPlan plan_compress(const mla_config *c, int64_t n) {
   return p;
 }
 
+// Split over k of the 256x256 kernel's tiles when they fill at most half the
+// CUs (a few hundred tokens against a wide weight): about one wave of
+// workgroups, at least 1024 k per split, then the ordered reduce.
+int big_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles <= kCUs / 2)
+    for (int s = 8; s >= 2; --s)
+      if (s * tiles <= kCUs && K % (128 * s) == 0 && K / s >= 1024) return s;
+  return 1;
+}
+
 // 256x256 tiles (bf16) unless they would leave all but a few CUs idle: a
 // few hundred tokens against a narrow weight (a 512-token chunk: 18 tiles for
 // the down projection) go to the 32x64-tile kernel, which spreads over every
 // CU (180 -> 90 us there); from 32 tiles on the big tiles win (W_O at 512
-// tokens, 56 tiles: 362 against 393 us).
-int gemm_tile_for(int dtype, int64_t M, int64_t N, int64_t batch) {
+// tokens, 56 tiles: 362 against 393 us).  From 96 to 255 tokens the
+// weight-streaming kernels re-read the activation slice with every 64-column
+// unit (at 128 tokens twice the weight bytes); the 256x256 kernel (rows past
+// M clamped) takes such a product when its tiles, split over k, fill three
+// quarters of the CUs (W_O at 128 tokens: 118 -> 73 us; the query
+// up-projection's 96 unsplit tiles were slower than streaming).
+int gemm_tile_for(int dtype, int64_t M, int64_t N, int64_t batch, int64_t K) {
+  if (dtype == MLA_BF16 && batch == 1 && M >= 96 && M < 256)
+    return ((N + 255) / 256) * big_splits(M, N, K) >= kCUs * 3 / 4 ? TILE_BIG : TILE_SKINNY;
   if (dtype != MLA_BF16 || M < 256) return TILE_SKINNY;
   return ((M + 255) / 256) * ((N + 255) / 256) * batch >= kCUs / 8 ? TILE_BIG : TILE_SKINNY;
 }
@@ -201,20 +219,11 @@ SplitK choose_splitk(int dtype, int64_t M, int64_t N, int64_t K, int batch) {
   SplitK r;
   r.splits = 1;
   r.k_chunk = (int)K;
-  const int tile = gemm_tile_for(dtype, M, N, batch);
+  const int tile = gemm_tile_for(dtype, M, N, batch, K);
   if (tile != TILE_SKINNY) {
-    // 256x256 tiles filling at most half the CUs (a few hundred tokens
-    // against a wide weight): split k so that about one wave of workgroups
-    // runs, at least 1024 k per split, then the ordered reduce
     if (dtype == MLA_BF16 && batch == 1) {
-      const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-      if (tiles <= kCUs / 2)
-        for (int s = 8; s >= 2; --s)
-          if (s * tiles <= kCUs && K % (128 * s) == 0 && K / s >= 1024) {
-            r.splits = s;
-            r.k_chunk = (int)(K / s);
-            break;
-          }
+      r.splits = big_splits(M, N, K);
+      r.k_chunk = (int)(K / r.splits);
     }
     return r;
   }
@@ -529,7 +538,7 @@ hipError_t run_compress(const mla_config *c, const mla_weights *w, const void *h
     hipError_t e = fp8_operands(*f8, h, M, c->d_model, a, false, st);
     if (e != hipSuccess) return e;
   }
-  hipError_t e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 1, 0, a, st);
+  hipError_t e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch, a.K), 1, 0, a, st);
   if (e != hipSuccess || !fp8) return e;
   CacheAppendArgs ap;
   ap.ckv = (const bf16 *)ckv_mirror;
@@ -584,7 +593,7 @@ hipError_t run_query(const mla_config *c, const mla_weights *w, const void *c_q,
                      void *qc, long qc_ld, long qc_head_ld, void *qr, long qr_ld, long qr_head_ld, int qr_off,
                      SplitK sk, Part partial, hipStream_t st) {
   GemmArgs a = query_args(c, w, c_q, M, rows, qc, qc_ld, qc_head_ld, qr, qr_ld, qr_head_ld, qr_off, sk, partial);
-  return launch_gemm(c->dtype == MLA_BF16, gemm_tile_for(c->dtype, M, a.N, a.batch), 1, 0, a, st);
+  return launch_gemm(c->dtype == MLA_BF16, gemm_tile_for(c->dtype, M, a.N, a.batch, a.K), 1, 0, a, st);
 }
 
 // u = o W_O^T
@@ -609,7 +618,7 @@ hipError_t run_output(const mla_config *c, const mla_weights *w, const void *o, 
     hipError_t e = fp8_operands(*f8, o, M, K, a, f8_ready, st);
     if (e != hipSuccess) return e;
   }
-  return launch_gemm(c->dtype == MLA_BF16, gemm_tile_for(c->dtype, M, a.N, a.batch), 1, 0, a, st);
+  return launch_gemm(c->dtype == MLA_BF16, gemm_tile_for(c->dtype, M, a.N, a.batch, a.K), 1, 0, a, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -778,7 +787,7 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
     a.epi.seg[0] = seg_plain(NH * cfg->d_nope, ws + p.k, (long)NH * cfg->d_nope);
     a.epi.nseg = 1;
     a.name = "k_up";
-    e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 1, 0, a, st);
+    e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch, a.K), 1, 0, a, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
   }
   {  // V^T = (c_KV W_UV^T)^T -> [n_h*d_v][T]
@@ -789,7 +798,7 @@ mla_status mla_prefill(const mla_config *cfg, const mla_weights *w, const void *
     a.epi.seg[0] = seg_plain(NH * cfg->d_v, ws + p.vt, (long)T);
     a.epi.nseg = 1;
     a.name = "v_up";
-    e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 0, 0, a, st);
+    e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch, a.K), 0, 0, a, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
   }
   {
@@ -883,7 +892,7 @@ mla_status decode_steps(const mla_config *cfg, const mla_weights *w, const void 
       a.epi.seg[0] = seg_plain(NH * cfg->d_nope, ws + p.kf, (long)NH * cfg->d_nope);
       a.epi.nseg = 1;
       a.name = "k_up";
-      e = launch_gemm(1, gemm_tile_for(dt, MK, a.N, 1), 1, 0, a, st);
+      e = launch_gemm(1, gemm_tile_for(dt, MK, a.N, 1, a.K), 1, 0, a, st);
       if (e != hipSuccess) return MLA_ERR_HIP;
     }
     {  // V^T = (c_KV W_UV^T)^T -> [n_h*d_v][B*Lpad]
@@ -894,7 +903,7 @@ mla_status decode_steps(const mla_config *cfg, const mla_weights *w, const void 
       a.epi.seg[0] = seg_plain(NH * cfg->d_v, ws + p.vtf, (long)MK);
       a.epi.nseg = 1;
       a.name = "v_up";
-      e = launch_gemm(1, gemm_tile_for(dt, MK, a.N, 1), 0, 0, a, st);
+      e = launch_gemm(1, gemm_tile_for(dt, MK, a.N, 1, a.K), 0, 0, a, st);
       if (e != hipSuccess) return MLA_ERR_HIP;
     }
     FlashArgs f;
@@ -951,7 +960,7 @@ mla_status decode_steps(const mla_config *cfg, const mla_weights *w, const void 
       a.partial = partial.p;
       a.partial_bytes = partial.bytes;
       a.name = "absorb";
-      e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 1, 1, a, st);
+      e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch, a.K), 1, 1, a, st);
       if (e != hipSuccess) return MLA_ERR_HIP;
     }
   }
@@ -1000,7 +1009,7 @@ mla_status decode_steps(const mla_config *cfg, const mla_weights *w, const void 
     a.partial = partial.p;
     a.partial_bytes = partial.bytes;
     a.name = "unabsorb";
-    e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch), 1, 0, a, st);
+    e = launch_gemm(dt == MLA_BF16, gemm_tile_for(dt, M, a.N, a.batch, a.K), 1, 0, a, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
   }
   e = run_output(cfg, w, o, M, u, p.sk5, partial, f8p, o_ready, st);

@@ -198,7 +198,7 @@ def mla_decode(cfg, w: mla_weights, h, batch: int, n_q: int, cache_lens, max_cac
                                            _stream(stream)))
 
 
-MLA_NOALLOC_WORKSPACE_BYTES = 96 << 20
+MLA_NOALLOC_WORKSPACE_BYTES = 128 << 20
 
 
 def mla_decode_noalloc(cfg, w: mla_weights, h, batch: int, n_q: int, cache_lens, max_cache_len: int,

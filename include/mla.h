@@ -283,10 +283,10 @@ mla_status mla_decode(const mla_config *cfg, const mla_weights *w, const void *h
                       const mla_cache *cache, void *u, void *o_heads,
                       void *workspace, size_t workspace_bytes, void *stream);
 
-/* Largest workspace mla_decode_noalloc can use: 96 MiB (DeepSeek-V3 widths:
- * batch 128 x one new token at cache lengths up to 32768 needs 90.5 MiB,
- * batch 32 at 4096 needs 35 MiB). */
-#define MLA_NOALLOC_WORKSPACE_BYTES (96u << 20)
+/* Largest workspace mla_decode_noalloc can use: 128 MiB (DeepSeek-V3 widths:
+ * batch 128 x one new token at cache lengths up to 32768 needs 102.5 MiB,
+ * 104.7 MiB with FP8 projections; batch 32 at 4096 needs 35 MiB). */
+#define MLA_NOALLOC_WORKSPACE_BYTES (128u << 20)
 
 /* mla_decode for callers that cannot allocate device memory or bring a
  * workspace (code under HIP graph capture, tight serving loops, harnesses

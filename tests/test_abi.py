@@ -185,7 +185,7 @@ def test_decode_noalloc_validation():
     assert call(lens=None) == -1
     assert call(nq=0) == -2
     assert call(cfg=_cfg(d_c=256)) == -7
-    # 2 sequences x 300 new tokens: about 312 MB of workspace, over the 96 MiB array
+    # 2 sequences x 300 new tokens: about 312 MB of workspace, over the 128 MiB array
     big = L.mla_workspace_size(cfg, L.MLA_OP_DECODE, 2, 300, 633)
     assert big > L.MLA_NOALLOC_WORKSPACE_BYTES
     assert call(B=2, nq=300, ml=633) == -4

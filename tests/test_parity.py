@@ -157,6 +157,27 @@ def test_dsv3_decode_small(B, L, nq):
         assert_close(got_new, ref["row_new"], True, f"new cache rows b={b}")
 
 
+@pytest.mark.parametrize("B,L,nq", [(100, 300, 2), (96, 200, 1)])
+def test_dsv3_decode_96_to_255_tokens(B, L, nq):
+    """200 and 96 new tokens in one decode call: W_O runs on the 256x256-tile
+    kernel split eight ways over k (one tile row, its rows past the token
+    count clamped and not stored) and the ordered reduce; the other products
+    keep their kernels.  Sequences at both ends and one inside against the
+    oracle."""
+    wl = make_workload(2, batch=B, uniform_len=L, n_q=nq)
+    layer = layer_for(wl)
+    cache = decode_cache(wl, layer)
+    say(f"decode B={B} L={L} n_q={nq} ({B * nq} tokens)")
+    u, o = run_decode(wl, layer, cache)
+    d = wl.dims
+    for b in (0, B // 2 + 7, B - 1):
+        ref = oracle_decode_seq(wl, b)
+        assert_close(u[b], ref["u"], True, f"u b={b}")
+        assert_close(o.view(B, nq, d.n_heads, d.d_v)[b], ref["o"], True, f"o b={b}")
+        got_new = cache.read_rows(b, np.arange(L - nq, L))
+        assert_close(got_new, ref["row_new"], True, f"new cache rows b={b}")
+
+
 # DeepSeek-V3 latent and head widths with 20 heads and a narrower model:
 # head counts off the multiples of 8 that the workgroup-to-XCD maps assume,
 # fewer query rows (20) than a 64-row decode workgroup, a W_O input width
