@@ -1043,8 +1043,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 // section 2.1 of the DeepSeek-V3 paper-reading notes), bf16, d_c = 512.  One
 // workgroup = (head i, 16 tokens), eight waves in two roles whose memory
 // counters are separate, so neither waits for the other's loads:
-//   waves 0..3 merge the splits of four tokens each (a lane per eight latent
-//     columns) into LDS, rounded to bf16 as a stored o_lat would be; only
+//   waves 0..3 merge the splits of four tokens each (wave w: tokens w, w+4,
+//     w+8, w+12; a lane per eight latent columns) into LDS, rounded to bf16
+//     as a stored o_lat would be; only
 //     the splits a token has are loaded, all of them before any is used;
 //   waves 4..7 copy W_UV,i (128 KB) into LDS.
 // Then O^T[v][t] = W_UV,i[v][:] . o_lat[t][:] on the matrix cores, wave w
@@ -1087,13 +1088,14 @@ __global__ __launch_bounds__(512, 1) void decode_combine_uv_kernel(DecodeArgs a,
     }
     wait_vmcnt<0>();
   } else {
-    // merge: wave w takes tokens 4w..4w+3 of the group
+    // merge: wave w takes tokens w, w+4, w+8, w+12 of the group (interleaved,
+    // so that a group of fewer tokens still spreads over the four waves)
     constexpr int TW = TT / NM;
     int bq[TW], rq[TW], nsp[TW];
     long base[TW];
 #pragma unroll
     for (int j = 0; j < TW; ++j) {
-      const int t = min(tg * TT + wave * TW + j, T - 1);
+      const int t = min(tg * TT + j * NM + wave, T - 1);
       bq[j] = t / a.n_q;
       rq[j] = (t % a.n_q) * a.n_h + h;
     }
@@ -1106,7 +1108,7 @@ __global__ __launch_bounds__(512, 1) void decode_combine_uv_kernel(DecodeArgs a,
       for (int j = 0; j < TW; ++j) {
         int slot0;
         plan_slots(sp[j], P, slot0, nsp[j]);
-        if (tg * TT + wave * TW + j >= T) nsp[j] = 0;
+        if (tg * TT + j * NM + wave >= T) nsp[j] = 0;
         nsp[j] = __builtin_amdgcn_readfirstlane(nsp[j]);
         base[j] = (long)slot0 * R + rq[j];
       }
@@ -1129,7 +1131,7 @@ __global__ __launch_bounds__(512, 1) void decode_combine_uv_kernel(DecodeArgs a,
     lds_bf16 *ol = (lds_bf16 *)olat;
 #pragma unroll
     for (int j = 0; j < TW; ++j) {
-      const int tl = wave * TW + j;
+      const int tl = j * NM + wave;
       float res[PER];
 #pragma unroll
       for (int i = 0; i < PER; ++i) res[i] = 0.f;
